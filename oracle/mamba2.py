@@ -1,0 +1,297 @@
+"""CPU oracle for the Mamba2 selective-state update over a slot pool (fp64).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+of the package entry point and the benchmark's CPU-baseline leg may import
+this module.  The HIP library never calls it, and this module imports nothing
+from the HIP side.
+
+What it computes, and where the pages say so
+--------------------------------------------
+Sources are four web pages on hybrid-model recurrent state:
+ * "Hybrid SSM / Mamba models and non-KV state" (mlinterviewnotes.com, ch. 7.3),
+   cited below as [SSM-hybrids];
+ * "hybrid-attn-ssm-kv-cache-sizing" (phantomic12.github.io), [sizing];
+ * "Hybrid KV cache vs recurrent state memory" (fanout.sh), [fanout];
+ * Mamba study notes (echobase-5bl.pages.dev, 2026.07.27.01), [notes].
+
+Per token t, per head h of group g = h // (H/G) (contiguous head->group map):
+ 1. conv: a rolling window of the last W-1 raw inputs per channel ([SSM-hybrids],
+    "There are two objects, not one": the short-convolution state of shape
+    (d_conv, W-1), d_conv = d_inner + 2*g*d_state), extended by the current
+    input u_t, feeds a causal depthwise Conv1d with bias, then SiLU
+    ([notes], "Mamba": x = SiLU(Conv1d(x'))).  All d_conv channels pass the
+    conv, in the order [x (H*P) | B (G*N) | C (G*N)].
+ 2. Delta = softplus(dt + dt_bias) ([SSM-hybrids], the decode call with
+    dt_bias and dt_softplus=True; [notes] Delta_t = Softplus(...)).
+ 3. h_t = exp(Delta*A) h_{t-1} + Delta * x_t B_t^T      ([notes], "Mamba")
+ 4. y_t = h_t C_t + D x_t   (readout of the new state; [notes], classic SSM
+    output y = C h + D x, and the Mamba readout y_t = C_t h_t)
+ 5. out_t = y_t * SiLU(z_t)                              ([notes], "Mamba")
+State lives in slots of a pool indexed [layer, slot, ...] ([SSM-hybrids],
+"MambaPool allocates one dense tensor per state object"); the temporal state
+has shape (H, P, N) ([SSM-hybrids], the state-shape function).
+
+Readings where the pages are silent (each also listed in the design notes):
+ * A is one negative scalar per head, passed directly; B-bar = Delta*B.
+ * conv tap k = W-1 multiplies the current token (causal cross-correlation).
+ * softplus is log(1 + e^v) evaluated exactly (no threshold).
+ * Stored state is rounded to its storage dtype: fp64 -> fp32 (RNE) -> bf16
+   (RNE on the fp32 bit pattern).  Decode rounds after every step; prefill
+   keeps the running state in fp64 and rounds only what it stores (final
+   state and checkpoints).  y is rounded to its output dtype.
+ * The conv window holds raw inputs rounded to the conv dtype; inside one
+   prefill call the conv reads the call's own inputs unrounded.
+ * has_initial_state = 0 means a zero state and a zero window; the slot is not read.
+ * A checkpoint at absolute position p (start_pos < p <= start_pos + L,
+   p % interval == 0) stores round(state after p tokens) and the window of the
+   raw inputs at positions p-W+1 .. p-1.
+
+Parity pins live in the test suite (matrix form of [notes] "Mamba and
+Attention", constant-input closed form, scipy lfilter scalar case,
+np.convolve conv, torch bf16 casts, byte counts printed on the pages).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_BYTES = {"f64": 8, "f32": 4, "bf16": 2}
+
+
+# --------------------------------------------------------------------------
+# rounding to a storage dtype
+# --------------------------------------------------------------------------
+def round_to(x, dtype: str) -> np.ndarray:
+    """Round float64 values to ``dtype`` and return them as float64.
+
+    'f64' is the identity, 'f32' is numpy's round-to-nearest-even cast, and
+    'bf16' rounds the fp32 bit pattern to its upper 16 bits with ties to even
+    (NaN stays a quiet NaN, overflow goes to infinity).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":
+        return x.copy()
+    with np.errstate(over="ignore", invalid="ignore"):
+        x32 = x.astype(np.float32)
+    if dtype == "f32":
+        return x32.astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    bits = x32.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    nan = np.isnan(x32)
+    quiet = ((bits | np.uint64(0x00400000)) >> np.uint64(16)) << np.uint64(16)
+    out = np.where(nan, quiet, rounded).astype(np.uint32)
+    return out.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# elementwise functions
+# --------------------------------------------------------------------------
+def silu(v):
+    """SiLU(v) = v / (1 + e^-v)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def softplus(v):
+    """softplus(v) = log(1 + e^v), written as max(v, 0) + log1p(e^-|v|)."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.maximum(v, 0.0) + np.log1p(np.exp(-np.abs(v)))
+
+
+# --------------------------------------------------------------------------
+# the two state objects of a slot pool
+# --------------------------------------------------------------------------
+class PoolRef:
+    """Oracle copy of a slot pool: ssm[layer, slot, H, P, N], conv[layer, slot, Cd, W-1].
+
+    Values are float64 holding numbers representable in the storage dtypes.
+    Slots the oracle never writes keep whatever the caller put there.
+    """
+
+    def __init__(self, shape, num_layers: int, num_slots: int, ssm_dtype: str, conv_dtype: str):
+        H, P, N = shape.nheads, shape.head_dim, shape.d_state
+        self.shape = shape
+        self.ssm_dtype, self.conv_dtype = ssm_dtype, conv_dtype
+        self.ssm = np.zeros((num_layers, num_slots, H, P, N))
+        self.conv = np.zeros((num_layers, num_slots, shape.conv_dim, shape.conv_kernel - 1))
+
+    def ssm_bytes_per_slot_layer(self) -> int:
+        """Temporal state bytes of one slot in one layer: H * P * N * sizeof(dtype)."""
+        s = self.shape
+        return s.nheads * s.head_dim * s.d_state * _BYTES[self.ssm_dtype]
+
+    def conv_bytes_per_slot_layer(self) -> int:
+        """Conv window bytes of one slot in one layer: d_conv * (W - 1) * sizeof(dtype)."""
+        s = self.shape
+        return s.conv_dim * (s.conv_kernel - 1) * _BYTES[self.conv_dtype]
+
+
+def _split(act, shape):
+    """Post-conv activations (..., Cd) -> x (..., H, P), B (..., G, N), C (..., G, N)."""
+    I, G, N = shape.intermediate, shape.n_groups, shape.d_state
+    lead = act.shape[:-1]
+    x = act[..., :I].reshape(lead + (shape.nheads, shape.head_dim))
+    B = act[..., I:I + G * N].reshape(lead + (G, N))
+    C = act[..., I + G * N:].reshape(lead + (G, N))
+    return x, B, C
+
+
+# --------------------------------------------------------------------------
+# decode: one token per sequence, in place on the pool
+# --------------------------------------------------------------------------
+def decode_step(pool: PoolRef, layer: int, params: dict, slots, u, z, dt, y_dtype: str):
+    """One decode token for each batch row.  Returns out (batch, H*P), rounded to y_dtype.
+
+    slots[b] < 0 is a padding row: the pool is neither read nor written and
+    its output row is zero.
+    """
+    s = pool.shape
+    H, P, G = s.nheads, s.head_dim, s.n_groups
+    hpg = H // G
+    gidx = np.arange(H) // hpg
+    A, D, dt_bias = params["A"], params["D"], params["dt_bias"]
+    w, b = params["conv_w"], params["conv_b"]
+    out = np.zeros((len(slots), s.intermediate))
+    for r, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        window = np.concatenate([pool.conv[layer, slot], np.asarray(u[r])[:, None]], axis=1)
+        act = silu(b + np.sum(w * window, axis=1))                     # step 1
+        x, Bm, Cm = _split(act, s)
+        delta = softplus(np.asarray(dt[r]) + dt_bias)                  # step 2
+        alpha = np.exp(delta * A)
+        h = pool.ssm[layer, slot]
+        h_new = alpha[:, None, None] * h + (delta[:, None] * x)[:, :, None] * Bm[gidx][:, None, :]   # 3
+        y = np.einsum("hpn,hn->hp", h_new, Cm[gidx]) + D[:, None] * x  # step 4
+        out[r] = (y.reshape(-1)) * silu(np.asarray(z[r]))              # step 5
+        pool.ssm[layer, slot] = round_to(h_new, pool.ssm_dtype)
+        pool.conv[layer, slot] = round_to(window[:, 1:], pool.conv_dtype)
+    return round_to(out, y_dtype)
+
+
+# --------------------------------------------------------------------------
+# the selective scan on post-conv inputs (one head)
+# --------------------------------------------------------------------------
+def ssm_scan(h0, x, Bm, Cm, delta, A: float, D: float):
+    """Token-by-token recurrence for one head; returns (y before the gate, final state).
+
+    h0 (P, N); x (L, P); Bm, Cm (L, N); delta (L,).
+    """
+    h = np.array(h0, dtype=np.float64, copy=True)
+    y = np.zeros_like(np.asarray(x, dtype=np.float64))
+    for t in range(len(delta)):
+        h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t], Bm[t])
+        y[t] = h @ Cm[t] + D * x[t]
+    return y, h
+
+
+def ssd_matrix_form(h0, x, Bm, Cm, delta, A: float, D: float):
+    """The semiseparable form Y = (M o L) X of [notes] ("Mamba and Attention"), one head.
+
+    M[i, j] = C_i . (prod_{k=j+1..i} Abar_k) Bbar_j with Abar_k = exp(Delta_k A)
+    and Bbar_j = Delta_j B_j; L is the causal mask.  A nonzero initial state
+    adds (prod_{k<=i} Abar_k) C_i . h0[p, :] to row i.  Built element by
+    element from the products, with no cumulative sums.
+    """
+    L = len(delta)
+    abar = np.exp(np.asarray(delta, dtype=np.float64) * A)
+    M = np.zeros((L, L))
+    for i in range(L):
+        for j in range(i + 1):
+            M[i, j] = (Cm[i] @ Bm[j]) * np.prod(abar[j + 1:i + 1]) * delta[j]
+    init = np.array([np.prod(abar[:i + 1]) * (np.asarray(h0) @ Cm[i]) for i in range(L)])
+    return M @ x + D * np.asarray(x) + init
+
+
+# --------------------------------------------------------------------------
+# prefill: packed variable-length sequences, chunk boundaries are invisible
+# --------------------------------------------------------------------------
+def conv_tokens(window0, u, conv_w, conv_b):
+    """Causal depthwise conv over a token stream: (W-1, C) initial window rows + (L, C) inputs.
+
+    Returns pre-activation v (L, C): v[t, c] = b[c] + sum_k w[c, k] * stream[t + k, c].
+    """
+    stream = np.concatenate([window0, u], axis=0)
+    W = conv_w.shape[1]
+    L = u.shape[0]
+    v = np.broadcast_to(conv_b, (L, conv_b.shape[0])).copy()
+    for k in range(W):
+        v += conv_w[:, k] * stream[k:k + L]
+    return v
+
+
+def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init, start_pos,
+            u, z, dt, y_dtype: str, ckpt_interval: int = 0, ckpt_slots=None, heads=None):
+    """Prefill packed sequences (cu_seqlens) into their slots; returns out (T, H*P).
+
+    heads (optional) restricts the recurrence and the state writes to those
+    heads; output columns of other heads are NaN.  Conv windows are always
+    written in full.  Checkpoints follow the rule in the module docstring.
+    """
+    s = pool.shape
+    H, P, N, G, W, I = s.nheads, s.head_dim, s.d_state, s.n_groups, s.conv_kernel, s.intermediate
+    heads = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    hpg = H // G
+    groups = heads // hpg
+    ug = np.unique(groups)
+    # channels this call needs: x of the chosen heads, B and C of their groups
+    xch = (heads[:, None] * P + np.arange(P)).ravel()
+    bch = (I + ug[:, None] * N + np.arange(N)).ravel()
+    cch = (I + G * N + ug[:, None] * N + np.arange(N)).ravel()
+    chans = np.concatenate([xch, bch, cch])
+    gpos = {g: i for i, g in enumerate(ug)}
+    gsel = np.array([gpos[g] for g in groups])
+    A, D, dt_bias = params["A"][heads], params["D"][heads], params["dt_bias"][heads]
+    T = int(cu_seqlens[-1])
+    out = np.full((T, I), np.nan)
+    for sq in range(len(slots)):
+        t0, t1 = int(cu_seqlens[sq]), int(cu_seqlens[sq + 1])
+        L = t1 - t0
+        if L == 0:
+            continue
+        slot = int(slots[sq])
+        if has_init[sq]:
+            h = pool.ssm[layer, slot][heads].copy()
+            win0 = pool.conv[layer, slot].T.copy()                 # (W-1, Cd)
+        else:
+            h = np.zeros((len(heads), P, N))
+            win0 = np.zeros((W - 1, s.conv_dim))
+        useq = np.asarray(u[t0:t1])
+        stream = np.concatenate([win0, useq], axis=0)             # raw inputs, window first
+        act = silu(conv_tokens(win0[:, chans], useq[:, chans],
+                               params["conv_w"][chans], params["conv_b"][chans]))
+        nx = len(xch)
+        x = act[:, :nx].reshape(L, len(heads), P)
+        Bm = act[:, nx:nx + len(bch)].reshape(L, len(ug), N)[:, gsel]
+        Cm = act[:, nx + len(bch):].reshape(L, len(ug), N)[:, gsel]
+        delta = softplus(np.asarray(dt[t0:t1])[:, heads] + dt_bias)
+        alpha = np.exp(delta * A)
+        zs = silu(np.asarray(z[t0:t1]).reshape(L, H, P)[:, heads])
+        sp = int(start_pos[sq])
+        for t in range(L):
+            h = alpha[t][:, None, None] * h + (delta[t][:, None] * x[t])[:, :, None] * Bm[t][:, None, :]
+            y = np.einsum("hpn,hn->hp", h, Cm[t]) + D[:, None] * x[t]
+            row = out[t0 + t].reshape(H, P)
+            row[heads] = y * zs[t]
+            p = sp + t + 1
+            if ckpt_interval and p % ckpt_interval == 0:
+                k = p // ckpt_interval - sp // ckpt_interval - 1
+                dst = int(ckpt_slots[sq][k]) if k < len(ckpt_slots[sq]) else -1
+                if dst >= 0:
+                    pool.ssm[layer, dst][heads] = round_to(h, pool.ssm_dtype)
+                    pool.conv[layer, dst] = round_to(stream[t + 1:t + W].T, pool.conv_dtype)
+        pool.ssm[layer, slot][heads] = round_to(h, pool.ssm_dtype)
+        pool.conv[layer, slot] = round_to(stream[L:L + W - 1].T, pool.conv_dtype)
+    return round_to(out, y_dtype)
+
+
+def checkpoint_states(pool: PoolRef, layer: int, src, dst):
+    """Copy both state objects of slot src[i] into slot dst[i] (layer < 0: every layer)."""
+    layers = range(pool.ssm.shape[0]) if layer < 0 else [layer]
+    for l in layers:
+        for a, b in zip(src, dst):
+            pool.ssm[l, b] = pool.ssm[l, a]
+            pool.conv[l, b] = pool.conv[l, a]

@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  The oracle is checked against forms that do
+not share its code path: the semiseparable matrix form built from explicit
+products, a closed form for constant inputs, scipy's IIR filter, numpy's
+convolution, torch's bf16 casts, and numbers printed on the pages
+(tests/golden/*.json, each entry with its citation).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import scipy.special
+import torch
+
+from oracle import mamba2 as orc
+from recurrent_state_update_amd import synth
+
+
+def rel_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- rounding
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(123)
+    n = 1_000_000
+    mags = 10.0 ** rng.uniform(-42, 39, n)
+    vals = rng.choice([-1.0, 1.0], n) * mags
+    one = 1.0
+    edges = np.array([
+        0.0, -0.0, np.inf, -np.inf, np.nan,
+        np.finfo(np.float32).max, -np.finfo(np.float32).max, 3.3895313892515355e38,
+        np.finfo(np.float32).tiny, 1e-45, -1e-45, 1e-40,
+        one + 2.0 ** -8, one + 3 * 2.0 ** -8, one + 2.0 ** -8 + 2.0 ** -30,  # ties and near-ties
+        -(one + 2.0 ** -8), 2.0 ** 127 * (2 - 2.0 ** -8),
+    ])
+    vals = np.concatenate([vals, edges, rng.standard_normal(10000)])
+    mine = orc.round_to(vals, "bf16")
+    ref = torch.from_numpy(vals).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref, equal_nan=True)
+    finite = ~np.isnan(ref)                     # torch canonicalises NaN to 0xFFFF; NaN sign is free
+    assert np.array_equal(np.signbit(mine[finite]), np.signbit(ref[finite]))
+    # fp32 rounding against torch's cast as well
+    ref32 = torch.from_numpy(vals).to(torch.float32).to(torch.float64).numpy()
+    assert np.array_equal(orc.round_to(vals, "f32"), ref32, equal_nan=True)
+
+
+# ---------------------------------------------------------------- elementwise
+def test_softplus_and_silu_match_library_forms():
+    v = np.concatenate([np.linspace(-60, 60, 20001), [-700.0, 700.0, 0.0]])
+    assert np.allclose(orc.softplus(v), np.logaddexp(0.0, v), rtol=1e-14, atol=0)
+    assert np.allclose(orc.silu(v), v * scipy.special.expit(v), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------- conv
+def test_conv_matches_np_convolve_with_reversed_taps():
+    rng = np.random.default_rng(7)
+    W, C, L = 4, 6, 25
+    w = rng.uniform(-0.5, 0.5, (C, W))
+    b = rng.uniform(-0.5, 0.5, C)
+    win0 = rng.standard_normal((W - 1, C))
+    u = rng.standard_normal((L, C))
+    v = orc.conv_tokens(win0, u, w, b)
+    stream = np.concatenate([win0, u])
+    for c in range(C):
+        ref = np.convolve(stream[:, c], w[c, ::-1], mode="valid") + b[c]
+        assert np.allclose(v[:, c], ref, rtol=1e-14, atol=1e-14)
+
+
+def test_decode_conv_window_is_exact_copy_and_matches_np_convolve():
+    rng = np.random.default_rng(8)
+    shape = synth.TINY
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 5)
+    pool = orc.PoolRef(shape, 1, 2, "f64", "f64")
+    pool.ssm[0, 1], pool.conv[0, 1] = ssm0, conv0
+    stream = np.concatenate([conv0.T, u])
+    for t in range(5):
+        orc.decode_step(pool, 0, params, [1], u[t:t + 1], z[t:t + 1], dt[t:t + 1], "f64")
+        assert np.array_equal(pool.conv[0, 1], stream[t + 1:t + 4].T)
+    # the decode conv value (through x of head 0 after one step) against np.convolve
+    pool2 = orc.PoolRef(shape, 1, 1, "f64", "f64")
+    pool2.conv[0, 0] = conv0
+    D0 = dict(params, D=np.ones(shape.nheads))
+    zbig = np.full((1, shape.intermediate), 50.0)          # SiLU(50) = 50 to 1e-20
+    out = orc.decode_step(pool2, 0, D0, [0], u[:1], zbig, np.full((1, shape.nheads), -80.0), "f64")
+    # with Delta ~ e^-84 the state term vanishes: out = (C.h0*alpha + x) * 50 with h0 = 0
+    c = 3
+    ref_v = np.convolve(stream[:4, c], params["conv_w"][c, ::-1], mode="valid")[0] + params["conv_b"][c]
+    assert math.isclose(out[0, c] / 50.0, ref_v * scipy.special.expit(ref_v), rel_tol=1e-12)
+
+
+# ---------------------------------------------------------------- recurrence
+def _post_conv(params, shape, conv0, u, dt):
+    act = orc.silu(orc.conv_tokens(conv0.T, u, params["conv_w"], params["conv_b"]))
+    I, G, N = shape.intermediate, shape.n_groups, shape.d_state
+    x = act[:, :I].reshape(len(u), shape.nheads, shape.head_dim)
+    B = act[:, I:I + G * N].reshape(len(u), G, N)
+    C = act[:, I + G * N:].reshape(len(u), G, N)
+    delta = np.logaddexp(0.0, dt + params["dt_bias"])
+    return x, B, C, delta
+
+
+@pytest.mark.parametrize("shape,L,seed", [
+    (synth.TINY, 24, 0),
+    (synth.Shape(4, 8, 8, 2, 4), 40, 1),
+    (synth.Shape(6, 4, 5, 3, 3), 17, 2),
+    (synth.Shape(2, 3, 7, 1, 2), 1, 3),
+])
+def test_prefill_equals_semiseparable_matrix_form(shape, L, seed):
+    rng = np.random.default_rng(seed)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, L)
+    pool = orc.PoolRef(shape, 1, 3, "f64", "f64")
+    pool.ssm[0, 2], pool.conv[0, 2] = ssm0, conv0
+    out = orc.prefill(pool, 0, params, [0, L], [2], [1], [0], u, z, dt, "f64")
+    x, B, C, delta = _post_conv(params, shape, conv0, u, dt)
+    hpg = shape.nheads // shape.n_groups
+    P = shape.head_dim
+    for h in range(shape.nheads):
+        g = h // hpg
+        Y = orc.ssd_matrix_form(ssm0[h], x[:, h], B[:, g], C[:, g], delta[:, h],
+                                params["A"][h], params["D"][h])
+        gate = z[:, h * P:(h + 1) * P] * scipy.special.expit(z[:, h * P:(h + 1) * P])
+        assert rel_err(out[:, h * P:(h + 1) * P], Y * gate) < 1e-12
+
+
+@pytest.mark.parametrize("L", [1, 16, 40])
+def test_ssm_scan_equals_matrix_form(L):
+    rng = np.random.default_rng(100 + L)
+    P, N = 3, 5
+    x, B, C = rng.standard_normal((L, P)), rng.standard_normal((L, N)), rng.standard_normal((L, N))
+    delta = np.logaddexp(0.0, rng.standard_normal(L) - 3.0)
+    A, D = -np.exp(rng.uniform(0, math.log(16))), rng.standard_normal()
+    h0 = rng.normal(0, 0.1, (P, N))
+    y, _ = orc.ssm_scan(h0, x, B, C, delta, A, D)
+    assert rel_err(y, orc.ssd_matrix_form(h0, x, B, C, delta, A, D)) < 1e-12
+
+
+def test_constant_input_closed_form():
+    """u_t = u with the initial window = u, and constant z, dt: a geometric series."""
+    shape = synth.Shape(4, 8, 6, 2, 4)
+    rng = np.random.default_rng(11)
+    params = synth.layer_params(rng, shape)
+    L = 40
+    u1 = rng.standard_normal(shape.conv_dim)
+    z1 = rng.standard_normal(shape.intermediate)
+    dt1 = rng.standard_normal(shape.nheads)
+    h0 = rng.normal(0, 0.1, (shape.nheads, shape.head_dim, shape.d_state))
+    pool = orc.PoolRef(shape, 1, 1, "f64", "f64")
+    pool.ssm[0, 0] = h0
+    pool.conv[0, 0] = np.repeat(u1[:, None], shape.conv_kernel - 1, axis=1)
+    u, z, dt = np.tile(u1, (L, 1)), np.tile(z1, (L, 1)), np.tile(dt1, (L, 1))
+    out = orc.prefill(pool, 0, params, [0, L], [0], [1], [0], u, z, dt, "f64")
+    # closed form
+    v = params["conv_b"] + u1 * params["conv_w"].sum(axis=1)
+    act = v * scipy.special.expit(v)
+    I, G, N, P, H = shape.intermediate, shape.n_groups, shape.d_state, shape.head_dim, shape.nheads
+    x = act[:I].reshape(H, P)
+    B = act[I:I + G * N].reshape(G, N)
+    C = act[I + G * N:].reshape(G, N)
+    delta = np.logaddexp(0.0, dt1 + params["dt_bias"])
+    alpha = np.exp(delta * params["A"])
+    g = np.arange(H) // (H // G)
+    inject = (delta[:, None] * x)[:, :, None] * B[g][:, None, :]
+    gate = z1 * scipy.special.expit(z1)
+    for t in (0, 1, 9, L - 1):
+        n = t + 1
+        h = alpha[:, None, None] ** n * h0 + ((1 - alpha ** n) / (1 - alpha))[:, None, None] * inject
+        y = np.einsum("hpn,hn->hp", h, C[g]) + params["D"][:, None] * x
+        assert rel_err(out[t], y.reshape(-1) * gate) < 1e-12
+    assert rel_err(pool.ssm[0, 0], h) < 1e-12
+
+
+def test_scalar_case_is_an_iir_filter():
+    """H = P = N = G = 1 with constant Delta: h is lfilter([1], [1, -alpha], Delta x B, zi = alpha h0)."""
+    shape = synth.Shape(1, 1, 1, 1, 4)
+    rng = np.random.default_rng(5)
+    params = synth.layer_params(rng, shape)
+    L = 64
+    u = rng.standard_normal((L, shape.conv_dim))
+    z = np.full((L, 1), 40.0)                    # gate ~ 40 exactly enough; compared after division
+    dt = np.full((L, 1), 0.3)
+    h0 = np.array([[[0.25]]])
+    pool = orc.PoolRef(shape, 1, 1, "f64", "f64")
+    pool.ssm[0, 0] = h0
+    conv0 = rng.standard_normal((shape.conv_dim, 3))
+    pool.conv[0, 0] = conv0
+    # make the readout the state itself: D = 0 and read C through the closed conv
+    p2 = dict(params, D=np.zeros(1))
+    out = orc.prefill(pool, 0, p2, [0, L], [0], [1], [0], u, z, dt, "f64")
+    x, B, C, delta = _post_conv(p2, shape, conv0, u, dt)
+    alpha = math.exp(delta[0, 0] * p2["A"][0])
+    drive = delta[:, 0] * x[:, 0, 0] * B[:, 0, 0]
+    h, _ = scipy.signal.lfilter([1.0], [1.0, -alpha], drive, zi=[alpha * h0[0, 0, 0]])
+    y_ref = h * C[:, 0, 0] * (z[:, 0] * scipy.special.expit(z[:, 0]))
+    assert rel_err(out[:, 0], y_ref) < 1e-12
+    assert math.isclose(pool.ssm[0, 0, 0, 0, 0], h[-1], rel_tol=1e-12)
+
+
+# ---------------------------------------------------------------- page snippet
+def test_affine_composition_and_restored_error_from_the_page(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "affine_snippet.json")))
+    steps = g["steps"]
+    # realise step (a_t, b_t) as alpha_t = exp(Delta_t A) with A = -1, and Delta_t x_t B_t = b_t
+    delta = np.array([-math.log(a) for a, _ in steps])
+    x = np.array([[b / d] for (_, b), d in zip(steps, delta)])
+    Bm, Cm = np.ones((3, 1)), np.ones((3, 1))
+    _, b_comp = orc.ssm_scan(np.zeros((1, 1)), x, Bm, Cm, delta, -1.0, 0.0)
+    _, a_comp = orc.ssm_scan(np.ones((1, 1)), np.zeros((3, 1)), Bm, Cm, delta, -1.0, 0.0)
+    assert math.isclose(a_comp[0, 0], g["composed_by_hand"]["a"], rel_tol=1e-12)
+    assert math.isclose(b_comp[0, 0], g["composed_by_hand"]["b"], rel_tol=1e-12)
+    r = g["restored_error"]
+    n = r["steps"]
+    for factor in r["factors"]:
+        d = np.ones(n)
+        xin = np.full((n, 1), r["input"])
+        _, h_exact = orc.ssm_scan(np.full((1, 1), r["exact_start"]), xin, np.ones((n, 1)),
+                                  np.ones((n, 1)), d, math.log(factor), 0.0)
+        _, h_rest = orc.ssm_scan(np.full((1, 1), r["restored_start"]), xin, np.ones((n, 1)),
+                                 np.ones((n, 1)), d, math.log(factor), 0.0)
+        assert np.isclose(h_rest[0, 0] - h_exact[0, 0], 0.01 * factor ** n)
+
+
+def test_linearity_in_initial_state():
+    shape = synth.Shape(4, 8, 8, 2, 4)
+    rng = np.random.default_rng(21)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 30)
+    dlt = rng.normal(0, 0.01, ssm0.shape)
+    outs, states = [], []
+    for h0 in (ssm0, ssm0 + dlt):
+        pool = orc.PoolRef(shape, 1, 1, "f64", "f64")
+        pool.ssm[0, 0], pool.conv[0, 0] = h0, conv0
+        outs.append(orc.prefill(pool, 0, params, [0, 30], [0], [1], [0], u, z, dt, "f64"))
+        states.append(pool.ssm[0, 0].copy())
+    delta = np.logaddexp(0.0, dt + params["dt_bias"])
+    decay = np.exp((delta * params["A"]).sum(axis=0))     # prod_t alpha_t per head
+    assert rel_err(states[1] - states[0], decay[:, None, None] * dlt) < 1e-9
+
+
+# ---------------------------------------------------------------- invariants
+def _fresh(shape, slots, dtype="f64"):
+    return orc.PoolRef(shape, 1, slots, dtype, dtype)
+
+
+def test_prefill_handoff_equals_one_call():
+    shape = synth.TINY
+    rng = np.random.default_rng(31)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 50)
+    one = _fresh(shape, 1)
+    one.ssm[0, 0], one.conv[0, 0] = ssm0, conv0
+    y1 = orc.prefill(one, 0, params, [0, 50], [0], [1], [0], u, z, dt, "f64")
+    two = _fresh(shape, 1)
+    two.ssm[0, 0], two.conv[0, 0] = ssm0, conv0
+    ya = orc.prefill(two, 0, params, [0, 16], [0], [1], [0], u[:16], z[:16], dt[:16], "f64")
+    yb = orc.prefill(two, 0, params, [0, 34], [0], [1], [16], u[16:], z[16:], dt[16:], "f64")
+    assert rel_err(np.concatenate([ya, yb]), y1) < 1e-12
+    assert rel_err(two.ssm[0, 0], one.ssm[0, 0]) < 1e-12
+    assert np.array_equal(two.conv[0, 0], one.conv[0, 0])
+
+
+@pytest.mark.parametrize("dtype,tol", [("f64", 1e-12), ("f32", 2e-6)])
+def test_decode_steps_equal_prefill(dtype, tol):
+    shape = synth.TINY
+    rng = np.random.default_rng(41)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 20)
+    dec = _fresh(shape, 1, dtype)
+    dec.ssm[0, 0], dec.conv[0, 0] = ssm0, conv0
+    ys = [orc.decode_step(dec, 0, params, [0], u[t:t + 1], z[t:t + 1], dt[t:t + 1], dtype)[0]
+          for t in range(20)]
+    pre = _fresh(shape, 1, dtype)
+    pre.ssm[0, 0], pre.conv[0, 0] = ssm0, conv0
+    yp = orc.prefill(pre, 0, params, [0, 20], [0], [1], [0], u, z, dt, dtype)
+    assert rel_err(np.array(ys), yp) < tol
+    assert rel_err(dec.ssm[0, 0], pre.ssm[0, 0]) < tol
+    assert np.array_equal(dec.conv[0, 0], pre.conv[0, 0])
+
+
+def test_checkpoints_equal_prefix_prefills():
+    shape = synth.TINY
+    rng = np.random.default_rng(51)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 30)
+    pool = _fresh(shape, 6, "f32")
+    pool.ssm[0, 0], pool.conv[0, 0] = ssm0, conv0
+    ck = np.array([[3, 5, 4]])
+    orc.prefill(pool, 0, params, [0, 30], [0], [1], [0], u, z, dt, "f32", ckpt_interval=8, ckpt_slots=ck)
+    for k, p in enumerate((8, 16, 24)):
+        ref = _fresh(shape, 1, "f32")
+        ref.ssm[0, 0], ref.conv[0, 0] = ssm0, conv0
+        orc.prefill(ref, 0, params, [0, p], [0], [1], [0], u[:p], z[:p], dt[:p], "f32")
+        assert np.array_equal(pool.ssm[0, ck[0, k]], ref.ssm[0, 0])
+        assert np.array_equal(pool.conv[0, ck[0, k]], ref.conv[0, 0])
+    # start_pos shifts the checkpoint grid to absolute positions
+    pool2 = _fresh(shape, 6, "f32")
+    pool2.ssm[0, 0], pool2.conv[0, 0] = ssm0, conv0
+    orc.prefill(pool2, 0, params, [0, 30], [0], [1], [4], u, z, dt, "f32", ckpt_interval=8,
+                ckpt_slots=np.array([[1, 2, 3, 4]]))
+    ref = _fresh(shape, 1, "f32")
+    ref.ssm[0, 0], ref.conv[0, 0] = ssm0, conv0
+    orc.prefill(ref, 0, params, [0, 4], [0], [1], [4], u[:4], z[:4], dt[:4], "f32")
+    assert np.array_equal(pool2.ssm[0, 1], ref.ssm[0, 0])      # absolute position 8
+
+
+def test_padding_rows_and_fresh_sequences_do_not_read_slots():
+    shape = synth.TINY
+    rng = np.random.default_rng(61)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 4)
+    pool = _fresh(shape, 4, "f32")
+    pool.ssm[:] = np.nan
+    pool.conv[:] = np.nan
+    pool.ssm[0, 2], pool.conv[0, 2] = ssm0, conv0
+    y = orc.decode_step(pool, 0, params, [-1, 2], u[:2], z[:2], dt[:2], "f32")
+    assert np.all(y[0] == 0) and np.all(np.isfinite(y[1]))
+    for s in (0, 1, 3):
+        assert np.all(np.isnan(pool.ssm[0, s])) and np.all(np.isnan(pool.conv[0, s]))
+    y2 = orc.prefill(pool, 0, params, [0, 4], [1], [0], [0], u, z, dt, "f32")
+    assert np.all(np.isfinite(y2)) and np.all(np.isfinite(pool.ssm[0, 1]))
+
+
+# ---------------------------------------------------------------- byte counts
+def test_state_bytes_match_the_pages(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "state_sizes.json")))
+    shape = synth.NEMOTRON_H
+    by = {e["id"]: e for e in g["entries"]}
+
+    def per_layer(ssm, conv):
+        p = orc.PoolRef(shape, 1, 1, ssm, conv or "bf16")
+        return p.ssm_bytes_per_slot_layer() + (p.conv_bytes_per_slot_layer() if conv else 0)
+
+    e = by["bf16_ssm_per_layer"]
+    assert per_layer("bf16", None) == 2 * 2 ** 20
+    assert e["layers"] * per_layer("bf16", None) == e["total_bytes"] == e["mib"] * 2 ** 20
+    e = by["fp32_ssm_bf16_conv_24_layers"]
+    total = e["layers"] * per_layer("f32", "bf16")
+    assert total == e["total_bytes"]
+    assert int(total // e["kv_bytes_per_token"]) == e["crossover_tokens"]
+    e = by["bf16_ssm_bf16_conv_24_layers"]
+    assert int(e["layers"] * per_layer("bf16", "bf16") // e["kv_bytes_per_token"]) == e["crossover_tokens"]
+    e = by["per_layer_block_mib"]
+    assert round(per_layer("f32", "bf16") / 2 ** 20, 2) == e["mib_2dp"]
+    e = by["pool_256_slots_gib"]
+    assert round(e["slots"] * e["layers"] * per_layer("f32", "bf16") / 2 ** 30, 1) == e["gib_1dp"]
+    e = by["conv_share_percent"]
+    p = orc.PoolRef(shape, 1, 1, "f32", "bf16")
+    assert round(100 * p.conv_bytes_per_slot_layer() / per_layer("f32", "bf16"), 1) == e["percent_1dp"]
+    e = by["long_context_per_layer"]
+    assert e["seqs"] * per_layer("f32", None) == e["total_bytes"]
+
+
+# ---------------------------------------------------------------- pin strength
+def test_pins_catch_planted_mistakes():
+    """Mistakes planted in a copy of the scan are caught by the matrix-form pin."""
+    rng = np.random.default_rng(71)
+    L, P, N = 12, 3, 4
+    x, B, C = rng.standard_normal((L, P)), rng.standard_normal((L, N)), rng.standard_normal((L, N))
+    delta = np.logaddexp(0.0, rng.standard_normal(L) - 2.0)
+    A, D = -2.0, 0.7
+    h0 = rng.normal(0, 0.1, (P, N))
+    ref = orc.ssd_matrix_form(h0, x, B, C, delta, A, D)
+
+    def scan(variant):
+        h = h0.copy()
+        y = np.zeros((L, P))
+        for t in range(L):
+            h_old = h
+            if variant == "no_delta_on_input":
+                h = np.exp(delta[t] * A) * h + np.outer(x[t], B[t])
+            elif variant == "sign_of_A":
+                h = np.exp(-delta[t] * A) * h + delta[t] * np.outer(x[t], B[t])
+            elif variant == "readout_old_state":
+                h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t], B[t])
+                y[t] = h_old @ C[t] + D * x[t]
+                continue
+            elif variant == "B_C_swapped":
+                h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t], C[t])
+                y[t] = h @ B[t] + D * x[t]
+                continue
+            elif variant == "no_D":
+                h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t], B[t])
+                y[t] = h @ C[t]
+                continue
+            elif variant == "input_index_shift":
+                h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t - 1], B[t])
+            y[t] = h @ C[t] + D * x[t]
+        return y
+
+    for v in ("no_delta_on_input", "sign_of_A", "readout_old_state", "B_C_swapped", "no_D",
+              "input_index_shift"):
+        assert rel_err(scan(v), ref) > 1e-3, v
+    assert rel_err(orc.ssm_scan(h0, x, B, C, delta, A, D)[0], ref) < 1e-12
