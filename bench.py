@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba2 slot-pool hot path on one MI355X.
+
+Step = one fused decode step of a Nemotron-H-shaped Mamba2 layer (H=128 heads
+of P=64, N=128, G=8 groups, conv width 4) for 256 live sequences at randomly
+permuted slots of a 512-slot bf16 pool: conv-window shift, conv + SiLU,
+softplus, state update, readout, gate, in place on the pool.  Inputs are
+synthetic (seeded, resident in HBM before timing).  A second leg times the
+chunked prefill of one 8192-token sequence (chunk 256) at the same shape.
+
+Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one
+decode launch divided by its average duration, timed with HIP events on the
+stream the kernel runs on.  `cpu_baseline` is the fp64 CPU oracle on a bounded
+sample of the same decode step, single-threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def decode_bytes_per_seq(sh, ssm_b=2, conv_b=2, io_b=2, y_b=2) -> int:
+    """Algorithmic HBM bytes of one decode token: state and window read+write, u, z, dt in, y out."""
+    state = 2 * sh.nheads * sh.head_dim * sh.d_state * ssm_b
+    window = 2 * sh.conv_dim * (sh.conv_kernel - 1) * conv_b
+    return state + window + (sh.conv_dim + sh.intermediate + sh.nheads) * io_b + sh.intermediate * y_b
+
+
+def prefill_dense_flops_per_token(sh, Q) -> int:
+    """MFMA flops of one prefill token, dense tiles: C.B^T per group, (M o L) X and the two state products per head."""
+    return 2 * Q * sh.d_state * sh.n_groups + 2 * Q * sh.head_dim * sh.nheads + 4 * sh.nheads * sh.head_dim * sh.d_state
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
+              "sequence and needs no collective); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from recurrent_state_update_amd import synth
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+
+    dev = "cuda"
+    w = synth.decode_workload(1)
+    sh, slots = w["shape"], w["slots"]
+    batch = len(slots)
+    pool = Pool.allocate(1, w["num_slots"], sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
+                         torch.bfloat16, torch.bfloat16, dev)
+    for i, s in enumerate(slots):
+        pool.ssm[0, int(s)] = synth.to_torch(w["ssm0"][i], "bf16").to(dev)
+        pool.conv[0, int(s)] = synth.to_torch(w["conv0"][i], "bf16").to(dev)
+    W = LayerWeights.from_numpy(w["params"], dev)
+    u = synth.to_torch(w["u"], "bf16").to(dev)
+    z = synth.to_torch(w["z"], "bf16").to(dev)
+    dt = synth.to_torch(w["dt"], "bf16").to(dev)
+    x, B, C = pool.split_xbc(u)
+    y = torch.empty((batch, sh.intermediate), dtype=torch.bfloat16, device=dev)
+    sl = torch.from_numpy(slots).to(dev)
+    pool.decode_step(0, W, sl, x, B, C, z, dt, y, slots_host=slots)   # validates once
+
+    def step():
+        pool.decode_step(0, W, sl, x, B, C, z, dt, y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    per_seq = decode_bytes_per_seq(sh)
+    launch_bytes = per_seq * batch
+    state_bytes = batch * 2 * (sh.nheads * sh.head_dim * sh.d_state * 2 + sh.conv_dim * (sh.conv_kernel - 1) * 2)
+    achieved = launch_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode tokens/s and state GB/s (% of HBM peak); prefill tokens/s (% MFMA)",
+        "value": batch / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Mamba2 decode step, Nemotron-H layer shape (H=128, P=64, N=128, G=8, W=4), "
+                        "256 live sequences at permuted slots of a 512-slot pool, one token each",
+            "batch": batch, "pool_slots": w["num_slots"], "state_dtype": "bf16", "io_dtype": "bf16",
+            "parallelism": "single GPU",
+        },
+        "state_gbps": state_bytes / (ms * 1e-3) / 1e9,
+        "wall_s_timed": wall,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "decode_kernel<bf16, N=128, W=4>", "bytes_per_launch": launch_bytes,
+            "bytes_per_sequence": per_seq,
+        },
+    }
+
+    if not args.no_prefill:
+        pw = synth.prefill_workload(2)
+        psh = pw["shape"]
+        ppool = Pool.allocate(1, 32, psh.nheads, psh.head_dim, psh.d_state, psh.n_groups, psh.conv_kernel,
+                              torch.bfloat16, torch.bfloat16, dev)
+        PW = LayerWeights.from_numpy(pw["params"], dev)
+        pu = synth.to_torch(pw["u"], "bf16").to(dev)
+        pz = synth.to_torch(pw["z"], "bf16").to(dev)
+        pdt = synth.to_torch(pw["dt"], "bf16").to(dev)
+        T = pu.shape[0]
+        py = torch.empty((T, psh.intermediate), dtype=torch.bfloat16, device=dev)
+        px, pB, pC = ppool.split_xbc(pu)
+        ws = torch.empty(ppool.workspace_size(1, T, pw["chunk"]), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            ppool.prefill(0, PW, pw["cu_seqlens"], [17], [0], px, pB, pC, pz, pdt, py,
+                          chunk_size=pw["chunk"], workspace=ws)
+
+        for _ in range(3):
+            pstep()
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            pstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / reps
+        flops = prefill_dense_flops_per_token(psh, pw["chunk"]) * T
+        io_bytes = T * (psh.conv_dim + psh.intermediate + psh.nheads + psh.intermediate) * 2 \
+            + psh.nheads * psh.head_dim * psh.d_state * 2 + psh.conv_dim * 3 * 2
+        out["prefill"] = {
+            "workload": "chunked prefill of one 8192-token sequence, chunk 256, same layer shape, bf16 state",
+            "ms": pms, "tokens_per_s": T / (pms * 1e-3),
+            "mfma_dense_tflops": flops / (pms * 1e-3) / 1e12,
+            "mfma_frac": flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_algorithmic_gbs": io_bytes / (pms * 1e-3) / 1e9,
+            "hbm_frac": io_bytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del ppool, ws
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 CPU oracle on the same decode step, single-threaded, for about budget_s seconds."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import mamba2 as orc
+    sh = w["shape"]
+    n = len(w["slots"])
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            ref = orc.PoolRef(sh, 1, 16, "bf16", "bf16")
+            lo = done % n
+            idx = np.arange(lo, min(lo + 16, n))
+            ref.ssm[0, :len(idx)], ref.conv[0, :len(idx)] = w["ssm0"][idx], w["conv0"][idx]
+            orc.decode_step(ref, 0, w["params"], np.arange(len(idx)), w["u"][idx], w["z"][idx], w["dt"][idx], "bf16")
+            done += len(idx)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode tokens (sequences of the same 256-sequence step, 16 at a time) "
+                      f"in {el:.1f} s on one host thread, numpy fp64"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

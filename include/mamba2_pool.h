@@ -1,0 +1,204 @@
+/*
+ * mamba2_pool.h -- C ABI of the Mamba2 selective-state update over a slot pool
+ * (MI355X / gfx950 HIP library libmamba2pool.so).
+ *
+ * Pages cited:
+ *   [SSM-hybrids] "Hybrid SSM / Mamba models and non-KV state"
+ *                 (mlinterviewnotes.com, inference course, chapter 7.3)
+ *   [notes]       Mamba study notes (echobase-5bl.pages.dev, log 2026.07.27.01)
+ *
+ * The method, per token t and head h of group g(h) = h / (H/G):
+ *   window <- last W-1 raw inputs per conv channel; v = conv_b + sum_k conv_w[k]*window_k
+ *   [x | B | C] = SiLU(v)            over d_conv = H*P + 2*G*N channels
+ *   Delta = softplus(dt + dt_bias);  h <- exp(Delta*A) h + Delta * x B^T
+ *   y = C h + D x;  out = y * SiLU(z)
+ * ([notes] "Mamba" equations; [SSM-hybrids] the selective_state_update and
+ * mamba_chunk_scan_combined call sites and the state-shape function.)
+ *
+ * Conventions for every entry point:
+ *  - All device pointers are caller-owned device memory; the library never
+ *    allocates device memory and never frees caller memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream).  Pointers must stay valid until the
+ *    stream has completed the work.  Host pointers are read before return.
+ *  - Strides are in elements of the tensor's own dtype, between consecutive
+ *    rows (tokens); the innermost dimension is contiguous.
+ *  - On any status other than M2_OK nothing has been enqueued and the pool
+ *    is untouched.  mamba2_last_error() gives a message (thread-local).
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Calls that update the same slot must not overlap in time (in-place update).
+ */
+#ifndef MAMBA2_POOL_H
+#define MAMBA2_POOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum m2_status {
+  M2_OK = 0,
+  M2_ERR_ARG = 1,         /* null pointer, negative count, bad enum */
+  M2_ERR_SHAPE = 2,       /* inconsistent sizes */
+  M2_ERR_DTYPE = 3,       /* unsupported dtype value */
+  M2_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned */
+  M2_ERR_SLOT = 5,        /* slot out of range, duplicated, or aliasing (host-visible slots) */
+  M2_ERR_UNSUPPORTED = 6, /* shape outside the compiled kernel set */
+  M2_ERR_HIP = 7,         /* a HIP runtime call failed */
+  M2_ERR_WORKSPACE = 8    /* workspace missing or too small */
+} m2_status;
+
+typedef enum m2_dtype { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
+
+/* Pool descriptor.  A pool is two dense caller-owned device tensors, one per
+ * state object, indexed [layer, slot, ...] ([SSM-hybrids], MambaPool passage):
+ *   ssm_base : [num_layers][num_slots][nheads][head_dim][d_state]   of ssm_dtype
+ *   conv_base: [num_layers][num_slots][d_conv][conv_kernel-1]        of conv_dtype
+ * with d_conv = nheads*head_dim + 2*n_groups*d_state; the conv window column
+ * conv_kernel-2 is the newest input.  ssm_bytes / conv_bytes must equal the
+ * dense sizes exactly.  Requirements: nheads % n_groups == 0, head_dim and
+ * d_state multiples of 8, 2 <= conv_kernel <= 4, bases 16-byte aligned. */
+typedef struct m2_pool_desc {
+  int32_t num_layers;
+  int32_t num_slots;
+  int32_t nheads;
+  int32_t head_dim;
+  int32_t d_state;
+  int32_t n_groups;
+  int32_t conv_kernel;
+  int32_t ssm_dtype;  /* m2_dtype */
+  int32_t conv_dtype; /* m2_dtype */
+  int32_t reserved;
+  void* ssm_base;
+  void* conv_base;
+  uint64_t ssm_bytes;
+  uint64_t conv_bytes;
+} m2_pool_desc;
+
+/* Opaque host-side handle; holds the descriptor, no device memory. */
+typedef struct m2_pool m2_pool;
+
+/* Per-layer parameters, fp32 device arrays:
+ *   A[nheads] (negative, used as given: alpha = exp(Delta*A)), D[nheads],
+ *   dt_bias[nheads], conv_w[d_conv][conv_kernel] (tap conv_kernel-1 multiplies
+ *   the current token), conv_b[d_conv].  conv_w must be 16-byte aligned. */
+typedef struct m2_layer_params {
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* conv_w;
+  const float* conv_b;
+} m2_layer_params;
+
+/* Validate `desc` and create a handle.  Host-only: makes no HIP call.
+ * Errors: M2_ERR_ARG, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIGN. */
+m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out);
+
+/* Free the handle (not the caller's tensors).  NULL is a no-op. */
+void mamba2_pool_destroy(m2_pool* pool);
+
+/* State bytes of one slot in one layer ([SSM-hybrids] state-shape function:
+ * temporal state (H, P, N), conv state (d_conv, W-1)):
+ *   *ssm_bytes  = nheads*head_dim*d_state*sizeof(ssm_dtype)
+ *   *conv_bytes = d_conv*(conv_kernel-1)*sizeof(conv_dtype)
+ * Host-only. */
+m2_status mamba2_pool_info(const m2_pool* pool, uint64_t* ssm_bytes_per_slot_layer,
+                           uint64_t* conv_bytes_per_slot_layer);
+
+/* One decode token per batch row, in place on the pool.  Decode has no time
+ * axis to parallelise, so each row is an elementwise state update on the slot
+ * named by its index ([SSM-hybrids], the selective_state_update call site);
+ * fused here with the conv window shift, SiLU, softplus and the gate of [notes]
+ * ("Mamba" equations).
+ *   slots      device int32[batch]; slot -1 marks a padding row: its slot is
+ *              neither read nor written and its output row is set to zero.
+ *              A device slot outside [0, num_slots) is treated as padding.
+ *   slots_host optional host copy of `slots`; when given, the call checks range
+ *              and duplicates and returns M2_ERR_SLOT before enqueueing anything.
+ *   x [batch][H*P], B [batch][G*N], C [batch][G*N]: raw (pre-conv) inputs of
+ *              io_dtype, row strides x_stride, B_stride, C_stride (a packed
+ *              [x|B|C] row of width d_conv works with B = x + H*P, C = B + G*N).
+ *   z [batch][H*P], dt [batch][H] of io_dtype.
+ *   y [batch][H*P] of y_dtype: out = (C h + D x) * SiLU(z), written for every row.
+ * x, B, C, z, y must be 16-byte aligned with 16-byte multiple row strides.
+ * Duplicated slots in one call race; pass slots_host to have them rejected. */
+m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params,
+                             int32_t batch, const int32_t* slots, const int32_t* slots_host,
+                             const void* x, int64_t x_stride, const void* B, int64_t B_stride,
+                             const void* C, int64_t C_stride, const void* z, int64_t z_stride,
+                             const void* dt, int64_t dt_stride, int32_t io_dtype,
+                             void* y, int64_t y_stride, int32_t y_dtype, void* stream);
+
+/* Bytes of device workspace mamba2_prefill_chunked needs for num_seqs packed
+ * sequences totalling total_tokens tokens, at chunk_size, with up to max_ckpt
+ * checkpoints per sequence.  Host-only. */
+m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
+                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
+
+/* Chunked (SSD) prefill of packed variable-length sequences.  Each chunk's
+ * own contribution is a causally masked matrix product, and a short scan over
+ * chunk states links the chunks ([SSM-hybrids], the mamba_chunk_scan_combined
+ * call site; [notes] "Mamba and Attention": Y = (M o L) X with L the causal
+ * mask).  The result equals the token-by-token recurrence up to rounding.
+ * Host arrays (read before return):
+ *   cu_seqlens int32[num_seqs+1], cu_seqlens[0] = 0, non-decreasing;
+ *              sequence s owns packed rows [cu_seqlens[s], cu_seqlens[s+1]).
+ *   slots      int32[num_seqs], distinct, in range: the final state and conv
+ *              window of sequence s are written to slots[s].
+ *   has_initial_state uint8[num_seqs]: nonzero seeds the recurrence and the conv
+ *              halo from slots[s] (a chunk boundary hands the state from one
+ *              launch to the next: [SSM-hybrids], chunked-prefill passage on
+ *              has_initial_states_p); zero means a zero state and window, and the slot is not read.
+ *   start_pos  int32[num_seqs] absolute position of the first row (tokens
+ *              already absorbed into the slot); may be NULL (all zero).
+ *   ckpt_slots int32[num_seqs][max_ckpt] or NULL.  With ckpt_interval > 0, entry k
+ *              of sequence s receives the state and conv window after absolute
+ *              position p, the k-th multiple of ckpt_interval with
+ *              start_pos < p <= start_pos + L_s ([SSM-hybrids] "align" mode:
+ *              states kept at block-aligned positions); -1 skips it.
+ *              Checkpoint slots must be distinct and disjoint from `slots`.
+ *              Requires ckpt_interval % chunk_size == 0 and start_pos % chunk_size == 0,
+ *              so checkpoints fall on chunk ends.
+ * Device tensors: x, B, C, z, dt, y as in mamba2_decode_step with rows = packed tokens.
+ * chunk_size: multiple of 16, at most 256.  Chunks start at each sequence's
+ * first row.  workspace: device memory of at least
+ * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch
+ * and not read across calls.  Sequences with zero length leave their slot untouched.
+ * With fp32 SSM state the contractions run in split-bf16 (three products)
+ * for fp32-level accuracy; with bf16 state they run in bf16 with fp32 accumulate. */
+m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_params* params,
+                                 int32_t num_seqs, const int32_t* cu_seqlens, const int32_t* slots,
+                                 const uint8_t* has_initial_state, const int32_t* start_pos,
+                                 const void* x, int64_t x_stride, const void* B, int64_t B_stride,
+                                 const void* C, int64_t C_stride, const void* z, int64_t z_stride,
+                                 const void* dt, int64_t dt_stride, int32_t io_dtype,
+                                 void* y, int64_t y_stride, int32_t y_dtype,
+                                 int32_t chunk_size, int32_t ckpt_interval, const int32_t* ckpt_slots,
+                                 int32_t max_ckpt, void* workspace, uint64_t workspace_bytes,
+                                 void* stream);
+
+/* Copy both state objects of slot src[i] into slot dst[i], bit-exact.  A
+ * cached state is copied to a fresh slot instead of being shared, since the
+ * recurrence overwrites its slot ([SSM-hybrids], SGLang checkpoint passage).
+ *   layer      one layer, or -1 for every layer of the pool.
+ *   src, dst   device int32[n]; pairs with an index outside [0, num_slots) are skipped.
+ *   src_host, dst_host optional host copies; when given, the call checks range,
+ *              src != dst, distinct dst and dst not used as a src, and returns
+ *              M2_ERR_SLOT otherwise. */
+m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, const int32_t* src,
+                                   const int32_t* dst, const int32_t* src_host,
+                                   const int32_t* dst_host, void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* mamba2_last_error(void);
+
+/* ABI version of this header (incremented on any signature change). */
+int32_t mamba2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_POOL_H */

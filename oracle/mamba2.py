@@ -16,7 +16,7 @@ Sources are four web pages on hybrid-model recurrent state:
 
 Per token t, per head h of group g = h // (H/G) (contiguous head->group map):
  1. conv: a rolling window of the last W-1 raw inputs per channel ([SSM-hybrids],
-    "There are two objects, not one": the short-convolution state of shape
+    the passage on the two state objects: the short-convolution state has shape
     (d_conv, W-1), d_conv = d_inner + 2*g*d_state), extended by the current
     input u_t, feeds a causal depthwise Conv1d with bias, then SiLU
     ([notes], "Mamba": x = SiLU(Conv1d(x'))).  All d_conv channels pass the
@@ -27,8 +27,8 @@ Per token t, per head h of group g = h // (H/G) (contiguous head->group map):
  4. y_t = h_t C_t + D x_t   (readout of the new state; [notes], classic SSM
     output y = C h + D x, and the Mamba readout y_t = C_t h_t)
  5. out_t = y_t * SiLU(z_t)                              ([notes], "Mamba")
-State lives in slots of a pool indexed [layer, slot, ...] ([SSM-hybrids],
-"MambaPool allocates one dense tensor per state object"); the temporal state
+State lives in slots of a pool indexed [layer, slot, ...], one dense tensor
+per state object ([SSM-hybrids], MambaPool passage); the temporal state
 has shape (H, P, N) ([SSM-hybrids], the state-shape function).
 
 Readings where the pages are silent (each also listed in the design notes):
@@ -76,12 +76,13 @@ def round_to(x, dtype: str) -> np.ndarray:
         return x32.astype(np.float64)
     if dtype != "bf16":
         raise ValueError(dtype)
-    bits = x32.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> np.uint64(16)) & np.uint64(1)
-    rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-    nan = np.isnan(x32)
-    quiet = ((bits | np.uint64(0x00400000)) >> np.uint64(16)) << np.uint64(16)
-    out = np.where(nan, quiet, rounded).astype(np.uint32)
+    bits = x32.view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    # uint32 arithmetic: only NaN bit patterns can wrap, and NaN takes the other branch
+    with np.errstate(over="ignore"):
+        rounded = (bits + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    quiet = (bits | np.uint32(0x00400000)) & np.uint32(0xFFFF0000)
+    out = np.where(np.isnan(x32), quiet, rounded).astype(np.uint32)
     return out.view(np.float32).astype(np.float64)
 
 
@@ -129,6 +130,11 @@ class PoolRef:
         return s.conv_dim * (s.conv_kernel - 1) * _BYTES[self.conv_dtype]
 
 
+def _f64(a) -> np.ndarray:
+    """Inputs arrive as exact values of their storage dtype; lift them to fp64."""
+    return np.asarray(a, dtype=np.float64)
+
+
 def _split(act, shape):
     """Post-conv activations (..., Cd) -> x (..., H, P), B (..., G, N), C (..., G, N)."""
     I, G, N = shape.intermediate, shape.n_groups, shape.d_state
@@ -152,21 +158,20 @@ def decode_step(pool: PoolRef, layer: int, params: dict, slots, u, z, dt, y_dtyp
     H, P, G = s.nheads, s.head_dim, s.n_groups
     hpg = H // G
     gidx = np.arange(H) // hpg
-    A, D, dt_bias = params["A"], params["D"], params["dt_bias"]
-    w, b = params["conv_w"], params["conv_b"]
+    A, D, dt_bias, w, b = (_f64(params[k]) for k in ("A", "D", "dt_bias", "conv_w", "conv_b"))
     out = np.zeros((len(slots), s.intermediate))
     for r, slot in enumerate(slots):
         if slot < 0:
             continue
-        window = np.concatenate([pool.conv[layer, slot], np.asarray(u[r])[:, None]], axis=1)
+        window = np.concatenate([pool.conv[layer, slot], _f64(u[r])[:, None]], axis=1)
         act = silu(b + np.sum(w * window, axis=1))                     # step 1
         x, Bm, Cm = _split(act, s)
-        delta = softplus(np.asarray(dt[r]) + dt_bias)                  # step 2
+        delta = softplus(_f64(dt[r]) + dt_bias)                        # step 2
         alpha = np.exp(delta * A)
         h = pool.ssm[layer, slot]
         h_new = alpha[:, None, None] * h + (delta[:, None] * x)[:, :, None] * Bm[gidx][:, None, :]   # 3
         y = np.einsum("hpn,hn->hp", h_new, Cm[gidx]) + D[:, None] * x  # step 4
-        out[r] = (y.reshape(-1)) * silu(np.asarray(z[r]))              # step 5
+        out[r] = (y.reshape(-1)) * silu(_f64(z[r]))                    # step 5
         pool.ssm[layer, slot] = round_to(h_new, pool.ssm_dtype)
         pool.conv[layer, slot] = round_to(window[:, 1:], pool.conv_dtype)
     return round_to(out, y_dtype)
@@ -181,7 +186,8 @@ def ssm_scan(h0, x, Bm, Cm, delta, A: float, D: float):
     h0 (P, N); x (L, P); Bm, Cm (L, N); delta (L,).
     """
     h = np.array(h0, dtype=np.float64, copy=True)
-    y = np.zeros_like(np.asarray(x, dtype=np.float64))
+    x, Bm, Cm, delta = _f64(x), _f64(Bm), _f64(Cm), _f64(delta)
+    y = np.zeros_like(x)
     for t in range(len(delta)):
         h = np.exp(delta[t] * A) * h + delta[t] * np.outer(x[t], Bm[t])
         y[t] = h @ Cm[t] + D * x[t]
@@ -197,7 +203,8 @@ def ssd_matrix_form(h0, x, Bm, Cm, delta, A: float, D: float):
     element from the products, with no cumulative sums.
     """
     L = len(delta)
-    abar = np.exp(np.asarray(delta, dtype=np.float64) * A)
+    x, Bm, Cm, delta, h0 = _f64(x), _f64(Bm), _f64(Cm), _f64(delta), _f64(h0)
+    abar = np.exp(delta * A)
     M = np.zeros((L, L))
     for i in range(L):
         for j in range(i + 1):
@@ -214,7 +221,8 @@ def conv_tokens(window0, u, conv_w, conv_b):
 
     Returns pre-activation v (L, C): v[t, c] = b[c] + sum_k w[c, k] * stream[t + k, c].
     """
-    stream = np.concatenate([window0, u], axis=0)
+    stream = np.concatenate([_f64(window0), _f64(u)], axis=0)
+    conv_w, conv_b = _f64(conv_w), _f64(conv_b)
     W = conv_w.shape[1]
     L = u.shape[0]
     v = np.broadcast_to(conv_b, (L, conv_b.shape[0])).copy()
@@ -244,7 +252,7 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
     chans = np.concatenate([xch, bch, cch])
     gpos = {g: i for i, g in enumerate(ug)}
     gsel = np.array([gpos[g] for g in groups])
-    A, D, dt_bias = params["A"][heads], params["D"][heads], params["dt_bias"][heads]
+    A, D, dt_bias = (_f64(params[k])[heads] for k in ("A", "D", "dt_bias"))
     T = int(cu_seqlens[-1])
     out = np.full((T, I), np.nan)
     for sq in range(len(slots)):
@@ -259,7 +267,7 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
         else:
             h = np.zeros((len(heads), P, N))
             win0 = np.zeros((W - 1, s.conv_dim))
-        useq = np.asarray(u[t0:t1])
+        useq = _f64(u[t0:t1])
         stream = np.concatenate([win0, useq], axis=0)             # raw inputs, window first
         act = silu(conv_tokens(win0[:, chans], useq[:, chans],
                                params["conv_w"][chans], params["conv_b"][chans]))
@@ -267,9 +275,9 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
         x = act[:, :nx].reshape(L, len(heads), P)
         Bm = act[:, nx:nx + len(bch)].reshape(L, len(ug), N)[:, gsel]
         Cm = act[:, nx + len(bch):].reshape(L, len(ug), N)[:, gsel]
-        delta = softplus(np.asarray(dt[t0:t1])[:, heads] + dt_bias)
+        delta = softplus(_f64(dt[t0:t1])[:, heads] + dt_bias)
         alpha = np.exp(delta * A)
-        zs = silu(np.asarray(z[t0:t1]).reshape(L, H, P)[:, heads])
+        zs = silu(_f64(z[t0:t1]).reshape(L, H, P)[:, heads])
         sp = int(start_pos[sq])
         for t in range(L):
             h = alpha[t][:, None, None] * h + (delta[t][:, None] * x[t])[:, :, None] * Bm[t][:, None, :]

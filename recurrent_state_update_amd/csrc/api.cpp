@@ -1,0 +1,500 @@
+// Host side of the C ABI in include/mamba2_pool.h: validation, pool handles,
+// prefill chunk tables, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "kernels.h"
+#include "mamba2_pool.h"
+
+struct m2_pool {
+  m2_pool_desc d;
+  m2::LayerShape sh;
+  uint64_t ssm_slot_bytes;   // one slot, one layer
+  uint64_t conv_slot_bytes;
+  // pinned host staging for the prefill tables, reused across calls
+  std::mutex mu;
+  void* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t staging_done = nullptr;
+  bool staging_pending = false;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+m2_status fail(m2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+m2_status ok() {
+  g_err.clear();
+  return M2_OK;
+}
+
+int esize(int32_t dt) { return dt == M2_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == M2_F32 || dt == M2_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a*b with overflow detection
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+  if (a != 0 && b > UINT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+struct IoCheck {
+  const char* name;
+  const void* p;
+  int64_t stride;
+  int64_t width;
+  int es;
+  bool need16;
+};
+
+m2_status check_io(const IoCheck* io, int n) {
+  for (int i = 0; i < n; ++i) {
+    const IoCheck& c = io[i];
+    if (!c.p) return fail(M2_ERR_ARG, "%s is NULL", c.name);
+    if (c.stride < c.width)
+      return fail(M2_ERR_SHAPE, "%s row stride %lld is smaller than the row width %lld", c.name,
+                  (long long)c.stride, (long long)c.width);
+    if (c.need16 && (!aligned16(c.p) || (c.stride * c.es) % 16 != 0))
+      return fail(M2_ERR_ALIGN, "%s must be 16-byte aligned with a 16-byte multiple row stride", c.name);
+  }
+  return M2_OK;
+}
+
+m2_status check_params(const m2_pool* pool, const m2_layer_params* w) {
+  if (!w) return fail(M2_ERR_ARG, "params is NULL");
+  if (!w->A || !w->D || !w->dt_bias || !w->conv_w || !w->conv_b)
+    return fail(M2_ERR_ARG, "a layer parameter pointer is NULL");
+  if (!aligned16(w->conv_w)) return fail(M2_ERR_ALIGN, "conv_w must be 16-byte aligned");
+  (void)pool;
+  return M2_OK;
+}
+
+m2::LayerShape make_shape(const m2_pool_desc& d) {
+  m2::LayerShape s;
+  s.H = d.nheads;
+  s.P = d.head_dim;
+  s.N = d.d_state;
+  s.G = d.n_groups;
+  s.W = d.conv_kernel;
+  s.I = d.nheads * d.head_dim;
+  s.Cd = s.I + 2 * d.n_groups * d.d_state;
+  return s;
+}
+
+m2_status hip_fail(hipError_t e, const char* what) {
+  return fail(M2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Prefill tables and workspace carving.
+struct PrefillLayout {
+  uint64_t nc_max, nw_max;
+  uint64_t off_seqs, off_chunks, off_windows, meta_bytes;
+  uint64_t off_act, off_delta, off_dA, off_states, total;
+};
+
+bool prefill_layout(const m2::LayerShape& sh, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
+  L->nc_max = (uint64_t)(T / Q) + (uint64_t)num_seqs;
+  L->nw_max = (uint64_t)num_seqs + L->nc_max;
+  L->off_seqs = 0;
+  L->off_chunks = align_up(L->off_seqs + num_seqs * sizeof(m2::SeqEntry), 256);
+  L->off_windows = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
+  L->meta_bytes = align_up(L->off_windows + L->nw_max * sizeof(m2::WindowEntry), 256);
+  uint64_t act, vec, st;
+  if (!mul_ok((uint64_t)T, (uint64_t)sh.Cd * 4, &act)) return false;
+  if (!mul_ok((uint64_t)T, (uint64_t)sh.H * 4, &vec)) return false;
+  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N * 4, &st)) return false;
+  L->off_act = L->meta_bytes;
+  L->off_delta = align_up(L->off_act + act, 256);
+  L->off_dA = align_up(L->off_delta + vec, 256);
+  L->off_states = align_up(L->off_dA + vec, 256);
+  L->total = align_up(L->off_states + st, 256);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mamba2_abi_version(void) { return 1; }
+
+const char* mamba2_last_error(void) { return g_err.c_str(); }
+
+m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out) {
+  if (!desc || !out) return fail(M2_ERR_ARG, "desc and out must not be NULL");
+  *out = nullptr;
+  const m2_pool_desc& d = *desc;
+  if (d.num_layers < 1 || d.num_slots < 1 || d.nheads < 1 || d.head_dim < 1 || d.d_state < 1 ||
+      d.n_groups < 1)
+    return fail(M2_ERR_ARG, "layer, slot, head, head_dim, d_state and group counts must be positive");
+  if (d.conv_kernel < 2 || d.conv_kernel > 4)
+    return fail(M2_ERR_UNSUPPORTED, "conv_kernel %d outside the supported range 2..4", d.conv_kernel);
+  if (d.nheads % d.n_groups != 0)
+    return fail(M2_ERR_SHAPE, "nheads %d is not a multiple of n_groups %d", d.nheads, d.n_groups);
+  if (d.head_dim % 8 != 0 || d.d_state % 8 != 0)
+    return fail(M2_ERR_SHAPE, "head_dim and d_state must be multiples of 8");
+  if (!dtype_ok(d.ssm_dtype) || !dtype_ok(d.conv_dtype)) return fail(M2_ERR_DTYPE, "ssm/conv dtype must be F32 or BF16");
+  if (!d.ssm_base || !d.conv_base) return fail(M2_ERR_ARG, "ssm_base and conv_base must not be NULL");
+  if (!aligned16(d.ssm_base) || !aligned16(d.conv_base))
+    return fail(M2_ERR_ALIGN, "pool bases must be 16-byte aligned");
+  const m2::LayerShape sh = make_shape(d);
+  uint64_t ssm_slot, conv_slot, tmp, ssm_total, conv_total;
+  if (!mul_ok((uint64_t)sh.H * sh.P, (uint64_t)sh.N * esize(d.ssm_dtype), &ssm_slot) ||
+      !mul_ok((uint64_t)sh.Cd, (uint64_t)(sh.W - 1) * esize(d.conv_dtype), &conv_slot) ||
+      !mul_ok((uint64_t)d.num_layers, (uint64_t)d.num_slots, &tmp) || !mul_ok(tmp, ssm_slot, &ssm_total) ||
+      !mul_ok(tmp, conv_slot, &conv_total))
+    return fail(M2_ERR_SHAPE, "pool size overflows 64 bits");
+  if (d.ssm_bytes != ssm_total)
+    return fail(M2_ERR_SHAPE, "ssm_bytes %llu != layers*slots*H*P*N*size = %llu", (unsigned long long)d.ssm_bytes,
+                (unsigned long long)ssm_total);
+  if (d.conv_bytes != conv_total)
+    return fail(M2_ERR_SHAPE, "conv_bytes %llu != layers*slots*d_conv*(W-1)*size = %llu",
+                (unsigned long long)d.conv_bytes, (unsigned long long)conv_total);
+  m2_pool* p = new (std::nothrow) m2_pool();
+  if (!p) return fail(M2_ERR_ARG, "out of host memory");
+  p->d = d;
+  p->sh = sh;
+  p->ssm_slot_bytes = ssm_slot;
+  p->conv_slot_bytes = conv_slot;
+  *out = p;
+  return ok();
+}
+
+void mamba2_pool_destroy(m2_pool* pool) {
+  if (!pool) return;
+  if (pool->staging_done) {
+    if (pool->staging_pending) (void)hipEventSynchronize(pool->staging_done);
+    (void)hipEventDestroy(pool->staging_done);
+  }
+  if (pool->staging) (void)hipHostFree(pool->staging);
+  delete pool;
+}
+
+m2_status mamba2_pool_info(const m2_pool* pool, uint64_t* ssm_bytes, uint64_t* conv_bytes) {
+  if (!pool || !ssm_bytes || !conv_bytes) return fail(M2_ERR_ARG, "NULL argument");
+  *ssm_bytes = pool->ssm_slot_bytes;
+  *conv_bytes = pool->conv_slot_bytes;
+  return ok();
+}
+
+m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t batch,
+                             const int32_t* slots, const int32_t* slots_host, const void* x, int64_t x_stride,
+                             const void* B, int64_t B_stride, const void* C, int64_t C_stride, const void* z,
+                             int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
+                             int64_t y_stride, int32_t y_dtype, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  const m2::LayerShape& sh = pool->sh;
+  if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
+  if (m2_status st = check_params(pool, params)) return st;
+  if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
+  if (batch == 0) return ok();
+  if (!slots) return fail(M2_ERR_ARG, "slots is NULL");
+  const int ies = esize(io_dtype);
+  const int GN = sh.G * sh.N;
+  const IoCheck io[] = {{"x", x, x_stride, sh.I, ies, true},        {"B", B, B_stride, GN, ies, true},
+                        {"C", C, C_stride, GN, ies, true},          {"z", z, z_stride, sh.I, ies, false},
+                        {"dt", dt, dt_stride, sh.H, ies, false},    {"y", y, y_stride, sh.I, esize(y_dtype), false}};
+  if (m2_status st = check_io(io, 6)) return st;
+  if (!m2::decode_supported(pool->d.ssm_dtype == M2_BF16, sh.N, sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "decode supports d_state in {16,32,64,128,256}, got %d", sh.N);
+  if (slots_host) {
+    std::vector<uint8_t> seen(pool->d.num_slots, 0);
+    for (int i = 0; i < batch; ++i) {
+      const int s = slots_host[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= pool->d.num_slots) return fail(M2_ERR_SLOT, "slot %d of row %d out of range", s, i);
+      if (seen[s]) return fail(M2_ERR_SLOT, "slot %d appears twice", s);
+      seen[s] = 1;
+    }
+  }
+  m2::DecodeParams p;
+  p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
+  p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
+  p.num_slots = pool->d.num_slots;
+  p.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
+  p.io_bf16 = io_dtype == M2_BF16;
+  p.y_bf16 = y_dtype == M2_BF16;
+  p.H = sh.H;
+  p.P = sh.P;
+  p.G = sh.G;
+  p.I = sh.I;
+  p.x_stride = x_stride;
+  p.B_stride = B_stride;
+  p.C_stride = C_stride;
+  p.z_stride = z_stride;
+  p.dt_stride = dt_stride;
+  p.y_stride = y_stride;
+  p.A = params->A;
+  p.D = params->D;
+  p.dt_bias = params->dt_bias;
+  p.conv_w = params->conv_w;
+  p.conv_b = params->conv_b;
+  const int kMaxRows = 65535;   // grid.y limit
+  for (int r0 = 0; r0 < batch; r0 += kMaxRows) {
+    const int nb = batch - r0 < kMaxRows ? batch - r0 : kMaxRows;
+    p.slots = slots + r0;
+    p.x = static_cast<const char*>(x) + (int64_t)r0 * x_stride * ies;
+    p.B = static_cast<const char*>(B) + (int64_t)r0 * B_stride * ies;
+    p.C = static_cast<const char*>(C) + (int64_t)r0 * C_stride * ies;
+    p.z = static_cast<const char*>(z) + (int64_t)r0 * z_stride * ies;
+    p.dt = static_cast<const char*>(dt) + (int64_t)r0 * dt_stride * ies;
+    p.y = static_cast<char*>(y) + (int64_t)r0 * y_stride * esize(y_dtype);
+    const hipError_t e = m2::launch_decode(p, sh.N, sh.W, nb, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  return ok();
+}
+
+m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
+                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes) {
+  if (!pool || !bytes) return fail(M2_ERR_ARG, "NULL argument");
+  if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
+  if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
+    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
+  PrefillLayout L;
+  if (!prefill_layout(pool->sh, num_seqs, total_tokens, chunk_size, &L))
+    return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
+  *bytes = L.total;
+  return ok();
+}
+
+m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t num_seqs,
+                                 const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_init,
+                                 const int32_t* start_pos, const void* x, int64_t x_stride, const void* B,
+                                 int64_t B_stride, const void* C, int64_t C_stride, const void* z, int64_t z_stride,
+                                 const void* dt, int64_t dt_stride, int32_t io_dtype, void* y, int64_t y_stride,
+                                 int32_t y_dtype, int32_t chunk_size, int32_t ckpt_interval,
+                                 const int32_t* ckpt_slots, int32_t max_ckpt, void* workspace,
+                                 uint64_t workspace_bytes, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  const m2::LayerShape& sh = pool->sh;
+  if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
+  if (m2_status st = check_params(pool, params)) return st;
+  if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
+  if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
+    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
+  if (ckpt_interval < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative checkpoint interval or count");
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens || !slots || !has_init) return fail(M2_ERR_ARG, "cu_seqlens, slots and has_initial_state are required");
+  if (cu_seqlens[0] != 0) return fail(M2_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < num_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return fail(M2_ERR_SHAPE, "cu_seqlens decreases at %d", s);
+  const int64_t T = cu_seqlens[num_seqs];
+  const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
+  if (ckpt_on) {
+    if (!ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
+    if (ckpt_interval % chunk_size != 0)
+      return fail(M2_ERR_ARG, "ckpt_interval %d is not a multiple of chunk_size %d", ckpt_interval, chunk_size);
+  }
+  const int S = pool->d.num_slots;
+  std::vector<uint8_t> used(S, 0);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int sl = slots[s];
+    if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "slot %d of sequence %d out of range", sl, s);
+    if (used[sl]) return fail(M2_ERR_SLOT, "slot %d appears twice", sl);
+    used[sl] = 1;
+    const int sp = start_pos ? start_pos[s] : 0;
+    if (sp < 0) return fail(M2_ERR_ARG, "start_pos of sequence %d is negative", s);
+    if (ckpt_on && sp % chunk_size != 0)
+      return fail(M2_ERR_ARG, "start_pos %d of sequence %d is not a multiple of chunk_size", sp, s);
+  }
+  if (ckpt_on) {
+    for (int64_t i = 0; i < (int64_t)num_seqs * max_ckpt; ++i) {
+      const int sl = ckpt_slots[i];
+      if (sl == -1) continue;
+      if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "checkpoint slot %d out of range", sl);
+      if (used[sl]) return fail(M2_ERR_SLOT, "checkpoint slot %d repeats or aliases a sequence slot", sl);
+      used[sl] = 1;
+    }
+  }
+  if (T == 0) return ok();
+  const int ies = esize(io_dtype);
+  const int GN = sh.G * sh.N;
+  const IoCheck io[] = {{"x", x, x_stride, sh.I, ies, false},       {"B", B, B_stride, GN, ies, false},
+                        {"C", C, C_stride, GN, ies, false},         {"z", z, z_stride, sh.I, ies, false},
+                        {"dt", dt, dt_stride, sh.H, ies, false},    {"y", y, y_stride, sh.I, esize(y_dtype), false}};
+  if (m2_status st = check_io(io, 6)) return st;
+  if (!m2::prefill_supported(sh.P, sh.N, sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,...,256}");
+  PrefillLayout L;
+  if (!prefill_layout(sh, num_seqs, T, chunk_size, &L)) return fail(M2_ERR_SHAPE, "workspace size overflows");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)L.total);
+
+  // ---- host tables
+  std::vector<m2::SeqEntry> seqs(num_seqs);
+  std::vector<m2::ChunkEntry> chunks;
+  std::vector<m2::WindowEntry> windows;
+  chunks.reserve(L.nc_max);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - cu_seqlens[s];
+    const int sp = start_pos ? start_pos[s] : 0;
+    m2::SeqEntry& e = seqs[s];
+    e.t0 = t0;
+    e.len = len;
+    e.slot = slots[s];
+    e.has_init = has_init[s] ? 1 : 0;
+    e.chunk0 = (int32_t)chunks.size();
+    e.nchunk = 0;
+    e.pad0 = e.pad1 = 0;
+    for (int c0 = 0; c0 < len; c0 += chunk_size) {
+      m2::ChunkEntry c;
+      c.seq = s;
+      c.t0 = t0 + c0;
+      c.len = len - c0 < chunk_size ? len - c0 : chunk_size;
+      c.tau0 = c0;
+      c.ckpt_slot = -1;
+      c.is_last = c0 + chunk_size >= len;
+      c.pad0 = c.pad1 = 0;
+      if (ckpt_on) {
+        const int64_t p = (int64_t)sp + c0 + c.len;
+        if (p % ckpt_interval == 0) {
+          const int64_t k = p / ckpt_interval - sp / ckpt_interval - 1;
+          if (k >= 0 && k < max_ckpt) c.ckpt_slot = ckpt_slots[(int64_t)s * max_ckpt + k];
+        }
+      }
+      if (c.ckpt_slot >= 0) windows.push_back({s, c0 + c.len, c.ckpt_slot, 0});
+      chunks.push_back(c);
+      ++e.nchunk;
+    }
+    if (len > 0) windows.push_back({s, len, slots[s], 0});
+  }
+  if (chunks.empty()) return ok();
+
+  // ---- upload the tables through pinned staging (one H2D copy)
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  {
+    std::lock_guard<std::mutex> lock(pool->mu);
+    hipError_t e;
+    if (pool->staging_pending) {
+      if ((e = hipEventSynchronize(pool->staging_done)) != hipSuccess) return hip_fail(e, "staging wait");
+      pool->staging_pending = false;
+    }
+    if (pool->staging_bytes < L.meta_bytes) {
+      if (pool->staging) (void)hipHostFree(pool->staging);
+      pool->staging = nullptr;
+      pool->staging_bytes = 0;
+      if ((e = hipHostMalloc(&pool->staging, L.meta_bytes, hipHostMallocDefault)) != hipSuccess)
+        return hip_fail(e, "pinned staging allocation");
+      pool->staging_bytes = L.meta_bytes;
+    }
+    if (!pool->staging_done) {
+      if ((e = hipEventCreateWithFlags(&pool->staging_done, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "staging event");
+    }
+    char* st = static_cast<char*>(pool->staging);
+    memset(st, 0, L.meta_bytes);
+    memcpy(st + L.off_seqs, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
+    memcpy(st + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
+    memcpy(st + L.off_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
+    if ((e = hipMemcpyAsync(ws, st, L.meta_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
+      return hip_fail(e, "table upload");
+    if ((e = hipEventRecord(pool->staging_done, hs)) != hipSuccess) return hip_fail(e, "staging event record");
+    pool->staging_pending = true;
+  }
+
+  m2::PrefillParams p;
+  p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
+  p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
+  p.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
+  p.io_bf16 = io_dtype == M2_BF16;
+  p.y_bf16 = y_dtype == M2_BF16;
+  p.sh = sh;
+  p.Q = chunk_size;
+  p.num_seqs = num_seqs;
+  p.num_chunks = (int)chunks.size();
+  p.num_windows = (int)windows.size();
+  p.total_tokens = (int)T;
+  p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws + L.off_seqs);
+  p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + L.off_chunks);
+  p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + L.off_windows);
+  p.x = x;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.dt = dt;
+  p.x_stride = x_stride;
+  p.B_stride = B_stride;
+  p.C_stride = C_stride;
+  p.z_stride = z_stride;
+  p.dt_stride = dt_stride;
+  p.y = y;
+  p.y_stride = y_stride;
+  p.A = params->A;
+  p.D = params->D;
+  p.dt_bias = params->dt_bias;
+  p.conv_w = params->conv_w;
+  p.conv_b = params->conv_b;
+  p.act = reinterpret_cast<float*>(ws + L.off_act);
+  p.delta = reinterpret_cast<float*>(ws + L.off_delta);
+  p.dA = reinterpret_cast<float*>(ws + L.off_dA);
+  p.states = reinterpret_cast<float*>(ws + L.off_states);
+  const hipError_t e = m2::launch_prefill(p, hs);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, const int32_t* src, const int32_t* dst,
+                                   const int32_t* src_host, const int32_t* dst_host, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (layer < -1 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (n < 0) return fail(M2_ERR_ARG, "n is negative");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(M2_ERR_ARG, "src and dst must not be NULL");
+  if (n > 65535) return fail(M2_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  if (src_host && dst_host) {
+    const int S = pool->d.num_slots;
+    std::vector<uint8_t> is_dst(S, 0), is_src(S, 0);
+    for (int i = 0; i < n; ++i) {
+      const int s = src_host[i], d = dst_host[i];
+      if (s < 0 || s >= S || d < 0 || d >= S) return fail(M2_ERR_SLOT, "pair %d (%d -> %d) out of range", i, s, d);
+      if (s == d) return fail(M2_ERR_SLOT, "pair %d copies slot %d onto itself", i, s);
+      if (is_dst[d]) return fail(M2_ERR_SLOT, "destination slot %d appears twice", d);
+      is_dst[d] = 1;
+      is_src[s] = 1;
+    }
+    for (int i = 0; i < n; ++i)
+      if (is_src[dst_host[i]]) return fail(M2_ERR_SLOT, "destination slot %d is also a source", dst_host[i]);
+  }
+  const int l0 = layer < 0 ? 0 : layer;
+  const int nl = layer < 0 ? pool->d.num_layers : 1;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int S = pool->d.num_slots;
+  hipError_t e = m2::launch_slot_copy(pool->d.ssm_base, pool->ssm_slot_bytes, (uint64_t)S * pool->ssm_slot_bytes, l0,
+                                      nl, S, n, src, dst, hs);
+  if (e == hipSuccess)
+    e = m2::launch_slot_copy(pool->d.conv_base, pool->conv_slot_bytes, (uint64_t)S * pool->conv_slot_bytes, l0, nl,
+                             S, n, src, dst, hs);
+  if (e != hipSuccess) return hip_fail(e, "checkpoint copy launch");
+  return ok();
+}
+
+}  // extern "C"

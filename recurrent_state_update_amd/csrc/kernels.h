@@ -1,0 +1,88 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+struct LayerShape {
+  int H, P, N, G, W;  // heads, head_dim, d_state, n_groups, conv kernel
+  int I, Cd;          // H*P, H*P + 2*G*N
+};
+
+// Fused decode step.  ssm/conv point at the layer's first slot.
+struct DecodeParams {
+  void* ssm;
+  void* conv;
+  int num_slots;
+  int ssm_bf16, conv_bf16, io_bf16, y_bf16;
+  int H, P, G, I;
+  const int32_t* slots;
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* z;
+  const void* dt;
+  int64_t x_stride, B_stride, C_stride, z_stride, dt_stride;
+  void* y;
+  int64_t y_stride;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* conv_w;
+  const float* conv_b;
+};
+hipError_t launch_decode(const DecodeParams& p, int N, int W, int batch, hipStream_t s);
+bool decode_supported(int ssm_bf16, int N, int W);
+
+// Slot-to-slot copy of one state object: bytes_per_slot bytes at
+// base + layer*layer_stride + slot*bytes_per_slot, for layers [l0, l0+nl).
+hipError_t launch_slot_copy(void* base, uint64_t bytes_per_slot, uint64_t layer_stride, int l0, int nl,
+                            int num_slots, int n, const int32_t* src, const int32_t* dst, hipStream_t s);
+
+// Chunked prefill.  Host-built tables live at the start of the workspace.
+struct SeqEntry {     // one per sequence
+  int32_t t0, len, slot, has_init;  // packed start row, rows, final slot, seed from slot
+  int32_t chunk0, nchunk, pad0, pad1;
+};
+struct ChunkEntry {   // one per chunk
+  int32_t seq, t0, len, tau0;       // packed start row, rows in chunk, offset inside the sequence
+  int32_t ckpt_slot, is_last, pad0, pad1;
+};
+struct WindowEntry {  // one conv-window write: window after `tau` rows of sequence `seq` -> slot
+  int32_t seq, tau, slot, pad;
+};
+
+struct PrefillParams {
+  void* ssm;
+  void* conv;
+  int ssm_bf16, conv_bf16, io_bf16, y_bf16;
+  LayerShape sh;
+  int Q;               // chunk size
+  int num_seqs, num_chunks, num_windows, total_tokens;
+  const SeqEntry* seqs;
+  const ChunkEntry* chunks;
+  const WindowEntry* windows;
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* z;
+  const void* dt;
+  int64_t x_stride, B_stride, C_stride, z_stride, dt_stride;
+  void* y;
+  int64_t y_stride;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* conv_w;
+  const float* conv_b;
+  // workspace arrays
+  float* act;      // [T][Cd] post-conv activations
+  float* delta;    // [H][T]
+  float* dA;       // [H][T] chunk-local inclusive cumsum of Delta*A
+  float* states;   // [num_chunks][H][P][N]: chunk states, then the state entering each chunk
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+bool prefill_supported(int P, int N, int W);
+
+}  // namespace m2

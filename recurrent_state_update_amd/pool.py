@@ -1,0 +1,179 @@
+"""Torch-facing binding of libmamba2pool.so: argument marshalling only.
+
+Tensors supply device pointers, dtypes and row strides; the stream is
+torch's current stream.  Every computation runs in the HIP kernels of the
+library, and a missing library raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_uint64, c_void_p
+
+import numpy as np
+import torch
+
+from ._ffi import M2_BF16, M2_F32, LayerParams, Mamba2Error, PoolDesc, check, lib
+
+_DT = {torch.float32: M2_F32, torch.bfloat16: M2_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with a contiguous last dimension")
+    return c_void_p(t.data_ptr()), t.stride(0)
+
+
+def _stream():
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _host_i32(a):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(c_void_p)
+
+
+class LayerWeights:
+    """fp32 device parameters of one layer: A, D, dt_bias [H], conv_w [Cd, W], conv_b [Cd]."""
+
+    def __init__(self, A, D, dt_bias, conv_w, conv_b):
+        self.tensors = [t.contiguous() for t in (A, D, dt_bias, conv_w, conv_b)]
+        for t in self.tensors:
+            if t.dtype != torch.float32:
+                raise TypeError("layer parameters must be float32")
+        self.A, self.D, self.dt_bias, self.conv_w, self.conv_b = self.tensors
+        self.struct = LayerParams(*(t.data_ptr() for t in self.tensors))
+
+    @classmethod
+    def from_numpy(cls, p: dict, device="cuda"):
+        f = lambda k: torch.as_tensor(np.asarray(p[k], np.float32), device=device)
+        return cls(f("A"), f("D"), f("dt_bias"), f("conv_w"), f("conv_b"))
+
+
+class Pool:
+    """Slot pool over caller-owned tensors ssm [L, S, H, P, N] and conv [L, S, Cd, W-1]."""
+
+    def __init__(self, ssm: torch.Tensor, conv: torch.Tensor, nheads: int, head_dim: int, d_state: int,
+                 n_groups: int, conv_kernel: int):
+        if not (ssm.is_contiguous() and conv.is_contiguous()):
+            raise ValueError("pool tensors must be contiguous")
+        self.ssm, self.conv = ssm, conv
+        self.nheads, self.head_dim, self.d_state = nheads, head_dim, d_state
+        self.n_groups, self.conv_kernel = n_groups, conv_kernel
+        self.intermediate = nheads * head_dim
+        self.conv_dim = self.intermediate + 2 * n_groups * d_state
+        self.num_layers, self.num_slots = ssm.shape[0], ssm.shape[1]
+        desc = PoolDesc(self.num_layers, self.num_slots, nheads, head_dim, d_state, n_groups, conv_kernel,
+                        _dtype_code(ssm), _dtype_code(conv), 0, ssm.data_ptr(), conv.data_ptr(),
+                        ssm.numel() * ssm.element_size(), conv.numel() * conv.element_size())
+        h = c_void_p()
+        check(lib().mamba2_pool_create(byref(desc), byref(h)))
+        self._h = h
+
+    @classmethod
+    def allocate(cls, num_layers, num_slots, nheads, head_dim, d_state, n_groups, conv_kernel,
+                 ssm_dtype=torch.bfloat16, conv_dtype=torch.bfloat16, device="cuda"):
+        cd = nheads * head_dim + 2 * n_groups * d_state
+        ssm = torch.zeros((num_layers, num_slots, nheads, head_dim, d_state), dtype=ssm_dtype, device=device)
+        conv = torch.zeros((num_layers, num_slots, cd, conv_kernel - 1), dtype=conv_dtype, device=device)
+        return cls(ssm, conv, nheads, head_dim, d_state, n_groups, conv_kernel)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().mamba2_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def info(self):
+        s, c = c_uint64(), c_uint64()
+        check(lib().mamba2_pool_info(self._h, byref(s), byref(c)))
+        return s.value, c.value
+
+    def split_xbc(self, u: torch.Tensor):
+        """Views x, B, C of packed pre-conv rows u [rows, Cd]."""
+        I, GN = self.intermediate, self.n_groups * self.d_state
+        return u[:, :I], u[:, I:I + GN], u[:, I + GN:]
+
+    # ------------------------------------------------------------------ decode
+    def decode_step(self, layer: int, w: LayerWeights, slots: torch.Tensor, x, B, C, z, dt, y,
+                    slots_host=None):
+        """One token per row of slots (device int32); writes y in place and updates the pool."""
+        if slots.dtype != torch.int32:
+            raise TypeError("slots must be int32")
+        _, sh_ptr = _host_i32(slots_host)
+        io = _dtype_code(x)
+        for t in (B, C, z, dt):
+            if _dtype_code(t) != io:
+                raise TypeError("x, B, C, z and dt must share one dtype")
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba2_decode_step(self._h, layer, byref(w.struct), slots.numel(), c_void_p(slots.data_ptr()),
+                                       sh_ptr, xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, io, yp, ys,
+                                       _dtype_code(y), _stream()))
+        return y
+
+    # ------------------------------------------------------------------ prefill
+    def workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int, max_ckpt: int = 0) -> int:
+        n = c_uint64()
+        check(lib().mamba2_prefill_workspace_size(self._h, num_seqs, total_tokens, chunk_size, max_ckpt, byref(n)))
+        return n.value
+
+    def prefill(self, layer: int, w: LayerWeights, cu_seqlens, slots, has_init, x, B, C, z, dt, y,
+                start_pos=None, chunk_size: int = 256, ckpt_interval: int = 0, ckpt_slots=None,
+                workspace: torch.Tensor | None = None):
+        """Chunked prefill of packed sequences; cu_seqlens/slots/has_init/start_pos/ckpt_slots are host arrays."""
+        cu, cu_p = _host_i32(cu_seqlens)
+        sl, sl_p = _host_i32(slots)
+        hi = np.ascontiguousarray(np.asarray(has_init, dtype=np.uint8))
+        sp, sp_p = _host_i32(start_pos)
+        ns = len(sl)
+        max_ck = 0
+        ck_p = None
+        if ckpt_slots is not None:
+            ck = np.ascontiguousarray(np.asarray(ckpt_slots, dtype=np.int32).reshape(ns, -1))
+            max_ck = ck.shape[1]
+            ck_p = ck.ctypes.data_as(c_void_p)
+        total = int(cu[-1]) if len(cu) else 0
+        need = self.workspace_size(ns, total, chunk_size, max_ck)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.ssm.device)
+        io = _dtype_code(x)
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba2_prefill_chunked(
+            self._h, layer, byref(w.struct), ns, cu.ctypes.data_as(c_void_p), sl_p,
+            hi.ctypes.data_as(c_void_p), sp_p, xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, io, yp, ys,
+            _dtype_code(y), chunk_size, ckpt_interval, ck_p, max_ck, c_void_p(workspace.data_ptr()),
+            workspace.numel(), _stream()))
+        return y
+
+    # ------------------------------------------------------------------ checkpoints
+    def checkpoint(self, layer: int, src: torch.Tensor, dst: torch.Tensor, src_host=None, dst_host=None):
+        """Copy both state objects slot src[i] -> dst[i] (device int32); layer -1 = all layers."""
+        _, s_p = _host_i32(src_host)
+        _, d_p = _host_i32(dst_host)
+        check(lib().mamba2_checkpoint_states(self._h, layer, src.numel(), c_void_p(src.data_ptr()),
+                                             c_void_p(dst.data_ptr()), s_p, d_p, _stream()))
+
+
+__all__ = ["Pool", "LayerWeights", "Mamba2Error"]

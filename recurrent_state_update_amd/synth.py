@@ -2,11 +2,13 @@
 
 This module only draws random numbers and lays them out.  It holds none of
 the method's arithmetic, so both sides of a parity check (the CPU oracle and
-the HIP path) may take their inputs from it.  Values are drawn in float64 with
-``numpy.random.default_rng`` and then cast to their storage dtype with torch's
-CPU casts (float64 -> float32 -> bfloat16, round-to-nearest-even at each
-step).  Every returned float array is float64 holding values that are exactly
-representable in the dtype named beside it.
+the HIP path) may take their inputs from it.  Normal values are drawn as
+float32 with ``numpy.random.default_rng(...).standard_normal(dtype=float32)``,
+uniform values as float64; both are then cast to their storage dtype with
+torch's CPU casts (-> float32 -> bfloat16, round-to-nearest-even at each step).
+Large arrays (states, tokens) are float32 holding values exactly representable
+in the dtype named beside them (bf16 values are exact in float32); layer
+parameters are float64 arrays of fp32-exact values.
 
 Shapes follow the Nemotron-H Mamba2 layer the first page prints in its model
 config (128 heads of 64 channels, state size 128, 8 groups, conv width 4,
@@ -56,29 +58,40 @@ NEMOTRON_H = Shape(nheads=128, head_dim=64, d_state=128, n_groups=8, conv_kernel
 
 
 def cast_exact(a, dtype: str) -> np.ndarray:
-    """Round float64 values to ``dtype`` (torch CPU casts) and return them as float64."""
-    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.float32)
+    """Round values to ``dtype`` (torch CPU casts) and return them as a float32 array."""
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        a = a.astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32)
     if dtype == "bf16":
-        t = t.to(torch.bfloat16)
+        t = t.to(torch.bfloat16).to(torch.float32)
     elif dtype != "f32":
         raise ValueError(dtype)
-    return t.to(torch.float64).numpy()
+    return t.numpy()
+
+
+def normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws."""
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
 
 
 def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
-    """Exact float64 values -> CPU tensor of the storage dtype."""
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.float32).to(_TORCH[dtype])
+    """Values exact in ``dtype`` -> CPU tensor of the storage dtype."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(_TORCH[dtype])
 
 
 def layer_params(rng: np.random.Generator, shape: Shape) -> dict:
-    """Per-layer parameters, fp32-exact, drawn in a fixed order."""
+    """Per-layer parameters drawn in a fixed order; float64 arrays of fp32-exact values."""
     H, Cd, W = shape.nheads, shape.conv_dim, shape.conv_kernel
     dt_bias = rng.uniform(-4.0, -2.0, H)
     A = -np.exp(rng.uniform(0.0, math.log(16.0), H))
-    D = rng.standard_normal(H)
+    D = rng.standard_normal(H)   # float64: parameters are small
     conv_w = rng.uniform(-0.5, 0.5, (Cd, W))
     conv_b = rng.uniform(-0.5, 0.5, Cd)
-    return {k: cast_exact(v, "f32") for k, v in
+    return {k: cast_exact(v, "f32").astype(np.float64) for k, v in
             dict(A=A, D=D, dt_bias=dt_bias, conv_w=conv_w, conv_b=conv_b).items()}
 
 
@@ -94,15 +107,15 @@ def pool_bytes(shape: Shape, num_layers: int, num_slots: int, ssm_dtype: str, co
 
 def _live_state(rng, shape: Shape, n: int, ssm_dtype: str, conv_dtype: str):
     H, P, N, Cd, W = shape.nheads, shape.head_dim, shape.d_state, shape.conv_dim, shape.conv_kernel
-    ssm = cast_exact(rng.normal(0.0, 0.1, (n, H, P, N)), ssm_dtype)
-    conv = cast_exact(rng.normal(0.0, 0.1, (n, Cd, W - 1)), conv_dtype)
+    ssm = cast_exact(normal(rng, (n, H, P, N), 0.1), ssm_dtype)
+    conv = cast_exact(normal(rng, (n, Cd, W - 1), 0.1), conv_dtype)
     return ssm, conv
 
 
 def _tokens(rng, shape: Shape, T: int, io_dtype: str):
-    u = cast_exact(rng.standard_normal((T, shape.conv_dim)), io_dtype)
-    z = cast_exact(rng.standard_normal((T, shape.intermediate)), io_dtype)
-    dt = cast_exact(rng.standard_normal((T, shape.nheads)), io_dtype)
+    u = cast_exact(normal(rng, (T, shape.conv_dim)), io_dtype)
+    z = cast_exact(normal(rng, (T, shape.intermediate)), io_dtype)
+    dt = cast_exact(normal(rng, (T, shape.nheads)), io_dtype)
     return u, z, dt
 
 
@@ -118,9 +131,9 @@ def tiny_workload(seed: int = 0) -> dict:
     slots = np.array([5, 0, 3, 7], dtype=np.int32)
     ssm0, conv0 = _live_state(rng, shape, len(slots), "f32", "f32")
     steps, batch = 64, len(slots)
-    u = cast_exact(rng.standard_normal((steps, batch, shape.conv_dim)), "f32")
-    z = cast_exact(rng.standard_normal((steps, batch, shape.intermediate)), "f32")
-    dt = cast_exact(rng.standard_normal((steps, batch, shape.nheads)), "f32")
+    u = cast_exact(normal(rng, (steps, batch, shape.conv_dim)), "f32")
+    z = cast_exact(normal(rng, (steps, batch, shape.intermediate)), "f32")
+    dt = cast_exact(normal(rng, (steps, batch, shape.nheads)), "f32")
     ssm_bytes, conv_bytes = pool_bytes(shape, 1, 8, "f32", "f32")
     return dict(
         name="tiny fp32 layer (H=8, P=16, N=16, G=1, W=4), 4 of 8 slots, 64 steps",
@@ -228,7 +241,8 @@ def random_problem(rng: np.random.Generator, shape: Shape, T: int, io_dtype: str
                    state_std: float = 0.1):
     """Small random problem used by property tests: params, one initial state and T tokens."""
     params = layer_params(rng, shape)
-    ssm0 = rng.normal(0.0, state_std, (shape.nheads, shape.head_dim, shape.d_state))
-    conv0 = rng.normal(0.0, state_std, (shape.conv_dim, shape.conv_kernel - 1))
+    ssm0 = normal(rng, (shape.nheads, shape.head_dim, shape.d_state), state_std)
+    conv0 = normal(rng, (shape.conv_dim, shape.conv_kernel - 1), state_std)
     u, z, dt = _tokens(rng, shape, T, io_dtype)
-    return params, cast_exact(ssm0, "f32"), cast_exact(conv0, "f32"), u, z, dt
+    f64 = lambda a: np.asarray(a, np.float64)
+    return params, f64(cast_exact(ssm0, "f32")), f64(cast_exact(conv0, "f32")), f64(u), f64(z), f64(dt)

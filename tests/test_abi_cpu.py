@@ -1,0 +1,255 @@
+"""C-ABI checks that run without a GPU.
+
+The library is loaded, every function include/mamba2_pool.h declares must be
+exported, the host-only calls (pool_create, pool_info, workspace sizing) are
+exercised, and every validation error path is driven with fake device
+pointers: validation runs before any HIP call, so none of these calls touches
+a device.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+from ctypes import byref, c_uint64, c_void_p
+
+import numpy as np
+import pytest
+
+from recurrent_state_update_amd import _ffi
+from recurrent_state_update_amd._ffi import LayerParams, PoolDesc, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba2_pool.h")
+
+ARG, SHAPE, DTYPE, ALIGN, SLOT, UNSUP, HIP, WS = 1, 2, 3, 4, 5, 6, 7, 8
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba2_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 9
+    l = lib()
+    for n in names:
+        assert hasattr(l, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _ffi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mamba2_\w+)", out))
+    assert set(names) <= exported
+    assert set(_ffi.exported_symbols()) == set(names)
+    assert l.mamba2_abi_version() == 1
+
+
+def make_desc(H=128, P=64, N=128, G=8, W=4, L=1, S=4, ssm=1, conv=1, ssm_base=FAKE, conv_base=FAKE):
+    es = {0: 4, 1: 2, 2: 2, -1: 2}
+    cd = H * P + 2 * G * N
+    return PoolDesc(L, S, H, P, N, G, W, ssm, conv, 0, ssm_base, conv_base,
+                    L * S * H * P * N * es[ssm], L * S * cd * (W - 1) * es[conv])
+
+
+def create(desc):
+    h = c_void_p()
+    st = lib().mamba2_pool_create(byref(desc), byref(h))
+    return st, h
+
+
+@pytest.fixture
+def pool():
+    st, h = create(make_desc())
+    assert st == 0, lib().mamba2_last_error()
+    yield h
+    lib().mamba2_pool_destroy(h)
+
+
+def test_pool_info_matches_page_byte_counts():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "state_sizes.json")))
+    by = {e["id"]: e for e in g["entries"]}
+    info = {}
+    for ssm, conv in ((0, 1), (1, 1)):
+        st, h = create(make_desc(ssm=ssm, conv=conv))
+        assert st == 0
+        a, b = c_uint64(), c_uint64()
+        assert lib().mamba2_pool_info(h, byref(a), byref(b)) == 0
+        info[(ssm, conv)] = (a.value, b.value)
+        lib().mamba2_pool_destroy(h)
+    s32, c16 = info[(0, 1)]
+    s16, _ = info[(1, 1)]
+    assert s16 == 128 * 64 * 128 * 2 == 2 * 2 ** 20
+    assert 48 * s16 == by["bf16_ssm_per_layer"]["total_bytes"]
+    assert 24 * (s32 + c16) == by["fp32_ssm_bf16_conv_24_layers"]["total_bytes"]
+    assert 24 * (s16 + c16) // 131072 == by["bf16_ssm_bf16_conv_24_layers"]["crossover_tokens"]
+    assert round((s32 + c16) / 2 ** 20, 2) == by["per_layer_block_mib"]["mib_2dp"]
+    assert round(256 * 24 * (s32 + c16) / 2 ** 30, 1) == by["pool_256_slots_gib"]["gib_1dp"]
+    assert round(100 * c16 / (s32 + c16), 1) == by["conv_share_percent"]["percent_1dp"]
+    assert 2 * s32 == by["long_context_per_layer"]["total_bytes"]
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(L=0), ARG), (dict(S=0), ARG), (dict(H=0), ARG),
+    (dict(H=12, G=8), SHAPE), (dict(P=60), SHAPE), (dict(N=20), SHAPE),
+    (dict(W=5), UNSUP), (dict(W=1), UNSUP),
+    (dict(ssm=2), DTYPE), (dict(conv=-1), DTYPE),
+    (dict(ssm_base=0), ARG), (dict(ssm_base=FAKE + 8), ALIGN), (dict(conv_base=FAKE + 4), ALIGN),
+])
+def test_pool_create_rejects(change, code):
+    st, _ = create(make_desc(**change))
+    assert st == code
+    assert lib().mamba2_last_error()
+
+
+def test_pool_create_rejects_wrong_byte_counts():
+    d = make_desc()
+    d.ssm_bytes += 2
+    assert create(d)[0] == SHAPE
+    d = make_desc()
+    d.conv_bytes -= 16
+    assert create(d)[0] == SHAPE
+
+
+PARAMS = LayerParams(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def decode(h, **kw):
+    a = dict(layer=0, params=byref(PARAMS), batch=2, slots=FAKE, slots_host=None, x=FAKE, xs=8192,
+             B=FAKE, Bs=1024, C=FAKE, Cs=1024, z=FAKE, zs=8192, dt=FAKE, dts=128, io=1, y=FAKE, ys=8192, yd=1)
+    a.update(kw)
+    return lib().mamba2_decode_step(h, a["layer"], a["params"], a["batch"], a["slots"], a["slots_host"],
+                                    a["x"], a["xs"], a["B"], a["Bs"], a["C"], a["Cs"], a["z"], a["zs"],
+                                    a["dt"], a["dts"], a["io"], a["y"], a["ys"], a["yd"], None)
+
+
+def test_decode_validation(pool):
+    assert decode(pool, batch=0) == 0                     # empty batch: nothing launched
+    assert decode(pool, layer=1) == ARG
+    assert decode(pool, layer=-1) == ARG
+    assert decode(pool, batch=-1) == ARG
+    assert decode(pool, params=None) == ARG
+    bad = LayerParams(FAKE, 0, FAKE, FAKE, FAKE)
+    assert decode(pool, params=byref(bad)) == ARG
+    bad = LayerParams(FAKE, FAKE, FAKE, FAKE + 4, FAKE)
+    assert decode(pool, params=byref(bad)) == ALIGN
+    assert decode(pool, io=3) == DTYPE
+    assert decode(pool, yd=7) == DTYPE
+    assert decode(pool, slots=None) == ARG
+    assert decode(pool, x=None) == ARG
+    assert decode(pool, x=FAKE + 2) == ALIGN
+    assert decode(pool, xs=8196) == ALIGN
+    assert decode(pool, xs=100) == SHAPE
+    assert decode(pool, Bs=512) == SHAPE
+    assert decode(pool, dts=64) == SHAPE
+    assert decode(pool, ys=10) == SHAPE
+    sh = (ctypes.c_int32 * 2)(3, 4)
+    assert decode(pool, slots_host=sh) == SLOT            # slot 4 of a 4-slot pool
+    sh = (ctypes.c_int32 * 2)(2, 2)
+    assert decode(pool, slots_host=sh) == SLOT            # duplicate
+    sh = (ctypes.c_int32 * 2)(-2, 1)
+    assert decode(pool, slots_host=sh) == SLOT
+    assert b"slot" in lib().mamba2_last_error()
+
+
+def test_decode_rejects_unsupported_state_size():
+    st, h = create(make_desc(H=8, P=16, N=24, G=1))
+    assert st == 0
+    assert decode(h, xs=128, Bs=24, Cs=24, zs=128, dts=8, ys=128) == UNSUP
+    lib().mamba2_pool_destroy(h)
+
+
+def prefill(h, cu, slots, has_init=None, start=None, ck=None, max_ck=0, interval=0, chunk=256,
+            ws=FAKE, ws_bytes=1 << 40, **kw):
+    n = len(slots)
+    cu_a = np.asarray(cu, np.int32)
+    sl_a = np.asarray(slots, np.int32)
+    hi_a = np.asarray(has_init if has_init is not None else [0] * n, np.uint8)
+    sp_a = None if start is None else np.asarray(start, np.int32)
+    ck_a = None if ck is None else np.asarray(ck, np.int32)
+    p = lambda a: None if a is None else a.ctypes.data_as(c_void_p)
+    a = dict(x=FAKE, xs=8192, B=FAKE, Bs=1024, C=FAKE, Cs=1024, z=FAKE, zs=8192, dt=FAKE, dts=128, io=1,
+             y=FAKE, ys=8192, yd=1, params=byref(PARAMS), layer=0)
+    a.update(kw)
+    return lib().mamba2_prefill_chunked(h, a["layer"], a["params"], n, p(cu_a), p(sl_a), p(hi_a), p(sp_a),
+                                        a["x"], a["xs"], a["B"], a["Bs"], a["C"], a["Cs"], a["z"], a["zs"],
+                                        a["dt"], a["dts"], a["io"], a["y"], a["ys"], a["yd"], chunk, interval,
+                                        p(ck_a), max_ck, ws, ws_bytes, None)
+
+
+def test_prefill_validation(pool):
+    assert prefill(pool, [0], []) == 0                    # no sequences
+    assert prefill(pool, [0, 0, 0], [0, 1]) == 0          # only empty sequences
+    assert prefill(pool, [1, 4], [0]) == SHAPE
+    assert prefill(pool, [0, 5, 3], [0, 1]) == SHAPE
+    assert prefill(pool, [0, 5, 9], [1, 1]) == SLOT
+    assert prefill(pool, [0, 5], [4]) == SLOT
+    assert prefill(pool, [0, 5], [0], chunk=24) == UNSUP
+    assert prefill(pool, [0, 5], [0], chunk=512) == UNSUP
+    assert prefill(pool, [0, 5], [0], start=[-1]) == ARG
+    ck = [[2, 3]]
+    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300) == ARG      # interval % chunk
+    assert prefill(pool, [0, 600], [0], start=[100], ck=ck, max_ck=2, interval=256) == ARG
+    assert prefill(pool, [0, 600], [0], ck=[[0, 3]], max_ck=2, interval=256) == SLOT  # aliases the slot
+    assert prefill(pool, [0, 600], [0], ck=[[2, 2]], max_ck=2, interval=256) == SLOT  # repeated
+    assert prefill(pool, [0, 600], [0], ck=[[2, 9]], max_ck=2, interval=256) == SLOT  # range
+    assert prefill(pool, [0, 600], [0], ck=None, max_ck=2, interval=256) == ARG
+    assert prefill(pool, [0, 5], [0], x=None) == ARG
+    assert prefill(pool, [0, 5], [0], zs=100) == SHAPE
+    assert prefill(pool, [0, 5], [0], io=5) == DTYPE
+    assert prefill(pool, [0, 5], [0], ws=0) == WS
+    assert prefill(pool, [0, 5], [0], ws=FAKE + 128) == WS
+    assert prefill(pool, [0, 5], [0], ws_bytes=1024) == WS
+    assert prefill(pool, [0, 5], [0], layer=3) == ARG
+
+
+def test_workspace_size_formula(pool):
+    n = c_uint64()
+    assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 256, 0, byref(n)) == 0
+    H, P, N, Cd, T = 128, 64, 128, 10240, 8192
+    nc = T // 256 + 1
+    act = T * Cd * 4
+    assert n.value >= act + 2 * H * T * 4 + nc * H * P * N * 4
+    assert n.value < act + 2 * H * T * 4 + nc * H * P * N * 4 + 64 * 1024
+    assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 20, 0, byref(n)) == UNSUP
+    assert lib().mamba2_prefill_workspace_size(pool, -1, 8192, 256, 0, byref(n)) == ARG
+
+
+def test_prefill_rejects_unsupported_head_dim():
+    st, h = create(make_desc(H=8, P=24, N=16, G=1))
+    assert st == 0
+    assert prefill(h, [0, 5], [0], xs=192, Bs=16, Cs=16, zs=192, dts=8, ys=192, chunk=16) == UNSUP
+    lib().mamba2_pool_destroy(h)
+
+
+def ckpt(h, src_host, dst_host, layer=0, n=None):
+    n = len(src_host) if n is None else n
+    s = np.asarray(src_host, np.int32)
+    d = np.asarray(dst_host, np.int32)
+    return lib().mamba2_checkpoint_states(h, layer, n, FAKE, FAKE, s.ctypes.data_as(c_void_p),
+                                          d.ctypes.data_as(c_void_p), None)
+
+
+def test_checkpoint_validation(pool):
+    assert ckpt(pool, [], [], n=0) == 0
+    assert ckpt(pool, [0], [1], layer=-2) == ARG
+    assert ckpt(pool, [0], [1], layer=1) == ARG
+    assert ckpt(pool, [0], [0]) == SLOT
+    assert ckpt(pool, [0, 1], [2, 2]) == SLOT
+    assert ckpt(pool, [0, 2], [2, 3]) == SLOT        # dst 2 is also a source
+    assert ckpt(pool, [0], [4]) == SLOT
+    assert ckpt(pool, [-1], [1]) == SLOT
+    assert lib().mamba2_checkpoint_states(pool, 0, -1, FAKE, FAKE, None, None, None) == ARG
+    assert lib().mamba2_checkpoint_states(pool, 0, 1, None, FAKE, None, None, None) == ARG
+
+
+def test_last_error_is_cleared_by_success(pool):
+    assert decode(pool, layer=5) == ARG
+    assert lib().mamba2_last_error() != b""
+    a, b = c_uint64(), c_uint64()
+    assert lib().mamba2_pool_info(pool, byref(a), byref(b)) == 0
+    assert lib().mamba2_last_error() == b""
+
+
+def test_destroy_null_is_noop():
+    lib().mamba2_pool_destroy(None)

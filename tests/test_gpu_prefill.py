@@ -1,0 +1,198 @@
+"""GPU parity of the chunked prefill against the CPU oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mamba2 as orc
+from recurrent_state_update_amd import synth
+from tests.gpu_helpers import (TOL, dev, host, log, make_pool, put_slot, raw_bytes, rel_err, untouched,
+                               weights)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(pool, W, cu, slots, has_init, u, z, dt, io, y_dtype, start_pos=None, chunk=256,
+                interval=0, ckpt=None):
+    T = int(cu[-1])
+    y = torch.full((T, pool.intermediate), float("nan"), dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16,
+                   device="cuda")
+    x, B, C = pool.split_xbc(dev(u, io))
+    pool.prefill(0, W, cu, slots, has_init, x, B, C, dev(z, io), dev(dt, io), y, start_pos=start_pos,
+                 chunk_size=chunk, ckpt_interval=interval, ckpt_slots=ckpt)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_tiny_prefill_matches_oracle_and_64_decode_steps():
+    w = synth.tiny_workload(0)
+    sh, slots = w["shape"], w["slots"]
+    log(f"case: {w['name']}, prefill chunk 16")
+    pack = lambda a: a.transpose(1, 0, 2).reshape(-1, a.shape[-1])
+    u, z, dt = pack(w["u"]), pack(w["z"]), pack(w["dt"])
+    cu = w["cu_seqlens"]
+    W = weights(w["params"])
+    pool = make_pool(sh, 1, 8, "f32", "f32")
+    for i, s in enumerate(slots):
+        put_slot(pool, 0, int(s), w["ssm0"][i], w["conv0"][i])
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    y = run_prefill(pool, W, cu, slots, [1] * 4, u, z, dt, "f32", "f32", chunk=16)
+    ref = orc.PoolRef(sh, 1, 8, "f32", "f32")
+    ref.ssm[0, slots], ref.conv[0, slots] = w["ssm0"], w["conv0"]
+    y_ref = orc.prefill(ref, 0, w["params"], cu, slots, [1] * 4, [0] * 4, u, z, dt, "f32")
+    e = rel_err(host(y), y_ref)
+    log(f"prefill y rel error {e:.3e}")
+    assert e <= TOL["f32"]
+    for s in slots:
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= TOL["f32"]
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s])
+    assert untouched(before_s, pool.ssm, slots) and untouched(before_c, pool.conv, slots)
+    # the same tokens as 64 decode steps on the GPU
+    dpool = make_pool(sh, 1, 8, "f32", "f32")
+    for i, s in enumerate(slots):
+        put_slot(dpool, 0, int(s), w["ssm0"][i], w["conv0"][i])
+    yd = torch.empty((4, sh.intermediate), dtype=torch.float32, device="cuda")
+    ys = []
+    sl = torch.from_numpy(slots).cuda()
+    for t in range(64):
+        x, B, C = dpool.split_xbc(dev(w["u"][t], "f32"))
+        dpool.decode_step(0, W, sl, x, B, C, dev(w["z"][t], "f32"), dev(w["dt"][t], "f32"), yd)
+        ys.append(host(yd))
+    y_dec = np.stack(ys, 1).reshape(256, -1)
+    e2 = rel_err(host(y), y_dec)
+    log(f"prefill vs decode rel difference {e2:.3e}")
+    assert e2 <= TOL["f32"]
+    for s in slots:
+        assert rel_err(host(pool.ssm[0, s]), host(dpool.ssm[0, s])) <= TOL["f32"]
+        assert torch.equal(pool.conv[0, s], dpool.conv[0, s])
+
+
+def _varlen_case(ssm_dtype, Q, seed):
+    sh = synth.Shape(8, 64, 128, 2, 4)
+    rng = np.random.default_rng(seed)
+    params = synth.layer_params(rng, sh)
+    lens = np.array([1, 3, 16, 17, 100, 255, 256, 257, 600], np.int32)
+    n = len(lens)
+    has_init = np.array([1, 0, 1, 0, 1, 0, 1, 0, 1], np.uint8)
+    start = np.array([Q, 0, 2 * Q, 0, 0, 0, Q, 0, 3 * Q], np.int32)
+    slots = np.arange(n, dtype=np.int32) * 2 + 1             # 1, 3, ..., 17
+    free = [s for s in range(40) if s not in set(slots.tolist())]
+    interval = 2 * Q
+    kmax = 4
+    ck = np.full((n, kmax), -1, np.int32)
+    it = iter(free)
+    for i in range(n):
+        for k in range((start[i] + lens[i]) // interval - start[i] // interval):
+            if k < kmax:
+                ck[i, k] = next(it)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    io = ssm_dtype
+    u, z, dt = synth._tokens(rng, sh, int(cu[-1]), io)
+    ssm0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.nheads, sh.head_dim, sh.d_state)), ssm_dtype)
+    conv0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.conv_dim, 3)), "bf16")
+    return dict(sh=sh, params=params, lens=lens, has_init=has_init, start=start, slots=slots, ck=ck, cu=cu,
+                u=u, z=z, dt=dt, ssm0=ssm0, conv0=conv0, interval=interval, io=io)
+
+
+@pytest.mark.parametrize("ssm_dtype,Q", [("bf16", 256), ("bf16", 64), ("f32", 256), ("f32", 32)])
+def test_varlen_prefill_with_seeds_and_checkpoints(ssm_dtype, Q):
+    c = _varlen_case(ssm_dtype, Q, seed=100 + Q)
+    sh = c["sh"]
+    log(f"case: varlen prefill lens={c['lens'].tolist()} ssm={ssm_dtype} Q={Q} interval={c['interval']}")
+    pool = make_pool(sh, 1, 40, ssm_dtype, "bf16")
+    ref = orc.PoolRef(sh, 1, 40, ssm_dtype, "bf16")
+    for i, s in enumerate(c["slots"]):
+        put_slot(pool, 0, int(s), c["ssm0"][i], c["conv0"][i])
+        ref.ssm[0, s], ref.conv[0, s] = c["ssm0"][i], c["conv0"][i]
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    y = run_prefill(pool, weights(c["params"]), c["cu"], c["slots"], c["has_init"], c["u"], c["z"], c["dt"],
+                    c["io"], ssm_dtype, start_pos=c["start"], chunk=Q, interval=c["interval"], ckpt=c["ck"])
+    y_ref = orc.prefill(ref, 0, c["params"], c["cu"], c["slots"], c["has_init"], c["start"], c["u"], c["z"],
+                        c["dt"], ssm_dtype, ckpt_interval=c["interval"], ckpt_slots=c["ck"])
+    tol = TOL[ssm_dtype]
+    yh = host(y)
+    for i in range(len(c["lens"])):
+        a, b = c["cu"][i], c["cu"][i + 1]
+        e = rel_err(yh[a:b], y_ref[a:b])
+        assert e <= tol, (i, e)
+    written = list(c["slots"]) + [int(s) for s in c["ck"].ravel() if s >= 0]
+    log(f"y rel error {rel_err(yh, y_ref):.3e}; {len(written) - len(c['slots'])} checkpoints")
+    for s in written:
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= tol, s
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+    assert untouched(before_s, pool.ssm, written) and untouched(before_c, pool.conv, written)
+
+
+def test_prefill_8192_tokens_from_zero_state():
+    w = synth.prefill_workload(2)
+    sh = w["shape"]
+    log(f"case: {w['name']}")
+    pool = make_pool(sh, 1, 512, "bf16", "bf16")
+    pool.ssm[0, 17] = float("nan")
+    pool.conv[0, 17] = float("nan")
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    y = run_prefill(pool, weights(w["params"]), w["cu_seqlens"], w["slots"], w["has_init"], w["u"], w["z"],
+                    w["dt"], "bf16", "bf16", chunk=w["chunk"])
+    heads = [0, 37, 90, 127]
+    ref = orc.PoolRef(sh, 1, 18, "bf16", "bf16")
+    y_ref = orc.prefill(ref, 0, w["params"], w["cu_seqlens"], w["slots"], w["has_init"], w["start_pos"],
+                        w["u"], w["z"], w["dt"], "bf16", heads=heads)
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    e = rel_err(yh, y_ref)      # only the sampled heads' columns are defined in y_ref
+    log(f"sampled-head y rel error {e:.3e}")
+    assert e <= TOL["bf16"]
+    for h in heads:
+        assert rel_err(host(pool.ssm[0, 17, h]), ref.ssm[0, 17, h]) <= TOL["bf16"]
+    assert np.array_equal(host(pool.conv[0, 17]), ref.conv[0, 17])
+    assert untouched(before_s, pool.ssm, [17]) and untouched(before_c, pool.conv, [17])
+
+
+def test_two_call_handoff_is_bit_exact_with_fp32_state():
+    """prefill(L1) then prefill(L2, seeded, start_pos=L1) == prefill(L1+L2) when L1 is chunk-aligned."""
+    sh = synth.Shape(8, 64, 128, 2, 4)
+    rng = np.random.default_rng(77)
+    params = synth.layer_params(rng, sh)
+    L1, L2, Q = 512, 333, 256
+    u, z, dt = synth._tokens(rng, sh, L1 + L2, "bf16")
+    ssm0 = synth.cast_exact(rng.normal(0, 0.1, (sh.nheads, sh.head_dim, sh.d_state)), "f32")
+    conv0 = synth.cast_exact(rng.normal(0, 0.1, (sh.conv_dim, 3)), "bf16")
+    W = weights(params)
+    one = make_pool(sh, 1, 4, "f32", "bf16")
+    put_slot(one, 0, 2, ssm0, conv0)
+    y1 = run_prefill(one, W, [0, L1 + L2], [2], [1], u, z, dt, "bf16", "f32", chunk=Q)
+    two = make_pool(sh, 1, 4, "f32", "bf16")
+    put_slot(two, 0, 2, ssm0, conv0)
+    ya = run_prefill(two, W, [0, L1], [2], [1], u[:L1], z[:L1], dt[:L1], "bf16", "f32", chunk=Q)
+    yb = run_prefill(two, W, [0, L2], [2], [1], u[L1:], z[L1:], dt[L1:], "bf16", "f32", chunk=Q,
+                     start_pos=[L1])
+    assert torch.equal(torch.cat([ya, yb]), y1)
+    assert torch.equal(one.ssm[0, 2], two.ssm[0, 2]) and torch.equal(one.conv[0, 2], two.conv[0, 2])
+
+
+def test_checkpoint_equals_prefix_prefill_and_restore_replay():
+    """With fp32 state a checkpoint at 256 equals a 256-token prefill bit for bit, and restoring
+    it into a fresh slot and replaying the suffix reproduces the uninterrupted run bit for bit."""
+    sh = synth.Shape(8, 64, 128, 2, 4)
+    rng = np.random.default_rng(78)
+    params = synth.layer_params(rng, sh)
+    L, Q = 700, 256
+    u, z, dt = synth._tokens(rng, sh, L, "bf16")
+    W = weights(params)
+    pool = make_pool(sh, 1, 8, "f32", "bf16")
+    y_full = run_prefill(pool, W, [0, L], [0], [0], u, z, dt, "bf16", "f32", chunk=Q, interval=256,
+                         ckpt=[[5, 6]])
+    pref = make_pool(sh, 1, 8, "f32", "bf16")
+    run_prefill(pref, W, [0, 256], [0], [0], u[:256], z[:256], dt[:256], "bf16", "f32", chunk=Q)
+    assert torch.equal(pool.ssm[0, 5], pref.ssm[0, 0]) and torch.equal(pool.conv[0, 5], pref.conv[0, 0])
+    run_prefill(pref, W, [0, 256], [0], [1], u[256:512], z[256:512], dt[256:512], "bf16", "f32",
+                chunk=Q, start_pos=[256])
+    assert torch.equal(pref.ssm[0, 0], pool.ssm[0, 6]) and torch.equal(pool.conv[0, 6], pref.conv[0, 0])
+    # restore: copy checkpoint slot 5 into fresh slot 3, clobber slot 0, replay tokens 256..700 from slot 3
+    pool.ssm[0, 0] = float("nan")
+    pool.conv[0, 0] = float("nan")
+    src = torch.tensor([5], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([3], dtype=torch.int32, device="cuda")
+    pool.checkpoint(0, src, dst, src_host=[5], dst_host=[3])
+    y_tail = run_prefill(pool, W, [0, L - 256], [3], [1], u[256:], z[256:], dt[256:], "bf16", "f32",
+                         chunk=Q, start_pos=[256])
+    assert torch.equal(y_tail, y_full[256:])
