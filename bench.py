@@ -39,6 +39,18 @@ def prefill_dense_flops_per_token(sh, Q) -> int:
     return 2 * Q * sh.d_state * sh.n_groups + 2 * Q * sh.head_dim * sh.nheads + 4 * sh.nheads * sh.head_dim * sh.d_state
 
 
+def measured_traffic(root: str):
+    """HBM bytes per decode launch from the committed counter profile, if the kernel sources still match."""
+    import hashlib
+    path = os.path.join(root, "profiles", "decode_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(root, p), "rb").read() for p in rec["sources"])
+    except (OSError, ValueError, KeyError):
+        return None
+    return rec["traffic_bytes_per_launch"] if hashlib.sha256(src).hexdigest() == rec["source_sha256"] else None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -47,6 +59,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
+                    help="after timing, run 10 slot copies of PAIRS slot pairs (a plain copy kernel of "
+                         "known size, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
@@ -118,11 +133,23 @@ def main() -> int:
         "wall_s_timed": wall,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
             "kernel": "decode_kernel<bf16, N=128, W=4>", "bytes_per_launch": launch_bytes,
             "bytes_per_sequence": per_seq,
         },
     }
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy
+        src = torch.arange(0, n, device=dev, dtype=torch.int32)
+        dst = torch.arange(w["num_slots"] - n, w["num_slots"], device=dev, dtype=torch.int32)
+        for _ in range(10):
+            pool.checkpoint(0, src, dst)
+        torch.cuda.synchronize()
+        ssm_b, conv_b = pool.info()
+        out["copy_calibration"] = {"pairs": n, "ssm_bytes_per_copy_launch": n * ssm_b,
+                                   "conv_bytes_per_copy_launch": n * conv_b, "launches": 10}
 
     if not args.no_prefill:
         pw = synth.prefill_workload(2)

@@ -1,6 +1,6 @@
 // Fused Mamba2 decode step over a slot pool, gfx950.
 //
-// One workgroup of 256 threads (four wave64s) per (sequence row, group).
+// One workgroup of 512 threads (eight wave64s) per (sequence row, group).
 // Phase 1 shifts the conv window of the group's channels (x of its heads,
 // then its B and C), applies the depthwise conv and SiLU, and stages the
 // activations in LDS, together with Delta = softplus(dt + dt_bias) and
@@ -19,7 +19,47 @@
 #include "device_common.h"
 #include "kernels.h"
 
+// Tuning knobs (compile-time): state rows per lane batch, threads per
+// workgroup, minimum waves per SIMD the register budget must allow,
+// non-temporal state accesses, prefetch depth, and whether the first state
+// tile is requested before the conv phase.  Defaults are the fastest
+// combination measured on MI355X for the 8B-hybrid decode (see the design notes).
+#ifndef M2_DECODE_ROWS
+#define M2_DECODE_ROWS 8
+#endif
+#ifndef M2_DECODE_THREADS
+#define M2_DECODE_THREADS 512
+#endif
+#ifndef M2_DECODE_WAVES_PER_EU
+#define M2_DECODE_WAVES_PER_EU 1
+#endif
+#ifndef M2_DECODE_NT
+#define M2_DECODE_NT 1
+#endif
+#ifndef M2_DECODE_PF
+#define M2_DECODE_PF 1
+#endif
+#ifndef M2_DECODE_EARLY
+#define M2_DECODE_EARLY 1
+#endif
+
 namespace m2 {
+
+// M2_DECODE_NT: 1 = non-temporal loads and stores, 2 = loads only, 3 = stores only.
+template <typename V> __device__ __forceinline__ V ld_state(const V* p) {
+#if M2_DECODE_NT == 1 || M2_DECODE_NT == 2
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+template <typename V> __device__ __forceinline__ void st_state(V* p, const V& v) {
+#if M2_DECODE_NT == 1 || M2_DECODE_NT == 3
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 
 template <typename T> struct Vec16;
 template <> struct Vec16<float> { typedef floatx4 type; };
@@ -52,13 +92,14 @@ template <int M, int O> struct RowReduce {
 };
 
 template <typename TS, int N, int W>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
+__global__ __launch_bounds__(M2_DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(M2_DECODE_WAVES_PER_EU)))
+void decode_kernel(DecodeParams a) {
   typedef typename Vec16<TS>::type vec_t;
   constexpr int VEC = 16 / sizeof(TS);   // state elements per 16-byte access
   constexpr int LPR = N / VEC;           // lanes per state row
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "unsupported d_state");
   constexpr int RPI = 64 / LPR;          // rows per wave-wide access
-  constexpr int U0 = 32 / RPI;
+  constexpr int U0 = M2_DECODE_ROWS / RPI;
   constexpr int U = U0 < 1 ? 1 : (U0 > 16 ? 16 : U0);   // accesses in flight per lane
   constexpr int RB = RPI * U;            // rows per batch
   constexpr int MF = U > LPR ? U / LPR : 1;             // row sums held per lane at the end
@@ -84,6 +125,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   float* s_delta = smem + nx + 2 * N;   // [hpg]
   float* s_alpha = s_delta + hpg;       // [hpg]
 
+  // ---------------------------------------------------------------- state geometry
+  const int sub = lane % LPR;
+  const int rsub = lane / LPR;
+  const int n0 = sub * VEC;
+  const int nwaves = blockDim.x >> 6;
+  TS* const base = static_cast<TS*>(a.ssm) + ((int64_t)slot * a.H + g * hpg) * P * N;
+  // Flattened (head, row batch) tiles of this wave; with prefetch the next
+  // tile's loads are issued before the current tile is computed.
+  const int nbat = (P + RB - 1) / RB;
+  const int my_heads = hpg > wave ? (hpg - wave + nwaves - 1) / nwaves : 0;
+  const int ntile = my_heads * nbat;
+  auto tile_ptr = [&](int t, int& hl, int& r0) -> TS* {
+    hl = wave + (t / nbat) * nwaves;
+    r0 = (t % nbat) * RB;
+    return base + (int64_t)hl * P * N;
+  };
+  auto load_tile = [&](int t, vec_t (&d)[U]) {
+    int hl, r0;
+    const TS* st = tile_ptr(t, hl, r0);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int row = r0 + j * RPI + rsub;
+      if (row < P) d[j] = ld_state(reinterpret_cast<const vec_t*>(st + (int64_t)row * N + n0));
+    }
+  };
+  vec_t data[U];
+#if M2_DECODE_PF >= 1
+  vec_t next[U];
+#endif
+#if M2_DECODE_PF >= 2
+  vec_t next2[U];
+#endif
+#if M2_DECODE_EARLY && M2_DECODE_PF >= 1
+  if (ntile > 0) load_tile(0, next);
+#if M2_DECODE_PF >= 2
+  if (ntile > 1) load_tile(1, next2);
+#endif
+#endif
   // ---------------------------------------------------------------- conv
   const int nch = nx + 2 * N;
   for (int ck = tid * 8; ck < nch; ck += blockDim.x * 8) {
@@ -177,62 +256,65 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   __syncthreads();
 
   // ---------------------------------------------------------------- state
-  const int sub = lane % LPR;
-  const int rsub = lane / LPR;
-  const int n0 = sub * VEC;
   float Bv[VEC], Cv[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     Bv[e] = s_act[nx + n0 + e];
     Cv[e] = s_act[nx + N + n0 + e];
   }
-  const int nwaves = blockDim.x >> 6;
-  TS* const base = static_cast<TS*>(a.ssm) + ((int64_t)slot * a.H + g * hpg) * P * N;
-
-  for (int hl = wave; hl < hpg; hl += nwaves) {
+#if !M2_DECODE_EARLY && M2_DECODE_PF >= 1
+  if (ntile > 0) load_tile(0, next);
+#if M2_DECODE_PF >= 2
+  if (ntile > 1) load_tile(1, next2);
+#endif
+#endif
+  for (int t = 0; t < ntile; ++t) {
+#if M2_DECODE_PF >= 2
+#pragma unroll
+    for (int j = 0; j < U; ++j) { data[j] = next[j]; next[j] = next2[j]; }
+    if (t + 2 < ntile) load_tile(t + 2, next2);
+#elif M2_DECODE_PF == 1
+#pragma unroll
+    for (int j = 0; j < U; ++j) data[j] = next[j];
+    if (t + 1 < ntile) load_tile(t + 1, next);
+#else
+    load_tile(t, data);
+#endif
+    int hl, r0;
+    TS* const st = tile_ptr(t, hl, r0);
     const float delta = s_delta[hl];
     const float alpha = s_alpha[hl];
     const int h = g * hpg + hl;
-    const float Dh = a.D[h];
     const float* xs = s_act + hl * P;
-    TS* const st = base + (int64_t)hl * P * N;
-
-    for (int r0 = 0; r0 < P; r0 += RB) {
-      vec_t data[U];
+    float acc[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int row = r0 + j * RPI + rsub;
-        if (row < P) data[j] = *reinterpret_cast<const vec_t*>(st + (int64_t)row * N + n0);
-      }
-      float acc[U];
+    for (int j = 0; j < U; ++j) {
+      const int row = r0 + j * RPI + rsub;
+      acc[j] = 0.f;
+      if (row < P) {
+        const float dx = delta * xs[row];
+        vec_t o;
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int row = r0 + j * RPI + rsub;
-        acc[j] = 0.f;
-        if (row < P) {
-          const float dx = delta * xs[row];
-          vec_t o;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float hn = alpha * to_f32(data[j][e]) + dx * Bv[e];
-            acc[j] += hn * Cv[e];
-            o[e] = from_f32<TS>(hn);
-          }
-          *reinterpret_cast<vec_t*>(st + (int64_t)row * N + n0) = o;
+        for (int e = 0; e < VEC; ++e) {
+          const float hn = alpha * to_f32(data[j][e]) + dx * Bv[e];
+          acc[j] += hn * Cv[e];
+          o[e] = from_f32<TS>(hn);
         }
+        st_state(reinterpret_cast<vec_t*>(st + (int64_t)row * N + n0), o);
       }
-      int sel = 0;
-      RowReduce<U, LPR / 2>::run(acc, lane, sel);
-      if ((lane % DUP) == 0) {
+    }
+    int sel = 0;
+    RowReduce<U, LPR / 2>::run(acc, lane, sel);
+    if ((lane % DUP) == 0) {
+      const float Dh = a.D[h];
 #pragma unroll
-        for (int k = 0; k < MF; ++k) {
-          const int row = r0 + (sel + k) * RPI + rsub;
-          if (row < P) {
-            const int64_t ci = (int64_t)h * P + row;
-            const float yv = acc[k] + Dh * xs[row];
-            const float zv = load_any(a.z, b * a.z_stride + ci, a.io_bf16);
-            store_any(a.y, b * a.y_stride + ci, yv * silu(zv), a.y_bf16);
-          }
+      for (int k = 0; k < MF; ++k) {
+        const int row = r0 + (sel + k) * RPI + rsub;
+        if (row < P) {
+          const int64_t ci = (int64_t)h * P + row;
+          const float yv = acc[k] + Dh * xs[row];
+          const float zv = load_any(a.z, b * a.z_stride + ci, a.io_bf16);
+          store_any(a.y, b * a.y_stride + ci, yv * silu(zv), a.y_bf16);
         }
       }
     }
@@ -243,7 +325,7 @@ template <typename TS, int N>
 static hipError_t launch_w(const DecodeParams& p, int W, int batch, hipStream_t s) {
   const int hpg = p.H / p.G;
   const size_t lds = sizeof(float) * (hpg * p.P + 2 * N + 2 * hpg);
-  const dim3 grid(p.G, batch), block(256);
+  const dim3 grid(p.G, batch), block(M2_DECODE_THREADS);
   switch (W) {
     case 2: hipLaunchKernelGGL((decode_kernel<TS, N, 2>), grid, block, lds, s, p); break;
     case 3: hipLaunchKernelGGL((decode_kernel<TS, N, 3>), grid, block, lds, s, p); break;
