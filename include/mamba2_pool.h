@@ -122,7 +122,7 @@ m2_status mamba2_pool_info(const m2_pool* pool, uint64_t* ssm_bytes_per_slot_lay
  *              [x|B|C] row of width d_conv works with B = x + H*P, C = B + G*N).
  *   z [batch][H*P], dt [batch][H] of io_dtype.
  *   y [batch][H*P] of y_dtype: out = (C h + D x) * SiLU(z), written for every row.
- * x, B, C, z, y must be 16-byte aligned with 16-byte multiple row strides.
+ * x, B, C must be 16-byte aligned with 16-byte multiple row strides.
  * Duplicated slots in one call race; pass slots_host to have them rejected. */
 m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params,
                              int32_t batch, const int32_t* slots, const int32_t* slots_host,
@@ -161,7 +161,8 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  *              Checkpoint slots must be distinct and disjoint from `slots`.
  *              Requires ckpt_interval % chunk_size == 0 and start_pos % chunk_size == 0,
  *              so checkpoints fall on chunk ends.
- * Device tensors: x, B, C, z, dt, y as in mamba2_decode_step with rows = packed tokens.
+ * Device tensors: x, B, C, z, dt, y as in mamba2_decode_step with rows = packed tokens
+ * (x, B, C 16-byte aligned with 16-byte multiple row strides).
  * chunk_size: multiple of 16, at most 256.  Chunks start at each sequence's
  * first row.  workspace: device memory of at least
  * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch

@@ -108,27 +108,42 @@ m2_status hip_fail(hipError_t e, const char* what) {
 
 // Prefill tables and workspace carving.
 struct PrefillLayout {
-  uint64_t nc_max, nw_max;
-  uint64_t off_seqs, off_chunks, off_windows, meta_bytes;
-  uint64_t off_act, off_delta, off_dA, off_states, total;
+  uint64_t nc_max, ns_max, nw_max, planes;
+  uint64_t off_seqs, off_chunks, off_segs, off_windows, meta_bytes;
+  uint64_t off_xT, off_Bt, off_Br, off_Cr, plane_xT, plane_Bt, plane_Br, plane_Cr;
+  uint64_t off_delta, off_dA, off_seg_state, off_seg_decay, total;
 };
 
-bool prefill_layout(const m2::LayerShape& sh, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
+bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
   L->nc_max = (uint64_t)(T / Q) + (uint64_t)num_seqs;
+  L->ns_max = L->nc_max;
   L->nw_max = (uint64_t)num_seqs + L->nc_max;
+  L->planes = split ? 2 : 1;
   L->off_seqs = 0;
   L->off_chunks = align_up(L->off_seqs + num_seqs * sizeof(m2::SeqEntry), 256);
-  L->off_windows = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
+  L->off_segs = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
+  L->off_windows = align_up(L->off_segs + L->ns_max * sizeof(m2::SegEntry), 256);
   L->meta_bytes = align_up(L->off_windows + L->nw_max * sizeof(m2::WindowEntry), 256);
-  uint64_t act, vec, st;
-  if (!mul_ok((uint64_t)T, (uint64_t)sh.Cd * 4, &act)) return false;
-  if (!mul_ok((uint64_t)T, (uint64_t)sh.H * 4, &vec)) return false;
-  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N * 4, &st)) return false;
-  L->off_act = L->meta_bytes;
-  L->off_delta = align_up(L->off_act + act, 256);
-  L->off_dA = align_up(L->off_delta + vec, 256);
-  L->off_states = align_up(L->off_dA + vec, 256);
-  L->total = align_up(L->off_states + st, 256);
+  const uint64_t rows = L->nc_max * (uint64_t)Q;          // chunk-blocked rows
+  uint64_t v;
+  if (!mul_ok(rows, (uint64_t)sh.H * sh.P, &L->plane_xT)) return false;
+  if (!mul_ok(rows, (uint64_t)sh.G * sh.N, &L->plane_Bt)) return false;
+  L->plane_Br = L->plane_Cr = L->plane_Bt;
+  uint64_t off = L->meta_bytes;
+  const uint64_t planes[4] = {L->plane_xT, L->plane_Bt, L->plane_Br, L->plane_Cr};
+  uint64_t* offs[4] = {&L->off_xT, &L->off_Bt, &L->off_Br, &L->off_Cr};
+  for (int i = 0; i < 4; ++i) {
+    if (!mul_ok(planes[i], 2 * L->planes, &v)) return false;
+    *offs[i] = off;
+    off = align_up(off + v, 256);
+  }
+  if (!mul_ok((uint64_t)T, (uint64_t)sh.H * 4, &v)) return false;
+  L->off_delta = off;
+  L->off_dA = align_up(L->off_delta + v, 256);
+  L->off_seg_state = align_up(L->off_dA + v, 256);
+  if (!mul_ok(L->ns_max, (uint64_t)sh.H * sh.P * sh.N * 4, &v)) return false;
+  L->off_seg_decay = align_up(L->off_seg_state + v, 256);
+  L->total = align_up(L->off_seg_decay + L->ns_max * sh.H * 4, 256);
   return true;
 }
 
@@ -274,7 +289,7 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
   if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
     return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
   PrefillLayout L;
-  if (!prefill_layout(pool->sh, num_seqs, total_tokens, chunk_size, &L))
+  if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, total_tokens, chunk_size, &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();
@@ -333,23 +348,30 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   if (T == 0) return ok();
   const int ies = esize(io_dtype);
   const int GN = sh.G * sh.N;
-  const IoCheck io[] = {{"x", x, x_stride, sh.I, ies, false},       {"B", B, B_stride, GN, ies, false},
-                        {"C", C, C_stride, GN, ies, false},         {"z", z, z_stride, sh.I, ies, false},
+  const IoCheck io[] = {{"x", x, x_stride, sh.I, ies, true},        {"B", B, B_stride, GN, ies, true},
+                        {"C", C, C_stride, GN, ies, true},          {"z", z, z_stride, sh.I, ies, false},
                         {"dt", dt, dt_stride, sh.H, ies, false},    {"y", y, y_stride, sh.I, esize(y_dtype), false}};
   if (m2_status st = check_io(io, 6)) return st;
   if (!m2::prefill_supported(sh.P, sh.N, sh.W))
-    return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,...,256}");
+    return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,32,64,128}");
   PrefillLayout L;
-  if (!prefill_layout(sh, num_seqs, T, chunk_size, &L)) return fail(M2_ERR_SHAPE, "workspace size overflows");
+  if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, &L))
+    return fail(M2_ERR_SHAPE, "workspace size overflows");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < L.total)
     return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
                 (unsigned long long)L.total);
 
+  // ---- segment length: a function of each sequence's own chunk count only, so a
+  // sequence's results do not depend on the rest of the batch (up to 8 segments per sequence,
+  // at most 16 chunks per segment)
+  auto seg_chunks_of = [](int nchunk) { int s = (nchunk + 7) / 8; return s < 1 ? 1 : (s > 16 ? 16 : s); };
+
   // ---- host tables
   std::vector<m2::SeqEntry> seqs(num_seqs);
   std::vector<m2::ChunkEntry> chunks;
+  std::vector<m2::SegEntry> segs;
   std::vector<m2::WindowEntry> windows;
   chunks.reserve(L.nc_max);
   for (int s = 0; s < num_seqs; ++s) {
@@ -362,7 +384,8 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     e.has_init = has_init[s] ? 1 : 0;
     e.chunk0 = (int32_t)chunks.size();
     e.nchunk = 0;
-    e.pad0 = e.pad1 = 0;
+    e.seg0 = (int32_t)segs.size();
+    e.nseg = 0;
     for (int c0 = 0; c0 < len; c0 += chunk_size) {
       m2::ChunkEntry c;
       c.seq = s;
@@ -382,6 +405,16 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
       if (c.ckpt_slot >= 0) windows.push_back({s, c0 + c.len, c.ckpt_slot, 0});
       chunks.push_back(c);
       ++e.nchunk;
+    }
+    const int seg_chunks = seg_chunks_of(e.nchunk);
+    for (int k = 0; k < e.nchunk; k += seg_chunks) {
+      m2::SegEntry g;
+      g.seq = s;
+      g.chunk0 = e.chunk0 + k;
+      g.nchunk = e.nchunk - k < seg_chunks ? e.nchunk - k : seg_chunks;
+      g.is_last = k + seg_chunks >= e.nchunk;
+      segs.push_back(g);
+      ++e.nseg;
     }
     if (len > 0) windows.push_back({s, len, slots[s], 0});
   }
@@ -413,6 +446,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     memset(st, 0, L.meta_bytes);
     memcpy(st + L.off_seqs, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
     memcpy(st + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
+    memcpy(st + L.off_segs, segs.data(), segs.size() * sizeof(m2::SegEntry));
     memcpy(st + L.off_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
     if ((e = hipMemcpyAsync(ws, st, L.meta_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
       return hip_fail(e, "table upload");
@@ -431,10 +465,12 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.Q = chunk_size;
   p.num_seqs = num_seqs;
   p.num_chunks = (int)chunks.size();
+  p.num_segments = (int)segs.size();
   p.num_windows = (int)windows.size();
   p.total_tokens = (int)T;
   p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws + L.off_seqs);
   p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + L.off_chunks);
+  p.segs = reinterpret_cast<const m2::SegEntry*>(ws + L.off_segs);
   p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + L.off_windows);
   p.x = x;
   p.B = B;
@@ -453,10 +489,18 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.dt_bias = params->dt_bias;
   p.conv_w = params->conv_w;
   p.conv_b = params->conv_b;
-  p.act = reinterpret_cast<float*>(ws + L.off_act);
+  p.xT = reinterpret_cast<uint16_t*>(ws + L.off_xT);
+  p.Bt = reinterpret_cast<uint16_t*>(ws + L.off_Bt);
+  p.Br = reinterpret_cast<uint16_t*>(ws + L.off_Br);
+  p.Cr = reinterpret_cast<uint16_t*>(ws + L.off_Cr);
+  p.xT_plane = (int64_t)L.plane_xT;
+  p.Bt_plane = (int64_t)L.plane_Bt;
+  p.Br_plane = (int64_t)L.plane_Br;
+  p.Cr_plane = (int64_t)L.plane_Cr;
   p.delta = reinterpret_cast<float*>(ws + L.off_delta);
   p.dA = reinterpret_cast<float*>(ws + L.off_dA);
-  p.states = reinterpret_cast<float*>(ws + L.off_states);
+  p.seg_state = reinterpret_cast<float*>(ws + L.off_seg_state);
+  p.seg_decay = reinterpret_cast<float*>(ws + L.off_seg_decay);
   const hipError_t e = m2::launch_prefill(p, hs);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

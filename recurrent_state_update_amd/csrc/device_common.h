@@ -45,7 +45,8 @@ __device__ __forceinline__ void load8_any(const void* p, int64_t i, int is_bf16,
 }
 
 // ------------------------------------------------------------------ math
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(v) = v / (1 + e^-v) with the hardware reciprocal (about 1 ulp) instead of an IEEE divide.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // log(1 + e^v); for v > 20 the correction log1p(e^-v) < 2.1e-9 is below fp32 resolution of v.
 __device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }

@@ -1,80 +1,312 @@
 // Chunked (SSD) prefill of packed variable-length sequences, gfx950.
 //
-// The sequence is cut into chunks of Q tokens starting at each sequence's
-// first row.  Inside a chunk the output is the causally masked product
-// Y = (M o L) X of the Mamba study notes (echobase-5bl.pages.dev, "Mamba and
-// Attention"), M[i][j] = (C_i . B_j) exp(a_i - a_j) Delta_j, with a the
-// chunk-local cumulative sum of Delta*A; chunks are linked by a scan over
-// their end states, each chunk handing its state to the next
-// ("Hybrid SSM / Mamba models and non-KV state", mlinterviewnotes.com
-// ch. 7.3: the chunked-prefill handoff and the SSD chunk-scan call site).
+// Each sequence is cut into chunks of Q tokens from its first row, and runs
+// of consecutive chunks form segments.  Inside a chunk the output is the
+// causally masked product Y = (M o L) X of the Mamba study notes
+// (echobase-5bl.pages.dev, "Mamba and Attention"),
+//   M[i][j] = (C_i . B_j) exp(a_i - a_j) Delta_j   (j <= i),
+// with a the chunk-local cumulative sum of Delta*A, plus exp(a_i) C_i h_in
+// for the state h_in entering the chunk; chunk end states follow
+// h_out = exp(a_last) h_in + sum_j exp(a_last - a_j) Delta_j x_j B_j^T, the
+// affine step that links chunks and segments ("Hybrid SSM / Mamba models and
+// non-KV state", mlinterviewnotes.com ch. 7.3: chunked-prefill handoff,
+// affine-composition passage, SSD chunk-scan call site).
 //
 // Launch sequence (one stream):
-//   1. conv_kernel         causal depthwise conv + SiLU of every (token, channel)
-//   2. dt_kernel           Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
-//   3. chunk_state_kernel  S_c = sum_j exp(a_last - a_j) Delta_j x_j B_j^T  (MFMA)
-//   4. state_pass_kernel   h_c = exp(a_last) h_{c-1} + S_c along each sequence; the state
-//                          entering each chunk replaces S_c; final and checkpoint states
-//                          go to their pool slots rounded to the state dtype
-//   5. chunk_scan_kernel   y = C h_{c-1} exp(a_i) + (M o L) X + D x, gated by SiLU(z)  (MFMA)
-//   6. window_kernel       final and checkpoint conv windows (raw inputs) into their slots
-// With SPLIT the MFMA operands are split into bf16 hi + lo parts and each
-// product takes three bf16 MFMAs, which keeps fp32-level accuracy for fp32
-// state; otherwise operands are rounded to bf16 (fp32 accumulate).
+//   1. conv_kernel       causal conv + SiLU of every (token, channel), written as bf16
+//                        operand planes in the layouts the products read
+//   2. dt_kernel         Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
+//   3. seg_state_kernel  per (segment, head): end state of the segment from a zero state (MFMA);
+//                        skipped for each sequence's last segment
+//   4. seg_pass_kernel   per (sequence, head): scan over segments -> state entering each segment
+//   5. seg_scan_kernel   per (segment, head): walks its chunks with the state in MFMA
+//                        accumulators: outputs (MFMA), state update (MFMA), checkpoint and
+//                        final states rounded into their slots
+//   6. window_kernel     final and checkpoint conv windows (raw inputs) into their slots
+// With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
+// each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
+// otherwise operands are single bf16 planes with fp32 accumulation.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace m2 {
 
-// ------------------------------------------------------------------ helpers
-__device__ __forceinline__ const void* io_col(const PrefillParams& a, int c, int64_t& col, int64_t& stride) {
-  const int I = a.sh.I, GN = a.sh.G * a.sh.N;
-  if (c < I) { col = c; stride = a.x_stride; return a.x; }
-  if (c < I + GN) { col = c - I; stride = a.B_stride; return a.B; }
-  col = c - I - GN;
-  stride = a.C_stride;
-  return a.C;
+constexpr int kJB = 32;          // tokens per staged block (one MFMA K-step)
+constexpr int kScanThreads = 512;
+constexpr int kStateThreads = 512;
+
+typedef uint16_t u16;
+typedef u16 u16x4 __attribute__((ext_vector_type(4)));
+typedef u16 u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ u16 bits_of(bf16 v) { return __builtin_bit_cast(u16, v); }
+__device__ __forceinline__ bf16 bf_of(u16 v) { return __builtin_bit_cast(bf16, v); }
+__device__ __forceinline__ float f_of(u16 v) { return static_cast<float>(bf_of(v)); }
+
+// fp32 -> (hi, lo) bf16 bit patterns.
+__device__ __forceinline__ void split2(float v, u16& hi, u16& lo) {
+  const bf16 h = from_f32<bf16>(v);
+  hi = bits_of(h);
+  lo = bits_of(from_f32<bf16>(v - static_cast<float>(h)));
 }
 
-// ------------------------------------------------------------------ 1. conv
-template <int W>
-__global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
-  const ChunkEntry ch = a.chunks[blockIdx.x];
-  const SeqEntry sq = a.seqs[ch.seq];
-  const int Cd = a.sh.Cd;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= Cd) return;
-  int64_t col, stride;
-  const void* src = io_col(a, c, col, stride);
-  float win[W - 1];
+// A fragment from bf16 planes in LDS: row `row`, K positions kb + kmap(q, 0..7).
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> lds_frag(const u16* base, int64_t plane, int ld, int row, int kb, int q) {
+  Frag<SPLIT> f;
+  const u16* p = base + row * ld + kb + 4 * q;
+  const u16x4 a = *reinterpret_cast<const u16x4*>(p);
+  const u16x4 b = *reinterpret_cast<const u16x4*>(p + 16);
 #pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
-    const int tau = ch.tau0 - (W - 1) + k;
-    if (tau >= 0) {
-      win[k] = load_any(src, (int64_t)(sq.t0 + tau) * stride + col, a.io_bf16);
-    } else if (sq.has_init) {
-      const int64_t wi = ((int64_t)sq.slot * Cd + c) * (W - 1) + (W - 1 + tau);
-      win[k] = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
-    } else {
-      win[k] = 0.f;
+  for (int e = 0; e < 4; ++e) { f.hi[e] = bf_of(a[e]); f.hi[e + 4] = bf_of(b[e]); }
+  if (SPLIT) {
+    const u16x4 c = *reinterpret_cast<const u16x4*>(p + plane);
+    const u16x4 d = *reinterpret_cast<const u16x4*>(p + plane + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.lo[e] = bf_of(c[e]); f.lo[e + 4] = bf_of(d[e]); }
+  }
+  return f;
+}
+
+// The same fragment's values as fp32 (hi + lo).
+template <bool SPLIT>
+__device__ __forceinline__ void lds_vals(const u16* base, int64_t plane, int ld, int row, int kb, int q, float (&v)[8]) {
+  const u16* p = base + row * ld + kb + 4 * q;
+  const u16x4 a = *reinterpret_cast<const u16x4*>(p);
+  const u16x4 b = *reinterpret_cast<const u16x4*>(p + 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v[e] = f_of(a[e]); v[e + 4] = f_of(b[e]); }
+  if (SPLIT) {
+    const u16x4 c = *reinterpret_cast<const u16x4*>(p + plane);
+    const u16x4 d = *reinterpret_cast<const u16x4*>(p + plane + 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] += f_of(c[e]); v[e + 4] += f_of(d[e]); }
+  }
+}
+
+// Copy rows of 8-element vectors from global bf16 planes into LDS planes.  Row r of the
+// source starts at src + r * src_ld.  Rows at or past valid_rows and columns at or past
+// valid_cols are written as zero and never read from global memory.
+template <int NPL>
+__device__ __forceinline__ void stage_rows(u16* dst, int64_t dst_plane, int dst_ld, const u16* src, int64_t src_plane,
+                                           int64_t src_ld, int rows, int cols, int valid_rows, int valid_cols,
+                                           int tid, int nthreads) {
+  const int vpr = cols / 8;
+  for (int idx = tid; idx < rows * vpr; idx += nthreads) {
+    const int r = idx / vpr, c = (idx % vpr) * 8;
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      const u16* s = src + pl * src_plane + r * src_ld + c;
+      if (r < valid_rows) {
+        if (c + 8 <= valid_cols) {
+          v = *reinterpret_cast<const u16x8*>(s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (c + e < valid_cols) ? s[e] : u16(0);
+        }
+      }
+      u16* d = dst + pl * dst_plane + r * dst_ld + c;
+      *reinterpret_cast<u16x4*>(d) = u16x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<u16x4*>(d + 4) = u16x4{v[4], v[5], v[6], v[7]};
     }
   }
-  float w[W];
+}
+
+// Register prefetch of a staged block: ITEMS 8-element vectors per plane, taken from a
+// (rows x cols) tile exactly as stage_rows does, held in registers until written to LDS.
+template <int NPL, int ITEMS> struct TilePrefetch {
+  u16x8 v[ITEMS][NPL];
+
+  __device__ __forceinline__ void load(const u16* src, int64_t src_plane, int64_t src_ld, int rows, int cols,
+                                       int valid_rows, int valid_cols, int tid, int nthreads) {
+    const int vpr = cols / 8;
 #pragma unroll
-  for (int k = 0; k < W; ++k) w[k] = a.conv_w[(int64_t)c * W + k];
-  const float bias = a.conv_b[c];
-  float* out = a.act + (int64_t)ch.t0 * Cd + c;
-#pragma unroll 8
-  for (int i = 0; i < ch.len; ++i) {
-    const float u = load_any(src, (int64_t)(ch.t0 + i) * stride + col, a.io_bf16);
-    float v = bias;
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * nthreads;
+      const int r = idx / vpr, c = (idx % vpr) * 8;
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) v += w[k] * win[k];
-    v += w[W - 1] * u;
-    out[(int64_t)i * Cd] = silu(v);
+      for (int pl = 0; pl < NPL; ++pl) {
+        u16x8 x = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (idx < rows * vpr && r < valid_rows) {
+          const u16* s = src + pl * src_plane + r * src_ld + c;
+          if (c + 8 <= valid_cols) {
+            x = *reinterpret_cast<const u16x8*>(s);
+          } else {
 #pragma unroll
-    for (int k = 0; k < W - 2; ++k) win[k] = win[k + 1];
-    win[W - 2] = u;
+            for (int e = 0; e < 8; ++e) x[e] = (c + e < valid_cols) ? s[e] : u16(0);
+          }
+        }
+        v[it][pl] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(u16* dst, int64_t dst_plane, int dst_ld, int rows, int cols, int tid,
+                                        int nthreads) const {
+    const int vpr = cols / 8;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * nthreads;
+      if (idx < rows * vpr) {
+        const int r = idx / vpr, c = (idx % vpr) * 8;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) {
+          u16* d = dst + pl * dst_plane + r * dst_ld + c;
+          const u16x8 x = v[it][pl];
+          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+        }
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------ 1. conv
+// Workgroup per (chunk, 64 channels), 256 threads: thread (octet o, token group tg) convolves
+// channels 8o .. 8o+7 over its rows with 16-byte input loads, into an fp32 LDS tile; the tile is
+// then written as operand planes: x transposed per head, B both ways, C token-major.
+constexpr int kConvCB = 64;
+constexpr int kConvLD = kConvCB + 1;
+constexpr int kConvLdsBytes = 256 * kConvLD * 4;
+
+template <int W, bool SPLIT>
+__global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
+  constexpr int CB = kConvCB;
+  extern __shared__ __align__(16) unsigned char conv_smem[];
+  float* const s_out = reinterpret_cast<float*>(conv_smem);
+  const ChunkEntry ch = a.chunks[blockIdx.x];
+  const SeqEntry sq = a.seqs[ch.seq];
+  const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
+  const int Q = a.Q, len = ch.len;
+  const int c0 = blockIdx.y * CB;
+  const int tid = threadIdx.x;
+  const int oc = tid % (CB / 8), tg = tid / (CB / 8);   // 8 octets x 32 token groups
+  const int c = c0 + 8 * oc;
+  if (c < Cd) {
+    const void* src;
+    int64_t col, stride;
+    if (c < I) { src = a.x; col = c; stride = a.x_stride; }
+    else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
+    else { src = a.C; col = c - I - GN; stride = a.C_stride; }
+    const int per = (len + 31) / 32;
+    const int j0 = tg * per, j1 = min(len, j0 + per);
+    if (j0 < j1) {
+      float win[W - 1][8];
+#pragma unroll
+      for (int k = 0; k < W - 1; ++k) {
+        const int tau = ch.tau0 + j0 - (W - 1) + k;   // offset inside the sequence
+        if (tau >= 0) {
+          load8_any(src, (int64_t)(sq.t0 + tau) * stride + col, a.io_bf16, win[k]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float v = 0.f;
+            if (sq.has_init) {
+              const int64_t wi = ((int64_t)sq.slot * Cd + c + e) * (W - 1) + (W - 1 + tau);
+              v = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
+            }
+            win[k][e] = v;
+          }
+        }
+      }
+      float w[8][W], bias[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[e][k] = a.conv_w[(int64_t)(c + e) * W + k];
+        bias[e] = a.conv_b[c + e];
+      }
+      for (int j = j0; j < j1; j += 4) {
+        float u[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (j + r < j1) load8_any(src, (int64_t)(ch.t0 + j + r) * stride + col, a.io_bf16, u[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (j + r < j1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float v = bias[e];
+#pragma unroll
+              for (int k = 0; k < W - 1; ++k) v += w[e][k] * win[k][e];
+              v += w[e][W - 1] * u[r][e];
+              s_out[(j + r) * kConvLD + 8 * oc + e] = silu(v);
+            }
+#pragma unroll
+            for (int k = 0; k < W - 2; ++k)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) win[k][e] = win[k + 1][e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[W - 2][e] = u[r][e];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int NPL = SPLIT ? 2 : 1;
+  const int64_t chunk = blockIdx.x;
+  // channel-major outputs (x transposed, B transposed): thread per (channel, 8 rows)
+  const int vpr = (len + 7) / 8;
+  for (int idx = tid; idx < CB * vpr; idx += 256) {
+    const int ccl = idx / vpr, j = (idx % vpr) * 8;
+    const int cc = c0 + ccl;
+    if (cc >= I + GN) continue;
+    u16* dst;
+    int64_t pstride;
+    if (cc < I) {
+      const int h = cc / P, p = cc % P;
+      dst = a.xT + ((chunk * H + h) * P + p) * Q + j;
+      pstride = a.xT_plane;
+    } else {
+      const int g = (cc - I) / N, n = (cc - I) % N;
+      dst = a.Bt + ((chunk * G + g) * N + n) * Q + j;
+      pstride = a.Bt_plane;
+    }
+    u16 hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (j + e < len) ? s_out[(j + e) * kConvLD + ccl] : 0.f;
+      if (SPLIT) split2(v, hi[e], lo[e]);
+      else hi[e] = bits_of(from_f32<bf16>(v));
+    }
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      const u16* hv = pl ? lo : hi;
+      if (j + 8 <= len) {
+        *reinterpret_cast<u16x8*>(dst + pl * pstride) = u16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+      } else {
+        for (int e = 0; e < 8 && j + e < len; ++e) dst[pl * pstride + e] = hv[e];
+      }
+    }
+  }
+  // token-major outputs (B rows, C rows): thread per (row, 8 channels)
+  for (int idx = tid; idx < len * (CB / 8); idx += 256) {
+    const int j = idx / (CB / 8), cc = c0 + (idx % (CB / 8)) * 8;
+    if (cc < I || cc >= Cd) continue;
+    u16 hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = s_out[j * kConvLD + (cc - c0) + e];
+      if (SPLIT) split2(v, hi[e], lo[e]);
+      else hi[e] = bits_of(from_f32<bf16>(v));
+    }
+    u16* dst;
+    int64_t pstride;
+    if (cc < I + GN) {
+      dst = a.Br + (chunk * Q + j) * GN + (cc - I);
+      pstride = a.Br_plane;
+    } else {
+      dst = a.Cr + (chunk * Q + j) * GN + (cc - I - GN);
+      pstride = a.Cr_plane;
+    }
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      const u16* hv = pl ? lo : hi;
+      *reinterpret_cast<u16x8*>(dst + pl * pstride) = u16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+    }
   }
 }
 
@@ -113,293 +345,463 @@ __global__ __launch_bounds__(256) void dt_kernel(PrefillParams a) {
   }
 }
 
-// ------------------------------------------------------------------ 3. chunk states
-// Workgroup per (chunk, head).  S[p][n] = sum_j (w_j x_j[p]) B_j[n] with
-// w_j = exp(a_last - a_j) Delta_j.  32-token blocks of x (transposed, weighted)
-// and B (transposed) are staged in LDS; wave w owns p-tiles w, w+4, ...
-template <bool SPLIT, int P, int N>
-__global__ __launch_bounds__(256) void chunk_state_kernel(PrefillParams a) {
-  constexpr int PT = P / 16, NT = N / 16;
-  constexpr int PTW = (PT + 3) / 4;   // p-tiles per wave
-  constexpr int LDJ = 36;             // row pitch (floats) of the transposed tiles
-  __shared__ float sX[P * LDJ];
-  __shared__ float sB[N * LDJ];
-  __shared__ float sW[256];
+// State tiles (P/16 x N/16 of 16x16) spread over the 8 waves of a workgroup.
+template <int P, int N> struct StateTiles {
+  static constexpr int NT = N / 16;
+  static constexpr int TOTAL = (P / 16) * NT;
+  static constexpr int PER_WAVE = (TOTAL + 7) / 8;
+};
 
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkEntry ch = a.chunks[c];
-  const int I = a.sh.I, Cd = a.sh.Cd, G = a.sh.G;
-  const int g = h / (a.sh.H / G);
+// ------------------------------------------------------------------ 3. segment end states
+template <bool SPLIT, int P, int N>
+__global__ __launch_bounds__(kStateThreads) void seg_state_kernel(PrefillParams a) {
+  constexpr int NPL = SPLIT ? 2 : 1;
+  constexpr int LDX = kJB + 4;   // 18 dwords: conflict-free fragment rows
+  typedef StateTiles<P, N> ST;
+  __shared__ u16 sXT[NPL * P * LDX];
+  __shared__ u16 sBT[NPL * N * LDX];
+  __shared__ float sW[256];
+  const SegEntry sg = a.segs[blockIdx.x];
+  if (sg.is_last) return;
+  const int h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
+  const int g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t T = a.total_tokens;
-  const float* dAh = a.dA + (int64_t)h * T + ch.t0;
-  const float* dh = a.delta + (int64_t)h * T + ch.t0;
-  const float alast = dAh[ch.len - 1];
-  for (int j = tid; j < 256; j += 256) sW[j] = j < ch.len ? __expf(alast - dAh[j]) * dh[j] : 0.f;
-
-  floatx4 acc[PTW][NT];
+  floatx4 acc[ST::PER_WAVE];
 #pragma unroll
-  for (int t = 0; t < PTW; ++t)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[t][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int jb = 0; jb < ch.len; jb += 32) {
+  for (int k = 0; k < ST::PER_WAVE; ++k) acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float logdecay = 0.f;
+  for (int c = sg.chunk0; c < sg.chunk0 + sg.nchunk; ++c) {
+    const ChunkEntry ch = a.chunks[c];
+    const int len = ch.len;
+    const float* dAh = a.dA + (int64_t)h * T + ch.t0;
+    const float* dh = a.delta + (int64_t)h * T + ch.t0;
+    const float alast = dAh[len - 1];
+    logdecay += alast;
     __syncthreads();
-    // stage x^T (weighted) and B^T for rows jb .. jb+31
-    for (int idx = tid; idx < 32 * (P / 4); idx += 256) {
-      const int jj = idx / (P / 4), p4 = (idx % (P / 4)) * 4;
-      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (jb + jj < ch.len) {
-        v = *reinterpret_cast<const floatx4*>(a.act + (int64_t)(ch.t0 + jb + jj) * Cd + h * P + p4);
-        v *= sW[jb + jj];
-      }
+    for (int j = tid; j < 256; j += kStateThreads) sW[j] = j < len ? __expf(alast - dAh[j]) * dh[j] : 0.f;
+    const float decay = __expf(alast);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sX[(p4 + e) * LDJ + jj] = v[e];
-    }
-    for (int idx = tid; idx < 32 * (N / 4); idx += 256) {
-      const int jj = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
-      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (jb + jj < ch.len)
-        v = *reinterpret_cast<const floatx4*>(a.act + (int64_t)(ch.t0 + jb + jj) * Cd + I + g * N + n4);
+    for (int k = 0; k < ST::PER_WAVE; ++k) acc[k] *= decay;
+    for (int jb = 0; jb < len; jb += kJB) {
+      __syncthreads();
+      stage_rows<NPL>(sXT, P * LDX, LDX, a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kJB,
+                      P, len - jb, tid, kStateThreads);
+      stage_rows<NPL>(sBT, N * LDX, LDX, a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kJB,
+                      N, len - jb, tid, kStateThreads);
+      __syncthreads();
+      int cur_pt = -1;
+      Frag<SPLIT> fa;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sB[(n4 + e) * LDJ + jj] = v[e];
-    }
-    __syncthreads();
+      for (int m = 0; m < ST::PER_WAVE; ++m) {
+        const int k = wave * ST::PER_WAVE + m;
+        if (k < ST::TOTAL) {
+          const int pt = k / ST::NT, nt = k % ST::NT;
+          if (pt != cur_pt) {
+            float v[8];
+            lds_vals<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, 0, q, v);
 #pragma unroll
-    for (int t = 0; t < PTW; ++t) {
-      const int pt = wave + 4 * t;
-      if (pt < PT) {
-        float av[8];
-        const floatx4 a0 = *reinterpret_cast<const floatx4*>(&sX[(pt * 16 + l16) * LDJ + 4 * q]);
-        const floatx4 a1 = *reinterpret_cast<const floatx4*>(&sX[(pt * 16 + l16) * LDJ + 16 + 4 * q]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { av[e] = a0[e]; av[e + 4] = a1[e]; }
-        const Frag<SPLIT> fa = make_frag<SPLIT>(av);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float bv[8];
-          const floatx4 b0 = *reinterpret_cast<const floatx4*>(&sB[(nt * 16 + l16) * LDJ + 4 * q]);
-          const floatx4 b1 = *reinterpret_cast<const floatx4*>(&sB[(nt * 16 + l16) * LDJ + 16 + 4 * q]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { bv[e] = b0[e]; bv[e + 4] = b1[e]; }
-          acc[t][nt] = mma<SPLIT>(fa, make_frag<SPLIT>(bv), acc[t][nt]);
+            for (int e = 0; e < 8; ++e) v[e] *= sW[jb + kmap(q, e)];
+            fa = make_frag<SPLIT>(v);
+            cur_pt = pt;
+          }
+          const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, nt * 16 + l16, 0, q);
+          acc[m] = mma<SPLIT>(fa, fb, acc[m]);
         }
       }
     }
   }
-  // acc[t][nt] lane holds S[p = pt*16 + 4q + r][n = nt*16 + l16]
-  float* out = a.states + ((int64_t)c * a.sh.H + h) * P * N;
+  float* out = a.seg_state + ((int64_t)blockIdx.x * H + h) * P * N;
 #pragma unroll
-  for (int t = 0; t < PTW; ++t) {
-    const int pt = wave + 4 * t;
-    if (pt < PT) {
+  for (int m = 0; m < ST::PER_WAVE; ++m) {
+    const int k = wave * ST::PER_WAVE + m;
+    if (k < ST::TOTAL) {
+      const int pt = k / ST::NT, nt = k % ST::NT;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) out[(pt * 16 + 4 * q + r) * N + nt * 16 + l16] = acc[t][nt][r];
+      for (int r = 0; r < 4; ++r) out[(pt * 16 + 4 * q + r) * N + nt * 16 + l16] = acc[m][r];
     }
   }
+  if (tid == 0) a.seg_decay[(int64_t)blockIdx.x * H + h] = logdecay;
 }
 
-// ------------------------------------------------------------------ 4. state passing
-// Thread per 4 state elements of one head of one sequence, walking its chunks
-// in order, eight chunk states in flight.
+// ------------------------------------------------------------------ 4. scan over segments
 template <typename TS>
-__device__ __forceinline__ void store_state4(void* pool, int64_t i, const floatx4& v) {
-  TS* p = static_cast<TS*>(pool) + i;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = from_f32<TS>(v[e]);
-}
-
-template <typename TS>
-__global__ __launch_bounds__(256) void state_pass_kernel(PrefillParams a) {
+__global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
   const SeqEntry sq = a.seqs[blockIdx.x];
-  if (sq.nchunk == 0) return;
-  const int h = blockIdx.y;
+  if (sq.nseg == 0) return;
+  const int h = blockIdx.y, H = a.sh.H;
   const int PN = a.sh.P * a.sh.N;
   const int e4 = (blockIdx.z * 256 + threadIdx.x) * 4;
   if (e4 >= PN) return;
-  const int64_t T = a.total_tokens;
   const int64_t head_off = (int64_t)h * PN + e4;
-  const int64_t slot_stride = (int64_t)a.sh.H * PN;
   floatx4 hs = floatx4{0.f, 0.f, 0.f, 0.f};
   if (sq.has_init) {
-    const TS* src = static_cast<const TS*>(a.ssm) + sq.slot * slot_stride + head_off;
+    const TS* src = static_cast<const TS*>(a.ssm) + (int64_t)sq.slot * H * PN + head_off;
 #pragma unroll
     for (int e = 0; e < 4; ++e) hs[e] = to_f32(src[e]);
   }
   constexpr int D = 8;
-  for (int c0 = 0; c0 < sq.nchunk; c0 += D) {
+  for (int s0 = 0; s0 < sq.nseg; s0 += D) {
     floatx4 sc[D];
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      if (c0 + k < sq.nchunk)
-        sc[k] = *reinterpret_cast<const floatx4*>(a.states + (int64_t)(sq.chunk0 + c0 + k) * a.sh.H * PN + head_off);
+      const int s = sq.seg0 + s0 + k;
+      if (s0 + k < sq.nseg && !a.segs[s].is_last)
+        sc[k] = *reinterpret_cast<const floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off);
     }
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      if (c0 + k < sq.nchunk) {
-        const int c = sq.chunk0 + c0 + k;
-        const ChunkEntry ch = a.chunks[c];
-        *reinterpret_cast<floatx4*>(a.states + (int64_t)c * a.sh.H * PN + head_off) = hs;
-        const float decay = __expf(a.dA[(int64_t)h * T + ch.t0 + ch.len - 1]);
-        hs = decay * hs + sc[k];
-        if (ch.ckpt_slot >= 0) store_state4<TS>(a.ssm, ch.ckpt_slot * slot_stride + head_off, hs);
+      if (s0 + k < sq.nseg) {
+        const int s = sq.seg0 + s0 + k;
+        *reinterpret_cast<floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off) = hs;
+        if (!a.segs[s].is_last) hs = __expf(a.seg_decay[(int64_t)s * H + h]) * hs + sc[k];
       }
     }
   }
-  store_state4<TS>(a.ssm, sq.slot * slot_stride + head_off, hs);
 }
 
-// ------------------------------------------------------------------ 5. chunk outputs
-// Workgroup per (chunk, head, 64-row block); wave w owns rows i0 + 16w .. +15.
-template <bool SPLIT, int P, int N>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillParams a) {
-  constexpr int PT = P / 16;
-  constexpr int NK = (N + 31) / 32;    // K-steps over the state dimension
-  constexpr int LDB = N + 4;           // row pitch of the staged B block
-  constexpr int LDJ = 36;              // row pitch of the staged x^T block
-  __shared__ float sB[32 * LDB];
-  __shared__ float sX[P * LDJ];
-  __shared__ float sdA[256];
-  __shared__ float sD[256];
+// ------------------------------------------------------------------ 5. segment walk
+// Tokens per staged block in the segment walk: two K-steps with single bf16 planes, one with
+// hi/lo planes (the register prefetch of a block doubles with two planes).
+template <bool SPLIT> struct ScanBlock { static constexpr int JB = SPLIT ? 32 : 64; };
 
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkEntry ch = a.chunks[c];
-  const int rb0 = blockIdx.z * 64;
-  if (rb0 >= ch.len) return;
-  const int I = a.sh.I, Cd = a.sh.Cd, G = a.sh.G;
-  const int g = h / (a.sh.H / G);
+template <bool SPLIT, int P, int N> struct ScanLds {
+  static constexpr int kSJB = ScanBlock<SPLIT>::JB;
+  static constexpr int NPL = SPLIT ? 2 : 1;
+  // row pitches of 2 (mod 32) dwords: the 16 rows of a fragment read land in distinct banks
+  static constexpr int LDH = N + 4;      // state operand rows [p][n]
+  static constexpr int LDB = N + 4;      // B rows [j][n]
+  static constexpr int LDX = kSJB + 4;   // transposed blocks [p or n][j]
+  static constexpr int H_OFF = 0;
+  static constexpr int BR_OFF = H_OFF + NPL * P * LDH;
+  static constexpr int XT_OFF = BR_OFF + NPL * kSJB * LDB;
+  static constexpr int BT_OFF = XT_OFF + NPL * P * LDX;
+  static constexpr int U16_END = BT_OFF + NPL * N * LDX;
+  static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes
+  static constexpr int BYTES = F_OFF + 4 * 256 * 4;
+  // staging vectors per thread
+  static constexpr int IT_BR = (kSJB * (N / 8) + kScanThreads - 1) / kScanThreads;
+  static constexpr int IT_XT = (P * (kSJB / 8) + kScanThreads - 1) / kScanThreads;
+  static constexpr int IT_BT = (N * (kSJB / 8) + kScanThreads - 1) / kScanThreads;
+};
+
+template <typename TS>
+__device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N, int p, int n, const floatx4& v) {
+  TS* d = static_cast<TS*>(pool) + base;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[(int64_t)(p + r) * N + n] = from_f32<TS>(v[r]);
+}
+
+template <bool SPLIT, int P, int N> struct ScanPrefetch {
+  typedef ScanLds<SPLIT, P, N> L;
+  static constexpr int kSJB = L::kSJB;
+  TilePrefetch<L::NPL, L::IT_BR> br;
+  TilePrefetch<L::NPL, L::IT_XT> xt;
+  TilePrefetch<L::NPL, L::IT_BT> bt;
+
+  __device__ __forceinline__ void load(const PrefillParams& a, int c, int jb, int len, int h, int g, int tid) {
+    const int Q = a.Q, H = a.sh.H, G = a.sh.G, GN = G * N;
+    br.load(a.Br + ((int64_t)c * Q + jb) * GN + g * N, a.Br_plane, GN, kSJB, N, len - jb, N, tid, kScanThreads);
+    xt.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kSJB, P, len - jb, tid, kScanThreads);
+    bt.load(a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kSJB, N, len - jb, tid, kScanThreads);
+  }
+  __device__ __forceinline__ void store(u16* sBr, u16* sXT, u16* sBT, int tid) const {
+    br.store(sBr, kSJB * L::LDB, L::LDB, kSJB, N, tid, kScanThreads);
+    xt.store(sXT, P * L::LDX, L::LDX, P, kSJB, tid, kScanThreads);
+    bt.store(sBT, N * L::LDX, L::LDX, N, kSJB, tid, kScanThreads);
+  }
+};
+
+template <bool SPLIT, int P, int N>
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(PrefillParams a) {
+  typedef ScanLds<SPLIT, P, N> L;
+  typedef StateTiles<P, N> ST;
+  constexpr int kSJB = L::kSJB;
+  constexpr int NPL = L::NPL;
+  constexpr int PT = P / 16;
+  constexpr int NK = N / 32 > 0 ? N / 32 : 1;   // K-steps over the state dimension
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  u16* const smem = reinterpret_cast<u16*>(smem_raw);
+  u16* const sH = smem + L::H_OFF;
+  u16* const sBr = smem + L::BR_OFF;
+  u16* const sXT = smem + L::XT_OFF;
+  u16* const sBT = smem + L::BT_OFF;
+  float* const sA = reinterpret_cast<float*>(smem_raw + L::F_OFF);
+  float* const sD = sA + 256;
+  float* const sW = sD + 256;
+  float* const sCw = sW + 256;   // exp(a_ref - a_j) Delta_j, a_ref = cumsum at the last token of j's K-step
+
+  const SegEntry sg = a.segs[blockIdx.x];
+  const SeqEntry sq = a.seqs[sg.seq];
+  const int h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
+  const int GN = G * N;
+  const int g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const int i0 = rb0 + wave * 16;
   const int64_t T = a.total_tokens;
-  const int jend = min(rb0 + 64, ch.len);
-  for (int j = tid; j < 256; j += 256) {
-    sdA[j] = j < ch.len ? a.dA[(int64_t)h * T + ch.t0 + j] : 0.f;
-    sD[j] = j < ch.len ? a.delta[(int64_t)h * T + ch.t0 + j] : 0.f;
-  }
+  const float Dh = a.D[h];
+  const int64_t slot_elems = (int64_t)H * P * N;
 
-  // C rows of this wave as fragments (lane: row i0 + l16, K positions kmap)
-  const int irow = i0 + l16;
-  const bool row_ok = irow < ch.len;
-  const float* crow = a.act + (int64_t)(ch.t0 + irow) * Cd + I + G * N + g * N;
-  Frag<SPLIT> cf[NK];
+  // running state in accumulator layout: tile (pt, nt), lane holds h[pt*16 + 4q + r][nt*16 + l16]
+  floatx4 hacc[ST::PER_WAVE];
+  {
+    const float* hin = a.seg_state + ((int64_t)blockIdx.x * H + h) * P * N;
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    float v[8];
+    for (int m = 0; m < ST::PER_WAVE; ++m) {
+      const int k = wave * ST::PER_WAVE + m;
+      hacc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (k < ST::TOTAL) {
+        const int pt = k / ST::NT, nt = k % ST::NT;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int n = ks * 32 + half * 16 + 4 * q;
-      floatx4 t = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (row_ok && n < N) t = *reinterpret_cast<const floatx4*>(crow + n);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[half * 4 + e] = t[e];
-    }
-    cf[ks] = make_frag<SPLIT>(v);
-  }
-
-  // contribution of the state entering the chunk: acc[pt] = C h_prev^T
-  floatx4 acc[PT];
-  const float* hp = a.states + ((int64_t)c * a.sh.H + h) * P * N;
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      float v[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int n = ks * 32 + half * 16 + 4 * q;
-        floatx4 t = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (n < N) t = *reinterpret_cast<const floatx4*>(hp + (pt * 16 + l16) * N + n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[half * 4 + e] = t[e];
+        for (int r = 0; r < 4; ++r) hacc[m][r] = hin[(pt * 16 + 4 * q + r) * N + nt * 16 + l16];
       }
-      acc[pt] = mma<SPLIT>(cf[ks], make_frag<SPLIT>(v), acc[pt]);
     }
   }
-  __syncthreads();   // sdA ready
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + 4 * q + r;
-    const float s = i < ch.len ? __expf(sdA[i]) : 0.f;
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) acc[pt][r] *= s;
-  }
+  // row tiles of this wave: wave and 15 - wave (balanced causal work for Q = 256)
+  const int nrt = Q / 16;
+  const int rts[2] = {wave, 15 - wave};
+  const int c_end = sg.chunk0 + sg.nchunk;
 
-  const float dAi = row_ok ? sdA[irow] : 0.f;
-  for (int jb = 0; jb < jend; jb += 32) {
-    __syncthreads();
-    for (int idx = tid; idx < 32 * (N / 4); idx += 256) {
-      const int jj = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
-      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (jb + jj < ch.len)
-        v = *reinterpret_cast<const floatx4*>(a.act + (int64_t)(ch.t0 + jb + jj) * Cd + I + g * N + n4);
-      *reinterpret_cast<floatx4*>(&sB[jj * LDB + n4]) = v;
+  ScanPrefetch<SPLIT, P, N> pf;
+  pf.load(a, sg.chunk0, 0, a.chunks[sg.chunk0].len, h, g, tid);
+
+  for (int c = sg.chunk0; c < c_end; ++c) {
+    const ChunkEntry ch = a.chunks[c];
+    const int len = ch.len;
+    const float* dAh = a.dA + (int64_t)h * T + ch.t0;
+    const float* dh = a.delta + (int64_t)h * T + ch.t0;
+    const float alast = dAh[len - 1];
+    __syncthreads();   // previous chunk's LDS reads are done
+    for (int j = tid; j < 256; j += kScanThreads) {
+      const bool ok = j < len;
+      const float aj = ok ? dAh[j] : 0.f, dj = ok ? dh[j] : 0.f;
+      const int jr = min((j | 31), len - 1);   // last token of j's K-step
+      sA[j] = aj;
+      sD[j] = dj;
+      sW[j] = ok ? __expf(alast - aj) * dj : 0.f;
+      sCw[j] = ok ? __expf(dAh[jr] - aj) * dj : 0.f;
     }
-    for (int idx = tid; idx < 32 * (P / 4); idx += 256) {
-      const int jj = idx / (P / 4), p4 = (idx % (P / 4)) * 4;
-      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (jb + jj < ch.len)
-        v = *reinterpret_cast<const floatx4*>(a.act + (int64_t)(ch.t0 + jb + jj) * Cd + h * P + p4);
+    // state entering the chunk -> operand planes [p][n]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sX[(p4 + e) * LDJ + jj] = v[e];
-    }
-    __syncthreads();
-    if (jb <= i0 + 15 && i0 < ch.len) {
-      // G^T tiles: lane holds G[i0 + l16][jb + 16 jt + 4q + r]
-      floatx4 gt[2];
+    for (int m = 0; m < ST::PER_WAVE; ++m) {
+      const int k = wave * ST::PER_WAVE + m;
+      if (k < ST::TOTAL) {
+        const int pt = k / ST::NT, nt = k % ST::NT;
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        gt[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-          float v[8];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int n = ks * 32 + half * 16 + 4 * q;
-            floatx4 t = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (n < N) t = *reinterpret_cast<const floatx4*>(&sB[(jt * 16 + l16) * LDB + n]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[half * 4 + e] = t[e];
-          }
-          gt[jt] = mma<SPLIT>(make_frag<SPLIT>(v), cf[ks], gt[jt]);
+        for (int r = 0; r < 4; ++r) {
+          const int idx = (pt * 16 + 4 * q + r) * L::LDH + nt * 16 + l16;
+          u16 hi, lo = 0;
+          if (SPLIT) split2(hacc[m][r], hi, lo);
+          else hi = bits_of(from_f32<bf16>(hacc[m][r]));
+          sH[idx] = hi;
+          if (SPLIT) sH[P * L::LDH + idx] = lo;
         }
       }
-      float m[8];
+    }
+    // C rows of this wave's row tiles as fragments (global loads issued before the barrier)
+    Frag<SPLIT> cf[2][NK];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = jb + (e >> 2) * 16 + 4 * q + (e & 3);
-        m[e] = (row_ok && j <= irow) ? gt[e >> 2][e & 3] * __expf(dAi - sdA[j]) * sD[j] : 0.f;
-      }
-      const Frag<SPLIT> fm = make_frag<SPLIT>(m);
+    for (int t = 0; t < 2; ++t) {
+      const int rt = rts[t];
+      const int i = rt * 16 + l16;
+      if (!(rt < nrt && rt * 16 < len)) continue;
+      const u16* crow = a.Cr + ((int64_t)c * Q + i) * GN + g * N;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        float v[8];
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(&sX[(pt * 16 + l16) * LDJ + 4 * q]);
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(&sX[(pt * 16 + l16) * LDJ + 16 + 4 * q]);
+      for (int ks = 0; ks < NK; ++ks) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] = x0[e]; v[e + 4] = x1[e]; }
-        acc[pt] = mma<SPLIT>(fm, make_frag<SPLIT>(v), acc[pt]);
+        for (int pl = 0; pl < NPL; ++pl) {
+          u16x4 lo4 = u16x4{0, 0, 0, 0}, hi4 = u16x4{0, 0, 0, 0};
+          const int n = ks * 32 + 4 * q;
+          if (i < len) {
+            if (n < N) lo4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n);
+            if (n + 16 < N) hi4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n + 16);
+          }
+          bf16x8 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { f[e] = bf_of(lo4[e]); f[e + 4] = bf_of(hi4[e]); }
+          if (pl == 0) cf[t][ks].hi = f;
+          else cf[t][ks].lo = f;
+        }
       }
     }
-  }
+    __syncthreads();
 
-  // y = acc + D x, gated; lane holds rows i0 + 4q + r, column pt*16 + l16
-  const float Dh = a.D[h];
+    // the entering-state term
+    floatx4 acc[2][PT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + 4 * q + r;
-    if (i < ch.len) {
-      const int64_t row = ch.t0 + i;
+    for (int t = 0; t < 2; ++t) {
+      const int rt = rts[t];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[t][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (!(rt < nrt && rt * 16 < len)) continue;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const int col = h * P + pt * 16 + l16;
-        const float xv = a.act[row * Cd + col];
-        const float zv = load_any(a.z, row * a.z_stride + col, a.io_bf16);
-        store_any(a.y, row * a.y_stride + col, (acc[pt][r] + Dh * xv) * silu(zv), a.y_bf16);
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          Frag<SPLIT> fh = lds_frag<SPLIT>(sH, P * L::LDH, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+          if (N < 32) {   // upper K half is padding
+#pragma unroll
+            for (int e = 4; e < 8; ++e) { fh.hi[e] = bf_of(0); if (SPLIT) fh.lo[e] = bf_of(0); }
+          }
+          acc[t][pt] = mma<SPLIT>(cf[t][ks], fh, acc[t][pt]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = rt * 16 + 4 * q + r;
+        const float sc = ii < len ? __expf(sA[ii]) : 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[t][pt][r] *= sc;
+      }
+    }
+
+    // the chunk's state update starts from the decayed entering state
+    const float decay = __expf(alast);
+#pragma unroll
+    for (int m = 0; m < ST::PER_WAVE; ++m) hacc[m] *= decay;
+
+    for (int jb = 0; jb < len; jb += kSJB) {
+      __syncthreads();   // all reads of the previous block are done
+      pf.store(sBr, sXT, sBT, tid);
+      __syncthreads();
+      // prefetch the next block (next chunk's first block at the end of this chunk)
+      if (jb + kSJB < len) pf.load(a, c, jb + kSJB, len, h, g, tid);
+      else if (c + 1 < c_end) pf.load(a, c + 1, 0, a.chunks[c + 1].len, h, g, tid);
+
+#pragma unroll
+      for (int kb = 0; kb < kSJB; kb += 32) {
+        const int jk = jb + kb;   // first token of this K-step
+        if (jk >= len) break;
+        // diagonal blocks: G^T tiles -> M -> (M o L) X  (D x rides on the diagonal of M).
+        // Each B-row and x fragment is read from LDS once and used for both row tiles.
+        bool act[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) act[t] = rts[t] < nrt && rts[t] * 16 < len && jk <= rts[t] * 16 + 15;
+        if (act[0] || act[1]) {
+          floatx4 gt[2][2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) gt[t][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const bool need0 = act[0] && jk + 16 * jt <= rts[0] * 16 + 15;
+            const bool need1 = act[1] && jk + 16 * jt <= rts[1] * 16 + 15;
+            if (!(need0 || need1)) continue;
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+              Frag<SPLIT> fb = lds_frag<SPLIT>(sBr, kSJB * L::LDB, L::LDB, kb + jt * 16 + l16,
+                                               N >= 32 ? ks * 32 : 0, q);
+              if (N < 32) {
+#pragma unroll
+                for (int e = 4; e < 8; ++e) { fb.hi[e] = bf_of(0); if (SPLIT) fb.lo[e] = bf_of(0); }
+              }
+              if (need0) gt[0][jt] = mma<SPLIT>(fb, cf[0][ks], gt[0][jt]);
+              if (need1) gt[1][jt] = mma<SPLIT>(fb, cf[1][ks], gt[1][jt]);
+            }
+          }
+          // decay mask.  Below the diagonal (every token of the K-step precedes every row),
+          // exp(a_i - a_j) = exp(a_i - a_ref) exp(a_ref - a_j) with a_ref the cumsum at the
+          // K-step's last token: both factors are <= 1, one exp per row and a column table.
+          // On the diagonal the exponent is taken directly.
+          Frag<SPLIT> fm[2];
+          float cw[8];
+          {
+            const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
+            const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
+          }
+          const float aref = sA[min(jk + 31, len - 1)];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = rts[t] * 16 + l16;
+            const bool row_ok = act[t] && i < len;
+            const float ai = row_ok ? sA[i] : 0.f;
+            float mv[8];
+            if (jk + 31 < rts[t] * 16) {
+              const float rf = row_ok ? __expf(ai - aref) : 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) mv[e] = gt[t][e >> 2][e & 3] * rf * cw[e];
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int j = jk + kmap(q, e);
+                float v = 0.f;
+                if (row_ok && j <= i) {
+                  v = gt[t][e >> 2][e & 3] * __expf(ai - sA[j]) * sD[j];
+                  if (j == i) v += Dh;
+                }
+                mv[e] = v;
+              }
+            }
+            fm[t] = make_frag<SPLIT>(mv);
+          }
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            const Frag<SPLIT> fx = lds_frag<SPLIT>(sXT, P * L::LDX, L::LDX, pt * 16 + l16, kb, q);
+            if (act[0]) acc[0][pt] = mma<SPLIT>(fm[0], fx, acc[0][pt]);
+            if (act[1]) acc[1][pt] = mma<SPLIT>(fm[1], fx, acc[1][pt]);
+          }
+        }
+        // state update: h += (w x)^T B over this K-step's tokens
+        int cur_pt = -1;
+        Frag<SPLIT> fa;
+#pragma unroll
+        for (int m = 0; m < ST::PER_WAVE; ++m) {
+          const int k = wave * ST::PER_WAVE + m;
+          if (k < ST::TOTAL) {
+            const int pt = k / ST::NT, nt = k % ST::NT;
+            if (pt != cur_pt) {
+              float v[8];
+              lds_vals<SPLIT>(sXT, P * L::LDX, L::LDX, pt * 16 + l16, kb, q, v);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] *= sW[jk + kmap(q, e)];
+              fa = make_frag<SPLIT>(v);
+              cur_pt = pt;
+            }
+            const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * L::LDX, L::LDX, nt * 16 + l16, kb, q);
+            hacc[m] = mma<SPLIT>(fa, fb, hacc[m]);
+          }
+        }
+      }
+    }
+
+    // outputs: y = acc gated by SiLU(z); lane holds rows rt*16 + 4q + r, columns pt*16 + l16
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int rt = rts[t];
+      if (rt >= nrt || rt * 16 >= len) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = rt * 16 + 4 * q + r;
+        if (ii < len) {
+          const int64_t row = ch.t0 + ii;
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            const int col = h * P + pt * 16 + l16;
+            const float zv = load_any(a.z, row * a.z_stride + col, a.io_bf16);
+            store_any(a.y, row * a.y_stride + col, acc[t][pt][r] * silu(zv), a.y_bf16);
+          }
+        }
+      }
+    }
+
+    // checkpoint and final states, rounded to the state dtype
+    const int dsts[2] = {ch.ckpt_slot, ch.is_last ? sq.slot : -1};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (dsts[d] < 0) continue;
+      const int64_t base = (int64_t)dsts[d] * slot_elems + (int64_t)h * P * N;
+#pragma unroll
+      for (int m = 0; m < ST::PER_WAVE; ++m) {
+        const int k = wave * ST::PER_WAVE + m;
+        if (k < ST::TOTAL) {
+          const int pt = k / ST::NT, nt = k % ST::NT;
+          if (a.ssm_bf16) store_state_tile<bf16>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, hacc[m]);
+          else store_state_tile<float>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, hacc[m]);
+        }
       }
     }
   }
@@ -410,11 +812,14 @@ template <int W>
 __global__ __launch_bounds__(256) void window_kernel(PrefillParams a) {
   const WindowEntry we = a.windows[blockIdx.x];
   const SeqEntry sq = a.seqs[we.seq];
-  const int Cd = a.sh.Cd;
+  const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N;
   const int c = blockIdx.y * 256 + threadIdx.x;
   if (c >= Cd) return;
+  const void* src;
   int64_t col, stride;
-  const void* src = io_col(a, c, col, stride);
+  if (c < I) { src = a.x; col = c; stride = a.x_stride; }
+  else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
+  else { src = a.C; col = c - I - GN; stride = a.C_stride; }
   float v[W - 1];
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) {
@@ -437,59 +842,78 @@ __global__ __launch_bounds__(256) void window_kernel(PrefillParams a) {
 }
 
 // ------------------------------------------------------------------ launch
+// Allow `bytes` of dynamic LDS for a kernel (idempotent; called before each launch).
+static hipError_t set_lds_attr(const void* fn, int bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 template <bool SPLIT, int P, int N>
-static void launch_mfma(const PrefillParams& a, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N>), dim3(a.num_chunks, a.sh.H), dim3(256), 0, s, a);
+static hipError_t launch_segments(const PrefillParams& a, hipStream_t s) {
+  hipLaunchKernelGGL((seg_state_kernel<SPLIT, P, N>), dim3(a.num_segments, a.sh.H), dim3(kStateThreads), 0, s, a);
   const int PN = P * N;
   const dim3 gp(a.num_seqs, a.sh.H, (PN / 4 + 255) / 256);
-  if (a.ssm_bf16) hipLaunchKernelGGL(state_pass_kernel<bf16>, gp, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(state_pass_kernel<float>, gp, dim3(256), 0, s, a);
-  hipLaunchKernelGGL((chunk_scan_kernel<SPLIT, P, N>), dim3(a.num_chunks, a.sh.H, (a.Q + 63) / 64), dim3(256),
-                     0, s, a);
+  if (a.ssm_bf16) hipLaunchKernelGGL(seg_pass_kernel<bf16>, gp, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(seg_pass_kernel<float>, gp, dim3(256), 0, s, a);
+  typedef ScanLds<SPLIT, P, N> L;
+  const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&seg_scan_kernel<SPLIT, P, N>), L::BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((seg_scan_kernel<SPLIT, P, N>), dim3(a.num_segments, a.sh.H), dim3(kScanThreads), L::BYTES, s,
+                     a);
+  return hipSuccess;
 }
 
 template <int P, int N>
-static void launch_pn(const PrefillParams& a, hipStream_t s) {
-  if (a.ssm_bf16) launch_mfma<false, P, N>(a, s);
-  else launch_mfma<true, P, N>(a, s);
+static hipError_t launch_pn(const PrefillParams& a, hipStream_t s) {
+  return a.ssm_bf16 ? launch_segments<false, P, N>(a, s) : launch_segments<true, P, N>(a, s);
 }
 
 template <int P>
-static bool launch_p(const PrefillParams& a, int N, hipStream_t s) {
-  switch (N) {
-    case 16: launch_pn<P, 16>(a, s); return true;
-    case 32: launch_pn<P, 32>(a, s); return true;
-    case 64: launch_pn<P, 64>(a, s); return true;
-    case 128: launch_pn<P, 128>(a, s); return true;
-    case 256: launch_pn<P, 256>(a, s); return true;
-    default: return false;
+static hipError_t launch_p(const PrefillParams& a, hipStream_t s) {
+  switch (a.sh.N) {
+    case 16: return launch_pn<P, 16>(a, s);
+    case 32: return launch_pn<P, 32>(a, s);
+    case 64: return launch_pn<P, 64>(a, s);
+    case 128: return launch_pn<P, 128>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
 bool prefill_supported(int P, int N, int W) {
   const bool p_ok = P == 16 || P == 32 || P == 64 || P == 128;
-  const bool n_ok = N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+  const bool n_ok = N == 16 || N == 32 || N == 64 || N == 128;
   return p_ok && n_ok && W >= 2 && W <= 4;
 }
 
 hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
   if (a.num_chunks == 0) return hipSuccess;
-  const dim3 gc(a.num_chunks, (a.sh.Cd + 255) / 256);
+  const dim3 gc(a.num_chunks, (a.sh.Cd + kConvCB - 1) / kConvCB);
+  const bool split = !a.ssm_bf16;
+  hipError_t ea = hipSuccess;
+#define M2_CONV(WW)                                                                                        \
+  if (split) {                                                                                             \
+    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, true>), kConvLdsBytes);               \
+    hipLaunchKernelGGL((conv_kernel<WW, true>), gc, dim3(256), kConvLdsBytes, s, a);                       \
+  } else {                                                                                                 \
+    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, false>), kConvLdsBytes);              \
+    hipLaunchKernelGGL((conv_kernel<WW, false>), gc, dim3(256), kConvLdsBytes, s, a);                      \
+  }
   switch (a.sh.W) {
-    case 2: hipLaunchKernelGGL(conv_kernel<2>, gc, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(conv_kernel<3>, gc, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(conv_kernel<4>, gc, dim3(256), 0, s, a); break;
+    case 2: M2_CONV(2) break;
+    case 3: M2_CONV(3) break;
+    case 4: M2_CONV(4) break;
     default: return hipErrorInvalidValue;
   }
+#undef M2_CONV
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(dt_kernel, dim3(a.num_chunks, (a.sh.H + 3) / 4), dim3(256), 0, s, a);
-  bool ok = false;
+  hipError_t e = hipErrorInvalidValue;
   switch (a.sh.P) {
-    case 16: ok = launch_p<16>(a, a.sh.N, s); break;
-    case 32: ok = launch_p<32>(a, a.sh.N, s); break;
-    case 64: ok = launch_p<64>(a, a.sh.N, s); break;
-    case 128: ok = launch_p<128>(a, a.sh.N, s); break;
+    case 16: e = launch_p<16>(a, s); break;
+    case 32: e = launch_p<32>(a, s); break;
+    case 64: e = launch_p<64>(a, s); break;
+    case 128: e = launch_p<128>(a, s); break;
   }
-  if (!ok) return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
   if (a.num_windows > 0) {
     const dim3 gw(a.num_windows, (a.sh.Cd + 255) / 256);
     switch (a.sh.W) {

@@ -206,11 +206,13 @@ def test_prefill_validation(pool):
 def test_workspace_size_formula(pool):
     n = c_uint64()
     assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 256, 0, byref(n)) == 0
-    H, P, N, Cd, T = 128, 64, 128, 10240, 8192
-    nc = T // 256 + 1
-    act = T * Cd * 4
-    assert n.value >= act + 2 * H * T * 4 + nc * H * P * N * 4
-    assert n.value < act + 2 * H * T * 4 + nc * H * P * N * 4 + 64 * 1024
+    H, P, N, G, T, Q = 128, 64, 128, 8, 8192, 256
+    nc = T // Q + 1
+    planes = 1                                   # bf16 state: single bf16 operand planes
+    acts = nc * Q * (H * P + 3 * G * N) * 2 * planes
+    vecs = 2 * H * T * 4                         # Delta and its chunk-local cumsum
+    segs = nc * H * P * N * 4 + nc * H * 4       # segment states and decays
+    assert acts + vecs + segs <= n.value < acts + vecs + segs + 64 * 1024
     assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 20, 0, byref(n)) == UNSUP
     assert lib().mamba2_prefill_workspace_size(pool, -1, 8192, 256, 0, byref(n)) == ARG
 

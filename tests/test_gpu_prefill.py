@@ -147,15 +147,19 @@ def test_prefill_8192_tokens_from_zero_state():
     assert untouched(before_s, pool.ssm, [17]) and untouched(before_c, pool.conv, [17])
 
 
-def test_two_call_handoff_is_bit_exact_with_fp32_state():
-    """prefill(L1) then prefill(L2, seeded, start_pos=L1) == prefill(L1+L2) when L1 is chunk-aligned."""
+def test_two_call_handoff_matches_one_call_with_fp32_state():
+    """prefill(L1) then prefill(L2, seeded, start_pos=L1) agrees with prefill(L1+L2).
+
+    The two runs associate the chunk-state sums differently (the segment scan of one call
+    against the running state of the other), so they agree to fp32 rounding, not bit for bit.
+    """
     sh = synth.Shape(8, 64, 128, 2, 4)
     rng = np.random.default_rng(77)
     params = synth.layer_params(rng, sh)
-    L1, L2, Q = 512, 333, 256
+    L1, L2, Q = 512, 1400, 256
     u, z, dt = synth._tokens(rng, sh, L1 + L2, "bf16")
-    ssm0 = synth.cast_exact(rng.normal(0, 0.1, (sh.nheads, sh.head_dim, sh.d_state)), "f32")
-    conv0 = synth.cast_exact(rng.normal(0, 0.1, (sh.conv_dim, 3)), "bf16")
+    ssm0 = synth.cast_exact(synth.normal(rng, (sh.nheads, sh.head_dim, sh.d_state), 0.1), "f32")
+    conv0 = synth.cast_exact(synth.normal(rng, (sh.conv_dim, 3), 0.1), "bf16")
     W = weights(params)
     one = make_pool(sh, 1, 4, "f32", "bf16")
     put_slot(one, 0, 2, ssm0, conv0)
@@ -165,13 +169,49 @@ def test_two_call_handoff_is_bit_exact_with_fp32_state():
     ya = run_prefill(two, W, [0, L1], [2], [1], u[:L1], z[:L1], dt[:L1], "bf16", "f32", chunk=Q)
     yb = run_prefill(two, W, [0, L2], [2], [1], u[L1:], z[L1:], dt[L1:], "bf16", "f32", chunk=Q,
                      start_pos=[L1])
-    assert torch.equal(torch.cat([ya, yb]), y1)
-    assert torch.equal(one.ssm[0, 2], two.ssm[0, 2]) and torch.equal(one.conv[0, 2], two.conv[0, 2])
+    assert rel_err(host(torch.cat([ya, yb])), host(y1)) <= 2e-6
+    assert rel_err(host(two.ssm[0, 2]), host(one.ssm[0, 2])) <= 2e-6
+    assert torch.equal(one.conv[0, 2], two.conv[0, 2])
+
+
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_prefill_is_batch_invariant_and_deterministic(ssm_dtype):
+    """A sequence's outputs and states are bit-identical alone, in a batch, and on a rerun."""
+    c = _varlen_case(ssm_dtype, 64, seed=500)
+    sh = c["sh"]
+    W = weights(c["params"])
+
+    def run(idx):
+        pool = make_pool(sh, 1, 40, ssm_dtype, "bf16", sentinel_seed=7)
+        for i in idx:
+            put_slot(pool, 0, int(c["slots"][i]), c["ssm0"][i], c["conv0"][i])
+        rows = np.concatenate([np.arange(c["cu"][i], c["cu"][i + 1]) for i in idx])
+        cu = np.concatenate([[0], np.cumsum(c["lens"][idx])]).astype(np.int32)
+        y = run_prefill(pool, W, cu, c["slots"][idx], c["has_init"][idx], c["u"][rows], c["z"][rows],
+                        c["dt"][rows], c["io"], ssm_dtype, start_pos=c["start"][idx], chunk=64,
+                        interval=c["interval"], ckpt=c["ck"][idx])
+        return pool, y, cu
+
+    full = np.arange(len(c["lens"]))
+    pool_a, y_a, cu_a = run(full)
+    pool_b, y_b, _ = run(full)
+    assert torch.equal(y_a.view(torch.int16 if ssm_dtype == "bf16" else torch.int32),
+                       y_b.view(torch.int16 if ssm_dtype == "bf16" else torch.int32))
+    assert torch.equal(pool_a.ssm.view(torch.uint8), pool_b.ssm.view(torch.uint8))
+    k = 8                                    # the 600-token sequence, alone
+    pool_c, y_c, _ = run(np.array([k]))
+    s = int(c["slots"][k])
+    bits = torch.int16 if ssm_dtype == "bf16" else torch.int32
+    assert torch.equal(y_c.view(bits), y_a[cu_a[k]:cu_a[k + 1]].view(bits))
+    assert torch.equal(pool_c.ssm[0, s].view(torch.uint8), pool_a.ssm[0, s].view(torch.uint8))
+    for ck in c["ck"][k]:
+        if ck >= 0:
+            assert torch.equal(pool_c.ssm[0, ck].view(torch.uint8), pool_a.ssm[0, ck].view(torch.uint8))
 
 
 def test_checkpoint_equals_prefix_prefill_and_restore_replay():
-    """With fp32 state a checkpoint at 256 equals a 256-token prefill bit for bit, and restoring
-    it into a fresh slot and replaying the suffix reproduces the uninterrupted run bit for bit."""
+    """A checkpoint at 256 equals a 256-token prefill; restoring it into a fresh slot and
+    replaying the suffix reproduces the uninterrupted run (fp32 state, to fp32 rounding)."""
     sh = synth.Shape(8, 64, 128, 2, 4)
     rng = np.random.default_rng(78)
     params = synth.layer_params(rng, sh)
@@ -183,10 +223,12 @@ def test_checkpoint_equals_prefix_prefill_and_restore_replay():
                          ckpt=[[5, 6]])
     pref = make_pool(sh, 1, 8, "f32", "bf16")
     run_prefill(pref, W, [0, 256], [0], [0], u[:256], z[:256], dt[:256], "bf16", "f32", chunk=Q)
-    assert torch.equal(pool.ssm[0, 5], pref.ssm[0, 0]) and torch.equal(pool.conv[0, 5], pref.conv[0, 0])
+    assert rel_err(host(pool.ssm[0, 5]), host(pref.ssm[0, 0])) <= 2e-6
+    assert torch.equal(pool.conv[0, 5], pref.conv[0, 0])
     run_prefill(pref, W, [0, 256], [0], [1], u[256:512], z[256:512], dt[256:512], "bf16", "f32",
                 chunk=Q, start_pos=[256])
-    assert torch.equal(pref.ssm[0, 0], pool.ssm[0, 6]) and torch.equal(pool.conv[0, 6], pref.conv[0, 0])
+    assert rel_err(host(pref.ssm[0, 0]), host(pool.ssm[0, 6])) <= 2e-6
+    assert torch.equal(pool.conv[0, 6], pref.conv[0, 0])
     # restore: copy checkpoint slot 5 into fresh slot 3, clobber slot 0, replay tokens 256..700 from slot 3
     pool.ssm[0, 0] = float("nan")
     pool.conv[0, 0] = float("nan")
@@ -195,4 +237,4 @@ def test_checkpoint_equals_prefix_prefill_and_restore_replay():
     pool.checkpoint(0, src, dst, src_host=[5], dst_host=[3])
     y_tail = run_prefill(pool, W, [0, L - 256], [3], [1], u[256:], z[256:], dt[256:], "bf16", "f32",
                          chunk=Q, start_pos=[256])
-    assert torch.equal(y_tail, y_full[256:])
+    assert rel_err(host(y_tail), host(y_full[256:])) <= 2e-6

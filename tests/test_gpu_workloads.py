@@ -70,7 +70,8 @@ def test_mixed_batch_prefills_with_checkpoints_and_decodes():
                 assert rel_err(host(pool.ssm[0, s, h]), ref.ssm[0, s, h]) <= TOL["bf16"]
             assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s])
 
-    # checkpoint placement: the checkpoint at 1024 equals a separate 1024-token prefill bit for bit
+    # checkpoint placement: the checkpoint at 1024 holds the state of a separate 1024-token prefill
+    # (the two calls split the chunk-state sums differently, so bf16-state values agree to rounding)
     i = int(np.argmax(w["ckpt_slots"][:, 0] >= 0))
     a = int(w["cu_seqlens"][i])
     scratch = [s for s in range(512) if s not in set(written)][0]
@@ -79,9 +80,9 @@ def test_mixed_batch_prefills_with_checkpoints_and_decodes():
                  dev(w["z"][a:a + 1024], "bf16"), dev(w["dt"][a:a + 1024], "bf16"), y2, chunk_size=w["chunk"])
     torch.cuda.synchronize()
     c0 = int(w["ckpt_slots"][i, 0])
-    assert torch.equal(pool.ssm[0, c0].view(torch.int16), pool.ssm[0, scratch].view(torch.int16))
+    assert rel_err(host(pool.ssm[0, c0]), host(pool.ssm[0, scratch])) <= TOL["bf16"]
     assert torch.equal(pool.conv[0, c0].view(torch.int16), pool.conv[0, scratch].view(torch.int16))
-    assert torch.equal(y2.view(torch.int16), y[a:a + 1024].view(torch.int16))
+    assert rel_err(host(y2), host(y[a:a + 1024])) <= TOL["bf16"]
 
 
 def _compact_problem(params, heads, shape):
