@@ -32,6 +32,12 @@
 namespace m2 {
 
 constexpr int kJB = 32;          // tokens per staged block (one MFMA K-step)
+#ifndef M2_SCAN_WAVES_PER_EU
+#define M2_SCAN_WAVES_PER_EU 1
+#endif
+#ifndef M2_SCAN_PREFETCH
+#define M2_SCAN_PREFETCH 1
+#endif
 constexpr int kScanThreads = 512;
 constexpr int kStateThreads = 512;
 
@@ -163,18 +169,25 @@ template <int NPL, int ITEMS> struct TilePrefetch {
 };
 
 // ------------------------------------------------------------------ 1. conv
-// Workgroup per (chunk, 64 channels), 256 threads: thread (octet o, token group tg) convolves
-// channels 8o .. 8o+7 over its rows with 16-byte input loads, into an fp32 LDS tile; the tile is
-// then written as operand planes: x transposed per head, B both ways, C token-major.
+// Workgroup per (chunk, 64 channels), 256 threads.  Thread (octet o, token group tg) convolves
+// channels 8o .. 8o+7 over its rows with 16-byte input loads and writes each row's 8 results to
+// LDS as one 16-byte store per operand plane.  The tile is then written out: x and B transposed
+// (consecutive lanes on consecutive channels, 8 tokens per 16-byte store), and B and C rows.
 constexpr int kConvCB = 64;
-constexpr int kConvLD = kConvCB + 1;
-constexpr int kConvLdsBytes = 256 * kConvLD * 4;
+constexpr int kConvLD = kConvCB + 8;   // u16 pitch of the LDS rows (16-byte aligned)
+
+template <bool SPLIT> struct ConvLds {
+  static constexpr int NPL = SPLIT ? 2 : 1;
+  static constexpr int BYTES = NPL * 256 * kConvLD * 2;
+};
 
 template <int W, bool SPLIT>
 __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   constexpr int CB = kConvCB;
+  constexpr int NPL = ConvLds<SPLIT>::NPL;
+  constexpr int PLANE = 256 * kConvLD;
   extern __shared__ __align__(16) unsigned char conv_smem[];
-  float* const s_out = reinterpret_cast<float*>(conv_smem);
+  u16* const s_t = reinterpret_cast<u16*>(conv_smem);
   const ChunkEntry ch = a.chunks[blockIdx.x];
   const SeqEntry sq = a.seqs[ch.seq];
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
@@ -226,14 +239,25 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (j + r < j1) {
+            u16x8 hv, lv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               float v = bias[e];
 #pragma unroll
               for (int k = 0; k < W - 1; ++k) v += w[e][k] * win[k][e];
               v += w[e][W - 1] * u[r][e];
-              s_out[(j + r) * kConvLD + 8 * oc + e] = silu(v);
+              v = silu(v);
+              if (SPLIT) {
+                u16 hi, lo;
+                split2(v, hi, lo);
+                hv[e] = hi;
+                lv[e] = lo;
+              } else {
+                hv[e] = bits_of(from_f32<bf16>(v));
+              }
             }
+            *reinterpret_cast<u16x8*>(s_t + (j + r) * kConvLD + 8 * oc) = hv;
+            if (SPLIT) *reinterpret_cast<u16x8*>(s_t + PLANE + (j + r) * kConvLD + 8 * oc) = lv;
 #pragma unroll
             for (int k = 0; k < W - 2; ++k)
 #pragma unroll
@@ -246,12 +270,11 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
     }
   }
   __syncthreads();
-  constexpr int NPL = SPLIT ? 2 : 1;
   const int64_t chunk = blockIdx.x;
-  // channel-major outputs (x transposed, B transposed): thread per (channel, 8 rows)
-  const int vpr = (len + 7) / 8;
-  for (int idx = tid; idx < CB * vpr; idx += 256) {
-    const int ccl = idx / vpr, j = (idx % vpr) * 8;
+  // channel-major outputs (x transposed, B transposed): lane per channel, 8 rows per store
+  const int ngr = (len + 7) / 8;
+  for (int idx = tid; idx < CB * ngr; idx += 256) {
+    const int ccl = idx % CB, j = (idx / CB) * 8;
     const int cc = c0 + ccl;
     if (cc >= I + GN) continue;
     u16* dst;
@@ -265,20 +288,15 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
       dst = a.Bt + ((chunk * G + g) * N + n) * Q + j;
       pstride = a.Bt_plane;
     }
-    u16 hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = (j + e < len) ? s_out[(j + e) * kConvLD + ccl] : 0.f;
-      if (SPLIT) split2(v, hi[e], lo[e]);
-      else hi[e] = bits_of(from_f32<bf16>(v));
-    }
 #pragma unroll
     for (int pl = 0; pl < NPL; ++pl) {
-      const u16* hv = pl ? lo : hi;
+      u16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = s_t[pl * PLANE + (j + e) * kConvLD + ccl];
       if (j + 8 <= len) {
-        *reinterpret_cast<u16x8*>(dst + pl * pstride) = u16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+        *reinterpret_cast<u16x8*>(dst + pl * pstride) = v;
       } else {
-        for (int e = 0; e < 8 && j + e < len; ++e) dst[pl * pstride + e] = hv[e];
+        for (int e = 0; e < 8 && j + e < len; ++e) dst[pl * pstride + e] = v[e];
       }
     }
   }
@@ -286,13 +304,6 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   for (int idx = tid; idx < len * (CB / 8); idx += 256) {
     const int j = idx / (CB / 8), cc = c0 + (idx % (CB / 8)) * 8;
     if (cc < I || cc >= Cd) continue;
-    u16 hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = s_out[j * kConvLD + (cc - c0) + e];
-      if (SPLIT) split2(v, hi[e], lo[e]);
-      else hi[e] = bits_of(from_f32<bf16>(v));
-    }
     u16* dst;
     int64_t pstride;
     if (cc < I + GN) {
@@ -303,10 +314,9 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
       pstride = a.Cr_plane;
     }
 #pragma unroll
-    for (int pl = 0; pl < NPL; ++pl) {
-      const u16* hv = pl ? lo : hi;
-      *reinterpret_cast<u16x8*>(dst + pl * pstride) = u16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
-    }
+    for (int pl = 0; pl < NPL; ++pl)
+      *reinterpret_cast<u16x8*>(dst + pl * pstride) =
+          *reinterpret_cast<const u16x8*>(s_t + pl * PLANE + j * kConvLD + (cc - c0));
   }
 }
 
@@ -514,7 +524,8 @@ template <bool SPLIT, int P, int N> struct ScanPrefetch {
 };
 
 template <bool SPLIT, int P, int N>
-__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(M2_SCAN_WAVES_PER_EU)))
+void seg_scan_kernel(PrefillParams a) {
   typedef ScanLds<SPLIT, P, N> L;
   typedef StateTiles<P, N> ST;
   constexpr int kSJB = L::kSJB;
@@ -564,7 +575,9 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(PrefillParams a)
   const int c_end = sg.chunk0 + sg.nchunk;
 
   ScanPrefetch<SPLIT, P, N> pf;
+#if M2_SCAN_PREFETCH
   pf.load(a, sg.chunk0, 0, a.chunks[sg.chunk0].len, h, g, tid);
+#endif
 
   for (int c = sg.chunk0; c < c_end; ++c) {
     const ChunkEntry ch = a.chunks[c];
@@ -663,11 +676,17 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(PrefillParams a)
 
     for (int jb = 0; jb < len; jb += kSJB) {
       __syncthreads();   // all reads of the previous block are done
+#if M2_SCAN_PREFETCH
       pf.store(sBr, sXT, sBT, tid);
       __syncthreads();
       // prefetch the next block (next chunk's first block at the end of this chunk)
       if (jb + kSJB < len) pf.load(a, c, jb + kSJB, len, h, g, tid);
       else if (c + 1 < c_end) pf.load(a, c + 1, 0, a.chunks[c + 1].len, h, g, tid);
+#else
+      pf.load(a, c, jb, len, h, g, tid);
+      pf.store(sBr, sXT, sBT, tid);
+      __syncthreads();
+#endif
 
 #pragma unroll
       for (int kb = 0; kb < kSJB; kb += 32) {
@@ -891,11 +910,11 @@ hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
   hipError_t ea = hipSuccess;
 #define M2_CONV(WW)                                                                                        \
   if (split) {                                                                                             \
-    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, true>), kConvLdsBytes);               \
-    hipLaunchKernelGGL((conv_kernel<WW, true>), gc, dim3(256), kConvLdsBytes, s, a);                       \
+    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, true>), ConvLds<true>::BYTES);        \
+    hipLaunchKernelGGL((conv_kernel<WW, true>), gc, dim3(256), ConvLds<true>::BYTES, s, a);                \
   } else {                                                                                                 \
-    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, false>), kConvLdsBytes);              \
-    hipLaunchKernelGGL((conv_kernel<WW, false>), gc, dim3(256), kConvLdsBytes, s, a);                      \
+    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, false>), ConvLds<false>::BYTES);     \
+    hipLaunchKernelGGL((conv_kernel<WW, false>), gc, dim3(256), ConvLds<false>::BYTES, s, a);             \
   }
   switch (a.sh.W) {
     case 2: M2_CONV(2) break;
