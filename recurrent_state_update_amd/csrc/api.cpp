@@ -111,7 +111,7 @@ struct PrefillLayout {
   uint64_t nc_max, ns_max, nw_max, planes;
   uint64_t off_seqs, off_chunks, off_segs, off_windows, meta_bytes;
   uint64_t off_xT, off_Bt, off_Br, off_Cr, plane_xT, plane_Bt, plane_Br, plane_Cr;
-  uint64_t off_delta, off_dA, off_seg_state, off_seg_decay, total;
+  uint64_t off_delta, off_dA, off_seg_state, off_seg_decay, off_hin, plane_hin, total;
 };
 
 bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
@@ -143,7 +143,10 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   L->off_seg_state = align_up(L->off_dA + v, 256);
   if (!mul_ok(L->ns_max, (uint64_t)sh.H * sh.P * sh.N * 4, &v)) return false;
   L->off_seg_decay = align_up(L->off_seg_state + v, 256);
-  L->total = align_up(L->off_seg_decay + L->ns_max * sh.H * 4, 256);
+  L->off_hin = align_up(L->off_seg_decay + L->ns_max * sh.H * 4, 256);
+  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N, &L->plane_hin)) return false;
+  if (!mul_ok(L->plane_hin, 2 * L->planes, &v)) return false;
+  L->total = align_up(L->off_hin + v, 256);
   return true;
 }
 
@@ -461,6 +464,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
   p.io_bf16 = io_dtype == M2_BF16;
   p.y_bf16 = y_dtype == M2_BF16;
+  p.zy_vec = aligned16(z) && aligned16(y) && (z_stride * ies) % 16 == 0 && (y_stride * esize(y_dtype)) % 16 == 0;
   p.sh = sh;
   p.Q = chunk_size;
   p.num_seqs = num_seqs;
@@ -501,6 +505,8 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.dA = reinterpret_cast<float*>(ws + L.off_dA);
   p.seg_state = reinterpret_cast<float*>(ws + L.off_seg_state);
   p.seg_decay = reinterpret_cast<float*>(ws + L.off_seg_decay);
+  p.hin = reinterpret_cast<uint16_t*>(ws + L.off_hin);
+  p.hin_plane = (int64_t)L.plane_hin;
   const hipError_t e = m2::launch_prefill(p, hs);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

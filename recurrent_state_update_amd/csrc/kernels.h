@@ -60,6 +60,7 @@ struct PrefillParams {
   void* ssm;
   void* conv;
   int ssm_bf16, conv_bf16, io_bf16, y_bf16;
+  int zy_vec;          // z and y rows allow 16-byte vector access (aligned bases and row pitches)
   LayerShape sh;
   int Q;               // chunk size
   int num_seqs, num_chunks, num_segments, num_windows, total_tokens;
@@ -91,6 +92,8 @@ struct PrefillParams {
   float* dA;             // [H][T] chunk-local inclusive cumsum of Delta*A
   float* seg_state;      // [segments][H][P][N]: segment end state from zero, then the entering state
   float* seg_decay;      // [segments][H]: sum over the segment's chunks of the chunk's last cumsum
+  uint16_t* hin;         // [planes][chunks][H][P][N]: state entering each chunk, bf16 operand planes
+  int64_t hin_plane;     // elements per plane
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 bool prefill_supported(int P, int N, int W);

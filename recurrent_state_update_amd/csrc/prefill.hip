@@ -13,16 +13,16 @@
 // affine-composition passage, SSD chunk-scan call site).
 //
 // Launch sequence (one stream):
-//   1. conv_kernel       causal conv + SiLU of every (token, channel), written as bf16
-//                        operand planes in the layouts the products read
-//   2. dt_kernel         Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
-//   3. seg_state_kernel  per (segment, head): end state of the segment from a zero state (MFMA);
-//                        skipped for each sequence's last segment
-//   4. seg_pass_kernel   per (sequence, head): scan over segments -> state entering each segment
-//   5. seg_scan_kernel   per (segment, head): walks its chunks with the state in MFMA
-//                        accumulators: outputs (MFMA), state update (MFMA), checkpoint and
-//                        final states rounded into their slots
-//   6. window_kernel     final and checkpoint conv windows (raw inputs) into their slots
+//   1. conv_kernel        causal conv + SiLU of every (token, channel), written as bf16
+//                         operand planes in the layouts the products read
+//   2. dt_kernel          Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
+//   3. state_walk_kernel  per (segment, head), from a zero state: the segment's end state (MFMA);
+//                         skipped for each sequence's last segment
+//   4. seg_pass_kernel    per (sequence, head): scan over segments -> state entering each segment
+//   5. state_walk_kernel  per (segment, head), from the entering state: the state entering each
+//                         chunk (operand planes), checkpoint and final states into their slots
+//   6. chunk_out_kernel   per (chunk, head): outputs (MFMA), independent across chunks
+//   7. window_kernel      final and checkpoint conv windows (raw inputs) into their slots
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
 // otherwise operands are single bf16 planes with fp32 accumulation.
@@ -31,13 +31,6 @@
 
 namespace m2 {
 
-constexpr int kJB = 32;          // tokens per staged block (one MFMA K-step)
-#ifndef M2_SCAN_WAVES_PER_EU
-#define M2_SCAN_WAVES_PER_EU 1
-#endif
-#ifndef M2_SCAN_PREFETCH
-#define M2_SCAN_PREFETCH 1
-#endif
 constexpr int kScanThreads = 512;
 constexpr int kStateThreads = 512;
 
@@ -119,8 +112,12 @@ __device__ __forceinline__ void stage_rows(u16* dst, int64_t dst_plane, int dst_
   }
 }
 
-// Register prefetch of a staged block: ITEMS 8-element vectors per plane, taken from a
-// (rows x cols) tile exactly as stage_rows does, held in registers until written to LDS.
+// Register prefetch of a staged block: ITEMS 8-element vectors per plane of a (rows x cols)
+// tile, held in registers until written to LDS.  Every thread issues the same number of 16-byte
+// loads with no branch (vectors outside the valid region read the tile's first vector; source
+// rows are whole multiples of 8 elements, so a vector that starts inside a row stays inside
+// it), and nothing touches the loaded registers until store(), which zeroes what lies outside
+// the valid region.  The loads therefore stay in flight until the block is stored.
 template <int NPL, int ITEMS> struct TilePrefetch {
   u16x8 v[ITEMS][NPL];
 
@@ -131,35 +128,28 @@ template <int NPL, int ITEMS> struct TilePrefetch {
     for (int it = 0; it < ITEMS; ++it) {
       const int idx = tid + it * nthreads;
       const int r = idx / vpr, c = (idx % vpr) * 8;
+      const bool in = idx < rows * vpr && r < valid_rows && c < valid_cols;
+      const int64_t off = in ? r * src_ld + c : 0;
 #pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) {
-        u16x8 x = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (idx < rows * vpr && r < valid_rows) {
-          const u16* s = src + pl * src_plane + r * src_ld + c;
-          if (c + 8 <= valid_cols) {
-            x = *reinterpret_cast<const u16x8*>(s);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (c + e < valid_cols) ? s[e] : u16(0);
-          }
-        }
-        v[it][pl] = x;
-      }
+      for (int pl = 0; pl < NPL; ++pl) v[it][pl] = *reinterpret_cast<const u16x8*>(src + pl * src_plane + off);
     }
   }
 
-  __device__ __forceinline__ void store(u16* dst, int64_t dst_plane, int dst_ld, int rows, int cols, int tid,
-                                        int nthreads) const {
+  __device__ __forceinline__ void store(u16* dst, int64_t dst_plane, int dst_ld, int rows, int cols, int valid_rows,
+                                        int valid_cols, int tid, int nthreads) const {
     const int vpr = cols / 8;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
       const int idx = tid + it * nthreads;
       if (idx < rows * vpr) {
         const int r = idx / vpr, c = (idx % vpr) * 8;
+        const bool in = r < valid_rows;
 #pragma unroll
         for (int pl = 0; pl < NPL; ++pl) {
+          u16x8 x = v[it][pl];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (in && c + e < valid_cols) ? x[e] : u16(0);
           u16* d = dst + pl * dst_plane + r * dst_ld + c;
-          const u16x8 x = v[it][pl];
           *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
           *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
         }
@@ -188,8 +178,8 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   constexpr int PLANE = 256 * kConvLD;
   extern __shared__ __align__(16) unsigned char conv_smem[];
   u16* const s_t = reinterpret_cast<u16*>(conv_smem);
-  const ChunkEntry ch = a.chunks[blockIdx.x];
-  const SeqEntry sq = a.seqs[ch.seq];
+  const ChunkEntry ch = load_uniform(&a.chunks[blockIdx.x]);
+  const SeqEntry sq = load_uniform(&a.seqs[ch.seq]);
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
   const int Q = a.Q, len = ch.len;
   const int c0 = blockIdx.y * CB;
@@ -323,7 +313,7 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
 // ------------------------------------------------------------------ 2. Delta, cumsum
 // One wave per (chunk, head); lane l owns rows 4l .. 4l+3 of the chunk (Q <= 256).
 __global__ __launch_bounds__(256) void dt_kernel(PrefillParams a) {
-  const ChunkEntry ch = a.chunks[blockIdx.x];
+  const ChunkEntry ch = load_uniform(&a.chunks[blockIdx.x]);
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (h >= a.sh.H) return;
@@ -355,90 +345,230 @@ __global__ __launch_bounds__(256) void dt_kernel(PrefillParams a) {
   }
 }
 
-// State tiles (P/16 x N/16 of 16x16) spread over the 8 waves of a workgroup.
+// State tiles (P/16 x N/16 of 16x16) spread over the 8 waves of a workgroup.  When the
+// shape allows, each wave owns PER_WAVE tiles of one tile row (ALIGNED), so the x-side operand
+// of the state product is built once per K-step and shared by all of the wave's tiles.
 template <int P, int N> struct StateTiles {
+  static constexpr int PT = P / 16;
   static constexpr int NT = N / 16;
-  static constexpr int TOTAL = (P / 16) * NT;
-  static constexpr int PER_WAVE = (TOTAL + 7) / 8;
+  static constexpr int TOTAL = PT * NT;
+  static constexpr bool ALIGNED = PT <= 8 && 8 % PT == 0 && NT % (8 / PT) == 0;
+  static constexpr int WPR = ALIGNED ? 8 / PT : 1;                        // waves per tile row
+  static constexpr int PER_WAVE = ALIGNED ? NT / WPR : (TOTAL + 7) / 8;
+  __device__ static bool valid(int w, int m) { return ALIGNED || w * PER_WAVE + m < TOTAL; }
+  __device__ static int pt(int w, int m) { return ALIGNED ? w / WPR : (w * PER_WAVE + m) / NT; }
+  __device__ static int nt(int w, int m) { return ALIGNED ? (w % WPR) * PER_WAVE + m : (w * PER_WAVE + m) % NT; }
 };
 
-// ------------------------------------------------------------------ 3. segment end states
-template <bool SPLIT, int P, int N>
-__global__ __launch_bounds__(kStateThreads) void seg_state_kernel(PrefillParams a) {
-  constexpr int NPL = SPLIT ? 2 : 1;
-  constexpr int LDX = kJB + 4;   // 18 dwords: conflict-free fragment rows
+template <typename TS>
+__device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N, int p, int n, const floatx4& v) {
+  TS* d = static_cast<TS*>(pool) + base;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[(int64_t)(p + r) * N + n] = from_f32<TS>(v[r]);
+}
+
+// ------------------------------------------------------------------ 3. state walks
+// Per (segment, head), 512 threads: the state runs through the segment's chunks in MFMA
+// accumulators, h <- exp(a_last) h + sum_j exp(a_last - a_j) Delta_j x_j B_j^T, over staged
+// blocks of kWB tokens with the next block held in registers while the current one is used.
+//   EMIT = false: from a zero state; writes the segment's end state and its summed log decay
+//                 (each sequence's last segment is skipped: nothing follows it).
+//   EMIT = true:  from the state entering the segment; writes the state entering every chunk
+//                 as bf16 operand planes for the output kernel, and after each chunk the
+//                 checkpoint and final states rounded into their slots.
+constexpr int kWB = 64;
+
+template <bool SPLIT, int P, int N> struct WalkLds {
+  static constexpr int NPL = SPLIT ? 2 : 1;
+  static constexpr int LDX = kWB + 4;   // 34 dwords per row: the 16 rows of a fragment hit distinct banks
+  static constexpr int XT_OFF = 0;                          // u16 offsets
+  static constexpr int BT_OFF = XT_OFF + NPL * P * LDX;
+  static constexpr int STAGE_END = BT_OFF + NPL * N * LDX;
+  // state staging for 16-byte stores of the entering state (overlays the blocks)
+  static constexpr int LDS_ST = N + 8;
+  static constexpr int ST_END = NPL * P * LDS_ST;
+  static constexpr int U16S = STAGE_END > ST_END ? STAGE_END : ST_END;
+  static constexpr int IT_XT = (P * (kWB / 8) + kStateThreads - 1) / kStateThreads;
+  static constexpr int IT_BT = (N * (kWB / 8) + kStateThreads - 1) / kStateThreads;
+};
+
+template <bool SPLIT, int P, int N, bool EMIT>
+__global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams a) {
+  typedef WalkLds<SPLIT, P, N> L;
   typedef StateTiles<P, N> ST;
-  __shared__ u16 sXT[NPL * P * LDX];
-  __shared__ u16 sBT[NPL * N * LDX];
-  __shared__ float sW[256];
-  const SegEntry sg = a.segs[blockIdx.x];
-  if (sg.is_last) return;
+  constexpr int NPL = L::NPL, LDX = L::LDX;
+  __shared__ __align__(16) u16 smem_w[L::U16S];
+  __shared__ __align__(16) float sW[256];
+  u16* const sXT = smem_w + L::XT_OFF;
+  u16* const sBT = smem_w + L::BT_OFF;
+  const SegEntry sg = load_uniform(&a.segs[blockIdx.x]);
+  if (!EMIT && sg.is_last) return;
+  const SeqEntry sq = load_uniform(&a.seqs[sg.seq]);
   const int h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t T = a.total_tokens;
+  const int64_t PN = (int64_t)P * N;
+  float* const seg = a.seg_state + ((int64_t)blockIdx.x * H + h) * PN;
+
   floatx4 acc[ST::PER_WAVE];
 #pragma unroll
-  for (int k = 0; k < ST::PER_WAVE; ++k) acc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float logdecay = 0.f;
-  for (int c = sg.chunk0; c < sg.chunk0 + sg.nchunk; ++c) {
-    const ChunkEntry ch = a.chunks[c];
-    const int len = ch.len;
-    const float* dAh = a.dA + (int64_t)h * T + ch.t0;
-    const float* dh = a.delta + (int64_t)h * T + ch.t0;
-    const float alast = dAh[len - 1];
-    logdecay += alast;
-    __syncthreads();
-    for (int j = tid; j < 256; j += kStateThreads) sW[j] = j < len ? __expf(alast - dAh[j]) * dh[j] : 0.f;
-    const float decay = __expf(alast);
+  for (int m = 0; m < ST::PER_WAVE; ++m) {
+    acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (EMIT && ST::valid(wave, m)) {
+      const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
 #pragma unroll
-    for (int k = 0; k < ST::PER_WAVE; ++k) acc[k] *= decay;
-    for (int jb = 0; jb < len; jb += kJB) {
-      __syncthreads();
-      stage_rows<NPL>(sXT, P * LDX, LDX, a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kJB,
-                      P, len - jb, tid, kStateThreads);
-      stage_rows<NPL>(sBT, N * LDX, LDX, a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kJB,
-                      N, len - jb, tid, kStateThreads);
-      __syncthreads();
-      int cur_pt = -1;
-      Frag<SPLIT> fa;
+      for (int r = 0; r < 4; ++r) acc[m][r] = seg[(pt * 16 + 4 * q + r) * N + nt * 16 + l16];
+    }
+  }
+
+  TilePrefetch<NPL, L::IT_XT> px;
+  TilePrefetch<NPL, L::IT_BT> pb;
+  const int c_end = sg.chunk0 + sg.nchunk;
+  auto prefetch = [&](int c, int jb, int len) {
+    px.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kWB, P, len - jb, tid, kStateThreads);
+    pb.load(a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kWB, N, len - jb, tid, kStateThreads);
+  };
+  // a chunk's cumsum and Delta at token tid and its last cumsum, loaded with its first block
+  float wa, wd, wl;
+  auto prefetch_tables = [&](const ChunkEntry& nc) {
+    const int64_t base = (int64_t)h * T + nc.t0;
+    const int j = min(tid & 255, nc.len - 1);
+    wa = a.dA[base + j];
+    wd = a.delta[base + j];
+    wl = a.dA[base + nc.len - 1];
+  };
+  {
+    const ChunkEntry c0 = load_uniform(&a.chunks[sg.chunk0]);
+    prefetch(sg.chunk0, 0, c0.len);
+    prefetch_tables(c0);
+  }
+
+  float logdecay = 0.f;
+  for (int c = sg.chunk0; c < c_end; ++c) {
+    const ChunkEntry ch = load_uniform(&a.chunks[c]);
+    const int len = ch.len;
+    const float alast = wl, aj = wa, dj = wd;
+    logdecay += alast;
+    __syncthreads();   // the previous chunk's reads of sW and of the staged blocks are done
+    if (EMIT) {   // the state entering this chunk -> LDS, as the output kernel's operand planes
 #pragma unroll
       for (int m = 0; m < ST::PER_WAVE; ++m) {
-        const int k = wave * ST::PER_WAVE + m;
-        if (k < ST::TOTAL) {
-          const int pt = k / ST::NT, nt = k % ST::NT;
-          if (pt != cur_pt) {
-            float v[8];
-            lds_vals<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, 0, q, v);
+        if (ST::valid(wave, m)) {
+          const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= sW[jb + kmap(q, e)];
-            fa = make_frag<SPLIT>(v);
-            cur_pt = pt;
+          for (int r = 0; r < 4; ++r) {
+            const int i = (pt * 16 + 4 * q + r) * L::LDS_ST + nt * 16 + l16;
+            u16 hi, lo = 0;
+            if (SPLIT) split2(acc[m][r], hi, lo);
+            else hi = bits_of(from_f32<bf16>(acc[m][r]));
+            smem_w[i] = hi;
+            if (SPLIT) smem_w[P * L::LDS_ST + i] = lo;
           }
-          const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, nt * 16 + l16, 0, q);
-          acc[m] = mma<SPLIT>(fa, fb, acc[m]);
+        }
+      }
+    }
+    if (tid < 256) sW[tid] = tid < len ? __expf(alast - aj) * dj : 0.f;
+    if (EMIT) {   // ... and out with 16-byte stores (the block loop's first barrier protects the overlay)
+      __syncthreads();
+      u16* dst = a.hin + ((int64_t)c * H + h) * PN;
+      constexpr int CG = N / 8;
+      for (int idx = tid; idx < P * CG; idx += kStateThreads) {
+        const int row = idx / CG, c8 = (idx % CG) * 8;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl)
+          *reinterpret_cast<u16x8*>(dst + pl * a.hin_plane + row * N + c8) =
+              *reinterpret_cast<const u16x8*>(smem_w + pl * P * L::LDS_ST + row * L::LDS_ST + c8);
+      }
+    }
+    const float decay = __expf(alast);
+#pragma unroll
+    for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] *= decay;
+
+    for (int jb = 0; jb < len; jb += kWB) {
+      __syncthreads();   // all reads of the previous block are done
+      px.store(sXT, P * LDX, LDX, P, kWB, P, len - jb, tid, kStateThreads);
+      pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+      __syncthreads();
+      {   // the next block, or the next chunk's first block with its tables; one straight path
+          // (past the segment's last block the current block is fetched again and not used)
+        const bool more = jb + kWB < len;
+        const int pc = more ? c : min(c + 1, c_end - 1);
+        const int pj = more ? jb + kWB : (c + 1 < c_end ? 0 : jb);
+        const ChunkEntry nc = load_uniform(&a.chunks[pc]);
+        prefetch(pc, pj, nc.len);
+        prefetch_tables(nc);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kWB; kb += 32) {
+        if (jb + kb >= len) break;
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + kb + 4 * q]);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + kb + 16 + 4 * q]);
+        // x-side operand of tile row pt: (w x)^T over the K-step's tokens
+        auto xfrag = [&](int pt) {
+          float v[8];
+          lds_vals<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q, v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { v[e] *= w0[e]; v[e + 4] *= w1[e]; }
+          return make_frag<SPLIT>(v);
+        };
+        if (ST::ALIGNED) {
+          const Frag<SPLIT> fa = xfrag(ST::pt(wave, 0));
+          Frag<SPLIT> fb[ST::PER_WAVE];
+#pragma unroll
+          for (int m = 0; m < ST::PER_WAVE; ++m)
+            fb[m] = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+#pragma unroll
+          for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = mma<SPLIT>(fa, fb[m], acc[m]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < ST::PER_WAVE; ++m) {
+            if (ST::valid(wave, m)) {
+              const Frag<SPLIT> fa = xfrag(ST::pt(wave, m));
+              const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+              acc[m] = mma<SPLIT>(fa, fb, acc[m]);
+            }
+          }
+        }
+      }
+    }
+
+    if (EMIT) {   // checkpoint and final states, rounded to the state dtype
+      const int dsts[2] = {ch.ckpt_slot, ch.is_last ? sq.slot : -1};
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (dsts[d] < 0) continue;
+        const int64_t base = (int64_t)dsts[d] * H * PN + (int64_t)h * PN;
+#pragma unroll
+        for (int m = 0; m < ST::PER_WAVE; ++m) {
+          if (ST::valid(wave, m)) {
+            const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
+            if (a.ssm_bf16) store_state_tile<bf16>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, acc[m]);
+            else store_state_tile<float>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, acc[m]);
+          }
         }
       }
     }
   }
-  float* out = a.seg_state + ((int64_t)blockIdx.x * H + h) * P * N;
+  if (!EMIT) {
 #pragma unroll
-  for (int m = 0; m < ST::PER_WAVE; ++m) {
-    const int k = wave * ST::PER_WAVE + m;
-    if (k < ST::TOTAL) {
-      const int pt = k / ST::NT, nt = k % ST::NT;
+    for (int m = 0; m < ST::PER_WAVE; ++m) {
+      if (ST::valid(wave, m)) {
+        const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(pt * 16 + 4 * q + r) * N + nt * 16 + l16] = acc[m][r];
+        for (int r = 0; r < 4; ++r) seg[(pt * 16 + 4 * q + r) * N + nt * 16 + l16] = acc[m][r];
+      }
     }
+    if (tid == 0) a.seg_decay[(int64_t)blockIdx.x * H + h] = logdecay;
   }
-  if (tid == 0) a.seg_decay[(int64_t)blockIdx.x * H + h] = logdecay;
 }
 
 // ------------------------------------------------------------------ 4. scan over segments
 template <typename TS>
 __global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
-  const SeqEntry sq = a.seqs[blockIdx.x];
+  const SeqEntry sq = load_uniform(&a.seqs[blockIdx.x]);
   if (sq.nseg == 0) return;
   const int h = blockIdx.y, H = a.sh.H;
   const int PN = a.sh.P * a.sh.N;
@@ -457,7 +587,7 @@ __global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       const int s = sq.seg0 + s0 + k;
-      if (s0 + k < sq.nseg && !a.segs[s].is_last)
+      if (s0 + k < sq.nseg && !load_uniform(&a.segs[s]).is_last)
         sc[k] = *reinterpret_cast<const floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off);
     }
 #pragma unroll
@@ -465,70 +595,119 @@ __global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
       if (s0 + k < sq.nseg) {
         const int s = sq.seg0 + s0 + k;
         *reinterpret_cast<floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off) = hs;
-        if (!a.segs[s].is_last) hs = __expf(a.seg_decay[(int64_t)s * H + h]) * hs + sc[k];
+        if (!load_uniform(&a.segs[s]).is_last) hs = __expf(a.seg_decay[(int64_t)s * H + h]) * hs + sc[k];
       }
     }
   }
 }
 
-// ------------------------------------------------------------------ 5. segment walk
-// Tokens per staged block in the segment walk: two K-steps with single bf16 planes, one with
-// hi/lo planes (the register prefetch of a block doubles with two planes).
-template <bool SPLIT> struct ScanBlock { static constexpr int JB = SPLIT ? 32 : 64; };
+// ------------------------------------------------------------------ 5. chunk outputs
+// Per (chunk, head), 512 threads; wave w owns the 16-row tiles w and 15 - w of the chunk
+// (equal causal work per wave for Q = 256).  Y = exp(a_i) C_i h_in + (M o L) X + D x, gated.
+// Tokens per staged block: two K-steps with single bf16 planes, one with hi/lo planes.
+template <bool SPLIT> struct OutBlock { static constexpr int JB = SPLIT ? 32 : 64; };
 
-template <bool SPLIT, int P, int N> struct ScanLds {
-  static constexpr int kSJB = ScanBlock<SPLIT>::JB;
+template <bool SPLIT, int P, int N> struct OutLds {
+  static constexpr int kOB = OutBlock<SPLIT>::JB;
   static constexpr int NPL = SPLIT ? 2 : 1;
   // row pitches of 2 (mod 32) dwords: the 16 rows of a fragment read land in distinct banks
-  static constexpr int LDH = N + 4;      // state operand rows [p][n]
+  static constexpr int LDH = N + 4;      // entering state [p][n]
   static constexpr int LDB = N + 4;      // B rows [j][n]
-  static constexpr int LDX = kSJB + 4;   // transposed blocks [p or n][j]
+  static constexpr int LDX = kOB + 4;    // x transposed [p][j]
   static constexpr int H_OFF = 0;
   static constexpr int BR_OFF = H_OFF + NPL * P * LDH;
-  static constexpr int XT_OFF = BR_OFF + NPL * kSJB * LDB;
-  static constexpr int BT_OFF = XT_OFF + NPL * P * LDX;
-  static constexpr int U16_END = BT_OFF + NPL * N * LDX;
+  static constexpr int XT_OFF = BR_OFF + NPL * kOB * LDB;
+  static constexpr int U16_END = XT_OFF + NPL * P * LDX;
   static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes
-  static constexpr int BYTES = F_OFF + 4 * 256 * 4;
-  // staging vectors per thread
-  static constexpr int IT_BR = (kSJB * (N / 8) + kScanThreads - 1) / kScanThreads;
-  static constexpr int IT_XT = (P * (kSJB / 8) + kScanThreads - 1) / kScanThreads;
-  static constexpr int IT_BT = (N * (kSJB / 8) + kScanThreads - 1) / kScanThreads;
+  // output staging after the products: one 16-row fp32 tile per wave (overlays the above)
+  static constexpr int LDO = P + 4;
+  static constexpr int OUT_BYTES = 8 * 16 * LDO * 4;
+  static constexpr int BYTES = F_OFF + 3 * 256 * 4 > OUT_BYTES ? F_OFF + 3 * 256 * 4 : OUT_BYTES;
+  static constexpr int IT_BR = (kOB * (N / 8) + kScanThreads - 1) / kScanThreads;
+  static constexpr int IT_XT = (P * (kOB / 8) + kScanThreads - 1) / kScanThreads;
 };
 
-template <typename TS>
-__device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N, int p, int n, const floatx4& v) {
-  TS* d = static_cast<TS*>(pool) + base;
+// C rows of a wave's two row tiles as B-operand fragments of G^T (zero past the chunk).
+template <bool SPLIT, int N, int NK>
+__device__ __forceinline__ void load_c_frags(const PrefillParams& a, int c, int g, int len, const int (&rts)[2],
+                                             int nrt, int q, int l16, Frag<SPLIT> (&cf)[2][NK]) {
+  constexpr int NPL = SPLIT ? 2 : 1;
+  const int GN = a.sh.G * N;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) d[(int64_t)(p + r) * N + n] = from_f32<TS>(v[r]);
+  for (int t = 0; t < 2; ++t) {
+    const int rt = rts[t];
+    const int i = rt * 16 + l16;
+    const u16* crow = a.Cr + ((int64_t)c * a.Q + i) * GN + g * N;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        u16x4 lo4 = u16x4{0, 0, 0, 0}, hi4 = u16x4{0, 0, 0, 0};
+        const int n = ks * 32 + 4 * q;
+        if (rt < nrt && i < len) {
+          if (n < N) lo4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n);
+          if (n + 16 < N) hi4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n + 16);
+        }
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[e] = bf_of(lo4[e]); f[e + 4] = bf_of(hi4[e]); }
+        if (pl == 0) cf[t][ks].hi = f;
+        else cf[t][ks].lo = f;
+      }
+    }
+  }
 }
 
-template <bool SPLIT, int P, int N> struct ScanPrefetch {
-  typedef ScanLds<SPLIT, P, N> L;
-  static constexpr int kSJB = L::kSJB;
-  TilePrefetch<L::NPL, L::IT_BR> br;
-  TilePrefetch<L::NPL, L::IT_XT> xt;
-  TilePrefetch<L::NPL, L::IT_BT> bt;
+// G^T = B C^T for the 32 tokens of a K-step and the 16 rows of one tile (two 16x16 halves).
+template <bool SPLIT, int NK>
+__device__ __forceinline__ void gt_tile(const Frag<SPLIT> (&cft)[NK], const Frag<SPLIT> (&fb)[2][NK],
+                                        floatx4 (&gtt)[2]) {
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    gtt[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) gtt[jt] = mma<SPLIT>(fb[jt][ks], cft[ks], gtt[jt]);
+  }
+}
 
-  __device__ __forceinline__ void load(const PrefillParams& a, int c, int jb, int len, int h, int g, int tid) {
-    const int Q = a.Q, H = a.sh.H, G = a.sh.G, GN = G * N;
-    br.load(a.Br + ((int64_t)c * Q + jb) * GN + g * N, a.Br_plane, GN, kSJB, N, len - jb, N, tid, kScanThreads);
-    xt.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kSJB, P, len - jb, tid, kScanThreads);
-    bt.load(a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kSJB, N, len - jb, tid, kScanThreads);
+// Decay mask of one row tile -> the A operand of (M o L) X, with D x riding on the diagonal.
+// Below the diagonal (every token of the K-step precedes every row), exp(a_i - a_j) =
+// exp(a_i - a_ref) exp(a_ref - a_j) with a_ref the cumsum at the K-step's last token: both
+// factors are <= 1, one exp per row and a column table cw.  On the diagonal the exponent is
+// taken directly, and entries above it are selected away.
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> decay_mask(const floatx4 (&gtt)[2], int rt, int jk, int len, float aref,
+                                                  const float (&cw)[8], const float* sA, const float* sD, float Dh,
+                                                  int q, int l16) {
+  const int i = rt * 16 + l16;
+  const bool row_ok = i < len;
+  const float ai = sA[i & 255];
+  float mv[8];
+  if (jk + 31 < rt * 16) {
+    const float rf = row_ok ? __expf(ai - aref) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] = gtt[e >> 2][e & 3] * rf * cw[e];
+  } else {
+    const floatx4 a0 = *reinterpret_cast<const floatx4*>(&sA[jk + 4 * q]);
+    const floatx4 a1 = *reinterpret_cast<const floatx4*>(&sA[jk + 16 + 4 * q]);
+    const floatx4 d0 = *reinterpret_cast<const floatx4*>(&sD[jk + 4 * q]);
+    const floatx4 d1 = *reinterpret_cast<const floatx4*>(&sD[jk + 16 + 4 * q]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = jk + kmap(q, e);
+      const float aj = e < 4 ? a0[e & 3] : a1[e & 3];
+      const float dj = e < 4 ? d0[e & 3] : d1[e & 3];
+      const float v = gtt[e >> 2][e & 3] * __expf(fminf(ai - aj, 0.f)) * dj + (j == i ? Dh : 0.f);
+      mv[e] = (row_ok && j <= i) ? v : 0.f;
+    }
   }
-  __device__ __forceinline__ void store(u16* sBr, u16* sXT, u16* sBT, int tid) const {
-    br.store(sBr, kSJB * L::LDB, L::LDB, kSJB, N, tid, kScanThreads);
-    xt.store(sXT, P * L::LDX, L::LDX, P, kSJB, tid, kScanThreads);
-    bt.store(sBT, N * L::LDX, L::LDX, N, kSJB, tid, kScanThreads);
-  }
-};
+  return make_frag<SPLIT>(mv);
+}
 
 template <bool SPLIT, int P, int N>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(M2_SCAN_WAVES_PER_EU)))
-void seg_scan_kernel(PrefillParams a) {
-  typedef ScanLds<SPLIT, P, N> L;
-  typedef StateTiles<P, N> ST;
-  constexpr int kSJB = L::kSJB;
+__global__ __launch_bounds__(kScanThreads) void chunk_out_kernel(PrefillParams a) {
+  typedef OutLds<SPLIT, P, N> L;
+  constexpr int kOB = L::kOB;
   constexpr int NPL = L::NPL;
   constexpr int PT = P / 16;
   constexpr int NK = N / 32 > 0 ? N / 32 : 1;   // K-steps over the state dimension
@@ -537,289 +716,439 @@ void seg_scan_kernel(PrefillParams a) {
   u16* const sH = smem + L::H_OFF;
   u16* const sBr = smem + L::BR_OFF;
   u16* const sXT = smem + L::XT_OFF;
-  u16* const sBT = smem + L::BT_OFF;
   float* const sA = reinterpret_cast<float*>(smem_raw + L::F_OFF);
   float* const sD = sA + 256;
-  float* const sW = sD + 256;
-  float* const sCw = sW + 256;   // exp(a_ref - a_j) Delta_j, a_ref = cumsum at the last token of j's K-step
+  float* const sCw = sD + 256;   // exp(a_ref - a_j) Delta_j, a_ref = cumsum at the last token of j's K-step
 
-  const SegEntry sg = a.segs[blockIdx.x];
-  const SeqEntry sq = a.seqs[sg.seq];
+  const int c = blockIdx.x;
+  const ChunkEntry ch = load_uniform(&a.chunks[c]);
+  const int len = ch.len;
   const int h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
   const int GN = G * N;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t T = a.total_tokens;
-  const float Dh = a.D[h];
-  const int64_t slot_elems = (int64_t)H * P * N;
-
-  // running state in accumulator layout: tile (pt, nt), lane holds h[pt*16 + 4q + r][nt*16 + l16]
-  floatx4 hacc[ST::PER_WAVE];
-  {
-    const float* hin = a.seg_state + ((int64_t)blockIdx.x * H + h) * P * N;
-#pragma unroll
-    for (int m = 0; m < ST::PER_WAVE; ++m) {
-      const int k = wave * ST::PER_WAVE + m;
-      hacc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (k < ST::TOTAL) {
-        const int pt = k / ST::NT, nt = k % ST::NT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hacc[m][r] = hin[(pt * 16 + 4 * q + r) * N + nt * 16 + l16];
-      }
-    }
-  }
-  // row tiles of this wave: wave and 15 - wave (balanced causal work for Q = 256)
+  // uniform: held in a scalar register, so no later vector-memory wait depends on it
+  const float Dh = load_uniform(&a.D[h]);
   const int nrt = Q / 16;
   const int rts[2] = {wave, 15 - wave};
-  const int c_end = sg.chunk0 + sg.nchunk;
 
-  ScanPrefetch<SPLIT, P, N> pf;
-#if M2_SCAN_PREFETCH
-  pf.load(a, sg.chunk0, 0, a.chunks[sg.chunk0].len, h, g, tid);
-#endif
+  TilePrefetch<NPL, L::IT_BR> pbr;
+  TilePrefetch<NPL, L::IT_XT> pxt;
+  auto prefetch = [&](int jb) {
+    pbr.load(a.Br + ((int64_t)c * Q + jb) * GN + g * N, a.Br_plane, GN, kOB, N, len - jb, N, tid, kScanThreads);
+    pxt.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kOB, P, len - jb, tid, kScanThreads);
+  };
+  prefetch(0);
 
-  for (int c = sg.chunk0; c < c_end; ++c) {
-    const ChunkEntry ch = a.chunks[c];
-    const int len = ch.len;
+  // C rows of this wave's row tiles as fragments
+  Frag<SPLIT> cf[2][NK];
+  load_c_frags<SPLIT, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
+  // per-token tables and the entering state
+  {
     const float* dAh = a.dA + (int64_t)h * T + ch.t0;
     const float* dh = a.delta + (int64_t)h * T + ch.t0;
-    const float alast = dAh[len - 1];
-    __syncthreads();   // previous chunk's LDS reads are done
     for (int j = tid; j < 256; j += kScanThreads) {
       const bool ok = j < len;
       const float aj = ok ? dAh[j] : 0.f, dj = ok ? dh[j] : 0.f;
       const int jr = min((j | 31), len - 1);   // last token of j's K-step
       sA[j] = aj;
       sD[j] = dj;
-      sW[j] = ok ? __expf(alast - aj) * dj : 0.f;
       sCw[j] = ok ? __expf(dAh[jr] - aj) * dj : 0.f;
     }
-    // state entering the chunk -> operand planes [p][n]
-#pragma unroll
-    for (int m = 0; m < ST::PER_WAVE; ++m) {
-      const int k = wave * ST::PER_WAVE + m;
-      if (k < ST::TOTAL) {
-        const int pt = k / ST::NT, nt = k % ST::NT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int idx = (pt * 16 + 4 * q + r) * L::LDH + nt * 16 + l16;
-          u16 hi, lo = 0;
-          if (SPLIT) split2(hacc[m][r], hi, lo);
-          else hi = bits_of(from_f32<bf16>(hacc[m][r]));
-          sH[idx] = hi;
-          if (SPLIT) sH[P * L::LDH + idx] = lo;
-        }
-      }
-    }
-    // C rows of this wave's row tiles as fragments (global loads issued before the barrier)
-    Frag<SPLIT> cf[2][NK];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rt = rts[t];
-      const int i = rt * 16 + l16;
-      if (!(rt < nrt && rt * 16 < len)) continue;
-      const u16* crow = a.Cr + ((int64_t)c * Q + i) * GN + g * N;
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl) {
-          u16x4 lo4 = u16x4{0, 0, 0, 0}, hi4 = u16x4{0, 0, 0, 0};
-          const int n = ks * 32 + 4 * q;
-          if (i < len) {
-            if (n < N) lo4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n);
-            if (n + 16 < N) hi4 = *reinterpret_cast<const u16x4*>(crow + pl * a.Cr_plane + n + 16);
-          }
-          bf16x8 f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { f[e] = bf_of(lo4[e]); f[e + 4] = bf_of(hi4[e]); }
-          if (pl == 0) cf[t][ks].hi = f;
-          else cf[t][ks].lo = f;
-        }
-      }
-    }
-    __syncthreads();
+    stage_rows<NPL>(sH, P * L::LDH, L::LDH, a.hin + ((int64_t)c * H + h) * P * N, a.hin_plane, N, P, N, P, N, tid,
+                    kScanThreads);
+  }
+  __syncthreads();
 
-    // the entering-state term
-    floatx4 acc[2][PT];
+  // Row-tile validity is uniform per wave, so every branch below is a scalar branch and each
+  // code path is straight-line MFMA work the compiler can schedule freely.
+  const bool v0 = rts[0] < nrt && rts[0] * 16 < len;
+  const bool v1 = rts[1] < nrt && rts[1] * 16 < len;
+
+  // the entering-state term exp(a_i) C_i h_in (C fragments of invalid rows are zero)
+  floatx4 acc[2][PT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rt = rts[t];
+  for (int pt = 0; pt < PT; ++pt) {
+    acc[0][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc[1][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    Frag<SPLIT> fh[NK];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) acc[t][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (!(rt < nrt && rt * 16 < len)) continue;
+    for (int ks = 0; ks < NK; ++ks) {
+      fh[ks] = lds_frag<SPLIT>(sH, P * L::LDH, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+      if (N < 32) {   // upper K half is padding
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
+        for (int e = 4; e < 8; ++e) { fh[ks].hi[e] = bf_of(0); if (SPLIT) fh[ks].lo[e] = bf_of(0); }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      acc[0][pt] = mma<SPLIT>(cf[0][ks], fh[ks], acc[0][pt]);
+      acc[1][pt] = mma<SPLIT>(cf[1][ks], fh[ks], acc[1][pt]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ii = rts[t] * 16 + 4 * q + r;
+      const float sc = ii < len ? __expf(sA[ii & 255]) : 0.f;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[t][pt][r] *= sc;
+    }
+  }
+
+  auto gmat = [&](const Frag<SPLIT> (&cft)[NK], const Frag<SPLIT> (&fb)[2][NK], floatx4 (&gtt)[2]) {
+    gt_tile<SPLIT, NK>(cft, fb, gtt);
+  };
+  auto mask = [&](const floatx4 (&gtt)[2], int rt, int jk, float aref, const float (&cw)[8]) {
+    return decay_mask<SPLIT>(gtt, rt, jk, len, aref, cw, sA, sD, Dh, q, l16);
+  };
+
+  for (int jb = 0; jb < len; jb += kOB) {
+    __syncthreads();   // all reads of the previous block are done
+    pbr.store(sBr, kOB * L::LDB, L::LDB, kOB, N, len - jb, N, tid, kScanThreads);
+    pxt.store(sXT, P * L::LDX, L::LDX, P, kOB, P, len - jb, tid, kScanThreads);
+    __syncthreads();
+    prefetch(jb + kOB < len ? jb + kOB : jb);   // unconditional: one straight path
+#pragma unroll
+    for (int kb = 0; kb < kOB; kb += 32) {
+      const int jk = jb + kb;   // first token of this K-step
+      if (jk >= len) break;
+      const bool a0 = v0 && jk <= rts[0] * 16 + 15;
+      const bool a1 = v1 && jk <= rts[1] * 16 + 15;
+      if (!(a0 || a1)) continue;
+      Frag<SPLIT> fb[2][NK];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-          Frag<SPLIT> fh = lds_frag<SPLIT>(sH, P * L::LDH, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
-          if (N < 32) {   // upper K half is padding
+          fb[jt][ks] = lds_frag<SPLIT>(sBr, kOB * L::LDB, L::LDB, kb + jt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+          if (N < 32) {
 #pragma unroll
-            for (int e = 4; e < 8; ++e) { fh.hi[e] = bf_of(0); if (SPLIT) fh.lo[e] = bf_of(0); }
+            for (int e = 4; e < 8; ++e) { fb[jt][ks].hi[e] = bf_of(0); if (SPLIT) fb[jt][ks].lo[e] = bf_of(0); }
           }
-          acc[t][pt] = mma<SPLIT>(cf[t][ks], fh, acc[t][pt]);
+        }
+      }
+      Frag<SPLIT> fx[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<SPLIT>(sXT, P * L::LDX, L::LDX, pt * 16 + l16, kb, q);
+      float cw[8];
+      {
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
+        const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
+      }
+      const float aref = sA[min(jk + 31, len - 1)];
+      if (a0 && a1) {
+        floatx4 g0[2], g1[2];
+        gmat(cf[0], fb, g0);
+        gmat(cf[1], fb, g1);
+        const Frag<SPLIT> m0 = mask(g0, rts[0], jk, aref, cw);
+        const Frag<SPLIT> m1 = mask(g1, rts[1], jk, aref, cw);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          acc[0][pt] = mma<SPLIT>(m0, fx[pt], acc[0][pt]);
+          acc[1][pt] = mma<SPLIT>(m1, fx[pt], acc[1][pt]);
+        }
+      } else if (a1) {
+        floatx4 g1[2];
+        gmat(cf[1], fb, g1);
+        const Frag<SPLIT> m1 = mask(g1, rts[1], jk, aref, cw);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[1][pt] = mma<SPLIT>(m1, fx[pt], acc[1][pt]);
+      } else {
+        floatx4 g0[2];
+        gmat(cf[0], fb, g0);
+        const Frag<SPLIT> m0 = mask(g0, rts[0], jk, aref, cw);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[0][pt] = mma<SPLIT>(m0, fx[pt], acc[0][pt]);
+      }
+    }
+  }
+
+  // outputs y = acc * SiLU(z).  Each wave stages one 16-row tile at a time in its own fp32 LDS
+  // region and reads it back as 8 consecutive columns per lane, so that z is read and y written
+  // with 16-byte accesses (element accesses when the caller's rows are not 16-byte aligned).
+  __syncthreads();   // every wave is done with the staged blocks
+  float* const sO = reinterpret_cast<float*>(smem_raw) + wave * 16 * L::LDO;
+  constexpr int CG = P / 8;   // 8-column groups per row
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int rt = rts[t];
+    if (!(t == 0 ? v0 : v1)) continue;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sO[(4 * q + r) * L::LDO + pt * 16 + l16] = acc[t][pt][r];
+#pragma unroll
+    for (int it = lane; it < 16 * CG; it += 64) {
+      const int rr = it / CG, c8 = (it % CG) * 8;
+      const int ii = rt * 16 + rr;
+      if (ii >= len) continue;
+      const floatx4 o0 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8]);
+      const floatx4 o1 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8 + 4]);
+      const int64_t row = ch.t0 + ii;
+      const int col = h * P + c8;
+      float v[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+      if (a.zy_vec) {
+        float zf[8];
+        load8_any(a.z, row * a.z_stride + col, a.io_bf16, zf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= silu(zf[e]);
+        store8_any(a.y, row * a.y_stride + col, a.y_bf16, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float zv = load_any(a.z, row * a.z_stride + col + e, a.io_bf16);
+          store_any(a.y, row * a.y_stride + col + e, v[e] * silu(zv), a.y_bf16);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 5b. chunk outputs, a group's heads in turn
+// Per (chunk, group, part of the group's heads), 512 threads, single bf16 operand planes.  The
+// chunk's B rows (LDS) and the C fragments of each wave's row tiles (registers) are loaded once
+// and serve all of the workgroup's heads; the next head's x, entering state and Delta tables are
+// prefetched into registers while the current head is computed, so a head's products run with
+// no barrier and no wait on global memory.  Used when the staging fits in LDS.
+template <int P, int N> struct GroupLds {
+  static constexpr int QM = 256;          // staging for the largest chunk
+  static constexpr int LDB = N + 4;       // B rows [j][n]
+  static constexpr int LDX = QM + 4;      // x transposed [p][j]
+  static constexpr int LDH = N + 4;       // entering state [p][n]
+  static constexpr int LDO = P + 4;       // output staging [row][p], fp32, one 16-row tile per wave
+  static constexpr int BR_OFF = 0;        // u16 offsets
+  static constexpr int XT_OFF = BR_OFF + QM * LDB;
+  static constexpr int H_OFF = XT_OFF + P * LDX;
+  static constexpr int U16_END = H_OFF + P * LDH;
+  static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes: sA, sD, sCw
+  static constexpr int O_OFF = F_OFF + 3 * 256 * 4;            // bytes: output staging
+  static constexpr int BYTES = O_OFF + 8 * 16 * LDO * 4;
+  static constexpr bool FITS = BYTES <= 160 * 1024;
+  static constexpr int IT_BR = (QM * (N / 8) + 511) / 512;
+  static constexpr int IT_XT = (P * (QM / 8) + 511) / 512;
+  static constexpr int IT_H = (P * (N / 8) + 511) / 512;
+};
+
+template <int P, int N>
+__global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, int heads_per_wg) {
+  typedef GroupLds<P, N> L;
+  constexpr int PT = P / 16;
+  constexpr int NK = N / 32 > 0 ? N / 32 : 1;
+  constexpr int QM = L::QM;
+  constexpr int CG = P / 8;                   // 8-column groups of an output row
+  constexpr int ZI = (16 * CG + 63) / 64;     // output items per lane per row tile
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  u16* const smem = reinterpret_cast<u16*>(smem_raw);
+  u16* const sBr = smem + L::BR_OFF;
+  u16* const sXT = smem + L::XT_OFF;
+  u16* const sH = smem + L::H_OFF;
+  float* const sA = reinterpret_cast<float*>(smem_raw + L::F_OFF);
+  float* const sD = sA + 256;
+  float* const sCw = sD + 256;   // exp(a_ref - a_j) Delta_j, a_ref = cumsum at the last token of j's K-step
+
+  const int c = blockIdx.x;
+  const ChunkEntry ch = load_uniform(&a.chunks[c]);
+  const int len = ch.len;
+  const int H = a.sh.H, G = a.sh.G, Q = a.Q, GN = G * N;
+  const int hpg = H / G;
+  const int parts = hpg / heads_per_wg;
+  const int g = blockIdx.y / parts;
+  const int h0 = g * hpg + (blockIdx.y % parts) * heads_per_wg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();
+  const int q = lane >> 4, l16 = lane & 15;
+  const int64_t T = a.total_tokens;
+  const int nrt = Q / 16;
+  const int rts[2] = {wave, 15 - wave};
+  const bool v0 = rts[0] < nrt && rts[0] * 16 < len;
+  const bool v1 = rts[1] < nrt && rts[1] * 16 < len;
+  float* const sO = reinterpret_cast<float*>(smem_raw + L::O_OFF) + wave * 16 * L::LDO;
+  const bool zpre = a.io_bf16 && a.zy_vec;
+
+  // the chunk's B rows -> LDS, once for all heads
+  {
+    TilePrefetch<1, L::IT_BR> pb;
+    pb.load(a.Br + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
+    pb.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
+  }
+  Frag<false> cf[2][NK];
+  load_c_frags<false, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
+
+  TilePrefetch<1, L::IT_XT> px;
+  TilePrefetch<1, L::IT_H> ph;
+  float pa, pd, pr;
+  auto prefetch = [&](int h) {
+    px.load(a.xT + (((int64_t)c * H + h) * P) * Q, 0, Q, P, QM, P, len, tid, 512);
+    ph.load(a.hin + ((int64_t)c * H + h) * P * N, 0, N, P, N, P, N, tid, 512);
+    const int j = min(tid, len - 1);
+    const float* dAh = a.dA + (int64_t)h * T + ch.t0;
+    pa = dAh[j];
+    pd = a.delta[(int64_t)h * T + ch.t0 + j];
+    pr = dAh[min(j | 31, len - 1)];
+  };
+  prefetch(h0);
+
+  for (int hh = 0; hh < heads_per_wg; ++hh) {
+    const int h = h0 + hh;
+    const float Dh = load_uniform(&a.D[h]);
+    __syncthreads();   // the previous head's reads of sXT, sH and the tables are done
+    px.store(sXT, 0, L::LDX, P, QM, P, len, tid, 512);
+    ph.store(sH, 0, L::LDH, P, N, P, N, tid, 512);
+    if (tid < 256) {
+      const bool ok = tid < len;
+      sA[tid] = ok ? pa : 0.f;
+      sD[tid] = ok ? pd : 0.f;
+      sCw[tid] = ok ? __expf(pr - pa) * pd : 0.f;
+    }
+    __syncthreads();
+    // z of this head's output items (bf16, 16-byte rows), issued before the next head's
+    // prefetch so that the output waits for these loads only; rows past the chunk read the
+    // chunk's first row and are never stored
+    u16x8 zr[2][ZI];
+    if (zpre) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int k = 0; k < ZI; ++k) {
+          const int it = min(lane + 64 * k, 16 * CG - 1);
+          int ii = rts[t] * 16 + it / CG;
+          ii = ii < len ? ii : 0;
+          zr[t][k] = *reinterpret_cast<const u16x8*>(static_cast<const u16*>(a.z) + (ch.t0 + ii) * a.z_stride +
+                                                     h * P + (it % CG) * 8);
+        }
+      }
+    }
+    prefetch(min(h + 1, h0 + heads_per_wg - 1));   // unconditional: one straight path
+
+    // the entering-state term exp(a_i) C_i h_in
+    floatx4 acc[2][PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      acc[0][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc[1][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      Frag<false> fh[NK];
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        fh[ks] = lds_frag<false>(sH, 0, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+        if (N < 32) {
+#pragma unroll
+          for (int e = 4; e < 8; ++e) fh[ks].hi[e] = bf_of(0);
         }
       }
 #pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        acc[0][pt] = mma<false>(cf[0][ks], fh[ks], acc[0][pt]);
+        acc[1][pt] = mma<false>(cf[1][ks], fh[ks], acc[1][pt]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int ii = rt * 16 + 4 * q + r;
-        const float sc = ii < len ? __expf(sA[ii]) : 0.f;
+        const int ii = rts[t] * 16 + 4 * q + r;
+        const float sc = ii < len ? __expf(sA[ii & 255]) : 0.f;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[t][pt][r] *= sc;
       }
     }
 
-    // the chunk's state update starts from the decayed entering state
-    const float decay = __expf(alast);
+    // (M o L) X over the K-steps up to each row tile's diagonal; all operands are in LDS.
+    // G^T is built one 16-token half at a time and the x fragments are read after it, which
+    // keeps the fragments live at any moment to about 16 registers.
+    for (int jk = 0; jk < len; jk += 32) {
+      const bool a0 = v0 && jk <= rts[0] * 16 + 15;
+      const bool a1 = v1 && jk <= rts[1] * 16 + 15;
+      if (!(a0 || a1)) break;   // tile 1 ends last; past it there is nothing left for this wave
+      floatx4 g0[2], g1[2];
 #pragma unroll
-    for (int m = 0; m < ST::PER_WAVE; ++m) hacc[m] *= decay;
-
-    for (int jb = 0; jb < len; jb += kSJB) {
-      __syncthreads();   // all reads of the previous block are done
-#if M2_SCAN_PREFETCH
-      pf.store(sBr, sXT, sBT, tid);
-      __syncthreads();
-      // prefetch the next block (next chunk's first block at the end of this chunk)
-      if (jb + kSJB < len) pf.load(a, c, jb + kSJB, len, h, g, tid);
-      else if (c + 1 < c_end) pf.load(a, c + 1, 0, a.chunks[c + 1].len, h, g, tid);
-#else
-      pf.load(a, c, jb, len, h, g, tid);
-      pf.store(sBr, sXT, sBT, tid);
-      __syncthreads();
-#endif
-
+      for (int jt = 0; jt < 2; ++jt) {
+        Frag<false> fb[NK];
 #pragma unroll
-      for (int kb = 0; kb < kSJB; kb += 32) {
-        const int jk = jb + kb;   // first token of this K-step
-        if (jk >= len) break;
-        // diagonal blocks: G^T tiles -> M -> (M o L) X  (D x rides on the diagonal of M).
-        // Each B-row and x fragment is read from LDS once and used for both row tiles.
-        bool act[2];
+        for (int ks = 0; ks < NK; ++ks) {
+          fb[ks] = lds_frag<false>(sBr, 0, L::LDB, jk + jt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+          if (N < 32) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) act[t] = rts[t] < nrt && rts[t] * 16 < len && jk <= rts[t] * 16 + 15;
-        if (act[0] || act[1]) {
-          floatx4 gt[2][2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) gt[t][jt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const bool need0 = act[0] && jk + 16 * jt <= rts[0] * 16 + 15;
-            const bool need1 = act[1] && jk + 16 * jt <= rts[1] * 16 + 15;
-            if (!(need0 || need1)) continue;
-#pragma unroll
-            for (int ks = 0; ks < NK; ++ks) {
-              Frag<SPLIT> fb = lds_frag<SPLIT>(sBr, kSJB * L::LDB, L::LDB, kb + jt * 16 + l16,
-                                               N >= 32 ? ks * 32 : 0, q);
-              if (N < 32) {
-#pragma unroll
-                for (int e = 4; e < 8; ++e) { fb.hi[e] = bf_of(0); if (SPLIT) fb.lo[e] = bf_of(0); }
-              }
-              if (need0) gt[0][jt] = mma<SPLIT>(fb, cf[0][ks], gt[0][jt]);
-              if (need1) gt[1][jt] = mma<SPLIT>(fb, cf[1][ks], gt[1][jt]);
-            }
-          }
-          // decay mask.  Below the diagonal (every token of the K-step precedes every row),
-          // exp(a_i - a_j) = exp(a_i - a_ref) exp(a_ref - a_j) with a_ref the cumsum at the
-          // K-step's last token: both factors are <= 1, one exp per row and a column table.
-          // On the diagonal the exponent is taken directly.
-          Frag<SPLIT> fm[2];
-          float cw[8];
-          {
-            const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
-            const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
-          }
-          const float aref = sA[min(jk + 31, len - 1)];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int i = rts[t] * 16 + l16;
-            const bool row_ok = act[t] && i < len;
-            const float ai = row_ok ? sA[i] : 0.f;
-            float mv[8];
-            if (jk + 31 < rts[t] * 16) {
-              const float rf = row_ok ? __expf(ai - aref) : 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) mv[e] = gt[t][e >> 2][e & 3] * rf * cw[e];
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int j = jk + kmap(q, e);
-                float v = 0.f;
-                if (row_ok && j <= i) {
-                  v = gt[t][e >> 2][e & 3] * __expf(ai - sA[j]) * sD[j];
-                  if (j == i) v += Dh;
-                }
-                mv[e] = v;
-              }
-            }
-            fm[t] = make_frag<SPLIT>(mv);
-          }
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) {
-            const Frag<SPLIT> fx = lds_frag<SPLIT>(sXT, P * L::LDX, L::LDX, pt * 16 + l16, kb, q);
-            if (act[0]) acc[0][pt] = mma<SPLIT>(fm[0], fx, acc[0][pt]);
-            if (act[1]) acc[1][pt] = mma<SPLIT>(fm[1], fx, acc[1][pt]);
+            for (int e = 4; e < 8; ++e) fb[ks].hi[e] = bf_of(0);
           }
         }
-        // state update: h += (w x)^T B over this K-step's tokens
-        int cur_pt = -1;
-        Frag<SPLIT> fa;
+        g0[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        g1[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (a0 && a1) {
 #pragma unroll
-        for (int m = 0; m < ST::PER_WAVE; ++m) {
-          const int k = wave * ST::PER_WAVE + m;
-          if (k < ST::TOTAL) {
-            const int pt = k / ST::NT, nt = k % ST::NT;
-            if (pt != cur_pt) {
-              float v[8];
-              lds_vals<SPLIT>(sXT, P * L::LDX, L::LDX, pt * 16 + l16, kb, q, v);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] *= sW[jk + kmap(q, e)];
-              fa = make_frag<SPLIT>(v);
-              cur_pt = pt;
-            }
-            const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * L::LDX, L::LDX, nt * 16 + l16, kb, q);
-            hacc[m] = mma<SPLIT>(fa, fb, hacc[m]);
+          for (int ks = 0; ks < NK; ++ks) {
+            g0[jt] = mma<false>(fb[ks], cf[0][ks], g0[jt]);
+            g1[jt] = mma<false>(fb[ks], cf[1][ks], g1[jt]);
           }
+        } else if (a1) {
+#pragma unroll
+          for (int ks = 0; ks < NK; ++ks) g1[jt] = mma<false>(fb[ks], cf[1][ks], g1[jt]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NK; ++ks) g0[jt] = mma<false>(fb[ks], cf[0][ks], g0[jt]);
         }
+      }
+      float cw[8];
+      {
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
+        const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
+      }
+      const float aref = sA[min(jk + 31, len - 1)];
+      const Frag<false> m0 = decay_mask<false>(g0, rts[0], jk, len, aref, cw, sA, sD, Dh, q, l16);
+      const Frag<false> m1 = decay_mask<false>(g1, rts[1], jk, len, aref, cw, sA, sD, Dh, q, l16);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const Frag<false> fx = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
+        if (a0) acc[0][pt] = mma<false>(m0, fx, acc[0][pt]);
+        if (a1) acc[1][pt] = mma<false>(m1, fx, acc[1][pt]);
       }
     }
 
-    // outputs: y = acc gated by SiLU(z); lane holds rows rt*16 + 4q + r, columns pt*16 + l16
+    // outputs y = acc * SiLU(z) through this wave's LDS tile, 16-byte z reads and y writes
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int rt = rts[t];
-      if (rt >= nrt || rt * 16 >= len) continue;
+      if (!(t == 0 ? v0 : v1)) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = rt * 16 + 4 * q + r;
-        if (ii < len) {
-          const int64_t row = ch.t0 + ii;
+      for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt) {
-            const int col = h * P + pt * 16 + l16;
-            const float zv = load_any(a.z, row * a.z_stride + col, a.io_bf16);
-            store_any(a.y, row * a.y_stride + col, acc[t][pt][r] * silu(zv), a.y_bf16);
+        for (int r = 0; r < 4; ++r) sO[(4 * q + r) * L::LDO + pt * 16 + l16] = acc[t][pt][r];
+#pragma unroll
+      for (int k = 0; k < ZI; ++k) {
+        const int it = lane + 64 * k;
+        if (it >= 16 * CG) continue;
+        const int rr = it / CG, c8 = (it % CG) * 8;
+        const int ii = rt * 16 + rr;
+        if (ii >= len) continue;
+        const floatx4 o0 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8]);
+        const floatx4 o1 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8 + 4]);
+        const int64_t row = ch.t0 + ii;
+        const int col = h * P + c8;
+        float v[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+        if (zpre) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= silu(f_of(zr[t][k][e]));
+          store8_any(a.y, row * a.y_stride + col, a.y_bf16, v);
+        } else if (a.zy_vec) {
+          float zf[8];
+          load8_any(a.z, row * a.z_stride + col, a.io_bf16, zf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= silu(zf[e]);
+          store8_any(a.y, row * a.y_stride + col, a.y_bf16, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float zv = load_any(a.z, row * a.z_stride + col + e, a.io_bf16);
+            store_any(a.y, row * a.y_stride + col + e, v[e] * silu(zv), a.y_bf16);
           }
-        }
-      }
-    }
-
-    // checkpoint and final states, rounded to the state dtype
-    const int dsts[2] = {ch.ckpt_slot, ch.is_last ? sq.slot : -1};
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      if (dsts[d] < 0) continue;
-      const int64_t base = (int64_t)dsts[d] * slot_elems + (int64_t)h * P * N;
-#pragma unroll
-      for (int m = 0; m < ST::PER_WAVE; ++m) {
-        const int k = wave * ST::PER_WAVE + m;
-        if (k < ST::TOTAL) {
-          const int pt = k / ST::NT, nt = k % ST::NT;
-          if (a.ssm_bf16) store_state_tile<bf16>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, hacc[m]);
-          else store_state_tile<float>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, hacc[m]);
         }
       }
     }
@@ -868,15 +1197,40 @@ static hipError_t set_lds_attr(const void* fn, int bytes) {
 
 template <bool SPLIT, int P, int N>
 static hipError_t launch_segments(const PrefillParams& a, hipStream_t s) {
-  hipLaunchKernelGGL((seg_state_kernel<SPLIT, P, N>), dim3(a.num_segments, a.sh.H), dim3(kStateThreads), 0, s, a);
+  const dim3 gs(a.num_segments, a.sh.H);
+  hipLaunchKernelGGL((state_walk_kernel<SPLIT, P, N, false>), gs, dim3(kStateThreads), 0, s, a);
   const int PN = P * N;
   const dim3 gp(a.num_seqs, a.sh.H, (PN / 4 + 255) / 256);
   if (a.ssm_bf16) hipLaunchKernelGGL(seg_pass_kernel<bf16>, gp, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(seg_pass_kernel<float>, gp, dim3(256), 0, s, a);
-  typedef ScanLds<SPLIT, P, N> L;
-  const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&seg_scan_kernel<SPLIT, P, N>), L::BYTES);
+  hipLaunchKernelGGL((state_walk_kernel<SPLIT, P, N, true>), gs, dim3(kStateThreads), 0, s, a);
+  if (!SPLIT && GroupLds<P, N>::FITS) {
+    // heads per workgroup: the whole group unless that leaves CUs idle
+    static int num_cu = 0;
+    if (num_cu == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cu < 1)
+        num_cu = 256;
+    }
+    const int hpg = a.sh.H / a.sh.G;
+    int parts = 1;
+    while ((int64_t)a.num_chunks * a.sh.G * parts < num_cu && parts < hpg) {
+      int next = parts + 1;
+      while (hpg % next != 0) ++next;
+      parts = next;
+    }
+    typedef GroupLds<P, N> L;
+    const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&chunk_out_group_kernel<P, N>), L::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_out_group_kernel<P, N>), dim3(a.num_chunks, a.sh.G * parts), dim3(512), L::BYTES, s, a,
+                       hpg / parts);
+    return hipSuccess;
+  }
+  typedef OutLds<SPLIT, P, N> L;
+  const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&chunk_out_kernel<SPLIT, P, N>), L::BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((seg_scan_kernel<SPLIT, P, N>), dim3(a.num_segments, a.sh.H), dim3(kScanThreads), L::BYTES, s,
+  hipLaunchKernelGGL((chunk_out_kernel<SPLIT, P, N>), dim3(a.num_chunks, a.sh.H), dim3(kScanThreads), L::BYTES, s,
                      a);
   return hipSuccess;
 }
