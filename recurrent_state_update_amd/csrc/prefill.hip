@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
     px.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kWB, P, len - jb, tid, kStateThreads);
     pb.load(a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kWB, N, len - jb, tid, kStateThreads);
   };
-  // a chunk's cumsum and Delta at token tid and its last cumsum, loaded with its first block
+  // a chunk's cumsum and Delta at token tid and its last cumsum, loaded one chunk ahead
   float wa, wd, wl;
   auto prefetch_tables = [&](const ChunkEntry& nc) {
     const int64_t base = (int64_t)h * T + nc.t0;
@@ -440,17 +440,17 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
     wd = a.delta[base + j];
     wl = a.dA[base + nc.len - 1];
   };
-  {
-    const ChunkEntry c0 = load_uniform(&a.chunks[sg.chunk0]);
-    prefetch(sg.chunk0, 0, c0.len);
-    prefetch_tables(c0);
-  }
+  ChunkEntry ch = load_uniform(&a.chunks[sg.chunk0]);
+  prefetch(sg.chunk0, 0, ch.len);
+  prefetch_tables(ch);
 
   float logdecay = 0.f;
   for (int c = sg.chunk0; c < c_end; ++c) {
-    const ChunkEntry ch = load_uniform(&a.chunks[c]);
     const int len = ch.len;
     const float alast = wl, aj = wa, dj = wd;
+    // the next chunk's entry and tables (the current one again past the segment's end)
+    const int cn = min(c + 1, c_end - 1);
+    const ChunkEntry nch = load_uniform(&a.chunks[cn]);
     logdecay += alast;
     __syncthreads();   // the previous chunk's reads of sW and of the staged blocks are done
     if (EMIT) {   // the state entering this chunk -> LDS, as the output kernel's operand planes
@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
       }
     }
     if (tid < 256) sW[tid] = tid < len ? __expf(alast - aj) * dj : 0.f;
+    prefetch_tables(nch);
     if (EMIT) {   // ... and out with 16-byte stores (the block loop's first barrier protects the overlay)
       __syncthreads();
       u16* dst = a.hin + ((int64_t)c * H + h) * PN;
@@ -492,14 +493,11 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
       px.store(sXT, P * LDX, LDX, P, kWB, P, len - jb, tid, kStateThreads);
       pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
       __syncthreads();
-      {   // the next block, or the next chunk's first block with its tables; one straight path
-          // (past the segment's last block the current block is fetched again and not used)
+      {   // the next block, or the next chunk's first block; one straight path (past the
+          // segment's last block the current block is fetched again and not used)
         const bool more = jb + kWB < len;
-        const int pc = more ? c : min(c + 1, c_end - 1);
-        const int pj = more ? jb + kWB : (c + 1 < c_end ? 0 : jb);
-        const ChunkEntry nc = load_uniform(&a.chunks[pc]);
-        prefetch(pc, pj, nc.len);
-        prefetch_tables(nc);
+        const bool last = !more && c + 1 >= c_end;
+        prefetch(more || last ? c : cn, more ? jb + kWB : (last ? jb : 0), more || last ? len : nch.len);
       }
 #pragma unroll
       for (int kb = 0; kb < kWB; kb += 32) {
@@ -551,6 +549,7 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
         }
       }
     }
+    ch = nch;
   }
   if (!EMIT) {
 #pragma unroll
@@ -697,8 +696,10 @@ __device__ __forceinline__ Frag<SPLIT> decay_mask(const floatx4 (&gtt)[2], int r
       const int j = jk + kmap(q, e);
       const float aj = e < 4 ? a0[e & 3] : a1[e & 3];
       const float dj = e < 4 ? d0[e & 3] : d1[e & 3];
+      // branch-free: every factor is finite, so the causal mask is a multiply by 0 or 1
+      const float keep = (row_ok && j <= i) ? 1.f : 0.f;
       const float v = gtt[e >> 2][e & 3] * __expf(fminf(ai - aj, 0.f)) * dj + (j == i ? Dh : 0.f);
-      mv[e] = (row_ok && j <= i) ? v : 0.f;
+      mv[e] = v * keep;
     }
   }
   return make_frag<SPLIT>(mv);
