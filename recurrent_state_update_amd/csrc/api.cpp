@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "prefill.h"
 #include "mamba2_pool.h"
 
 struct m2_pool {

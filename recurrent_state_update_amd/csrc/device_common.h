@@ -44,37 +44,6 @@ __device__ __forceinline__ void load8_any(const void* p, int64_t i, int is_bf16,
   }
 }
 
-// A wave-uniform read of read-only data (launch tables, per-head parameters) through the
-// constant address space, so that it becomes a scalar-memory load: it does not join the
-// in-order vector-memory counter that covers prefetches in flight.
-template <typename T> __device__ __forceinline__ T load_uniform(const T* p) {
-  static_assert(sizeof(T) % 4 == 0, "whole dwords");
-  typedef const __attribute__((address_space(4))) int cint;
-  const cint* q = (const cint*)p;
-  struct W { int w[sizeof(T) / 4]; } w;
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) w.w[i] = q[i];
-  return __builtin_bit_cast(T, w);
-}
-
-// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value, so that
-// branches on it are scalar branches rather than exec-masked ones.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// Eight consecutive fp32 values -> an io tensor (16-byte aligned position).
-__device__ __forceinline__ void store8_any(void* p, int64_t i, int is_bf16, const float (&v)[8]) {
-  if (is_bf16) {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = from_f32<bf16>(v[e]);
-    *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p) + i) = o;
-  } else {
-    float* d = static_cast<float*>(p) + i;
-    *reinterpret_cast<floatx4*>(d) = floatx4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<floatx4*>(d + 4) = floatx4{v[4], v[5], v[6], v[7]};
-  }
-}
-
 // ------------------------------------------------------------------ math
 // SiLU(v) = v / (1 + e^-v) with the hardware reciprocal (about 1 ulp) instead of an IEEE divide.
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }

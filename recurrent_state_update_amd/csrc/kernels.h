@@ -1,4 +1,5 @@
-// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 decode and
+// slot-copy kernels; the prefill has its own (prefill.h).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,63 +40,5 @@ bool decode_supported(int ssm_bf16, int N, int W);
 // base + layer*layer_stride + slot*bytes_per_slot, for layers [l0, l0+nl).
 hipError_t launch_slot_copy(void* base, uint64_t bytes_per_slot, uint64_t layer_stride, int l0, int nl,
                             int num_slots, int n, const int32_t* src, const int32_t* dst, hipStream_t s);
-
-// Chunked prefill.  Host-built tables live at the start of the workspace.
-struct SeqEntry {     // one per sequence
-  int32_t t0, len, slot, has_init;  // packed start row, rows, final slot, seed from slot
-  int32_t chunk0, nchunk, seg0, nseg;
-};
-struct ChunkEntry {   // one per chunk
-  int32_t seq, t0, len, tau0;       // packed start row, rows in chunk, offset inside the sequence
-  int32_t ckpt_slot, is_last, pad0, pad1;
-};
-struct SegEntry {     // one per segment: consecutive chunks of one sequence walked by one workgroup
-  int32_t seq, chunk0, nchunk, is_last;
-};
-struct WindowEntry {  // one conv-window write: window after `tau` rows of sequence `seq` -> slot
-  int32_t seq, tau, slot, pad;
-};
-
-struct PrefillParams {
-  void* ssm;
-  void* conv;
-  int ssm_bf16, conv_bf16, io_bf16, y_bf16;
-  int zy_vec;          // z and y rows allow 16-byte vector access (aligned bases and row pitches)
-  LayerShape sh;
-  int Q;               // chunk size
-  int num_seqs, num_chunks, num_segments, num_windows, total_tokens;
-  const SeqEntry* seqs;
-  const ChunkEntry* chunks;
-  const SegEntry* segs;
-  const WindowEntry* windows;
-  const void* x;
-  const void* B;
-  const void* C;
-  const void* z;
-  const void* dt;
-  int64_t x_stride, B_stride, C_stride, z_stride, dt_stride;
-  void* y;
-  int64_t y_stride;
-  const float* A;
-  const float* D;
-  const float* dt_bias;
-  const float* conv_w;
-  const float* conv_b;
-  // workspace arrays.  Post-conv activations as bf16 operand planes (one plane, or hi and lo
-  // planes for fp32-faithful products), chunk-blocked with Q rows per chunk:
-  uint16_t* xT;          // [planes][chunks][H][P][Q]   x, tokens contiguous
-  uint16_t* Bt;          // [planes][chunks][G][N][Q]   B, tokens contiguous
-  uint16_t* Br;          // [planes][chunks][Q][G*N]    B, channels contiguous
-  uint16_t* Cr;          // [planes][chunks][Q][G*N]    C, channels contiguous
-  int64_t xT_plane, Bt_plane, Br_plane, Cr_plane;   // elements per plane
-  float* delta;          // [H][T]
-  float* dA;             // [H][T] chunk-local inclusive cumsum of Delta*A
-  float* seg_state;      // [segments][H][P][N]: segment end state from zero, then the entering state
-  float* seg_decay;      // [segments][H]: sum over the segment's chunks of the chunk's last cumsum
-  uint16_t* hin;         // [planes][chunks][H][P][N]: state entering each chunk, bf16 operand planes
-  int64_t hin_plane;     // elements per plane
-};
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
-bool prefill_supported(int P, int N, int W);
 
 }  // namespace m2
