@@ -191,49 +191,80 @@ template <int NPL, int ITEMS> struct TilePrefetch {
 };
 
 // ------------------------------------------------------------------ 1. conv
-// Workgroup per (chunk, 64 channels), 256 threads.  Thread (octet o, token group tg) convolves
-// channels 8o .. 8o+7 over its rows with 16-byte input loads and writes each row's 8 results to
-// LDS as one 16-byte store per operand plane.  The tile is then written out: x and B transposed
-// (consecutive lanes on consecutive channels, 8 tokens per 16-byte store), and B and C rows.
+// One-dimensional grid over (chunk, 64 channels), channel block fastest, so that workgroups
+// running together read neighbouring pieces of the same token rows; 256 threads.  Thread
+// (octet o, group t) convolves channels 8o .. 8o+7 over tokens 8t .. 8t+7 of the chunk: the
+// W-1 halo rows and its 8 rows are requested together (16-byte loads), the taps and SiLU run in
+// fp32, and the results are rounded to the operand planes.  B and C rows go out straight from
+// registers (eight lanes cover 128 contiguous bytes of a row); x and B also go into a
+// channel-major LDS tile, from which the transposed planes are written with consecutive lanes on
+// consecutive 16-byte pieces of one row.
 constexpr int kConvCB = 64;
-constexpr int kConvLD = kConvCB + 8;   // u16 pitch of the LDS rows (16-byte aligned)
+constexpr int kConvLD = 256 + 8;   // u16 pitch of a channel row of the LDS tile (16-byte aligned)
 
 template <bool SPLIT> struct ConvLds {
   static constexpr int NPL = SPLIT ? 2 : 1;
-  static constexpr int BYTES = NPL * 256 * kConvLD * 2;
+  static constexpr int BYTES = NPL * kConvCB * kConvLD * 2;
 };
 
-template <int W, bool SPLIT>
+template <bool IOBF> __device__ __forceinline__ void load_row8(const void* p, int64_t i, float (&o)[8]) {
+  if (IOBF) {
+    const u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const u16*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f_of(v[e]);
+  } else {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(static_cast<const float*>(p) + i);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(static_cast<const float*>(p) + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[e + 4] = b[e]; }
+  }
+}
+
+template <int W, bool SPLIT, bool IOBF>
 __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   constexpr int CB = kConvCB;
   constexpr int NPL = ConvLds<SPLIT>::NPL;
-  constexpr int PLANE = 256 * kConvLD;
+  constexpr int PLANE = CB * kConvLD;
+  constexpr int R = 8;
   extern __shared__ __align__(16) unsigned char conv_smem[];
   u16* const s_t = reinterpret_cast<u16*>(conv_smem);
-  const ChunkEntry ch = load_uniform(&a.chunks[blockIdx.x]);
+  const int ncb = (a.sh.Cd + CB - 1) / CB;
+  const int64_t chunk = blockIdx.x / ncb;
+  const ChunkEntry ch = load_uniform(&a.chunks[chunk]);
   const SeqEntry sq = load_uniform(&a.seqs[ch.seq]);
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
   const int Q = a.Q, len = ch.len;
-  const int c0 = blockIdx.y * CB;
+  const int c0 = (blockIdx.x % ncb) * CB;
   const int tid = threadIdx.x;
   const int oc = tid % (CB / 8), tg = tid / (CB / 8);   // 8 octets x 32 token groups
   const int c = c0 + 8 * oc;
-  if (c < Cd) {
+  const int j0 = 8 * tg;
+  if (c < Cd && j0 < len) {
     const void* src;
     int64_t col, stride;
     if (c < I) { src = a.x; col = c; stride = a.x_stride; }
     else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
     else { src = a.C; col = c - I - GN; stride = a.C_stride; }
-    const int per = (len + 31) / 32;
-    const int j0 = tg * per, j1 = min(len, j0 + per);
-    if (j0 < j1) {
-      float win[W - 1][8];
+    // inputs: rows outside the sequence read the chunk's first row and are replaced below
+    float in[R + W - 1][8];
+#pragma unroll
+    for (int k = 0; k < R + W - 1; ++k) {
+      const int tau = ch.tau0 + j0 - (W - 1) + k;   // offset inside the sequence
+      const bool ok = tau >= 0 && j0 - (W - 1) + k < len;
+      load_row8<IOBF>(src, (ok ? sq.t0 + tau : ch.t0) * stride + col, in[k]);
+    }
+    float w[8][W], bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int k = 0; k < W; ++k) w[e][k] = a.conv_w[(int64_t)(c + e) * W + k];
+      bias[e] = a.conv_b[c + e];
+    }
+    if (ch.tau0 + j0 < W - 1) {   // halo before the sequence start: the slot's window or zeros
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) {
-        const int tau = ch.tau0 + j0 - (W - 1) + k;   // offset inside the sequence
-        if (tau >= 0) {
-          load8_any(src, (int64_t)(sq.t0 + tau) * stride + col, a.io_bf16, win[k]);
-        } else {
+        const int tau = ch.tau0 + j0 - (W - 1) + k;
+        if (tau < 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float v = 0.f;
@@ -241,104 +272,77 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
               const int64_t wi = ((int64_t)sq.slot * Cd + c + e) * (W - 1) + (W - 1 + tau);
               v = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
             }
-            win[k][e] = v;
-          }
-        }
-      }
-      float w[8][W], bias[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-#pragma unroll
-        for (int k = 0; k < W; ++k) w[e][k] = a.conv_w[(int64_t)(c + e) * W + k];
-        bias[e] = a.conv_b[c + e];
-      }
-      for (int j = j0; j < j1; j += 4) {
-        float u[4][8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (j + r < j1) load8_any(src, (int64_t)(ch.t0 + j + r) * stride + col, a.io_bf16, u[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (j + r < j1) {
-            u16x8 hv, lv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float v = bias[e];
-#pragma unroll
-              for (int k = 0; k < W - 1; ++k) v += w[e][k] * win[k][e];
-              v += w[e][W - 1] * u[r][e];
-              v = silu(v);
-              if (SPLIT) {
-                u16 hi, lo;
-                split2(v, hi, lo);
-                hv[e] = hi;
-                lv[e] = lo;
-              } else {
-                hv[e] = bits_of(from_f32<bf16>(v));
-              }
-            }
-            *reinterpret_cast<u16x8*>(s_t + (j + r) * kConvLD + 8 * oc) = hv;
-            if (SPLIT) *reinterpret_cast<u16x8*>(s_t + PLANE + (j + r) * kConvLD + 8 * oc) = lv;
-#pragma unroll
-            for (int k = 0; k < W - 2; ++k)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) win[k][e] = win[k + 1][e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) win[W - 2][e] = u[r][e];
+            in[k][e] = v;
           }
         }
       }
     }
+    // out[pl][r][e]: token j0 + r, channel c + e (zero past the chunk)
+    u16 out[NPL][R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = bias[e];
+#pragma unroll
+        for (int k = 0; k < W; ++k) v += w[e][k] * in[r + k][e];
+        v = j0 + r < len ? silu(v) : 0.f;
+        if (SPLIT) split2(v, out[0][r][e], out[1][r][e]);
+        else out[0][r][e] = bits_of(from_f32<bf16>(v));
+      }
+    }
+    if (c >= I) {   // B and C rows, channels contiguous
+      u16* dst = c < I + GN ? a.Br + (chunk * Q + j0) * GN + (c - I) : a.Cr + (chunk * Q + j0) * GN + (c - I - GN);
+      const int64_t pstride = c < I + GN ? a.Br_plane : a.Cr_plane;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (j0 + r < len) {
+#pragma unroll
+          for (int pl = 0; pl < NPL; ++pl) {
+            u16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = out[pl][r][e];
+            *reinterpret_cast<u16x8*>(dst + pl * pstride + (int64_t)r * GN) = v;
+          }
+        }
+      }
+    }
+    if (c < I + GN) {   // x and B -> channel-major LDS tile
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          u16x8 v;
+#pragma unroll
+          for (int r = 0; r < R; ++r) v[r] = out[pl][r][e];
+          *reinterpret_cast<u16x8*>(s_t + pl * PLANE + (8 * oc + e) * kConvLD + j0) = v;
+        }
+      }
+    }
   }
+  if (c0 >= I + GN) return;   // C channels only: nothing transposed (uniform per workgroup)
   __syncthreads();
-  const int64_t chunk = blockIdx.x;
-  // channel-major outputs (x transposed, B transposed): lane per channel, 8 rows per store
+  // x and B transposed: lane per 8-token group, consecutive lanes along one channel row
   const int ngr = (len + 7) / 8;
   for (int idx = tid; idx < CB * ngr; idx += 256) {
-    const int ccl = idx % CB, j = (idx / CB) * 8;
+    const int g = idx % ngr, ccl = idx / ngr;
     const int cc = c0 + ccl;
     if (cc >= I + GN) continue;
     u16* dst;
     int64_t pstride;
     if (cc < I) {
       const int h = cc / P, p = cc % P;
-      dst = a.xT + ((chunk * H + h) * P + p) * Q + j;
+      dst = a.xT + ((chunk * H + h) * P + p) * Q + 8 * g;
       pstride = a.xT_plane;
     } else {
-      const int g = (cc - I) / N, n = (cc - I) % N;
-      dst = a.Bt + ((chunk * G + g) * N + n) * Q + j;
+      const int gg = (cc - I) / N, n = (cc - I) % N;
+      dst = a.Bt + ((chunk * G + gg) * N + n) * Q + 8 * g;
       pstride = a.Bt_plane;
-    }
-#pragma unroll
-    for (int pl = 0; pl < NPL; ++pl) {
-      u16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = s_t[pl * PLANE + (j + e) * kConvLD + ccl];
-      if (j + 8 <= len) {
-        *reinterpret_cast<u16x8*>(dst + pl * pstride) = v;
-      } else {
-        for (int e = 0; e < 8 && j + e < len; ++e) dst[pl * pstride + e] = v[e];
-      }
-    }
-  }
-  // token-major outputs (B rows, C rows): thread per (row, 8 channels)
-  for (int idx = tid; idx < len * (CB / 8); idx += 256) {
-    const int j = idx / (CB / 8), cc = c0 + (idx % (CB / 8)) * 8;
-    if (cc < I || cc >= Cd) continue;
-    u16* dst;
-    int64_t pstride;
-    if (cc < I + GN) {
-      dst = a.Br + (chunk * Q + j) * GN + (cc - I);
-      pstride = a.Br_plane;
-    } else {
-      dst = a.Cr + (chunk * Q + j) * GN + (cc - I - GN);
-      pstride = a.Cr_plane;
     }
 #pragma unroll
     for (int pl = 0; pl < NPL; ++pl)
       *reinterpret_cast<u16x8*>(dst + pl * pstride) =
-          *reinterpret_cast<const u16x8*>(s_t + pl * PLANE + j * kConvLD + (cc - c0));
+          *reinterpret_cast<const u16x8*>(s_t + pl * PLANE + ccl * kConvLD + 8 * g);
   }
 }
 
@@ -1292,16 +1296,19 @@ bool prefill_supported(int P, int N, int W) {
 
 hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
   if (a.num_chunks == 0) return hipSuccess;
-  const dim3 gc(a.num_chunks, (a.sh.Cd + kConvCB - 1) / kConvCB);
+  const dim3 gc((unsigned)a.num_chunks * ((a.sh.Cd + kConvCB - 1) / kConvCB));
   const bool split = !a.ssm_bf16;
   hipError_t ea = hipSuccess;
-#define M2_CONV(WW)                                                                                        \
-  if (split) {                                                                                             \
-    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, true>), ConvLds<true>::BYTES);        \
-    hipLaunchKernelGGL((conv_kernel<WW, true>), gc, dim3(256), ConvLds<true>::BYTES, s, a);                \
-  } else {                                                                                                 \
-    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, false>), ConvLds<false>::BYTES);     \
-    hipLaunchKernelGGL((conv_kernel<WW, false>), gc, dim3(256), ConvLds<false>::BYTES, s, a);             \
+#define M2_CONV_IO(WW, SP, IO)                                                                           \
+  {                                                                                                      \
+    ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, SP, IO>), ConvLds<SP>::BYTES);      \
+    hipLaunchKernelGGL((conv_kernel<WW, SP, IO>), gc, dim3(256), ConvLds<SP>::BYTES, s, a);              \
+  }
+#define M2_CONV(WW)                                                                                       \
+  if (split) {                                                                                            \
+    if (a.io_bf16) M2_CONV_IO(WW, true, true) else M2_CONV_IO(WW, true, false)                            \
+  } else {                                                                                                \
+    if (a.io_bf16) M2_CONV_IO(WW, false, true) else M2_CONV_IO(WW, false, false)                          \
   }
   switch (a.sh.W) {
     case 2: M2_CONV(2) break;
@@ -1310,6 +1317,7 @@ hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef M2_CONV
+#undef M2_CONV_IO
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(dt_kernel, dim3(a.num_chunks, (a.sh.H + 3) / 4), dim3(256), 0, s, a);
   hipError_t e = hipErrorInvalidValue;
