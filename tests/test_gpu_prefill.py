@@ -66,8 +66,8 @@ def test_tiny_prefill_matches_oracle_and_64_decode_steps():
         assert torch.equal(pool.conv[0, s], dpool.conv[0, s])
 
 
-def _varlen_case(ssm_dtype, Q, seed):
-    sh = synth.Shape(8, 64, 128, 2, 4)
+def _varlen_case(ssm_dtype, Q, seed, sh=None):
+    sh = sh or synth.Shape(8, 64, 128, 2, 4)
     rng = np.random.default_rng(seed)
     params = synth.layer_params(rng, sh)
     lens = np.array([1, 3, 16, 17, 100, 255, 256, 257, 600], np.int32)
@@ -88,16 +88,13 @@ def _varlen_case(ssm_dtype, Q, seed):
     io = ssm_dtype
     u, z, dt = synth._tokens(rng, sh, int(cu[-1]), io)
     ssm0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.nheads, sh.head_dim, sh.d_state)), ssm_dtype)
-    conv0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.conv_dim, 3)), "bf16")
+    conv0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.conv_dim, sh.conv_kernel - 1)), "bf16")
     return dict(sh=sh, params=params, lens=lens, has_init=has_init, start=start, slots=slots, ck=ck, cu=cu,
                 u=u, z=z, dt=dt, ssm0=ssm0, conv0=conv0, interval=interval, io=io)
 
 
-@pytest.mark.parametrize("ssm_dtype,Q", [("bf16", 256), ("bf16", 64), ("f32", 256), ("f32", 32)])
-def test_varlen_prefill_with_seeds_and_checkpoints(ssm_dtype, Q):
-    c = _varlen_case(ssm_dtype, Q, seed=100 + Q)
+def _check_varlen(c, ssm_dtype, Q):
     sh = c["sh"]
-    log(f"case: varlen prefill lens={c['lens'].tolist()} ssm={ssm_dtype} Q={Q} interval={c['interval']}")
     pool = make_pool(sh, 1, 40, ssm_dtype, "bf16")
     ref = orc.PoolRef(sh, 1, 40, ssm_dtype, "bf16")
     for i, s in enumerate(c["slots"]):
@@ -120,6 +117,59 @@ def test_varlen_prefill_with_seeds_and_checkpoints(ssm_dtype, Q):
         assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= tol, s
         assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
     assert untouched(before_s, pool.ssm, written) and untouched(before_c, pool.conv, written)
+
+
+@pytest.mark.parametrize("ssm_dtype,Q", [("bf16", 256), ("bf16", 64), ("bf16", 48), ("f32", 256), ("f32", 32),
+                                         ("f32", 80)])
+def test_varlen_prefill_with_seeds_and_checkpoints(ssm_dtype, Q):
+    c = _varlen_case(ssm_dtype, Q, seed=100 + Q)
+    log(f"case: varlen prefill lens={c['lens'].tolist()} ssm={ssm_dtype} Q={Q} interval={c['interval']}")
+    _check_varlen(c, ssm_dtype, Q)
+
+
+# (heads, head_dim, d_state, groups, conv kernel): the supported head_dim / d_state sizes, group
+# counts other than a power of two, and every conv width; the 128 x 128 shape does not fit the
+# per-group output kernel's LDS staging and takes the per-head kernel with single planes
+SHAPES = [(4, 16, 16, 1, 4), (4, 32, 64, 2, 3), (6, 64, 32, 3, 2), (4, 128, 128, 2, 4)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda t: "H%dP%dN%dG%dW%d" % t)
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_varlen_prefill_other_shapes(shape, ssm_dtype):
+    sh = synth.Shape(*shape)
+    Q = 64
+    c = _varlen_case(ssm_dtype, Q, seed=300 + sum(shape), sh=sh)
+    log(f"case: varlen prefill shape={shape} ssm={ssm_dtype} Q={Q}")
+    _check_varlen(c, ssm_dtype, Q)
+
+
+def test_prefill_with_unaligned_z_and_y_rows_matches_aligned():
+    """z and y rows that are not 16-byte aligned take the element-wise output path; the values
+    are computed the same way, so the outputs agree bit for bit with the aligned call."""
+    c = _varlen_case("bf16", 64, seed=7)
+    sh, T = c["sh"], int(c["cu"][-1])
+    outs = []
+    for aligned in (True, False):
+        pool = make_pool(sh, 1, 40, "bf16", "bf16")
+        for i, s in enumerate(c["slots"]):
+            put_slot(pool, 0, int(s), c["ssm0"][i], c["conv0"][i])
+        x, B, C = pool.split_xbc(dev(c["u"], "bf16"))
+        zz = dev(c["z"], "bf16")
+        if aligned:
+            z = zz
+            y = torch.empty((T, sh.intermediate), dtype=torch.bfloat16, device="cuda")
+        else:   # views one element into wider rows: odd byte offsets and row pitches
+            zb = torch.zeros((T, sh.intermediate + 1), dtype=torch.bfloat16, device="cuda")
+            zb[:, 1:] = zz
+            z = zb[:, 1:]
+            y = torch.empty((T, sh.intermediate + 1), dtype=torch.bfloat16, device="cuda")[:, 1:]
+        pool.prefill(0, weights(c["params"]), c["cu"], c["slots"], c["has_init"], x, B, C, z,
+                     dev(c["dt"], "bf16"), y, start_pos=c["start"], chunk_size=64, ckpt_interval=c["interval"],
+                     ckpt_slots=c["ck"])
+        torch.cuda.synchronize()
+        outs.append((y.contiguous(), raw_bytes(pool.ssm)))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
 
 
 def test_prefill_8192_tokens_from_zero_state():
