@@ -140,3 +140,41 @@ def test_fp32_state_decode_at_8b_shape():
     assert rel_err(host(y), y_ref) <= TOL["f32"]
     for i, s in enumerate(slots):
         assert rel_err(host(pool.ssm[0, int(s)]), ref.ssm[0, i]) <= TOL["f32"]
+
+
+# (heads, head_dim, d_state, groups, conv kernel): every supported d_state, head_dim other than 64,
+# group counts other than a power of two and every conv width
+DECODE_SHAPES = [(4, 32, 32, 2, 2), (6, 64, 64, 3, 3), (4, 128, 256, 1, 4), (8, 16, 16, 4, 4)]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda t: "H%dP%dN%dG%dW%d" % t)
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_decode_other_shapes(shape, ssm_dtype):
+    sh = synth.Shape(*shape)
+    rng = np.random.default_rng(500 + sum(shape))
+    params = synth.layer_params(rng, sh)
+    slots = np.array([6, 1, 9, 3, 12], np.int32)
+    n = len(slots)
+    io = ssm_dtype
+    log(f"case: decode shape={shape} ssm={ssm_dtype}, {n} rows, 4 steps")
+    ssm0 = synth.cast_exact(synth.normal(rng, (n, sh.nheads, sh.head_dim, sh.d_state), 0.1), ssm_dtype)
+    conv0 = synth.cast_exact(synth.normal(rng, (n, sh.conv_dim, sh.conv_kernel - 1), 0.1), "bf16")
+    pool = make_pool(sh, 1, 16, ssm_dtype, "bf16")
+    ref = orc.PoolRef(sh, 1, 16, ssm_dtype, "bf16")
+    for i, s in enumerate(slots):
+        put_slot(pool, 0, int(s), ssm0[i], conv0[i])
+        ref.ssm[0, s], ref.conv[0, s] = ssm0[i], conv0[i]
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    W = weights(params)
+    sl = torch.from_numpy(slots).cuda()
+    y = torch.empty((n, sh.intermediate), dtype=torch.float32 if io == "f32" else torch.bfloat16, device="cuda")
+    for t in range(4):
+        u, z, dt = synth._tokens(rng, sh, n, io)
+        x, B, C = pool.split_xbc(dev(u, io))
+        pool.decode_step(0, W, sl, x, B, C, dev(z, io), dev(dt, io), y, slots_host=slots)
+        y_ref = orc.decode_step(ref, 0, params, slots, u, z, dt, io)
+        assert rel_err(host(y), y_ref) <= TOL[ssm_dtype], t
+    for i, s in enumerate(slots):
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= TOL[ssm_dtype]
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s])
+    assert untouched(before_s, pool.ssm, slots) and untouched(before_c, pool.conv, slots)
