@@ -58,6 +58,14 @@ template <typename T> __device__ __forceinline__ T load_uniform(const T* p) {
   return __builtin_bit_cast(T, w);
 }
 
+// A wave-uniform value the compiler cannot see through.  Folding it into an index inside a
+// loop keeps the compiler from hoisting everything derived from that index out of the loop
+// (which, for values that are cheap to recompute, costs registers the loop needs).
+__device__ __forceinline__ int opaque_uniform(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value, so that
 // branches on it are scalar branches rather than exec-masked ones.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -967,7 +975,7 @@ template <int P, int N> struct GroupLds {
   static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes: sA, sD, sCw
   static constexpr int O_OFF = F_OFF + 3 * 256 * 4;            // bytes: output staging
   static constexpr int BYTES = O_OFF + 8 * 16 * LDO * 4;
-  static constexpr bool FITS = BYTES <= 160 * 1024;
+  static constexpr bool FITS = BYTES <= 160 * 1024 && P <= 64;   // P = 128 needs more registers than a wave has
   static constexpr int IT_BR = (QM * (N / 8) + 511) / 512;
   static constexpr int IT_XT = (P * (QM / 8) + 511) / 512;
   static constexpr int IT_H = (P * (N / 8) + 511) / 512;
@@ -1009,15 +1017,6 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   float* const sO = reinterpret_cast<float*>(smem_raw + L::O_OFF) + wave * 16 * L::LDO;
   const bool zpre = a.io_bf16 && a.zy_vec;
 
-  // the chunk's B rows -> LDS, once for all heads
-  {
-    TilePrefetch<1, L::IT_BR> pb;
-    pb.load(a.Br + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
-    pb.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
-  }
-  Frag<false> cf[2][NK];
-  load_c_frags<false, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
-
   TilePrefetch<1, L::IT_XT> px;
   TilePrefetch<1, L::IT_H> ph;
   float pa, pd, pr;
@@ -1031,6 +1030,50 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
     pr = dAh[min(j | 31, len - 1)];
   };
   prefetch(h0);
+
+  // G^T = B C^T for this wave's row tiles, once for all heads.  The wave's 9 (row tile, K-step)
+  // slots up to the diagonals: tile 0 (rows of tile w) has K-steps 0 .. w/2, tile 1 (tile
+  // 15 - w) has K-steps 0 .. 7 - w/2; slot s belongs to tile 0 when s <= w/2.
+  const int w2 = wave >> 1;
+  floatx4 Gs[9][2];
+  {
+    TilePrefetch<1, L::IT_BR> pb;
+    pb.load(a.Br + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
+    Frag<false> cf[2][NK];
+    load_c_frags<false, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
+    pb.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
+    __syncthreads();
+#pragma clang loop unroll(full)
+    for (int sl = 0; sl < 9; ++sl) {
+      const bool t1 = sl > w2;
+      const int jk = 32 * (t1 ? sl - w2 - 1 : sl);
+      Gs[sl][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      Gs[sl][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (!((t1 ? v1 : v0) && jk < len)) continue;
+      Frag<false> fb[2][NK];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          fb[jt][ks] = lds_frag<false>(sBr, 0, L::LDB, jk + jt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+          if (N < 32) {
+#pragma unroll
+            for (int e = 4; e < 8; ++e) fb[jt][ks].hi[e] = bf_of(0);
+          }
+        }
+      }
+      if (t1) gt_tile<false, NK>(cf[1], fb, Gs[sl]);
+      else gt_tile<false, NK>(cf[0], fb, Gs[sl]);
+    }
+  }
+  // the chunk's C rows replace the B rows in LDS, for C h_in of every head
+  __syncthreads();
+  {
+    TilePrefetch<1, L::IT_BR> pc;
+    pc.load(a.Cr + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
+    pc.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
+  }
+  const u16* const sC = sBr;
 
   for (int hh = 0; hh < heads_per_wg; ++hh) {
     const int h = h0 + hh;
@@ -1064,25 +1107,34 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
     }
     prefetch(min(h + 1, h0 + heads_per_wg - 1));   // unconditional: one straight path
 
-    // the entering-state term exp(a_i) C_i h_in
+    // the entering-state term exp(a_i) C_i h_in (C rows past the chunk are zero)
     floatx4 acc[2][PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       acc[0][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
       acc[1][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      Frag<false> fh[NK];
+    }
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        fh[ks] = lds_frag<false>(sH, 0, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
-        if (N < 32) {
+    for (int ks = 0; ks < NK; ++ks) {
+      const int kn = N >= 32 ? ks * 32 : 0;
+      Frag<false> fc0 = lds_frag<false>(sC, 0, L::LDB, rts[0] * 16 + l16, kn, q);
+      Frag<false> fc1 = lds_frag<false>(sC, 0, L::LDB, rts[1] * 16 + l16, kn, q);
+      Frag<false> fh[PT];
 #pragma unroll
-          for (int e = 4; e < 8; ++e) fh[ks].hi[e] = bf_of(0);
+      for (int pt = 0; pt < PT; ++pt) fh[pt] = lds_frag<false>(sH, 0, L::LDH, pt * 16 + l16, kn, q);
+      if (N < 32) {   // upper K half is padding
+#pragma unroll
+        for (int e = 4; e < 8; ++e) {
+          fc0.hi[e] = bf_of(0);
+          fc1.hi[e] = bf_of(0);
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) fh[pt].hi[e] = bf_of(0);
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        acc[0][pt] = mma<false>(cf[0][ks], fh[ks], acc[0][pt]);
-        acc[1][pt] = mma<false>(cf[1][ks], fh[ks], acc[1][pt]);
+      for (int pt = 0; pt < PT; ++pt) {
+        acc[0][pt] = mma<false>(fc0, fh[pt], acc[0][pt]);
+        acc[1][pt] = mma<false>(fc1, fh[pt], acc[1][pt]);
       }
     }
 #pragma unroll
@@ -1096,41 +1148,17 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
       }
     }
 
-    // (M o L) X over the K-steps up to each row tile's diagonal; all operands are in LDS.
-    // G^T is built one 16-token half at a time and the x fragments are read after it, which
-    // keeps the fragments live at any moment to about 16 registers.
-    for (int jk = 0; jk < len; jk += 32) {
-      const bool a0 = v0 && jk <= rts[0] * 16 + 15;
-      const bool a1 = v1 && jk <= rts[1] * 16 + 15;
-      if (!(a0 || a1)) break;   // tile 1 ends last; past it there is nothing left for this wave
-      floatx4 g0[2], g1[2];
+    // (M o L) X: this head's decay mask on each stored G^T slot, times the x fragments.  The
+    // slot offsets go through an opaque zero so the per-slot index work stays inside the loop.
+    const int zero = opaque_uniform(0);
+#pragma clang loop unroll(full)
+    for (int sl = 0; sl < 9; ++sl) {
+      const bool t1 = sl > w2;
+      const int jk = 32 * (t1 ? sl - w2 - 1 : sl) + zero;
+      if (!((t1 ? v1 : v0) && jk < len)) continue;
+      Frag<false> fx[PT];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        Frag<false> fb[NK];
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-          fb[ks] = lds_frag<false>(sBr, 0, L::LDB, jk + jt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
-          if (N < 32) {
-#pragma unroll
-            for (int e = 4; e < 8; ++e) fb[ks].hi[e] = bf_of(0);
-          }
-        }
-        g0[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        g1[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (a0 && a1) {
-#pragma unroll
-          for (int ks = 0; ks < NK; ++ks) {
-            g0[jt] = mma<false>(fb[ks], cf[0][ks], g0[jt]);
-            g1[jt] = mma<false>(fb[ks], cf[1][ks], g1[jt]);
-          }
-        } else if (a1) {
-#pragma unroll
-          for (int ks = 0; ks < NK; ++ks) g1[jt] = mma<false>(fb[ks], cf[1][ks], g1[jt]);
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < NK; ++ks) g0[jt] = mma<false>(fb[ks], cf[0][ks], g0[jt]);
-        }
-      }
+      for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
       float cw[8];
       {
         const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
@@ -1139,13 +1167,14 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
         for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
       }
       const float aref = sA[min(jk + 31, len - 1)];
-      const Frag<false> m0 = decay_mask<false>(g0, rts[0], jk, len, aref, cw, sA, sD, Dh, q, l16);
-      const Frag<false> m1 = decay_mask<false>(g1, rts[1], jk, len, aref, cw, sA, sD, Dh, q, l16);
+      if (t1) {
+        const Frag<false> m = decay_mask<false>(Gs[sl], rts[1], jk, len, aref, cw, sA, sD, Dh, q, l16);
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const Frag<false> fx = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
-        if (a0) acc[0][pt] = mma<false>(m0, fx, acc[0][pt]);
-        if (a1) acc[1][pt] = mma<false>(m1, fx, acc[1][pt]);
+        for (int pt = 0; pt < PT; ++pt) acc[1][pt] = mma<false>(m, fx[pt], acc[1][pt]);
+      } else {
+        const Frag<false> m = decay_mask<false>(Gs[sl], rts[0], jk, len, aref, cw, sA, sD, Dh, q, l16);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[0][pt] = mma<false>(m, fx[pt], acc[0][pt]);
       }
     }
 
