@@ -169,7 +169,7 @@ template <int NPL, int ITEMS> struct TilePrefetch {
       const int idx = tid + it * nthreads;
       const int r = idx / vpr, c = (idx % vpr) * 8;
       const bool in = idx < rows * vpr && r < valid_rows && c < valid_cols;
-      const int64_t off = in ? r * src_ld + c : 0;
+      const int off = in ? r * (int)src_ld + c : 0;   // offsets inside one tile fit in 32 bits
 #pragma unroll
       for (int pl = 0; pl < NPL; ++pl) v[it][pl] = *reinterpret_cast<const u16x8*>(src + pl * src_plane + off);
     }
@@ -190,6 +190,26 @@ template <int NPL, int ITEMS> struct TilePrefetch {
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = (in && c + e < valid_cols) ? x[e] : u16(0);
           u16* d = dst + pl * dst_plane + r * dst_ld + c;
+          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+        }
+      }
+    }
+  }
+
+  // store() for a tile known to be entirely valid: no masking.
+  __device__ __forceinline__ void store_full(u16* dst, int64_t dst_plane, int dst_ld, int rows, int cols, int tid,
+                                             int nthreads) const {
+    const int vpr = cols / 8;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int idx = tid + it * nthreads;
+      if (idx < rows * vpr) {
+        const int r = idx / vpr, c = (idx % vpr) * 8;
+#pragma unroll
+        for (int pl = 0; pl < NPL; ++pl) {
+          u16* d = dst + pl * dst_plane + r * dst_ld + c;
+          const u16x8 x = v[it][pl];
           *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
           *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
         }
@@ -534,8 +554,13 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
 
     for (int jb = 0; jb < len; jb += kWB) {
       __syncthreads();   // all reads of the previous block are done
-      px.store(sXT, P * LDX, LDX, P, kWB, P, len - jb, tid, kStateThreads);
-      pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+      if (jb + kWB <= len) {   // whole block inside the chunk (uniform)
+        px.store_full(sXT, P * LDX, LDX, P, kWB, tid, kStateThreads);
+        pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);
+      } else {
+        px.store(sXT, P * LDX, LDX, P, kWB, P, len - jb, tid, kStateThreads);
+        pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+      }
       __syncthreads();
       {   // the next block, or the next chunk's first block; one straight path (past the
           // segment's last block the current block is fetched again and not used)
