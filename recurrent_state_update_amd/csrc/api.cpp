@@ -127,9 +127,11 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   L->meta_bytes = align_up(L->off_windows + L->nw_max * sizeof(m2::WindowEntry), 256);
   const uint64_t rows = L->nc_max * (uint64_t)Q;          // chunk-blocked rows
   uint64_t v;
-  if (!mul_ok(rows, (uint64_t)sh.H * sh.P, &L->plane_xT)) return false;
-  if (!mul_ok(rows, (uint64_t)sh.G * sh.N, &L->plane_Bt)) return false;
-  L->plane_Br = L->plane_Cr = L->plane_Bt;
+  const uint64_t brows = L->nc_max * (uint64_t)((Q + m2::kPB - 1) / m2::kPB * m2::kPB);   // whole blocks
+  if (!mul_ok(brows, (uint64_t)sh.H * sh.P, &L->plane_xT)) return false;
+  if (!mul_ok(brows, (uint64_t)sh.G * sh.N, &L->plane_Bt)) return false;
+  if (!mul_ok(rows, (uint64_t)sh.G * sh.N, &L->plane_Br)) return false;
+  L->plane_Cr = L->plane_Br;
   uint64_t off = L->meta_bytes;
   const uint64_t planes[4] = {L->plane_xT, L->plane_Bt, L->plane_Br, L->plane_Cr};
   uint64_t* offs[4] = {&L->off_xT, &L->off_Bt, &L->off_Br, &L->off_Cr};

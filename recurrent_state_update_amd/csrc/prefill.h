@@ -20,6 +20,8 @@ struct WindowEntry {  // one conv-window write: window after `tau` rows of seque
   int32_t seq, tau, slot, pad;
 };
 
+constexpr int kPB = 64;   // tokens per block of the transposed operand planes
+
 struct PrefillParams {
   void* ssm;
   void* conv;
@@ -47,8 +49,10 @@ struct PrefillParams {
   const float* conv_b;
   // workspace arrays.  Post-conv activations as bf16 operand planes (one plane, or hi and lo
   // planes for fp32-faithful products), chunk-blocked with Q rows per chunk:
-  uint16_t* xT;          // [planes][chunks][H][P][Q]   x, tokens contiguous
-  uint16_t* Bt;          // [planes][chunks][G][N][Q]   B, tokens contiguous
+  // x and B transposed in blocks of kPB tokens (QB = ceil(Q / kPB) blocks per chunk), each
+  // block contiguous: [planes][chunks][H][QB][P][kPB] and [planes][chunks][G][QB][N][kPB]
+  uint16_t* xT;
+  uint16_t* Bt;
   uint16_t* Br;          // [planes][chunks][Q][G*N]    B, channels contiguous
   uint16_t* Cr;          // [planes][chunks][Q][G*N]    C, channels contiguous
   int64_t xT_plane, Bt_plane, Br_plane, Cr_plane;   // elements per plane

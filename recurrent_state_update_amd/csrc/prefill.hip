@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
 #pragma unroll
         for (int k = 0; k < W; ++k) v += w[e][k] * in[r + k][e];
         v = j0 + r < len ? silu(v) : 0.f;
-        if (SPLIT) split2(v, out[0][r][e], out[1][r][e]);
+        if (SPLIT) split2(v, out[0][r][e], out[NPL - 1][r][e]);
         else out[0][r][e] = bits_of(from_f32<bf16>(v));
       }
     }
@@ -358,13 +358,14 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
     if (cc >= I + GN) continue;
     u16* dst;
     int64_t pstride;
+    const int QB = (Q + kPB - 1) / kPB, blk = (8 * g) / kPB, off = (8 * g) % kPB;
     if (cc < I) {
       const int h = cc / P, p = cc % P;
-      dst = a.xT + ((chunk * H + h) * P + p) * Q + 8 * g;
+      dst = a.xT + (((chunk * H + h) * QB + blk) * P + p) * kPB + off;
       pstride = a.xT_plane;
     } else {
       const int gg = (cc - I) / N, n = (cc - I) % N;
-      dst = a.Bt + ((chunk * G + gg) * N + n) * Q + 8 * g;
+      dst = a.Bt + (((chunk * G + gg) * QB + blk) * N + n) * kPB + off;
       pstride = a.Bt_plane;
     }
 #pragma unroll
@@ -409,16 +410,16 @@ __global__ __launch_bounds__(256) void dt_kernel(PrefillParams a) {
   }
 }
 
-// State tiles (P/16 x N/16 of 16x16) spread over the 8 waves of a workgroup.  When the
+// State tiles (P/16 x N/16 of 16x16) spread over the NW waves of a workgroup.  When the
 // shape allows, each wave owns PER_WAVE tiles of one tile row (ALIGNED), so the x-side operand
-// of the state product is built once per K-step and shared by all of the wave's tiles.
-template <int P, int N> struct StateTiles {
+// of the state product is read once per K-step and shared by all of the wave's tiles.
+template <int P, int N, int NW> struct StateTiles {
   static constexpr int PT = P / 16;
   static constexpr int NT = N / 16;
   static constexpr int TOTAL = PT * NT;
-  static constexpr bool ALIGNED = PT <= 8 && 8 % PT == 0 && NT % (8 / PT) == 0;
-  static constexpr int WPR = ALIGNED ? 8 / PT : 1;                        // waves per tile row
-  static constexpr int PER_WAVE = ALIGNED ? NT / WPR : (TOTAL + 7) / 8;
+  static constexpr bool ALIGNED = PT <= NW && NW % PT == 0 && NT % (NW / PT) == 0;
+  static constexpr int WPR = ALIGNED ? NW / PT : 1;                       // waves per tile row
+  static constexpr int PER_WAVE = ALIGNED ? NT / WPR : (TOTAL + NW - 1) / NW;
   __device__ static bool valid(int w, int m) { return ALIGNED || w * PER_WAVE + m < TOTAL; }
   __device__ static int pt(int w, int m) { return ALIGNED ? w / WPR : (w * PER_WAVE + m) / NT; }
   __device__ static int nt(int w, int m) { return ALIGNED ? (w % WPR) * PER_WAVE + m : (w * PER_WAVE + m) % NT; }
@@ -440,7 +441,7 @@ __device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N
 //   EMIT = true:  from the state entering the segment; writes the state entering every chunk
 //                 as bf16 operand planes for the output kernel, and after each chunk the
 //                 checkpoint and final states rounded into their slots.
-constexpr int kWB = 64;
+constexpr int kWB = kPB;   // one block of the transposed planes
 
 template <bool SPLIT, int P, int N> struct WalkLds {
   static constexpr int NPL = SPLIT ? 2 : 1;
@@ -459,7 +460,7 @@ template <bool SPLIT, int P, int N> struct WalkLds {
 template <bool SPLIT, int P, int N, bool EMIT>
 __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams a) {
   typedef WalkLds<SPLIT, P, N> L;
-  typedef StateTiles<P, N> ST;
+  typedef StateTiles<P, N, kStateThreads / 64> ST;
   constexpr int NPL = L::NPL, LDX = L::LDX;
   __shared__ __align__(16) u16 smem_w[L::U16S];
   __shared__ __align__(16) float sW[256];
@@ -492,8 +493,11 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
   TilePrefetch<NPL, L::IT_BT> pb;
   const int c_end = sg.chunk0 + sg.nchunk;
   auto prefetch = [&](int c, int jb, int len) {
-    px.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kWB, P, len - jb, tid, kStateThreads);
-    pb.load(a.Bt + (((int64_t)c * G + g) * N) * Q + jb, a.Bt_plane, Q, N, kWB, N, len - jb, tid, kStateThreads);
+    const int QB = (Q + kPB - 1) / kPB;
+    px.load(a.xT + (((int64_t)c * H + h) * QB + jb / kPB) * P * kPB, a.xT_plane, kPB, P, kWB, P, len - jb, tid,
+            kStateThreads);
+    pb.load(a.Bt + (((int64_t)c * G + g) * QB + jb / kPB) * N * kPB, a.Bt_plane, kPB, N, kWB, N, len - jb, tid,
+            kStateThreads);
   };
   // a chunk's cumsum and Delta at token tid and its last cumsum, loaded one chunk ahead
   float wa, wd, wl;
@@ -554,13 +558,38 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
 
     for (int jb = 0; jb < len; jb += kWB) {
       __syncthreads();   // all reads of the previous block are done
-      if (jb + kWB <= len) {   // whole block inside the chunk (uniform)
-        px.store_full(sXT, P * LDX, LDX, P, kWB, tid, kStateThreads);
-        pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);
-      } else {
-        px.store(sXT, P * LDX, LDX, P, kWB, P, len - jb, tid, kStateThreads);
-        pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+      // x goes to LDS already scaled by w_j = exp(a_last - a_j) Delta_j (one rounding of the
+      // product, as the operand needs), so the K-steps read it as a finished fragment
+#pragma unroll
+      for (int it = 0; it < L::IT_XT; ++it) {
+        const int idx = tid + it * kStateThreads;
+        if (idx < P * (kWB / 8)) {
+          const int r = idx / (kWB / 8), cc = (idx % (kWB / 8)) * 8;
+          const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + cc]);
+          const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + cc + 4]);
+          u16x8 hv, lv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float xv = f_of(px.v[it][0][e]);
+            if (SPLIT) xv += f_of(px.v[it][NPL - 1][e]);
+            xv = jb + cc + e < len ? xv * (e < 4 ? w0[e] : w1[e - 4]) : 0.f;
+            u16 hi, lo = 0;
+            if (SPLIT) split2(xv, hi, lo);
+            else hi = bits_of(from_f32<bf16>(xv));
+            hv[e] = hi;
+            lv[e] = lo;
+          }
+          u16* d = sXT + r * LDX + cc;
+          *reinterpret_cast<u16x4*>(d) = u16x4{hv[0], hv[1], hv[2], hv[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{hv[4], hv[5], hv[6], hv[7]};
+          if (SPLIT) {
+            *reinterpret_cast<u16x4*>(d + P * LDX) = u16x4{lv[0], lv[1], lv[2], lv[3]};
+            *reinterpret_cast<u16x4*>(d + P * LDX + 4) = u16x4{lv[4], lv[5], lv[6], lv[7]};
+          }
+        }
       }
+      if (jb + kWB <= len) pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);   // uniform
+      else pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
       __syncthreads();
       {   // the next block, or the next chunk's first block; one straight path (past the
           // segment's last block the current block is fetched again and not used)
@@ -571,16 +600,8 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
 #pragma unroll
       for (int kb = 0; kb < kWB; kb += 32) {
         if (jb + kb >= len) break;
-        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + kb + 4 * q]);
-        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + kb + 16 + 4 * q]);
-        // x-side operand of tile row pt: (w x)^T over the K-step's tokens
-        auto xfrag = [&](int pt) {
-          float v[8];
-          lds_vals<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q, v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v[e] *= w0[e]; v[e + 4] *= w1[e]; }
-          return make_frag<SPLIT>(v);
-        };
+        // x-side operand of tile row pt: (w x)^T over the K-step's tokens, staged scaled
+        auto xfrag = [&](int pt) { return lds_frag<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q); };
         if (ST::ALIGNED) {
           const Frag<SPLIT> fa = xfrag(ST::pt(wave, 0));
           Frag<SPLIT> fb[ST::PER_WAVE];
@@ -809,7 +830,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_out_kernel(PrefillParams a
   TilePrefetch<NPL, L::IT_XT> pxt;
   auto prefetch = [&](int jb) {
     pbr.load(a.Br + ((int64_t)c * Q + jb) * GN + g * N, a.Br_plane, GN, kOB, N, len - jb, N, tid, kScanThreads);
-    pxt.load(a.xT + (((int64_t)c * H + h) * P) * Q + jb, a.xT_plane, Q, P, kOB, P, len - jb, tid, kScanThreads);
+    pxt.load(a.xT + (((int64_t)c * H + h) * ((Q + kPB - 1) / kPB) + jb / kPB) * P * kPB + jb % kPB, a.xT_plane,
+             kPB, P, kOB, P, len - jb, tid, kScanThreads);
   };
   prefetch(0);
 
@@ -1041,12 +1063,13 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   const bool v1 = rts[1] < nrt && rts[1] * 16 < len;
   float* const sO = reinterpret_cast<float*>(smem_raw + L::O_OFF) + wave * 16 * L::LDO;
   const bool zpre = a.io_bf16 && a.zy_vec;
+  const int QB = (Q + kPB - 1) / kPB;
 
   TilePrefetch<1, L::IT_XT> px;
   TilePrefetch<1, L::IT_H> ph;
   float pa, pd, pr;
   auto prefetch = [&](int h) {
-    px.load(a.xT + (((int64_t)c * H + h) * P) * Q, 0, Q, P, QM, P, len, tid, 512);
+    px.load(a.xT + ((int64_t)c * H + h) * QB * P * kPB, 0, kPB, QB * P, kPB, QB * P, kPB, tid, 512);
     ph.load(a.hin + ((int64_t)c * H + h) * P * N, 0, N, P, N, P, N, tid, 512);
     const int j = min(tid, len - 1);
     const float* dAh = a.dA + (int64_t)h * T + ch.t0;
@@ -1104,7 +1127,21 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
     const int h = h0 + hh;
     const float Dh = load_uniform(&a.D[h]);
     __syncthreads();   // the previous head's reads of sXT, sH and the tables are done
-    px.store(sXT, 0, L::LDX, P, QM, P, len, tid, 512);
+    // x blocks [QB][P][kPB] -> sXT[p][token]; tokens past the chunk are zeroed
+#pragma unroll
+    for (int it = 0; it < L::IT_XT; ++it) {
+      const int idx = tid + it * 512;
+      const int r = idx / (kPB / 8), cc = (idx % (kPB / 8)) * 8;
+      if (r < QB * P) {
+        const int blk = r / P, p = r % P, j = blk * kPB + cc;
+        u16x8 x = px.v[it][0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = j + e < len ? x[e] : u16(0);
+        u16* d = sXT + p * L::LDX + j;
+        *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+      }
+    }
     ph.store(sH, 0, L::LDH, P, N, P, N, tid, 512);
     if (tid < 256) {
       const bool ok = tid < len;
