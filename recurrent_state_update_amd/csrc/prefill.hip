@@ -26,6 +26,8 @@
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
 // otherwise operands are single bf16 planes with fp32 accumulation.
+#include <type_traits>
+
 #include "device_common.h"
 #include "prefill.h"
 
@@ -273,14 +275,23 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
     if (c < I) { src = a.x; col = c; stride = a.x_stride; }
     else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
     else { src = a.C; col = c - I - GN; stride = a.C_stride; }
-    // inputs: rows outside the sequence read the chunk's first row and are replaced below
-    float in[R + W - 1][8];
+    // inputs: rows outside the sequence read the chunk's first row and are replaced below.
+    // bf16 rows stay packed until used (half the registers of fp32 copies).
+    typedef typename std::conditional<IOBF, u16x8, float[8]>::type Row;
+    Row in_raw[R + W - 1];
 #pragma unroll
     for (int k = 0; k < R + W - 1; ++k) {
       const int tau = ch.tau0 + j0 - (W - 1) + k;   // offset inside the sequence
       const bool ok = tau >= 0 && j0 - (W - 1) + k < len;
-      load_row8<IOBF>(src, (ok ? sq.t0 + tau : ch.t0) * stride + col, in[k]);
+      const int64_t i = (ok ? sq.t0 + tau : ch.t0) * stride + col;
+      if constexpr (IOBF) in_raw[k] = *reinterpret_cast<const u16x8*>(static_cast<const u16*>(src) + i);
+      else load_row8<false>(src, i, in_raw[k]);
     }
+    auto in_at = [&](int k, int e) -> float {
+      if constexpr (IOBF) return f_of(in_raw[k][e]);
+      else return in_raw[k][e];
+    };
+    float halo[W - 1][8];   // the rows before the sequence start, when the chunk begins it
     float w[8][W], bias[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -288,7 +299,13 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
       for (int k = 0; k < W; ++k) w[e][k] = a.conv_w[(int64_t)(c + e) * W + k];
       bias[e] = a.conv_b[c + e];
     }
-    if (ch.tau0 + j0 < W - 1) {   // halo before the sequence start: the slot's window or zeros
+    const bool seq_start = ch.tau0 + j0 < W - 1;   // uniform per thread group; rare
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) halo[k][e] = in_at(k, e);
+    }
+    if (seq_start) {   // halo before the sequence start: the slot's window or zeros
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) {
         const int tau = ch.tau0 + j0 - (W - 1) + k;
@@ -300,50 +317,39 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
               const int64_t wi = ((int64_t)sq.slot * Cd + c + e) * (W - 1) + (W - 1 + tau);
               v = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
             }
-            in[k][e] = v;
+            halo[k][e] = v;
           }
         }
       }
     }
-    // out[pl][r][e]: token j0 + r, channel c + e (zero past the chunk)
-    u16 out[NPL][R][8];
+    // token j0 + r, channels c .. c+7 (zero past the chunk): B and C rows straight to global,
+    // x and B element by element into the channel-major LDS tile
+    u16* const brow = c < I + GN ? a.Br + (chunk * Q + j0) * GN + (c - I) : a.Cr + (chunk * Q + j0) * GN + (c - I - GN);
+    const int64_t bplane = c < I + GN ? a.Br_plane : a.Cr_plane;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      u16x8 hv, lv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v = bias[e];
 #pragma unroll
-        for (int k = 0; k < W; ++k) v += w[e][k] * in[r + k][e];
+        for (int k = 0; k < W; ++k) v += w[e][k] * (r + k < W - 1 ? halo[r + k][e] : in_at(r + k, e));
         v = j0 + r < len ? silu(v) : 0.f;
-        if (SPLIT) split2(v, out[0][r][e], out[NPL - 1][r][e]);
-        else out[0][r][e] = bits_of(from_f32<bf16>(v));
+        u16 hi, lo = 0;
+        if (SPLIT) split2(v, hi, lo);
+        else hi = bits_of(from_f32<bf16>(v));
+        hv[e] = hi;
+        lv[e] = lo;
       }
-    }
-    if (c >= I) {   // B and C rows, channels contiguous
-      u16* dst = c < I + GN ? a.Br + (chunk * Q + j0) * GN + (c - I) : a.Cr + (chunk * Q + j0) * GN + (c - I - GN);
-      const int64_t pstride = c < I + GN ? a.Br_plane : a.Cr_plane;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (j0 + r < len) {
-#pragma unroll
-          for (int pl = 0; pl < NPL; ++pl) {
-            u16x8 v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = out[pl][r][e];
-            *reinterpret_cast<u16x8*>(dst + pl * pstride + (int64_t)r * GN) = v;
-          }
-        }
+      if (c >= I && j0 + r < len) {
+        *reinterpret_cast<u16x8*>(brow + (int64_t)r * GN) = hv;
+        if (SPLIT) *reinterpret_cast<u16x8*>(brow + bplane + (int64_t)r * GN) = lv;
       }
-    }
-    if (c < I + GN) {   // x and B -> channel-major LDS tile
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) {
+      if (c < I + GN) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          u16x8 v;
-#pragma unroll
-          for (int r = 0; r < R; ++r) v[r] = out[pl][r][e];
-          *reinterpret_cast<u16x8*>(s_t + pl * PLANE + (8 * oc + e) * kConvLD + j0) = v;
+          s_t[(8 * oc + e) * kConvLD + j0 + r] = hv[e];
+          if (SPLIT) s_t[PLANE + (8 * oc + e) * kConvLD + j0 + r] = lv[e];
         }
       }
     }
