@@ -676,21 +676,27 @@ __global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) hs[e] = to_f32(src[e]);
   }
+  // D segments at a time: their end states are all requested before the first is used (one
+  // straight path; past the sequence's last segment the last one is read again and not used),
+  // and the log decays come through scalar loads
   constexpr int D = 8;
   for (int s0 = 0; s0 < sq.nseg; s0 += D) {
     floatx4 sc[D];
+    float dec[D];
+    bool step[D];
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      const int s = sq.seg0 + s0 + k;
-      if (s0 + k < sq.nseg && !load_uniform(&a.segs[s]).is_last)
-        sc[k] = *reinterpret_cast<const floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off);
+      const int s = sq.seg0 + min(s0 + k, sq.nseg - 1);
+      step[k] = s0 + k < sq.nseg && !load_uniform(&a.segs[s]).is_last;
+      dec[k] = load_uniform(&a.seg_decay[(int64_t)s * H + h]);
+      sc[k] = *reinterpret_cast<const floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off);
     }
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       if (s0 + k < sq.nseg) {
         const int s = sq.seg0 + s0 + k;
         *reinterpret_cast<floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off) = hs;
-        if (!load_uniform(&a.segs[s]).is_last) hs = __expf(a.seg_decay[(int64_t)s * H + h]) * hs + sc[k];
+        if (step[k]) hs = __expf(dec[k]) * hs + sc[k];
       }
     }
   }
