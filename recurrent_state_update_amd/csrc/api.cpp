@@ -467,7 +467,8 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
   p.io_bf16 = io_dtype == M2_BF16;
   p.y_bf16 = y_dtype == M2_BF16;
-  p.zy_vec = aligned16(z) && aligned16(y) && (z_stride * ies) % 16 == 0 && (y_stride * esize(y_dtype)) % 16 == 0;
+  p.zy_vec = aligned16(z) && aligned16(y) && (z_stride * ies) % 16 == 0 && (y_stride * esize(y_dtype)) % 16 == 0 &&
+             z_stride < ((int64_t)1 << 22) && y_stride < ((int64_t)1 << 22);
   p.sh = sh;
   p.Q = chunk_size;
   p.num_seqs = num_seqs;

@@ -26,7 +26,8 @@ struct PrefillParams {
   void* ssm;
   void* conv;
   int ssm_bf16, conv_bf16, io_bf16, y_bf16;
-  int zy_vec;          // z and y rows allow 16-byte vector access (aligned bases and row pitches)
+  int zy_vec;          // z and y rows allow 16-byte vector access (aligned bases and row pitches), and
+                       // offsets inside a chunk's rows fit in 32 bits
   LayerShape sh;
   int Q;               // chunk size
   int num_seqs, num_chunks, num_segments, num_windows, total_tokens;

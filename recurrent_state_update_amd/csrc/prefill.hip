@@ -21,7 +21,9 @@
 //   4. seg_pass_kernel    per (sequence, head): scan over segments -> state entering each segment
 //   5. state_walk_kernel  per (segment, head), from the entering state: the state entering each
 //                         chunk (operand planes), checkpoint and final states into their slots
-//   6. chunk_out_kernel   per (chunk, head): outputs (MFMA), independent across chunks
+//   6. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
+//                         C B^T formed once; chunk_out_kernel per (chunk, head) for hi/lo planes
+//                         and head_dim 128
 //   7. window_kernel      final and checkpoint conv windows (raw inputs) into their slots
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
@@ -1015,26 +1017,37 @@ __global__ __launch_bounds__(kScanThreads) void chunk_out_kernel(PrefillParams a
   }
 }
 
-// ------------------------------------------------------------------ 5b. chunk outputs, a group's heads in turn
-// Per (chunk, group, part of the group's heads), 512 threads, single bf16 operand planes.  The
-// chunk's B rows (LDS) and the C fragments of each wave's row tiles (registers) are loaded once
-// and serve all of the workgroup's heads; the next head's x, entering state and Delta tables are
-// prefetched into registers while the current head is computed, so a head's products run with
-// no barrier and no wait on global memory.  Used when the staging fits in LDS.
+// ------------------------------------------------------------------ 5b. helpers of the grouped output kernel
+// 2^x and log2(x) as the bare hardware instructions: results below 2^-126 flush to zero, which
+// only drops terms that are negligible against the rest of a sum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------ 5c. chunk outputs, a group's heads in turn
+// Per (chunk, group, part of the group's heads), 512 threads, single bf16 operand planes.  C B^T
+// depends on the chunk and group only: each wave forms its nine (row tile, K-step) slots once,
+// from the chunk's B rows staged in LDS and its C rows held as register fragments, and keeps
+// them in fp32 registers for all of the workgroup's heads; the same C fragments serve C h_in.
+// Heads alternate between two LDS buffers, so one barrier per head suffices: a head's x, entering
+// state and Delta values are requested into registers while the previous head is computed.  The
+// products are formed transposed, Y^T = h_in^T (exp(a) C)^T + X^T (M o L)^T, so that a lane's
+// accumulator holds four consecutive channels of one token: z is read and y written straight from
+// registers as pieces of token rows.  Wave w owns the row tiles w and 15 - w.  Decay factors are
+// taken as powers of two from per-head tables kept in log2 units:
+//   sA2[j] = a_j log2(e),  sB2[j] = a_j log2(e) - log2(Delta_j),  sCw[j] = exp(a_ref - a_j) Delta_j
+// (a_ref = the cumsum at the last token of j's K-step); rows past the chunk get sA2 = -inf, so
+// every factor of theirs is zero.
 template <int P, int N> struct GroupLds {
-  static constexpr int QM = 256;          // staging for the largest chunk
-  static constexpr int LDB = N + 4;       // B rows [j][n]
-  static constexpr int LDX = QM + 4;      // x transposed [p][j]
-  static constexpr int LDH = N + 4;       // entering state [p][n]
-  static constexpr int LDO = P + 4;       // output staging [row][p], fp32, one 16-row tile per wave
-  static constexpr int BR_OFF = 0;        // u16 offsets
-  static constexpr int XT_OFF = BR_OFF + QM * LDB;
-  static constexpr int H_OFF = XT_OFF + P * LDX;
-  static constexpr int U16_END = H_OFF + P * LDH;
-  static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes: sA, sD, sCw
-  static constexpr int O_OFF = F_OFF + 3 * 256 * 4;            // bytes: output staging
+  static constexpr int QM = 256;
+  static constexpr int LDB = N + 4;    // B rows [j][n] (set-up only, overlaid by the buffers)
+  static constexpr int LDX = QM + 4;   // x transposed [p][j]
+  static constexpr int LDH = N + 4;    // entering state [p][n]
+  static constexpr int BUF = P * LDX + P * LDH;   // u16 per head buffer
+  static constexpr int U16_END = 2 * BUF > QM * LDB ? 2 * BUF : QM * LDB;
+  static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes: two sets of sA2, sB2, sCw
+  static constexpr int LDO = P + 4;                              // output staging [row][p], fp32
+  static constexpr int O_OFF = F_OFF + 2 * 3 * 256 * 4;          // bytes: one 16-row tile per wave
   static constexpr int BYTES = O_OFF + 8 * 16 * LDO * 4;
-  static constexpr bool FITS = BYTES <= 160 * 1024 && P <= 64;   // P = 128 needs more registers than a wave has
+  static constexpr bool FITS = BYTES <= 160 * 1024 && P <= 64;
   static constexpr int IT_BR = (QM * (N / 8) + 511) / 512;
   static constexpr int IT_XT = (P * (QM / 8) + 511) / 512;
   static constexpr int IT_H = (P * (N / 8) + 511) / 512;
@@ -1045,17 +1058,10 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   typedef GroupLds<P, N> L;
   constexpr int PT = P / 16;
   constexpr int NK = N / 32 > 0 ? N / 32 : 1;
-  constexpr int QM = L::QM;
-  constexpr int CG = P / 8;                   // 8-column groups of an output row
-  constexpr int ZI = (16 * CG + 63) / 64;     // output items per lane per row tile
+  constexpr float kLog2e = 1.4426950408889634f;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   u16* const smem = reinterpret_cast<u16*>(smem_raw);
-  u16* const sBr = smem + L::BR_OFF;
-  u16* const sXT = smem + L::XT_OFF;
-  u16* const sH = smem + L::H_OFF;
-  float* const sA = reinterpret_cast<float*>(smem_raw + L::F_OFF);
-  float* const sD = sA + 256;
-  float* const sCw = sD + 256;   // exp(a_ref - a_j) Delta_j, a_ref = cumsum at the last token of j's K-step
+  float* const ftab = reinterpret_cast<float*>(smem_raw + L::F_OFF);
 
   const int c = blockIdx.x;
   const ChunkEntry ch = load_uniform(&a.chunks[c]);
@@ -1071,11 +1077,14 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   const int64_t T = a.total_tokens;
   const int nrt = Q / 16;
   const int rts[2] = {wave, 15 - wave};
-  const bool v0 = rts[0] < nrt && rts[0] * 16 < len;
-  const bool v1 = rts[1] < nrt && rts[1] * 16 < len;
-  float* const sO = reinterpret_cast<float*>(smem_raw + L::O_OFF) + wave * 16 * L::LDO;
-  const bool zpre = a.io_bf16 && a.zy_vec;
+  const bool vt[2] = {rts[0] < nrt && rts[0] * 16 < len, rts[1] < nrt && rts[1] * 16 < len};
   const int QB = (Q + kPB - 1) / kPB;
+  const bool zpre = a.io_bf16 && a.zy_vec;
+  const int m0 = wave >> 1;
+  const int mt[2] = {m0, 7 - m0};   // K-steps below each tile; K-step mt[t] holds its diagonal
+  constexpr int CG = P / 8;                   // 8-channel groups of an output row
+  constexpr int ZI = (16 * CG + 63) / 64;     // output items (8 channels of one token) per lane per tile
+  float* const sO = reinterpret_cast<float*>(smem_raw + L::O_OFF) + wave * 16 * L::LDO;
 
   TilePrefetch<1, L::IT_XT> px;
   TilePrefetch<1, L::IT_H> ph;
@@ -1091,176 +1100,205 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   };
   prefetch(h0);
 
-  // G^T = B C^T for this wave's row tiles, once for all heads.  The wave's 9 (row tile, K-step)
-  // slots up to the diagonals: tile 0 (rows of tile w) has K-steps 0 .. w/2, tile 1 (tile
-  // 15 - w) has K-steps 0 .. 7 - w/2; slot s belongs to tile 0 when s <= w/2.
-  const int w2 = wave >> 1;
-  floatx4 Gs[9][2];
+  // C B^T slots, fp32: below-diagonal slots of tile 0 in gb[0 .. m0-1] and of tile 1 from gb[6]
+  // downwards (constant indices for both tiles), the diagonal slots in gd
+  Frag<false> cf[2][NK];
+  floatx4 gb[7][2], gd[2][2];
   {
+    u16* const sBr = smem;
     TilePrefetch<1, L::IT_BR> pb;
-    pb.load(a.Br + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
-    Frag<false> cf[2][NK];
+    pb.load(a.Br + (int64_t)c * Q * GN + g * N, 0, GN, L::QM, N, len, N, tid, 512);
     load_c_frags<false, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
-    pb.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
+    pb.store(sBr, 0, L::LDB, L::QM, N, len, N, tid, 512);
     __syncthreads();
-#pragma clang loop unroll(full)
-    for (int sl = 0; sl < 9; ++sl) {
-      const bool t1 = sl > w2;
-      const int jk = 32 * (t1 ? sl - w2 - 1 : sl);
-      Gs[sl][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      Gs[sl][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (!((t1 ? v1 : v0) && jk < len)) continue;
+    auto slot = [&](int t, int ks, floatx4 (&out)[2]) {
       Frag<false> fb[2][NK];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) {
-          fb[jt][ks] = lds_frag<false>(sBr, 0, L::LDB, jk + jt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+        for (int kk = 0; kk < NK; ++kk) {
+          fb[jt][kk] = lds_frag<false>(sBr, 0, L::LDB, 32 * ks + jt * 16 + l16, N >= 32 ? kk * 32 : 0, q);
           if (N < 32) {
 #pragma unroll
-            for (int e = 4; e < 8; ++e) fb[jt][ks].hi[e] = bf_of(0);
+            for (int e = 4; e < 8; ++e) fb[jt][kk].hi[e] = bf_of(0);
           }
         }
       }
-      if (t1) gt_tile<false, NK>(cf[1], fb, Gs[sl]);
-      else gt_tile<false, NK>(cf[0], fb, Gs[sl]);
+      if (t == 0) gt_tile<false, NK>(cf[0], fb, out);
+      else gt_tile<false, NK>(cf[1], fb, out);
+    };
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      gb[k][0] = gb[k][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (k < m0) {
+        if (vt[0]) slot(0, k, gb[k]);
+      } else if (vt[1]) {
+        slot(1, 6 - k, gb[k]);
+      }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      gd[t][0] = gd[t][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (vt[t]) slot(t, mt[t], gd[t]);
+    }
+    __syncthreads();   // B rows are overwritten by the head buffers below
   }
-  // the chunk's C rows replace the B rows in LDS, for C h_in of every head
-  __syncthreads();
-  {
-    TilePrefetch<1, L::IT_BR> pc;
-    pc.load(a.Cr + (int64_t)c * Q * GN + g * N, 0, GN, QM, N, len, N, tid, 512);
-    pc.store(sBr, 0, L::LDB, QM, N, len, N, tid, 512);
-  }
-  const u16* const sC = sBr;
 
   for (int hh = 0; hh < heads_per_wg; ++hh) {
     const int h = h0 + hh;
-    const float Dh = load_uniform(&a.D[h]);
-    __syncthreads();   // the previous head's reads of sXT, sH and the tables are done
-    // x blocks [QB][P][kPB] -> sXT[p][token]; tokens past the chunk are zeroed
+    u16* const sXT = smem + (hh & 1) * L::BUF;
+    u16* const sH = sXT + P * L::LDX;
+    float* const sA2 = ftab + (hh & 1) * 768;
+    float* const sB2 = sA2 + 256;
+    float* const sCw = sB2 + 256;
+    // this head's x blocks [QB][P][kPB] -> sXT[p][token] (tokens past the chunk zeroed), its
+    // entering state and its tables, into the buffer last read two heads ago
+    if (len == QB * kPB) {
 #pragma unroll
-    for (int it = 0; it < L::IT_XT; ++it) {
-      const int idx = tid + it * 512;
-      const int r = idx / (kPB / 8), cc = (idx % (kPB / 8)) * 8;
-      if (r < QB * P) {
-        const int blk = r / P, p = r % P, j = blk * kPB + cc;
-        u16x8 x = px.v[it][0];
+      for (int it = 0; it < L::IT_XT; ++it) {
+        const int idx = tid + it * 512;
+        const int r = idx / (kPB / 8), cc = (idx % (kPB / 8)) * 8;
+        if (r < QB * P) {
+          const u16x8 x = px.v[it][0];
+          u16* d = sXT + (r % P) * L::LDX + (r / P) * kPB + cc;
+          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+        }
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = j + e < len ? x[e] : u16(0);
-        u16* d = sXT + p * L::LDX + j;
-        *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
-        *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+      for (int it = 0; it < L::IT_XT; ++it) {
+        const int idx = tid + it * 512;
+        const int r = idx / (kPB / 8), cc = (idx % (kPB / 8)) * 8;
+        if (r < QB * P) {
+          const int j = (r / P) * kPB + cc;
+          u16x8 x = px.v[it][0];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = j + e < len ? x[e] : u16(0);
+          u16* d = sXT + (r % P) * L::LDX + j;
+          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+        }
       }
     }
     ph.store(sH, 0, L::LDH, P, N, P, N, tid, 512);
     if (tid < 256) {
       const bool ok = tid < len;
-      sA[tid] = ok ? pa : 0.f;
-      sD[tid] = ok ? pd : 0.f;
-      sCw[tid] = ok ? __expf(pr - pa) * pd : 0.f;
+      sA2[tid] = ok ? pa * kLog2e : -INFINITY;
+      sB2[tid] = ok ? pa * kLog2e - __builtin_amdgcn_logf(pd) : 0.f;
+      sCw[tid] = ok ? fast_exp2((pr - pa) * kLog2e) * pd : 0.f;
     }
     __syncthreads();
-    // z of this head's output items (bf16, 16-byte rows), issued before the next head's
-    // prefetch so that the output waits for these loads only; rows past the chunk read the
-    // chunk's first row and are never stored
+    const float Dh = load_uniform(&a.D[h]);
+    // z of both tiles as 16-byte row pieces (the output items below), then the next head's
+    // operands (unconditional: one straight path); rows past the chunk read the chunk's first row
     u16x8 zr[2][ZI];
     if (zpre) {
+      const u16* zbase = static_cast<const u16*>(a.z) + ch.t0 * a.z_stride + h * P;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int k = 0; k < ZI; ++k) {
           const int it = min(lane + 64 * k, 16 * CG - 1);
-          int ii = rts[t] * 16 + it / CG;
-          ii = ii < len ? ii : 0;
-          zr[t][k] = *reinterpret_cast<const u16x8*>(static_cast<const u16*>(a.z) + (ch.t0 + ii) * a.z_stride +
-                                                     h * P + (it % CG) * 8);
+          const int ii = rts[t] * 16 + it / CG;
+          zr[t][k] = *reinterpret_cast<const u16x8*>(zbase + (ii < len ? ii : 0) * (int)a.z_stride + (it % CG) * 8);
         }
       }
     }
-    prefetch(min(h + 1, h0 + heads_per_wg - 1));   // unconditional: one straight path
+    prefetch(min(h + 1, h0 + heads_per_wg - 1));
 
-    // the entering-state term exp(a_i) C_i h_in (C rows past the chunk are zero)
-    floatx4 acc[2][PT];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      acc[0][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      acc[1][pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      const int kn = N >= 32 ? ks * 32 : 0;
-      Frag<false> fc0 = lds_frag<false>(sC, 0, L::LDB, rts[0] * 16 + l16, kn, q);
-      Frag<false> fc1 = lds_frag<false>(sC, 0, L::LDB, rts[1] * 16 + l16, kn, q);
-      Frag<false> fh[PT];
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) fh[pt] = lds_frag<false>(sH, 0, L::LDH, pt * 16 + l16, kn, q);
-      if (N < 32) {   // upper K half is padding
-#pragma unroll
-        for (int e = 4; e < 8; ++e) {
-          fc0.hi[e] = bf_of(0);
-          fc1.hi[e] = bf_of(0);
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) fh[pt].hi[e] = bf_of(0);
-        }
-      }
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        acc[0][pt] = mma<false>(fc0, fh[pt], acc[0][pt]);
-        acc[1][pt] = mma<false>(fc1, fh[pt], acc[1][pt]);
-      }
-    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if (!vt[t]) continue;
+      const int rt = rts[t];
+      const int i = rt * 16 + l16;
+      const float a2i = sA2[i];
+      // exp(a_i) h_in^T C_i^T first (state dimension in the kmap order of the C fragments), then
+      // (M o L) X accumulates on top
+      floatx4 acc[PT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = rts[t] * 16 + 4 * q + r;
-        const float sc = ii < len ? __expf(sA[ii & 255]) : 0.f;
+      for (int pt = 0; pt < PT; ++pt) acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[t][pt][r] *= sc;
+      for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          Frag<false> fh = lds_frag<false>(sH, 0, L::LDH, pt * 16 + l16, N >= 32 ? ks * 32 : 0, q);
+          if (N < 32) {
+#pragma unroll
+            for (int e = 4; e < 8; ++e) fh.hi[e] = bf_of(0);
+          }
+          acc[pt] = mfma_bf16(fh.hi, cf[t][ks].hi, acc[pt]);
+        }
       }
-    }
-
-    // (M o L) X: this head's decay mask on each stored G^T slot, times the x fragments.  The
-    // slot offsets go through an opaque zero so the per-slot index work stays inside the loop.
-    const int zero = opaque_uniform(0);
-#pragma clang loop unroll(full)
-    for (int sl = 0; sl < 9; ++sl) {
-      const bool t1 = sl > w2;
-      const int jk = 32 * (t1 ? sl - w2 - 1 : sl) + zero;
-      if (!((t1 ? v1 : v0) && jk < len)) continue;
-      Frag<false> fx[PT];
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
-      float cw[8];
       {
+        const float sc = fast_exp2(a2i);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pt][r] *= sc;
+      }
+
+      // (M o L) X over the K-steps entirely below the tile: exp(a_i - a_j) = 2^(a2_i - a2_ref)
+      // times the column factor, with a_ref the cumsum at the K-step's last token (both <= 1)
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        if (k >= mt[t]) break;
+        const int jk = 32 * k;
+        Frag<false> fx[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
         const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
         const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
+        const float rf = fast_exp2(a2i - sA2[jk + 31]);
+        const floatx4(&gs)[2] = t == 0 ? gb[k] : gb[6 - k];
+        float mv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { cw[e] = c0[e]; cw[e + 4] = c1[e]; }
+        for (int e = 0; e < 4; ++e) {
+          mv[e] = gs[0][e] * (rf * c0[e]);
+          mv[e + 4] = gs[1][e] * (rf * c1[e]);
+        }
+        const Frag<false> mf = make_frag<false>(mv);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma_bf16(fx[pt].hi, mf.hi, acc[pt]);
       }
-      const float aref = sA[min(jk + 31, len - 1)];
-      if (t1) {
-        const Frag<false> m = decay_mask<false>(Gs[sl], rts[1], jk, len, aref, cw, sA, sD, Dh, q, l16);
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[1][pt] = mma<false>(m, fx[pt], acc[1][pt]);
-      } else {
-        const Frag<false> m = decay_mask<false>(Gs[sl], rts[0], jk, len, aref, cw, sA, sD, Dh, q, l16);
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[0][pt] = mma<false>(m, fx[pt], acc[0][pt]);
-      }
-    }
 
-    // outputs y = acc * SiLU(z) through this wave's LDS tile, 16-byte z reads and y writes
+      // the diagonal K-step: the 16-token block on the diagonal takes its exponents directly, with
+      // the causal mask and D x on the diagonal; the other block lies entirely below the tile (odd
+      // tiles, direct exponents) or entirely above it (even tiles, zero)
+      {
+        const int jk = 32 * mt[t];
+        Frag<false> fx[PT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rt = rts[t];
-      if (!(t == 0 ? v0 : v1)) continue;
+        for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<false>(sXT, 0, L::LDX, pt * 16 + l16, jk, q);
+        const int dsel = l16 - 4 * q;
+        const floatx4 bd = *reinterpret_cast<const floatx4*>(&sB2[16 * rt + 4 * q]);
+        float mv[8];
+        if (rt & 1) {
+          const floatx4 bb = *reinterpret_cast<const floatx4*>(&sB2[jk + 4 * q]);
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
+          for (int e = 0; e < 4; ++e) {
+            const float v = fast_exp2(a2i - bd[e]) * gd[t][1][e];
+            mv[e + 4] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e] = fast_exp2(a2i - bb[e]) * gd[t][0][e];
+          }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sO[(4 * q + r) * L::LDO + pt * 16 + l16] = acc[t][pt][r];
+          for (int e = 0; e < 4; ++e) {
+            const float v = fast_exp2(a2i - bd[e]) * gd[t][0][e];
+            mv[e] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e + 4] = 0.f;
+          }
+        }
+        const Frag<false> mf = make_frag<false>(mv);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma_bf16(fx[pt].hi, mf.hi, acc[pt]);
+      }
+
+      // y = acc * SiLU(z) through this wave's LDS tile: the accumulators go in as 16-byte pieces
+      // of token rows, and eight lanes then cover one row's channels, so z and y move as 16-byte
+      // pieces of whole rows
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) *reinterpret_cast<floatx4*>(&sO[l16 * L::LDO + pt * 16 + 4 * q]) = acc[pt];
 #pragma unroll
       for (int k = 0; k < ZI; ++k) {
         const int it = lane + 64 * k;
@@ -1270,9 +1308,9 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
         if (ii >= len) continue;
         const floatx4 o0 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8]);
         const floatx4 o1 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8 + 4]);
-        const int64_t row = ch.t0 + ii;
-        const int col = h * P + c8;
         float v[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+        const int64_t row = ch.t0 + ii + opaque_uniform(0);   // keeps these addresses inside the loop
+        const int col = h * P + c8;
         if (zpre) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] *= silu(f_of(zr[t][k][e]));
