@@ -109,21 +109,19 @@ m2_status hip_fail(hipError_t e, const char* what) {
 
 // Prefill tables and workspace carving.
 struct PrefillLayout {
-  uint64_t nc_max, ns_max, nw_max, planes;
-  uint64_t off_seqs, off_chunks, off_segs, off_windows, meta_bytes;
+  uint64_t nc_max, nw_max, planes;
+  uint64_t off_seqs, off_chunks, off_windows, meta_bytes;
   uint64_t off_xT, off_Bt, off_Br, off_Cr, plane_xT, plane_Bt, plane_Br, plane_Cr;
-  uint64_t off_delta, off_dA, off_seg_state, off_seg_decay, off_hin, plane_hin, total;
+  uint64_t off_delta, off_dA, off_cstate, off_hin, plane_hin, total;
 };
 
 bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
   L->nc_max = (uint64_t)(T / Q) + (uint64_t)num_seqs;
-  L->ns_max = L->nc_max;
   L->nw_max = (uint64_t)num_seqs + L->nc_max;
   L->planes = split ? 2 : 1;
   L->off_seqs = 0;
   L->off_chunks = align_up(L->off_seqs + num_seqs * sizeof(m2::SeqEntry), 256);
-  L->off_segs = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
-  L->off_windows = align_up(L->off_segs + L->ns_max * sizeof(m2::SegEntry), 256);
+  L->off_windows = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
   L->meta_bytes = align_up(L->off_windows + L->nw_max * sizeof(m2::WindowEntry), 256);
   const uint64_t rows = L->nc_max * (uint64_t)Q;          // chunk-blocked rows
   uint64_t v;
@@ -143,10 +141,9 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   if (!mul_ok((uint64_t)T, (uint64_t)sh.H * 4, &v)) return false;
   L->off_delta = off;
   L->off_dA = align_up(L->off_delta + v, 256);
-  L->off_seg_state = align_up(L->off_dA + v, 256);
-  if (!mul_ok(L->ns_max, (uint64_t)sh.H * sh.P * sh.N * 4, &v)) return false;
-  L->off_seg_decay = align_up(L->off_seg_state + v, 256);
-  L->off_hin = align_up(L->off_seg_decay + L->ns_max * sh.H * 4, 256);
+  L->off_cstate = align_up(L->off_dA + v, 256);
+  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N * (split ? 4 : 2), &v)) return false;   // chunk end states
+  L->off_hin = align_up(L->off_cstate + v, 256);
   if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N, &L->plane_hin)) return false;
   if (!mul_ok(L->plane_hin, 2 * L->planes, &v)) return false;
   L->total = align_up(L->off_hin + v, 256);
@@ -369,15 +366,9 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
                 (unsigned long long)L.total);
 
-  // ---- segment length: a function of each sequence's own chunk count only, so a
-  // sequence's results do not depend on the rest of the batch (up to 8 segments per sequence,
-  // at most 16 chunks per segment)
-  auto seg_chunks_of = [](int nchunk) { int s = (nchunk + 7) / 8; return s < 1 ? 1 : (s > 16 ? 16 : s); };
-
   // ---- host tables
   std::vector<m2::SeqEntry> seqs(num_seqs);
   std::vector<m2::ChunkEntry> chunks;
-  std::vector<m2::SegEntry> segs;
   std::vector<m2::WindowEntry> windows;
   chunks.reserve(L.nc_max);
   for (int s = 0; s < num_seqs; ++s) {
@@ -390,8 +381,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     e.has_init = has_init[s] ? 1 : 0;
     e.chunk0 = (int32_t)chunks.size();
     e.nchunk = 0;
-    e.seg0 = (int32_t)segs.size();
-    e.nseg = 0;
+    e.pad0 = e.pad1 = 0;
     for (int c0 = 0; c0 < len; c0 += chunk_size) {
       m2::ChunkEntry c;
       c.seq = s;
@@ -411,16 +401,6 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
       if (c.ckpt_slot >= 0) windows.push_back({s, c0 + c.len, c.ckpt_slot, 0});
       chunks.push_back(c);
       ++e.nchunk;
-    }
-    const int seg_chunks = seg_chunks_of(e.nchunk);
-    for (int k = 0; k < e.nchunk; k += seg_chunks) {
-      m2::SegEntry g;
-      g.seq = s;
-      g.chunk0 = e.chunk0 + k;
-      g.nchunk = e.nchunk - k < seg_chunks ? e.nchunk - k : seg_chunks;
-      g.is_last = k + seg_chunks >= e.nchunk;
-      segs.push_back(g);
-      ++e.nseg;
     }
     if (len > 0) windows.push_back({s, len, slots[s], 0});
   }
@@ -452,7 +432,6 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     memset(st, 0, L.meta_bytes);
     memcpy(st + L.off_seqs, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
     memcpy(st + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
-    memcpy(st + L.off_segs, segs.data(), segs.size() * sizeof(m2::SegEntry));
     memcpy(st + L.off_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
     if ((e = hipMemcpyAsync(ws, st, L.meta_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
       return hip_fail(e, "table upload");
@@ -473,12 +452,10 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.Q = chunk_size;
   p.num_seqs = num_seqs;
   p.num_chunks = (int)chunks.size();
-  p.num_segments = (int)segs.size();
   p.num_windows = (int)windows.size();
   p.total_tokens = (int)T;
   p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws + L.off_seqs);
   p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + L.off_chunks);
-  p.segs = reinterpret_cast<const m2::SegEntry*>(ws + L.off_segs);
   p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + L.off_windows);
   p.x = x;
   p.B = B;
@@ -507,8 +484,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.Cr_plane = (int64_t)L.plane_Cr;
   p.delta = reinterpret_cast<float*>(ws + L.off_delta);
   p.dA = reinterpret_cast<float*>(ws + L.off_dA);
-  p.seg_state = reinterpret_cast<float*>(ws + L.off_seg_state);
-  p.seg_decay = reinterpret_cast<float*>(ws + L.off_seg_decay);
+  p.cstate = ws + L.off_cstate;
   p.hin = reinterpret_cast<uint16_t*>(ws + L.off_hin);
   p.hin_plane = (int64_t)L.plane_hin;
   const hipError_t e = m2::launch_prefill(p, hs);

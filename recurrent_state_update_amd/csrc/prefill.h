@@ -7,14 +7,11 @@ namespace m2 {
 // Chunked prefill.  Host-built tables live at the start of the workspace.
 struct SeqEntry {     // one per sequence
   int32_t t0, len, slot, has_init;  // packed start row, rows, final slot, seed from slot
-  int32_t chunk0, nchunk, seg0, nseg;
+  int32_t chunk0, nchunk, pad0, pad1;
 };
 struct ChunkEntry {   // one per chunk
   int32_t seq, t0, len, tau0;       // packed start row, rows in chunk, offset inside the sequence
   int32_t ckpt_slot, is_last, pad0, pad1;
-};
-struct SegEntry {     // one per segment: consecutive chunks of one sequence walked by one workgroup
-  int32_t seq, chunk0, nchunk, is_last;
 };
 struct WindowEntry {  // one conv-window write: window after `tau` rows of sequence `seq` -> slot
   int32_t seq, tau, slot, pad;
@@ -30,10 +27,9 @@ struct PrefillParams {
                        // offsets inside a chunk's rows fit in 32 bits
   LayerShape sh;
   int Q;               // chunk size
-  int num_seqs, num_chunks, num_segments, num_windows, total_tokens;
+  int num_seqs, num_chunks, num_windows, total_tokens;
   const SeqEntry* seqs;
   const ChunkEntry* chunks;
-  const SegEntry* segs;
   const WindowEntry* windows;
   const void* x;
   const void* B;
@@ -59,8 +55,8 @@ struct PrefillParams {
   int64_t xT_plane, Bt_plane, Br_plane, Cr_plane;   // elements per plane
   float* delta;          // [H][T]
   float* dA;             // [H][T] chunk-local inclusive cumsum of Delta*A
-  float* seg_state;      // [segments][H][P][N]: segment end state from zero, then the entering state
-  float* seg_decay;      // [segments][H]: sum over the segment's chunks of the chunk's last cumsum
+  void* cstate;          // [chunks][H][P][N]: each chunk's end state from a zero state; fp32 with
+                         // hi/lo planes, bf16 otherwise
   uint16_t* hin;         // [planes][chunks][H][P][N]: state entering each chunk, bf16 operand planes
   int64_t hin_plane;     // elements per plane
 };

@@ -1,14 +1,13 @@
 // Chunked (SSD) prefill of packed variable-length sequences, gfx950.
 //
-// Each sequence is cut into chunks of Q tokens from its first row, and runs
-// of consecutive chunks form segments.  Inside a chunk the output is the
-// causally masked product Y = (M o L) X of the Mamba study notes
+// Each sequence is cut into chunks of Q tokens from its first row.  Inside a
+// chunk the output is the causally masked product Y = (M o L) X of the Mamba study notes
 // (echobase-5bl.pages.dev, "Mamba and Attention"),
 //   M[i][j] = (C_i . B_j) exp(a_i - a_j) Delta_j   (j <= i),
 // with a the chunk-local cumulative sum of Delta*A, plus exp(a_i) C_i h_in
 // for the state h_in entering the chunk; chunk end states follow
 // h_out = exp(a_last) h_in + sum_j exp(a_last - a_j) Delta_j x_j B_j^T, the
-// affine step that links chunks and segments ("Hybrid SSM / Mamba models and
+// affine step that links chunks ("Hybrid SSM / Mamba models and
 // non-KV state", mlinterviewnotes.com ch. 7.3: chunked-prefill handoff,
 // affine-composition passage, SSD chunk-scan call site).
 //
@@ -16,15 +15,14 @@
 //   1. conv_kernel        causal conv + SiLU of every (token, channel), written as bf16
 //                         operand planes in the layouts the products read
 //   2. dt_kernel          Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
-//   3. state_walk_kernel  per (segment, head), from a zero state: the segment's end state (MFMA);
-//                         skipped for each sequence's last segment
-//   4. seg_pass_kernel    per (sequence, head): scan over segments -> state entering each segment
-//   5. state_walk_kernel  per (segment, head), from the entering state: the state entering each
-//                         chunk (operand planes), checkpoint and final states into their slots
-//   6. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
+//   3. chunk_state_kernel per (chunk, head): the chunk's end state from a zero state (MFMA)
+//   4. state_pass_kernel  per (sequence, head): the affine step through the sequence's chunks ->
+//                         state entering each chunk (operand planes), checkpoint and final
+//                         states into their slots
+//   5. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
 //                         C B^T formed once; chunk_out_kernel per (chunk, head) for hi/lo planes
 //                         and head_dim 128
-//   7. window_kernel      final and checkpoint conv windows (raw inputs) into their slots
+//   6. window_kernel      final and checkpoint conv windows (raw inputs) into their slots
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
 // otherwise operands are single bf16 planes with fp32 accumulation.
@@ -440,15 +438,12 @@ __device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N
   for (int r = 0; r < 4; ++r) d[(int64_t)(p + r) * N + n] = from_f32<TS>(v[r]);
 }
 
-// ------------------------------------------------------------------ 3. state walks
-// Per (segment, head), 512 threads: the state runs through the segment's chunks in MFMA
-// accumulators, h <- exp(a_last) h + sum_j exp(a_last - a_j) Delta_j x_j B_j^T, over staged
-// blocks of kWB tokens with the next block held in registers while the current one is used.
-//   EMIT = false: from a zero state; writes the segment's end state and its summed log decay
-//                 (each sequence's last segment is skipped: nothing follows it).
-//   EMIT = true:  from the state entering the segment; writes the state entering every chunk
-//                 as bf16 operand planes for the output kernel, and after each chunk the
-//                 checkpoint and final states rounded into their slots.
+// ------------------------------------------------------------------ 3. chunk end states
+// Per (chunk, head), 512 threads: the chunk's end state from a zero state,
+//   S_c = sum_j exp(a_last - a_j) Delta_j x_j B_j^T,
+// in MFMA accumulators over staged blocks of kWB tokens, the next block held in registers while
+// the current one is used.  Written to the chunk-state array through an LDS tile as 16-byte
+// pieces of rows: fp32 with hi/lo planes (fp32 state), bf16 otherwise.
 constexpr int kWB = kPB;   // one block of the transposed planes
 
 template <bool SPLIT, int P, int N> struct WalkLds {
@@ -457,16 +452,16 @@ template <bool SPLIT, int P, int N> struct WalkLds {
   static constexpr int XT_OFF = 0;                          // u16 offsets
   static constexpr int BT_OFF = XT_OFF + NPL * P * LDX;
   static constexpr int STAGE_END = BT_OFF + NPL * N * LDX;
-  // state staging for 16-byte stores of the entering state (overlays the blocks)
-  static constexpr int LDS_ST = N + 8;
-  static constexpr int ST_END = NPL * P * LDS_ST;
+  // end-state staging (overlays the blocks): fp32 rows of N + 4, or bf16 rows of N + 8
+  static constexpr int LDS_ST = SPLIT ? N + 4 : N + 8;
+  static constexpr int ST_END = P * LDS_ST * (SPLIT ? 2 : 1);
   static constexpr int U16S = STAGE_END > ST_END ? STAGE_END : ST_END;
   static constexpr int IT_XT = (P * (kWB / 8) + kStateThreads - 1) / kStateThreads;
   static constexpr int IT_BT = (N * (kWB / 8) + kStateThreads - 1) / kStateThreads;
 };
 
-template <bool SPLIT, int P, int N, bool EMIT>
-__global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams a) {
+template <bool SPLIT, int P, int N>
+__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams a) {
   typedef WalkLds<SPLIT, P, N> L;
   typedef StateTiles<P, N, kStateThreads / 64> ST;
   constexpr int NPL = L::NPL, LDX = L::LDX;
@@ -474,234 +469,214 @@ __global__ __launch_bounds__(kStateThreads) void state_walk_kernel(PrefillParams
   __shared__ __align__(16) float sW[256];
   u16* const sXT = smem_w + L::XT_OFF;
   u16* const sBT = smem_w + L::BT_OFF;
-  const SegEntry sg = load_uniform(&a.segs[blockIdx.x]);
-  if (!EMIT && sg.is_last) return;
-  const SeqEntry sq = load_uniform(&a.seqs[sg.seq]);
-  const int h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
+  const int c = blockIdx.x, h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
   const int g = h / (H / G);
+  const ChunkEntry ch = load_uniform(&a.chunks[c]);
+  const int len = ch.len;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t T = a.total_tokens;
   const int64_t PN = (int64_t)P * N;
-  float* const seg = a.seg_state + ((int64_t)blockIdx.x * H + h) * PN;
-
-  floatx4 acc[ST::PER_WAVE];
-#pragma unroll
-  for (int m = 0; m < ST::PER_WAVE; ++m) {
-    acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (EMIT && ST::valid(wave, m)) {
-      const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][r] = seg[(pt * 16 + 4 * q + r) * N + nt * 16 + l16];
-    }
-  }
+  const int QB = (Q + kPB - 1) / kPB;
 
   TilePrefetch<NPL, L::IT_XT> px;
   TilePrefetch<NPL, L::IT_BT> pb;
-  const int c_end = sg.chunk0 + sg.nchunk;
-  auto prefetch = [&](int c, int jb, int len) {
-    const int QB = (Q + kPB - 1) / kPB;
+  auto prefetch = [&](int jb) {
     px.load(a.xT + (((int64_t)c * H + h) * QB + jb / kPB) * P * kPB, a.xT_plane, kPB, P, kWB, P, len - jb, tid,
             kStateThreads);
     pb.load(a.Bt + (((int64_t)c * G + g) * QB + jb / kPB) * N * kPB, a.Bt_plane, kPB, N, kWB, N, len - jb, tid,
             kStateThreads);
   };
-  // a chunk's cumsum and Delta at token tid and its last cumsum, loaded one chunk ahead
-  float wa, wd, wl;
-  auto prefetch_tables = [&](const ChunkEntry& nc) {
-    const int64_t base = (int64_t)h * T + nc.t0;
-    const int j = min(tid & 255, nc.len - 1);
-    wa = a.dA[base + j];
-    wd = a.delta[base + j];
-    wl = a.dA[base + nc.len - 1];
-  };
-  ChunkEntry ch = load_uniform(&a.chunks[sg.chunk0]);
-  prefetch(sg.chunk0, 0, ch.len);
-  prefetch_tables(ch);
-
-  float logdecay = 0.f;
-  for (int c = sg.chunk0; c < c_end; ++c) {
-    const int len = ch.len;
-    const float alast = wl, aj = wa, dj = wd;
-    // the next chunk's entry and tables (the current one again past the segment's end)
-    const int cn = min(c + 1, c_end - 1);
-    const ChunkEntry nch = load_uniform(&a.chunks[cn]);
-    logdecay += alast;
-    __syncthreads();   // the previous chunk's reads of sW and of the staged blocks are done
-    if (EMIT) {   // the state entering this chunk -> LDS, as the output kernel's operand planes
-#pragma unroll
-      for (int m = 0; m < ST::PER_WAVE; ++m) {
-        if (ST::valid(wave, m)) {
-          const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = (pt * 16 + 4 * q + r) * L::LDS_ST + nt * 16 + l16;
-            u16 hi, lo = 0;
-            if (SPLIT) split2(acc[m][r], hi, lo);
-            else hi = bits_of(from_f32<bf16>(acc[m][r]));
-            smem_w[i] = hi;
-            if (SPLIT) smem_w[P * L::LDS_ST + i] = lo;
-          }
-        }
-      }
-    }
+  prefetch(0);
+  {   // weights w_j = exp(a_last - a_j) Delta_j of the chunk's tokens
+    const int64_t base = (int64_t)h * T + ch.t0;
+    const int j = min(tid & 255, len - 1);
+    const float aj = a.dA[base + j], dj = a.delta[base + j], alast = a.dA[base + len - 1];
     if (tid < 256) sW[tid] = tid < len ? __expf(alast - aj) * dj : 0.f;
-    prefetch_tables(nch);
-    if (EMIT) {   // ... and out with 16-byte stores (the block loop's first barrier protects the overlay)
-      __syncthreads();
-      u16* dst = a.hin + ((int64_t)c * H + h) * PN;
-      constexpr int CG = N / 8;
-      for (int idx = tid; idx < P * CG; idx += kStateThreads) {
-        const int row = idx / CG, c8 = (idx % CG) * 8;
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl)
-          *reinterpret_cast<u16x8*>(dst + pl * a.hin_plane + row * N + c8) =
-              *reinterpret_cast<const u16x8*>(smem_w + pl * P * L::LDS_ST + row * L::LDS_ST + c8);
-      }
-    }
-    const float decay = __expf(alast);
-#pragma unroll
-    for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] *= decay;
+  }
 
-    for (int jb = 0; jb < len; jb += kWB) {
-      __syncthreads();   // all reads of the previous block are done
-      // x goes to LDS already scaled by w_j = exp(a_last - a_j) Delta_j (one rounding of the
-      // product, as the operand needs), so the K-steps read it as a finished fragment
+  floatx4 acc[ST::PER_WAVE];
 #pragma unroll
-      for (int it = 0; it < L::IT_XT; ++it) {
-        const int idx = tid + it * kStateThreads;
-        if (idx < P * (kWB / 8)) {
-          const int r = idx / (kWB / 8), cc = (idx % (kWB / 8)) * 8;
-          const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + cc]);
-          const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + cc + 4]);
-          u16x8 hv, lv;
+  for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int jb = 0; jb < len; jb += kWB) {
+    __syncthreads();   // all reads of the previous block are done (and sW is written)
+    // x goes to LDS already scaled by w_j (one rounding of the product, as the operand needs),
+    // so the K-steps read it as a finished fragment
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float xv = f_of(px.v[it][0][e]);
-            if (SPLIT) xv += f_of(px.v[it][NPL - 1][e]);
-            xv = jb + cc + e < len ? xv * (e < 4 ? w0[e] : w1[e - 4]) : 0.f;
-            u16 hi, lo = 0;
-            if (SPLIT) split2(xv, hi, lo);
-            else hi = bits_of(from_f32<bf16>(xv));
-            hv[e] = hi;
-            lv[e] = lo;
-          }
-          u16* d = sXT + r * LDX + cc;
-          *reinterpret_cast<u16x4*>(d) = u16x4{hv[0], hv[1], hv[2], hv[3]};
-          *reinterpret_cast<u16x4*>(d + 4) = u16x4{hv[4], hv[5], hv[6], hv[7]};
-          if (SPLIT) {
-            *reinterpret_cast<u16x4*>(d + P * LDX) = u16x4{lv[0], lv[1], lv[2], lv[3]};
-            *reinterpret_cast<u16x4*>(d + P * LDX + 4) = u16x4{lv[4], lv[5], lv[6], lv[7]};
-          }
+    for (int it = 0; it < L::IT_XT; ++it) {
+      const int idx = tid + it * kStateThreads;
+      if (idx < P * (kWB / 8)) {
+        const int r = idx / (kWB / 8), cc = (idx % (kWB / 8)) * 8;
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + cc]);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + cc + 4]);
+        u16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float xv = f_of(px.v[it][0][e]);
+          if (SPLIT) xv += f_of(px.v[it][NPL - 1][e]);
+          xv = jb + cc + e < len ? xv * (e < 4 ? w0[e] : w1[e - 4]) : 0.f;
+          u16 hi, lo = 0;
+          if (SPLIT) split2(xv, hi, lo);
+          else hi = bits_of(from_f32<bf16>(xv));
+          hv[e] = hi;
+          lv[e] = lo;
         }
-      }
-      if (jb + kWB <= len) pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);   // uniform
-      else pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
-      __syncthreads();
-      {   // the next block, or the next chunk's first block; one straight path (past the
-          // segment's last block the current block is fetched again and not used)
-        const bool more = jb + kWB < len;
-        const bool last = !more && c + 1 >= c_end;
-        prefetch(more || last ? c : cn, more ? jb + kWB : (last ? jb : 0), more || last ? len : nch.len);
-      }
-#pragma unroll
-      for (int kb = 0; kb < kWB; kb += 32) {
-        if (jb + kb >= len) break;
-        // x-side operand of tile row pt: (w x)^T over the K-step's tokens, staged scaled
-        auto xfrag = [&](int pt) { return lds_frag<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q); };
-        if (ST::ALIGNED) {
-          const Frag<SPLIT> fa = xfrag(ST::pt(wave, 0));
-          Frag<SPLIT> fb[ST::PER_WAVE];
-#pragma unroll
-          for (int m = 0; m < ST::PER_WAVE; ++m)
-            fb[m] = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
-#pragma unroll
-          for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = mma<SPLIT>(fa, fb[m], acc[m]);
-        } else {
-#pragma unroll
-          for (int m = 0; m < ST::PER_WAVE; ++m) {
-            if (ST::valid(wave, m)) {
-              const Frag<SPLIT> fa = xfrag(ST::pt(wave, m));
-              const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
-              acc[m] = mma<SPLIT>(fa, fb, acc[m]);
-            }
-          }
+        u16* d = sXT + r * LDX + cc;
+        *reinterpret_cast<u16x4*>(d) = u16x4{hv[0], hv[1], hv[2], hv[3]};
+        *reinterpret_cast<u16x4*>(d + 4) = u16x4{hv[4], hv[5], hv[6], hv[7]};
+        if (SPLIT) {
+          *reinterpret_cast<u16x4*>(d + P * LDX) = u16x4{lv[0], lv[1], lv[2], lv[3]};
+          *reinterpret_cast<u16x4*>(d + P * LDX + 4) = u16x4{lv[4], lv[5], lv[6], lv[7]};
         }
       }
     }
-
-    if (EMIT) {   // checkpoint and final states, rounded to the state dtype
-      const int dsts[2] = {ch.ckpt_slot, ch.is_last ? sq.slot : -1};
+    if (jb + kWB <= len) pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);   // uniform
+    else pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+    __syncthreads();
+    // the next block; one straight path (past the last block the current one is fetched again
+    // and not used)
+    prefetch(jb + kWB < len ? jb + kWB : jb);
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (dsts[d] < 0) continue;
-        const int64_t base = (int64_t)dsts[d] * H * PN + (int64_t)h * PN;
+    for (int kb = 0; kb < kWB; kb += 32) {
+      if (jb + kb >= len) break;
+      // x-side operand of tile row pt: (w x)^T over the K-step's tokens, staged scaled
+      auto xfrag = [&](int pt) { return lds_frag<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q); };
+      if (ST::ALIGNED) {
+        const Frag<SPLIT> fa = xfrag(ST::pt(wave, 0));
+        Frag<SPLIT> fb[ST::PER_WAVE];
+#pragma unroll
+        for (int m = 0; m < ST::PER_WAVE; ++m)
+          fb[m] = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+#pragma unroll
+        for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = mma<SPLIT>(fa, fb[m], acc[m]);
+      } else {
 #pragma unroll
         for (int m = 0; m < ST::PER_WAVE; ++m) {
           if (ST::valid(wave, m)) {
-            const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
-            if (a.ssm_bf16) store_state_tile<bf16>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, acc[m]);
-            else store_state_tile<float>(a.ssm, base, N, pt * 16 + 4 * q, nt * 16 + l16, acc[m]);
+            const Frag<SPLIT> fa = xfrag(ST::pt(wave, m));
+            const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+            acc[m] = mma<SPLIT>(fa, fb, acc[m]);
           }
         }
       }
     }
-    ch = nch;
   }
-  if (!EMIT) {
+
+  // the end state -> LDS rows -> 16-byte stores
+  __syncthreads();   // the last block's reads are done before the staging overlays it
 #pragma unroll
-    for (int m = 0; m < ST::PER_WAVE; ++m) {
-      if (ST::valid(wave, m)) {
-        const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
+  for (int m = 0; m < ST::PER_WAVE; ++m) {
+    if (ST::valid(wave, m)) {
+      const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) seg[(pt * 16 + 4 * q + r) * N + nt * 16 + l16] = acc[m][r];
+      for (int r = 0; r < 4; ++r) {
+        const int i = (pt * 16 + 4 * q + r) * L::LDS_ST + nt * 16 + l16;
+        if (SPLIT) reinterpret_cast<float*>(smem_w)[i] = acc[m][r];
+        else smem_w[i] = bits_of(from_f32<bf16>(acc[m][r]));
       }
     }
-    if (tid == 0) a.seg_decay[(int64_t)blockIdx.x * H + h] = logdecay;
+  }
+  __syncthreads();
+  constexpr int VPR = SPLIT ? N / 4 : N / 8;   // 16-byte pieces per row
+  for (int idx = tid; idx < P * VPR; idx += kStateThreads) {
+    const int row = idx / VPR, cv = idx % VPR;
+    if (SPLIT) {
+      float* dst = static_cast<float*>(a.cstate) + ((int64_t)c * H + h) * PN + row * N + cv * 4;
+      *reinterpret_cast<floatx4*>(dst) =
+          *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(smem_w) + row * L::LDS_ST + cv * 4);
+    } else {
+      u16* dst = static_cast<u16*>(a.cstate) + ((int64_t)c * H + h) * PN + row * N + cv * 8;
+      *reinterpret_cast<u16x8*>(dst) = *reinterpret_cast<const u16x8*>(smem_w + row * L::LDS_ST + cv * 8);
+    }
   }
 }
 
-// ------------------------------------------------------------------ 4. scan over segments
-template <typename TS>
-__global__ __launch_bounds__(256) void seg_pass_kernel(PrefillParams a) {
+// ------------------------------------------------------------------ 4. pass over each sequence's chunks
+// Per (sequence, head, 2048 state elements), 256 threads of 8 elements each: the affine step
+//   h <- exp(a_last(c)) h + S_c
+// through the sequence's chunks from its initial state (the slot's, or zero).  Before each chunk
+// the state entering it goes out as the output kernel's bf16 operand planes; after a chunk that
+// ends on a checkpoint, and after the last one, the state is rounded into its slot.  Eight
+// chunks at a time: their end states and log decays are all requested before the first is used
+// (one straight path; past the last chunk the last one is read again and not used).
+template <typename TSS, typename TS>
+__global__ __launch_bounds__(256) void state_pass_kernel(PrefillParams a) {
   const SeqEntry sq = load_uniform(&a.seqs[blockIdx.x]);
-  if (sq.nseg == 0) return;
+  if (sq.nchunk == 0) return;
   const int h = blockIdx.y, H = a.sh.H;
   const int PN = a.sh.P * a.sh.N;
-  const int e4 = (blockIdx.z * 256 + threadIdx.x) * 4;
-  if (e4 >= PN) return;
-  const int64_t head_off = (int64_t)h * PN + e4;
-  floatx4 hs = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int e8 = (blockIdx.z * 256 + threadIdx.x) * 8;
+  if (e8 >= PN) return;
+  const int64_t head_off = (int64_t)h * PN + e8;
+  const int64_t T = a.total_tokens;
+  constexpr bool SPLIT = std::is_same<TSS, float>::value;
+  float hs[8];
   if (sq.has_init) {
     const TS* src = static_cast<const TS*>(a.ssm) + (int64_t)sq.slot * H * PN + head_off;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hs[e] = to_f32(src[e]);
+    for (int e = 0; e < 8; ++e) hs[e] = to_f32(src[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hs[e] = 0.f;
   }
-  // D segments at a time: their end states are all requested before the first is used (one
-  // straight path; past the sequence's last segment the last one is read again and not used),
-  // and the log decays come through scalar loads
-  constexpr int D = 8;
-  for (int s0 = 0; s0 < sq.nseg; s0 += D) {
-    floatx4 sc[D];
-    float dec[D];
-    bool step[D];
+  auto store_state = [&](int slot) {
+    TS* d = static_cast<TS*>(a.ssm) + (int64_t)slot * H * PN + head_off;
+    if (std::is_same<TS, float>::value) {
+      *reinterpret_cast<floatx4*>(d) = floatx4{hs[0], hs[1], hs[2], hs[3]};
+      *reinterpret_cast<floatx4*>(d + 4) = floatx4{hs[4], hs[5], hs[6], hs[7]};
+    } else {
+      u16x8 o;
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-      const int s = sq.seg0 + min(s0 + k, sq.nseg - 1);
-      step[k] = s0 + k < sq.nseg && !load_uniform(&a.segs[s]).is_last;
-      dec[k] = load_uniform(&a.seg_decay[(int64_t)s * H + h]);
-      sc[k] = *reinterpret_cast<const floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off);
+      for (int e = 0; e < 8; ++e) o[e] = bits_of(from_f32<bf16>(hs[e]));
+      *reinterpret_cast<u16x8*>(d) = o;
     }
+  };
+  constexpr int D = 8;
+  for (int k0 = 0; k0 < sq.nchunk; k0 += D) {
+    float sc[D][8], dec[D];
+    int ck[D];
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      if (s0 + k < sq.nseg) {
-        const int s = sq.seg0 + s0 + k;
-        *reinterpret_cast<floatx4*>(a.seg_state + (int64_t)s * H * PN + head_off) = hs;
-        if (step[k]) hs = __expf(dec[k]) * hs + sc[k];
+      const int c = sq.chunk0 + min(k0 + k, sq.nchunk - 1);
+      const ChunkEntry ch = load_uniform(&a.chunks[c]);
+      dec[k] = load_uniform(&a.dA[(int64_t)h * T + ch.t0 + ch.len - 1]);
+      ck[k] = ch.ckpt_slot;
+      const int64_t so = (int64_t)c * H * PN + head_off;
+      if (SPLIT) {
+        const floatx4 v0 = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a.cstate) + so);
+        const floatx4 v1 = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a.cstate) + so + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { sc[k][e] = v0[e]; sc[k][e + 4] = v1[e]; }
+      } else {
+        const u16x8 v = *reinterpret_cast<const u16x8*>(static_cast<const u16*>(a.cstate) + so);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[k][e] = f_of(v[e]);
       }
     }
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      if (k0 + k >= sq.nchunk) break;
+      const int c = sq.chunk0 + k0 + k;
+      u16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u16 vh, vl = 0;
+        if (SPLIT) split2(hs[e], vh, vl);
+        else vh = bits_of(from_f32<bf16>(hs[e]));
+        hi[e] = vh;
+        lo[e] = vl;
+      }
+      u16* dst = a.hin + (int64_t)c * H * PN + head_off;
+      *reinterpret_cast<u16x8*>(dst) = hi;
+      if (SPLIT) *reinterpret_cast<u16x8*>(dst + a.hin_plane) = lo;
+      const float decay = __expf(dec[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hs[e] = decay * hs[e] + sc[k][e];
+      if (ck[k] >= 0) store_state(ck[k]);
+    }
   }
+  store_state(sq.slot);
 }
 
 // ------------------------------------------------------------------ 5. chunk outputs
@@ -1374,14 +1349,12 @@ static hipError_t set_lds_attr(const void* fn, int bytes) {
 }
 
 template <bool SPLIT, int P, int N>
-static hipError_t launch_segments(const PrefillParams& a, hipStream_t s) {
-  const dim3 gs(a.num_segments, a.sh.H);
-  hipLaunchKernelGGL((state_walk_kernel<SPLIT, P, N, false>), gs, dim3(kStateThreads), 0, s, a);
-  const int PN = P * N;
-  const dim3 gp(a.num_seqs, a.sh.H, (PN / 4 + 255) / 256);
-  if (a.ssm_bf16) hipLaunchKernelGGL(seg_pass_kernel<bf16>, gp, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(seg_pass_kernel<float>, gp, dim3(256), 0, s, a);
-  hipLaunchKernelGGL((state_walk_kernel<SPLIT, P, N, true>), gs, dim3(kStateThreads), 0, s, a);
+static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t s) {
+  hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N>), dim3(a.num_chunks, a.sh.H), dim3(kStateThreads), 0, s, a);
+  const dim3 gp(a.num_seqs, a.sh.H, (P * N / 8 + 255) / 256);
+  // hi/lo planes go with fp32 state: fp32 chunk states; bf16 state: bf16 chunk states
+  if (SPLIT) hipLaunchKernelGGL((state_pass_kernel<float, float>), gp, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((state_pass_kernel<bf16, bf16>), gp, dim3(256), 0, s, a);
   if (!SPLIT && GroupLds<P, N>::FITS) {
     // heads per workgroup: the whole group unless that leaves CUs idle
     static int num_cu = 0;
@@ -1415,7 +1388,7 @@ static hipError_t launch_segments(const PrefillParams& a, hipStream_t s) {
 
 template <int P, int N>
 static hipError_t launch_pn(const PrefillParams& a, hipStream_t s) {
-  return a.ssm_bf16 ? launch_segments<false, P, N>(a, s) : launch_segments<true, P, N>(a, s);
+  return a.ssm_bf16 ? launch_states_and_outputs<false, P, N>(a, s) : launch_states_and_outputs<true, P, N>(a, s);
 }
 
 template <int P>

@@ -211,9 +211,9 @@ def test_workspace_size_formula(pool):
     planes = 1                                   # bf16 state: single bf16 operand planes
     acts = nc * Q * (H * P + 3 * G * N) * 2 * planes
     vecs = 2 * H * T * 4                         # Delta and its chunk-local cumsum
-    segs = nc * H * P * N * 4 + nc * H * 4       # segment states and decays
+    cstates = nc * H * P * N * 2                 # chunk end states (bf16 with bf16 state)
     hin = nc * H * P * N * 2 * planes            # state entering each chunk, operand planes
-    total = acts + vecs + segs + hin
+    total = acts + vecs + cstates + hin
     assert total <= n.value < total + 64 * 1024
     assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 20, 0, byref(n)) == UNSUP
     assert lib().mamba2_prefill_workspace_size(pool, -1, 8192, 256, 0, byref(n)) == ARG
