@@ -227,10 +227,13 @@ template <int NPL, int ITEMS> struct TilePrefetch {
 // W-1 halo rows and its 8 rows are requested together (16-byte loads), the taps and SiLU run in
 // fp32, and the results are rounded to the operand planes.  B and C rows go out straight from
 // registers (eight lanes cover 128 contiguous bytes of a row); x and B also go into a
-// channel-major LDS tile, from which the transposed planes are written with consecutive lanes on
-// consecutive 16-byte pieces of one row.
+// channel-major LDS tile, each thread's block transposed in registers so that it writes 8-byte
+// runs of 4 tokens, from which the transposed planes are written with consecutive lanes
+// on consecutive 16-byte pieces of one row.  In a channel row, token group t sits at position
+// t ^ (row / 8 % 8): the eight channel octets of one token group then fall in distinct banks.
 constexpr int kConvCB = 64;
 constexpr int kConvLD = 256 + 8;   // u16 pitch of a channel row of the LDS tile (16-byte aligned)
+__device__ __forceinline__ int conv_tpos(int row, int grp) { return 8 * (grp ^ ((row >> 3) & 7)); }
 
 template <bool SPLIT> struct ConvLds {
   static constexpr int NPL = SPLIT ? 2 : 1;
@@ -322,10 +325,11 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
         }
       }
     }
-    // token j0 + r, channels c .. c+7 (zero past the chunk): B and C rows straight to global,
-    // x and B element by element into the channel-major LDS tile
+    // token j0 + r, channels c .. c+7 (zero past the chunk): B and C rows straight to global;
+    // x and B collected per channel (tv[e][r]) for the channel-major LDS tile
     u16* const brow = c < I + GN ? a.Br + (chunk * Q + j0) * GN + (c - I) : a.Cr + (chunk * Q + j0) * GN + (c - I - GN);
     const int64_t bplane = c < I + GN ? a.Br_plane : a.Cr_plane;
+    u16x4 tv[8], tl[8];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       u16x8 hv, lv;
@@ -345,11 +349,18 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
         *reinterpret_cast<u16x8*>(brow + (int64_t)r * GN) = hv;
         if (SPLIT) *reinterpret_cast<u16x8*>(brow + bplane + (int64_t)r * GN) = lv;
       }
-      if (c < I + GN) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tv[e][r & 3] = hv[e];
+        tl[e][r & 3] = lv[e];
+      }
+      if ((r & 3) == 3 && c < I + GN) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          s_t[(8 * oc + e) * kConvLD + j0 + r] = hv[e];
-          if (SPLIT) s_t[PLANE + (8 * oc + e) * kConvLD + j0 + r] = lv[e];
+          const int row = 8 * oc + e;
+          u16* d = s_t + row * kConvLD + conv_tpos(row, tg) + (r & 4);
+          *reinterpret_cast<u16x4*>(d) = tv[e];
+          if (SPLIT) *reinterpret_cast<u16x4*>(d + PLANE) = tl[e];
         }
       }
     }
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
 #pragma unroll
     for (int pl = 0; pl < NPL; ++pl)
       *reinterpret_cast<u16x8*>(dst + pl * pstride) =
-          *reinterpret_cast<const u16x8*>(s_t + pl * PLANE + ccl * kConvLD + 8 * g);
+          *reinterpret_cast<const u16x8*>(s_t + pl * PLANE + ccl * kConvLD + conv_tpos(ccl, g));
   }
 }
 
