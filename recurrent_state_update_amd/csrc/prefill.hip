@@ -13,16 +13,17 @@
 //
 // Launch sequence (one stream):
 //   1. conv_kernel        causal conv + SiLU of every (token, channel), written as bf16
-//                         operand planes in the layouts the products read
-//   2. dt_kernel          Delta = softplus(dt + dt_bias) and the chunk-local cumsum of Delta*A
-//   3. chunk_state_kernel per (chunk, head): the chunk's end state from a zero state (MFMA)
-//   4. state_pass_kernel  per (sequence, head): the affine step through the sequence's chunks ->
+//                         operand planes in the layouts the products read; its leading
+//                         workgroups compute Delta = softplus(dt + dt_bias) and the chunk-local
+//                         cumsum of Delta*A
+//   2. chunk_state_kernel per (chunk, head): the chunk's end state from a zero state (MFMA); its
+//                         trailing workgroups write the final and checkpoint conv windows
+//   3. state_pass_kernel  per (sequence, head): the affine step through the sequence's chunks ->
 //                         state entering each chunk (operand planes), checkpoint and final
 //                         states into their slots
-//   5. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
+//   4. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
 //                         C B^T formed once; chunk_out_kernel per (chunk, head) for hi/lo planes
 //                         and head_dim 128
-//   6. window_kernel      final and checkpoint conv windows (raw inputs) into their slots
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
 // otherwise operands are single bf16 planes with fp32 accumulation.
@@ -220,7 +221,45 @@ template <int NPL, int ITEMS> struct TilePrefetch {
   }
 };
 
-// ------------------------------------------------------------------ 1. conv
+// ------------------------------------------------------------------ 1a. Delta, cumsum
+// Run by the first workgroups of the conv launch (they depend on nothing the conv writes and
+// overlap its memory traffic).  One wave per (chunk, head); lane l owns rows 4l .. 4l+3 of the
+// chunk (Q <= 256).
+__device__ __forceinline__ void dt_block(const PrefillParams& a, int b) {
+  const int hq = (a.sh.H + 3) / 4;
+  const ChunkEntry ch = load_uniform(&a.chunks[b / hq]);
+  const int lane = threadIdx.x & 63;
+  const int h = (b % hq) * 4 + (threadIdx.x >> 6);
+  if (h >= a.sh.H) return;
+  const float A = a.A[h], bias = a.dt_bias[h];
+  float d[4], s[4];
+  float run = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane * 4 + e;
+    d[e] = i < ch.len ? softplus(load_any(a.dt, (int64_t)(ch.t0 + i) * a.dt_stride + h, a.io_bf16) + bias) : 0.f;
+    run += d[e] * A;
+    s[e] = run;
+  }
+  float incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const float excl = incl - run;
+  const int64_t T = a.total_tokens;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane * 4 + e;
+    if (i < ch.len) {
+      a.delta[(int64_t)h * T + ch.t0 + i] = d[e];
+      a.dA[(int64_t)h * T + ch.t0 + i] = excl + s[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 1b. conv
 // One-dimensional grid over (chunk, 64 channels), channel block fastest, so that workgroups
 // running together read neighbouring pieces of the same token rows; 256 threads.  Thread
 // (octet o, group t) convolves channels 8o .. 8o+7 over tokens 8t .. 8t+7 of the chunk: the
@@ -261,13 +300,19 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   constexpr int R = 8;
   extern __shared__ __align__(16) unsigned char conv_smem[];
   u16* const s_t = reinterpret_cast<u16*>(conv_smem);
+  const int ndt = a.num_chunks * ((a.sh.H + 3) / 4);   // leading workgroups: Delta and cumsum
+  if ((int)blockIdx.x < ndt) {
+    dt_block(a, blockIdx.x);
+    return;
+  }
+  const int bx = blockIdx.x - ndt;
   const int ncb = (a.sh.Cd + CB - 1) / CB;
-  const int64_t chunk = blockIdx.x / ncb;
+  const int64_t chunk = bx / ncb;
   const ChunkEntry ch = load_uniform(&a.chunks[chunk]);
   const SeqEntry sq = load_uniform(&a.seqs[ch.seq]);
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
   const int Q = a.Q, len = ch.len;
-  const int c0 = (blockIdx.x % ncb) * CB;
+  const int c0 = (bx % ncb) * CB;
   const int tid = threadIdx.x;
   const int oc = tid % (CB / 8), tg = tid / (CB / 8);   // 8 octets x 32 token groups
   const int c = c0 + 8 * oc;
@@ -392,41 +437,6 @@ __global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
   }
 }
 
-// ------------------------------------------------------------------ 2. Delta, cumsum
-// One wave per (chunk, head); lane l owns rows 4l .. 4l+3 of the chunk (Q <= 256).
-__global__ __launch_bounds__(256) void dt_kernel(PrefillParams a) {
-  const ChunkEntry ch = load_uniform(&a.chunks[blockIdx.x]);
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (h >= a.sh.H) return;
-  const float A = a.A[h], bias = a.dt_bias[h];
-  float d[4], s[4];
-  float run = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = lane * 4 + e;
-    d[e] = i < ch.len ? softplus(load_any(a.dt, (int64_t)(ch.t0 + i) * a.dt_stride + h, a.io_bf16) + bias) : 0.f;
-    run += d[e] * A;
-    s[e] = run;
-  }
-  float incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  const float excl = incl - run;
-  const int64_t T = a.total_tokens;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = lane * 4 + e;
-    if (i < ch.len) {
-      a.delta[(int64_t)h * T + ch.t0 + i] = d[e];
-      a.dA[(int64_t)h * T + ch.t0 + i] = excl + s[e];
-    }
-  }
-}
-
 // State tiles (P/16 x N/16 of 16x16) spread over the NW waves of a workgroup.  When the
 // shape allows, each wave owns PER_WAVE tiles of one tile row (ALIGNED), so the x-side operand
 // of the state product is read once per K-step and shared by all of the wave's tiles.
@@ -449,7 +459,45 @@ __device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N
   for (int r = 0; r < 4; ++r) d[(int64_t)(p + r) * N + n] = from_f32<TS>(v[r]);
 }
 
-// ------------------------------------------------------------------ 3. chunk end states
+// ------------------------------------------------------------------ 2a. conv windows
+// Run by the trailing workgroups of the chunk-state launch (after the conv has read the initial
+// windows): for window entry w, the raw inputs of the W-1 rows before position tau (from the
+// slot's window, or zeros, before the sequence start) into the entry's slot.
+__device__ __forceinline__ void window_block(const PrefillParams& a, int w, int c_first, int c_step) {
+  const WindowEntry we = load_uniform(&a.windows[w]);
+  const SeqEntry sq = load_uniform(&a.seqs[we.seq]);
+  const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, W1 = a.sh.W - 1;
+  for (int c = c_first; c < Cd; c += c_step) {
+    const void* src;
+    int64_t col, stride;
+    if (c < I) { src = a.x; col = c; stride = a.x_stride; }
+    else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
+    else { src = a.C; col = c - I - GN; stride = a.C_stride; }
+    float v[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (k >= W1) break;
+      const int pos = we.tau - W1 + k;
+      if (pos >= 0) {
+        v[k] = load_any(src, (int64_t)(sq.t0 + pos) * stride + col, a.io_bf16);
+      } else if (sq.has_init) {
+        const int64_t wi = ((int64_t)sq.slot * Cd + c) * W1 + (W1 + pos);
+        v[k] = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
+      } else {
+        v[k] = 0.f;
+      }
+    }
+    const int64_t wo = ((int64_t)we.slot * Cd + c) * W1;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (k >= W1) break;
+      if (a.conv_bf16) static_cast<bf16*>(a.conv)[wo + k] = from_f32<bf16>(v[k]);
+      else static_cast<float*>(a.conv)[wo + k] = v[k];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 2b. chunk end states
 // Per (chunk, head), 512 threads: the chunk's end state from a zero state,
 //   S_c = sum_j exp(a_last - a_j) Delta_j x_j B_j^T,
 // in MFMA accumulators over staged blocks of kWB tokens, the next block held in registers while
@@ -480,6 +528,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   __shared__ __align__(16) float sW[256];
   u16* const sXT = smem_w + L::XT_OFF;
   u16* const sBT = smem_w + L::BT_OFF;
+  if ((int)blockIdx.x >= a.num_chunks) {   // trailing workgroups: conv windows
+    window_block(a, blockIdx.x - a.num_chunks, blockIdx.y * kStateThreads + threadIdx.x, gridDim.y * kStateThreads);
+    return;
+  }
   const int c = blockIdx.x, h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
   const int g = h / (H / G);
   const ChunkEntry ch = load_uniform(&a.chunks[c]);
@@ -603,7 +655,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   }
 }
 
-// ------------------------------------------------------------------ 4. pass over each sequence's chunks
+// ------------------------------------------------------------------ 3. pass over each sequence's chunks
 // Per (sequence, head, 2048 state elements), 256 threads of 8 elements each: the affine step
 //   h <- exp(a_last(c)) h + S_c
 // through the sequence's chunks from its initial state (the slot's, or zero).  Before each chunk
@@ -690,7 +742,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillParams a) {
   store_state(sq.slot);
 }
 
-// ------------------------------------------------------------------ 5. chunk outputs
+// ------------------------------------------------------------------ 4. chunk outputs
 // Per (chunk, head), 512 threads; wave w owns the 16-row tiles w and 15 - w of the chunk
 // (equal causal work per wave for Q = 256).  Y = exp(a_i) C_i h_in + (M o L) X + D x, gated.
 // Tokens per staged block: two K-steps with single bf16 planes, one with hi/lo planes.
@@ -1003,12 +1055,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_out_kernel(PrefillParams a
   }
 }
 
-// ------------------------------------------------------------------ 5b. helpers of the grouped output kernel
+// ------------------------------------------------------------------ 4b. helpers of the grouped output kernel
 // 2^x and log2(x) as the bare hardware instructions: results below 2^-126 flush to zero, which
 // only drops terms that are negligible against the rest of a sum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ------------------------------------------------------------------ 5c. chunk outputs, a group's heads in turn
+// ------------------------------------------------------------------ 4c. chunk outputs, a group's heads in turn
 // Per (chunk, group, part of the group's heads), 512 threads, single bf16 operand planes.  C B^T
 // depends on the chunk and group only: each wave forms its nine (row tile, K-step) slots once,
 // from the chunk's B rows staged in LDS and its C rows held as register fragments, and keeps
@@ -1319,40 +1371,6 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   }
 }
 
-// ------------------------------------------------------------------ 6. conv windows
-template <int W>
-__global__ __launch_bounds__(256) void window_kernel(PrefillParams a) {
-  const WindowEntry we = a.windows[blockIdx.x];
-  const SeqEntry sq = a.seqs[we.seq];
-  const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= Cd) return;
-  const void* src;
-  int64_t col, stride;
-  if (c < I) { src = a.x; col = c; stride = a.x_stride; }
-  else if (c < I + GN) { src = a.B; col = c - I; stride = a.B_stride; }
-  else { src = a.C; col = c - I - GN; stride = a.C_stride; }
-  float v[W - 1];
-#pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
-    const int pos = we.tau - (W - 1) + k;
-    if (pos >= 0) {
-      v[k] = load_any(src, (int64_t)(sq.t0 + pos) * stride + col, a.io_bf16);
-    } else if (sq.has_init) {
-      const int64_t wi = ((int64_t)sq.slot * Cd + c) * (W - 1) + (W - 1 + pos);
-      v[k] = a.conv_bf16 ? to_f32(static_cast<const bf16*>(a.conv)[wi]) : static_cast<const float*>(a.conv)[wi];
-    } else {
-      v[k] = 0.f;
-    }
-  }
-  const int64_t wo = ((int64_t)we.slot * Cd + c) * (W - 1);
-#pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
-    if (a.conv_bf16) static_cast<bf16*>(a.conv)[wo + k] = from_f32<bf16>(v[k]);
-    else static_cast<float*>(a.conv)[wo + k] = v[k];
-  }
-}
-
 // ------------------------------------------------------------------ launch
 // Allow `bytes` of dynamic LDS for a kernel (idempotent; called before each launch).
 static hipError_t set_lds_attr(const void* fn, int bytes) {
@@ -1361,7 +1379,8 @@ static hipError_t set_lds_attr(const void* fn, int bytes) {
 
 template <bool SPLIT, int P, int N>
 static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N>), dim3(a.num_chunks, a.sh.H), dim3(kStateThreads), 0, s, a);
+  hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N>), dim3(a.num_chunks + a.num_windows, a.sh.H),
+                     dim3(kStateThreads), 0, s, a);
   const dim3 gp(a.num_seqs, a.sh.H, (P * N / 8 + 255) / 256);
   // hi/lo planes go with fp32 state: fp32 chunk states; bf16 state: bf16 chunk states
   if (SPLIT) hipLaunchKernelGGL((state_pass_kernel<float, float>), gp, dim3(256), 0, s, a);
@@ -1421,7 +1440,9 @@ bool prefill_supported(int P, int N, int W) {
 
 hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
   if (a.num_chunks == 0) return hipSuccess;
-  const dim3 gc((unsigned)a.num_chunks * ((a.sh.Cd + kConvCB - 1) / kConvCB));
+  // Delta/cumsum workgroups first, then (chunk, 64 channels) with the channel block fastest
+  const unsigned per_chunk = (unsigned)((a.sh.H + 3) / 4 + (a.sh.Cd + kConvCB - 1) / kConvCB);
+  const dim3 gc((unsigned)a.num_chunks * per_chunk);
   const bool split = !a.ssm_bf16;
   hipError_t ea = hipSuccess;
 #define M2_CONV_IO(WW, SP, IO)                                                                           \
@@ -1444,7 +1465,6 @@ hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
 #undef M2_CONV
 #undef M2_CONV_IO
   if (ea != hipSuccess) return ea;
-  hipLaunchKernelGGL(dt_kernel, dim3(a.num_chunks, (a.sh.H + 3) / 4), dim3(256), 0, s, a);
   hipError_t e = hipErrorInvalidValue;
   switch (a.sh.P) {
     case 16: e = launch_p<16>(a, s); break;
@@ -1453,14 +1473,6 @@ hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
     case 128: e = launch_p<128>(a, s); break;
   }
   if (e != hipSuccess) return e;
-  if (a.num_windows > 0) {
-    const dim3 gw(a.num_windows, (a.sh.Cd + 255) / 256);
-    switch (a.sh.W) {
-      case 2: hipLaunchKernelGGL(window_kernel<2>, gw, dim3(256), 0, s, a); break;
-      case 3: hipLaunchKernelGGL(window_kernel<3>, gw, dim3(256), 0, s, a); break;
-      case 4: hipLaunchKernelGGL(window_kernel<4>, gw, dim3(256), 0, s, a); break;
-    }
-  }
   return hipGetLastError();
 }
 
