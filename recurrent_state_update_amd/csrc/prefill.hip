@@ -498,90 +498,108 @@ __device__ __forceinline__ void window_block(const PrefillParams& a, int w, int 
 }
 
 // ------------------------------------------------------------------ 2b. chunk end states
-// Per (chunk, head), 512 threads: the chunk's end state from a zero state,
+// Per (chunk, HPW heads of one group), 512 threads: each head's end state from a zero state,
 //   S_c = sum_j exp(a_last - a_j) Delta_j x_j B_j^T,
 // in MFMA accumulators over staged blocks of kWB tokens, the next block held in registers while
-// the current one is used.  Written to the chunk-state array through an LDS tile as 16-byte
-// pieces of rows: fp32 with hi/lo planes (fp32 state), bf16 otherwise.
+// the current one is used; the group's B block is staged once for the workgroup's heads.
+// Written to the chunk-state array through an LDS tile as 16-byte pieces of rows: fp32 with
+// hi/lo planes (fp32 state), bf16 otherwise.
 constexpr int kWB = kPB;   // one block of the transposed planes
 
-template <bool SPLIT, int P, int N> struct WalkLds {
+template <bool SPLIT, int P, int N, int HPW> struct WalkLds {
   static constexpr int NPL = SPLIT ? 2 : 1;
   static constexpr int LDX = kWB + 4;   // 34 dwords per row: the 16 rows of a fragment hit distinct banks
+  static constexpr int XROWS = HPW * P;                     // x rows of all the workgroup's heads
   static constexpr int XT_OFF = 0;                          // u16 offsets
-  static constexpr int BT_OFF = XT_OFF + NPL * P * LDX;
+  static constexpr int BT_OFF = XT_OFF + NPL * XROWS * LDX;
   static constexpr int STAGE_END = BT_OFF + NPL * N * LDX;
   // end-state staging (overlays the blocks): fp32 rows of N + 4, or bf16 rows of N + 8
   static constexpr int LDS_ST = SPLIT ? N + 4 : N + 8;
-  static constexpr int ST_END = P * LDS_ST * (SPLIT ? 2 : 1);
+  static constexpr int ST_END = XROWS * LDS_ST * (SPLIT ? 2 : 1);
   static constexpr int U16S = STAGE_END > ST_END ? STAGE_END : ST_END;
-  static constexpr int IT_XT = (P * (kWB / 8) + kStateThreads - 1) / kStateThreads;
+  static constexpr int IT_XT = (XROWS * (kWB / 8) + kStateThreads - 1) / kStateThreads;
   static constexpr int IT_BT = (N * (kWB / 8) + kStateThreads - 1) / kStateThreads;
 };
 
-template <bool SPLIT, int P, int N>
+template <bool SPLIT, int P, int N, int HPW>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParams a) {
-  typedef WalkLds<SPLIT, P, N> L;
-  typedef StateTiles<P, N, kStateThreads / 64> ST;
+  typedef WalkLds<SPLIT, P, N, HPW> L;
+  constexpr int WPH = (kStateThreads / 64) / HPW;   // waves per head
+  typedef StateTiles<P, N, WPH> ST;
   constexpr int NPL = L::NPL, LDX = L::LDX;
   __shared__ __align__(16) u16 smem_w[L::U16S];
-  __shared__ __align__(16) float sW[256];
+  __shared__ __align__(16) float sW[HPW * 256];
   u16* const sXT = smem_w + L::XT_OFF;
   u16* const sBT = smem_w + L::BT_OFF;
   if ((int)blockIdx.x >= a.num_chunks) {   // trailing workgroups: conv windows
     window_block(a, blockIdx.x - a.num_chunks, blockIdx.y * kStateThreads + threadIdx.x, gridDim.y * kStateThreads);
     return;
   }
-  const int c = blockIdx.x, h = blockIdx.y, H = a.sh.H, G = a.sh.G, Q = a.Q;
-  const int g = h / (H / G);
+  const int c = blockIdx.x, h0 = blockIdx.y * HPW, H = a.sh.H, G = a.sh.G, Q = a.Q;
+  const int g = h0 / (H / G);
   const ChunkEntry ch = load_uniform(&a.chunks[c]);
   const int len = ch.len;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = wave_id();
+  const int hw = wave / WPH, wh = wave % WPH;   // this wave's head and its index among the head's waves
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t T = a.total_tokens;
   const int64_t PN = (int64_t)P * N;
   const int QB = (Q + kPB - 1) / kPB;
 
-  TilePrefetch<NPL, L::IT_XT> px;
-  TilePrefetch<NPL, L::IT_BT> pb;
-  auto prefetch = [&](int jb) {
-    px.load(a.xT + (((int64_t)c * H + h) * QB + jb / kPB) * P * kPB, a.xT_plane, kPB, P, kWB, P, len - jb, tid,
-            kStateThreads);
-    pb.load(a.Bt + (((int64_t)c * G + g) * QB + jb / kPB) * N * kPB, a.Bt_plane, kPB, N, kWB, N, len - jb, tid,
+  // x rows of the HPW heads (row r: head r / P, channel r % P; a head's blocks are QB * P * kPB
+  // apart), requested like TilePrefetch: branch-free, clamped, masked when stored
+  // two register sets, two blocks in flight: set k holds the blocks jb with jb / kWB % 2 == k
+  u16x8 xv[2][L::IT_XT][NPL];
+  TilePrefetch<NPL, L::IT_BT> pb[2];
+  auto prefetch = [&](int k, int jb) {
+    const u16* xb = a.xT + (((int64_t)c * H + h0) * QB + jb / kPB) * P * kPB;
+#pragma unroll
+    for (int it = 0; it < L::IT_XT; ++it) {
+      const int idx = tid + it * kStateThreads;
+      const int r = idx / (kWB / 8), cc = (idx % (kWB / 8)) * 8;
+      const bool in = idx < L::XROWS * (kWB / 8) && cc < len - jb;
+      const int off = in ? (r / P) * QB * P * kPB + (r % P) * kPB + cc : 0;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) xv[k][it][pl] = *reinterpret_cast<const u16x8*>(xb + pl * a.xT_plane + off);
+    }
+    pb[k].load(a.Bt + (((int64_t)c * G + g) * QB + jb / kPB) * N * kPB, a.Bt_plane, kPB, N, kWB, N, len - jb, tid,
             kStateThreads);
   };
-  prefetch(0);
-  {   // weights w_j = exp(a_last - a_j) Delta_j of the chunk's tokens
-    const int64_t base = (int64_t)h * T + ch.t0;
-    const int j = min(tid & 255, len - 1);
-    const float aj = a.dA[base + j], dj = a.delta[base + j], alast = a.dA[base + len - 1];
-    if (tid < 256) sW[tid] = tid < len ? __expf(alast - aj) * dj : 0.f;
-  }
+  // weights w_j = exp(a_last - a_j) Delta_j of the chunk's tokens (head tid / 256), requested
+  // before the blocks so that their use waits for nothing else
+  const int whh = min(tid >> 8, HPW - 1);
+  const int64_t wbase = (int64_t)(h0 + whh) * T + ch.t0;
+  const int wj = min(tid & 255, len - 1);
+  const float aj = a.dA[wbase + wj], dj = a.delta[wbase + wj], alast = a.dA[wbase + len - 1];
+  prefetch(0, 0);
+  prefetch(1, kWB < len ? kWB : 0);
+  if ((tid >> 8) < HPW) sW[tid] = (tid & 255) < len ? __expf(alast - aj) * dj : 0.f;
 
   floatx4 acc[ST::PER_WAVE];
 #pragma unroll
   for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int jb = 0; jb < len; jb += kWB) {
+  auto step = [&](int k, int jb) {
     __syncthreads();   // all reads of the previous block are done (and sW is written)
     // x goes to LDS already scaled by w_j (one rounding of the product, as the operand needs),
     // so the K-steps read it as a finished fragment
 #pragma unroll
     for (int it = 0; it < L::IT_XT; ++it) {
       const int idx = tid + it * kStateThreads;
-      if (idx < P * (kWB / 8)) {
+      if (idx < L::XROWS * (kWB / 8)) {
         const int r = idx / (kWB / 8), cc = (idx % (kWB / 8)) * 8;
-        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sW[jb + cc]);
-        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sW[jb + cc + 4]);
+        const float* w = sW + (r / P) * 256 + jb + cc;
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>(w);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>(w + 4);
         u16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float xv = f_of(px.v[it][0][e]);
-          if (SPLIT) xv += f_of(px.v[it][NPL - 1][e]);
-          xv = jb + cc + e < len ? xv * (e < 4 ? w0[e] : w1[e - 4]) : 0.f;
+          float xf = f_of(xv[k][it][0][e]);
+          if (SPLIT) xf += f_of(xv[k][it][NPL - 1][e]);
+          xf = jb + cc + e < len ? xf * (e < 4 ? w0[e] : w1[e - 4]) : 0.f;
           u16 hi, lo = 0;
-          if (SPLIT) split2(xv, hi, lo);
-          else hi = bits_of(from_f32<bf16>(xv));
+          if (SPLIT) split2(xf, hi, lo);
+          else hi = bits_of(from_f32<bf16>(xf));
           hv[e] = hi;
           lv[e] = lo;
         }
@@ -589,52 +607,58 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
         *reinterpret_cast<u16x4*>(d) = u16x4{hv[0], hv[1], hv[2], hv[3]};
         *reinterpret_cast<u16x4*>(d + 4) = u16x4{hv[4], hv[5], hv[6], hv[7]};
         if (SPLIT) {
-          *reinterpret_cast<u16x4*>(d + P * LDX) = u16x4{lv[0], lv[1], lv[2], lv[3]};
-          *reinterpret_cast<u16x4*>(d + P * LDX + 4) = u16x4{lv[4], lv[5], lv[6], lv[7]};
+          *reinterpret_cast<u16x4*>(d + L::XROWS * LDX) = u16x4{lv[0], lv[1], lv[2], lv[3]};
+          *reinterpret_cast<u16x4*>(d + L::XROWS * LDX + 4) = u16x4{lv[4], lv[5], lv[6], lv[7]};
         }
       }
     }
-    if (jb + kWB <= len) pb.store_full(sBT, N * LDX, LDX, N, kWB, tid, kStateThreads);   // uniform
-    else pb.store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);
+    pb[k].store(sBT, N * LDX, LDX, N, kWB, N, len - jb, tid, kStateThreads);   // one path: precise waits
     __syncthreads();
-    // the next block; one straight path (past the last block the current one is fetched again
-    // and not used)
-    prefetch(jb + kWB < len ? jb + kWB : jb);
+    // the block after next into this set; one straight path (past the last block the current
+    // one is fetched again and not used)
+    prefetch(k, jb + 2 * kWB < len ? jb + 2 * kWB : jb);
+    const u16* const sXh = sXT + hw * P * LDX;   // this wave's head
 #pragma unroll
     for (int kb = 0; kb < kWB; kb += 32) {
       if (jb + kb >= len) break;
       // x-side operand of tile row pt: (w x)^T over the K-step's tokens, staged scaled
-      auto xfrag = [&](int pt) { return lds_frag<SPLIT>(sXT, P * LDX, LDX, pt * 16 + l16, kb, q); };
+      auto xfrag = [&](int pt) { return lds_frag<SPLIT>(sXh, L::XROWS * LDX, LDX, pt * 16 + l16, kb, q); };
       if (ST::ALIGNED) {
-        const Frag<SPLIT> fa = xfrag(ST::pt(wave, 0));
+        const Frag<SPLIT> fa = xfrag(ST::pt(wh, 0));
         Frag<SPLIT> fb[ST::PER_WAVE];
 #pragma unroll
         for (int m = 0; m < ST::PER_WAVE; ++m)
-          fb[m] = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+          fb[m] = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wh, m) * 16 + l16, kb, q);
 #pragma unroll
         for (int m = 0; m < ST::PER_WAVE; ++m) acc[m] = mma<SPLIT>(fa, fb[m], acc[m]);
       } else {
 #pragma unroll
         for (int m = 0; m < ST::PER_WAVE; ++m) {
-          if (ST::valid(wave, m)) {
-            const Frag<SPLIT> fa = xfrag(ST::pt(wave, m));
-            const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wave, m) * 16 + l16, kb, q);
+          if (ST::valid(wh, m)) {
+            const Frag<SPLIT> fa = xfrag(ST::pt(wh, m));
+            const Frag<SPLIT> fb = lds_frag<SPLIT>(sBT, N * LDX, LDX, ST::nt(wh, m) * 16 + l16, kb, q);
             acc[m] = mma<SPLIT>(fa, fb, acc[m]);
           }
         }
       }
     }
+  };
+  // a chunk has at most 256 / kWB blocks: straight-line code keeps every wait exact
+#pragma unroll
+  for (int b = 0; b < 256 / kWB; ++b) {
+    if (b * kWB >= len) break;
+    step(b & 1, b * kWB);
   }
 
-  // the end state -> LDS rows -> 16-byte stores
+  // the end states -> LDS rows -> 16-byte stores
   __syncthreads();   // the last block's reads are done before the staging overlays it
 #pragma unroll
   for (int m = 0; m < ST::PER_WAVE; ++m) {
-    if (ST::valid(wave, m)) {
-      const int pt = ST::pt(wave, m), nt = ST::nt(wave, m);
+    if (ST::valid(wh, m)) {
+      const int pt = ST::pt(wh, m), nt = ST::nt(wh, m);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = (pt * 16 + 4 * q + r) * L::LDS_ST + nt * 16 + l16;
+        const int i = (hw * P + pt * 16 + 4 * q + r) * L::LDS_ST + nt * 16 + l16;
         if (SPLIT) reinterpret_cast<float*>(smem_w)[i] = acc[m][r];
         else smem_w[i] = bits_of(from_f32<bf16>(acc[m][r]));
       }
@@ -642,14 +666,15 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   }
   __syncthreads();
   constexpr int VPR = SPLIT ? N / 4 : N / 8;   // 16-byte pieces per row
-  for (int idx = tid; idx < P * VPR; idx += kStateThreads) {
-    const int row = idx / VPR, cv = idx % VPR;
+  for (int idx = tid; idx < L::XROWS * VPR; idx += kStateThreads) {
+    const int row = idx / VPR, cv = idx % VPR;   // row = head * P + p
+    const int64_t o = ((int64_t)c * H + h0) * PN + (int64_t)row * N;   // heads are PN apart
     if (SPLIT) {
-      float* dst = static_cast<float*>(a.cstate) + ((int64_t)c * H + h) * PN + row * N + cv * 4;
+      float* dst = static_cast<float*>(a.cstate) + o + cv * 4;
       *reinterpret_cast<floatx4*>(dst) =
           *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(smem_w) + row * L::LDS_ST + cv * 4);
     } else {
-      u16* dst = static_cast<u16*>(a.cstate) + ((int64_t)c * H + h) * PN + row * N + cv * 8;
+      u16* dst = static_cast<u16*>(a.cstate) + o + cv * 8;
       *reinterpret_cast<u16x8*>(dst) = *reinterpret_cast<const u16x8*>(smem_w + row * L::LDS_ST + cv * 8);
     }
   }
@@ -1379,8 +1404,13 @@ static hipError_t set_lds_attr(const void* fn, int bytes) {
 
 template <bool SPLIT, int P, int N>
 static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N>), dim3(a.num_chunks + a.num_windows, a.sh.H),
-                     dim3(kStateThreads), 0, s, a);
+  // two heads of a group per workgroup share the staged B blocks (one for hi/lo planes)
+  if (!SPLIT && (a.sh.H / a.sh.G) % 2 == 0)
+    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 2>), dim3(a.num_chunks + a.num_windows, a.sh.H / 2),
+                       dim3(kStateThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 1>), dim3(a.num_chunks + a.num_windows, a.sh.H),
+                       dim3(kStateThreads), 0, s, a);
   const dim3 gp(a.num_seqs, a.sh.H, (P * N / 8 + 255) / 256);
   // hi/lo planes go with fp32 state: fp32 chunk states; bf16 state: bf16 chunk states
   if (SPLIT) hipLaunchKernelGGL((state_pass_kernel<float, float>), gp, dim3(256), 0, s, a);
