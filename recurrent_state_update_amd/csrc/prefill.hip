@@ -1396,10 +1396,345 @@ __global__ __launch_bounds__(512) void chunk_out_group_kernel(PrefillParams a, i
   }
 }
 
+// ------------------------------------------------------------------ 4d. chunk outputs with hi/lo planes, a group's heads in turn
+// fp32 state: every operand is a bf16 hi plane plus a lo plane and each product takes three
+// MFMAs.  Per (chunk, group, part of the group's heads), 512 threads, as the single-plane kernel
+// above, with what the doubled operands leave room for: C B^T is formed once per workgroup (split
+// products) and kept in fp32 registers; the C fragments of C h_in are read per head, state
+// dimension contiguous per lane; one LDS buffer (x, entering state and output staging take
+// 136 KB), so a head's operands are requested while the previous head writes its last tile.
+template <int P, int N> struct GroupSplitLds {
+  static constexpr int QM = 256;
+  static constexpr int LDB = N + 4;      // B rows [j][n], hi and lo (set-up only, overlaid below)
+  static constexpr int LDX = QM + 4;     // x transposed [p][j], hi and lo
+  static constexpr int LDH = N + 8;      // entering state [p][n], hi and lo, 16-byte aligned rows
+  static constexpr int LDO = P + 4;      // output staging [row][p], fp32, one 16-row tile per wave
+  static constexpr int XPL = P * LDX;    // u16 plane strides
+  static constexpr int HPL = P * LDH;
+  static constexpr int H_OFF = 2 * XPL;  // u16 offsets
+  static constexpr int O_OFF = H_OFF + 2 * HPL;
+  static constexpr int HEAD_END = O_OFF + 8 * 16 * LDO * 2;   // fp32 staging counted in u16
+  static constexpr int SETUP_END = 2 * QM * LDB;
+  static constexpr int U16_END = HEAD_END > SETUP_END ? HEAD_END : SETUP_END;
+  static constexpr int F_OFF = (U16_END * 2 + 15) / 16 * 16;   // bytes: sA2, sB2, sCw
+  static constexpr int BYTES = F_OFF + 3 * 256 * 4;
+  static constexpr bool FITS = BYTES <= 160 * 1024 && P <= 64;
+  static constexpr int IT_BR = (QM * (N / 8) + 511) / 512;
+  static constexpr int IT_XT = (P * (QM / 8) + 511) / 512;
+  static constexpr int IT_H = (P * (N / 8) + 511) / 512;
+};
+
+template <int P, int N>
+__global__ __launch_bounds__(512) void chunk_out_group_split_kernel(PrefillParams a, int heads_per_wg) {
+  typedef GroupSplitLds<P, N> L;
+  constexpr int PT = P / 16;
+  constexpr int NK = N / 32 > 0 ? N / 32 : 1;
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int CG = P / 8;                   // 8-channel groups of an output row
+  constexpr int ZI = (16 * CG + 63) / 64;     // output items (8 channels of one token) per lane per tile
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  u16* const smem = reinterpret_cast<u16*>(smem_raw);
+
+  const int c = blockIdx.x;
+  const ChunkEntry ch = load_uniform(&a.chunks[c]);
+  const int len = ch.len;
+  const int H = a.sh.H, G = a.sh.G, Q = a.Q, GN = G * N;
+  const int hpg = H / G;
+  const int parts = hpg / heads_per_wg;
+  const int g = blockIdx.y / parts;
+  const int h0 = g * hpg + (blockIdx.y % parts) * heads_per_wg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = wave_id();
+  const int q = lane >> 4, l16 = lane & 15;
+  const int64_t T = a.total_tokens;
+  const int nrt = Q / 16;
+  const int rts[2] = {wave, 15 - wave};
+  const bool vt[2] = {rts[0] < nrt && rts[0] * 16 < len, rts[1] < nrt && rts[1] * 16 < len};
+  const int QB = (Q + kPB - 1) / kPB;
+  const int m0 = wave >> 1;
+  const int mt[2] = {m0, 7 - m0};   // K-steps below each tile; K-step mt[t] holds its diagonal
+
+  TilePrefetch<2, L::IT_XT> px;
+  TilePrefetch<2, L::IT_H> ph;
+  float pa, pd, pr;
+  auto prefetch = [&](int h) {
+    px.load(a.xT + ((int64_t)c * H + h) * QB * P * kPB, a.xT_plane, kPB, QB * P, kPB, QB * P, kPB, tid, 512);
+    ph.load(a.hin + ((int64_t)c * H + h) * P * N, a.hin_plane, N, P, N, P, N, tid, 512);
+    const int j = min(tid, len - 1);
+    const float* dAh = a.dA + (int64_t)h * T + ch.t0;
+    pa = dAh[j];
+    pd = a.delta[(int64_t)h * T + ch.t0 + j];
+    pr = dAh[min(j | 31, len - 1)];
+  };
+  prefetch(h0);
+
+  // C B^T slots in fp32 (split products): below-diagonal slots of tile 0 in gb[0 .. m0-1] and of
+  // tile 1 from gb[6] downwards, the diagonal slots in gd
+  floatx4 gb[7][2], gd[2][2];
+  {
+    u16* const sBr = smem;
+    TilePrefetch<2, L::IT_BR> pb;
+    pb.load(a.Br + (int64_t)c * Q * GN + g * N, a.Br_plane, GN, L::QM, N, len, N, tid, 512);
+    Frag<true> cf[2][NK];
+    load_c_frags<true, N, NK>(a, c, g, len, rts, nrt, q, l16, cf);
+    pb.store(sBr, L::QM * L::LDB, L::LDB, L::QM, N, len, N, tid, 512);
+    __syncthreads();
+    auto slot = [&](int t, int ks, floatx4 (&out)[2]) {
+      Frag<true> fb[2][NK];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          fb[jt][kk] = lds_frag<true>(sBr, L::QM * L::LDB, L::LDB, 32 * ks + jt * 16 + l16, N >= 32 ? kk * 32 : 0, q);
+          if (N < 32) {
+#pragma unroll
+            for (int e = 4; e < 8; ++e) { fb[jt][kk].hi[e] = bf_of(0); fb[jt][kk].lo[e] = bf_of(0); }
+          }
+        }
+      }
+      if (t == 0) gt_tile<true, NK>(cf[0], fb, out);
+      else gt_tile<true, NK>(cf[1], fb, out);
+    };
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      gb[k][0] = gb[k][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (k < m0) {
+        if (vt[0]) slot(0, k, gb[k]);
+      } else if (vt[1]) {
+        slot(1, 6 - k, gb[k]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      gd[t][0] = gd[t][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (vt[t]) slot(t, mt[t], gd[t]);
+    }
+  }
+
+  const u16* const cbase = a.Cr + (int64_t)c * Q * GN + g * N;
+  for (int hh = 0; hh < heads_per_wg; ++hh) {
+    const int h = h0 + hh;
+    // LDS bases through an opaque zero: the per-lane addresses derived from them stay inside the
+    // head loop instead of being hoisted out of it and spilled
+    const int zo = opaque_uniform(0);
+    u16* const sXT = smem + zo;
+    u16* const sH = smem + L::H_OFF + zo;
+    float* const sA2 = reinterpret_cast<float*>(smem_raw + L::F_OFF) + zo;
+    float* const sB2 = sA2 + 256;
+    float* const sCw = sB2 + 256;
+    float* const sO = reinterpret_cast<float*>(smem + L::O_OFF) + wave * 16 * L::LDO + zo;
+    __syncthreads();   // the set-up or the previous head is done with the LDS buffer
+    // this head's x blocks [QB][P][kPB] -> sXT[p][token] (hi, lo; tokens past the chunk zeroed),
+    // its entering state and its tables
+#pragma unroll
+    for (int it = 0; it < L::IT_XT; ++it) {
+      const int idx = tid + it * 512;
+      const int r = idx / (kPB / 8), cc = (idx % (kPB / 8)) * 8;
+      if (r < QB * P) {
+        const int j = (r / P) * kPB + cc;
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          u16x8 x = px.v[it][pl];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = j + e < len ? x[e] : u16(0);
+          u16* d = sXT + pl * L::XPL + (r % P) * L::LDX + j;
+          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+        }
+      }
+    }
+    ph.store(sH, L::HPL, L::LDH, P, N, P, N, tid, 512);
+    if (tid < 256) {
+      const bool ok = tid < len;
+      sA2[tid] = ok ? pa * kLog2e : -INFINITY;
+      sB2[tid] = ok ? pa * kLog2e - __builtin_amdgcn_logf(pd) : 0.f;
+      sCw[tid] = ok ? fast_exp2((pr - pa) * kLog2e) * pd : 0.f;
+    }
+    __syncthreads();
+    const float Dh = load_uniform(&a.D[h]);
+    const bool zpre = a.io_bf16 && a.zy_vec;
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (!vt[t]) continue;
+      const int rt = rts[t];
+      const int i = rt * 16 + l16;
+      const float a2i = sA2[i];
+      // z of this tile (bf16 io: 16-byte row pieces, the output items below)
+      u16x8 zr[ZI];
+      if (zpre) {
+        const u16* zbase = static_cast<const u16*>(a.z) + ch.t0 * a.z_stride + h * P;
+#pragma unroll
+        for (int k = 0; k < ZI; ++k) {
+          const int it = min(lane + 64 * k, 16 * CG - 1);
+          const int ii = rt * 16 + it / CG;
+          zr[k] = *reinterpret_cast<const u16x8*>(zbase + (ii < len ? ii : 0) * (int)a.z_stride + (it % CG) * 8);
+        }
+      }
+      // exp(a_i) h_in^T C_i^T: C row i from global (hi, lo), n = 32 ks + 8 q .. + 7
+      floatx4 acc[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      {
+        const int ii = i < len ? i : 0;
+        Frag<true> fc[NK];
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          const int n = ks * 32 + 8 * q;
+          const u16* cr = cbase + ii * GN + (n < N ? n : 0);
+          const u16x8 ch8 = *reinterpret_cast<const u16x8*>(cr);
+          const u16x8 cl8 = *reinterpret_cast<const u16x8*>(cr + a.Cr_plane);
+          const bool ok = n < N && i < len;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            fc[ks].hi[e] = bf_of(ok ? ch8[e] : u16(0));
+            fc[ks].lo[e] = bf_of(ok ? cl8[e] : u16(0));
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          const int n = ks * 32 + 8 * q;
+          const bool ok = n < N;
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            const u16* hp = sH + (pt * 16 + l16) * L::LDH + (ok ? n : 0);
+            const u16x8 hh8 = *reinterpret_cast<const u16x8*>(hp);
+            const u16x8 hl8 = *reinterpret_cast<const u16x8*>(hp + L::HPL);
+            Frag<true> fh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              fh.hi[e] = bf_of(ok ? hh8[e] : u16(0));
+              fh.lo[e] = bf_of(ok ? hl8[e] : u16(0));
+            }
+            acc[pt] = mma<true>(fh, fc[ks], acc[pt]);
+          }
+        }
+        const float sc = fast_exp2(a2i);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pt][r] *= sc;
+      }
+
+      // (M o L) X below the diagonal: exp(a_i - a_j) = 2^(a2_i - a2_ref) times the column factor
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        if (k >= mt[t]) break;
+        const int jk = 32 * k;
+        Frag<true> fx[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<true>(sXT, L::XPL, L::LDX, pt * 16 + l16, jk, q);
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(&sCw[jk + 4 * q]);
+        const floatx4 c1 = *reinterpret_cast<const floatx4*>(&sCw[jk + 16 + 4 * q]);
+        const float rf = fast_exp2(a2i - sA2[jk + 31]);
+        const floatx4(&gs)[2] = t == 0 ? gb[k] : gb[6 - k];
+        float mv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mv[e] = gs[0][e] * (rf * c0[e]);
+          mv[e + 4] = gs[1][e] * (rf * c1[e]);
+        }
+        const Frag<true> mf = make_frag<true>(mv);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = mma<true>(fx[pt], mf, acc[pt]);
+      }
+
+      // the diagonal K-step (as in the single-plane kernel)
+      {
+        const int jk = 32 * mt[t];
+        Frag<true> fx[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) fx[pt] = lds_frag<true>(sXT, L::XPL, L::LDX, pt * 16 + l16, jk, q);
+        const int dsel = l16 - 4 * q;
+        const floatx4 bd = *reinterpret_cast<const floatx4*>(&sB2[16 * rt + 4 * q]);
+        float mv[8];
+        if (rt & 1) {
+          const floatx4 bb = *reinterpret_cast<const floatx4*>(&sB2[jk + 4 * q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = fast_exp2(a2i - bd[e]) * gd[t][1][e];
+            mv[e + 4] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e] = fast_exp2(a2i - bb[e]) * gd[t][0][e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = fast_exp2(a2i - bd[e]) * gd[t][0][e];
+            mv[e] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e + 4] = 0.f;
+          }
+        }
+        const Frag<true> mf = make_frag<true>(mv);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = mma<true>(fx[pt], mf, acc[pt]);
+      }
+
+      // the next head's operands go out before this workgroup's last tile is written (the last
+      // reads of x and h are behind; they land in LDS after the next barrier)
+      if (t == 1 || !vt[1]) prefetch(min(h + 1, h0 + heads_per_wg - 1));
+
+      // y = acc * SiLU(z) through this wave's LDS tile, z and y as 16-byte row pieces
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) *reinterpret_cast<floatx4*>(&sO[l16 * L::LDO + pt * 16 + 4 * q]) = acc[pt];
+#pragma unroll
+      for (int k = 0; k < ZI; ++k) {
+        const int it = lane + 64 * k;
+        if (it >= 16 * CG) continue;
+        const int rr = it / CG, c8 = (it % CG) * 8;
+        const int ii = rt * 16 + rr;
+        if (ii >= len) continue;
+        const floatx4 o0 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8]);
+        const floatx4 o1 = *reinterpret_cast<const floatx4*>(&sO[rr * L::LDO + c8 + 4]);
+        float v[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+        const int64_t row = ch.t0 + ii + opaque_uniform(0);   // keeps these addresses inside the loop
+        const int col = h * P + c8;
+        if (zpre) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= silu(f_of(zr[k][e]));
+          store8_any(a.y, row * a.y_stride + col, a.y_bf16, v);
+        } else if (a.zy_vec) {
+          float zf[8];
+          load8_any(a.z, row * a.z_stride + col, a.io_bf16, zf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= silu(zf[e]);
+          store8_any(a.y, row * a.y_stride + col, a.y_bf16, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float zv = load_any(a.z, row * a.z_stride + col + e, a.io_bf16);
+            store_any(a.y, row * a.y_stride + col + e, v[e] * silu(zv), a.y_bf16);
+          }
+        }
+      }
+    }
+    if (!vt[0] && !vt[1]) prefetch(min(h + 1, h0 + heads_per_wg - 1));   // waves with no tile
+  }
+}
+
 // ------------------------------------------------------------------ launch
 // Allow `bytes` of dynamic LDS for a kernel (idempotent; called before each launch).
 static hipError_t set_lds_attr(const void* fn, int bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// Workgroups per (chunk, group) of the grouped output kernels: the whole group in one unless
+// that leaves CUs idle (then the group's heads are split evenly).
+static int group_parts(const PrefillParams& a) {
+  static int num_cu = 0;
+  if (num_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cu < 1)
+      num_cu = 256;
+  }
+  const int hpg = a.sh.H / a.sh.G;
+  int parts = 1;
+  while ((int64_t)a.num_chunks * a.sh.G * parts < num_cu && parts < hpg) {
+    int next = parts + 1;
+    while (hpg % next != 0) ++next;
+    parts = next;
+  }
+  return parts;
 }
 
 template <bool SPLIT, int P, int N>
@@ -1416,26 +1751,22 @@ static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t 
   if (SPLIT) hipLaunchKernelGGL((state_pass_kernel<float, float>), gp, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((state_pass_kernel<bf16, bf16>), gp, dim3(256), 0, s, a);
   if (!SPLIT && GroupLds<P, N>::FITS) {
-    // heads per workgroup: the whole group unless that leaves CUs idle
-    static int num_cu = 0;
-    if (num_cu == 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cu < 1)
-        num_cu = 256;
-    }
     const int hpg = a.sh.H / a.sh.G;
-    int parts = 1;
-    while ((int64_t)a.num_chunks * a.sh.G * parts < num_cu && parts < hpg) {
-      int next = parts + 1;
-      while (hpg % next != 0) ++next;
-      parts = next;
-    }
+    const int parts = group_parts(a);
     typedef GroupLds<P, N> L;
     const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&chunk_out_group_kernel<P, N>), L::BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_out_group_kernel<P, N>), dim3(a.num_chunks, a.sh.G * parts), dim3(512), L::BYTES, s, a,
                        hpg / parts);
+    return hipSuccess;
+  }
+  if (SPLIT && GroupSplitLds<P, N>::FITS) {
+    typedef GroupSplitLds<P, N> L;
+    const hipError_t e = set_lds_attr(reinterpret_cast<const void*>(&chunk_out_group_split_kernel<P, N>), L::BYTES);
+    if (e != hipSuccess) return e;
+    const int hpg = a.sh.H / a.sh.G;
+    hipLaunchKernelGGL((chunk_out_group_split_kernel<P, N>), dim3(a.num_chunks, a.sh.G * group_parts(a)), dim3(512),
+                       L::BYTES, s, a, hpg / group_parts(a));
     return hipSuccess;
   }
   typedef OutLds<SPLIT, P, N> L;
