@@ -6,7 +6,9 @@ of P=64, N=128, G=8 groups, conv width 4) for 256 live sequences at randomly
 permuted slots of a 512-slot bf16 pool: conv-window shift, conv + SiLU,
 softplus, state update, readout, gate, in place on the pool.  Inputs are
 synthetic (seeded, resident in HBM before timing).  A second leg times the
-chunked prefill of one 8192-token sequence (chunk 256) at the same shape.
+chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
+third the prefills of the mixed continuous batch (with checkpoints) and one
+layer of the 2 x 131072-token long context with fp32 state.
 
 Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one
 decode launch divided by its average duration, timed with HIP events on the
@@ -59,6 +61,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill-workloads", action="store_true",
+                    help="skip the mixed-batch and long-context prefill timings")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="after timing, run 10 slot copies of PAIRS slot pairs (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
@@ -191,12 +195,79 @@ def main() -> int:
             "hbm_frac": io_bytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
         del ppool, ws
+        if not args.no_prefill_workloads:
+            out["prefill_workloads"] = prefill_workloads(dev, stream, e0, e1)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+def prefill_workloads(dev, stream, e0, e1) -> dict:
+    """Prefill throughput of the mixed continuous batch (its 32 varlen prefills with checkpoints
+    every 1024 tokens, bf16 state) and of one layer of the long context (2 x 131072 tokens, fp32
+    state).  Layouts come from the workload generators; token values are drawn on the GPU (they do
+    not affect the timing)."""
+    import torch
+
+    from recurrent_state_update_amd import synth
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+    sh = synth.NEMOTRON_H
+    gen = torch.Generator(device=dev).manual_seed(7)
+
+    def tokens(T, y_dtype):
+        u = torch.randn(T, sh.conv_dim, device=dev, generator=gen).bfloat16()
+        z = torch.randn(T, sh.intermediate, device=dev, generator=gen).bfloat16()
+        dt = torch.randn(T, sh.nheads, device=dev, generator=gen).bfloat16()
+        return u, z, dt, torch.empty(T, sh.intermediate, device=dev, dtype=y_dtype)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    _, params, lens, p_slots, _, ck = synth.mixed_layout(3)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    pool = Pool.allocate(1, 512, sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
+                         torch.bfloat16, torch.bfloat16, dev)
+    W = LayerWeights.from_numpy(params, dev)
+    u, z, dt, y = tokens(T, torch.bfloat16)
+    x, B, C = pool.split_xbc(u)
+    ws = torch.empty(pool.workspace_size(len(lens), T, 256), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: pool.prefill(0, W, cu, p_slots, np.zeros(len(lens), np.uint8), x, B, C, z, dt, y,
+                                    chunk_size=256, ckpt_interval=1024, ckpt_slots=ck, workspace=ws), 10)
+    res["mixed_batch"] = {"workload": f"{len(lens)} varlen prefills of U(128, 4096) tokens ({T} in all), chunk 256, "
+                                      "checkpoints every 1024 tokens, bf16 state",
+                          "ms": ms, "tokens_per_s": T / (ms * 1e-3)}
+    del pool, ws, u, z, dt, y, x, B, C
+    torch.cuda.empty_cache()
+
+    lw = synth.long_workload()
+    T = lw["seqs"] * lw["L"]
+    pool = Pool.allocate(1, lw["seqs"], sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
+                         torch.float32, torch.bfloat16, dev)
+    W = LayerWeights.from_numpy(synth.long_layer_params(0), dev)
+    u, z, dt, y = tokens(T, torch.float32)
+    x, B, C = pool.split_xbc(u)
+    ws = torch.empty(pool.workspace_size(lw["seqs"], T, lw["chunk"]), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: pool.prefill(0, W, lw["cu_seqlens"], lw["slots"], lw["has_init"], x, B, C, z, dt, y,
+                                    chunk_size=lw["chunk"], workspace=ws), 3)
+    res["long_context_fp32"] = {"workload": f"one layer of {lw['seqs']} x {lw['L']} tokens, chunk 256, fp32 state",
+                                "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
+                                "ms_per_48_layers": 48 * ms}
+    del pool, ws, u, z, dt, y, x, B, C
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, budget_s: float) -> dict:

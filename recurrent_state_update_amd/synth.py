@@ -177,15 +177,10 @@ def prefill_workload(seed: int = 2, L: int = 8192, chunk: int = 256, slot: int =
                 u=u, z=z, dt=dt, chunk=chunk)
 
 
-def mixed_workload(seed: int = 3, n_prefill: int = 32, n_decode: int = 224, num_slots: int = 512,
-                   interval: int = 1024, chunk: int = 256, shape: Shape = NEMOTRON_H,
-                   lmin: int = 128, lmax: int = 4096) -> dict:
-    """Continuous batch: varlen-packed prefills from zero state plus single-token decodes.
-
-    Checkpoint slots are taken from the free slots in ascending order, in
-    (sequence, checkpoint) order; a prefill of L tokens checkpoints at every
-    multiple of ``interval`` in (0, L].
-    """
+def mixed_layout(seed: int = 3, n_prefill: int = 32, n_decode: int = 224, num_slots: int = 512,
+                 interval: int = 1024, shape: Shape = NEMOTRON_H, lmin: int = 128, lmax: int = 4096):
+    """The mixed batch without its token data: (rng, params, prefill lengths, prefill slots,
+    decode slots, checkpoint slots); the rng is left where the token draws begin."""
     rng = np.random.default_rng(seed)
     params = layer_params(rng, shape)
     lens = rng.integers(lmin, lmax + 1, n_prefill).astype(np.int32)
@@ -199,6 +194,20 @@ def mixed_workload(seed: int = 3, n_prefill: int = 32, n_decode: int = 224, num_
     for i in range(n_prefill):
         for k in range(n_ck[i]):
             ck[i, k] = next(it)
+    return rng, params, lens, p_slots, d_slots, ck
+
+
+def mixed_workload(seed: int = 3, n_prefill: int = 32, n_decode: int = 224, num_slots: int = 512,
+                   interval: int = 1024, chunk: int = 256, shape: Shape = NEMOTRON_H,
+                   lmin: int = 128, lmax: int = 4096) -> dict:
+    """Continuous batch: varlen-packed prefills from zero state plus single-token decodes.
+
+    Checkpoint slots are taken from the free slots in ascending order, in
+    (sequence, checkpoint) order; a prefill of L tokens checkpoints at every
+    multiple of ``interval`` in (0, L].
+    """
+    rng, params, lens, p_slots, d_slots, ck = mixed_layout(seed, n_prefill, n_decode, num_slots, interval, shape,
+                                                           lmin, lmax)
     T = int(lens.sum())
     u, z, dt = _tokens(rng, shape, T, "bf16")
     d_ssm0, d_conv0 = _live_state(rng, shape, n_decode, "bf16", "bf16")
