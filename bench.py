@@ -41,16 +41,52 @@ def prefill_dense_flops_per_token(sh, Q) -> int:
     return 2 * Q * sh.d_state * sh.n_groups + 2 * Q * sh.head_dim * sh.nheads + 4 * sh.nheads * sh.head_dim * sh.d_state
 
 
+DECODE_SOURCES = ["recurrent_state_update_amd/csrc/decode.hip", "recurrent_state_update_amd/csrc/device_common.h",
+                  "recurrent_state_update_amd/csrc/kernels.h"]
+
+
+def decode_source_sha(root: str) -> str:
+    import hashlib
+    return hashlib.sha256(b"".join(open(os.path.join(root, p), "rb").read() for p in DECODE_SOURCES)).hexdigest()
+
+
+def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
+    """profiles/decode_traffic.json from the two counter runs of profiles/decode_256seq_hbm_traffic.md:
+    average FETCH_SIZE and WRITE_SIZE (KiB) per decode dispatch, each scaled by what the counter
+    reads for the slot copy of 131,072 KiB of state (the --calibrate-copy 64 launches)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, part):
+        acc = {}
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        for r in csv.DictReader(open(f)):
+            if part in r["Kernel_Name"]:
+                acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return list(acc.values())
+
+    avg = lambda v: sum(v) / len(v)
+    dec_f, dec_w = per_dispatch(fetch_dir, "decode_kernel"), per_dispatch(write_dir, "decode_kernel")
+    cp_f = [v for v in per_dispatch(fetch_dir, "slot_copy_kernel") if v > 10000]   # the state copies
+    cp_w = [v for v in per_dispatch(write_dir, "slot_copy_kernel") if v > 10000]
+    fs, ws = 131072.0 / avg(cp_f), 131072.0 / avg(cp_w)
+    rec = {"kernel": "decode_kernel<bf16, N=128, W=4>", "workload": "decode step, 256 sequences, Nemotron-H layer shape",
+           "source_sha256": decode_source_sha(root), "sources": DECODE_SOURCES,
+           "fetch_kib_per_launch": avg(dec_f), "write_kib_per_launch": avg(dec_w), "fetch_scale": fs,
+           "write_scale": ws, "traffic_bytes_per_launch": (avg(dec_f) * fs + avg(dec_w) * ws) * 1024}
+    json.dump(rec, open(os.path.join(root, "profiles", "decode_traffic.json"), "w"), indent=1)
+    return rec
+
+
 def measured_traffic(root: str):
     """HBM bytes per decode launch from the committed counter profile, if the kernel sources still match."""
-    import hashlib
     path = os.path.join(root, "profiles", "decode_traffic.json")
     try:
         rec = json.load(open(path))
-        src = b"".join(open(os.path.join(root, p), "rb").read() for p in rec["sources"])
+        sha = decode_source_sha(root)
     except (OSError, ValueError, KeyError):
         return None
-    return rec["traffic_bytes_per_launch"] if hashlib.sha256(src).hexdigest() == rec["source_sha256"] else None
+    return rec["traffic_bytes_per_launch"] if sha == rec["source_sha256"] else None
 
 
 def main() -> int:
@@ -61,12 +97,19 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--write-traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/decode_traffic.json from the FETCH_SIZE and WRITE_SIZE counter runs and exit")
     ap.add_argument("--no-prefill-workloads", action="store_true",
                     help="skip the mixed-batch and long-context prefill timings")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
                     help="after timing, run 10 slot copies of PAIRS slot pairs (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
     args = ap.parse_args()
+    if args.write_traffic_record:
+        root = os.path.dirname(os.path.abspath(__file__))
+        rec = write_traffic_record(root, *args.write_traffic_record)
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
               "sequence and needs no collective); run with --gpus 1", file=sys.stderr)

@@ -19,47 +19,19 @@
 #include "device_common.h"
 #include "kernels.h"
 
-// Tuning knobs (compile-time): state rows per lane batch, threads per
-// workgroup, minimum waves per SIMD the register budget must allow,
-// non-temporal state accesses, prefetch depth, and whether the first state
-// tile is requested before the conv phase.  Defaults are the fastest
-// combination measured on MI355X for the 8B-hybrid decode (see the design notes).
-#ifndef M2_DECODE_ROWS
-#define M2_DECODE_ROWS 8
-#endif
-#ifndef M2_DECODE_THREADS
-#define M2_DECODE_THREADS 512
-#endif
-#ifndef M2_DECODE_WAVES_PER_EU
-#define M2_DECODE_WAVES_PER_EU 1
-#endif
-#ifndef M2_DECODE_NT
-#define M2_DECODE_NT 1
-#endif
-#ifndef M2_DECODE_PF
-#define M2_DECODE_PF 1
-#endif
-#ifndef M2_DECODE_EARLY
-#define M2_DECODE_EARLY 1
-#endif
-
 namespace m2 {
 
-// M2_DECODE_NT: 1 = non-temporal loads and stores, 2 = loads only, 3 = stores only.
-template <typename V> __device__ __forceinline__ V ld_state(const V* p) {
-#if M2_DECODE_NT == 1 || M2_DECODE_NT == 2
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-template <typename V> __device__ __forceinline__ void st_state(V* p, const V& v) {
-#if M2_DECODE_NT == 1 || M2_DECODE_NT == 3
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
+// Shape of the launch, the fastest combination measured on MI355X for the 8B-hybrid decode:
+// state rows per lane batch, threads per workgroup, minimum waves per SIMD the register budget
+// must allow.
+constexpr int kDecodeRows = 8;
+constexpr int kDecodeThreads = 512;
+constexpr int kDecodeWavesPerEU = 1;
+
+// The state is streamed once per step: non-temporal loads and stores keep it from displacing
+// reusable lines in the caches.
+template <typename V> __device__ __forceinline__ V ld_state(const V* p) { return __builtin_nontemporal_load(p); }
+template <typename V> __device__ __forceinline__ void st_state(V* p, const V& v) { __builtin_nontemporal_store(v, p); }
 
 template <typename T> struct Vec16;
 template <> struct Vec16<float> { typedef floatx4 type; };
@@ -92,14 +64,14 @@ template <int M, int O> struct RowReduce {
 };
 
 template <typename TS, int N, int W>
-__global__ __launch_bounds__(M2_DECODE_THREADS) __attribute__((amdgpu_waves_per_eu(M2_DECODE_WAVES_PER_EU)))
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEU)))
 void decode_kernel(DecodeParams a) {
   typedef typename Vec16<TS>::type vec_t;
   constexpr int VEC = 16 / sizeof(TS);   // state elements per 16-byte access
   constexpr int LPR = N / VEC;           // lanes per state row
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "unsupported d_state");
   constexpr int RPI = 64 / LPR;          // rows per wave-wide access
-  constexpr int U0 = M2_DECODE_ROWS / RPI;
+  constexpr int U0 = kDecodeRows / RPI;
   constexpr int U = U0 < 1 ? 1 : (U0 > 16 ? 16 : U0);   // accesses in flight per lane
   constexpr int RB = RPI * U;            // rows per batch
   constexpr int MF = U > LPR ? U / LPR : 1;             // row sums held per lane at the end
@@ -150,19 +122,10 @@ void decode_kernel(DecodeParams a) {
       if (row < P) d[j] = ld_state(reinterpret_cast<const vec_t*>(st + (int64_t)row * N + n0));
     }
   };
-  vec_t data[U];
-#if M2_DECODE_PF >= 1
-  vec_t next[U];
-#endif
-#if M2_DECODE_PF >= 2
-  vec_t next2[U];
-#endif
-#if M2_DECODE_EARLY && M2_DECODE_PF >= 1
+  // one state tile held in registers ahead of the one in use; the first is requested before
+  // the conv phase so that its latency overlaps it
+  vec_t data[U], next[U];
   if (ntile > 0) load_tile(0, next);
-#if M2_DECODE_PF >= 2
-  if (ntile > 1) load_tile(1, next2);
-#endif
-#endif
   // ---------------------------------------------------------------- conv
   const int nch = nx + 2 * N;
   for (int ck = tid * 8; ck < nch; ck += blockDim.x * 8) {
@@ -262,24 +225,10 @@ void decode_kernel(DecodeParams a) {
     Bv[e] = s_act[nx + n0 + e];
     Cv[e] = s_act[nx + N + n0 + e];
   }
-#if !M2_DECODE_EARLY && M2_DECODE_PF >= 1
-  if (ntile > 0) load_tile(0, next);
-#if M2_DECODE_PF >= 2
-  if (ntile > 1) load_tile(1, next2);
-#endif
-#endif
   for (int t = 0; t < ntile; ++t) {
-#if M2_DECODE_PF >= 2
-#pragma unroll
-    for (int j = 0; j < U; ++j) { data[j] = next[j]; next[j] = next2[j]; }
-    if (t + 2 < ntile) load_tile(t + 2, next2);
-#elif M2_DECODE_PF == 1
 #pragma unroll
     for (int j = 0; j < U; ++j) data[j] = next[j];
     if (t + 1 < ntile) load_tile(t + 1, next);
-#else
-    load_tile(t, data);
-#endif
     int hl, r0;
     TS* const st = tile_ptr(t, hl, r0);
     const float delta = s_delta[hl];
@@ -325,7 +274,7 @@ template <typename TS, int N>
 static hipError_t launch_w(const DecodeParams& p, int W, int batch, hipStream_t s) {
   const int hpg = p.H / p.G;
   const size_t lds = sizeof(float) * (hpg * p.P + 2 * N + 2 * hpg);
-  const dim3 grid(p.G, batch), block(M2_DECODE_THREADS);
+  const dim3 grid(p.G, batch), block(kDecodeThreads);
   switch (W) {
     case 2: hipLaunchKernelGGL((decode_kernel<TS, N, 2>), grid, block, lds, s, p); break;
     case 3: hipLaunchKernelGGL((decode_kernel<TS, N, 3>), grid, block, lds, s, p); break;
