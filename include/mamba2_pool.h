@@ -167,6 +167,11 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  * first row.  workspace: device memory of at least
  * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch
  * and not read across calls.  Sequences with zero length leave their slot untouched.
+ * Launch tables (32 bytes per sequence and per chunk, 16 per conv window written)
+ * of up to 3072 bytes travel in the first kernel's arguments, so the call enqueues
+ * no copy and never blocks; larger tables go through a pinned host buffer owned by
+ * the pool handle, and the call may then wait on the host for the previous such
+ * upload to finish before it reuses the buffer.
  * With fp32 SSM state the contractions run in split-bf16 (three products)
  * for fp32-level accuracy; with bf16 state they run in bf16 with fp32 accumulate. */
 m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_params* params,

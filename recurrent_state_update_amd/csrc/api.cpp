@@ -110,7 +110,7 @@ m2_status hip_fail(hipError_t e, const char* what) {
 // Prefill tables and workspace carving.
 struct PrefillLayout {
   uint64_t nc_max, nw_max, planes;
-  uint64_t off_seqs, off_chunks, off_windows, meta_bytes;
+  uint64_t meta_bytes;   // the packed tables (sequences, chunks, windows) at the start
   uint64_t off_xT, off_Bt, off_Br, off_Cr, plane_xT, plane_Bt, plane_Br, plane_Cr;
   uint64_t off_delta, off_dA, off_cstate, off_hin, plane_hin, total;
 };
@@ -119,10 +119,9 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   L->nc_max = (uint64_t)(T / Q) + (uint64_t)num_seqs;
   L->nw_max = (uint64_t)num_seqs + L->nc_max;
   L->planes = split ? 2 : 1;
-  L->off_seqs = 0;
-  L->off_chunks = align_up(L->off_seqs + num_seqs * sizeof(m2::SeqEntry), 256);
-  L->off_windows = align_up(L->off_chunks + L->nc_max * sizeof(m2::ChunkEntry), 256);
-  L->meta_bytes = align_up(L->off_windows + L->nw_max * sizeof(m2::WindowEntry), 256);
+  L->meta_bytes = align_up(align_up(num_seqs * sizeof(m2::SeqEntry), 16) + align_up(L->nc_max * sizeof(m2::ChunkEntry), 16) +
+                               L->nw_max * sizeof(m2::WindowEntry),
+                           256);
   const uint64_t rows = L->nc_max * (uint64_t)Q;          // chunk-blocked rows
   uint64_t v;
   const uint64_t brows = L->nc_max * (uint64_t)((Q + m2::kPB - 1) / m2::kPB * m2::kPB);   // whole blocks
@@ -406,37 +405,50 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   }
   if (chunks.empty()) return ok();
 
-  // ---- upload the tables through pinned staging (one H2D copy)
+  // ---- pack the tables; small ones travel in the conv launch's arguments, larger ones are
+  // uploaded through pinned staging (one host-to-device copy)
+  const size_t tab_chunks = align_up(seqs.size() * sizeof(m2::SeqEntry), 16);
+  const size_t tab_windows = tab_chunks + align_up(chunks.size() * sizeof(m2::ChunkEntry), 16);
+  const size_t tab_bytes = align_up(tab_windows + windows.size() * sizeof(m2::WindowEntry), 16);
+  if (tab_bytes > L.meta_bytes) return fail(M2_ERR_WORKSPACE, "table packing exceeds its workspace region");
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  {
-    std::lock_guard<std::mutex> lock(pool->mu);
+  const bool tab_inline = tab_bytes <= (size_t)m2::kInlineTableBytes;
+  m2::InlineTables inl;
+  char* tab = reinterpret_cast<char*>(inl.w);
+  std::unique_lock<std::mutex> lock(pool->mu, std::defer_lock);
+  if (!tab_inline) {
+    lock.lock();
     hipError_t e;
     if (pool->staging_pending) {
       if ((e = hipEventSynchronize(pool->staging_done)) != hipSuccess) return hip_fail(e, "staging wait");
       pool->staging_pending = false;
     }
-    if (pool->staging_bytes < L.meta_bytes) {
+    if (pool->staging_bytes < tab_bytes) {
       if (pool->staging) (void)hipHostFree(pool->staging);
       pool->staging = nullptr;
       pool->staging_bytes = 0;
-      if ((e = hipHostMalloc(&pool->staging, L.meta_bytes, hipHostMallocDefault)) != hipSuccess)
+      if ((e = hipHostMalloc(&pool->staging, tab_bytes, hipHostMallocDefault)) != hipSuccess)
         return hip_fail(e, "pinned staging allocation");
-      pool->staging_bytes = L.meta_bytes;
+      pool->staging_bytes = tab_bytes;
     }
     if (!pool->staging_done) {
       if ((e = hipEventCreateWithFlags(&pool->staging_done, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "staging event");
     }
-    char* st = static_cast<char*>(pool->staging);
-    memset(st, 0, L.meta_bytes);
-    memcpy(st + L.off_seqs, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
-    memcpy(st + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
-    memcpy(st + L.off_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
-    if ((e = hipMemcpyAsync(ws, st, L.meta_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
+    tab = static_cast<char*>(pool->staging);
+  }
+  memset(tab, 0, tab_bytes);
+  memcpy(tab, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
+  memcpy(tab + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
+  memcpy(tab + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
+  if (!tab_inline) {
+    hipError_t e;
+    if ((e = hipMemcpyAsync(ws, tab, tab_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
       return hip_fail(e, "table upload");
     if ((e = hipEventRecord(pool->staging_done, hs)) != hipSuccess) return hip_fail(e, "staging event record");
     pool->staging_pending = true;
+    lock.unlock();
   }
 
   m2::PrefillParams p;
@@ -454,9 +466,12 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.num_chunks = (int)chunks.size();
   p.num_windows = (int)windows.size();
   p.total_tokens = (int)T;
-  p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws + L.off_seqs);
-  p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + L.off_chunks);
-  p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + L.off_windows);
+  p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws);
+  p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + tab_chunks);
+  p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + tab_windows);
+  p.tab_chunks = (int)tab_chunks;
+  p.tab_windows = (int)tab_windows;
+  p.tab_inline = tab_inline ? (int)tab_bytes : 0;
   p.x = x;
   p.B = B;
   p.C = C;
@@ -487,7 +502,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.cstate = ws + L.off_cstate;
   p.hin = reinterpret_cast<uint16_t*>(ws + L.off_hin);
   p.hin_plane = (int64_t)L.plane_hin;
-  const hipError_t e = m2::launch_prefill(p, hs);
+  const hipError_t e = m2::launch_prefill(p, tab_inline ? &inl : nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
 }

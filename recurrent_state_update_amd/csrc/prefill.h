@@ -28,9 +28,12 @@ struct PrefillParams {
   LayerShape sh;
   int Q;               // chunk size
   int num_seqs, num_chunks, num_windows, total_tokens;
-  const SeqEntry* seqs;
+  const SeqEntry* seqs;        // the tables, packed in this order at the start of the workspace
   const ChunkEntry* chunks;
   const WindowEntry* windows;
+  int tab_chunks, tab_windows;   // byte offsets of the chunk and window tables from the sequence table
+  int tab_inline;              // > 0: the tables (this many bytes) ride in the conv launch's arguments
+                               // and that launch writes them to the workspace; 0: already there
   const void* x;
   const void* B;
   const void* C;
@@ -60,7 +63,20 @@ struct PrefillParams {
   uint16_t* hin;         // [planes][chunks][H][P][N]: state entering each chunk, bf16 operand planes
   int64_t hin_plane;     // elements per plane
 };
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// Tables of up to kInlineTableBytes travel inside the conv launch's kernel arguments: its
+// workgroups read them from there and one extra workgroup writes them to the workspace for the
+// later launches, so a call needs no host-to-device copy.
+constexpr int kInlineTableBytes = 3072;
+struct alignas(16) InlineTables {
+  int32_t w[kInlineTableBytes / 4];
+};
+struct ConvArgs {   // the conv launch's one kernel argument
+  PrefillParams p;
+  InlineTables t;
+};
+
+// `inl` holds the packed tables when p.tab_inline > 0 (else it may be NULL).
+hipError_t launch_prefill(const PrefillParams& p, const InlineTables* inl, hipStream_t s);
 bool prefill_supported(int P, int N, int W);
 
 }  // namespace m2

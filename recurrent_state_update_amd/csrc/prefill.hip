@@ -27,6 +27,8 @@
 // With SPLIT every product operand is a bf16 hi plane plus a bf16 lo plane and
 // each product takes three MFMAs (fp32-level accuracy, used for fp32 state);
 // otherwise operands are single bf16 planes with fp32 accumulation.
+#include <cstddef>
+#include <cstring>
 #include <type_traits>
 
 #include "device_common.h"
@@ -225,9 +227,9 @@ template <int NPL, int ITEMS> struct TilePrefetch {
 // Run by the first workgroups of the conv launch (they depend on nothing the conv writes and
 // overlap its memory traffic).  One wave per (chunk, head); lane l owns rows 4l .. 4l+3 of the
 // chunk (Q <= 256).
-__device__ __forceinline__ void dt_block(const PrefillParams& a, int b) {
+__device__ __forceinline__ void dt_block(const PrefillParams& a, const ChunkEntry* chunks, int b) {
   const int hq = (a.sh.H + 3) / 4;
-  const ChunkEntry ch = load_uniform(&a.chunks[b / hq]);
+  const ChunkEntry ch = load_uniform(&chunks[b / hq]);
   const int lane = threadIdx.x & 63;
   const int h = (b % hq) * 4 + (threadIdx.x >> 6);
   if (h >= a.sh.H) return;
@@ -292,24 +294,50 @@ template <bool IOBF> __device__ __forceinline__ void load_row8(const void* p, in
   }
 }
 
+// The packed tables inside the conv launch's own kernel arguments.
+__device__ __forceinline__ const __attribute__((address_space(4))) unsigned char* conv_arg_tables() {
+  typedef const __attribute__((address_space(4))) unsigned char kbyte;
+  return (kbyte*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(ConvArgs, t);
+}
+
+// One workgroup of the conv launch: copy the tables from the kernel arguments to the workspace,
+// where the later launches read them (tab_inline is a multiple of 16 bytes).
+__device__ __forceinline__ void table_copy_block(const PrefillParams& a) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) i32x4 kquad;
+  kquad* src = reinterpret_cast<kquad*>(conv_arg_tables());
+  i32x4* dst = reinterpret_cast<i32x4*>(const_cast<SeqEntry*>(a.seqs));
+  for (int i = threadIdx.x; i < a.tab_inline / 16; i += blockDim.x) dst[i] = src[i];
+}
+
 template <int W, bool SPLIT, bool IOBF>
-__global__ __launch_bounds__(256) void conv_kernel(PrefillParams a) {
+__global__ __launch_bounds__(256) void conv_kernel(ConvArgs args) {
+  const PrefillParams& a = args.p;
   constexpr int CB = kConvCB;
   constexpr int NPL = ConvLds<SPLIT>::NPL;
   constexpr int PLANE = CB * kConvLD;
   constexpr int R = 8;
   extern __shared__ __align__(16) unsigned char conv_smem[];
   u16* const s_t = reinterpret_cast<u16*>(conv_smem);
+  // this launch reads the tables where the host put them: its own arguments or the workspace
+  const unsigned char* tab = a.tab_inline > 0 ? (const unsigned char*)conv_arg_tables()
+                                              : reinterpret_cast<const unsigned char*>(a.seqs);
+  const SeqEntry* seqs = reinterpret_cast<const SeqEntry*>(tab);
+  const ChunkEntry* chunks = reinterpret_cast<const ChunkEntry*>(tab + a.tab_chunks);
   const int ndt = a.num_chunks * ((a.sh.H + 3) / 4);   // leading workgroups: Delta and cumsum
   if ((int)blockIdx.x < ndt) {
-    dt_block(a, blockIdx.x);
+    dt_block(a, chunks, blockIdx.x);
     return;
   }
   const int bx = blockIdx.x - ndt;
   const int ncb = (a.sh.Cd + CB - 1) / CB;
+  if (bx >= a.num_chunks * ncb) {   // trailing workgroup (inline tables only)
+    table_copy_block(a);
+    return;
+  }
   const int64_t chunk = bx / ncb;
-  const ChunkEntry ch = load_uniform(&a.chunks[chunk]);
-  const SeqEntry sq = load_uniform(&a.seqs[ch.seq]);
+  const ChunkEntry ch = load_uniform(&chunks[chunk]);
+  const SeqEntry sq = load_uniform(&seqs[ch.seq]);
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
   const int Q = a.Q, len = ch.len;
   const int c0 = (bx % ncb) * CB;
@@ -1799,17 +1827,23 @@ bool prefill_supported(int P, int N, int W) {
   return p_ok && n_ok && W >= 2 && W <= 4;
 }
 
-hipError_t launch_prefill(const PrefillParams& a, hipStream_t s) {
+hipError_t launch_prefill(const PrefillParams& a, const InlineTables* inl, hipStream_t s) {
   if (a.num_chunks == 0) return hipSuccess;
-  // Delta/cumsum workgroups first, then (chunk, 64 channels) with the channel block fastest
+  if (a.tab_inline < 0 || a.tab_inline > kInlineTableBytes || a.tab_inline % 16 != 0 || (a.tab_inline > 0 && !inl))
+    return hipErrorInvalidValue;
+  ConvArgs ca;
+  ca.p = a;
+  if (a.tab_inline > 0) memcpy(&ca.t, inl, (size_t)a.tab_inline);
+  // Delta/cumsum workgroups first, then (chunk, 64 channels) with the channel block fastest, then
+  // the table copy
   const unsigned per_chunk = (unsigned)((a.sh.H + 3) / 4 + (a.sh.Cd + kConvCB - 1) / kConvCB);
-  const dim3 gc((unsigned)a.num_chunks * per_chunk);
+  const dim3 gc((unsigned)a.num_chunks * per_chunk + (a.tab_inline > 0 ? 1u : 0u));
   const bool split = !a.ssm_bf16;
   hipError_t ea = hipSuccess;
 #define M2_CONV_IO(WW, SP, IO)                                                                           \
   {                                                                                                      \
     ea = set_lds_attr(reinterpret_cast<const void*>(&conv_kernel<WW, SP, IO>), ConvLds<SP>::BYTES);      \
-    hipLaunchKernelGGL((conv_kernel<WW, SP, IO>), gc, dim3(256), ConvLds<SP>::BYTES, s, a);              \
+    hipLaunchKernelGGL((conv_kernel<WW, SP, IO>), gc, dim3(256), ConvLds<SP>::BYTES, s, ca);             \
   }
 #define M2_CONV(WW)                                                                                       \
   if (split) {                                                                                            \

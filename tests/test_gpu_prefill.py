@@ -259,6 +259,42 @@ def test_prefill_is_batch_invariant_and_deterministic(ssm_dtype):
             assert torch.equal(pool_c.ssm[0, ck].view(torch.uint8), pool_a.ssm[0, ck].view(torch.uint8))
 
 
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_large_tables_take_the_upload_path_with_identical_results(ssm_dtype):
+    """Small launch tables ride in the first kernel's arguments; 100 extra empty sequences push them
+    past that room, onto the staged upload.  The real sequences' outputs and states are bit-identical
+    either way, and the empty sequences' slots stay untouched."""
+    c = _varlen_case(ssm_dtype, 64, seed=501)
+    sh = c["sh"]
+    W = weights(c["params"])
+    n, extra = len(c["lens"]), 100
+    bits = torch.int16 if ssm_dtype == "bf16" else torch.int32
+
+    def run(pad):
+        pool = make_pool(sh, 1, 40 + extra, ssm_dtype, "bf16", sentinel_seed=9)
+        for i in range(n):
+            put_slot(pool, 0, int(c["slots"][i]), c["ssm0"][i], c["conv0"][i])
+        before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+        lens = np.concatenate([c["lens"], np.zeros(pad, np.int32)])
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        slots = np.concatenate([c["slots"], 40 + np.arange(pad, dtype=np.int32)])
+        has_init = np.concatenate([c["has_init"], np.ones(pad, np.uint8)])
+        start = np.concatenate([c["start"], np.zeros(pad, np.int32)])
+        ck = np.concatenate([c["ck"], np.full((pad, c["ck"].shape[1]), -1, np.int32)])
+        log(f"case: varlen {ssm_dtype}, chunk 64, {n} sequences + {pad} empty")
+        y = run_prefill(pool, W, cu, slots, has_init, c["u"], c["z"], c["dt"], c["io"], ssm_dtype, start_pos=start,
+                        chunk=64, interval=c["interval"], ckpt=ck)
+        written = list(c["slots"]) + [int(s) for s in c["ck"].ravel() if s >= 0]
+        assert untouched(before_s, pool.ssm, written) and untouched(before_c, pool.conv, written)
+        return pool, y
+
+    pool_a, y_a = run(0)
+    pool_b, y_b = run(extra)
+    assert torch.equal(y_a.view(bits), y_b.view(bits))
+    assert torch.equal(pool_a.ssm.view(torch.uint8), pool_b.ssm.view(torch.uint8))
+    assert torch.equal(pool_a.conv.view(torch.uint8), pool_b.conv.view(torch.uint8))
+
+
 def test_checkpoint_equals_prefix_prefill_and_restore_replay():
     """A checkpoint at 256 equals a 256-token prefill; restoring it into a fresh slot and
     replaying the suffix reproduces the uninterrupted run (fp32 state, to fp32 rounding)."""
