@@ -6,8 +6,10 @@ of P=64, N=128, G=8 groups, conv width 4) for 256 live sequences at randomly
 permuted slots of a 512-slot bf16 pool: conv-window shift, conv + SiLU,
 softplus, state update, readout, gate, in place on the pool.  Inputs are
 synthetic (seeded, resident in HBM before timing).  A second leg times the
+checkpoint copy (256 slot-to-slot copies of both state objects), which is also
+the measured ceiling of a streaming kernel on the part.  A third times the
 chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
-third the prefills of the mixed continuous batch (with checkpoints) and one
+fourth the prefills of the mixed continuous batch (with checkpoints) and one
 layer of the 2 x 131072-token long context with fp32 state.
 
 Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one
@@ -41,8 +43,10 @@ def prefill_dense_flops_per_token(sh, Q) -> int:
     return 2 * Q * sh.d_state * sh.n_groups + 2 * Q * sh.head_dim * sh.nheads + 4 * sh.nheads * sh.head_dim * sh.d_state
 
 
+# sources of the decode kernel and of the copy kernel whose counter readings scale the decode's
 DECODE_SOURCES = ["recurrent_state_update_amd/csrc/decode.hip", "recurrent_state_update_amd/csrc/device_common.h",
-                  "recurrent_state_update_amd/csrc/kernels.h"]
+                  "recurrent_state_update_amd/csrc/kernels.h", "recurrent_state_update_amd/csrc/ckpt.hip"]
+COPY_PAIRS = 256      # slot pairs per timed checkpoint copy (the decode pool's 512 slots, halves swapped)
 
 
 def decode_source_sha(root: str) -> str:
@@ -53,7 +57,8 @@ def decode_source_sha(root: str) -> str:
 def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
     """profiles/decode_traffic.json from the two counter runs of profiles/decode_256seq_hbm_traffic.md:
     average FETCH_SIZE and WRITE_SIZE (KiB) per decode dispatch, each scaled by what the counter
-    reads for the slot copy of 131,072 KiB of state (the --calibrate-copy 64 launches)."""
+    reads for the checkpoint copy of known size (COPY_PAIRS x (2 MiB of state + 60 KiB of conv window)
+    per launch)."""
     import csv
     import glob
 
@@ -67,9 +72,10 @@ def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
 
     avg = lambda v: sum(v) / len(v)
     dec_f, dec_w = per_dispatch(fetch_dir, "decode_kernel"), per_dispatch(write_dir, "decode_kernel")
+    known = COPY_PAIRS * (2097152 + 61440) / 1024           # KiB of state and conv window per copy launch
     cp_f = [v for v in per_dispatch(fetch_dir, "slot_copy_kernel") if v > 10000]   # the state copies
     cp_w = [v for v in per_dispatch(write_dir, "slot_copy_kernel") if v > 10000]
-    fs, ws = 131072.0 / avg(cp_f), 131072.0 / avg(cp_w)
+    fs, ws = known / avg(cp_f), known / avg(cp_w)
     rec = {"kernel": "decode_kernel<bf16, N=128, W=4>", "workload": "decode step, 256 sequences, Nemotron-H layer shape",
            "source_sha256": decode_source_sha(root), "sources": DECODE_SOURCES,
            "fetch_kib_per_launch": avg(dec_f), "write_kib_per_launch": avg(dec_w), "fetch_scale": fs,
@@ -101,9 +107,8 @@ def main() -> int:
                     help="write profiles/decode_traffic.json from the FETCH_SIZE and WRITE_SIZE counter runs and exit")
     ap.add_argument("--no-prefill-workloads", action="store_true",
                     help="skip the mixed-batch and long-context prefill timings")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="PAIRS",
-                    help="after timing, run 10 slot copies of PAIRS slot pairs (a plain copy kernel of "
-                         "known size, for scaling hardware byte counters)")
+    ap.add_argument("--no-checkpoint-copy", action="store_true",
+                    help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
     if args.write_traffic_record:
         root = os.path.dirname(os.path.abspath(__file__))
@@ -187,16 +192,32 @@ def main() -> int:
         },
     }
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy
+    if not args.no_checkpoint_copy:
+        # checkpoint copy: COPY_PAIRS slot pairs, both state objects, slots [0, 256) -> [256, 512)
+        n = COPY_PAIRS
         src = torch.arange(0, n, device=dev, dtype=torch.int32)
-        dst = torch.arange(w["num_slots"] - n, w["num_slots"], device=dev, dtype=torch.int32)
-        for _ in range(10):
+        dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
+        for _ in range(2):
             pool.checkpoint(0, src, dst)
         torch.cuda.synchronize()
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            pool.checkpoint(0, src, dst)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
         ssm_b, conv_b = pool.info()
-        out["copy_calibration"] = {"pairs": n, "ssm_bytes_per_copy_launch": n * ssm_b,
-                                   "conv_bytes_per_copy_launch": n * conv_b, "launches": 10}
+        moved = 2 * n * (ssm_b + conv_b)
+        gbs = moved / (cms * 1e-3) / 1e9
+        out["checkpoint_copy"] = {
+            "workload": f"{n} slot-to-slot copies of both state objects (bf16, {ssm_b + conv_b} B per slot)",
+            "ms": cms, "copies_per_s": n / (cms * 1e-3), "bytes_per_launch": moved, "gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+        }
+        # the copy is also the measured ceiling a streaming kernel reaches on this part
+        out["roofline"]["copy_ceiling_gbs"] = gbs
+        out["roofline"]["frac_of_copy_ceiling"] = achieved / gbs
 
     if not args.no_prefill:
         pw = synth.prefill_workload(2)

@@ -533,11 +533,8 @@ m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, cons
   const int nl = layer < 0 ? pool->d.num_layers : 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int S = pool->d.num_slots;
-  hipError_t e = m2::launch_slot_copy(pool->d.ssm_base, pool->ssm_slot_bytes, (uint64_t)S * pool->ssm_slot_bytes, l0,
-                                      nl, S, n, src, dst, hs);
-  if (e == hipSuccess)
-    e = m2::launch_slot_copy(pool->d.conv_base, pool->conv_slot_bytes, (uint64_t)S * pool->conv_slot_bytes, l0, nl,
-                             S, n, src, dst, hs);
+  const hipError_t e = m2::launch_slot_copy(pool->d.ssm_base, pool->ssm_slot_bytes, pool->d.conv_base,
+                                            pool->conv_slot_bytes, (uint64_t)S, l0, nl, n, src, dst, hs);
   if (e != hipSuccess) return hip_fail(e, "checkpoint copy launch");
   return ok();
 }

@@ -36,9 +36,11 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, int N, int W, int batch, hipStream_t s);
 bool decode_supported(int ssm_bf16, int N, int W);
 
-// Slot-to-slot copy of one state object: bytes_per_slot bytes at
-// base + layer*layer_stride + slot*bytes_per_slot, for layers [l0, l0+nl).
-hipError_t launch_slot_copy(void* base, uint64_t bytes_per_slot, uint64_t layer_stride, int l0, int nl,
-                            int num_slots, int n, const int32_t* src, const int32_t* dst, hipStream_t s);
+// Slot-to-slot copy of both state objects in one launch: for each object, bytes_per_slot bytes at
+// base + layer*num_slots*bytes_per_slot + slot*bytes_per_slot, for layers [l0, l0+nl).  Byte
+// counts per slot are multiples of 16.
+hipError_t launch_slot_copy(void* ssm_base, uint64_t ssm_bytes_per_slot, void* conv_base,
+                            uint64_t conv_bytes_per_slot, uint64_t num_slots, int l0, int nl, int n,
+                            const int32_t* src, const int32_t* dst, hipStream_t s);
 
 }  // namespace m2
