@@ -9,8 +9,9 @@ synthetic (seeded, resident in HBM before timing).  A second leg times the
 checkpoint copy (256 slot-to-slot copies of both state objects), which is also
 the measured ceiling of a streaming kernel on the part.  A third times the
 chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
-fourth the prefills of the mixed continuous batch (with checkpoints) and one
-layer of the 2 x 131072-token long context with fp32 state.
+fourth the mixed continuous batch (32 prefills with checkpoints and 224
+decodes on one stream) and the 2 x 131072-token long context through all 48
+layer calls with fp32 state.
 
 Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one
 decode launch divided by its average duration, timed with HIP events on the
@@ -27,6 +28,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
@@ -43,56 +45,73 @@ def prefill_dense_flops_per_token(sh, Q) -> int:
     return 2 * Q * sh.d_state * sh.n_groups + 2 * Q * sh.head_dim * sh.nheads + 4 * sh.nheads * sh.head_dim * sh.d_state
 
 
-# sources of the decode kernel and of the copy kernel whose counter readings scale the decode's
+# Sources whose kernels the counter records describe; the copy kernel is in both because its
+# counter readings scale the others'.  A record is reported only while these hash as recorded.
 DECODE_SOURCES = ["recurrent_state_update_amd/csrc/decode.hip", "recurrent_state_update_amd/csrc/device_common.h",
                   "recurrent_state_update_amd/csrc/kernels.h", "recurrent_state_update_amd/csrc/ckpt.hip"]
+PREFILL_SOURCES = ["recurrent_state_update_amd/csrc/prefill.hip", "recurrent_state_update_amd/csrc/prefill.h",
+                   "recurrent_state_update_amd/csrc/device_common.h", "recurrent_state_update_amd/csrc/kernels.h",
+                   "recurrent_state_update_amd/csrc/ckpt.hip"]
+PREFILL_KERNELS = ["conv_kernel", "chunk_state_kernel", "state_pass_kernel", "chunk_out"]
 COPY_PAIRS = 256      # slot pairs per timed checkpoint copy (the decode pool's 512 slots, halves swapped)
 
 
-def decode_source_sha(root: str) -> str:
+def source_sha(root: str, files) -> str:
     import hashlib
-    return hashlib.sha256(b"".join(open(os.path.join(root, p), "rb").read() for p in DECODE_SOURCES)).hexdigest()
+    return hashlib.sha256(b"".join(open(os.path.join(root, p), "rb").read() for p in files)).hexdigest()
 
 
 def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
-    """profiles/decode_traffic.json from the two counter runs of profiles/decode_256seq_hbm_traffic.md:
-    average FETCH_SIZE and WRITE_SIZE (KiB) per decode dispatch, each scaled by what the counter
-    reads for the checkpoint copy of known size (COPY_PAIRS x (2 MiB of state + 60 KiB of conv window)
-    per launch)."""
+    """profiles/decode_traffic.json and profiles/prefill_traffic.json from the two counter runs of
+    profiles/decode_256seq_hbm_traffic.md: average FETCH_SIZE and WRITE_SIZE (KiB) per dispatch of
+    the decode kernel and of each kernel of the 8192-token prefill, each scaled by what the counter
+    reads for the checkpoint copy of known size (COPY_PAIRS x (2 MiB of state + 60 KiB of conv
+    window) per launch)."""
     import csv
     import glob
 
     def per_dispatch(d, part):
-        acc = {}
+        acc, names = {}, set()
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
         for r in csv.DictReader(open(f)):
             if part in r["Kernel_Name"]:
                 acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-        return list(acc.values())
+                names.add(r["Kernel_Name"])
+        return list(acc.values()), sorted(names)
 
     avg = lambda v: sum(v) / len(v)
-    dec_f, dec_w = per_dispatch(fetch_dir, "decode_kernel"), per_dispatch(write_dir, "decode_kernel")
     known = COPY_PAIRS * (2097152 + 61440) / 1024           # KiB of state and conv window per copy launch
-    cp_f = [v for v in per_dispatch(fetch_dir, "slot_copy_kernel") if v > 10000]   # the state copies
-    cp_w = [v for v in per_dispatch(write_dir, "slot_copy_kernel") if v > 10000]
+    cp_f = [v for v in per_dispatch(fetch_dir, "slot_copy_kernel")[0] if v > 10000]   # the timed copies
+    cp_w = [v for v in per_dispatch(write_dir, "slot_copy_kernel")[0] if v > 10000]
     fs, ws = known / avg(cp_f), known / avg(cp_w)
-    rec = {"kernel": "decode_kernel<bf16, N=128, W=4>", "workload": "decode step, 256 sequences, Nemotron-H layer shape",
-           "source_sha256": decode_source_sha(root), "sources": DECODE_SOURCES,
+    dec_f, dec_w = per_dispatch(fetch_dir, "decode_kernel")[0], per_dispatch(write_dir, "decode_kernel")[0]
+    dec = {"kernel": "decode_kernel<bf16, N=128, W=4>", "workload": "decode step, 256 sequences, Nemotron-H layer shape",
+           "source_sha256": source_sha(root, DECODE_SOURCES), "sources": DECODE_SOURCES,
            "fetch_kib_per_launch": avg(dec_f), "write_kib_per_launch": avg(dec_w), "fetch_scale": fs,
            "write_scale": ws, "traffic_bytes_per_launch": (avg(dec_f) * fs + avg(dec_w) * ws) * 1024}
-    json.dump(rec, open(os.path.join(root, "profiles", "decode_traffic.json"), "w"), indent=1)
-    return rec
+    json.dump(dec, open(os.path.join(root, "profiles", "decode_traffic.json"), "w"), indent=1)
+    kernels, total = [], 0.0
+    for k in PREFILL_KERNELS:
+        (f, names), (w, _) = per_dispatch(fetch_dir, k), per_dispatch(write_dir, k)
+        b = (avg(f) * fs + avg(w) * ws) * 1024
+        kernels.append({"kernel": names, "dispatches": len(f), "fetch_kib": avg(f), "write_kib": avg(w),
+                        "read_bytes": avg(f) * fs * 1024, "write_bytes": avg(w) * ws * 1024})
+        total += b
+    pre = {"workload": "chunked prefill of one 8192-token sequence, chunk 256, Nemotron-H layer shape, bf16 state",
+           "source_sha256": source_sha(root, PREFILL_SOURCES), "sources": PREFILL_SOURCES, "fetch_scale": fs,
+           "write_scale": ws, "kernels": kernels, "traffic_bytes_per_call": total}
+    json.dump(pre, open(os.path.join(root, "profiles", "prefill_traffic.json"), "w"), indent=1)
+    return {"decode": dec, "prefill": pre}
 
 
-def measured_traffic(root: str):
-    """HBM bytes per decode launch from the committed counter profile, if the kernel sources still match."""
-    path = os.path.join(root, "profiles", "decode_traffic.json")
+def measured_traffic(root: str, record: str, sources, key: str):
+    """HBM bytes from a committed counter record, if the kernel sources still hash as recorded."""
     try:
-        rec = json.load(open(path))
-        sha = decode_source_sha(root)
+        rec = json.load(open(os.path.join(root, "profiles", record)))
+        sha = source_sha(root, sources)
     except (OSError, ValueError, KeyError):
         return None
-    return rec["traffic_bytes_per_launch"] if sha == rec["source_sha256"] else None
+    return rec[key] if sha == rec.get("source_sha256") else None
 
 
 def main() -> int:
@@ -111,8 +130,7 @@ def main() -> int:
                     help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
     if args.write_traffic_record:
-        root = os.path.dirname(os.path.abspath(__file__))
-        rec = write_traffic_record(root, *args.write_traffic_record)
+        rec = write_traffic_record(ROOT, *args.write_traffic_record)
         print(json.dumps(rec))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -186,7 +204,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+            "traffic": measured_traffic(ROOT, "decode_traffic.json", DECODE_SOURCES, "traffic_bytes_per_launch"),
             "kernel": "decode_kernel<bf16, N=128, W=4>", "bytes_per_launch": launch_bytes,
             "bytes_per_sequence": per_seq,
         },
@@ -258,6 +276,12 @@ def main() -> int:
             "hbm_algorithmic_gbs": io_bytes / (pms * 1e-3) / 1e9,
             "hbm_frac": io_bytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
+        # bytes the kernels move per call, intermediates included, from the committed counter record
+        ptraffic = measured_traffic(ROOT, "prefill_traffic.json", PREFILL_SOURCES, "traffic_bytes_per_call")
+        out["prefill"]["traffic"] = ptraffic
+        if ptraffic is not None:
+            out["prefill"]["traffic_gbs"] = ptraffic / (pms * 1e-3) / 1e9
+            out["prefill"]["traffic_frac"] = ptraffic / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS
         del ppool, ws
         if not args.no_prefill_workloads:
             out["prefill_workloads"] = prefill_workloads(dev, stream, e0, e1)
@@ -270,10 +294,11 @@ def main() -> int:
 
 
 def prefill_workloads(dev, stream, e0, e1) -> dict:
-    """Prefill throughput of the mixed continuous batch (its 32 varlen prefills with checkpoints
-    every 1024 tokens, bf16 state) and of one layer of the long context (2 x 131072 tokens, fp32
-    state).  Layouts come from the workload generators; token values are drawn on the GPU (they do
-    not affect the timing)."""
+    """The mixed continuous batch (32 varlen prefills with checkpoints every 1024 tokens plus 224
+    single-token decodes, bf16 state: both launches on one stream, and each part alone) and the
+    long context (2 x 131072 tokens through 48 independently parameterised layers, fp32 state).
+    Layouts and parameters come from the workload generators; token values and live decode states
+    are drawn on the GPU (they do not affect the timing)."""
     import torch
 
     from recurrent_state_update_amd import synth
@@ -287,8 +312,8 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
         dt = torch.randn(T, sh.nheads, device=dev, generator=gen).bfloat16()
         return u, z, dt, torch.empty(T, sh.intermediate, device=dev, dtype=y_dtype)
 
-    def timed(fn, reps):
-        for _ in range(2):
+    def timed(fn, reps, warm=2):
+        for _ in range(warm):
             fn()
         torch.cuda.synchronize()
         e0.record(stream)
@@ -299,36 +324,61 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
         return e0.elapsed_time(e1) / reps
 
     res = {}
-    _, params, lens, p_slots, _, ck = synth.mixed_layout(3)
+    _, params, lens, p_slots, d_slots, ck = synth.mixed_layout(3)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    T = int(cu[-1])
+    T, nd = int(cu[-1]), len(d_slots)
     pool = Pool.allocate(1, 512, sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
                          torch.bfloat16, torch.bfloat16, dev)
+    pool.ssm.normal_(0.0, 0.1, generator=gen)
+    pool.conv.normal_(0.0, 0.1, generator=gen)
     W = LayerWeights.from_numpy(params, dev)
     u, z, dt, y = tokens(T, torch.bfloat16)
     x, B, C = pool.split_xbc(u)
+    du, dz, ddt, dy = tokens(nd, torch.bfloat16)
+    dx, dB, dC = pool.split_xbc(du)
+    dsl = torch.from_numpy(d_slots).to(dev)
     ws = torch.empty(pool.workspace_size(len(lens), T, 256), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: pool.prefill(0, W, cu, p_slots, np.zeros(len(lens), np.uint8), x, B, C, z, dt, y,
-                                    chunk_size=256, ckpt_interval=1024, ckpt_slots=ck, workspace=ws), 10)
+
+    def pre():
+        pool.prefill(0, W, cu, p_slots, np.zeros(len(lens), np.uint8), x, B, C, z, dt, y, chunk_size=256,
+                     ckpt_interval=1024, ckpt_slots=ck, workspace=ws)
+
+    def dec():
+        pool.decode_step(0, W, dsl, dx, dB, dC, dz, ddt, dy)
+
+    def both():
+        pre()
+        dec()
+
+    ms_p, ms_d, ms = timed(pre, 10), timed(dec, 10), timed(both, 10)
     res["mixed_batch"] = {"workload": f"{len(lens)} varlen prefills of U(128, 4096) tokens ({T} in all), chunk 256, "
-                                      "checkpoints every 1024 tokens, bf16 state",
-                          "ms": ms, "tokens_per_s": T / (ms * 1e-3)}
-    del pool, ws, u, z, dt, y, x, B, C
+                                      f"checkpoints every 1024 tokens, plus {nd} single-token decodes, one stream, "
+                                      "bf16 state",
+                          "ms": ms, "tokens_per_s": (T + nd) / (ms * 1e-3),
+                          "prefill_ms": ms_p, "prefill_tokens_per_s": T / (ms_p * 1e-3),
+                          "decode_ms": ms_d, "decode_tokens_per_s": nd / (ms_d * 1e-3)}
+    del pool, ws, u, z, dt, y, x, B, C, du, dz, ddt, dy, dx, dB, dC
     torch.cuda.empty_cache()
 
     lw = synth.long_workload()
-    T = lw["seqs"] * lw["L"]
-    pool = Pool.allocate(1, lw["seqs"], sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
+    T, nl = lw["seqs"] * lw["L"], lw["num_layers"]
+    pool = Pool.allocate(nl, lw["seqs"], sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
                          torch.float32, torch.bfloat16, dev)
-    W = LayerWeights.from_numpy(synth.long_layer_params(0), dev)
+    Ws = [LayerWeights.from_numpy(synth.long_layer_params(layer), dev) for layer in range(nl)]
     u, z, dt, y = tokens(T, torch.float32)
     x, B, C = pool.split_xbc(u)
     ws = torch.empty(pool.workspace_size(lw["seqs"], T, lw["chunk"]), dtype=torch.uint8, device=dev)
-    ms = timed(lambda: pool.prefill(0, W, lw["cu_seqlens"], lw["slots"], lw["has_init"], x, B, C, z, dt, y,
-                                    chunk_size=lw["chunk"], workspace=ws), 3)
-    res["long_context_fp32"] = {"workload": f"one layer of {lw['seqs']} x {lw['L']} tokens, chunk 256, fp32 state",
-                                "ms_per_layer": ms, "tokens_per_s": T / (ms * 1e-3),
-                                "ms_per_48_layers": 48 * ms}
+
+    def stack():
+        for layer in range(nl):
+            pool.prefill(layer, Ws[layer], lw["cu_seqlens"], lw["slots"], lw["has_init"], x, B, C, z, dt, y,
+                         chunk_size=lw["chunk"], workspace=ws)
+
+    ms = timed(stack, 2, warm=1)
+    res["long_context_fp32"] = {"workload": f"{lw['seqs']} x {lw['L']} tokens through {nl} layer calls, chunk 256, "
+                                            "fp32 state",
+                                "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                                "ms_per_layer": ms / nl, "layer_tokens_per_s": T / (ms / nl * 1e-3)}
     del pool, ws, u, z, dt, y, x, B, C
     torch.cuda.empty_cache()
     return res

@@ -223,6 +223,14 @@ template <int NPL, int ITEMS> struct TilePrefetch {
   }
 };
 
+// Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups round-robin over
+// the 8 XCDs, each with its own L2).  This maps b to a logical index so that every XCD receives
+// one contiguous range of logical indices (a bijection on [0, n)).
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int x = b % 8, full = n / 8, rem = n % 8;
+  return x * full + min(x, rem) + b / 8;
+}
+
 // ------------------------------------------------------------------ 1a. Delta, cumsum
 // Run by the first workgroups of the conv launch (they depend on nothing the conv writes and
 // overlap its memory traffic).  One wave per (chunk, head); lane l owns rows 4l .. 4l+3 of the
@@ -559,12 +567,20 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   __shared__ __align__(16) float sW[HPW * 256];
   u16* const sXT = smem_w + L::XT_OFF;
   u16* const sBT = smem_w + L::BT_OFF;
-  if ((int)blockIdx.x >= a.num_chunks) {   // trailing workgroups: conv windows
-    window_block(a, blockIdx.x - a.num_chunks, blockIdx.y * kStateThreads + threadIdx.x, gridDim.y * kStateThreads);
+  const int H = a.sh.H, G = a.sh.G, Q = a.Q;
+  const int nh = H / HPW;                      // workgroups per chunk
+  const int nmain = a.num_chunks * nh;
+  if ((int)blockIdx.x >= nmain) {   // trailing workgroups: conv windows, nh per window
+    const int w = blockIdx.x - nmain;
+    window_block(a, w / nh, (w % nh) * kStateThreads + threadIdx.x, nh * kStateThreads);
     return;
   }
-  const int c = blockIdx.x, h0 = blockIdx.y * HPW, H = a.sh.H, G = a.sh.G, Q = a.Q;
-  const int g = h0 / (H / G);
+  // The workgroups of one (chunk, group) read the same B blocks: consecutive logical indices,
+  // all on one XCD (one L2), so that the blocks come from memory once.
+  const int hpg = (H / G) / HPW;               // workgroups per (chunk, group)
+  const int lg = xcd_contiguous(blockIdx.x, nmain);
+  const int c = lg / hpg / G, g = lg / hpg % G;
+  const int h0 = (g * hpg + lg % hpg) * HPW;
   const ChunkEntry ch = load_uniform(&a.chunks[c]);
   const int len = ch.len;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1769,10 +1785,10 @@ template <bool SPLIT, int P, int N>
 static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t s) {
   // two heads of a group per workgroup share the staged B blocks (one for hi/lo planes)
   if (!SPLIT && (a.sh.H / a.sh.G) % 2 == 0)
-    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 2>), dim3(a.num_chunks + a.num_windows, a.sh.H / 2),
+    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 2>), dim3((a.num_chunks + a.num_windows) * (a.sh.H / 2)),
                        dim3(kStateThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 1>), dim3(a.num_chunks + a.num_windows, a.sh.H),
+    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 1>), dim3((a.num_chunks + a.num_windows) * a.sh.H),
                        dim3(kStateThreads), 0, s, a);
   const dim3 gp(a.num_seqs, a.sh.H, (P * N / 8 + 255) / 256);
   // hi/lo planes go with fp32 state: fp32 chunk states; bf16 state: bf16 chunk states
