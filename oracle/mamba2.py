@@ -46,9 +46,15 @@ Readings where the pages are silent (each also listed in the design notes):
    p % interval == 0) stores round(state after p tokens) and the window of the
    raw inputs at positions p-W+1 .. p-1.
 
+Checkpoints may also be held in an int8 store apart from the pool ([SSM-hybrids],
+SGLang int8 checkpoint passage): see int8_quantize below for the arithmetic.
+
 Parity pins live in the test suite (matrix form of [notes] "Mamba and
 Attention", constant-input closed form, scipy lfilter scalar case,
-np.convolve conv, torch bf16 casts, byte counts printed on the pages).
+np.convolve conv, torch bf16 casts, byte counts printed on the pages; for the
+int8 store: states built from known codes and power-of-two scales, halves
+rounding to even, the half-step error bound, the page's ~2x capacity, and the
+restored error evolving through the decay product).
 """
 from __future__ import annotations
 
@@ -303,3 +309,69 @@ def checkpoint_states(pool: PoolRef, layer: int, src, dst):
         for a, b in zip(src, dst):
             pool.ssm[l, b] = pool.ssm[l, a]
             pool.conv[l, b] = pool.conv[l, a]
+
+
+# --------------------------------------------------------------------------
+# int8 checkpoint store
+# --------------------------------------------------------------------------
+# [SSM-hybrids], the SGLang passage on compressed checkpoints: cached states are
+# kept apart from the active pool, the temporal state in int8 with symmetric
+# scales per (head, k-channel), quantized once when stored and dequantized once
+# into a fresh active slot on a prefix hit; the conv window stays in its own
+# dtype.  Reading taken for the k-channel: the d_state index n (B is the key
+# the state is written with, h += Delta x B^T), so one scale covers the head_dim
+# entries h[h, :, n].  The pages fix neither the rounding nor the arithmetic;
+# both here are fp32, the precision of the kernels, so that the integer codes
+# are decided the same way on both sides:
+#     amax = max_p |h[h, p, n]|      scale = fp32(amax / 127)
+#     inv  = fp32(127 / amax)        code  = clamp(rint(fp32(h * inv)), -127, 127)
+#     restored = round_to(fp32(code * scale), ssm dtype)
+# A column of zeros gets scale 0 and codes 0.
+
+def int8_quantize(state) -> tuple[np.ndarray, np.ndarray]:
+    """Codes (int8, same shape) and scales (fp32, the head_dim axis -2 reduced) of a temporal
+    state [..., H, P, N] holding values of its fp32 or bf16 storage dtype."""
+    s32 = np.asarray(state, np.float64).astype(np.float32)
+    amax = np.max(np.abs(s32), axis=-2)
+    with np.errstate(divide="ignore"):
+        scale = (amax / np.float32(127.0)).astype(np.float32)
+        inv = np.where(amax > 0, np.float32(127.0) / amax, np.float32(0.0)).astype(np.float32)
+    prod = (s32 * inv[..., None, :]).astype(np.float32)
+    codes = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def int8_dequantize(codes, scale, dtype: str) -> np.ndarray:
+    """code * scale in fp32, rounded to the pool's ssm dtype, as float64."""
+    prod = (np.asarray(codes).astype(np.float32) * np.asarray(scale, np.float32)[..., None, :]).astype(np.float32)
+    return round_to(prod.astype(np.float64), dtype)
+
+
+class Int8StoreRef:
+    """Oracle copy of an int8 checkpoint store of `num_entries` entries for a pool's layers:
+    codes [E, L, H, P, N] int8, scales [E, L, H, N] fp32, conv [E, L, Cd, W-1] (float64 values
+    of the pool's conv dtype)."""
+
+    def __init__(self, pool: PoolRef, num_entries: int):
+        L, _, H, P, N = pool.ssm.shape
+        self.codes = np.zeros((num_entries, L, H, P, N), np.int8)
+        self.scales = np.zeros((num_entries, L, H, N), np.float32)
+        self.conv = np.zeros((num_entries, L) + pool.conv.shape[2:])
+
+
+def int8_store_put(pool: PoolRef, store: Int8StoreRef, layer: int, slots, entries):
+    """Quantize slot slots[i] into entry entries[i] (layer < 0: every layer)."""
+    layers = range(pool.ssm.shape[0]) if layer < 0 else [layer]
+    for l in layers:
+        for s, e in zip(slots, entries):
+            store.codes[e, l], store.scales[e, l] = int8_quantize(pool.ssm[l, s])
+            store.conv[e, l] = pool.conv[l, s]
+
+
+def int8_store_get(store: Int8StoreRef, pool: PoolRef, layer: int, entries, slots):
+    """Dequantize entry entries[i] into slot slots[i] (layer < 0: every layer)."""
+    layers = range(pool.ssm.shape[0]) if layer < 0 else [layer]
+    for l in layers:
+        for e, s in zip(entries, slots):
+            pool.ssm[l, s] = int8_dequantize(store.codes[e, l], store.scales[e, l], pool.ssm_dtype)
+            pool.conv[l, s] = store.conv[e, l]

@@ -391,3 +391,88 @@ def test_pins_catch_planted_mistakes():
               "input_index_shift"):
         assert rel_err(scan(v), ref) > 1e-3, v
     assert rel_err(orc.ssm_scan(h0, x, B, C, delta, A, D)[0], ref) < 1e-12
+
+
+# ---------------------------------------------------------------- int8 checkpoint store
+def test_int8_codes_of_exact_multiples_and_reduction_axis():
+    """States built as code * 2^-k with a different k per (head, d_state index) and a +-127 in
+    every such column: quantizing returns those codes and scales 2^-k exactly (so one scale per
+    (head, n), taken over head_dim), and dequantizing returns the state exactly."""
+    rng = np.random.default_rng(41)
+    H, P, N = 3, 8, 5
+    codes = rng.integers(-127, 128, (H, P, N))
+    rows = rng.integers(0, P, (H, N))
+    sign = rng.choice([-1, 1], (H, N))
+    for h in range(H):
+        for n in range(N):
+            codes[h, rows[h, n], n] = 127 * sign[h, n]
+    k = rng.integers(3, 12, (H, N))
+    state = codes * np.exp2(-k.astype(np.float64))[:, None, :]
+    q, s = orc.int8_quantize(state)
+    assert q.dtype == np.int8 and s.shape == (H, N)
+    assert np.array_equal(q.astype(np.int64), codes)
+    assert np.array_equal(s.astype(np.float64), np.exp2(-k.astype(np.float64)))
+    assert np.array_equal(orc.int8_dequantize(q, s, "f32"), state)
+    assert np.array_equal(orc.int8_quantize(-state)[0].astype(np.int64), -codes)
+
+
+def test_int8_codes_round_half_to_even():
+    """amax = 127/128 makes the multiplier exactly 128: halves land on the even code."""
+    vals = np.array([127.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, 126.5]) / 128.0
+    q, s = orc.int8_quantize(vals.reshape(1, -1, 1))
+    assert q[0, :, 0].tolist() == [127, 2, 4, -2, 0, 2, 0, 126]
+    assert s[0, 0] == np.float32(1.0 / 128.0)
+
+
+def test_int8_zero_column_and_error_bound():
+    rng = np.random.default_rng(42)
+    state = orc.round_to(rng.normal(0, 0.1, (4, 16, 32)), "bf16")
+    state[1, :, 7] = 0.0
+    q, s = orc.int8_quantize(state)
+    assert s[1, 7] == 0 and not q[1, :, 7].any()
+    restored = orc.int8_dequantize(q, s, "f32")
+    amax = np.max(np.abs(state), axis=1)                    # per (head, n), in fp64
+    # half a quantization step, plus the fp32 roundings of the multiplier and of the product
+    bound = amax / 254.0 * (1 + 2.0 ** -20) + np.abs(state).max() * 2.0 ** -22
+    assert np.all(np.abs(restored - state) <= bound[:, None, :])
+    assert np.all(np.max(np.abs(q.astype(np.int64)), axis=1)[amax > 0] == 127)
+
+
+def test_int8_store_holds_about_twice_the_cached_states_of_bf16():
+    """[SSM-hybrids], SGLang int8 checkpoint passage: about twice as many cached states as bf16.
+    At the Nemotron-H layer shape the int8 codes are half the bf16 state; with the per-(head, n)
+    scales and the bf16 conv window kept native, an entry is 1.84x smaller than a bf16 slot."""
+    sh = synth.NEMOTRON_H
+    pool = orc.PoolRef(sh, 1, 1, "bf16", "bf16")
+    st = orc.Int8StoreRef(pool, 1)
+    entry = st.codes.nbytes + st.scales.nbytes + st.conv.size * 2
+    slot = pool.ssm_bytes_per_slot_layer() + pool.conv_bytes_per_slot_layer()
+    assert 2 * st.codes.nbytes == pool.ssm_bytes_per_slot_layer()
+    assert 1.8 < slot / entry < 2.0
+
+
+def test_int8_restored_error_evolves_through_the_decay_product():
+    """[SSM-hybrids], the affine-composition passage: an error in a restored state evolves through
+    the product of the later transition factors.  Restoring an int8 entry and continuing with the
+    same inputs leaves the state off by (prod_t alpha_t) times the quantization error."""
+    shape = synth.Shape(4, 8, 16, 2, 4)
+    rng = np.random.default_rng(43)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 40)
+    ssm0 = orc.round_to(ssm0, "bf16")
+    pool = orc.PoolRef(shape, 1, 3, "bf16", "bf16")
+    pool.ssm[0, 0], pool.conv[0, 0] = ssm0, orc.round_to(conv0, "bf16")
+    store = orc.Int8StoreRef(pool, 2)
+    orc.int8_store_put(pool, store, 0, [0], [1])
+    orc.int8_store_get(store, pool, 0, [1], [2])
+    assert np.array_equal(pool.conv[0, 2], pool.conv[0, 0])
+    err0 = pool.ssm[0, 2] - pool.ssm[0, 0]
+    assert 0 < np.abs(err0).max() <= np.abs(ssm0).max() / 127
+    finals = []
+    for slot in (0, 2):
+        run = orc.PoolRef(shape, 1, 1, "f64", "f64")
+        run.ssm[0, 0], run.conv[0, 0] = pool.ssm[0, slot], pool.conv[0, slot]
+        orc.prefill(run, 0, params, [0, 40], [0], [1], [0], u, z, dt, "f64")
+        finals.append(run.ssm[0, 0].copy())
+    delta = np.logaddexp(0.0, dt + params["dt_bias"])
+    decay = np.exp((delta * params["A"]).sum(axis=0))
+    assert rel_err(finals[1] - finals[0], decay[:, None, None] * err0) < 1e-9
