@@ -197,6 +197,55 @@ m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, cons
                                    const int32_t* dst, const int32_t* src_host,
                                    const int32_t* dst_host, void* stream);
 
+/* int8 checkpoint store: cached states held apart from the active pool, the
+ * temporal state compressed to int8 when stored and expanded once into a fresh
+ * pool slot on a prefix hit, the conv window kept in its own dtype
+ * ([SSM-hybrids], the SGLang passage on int8 checkpoints: symmetric codes per
+ * (head, k-channel), quantized once, about twice the cached states of bf16).
+ * The k-channel is read as the d_state index n (B is the key the state is
+ * written with), so one fp32 scale covers h[head][0..P-1][n].  Arithmetic is
+ * fp32: amax = max_p |h[p][n]|; scale = amax / 127; code = rint(h * (127 / amax))
+ * clamped to [-127, 127] (both quotients correctly rounded; a zero column gives
+ * scale 0 and codes 0); restore: code * scale rounded (RNE) to the pool's ssm dtype.
+ * A store of num_entries entries for a pool of L layers is three caller-owned,
+ * dense, 16-byte aligned device arrays:
+ *   codes  int8        [num_entries][L][nheads][head_dim][d_state]
+ *   scales fp32        [num_entries][L][nheads][d_state]
+ *   conv   conv_dtype  [num_entries][L][d_conv][conv_kernel-1]
+ * The *_bytes fields must equal those dense sizes (mamba2_int8_store_size). */
+typedef struct m2_int8_store {
+  int32_t num_entries;
+  int32_t reserved;
+  void* codes;
+  void* scales;
+  void* conv;
+  uint64_t codes_bytes;
+  uint64_t scales_bytes;
+  uint64_t conv_bytes;
+} m2_int8_store;
+
+/* Dense byte sizes of a store of num_entries entries for this pool.  Host-only. */
+m2_status mamba2_int8_store_size(const m2_pool* pool, int32_t num_entries, uint64_t* codes_bytes,
+                                 uint64_t* scales_bytes, uint64_t* conv_bytes);
+
+/* Quantize slot slots[i] of the pool into store entry entries[i] (both state
+ * objects), for one layer or, with layer = -1, every layer.
+ *   slots, entries  device int32[n]; a pair with an index out of range is skipped.
+ *   slots_host, entries_host optional host copies; when given, the call checks
+ *              ranges and that entries are distinct, and returns M2_ERR_SLOT otherwise.
+ * Errors: M2_ERR_ARG, M2_ERR_SHAPE (store sizes), M2_ERR_ALIGN, M2_ERR_UNSUPPORTED
+ * (n > 65535, or d_state / 8 > 256), M2_ERR_SLOT, M2_ERR_HIP. */
+m2_status mamba2_int8_store_put(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n,
+                                const int32_t* slots, const int32_t* entries, const int32_t* slots_host,
+                                const int32_t* entries_host, void* stream);
+
+/* Restore store entry entries[i] into slot slots[i] of the pool (both state
+ * objects), for one layer or every layer (layer = -1).  Same argument rules as
+ * mamba2_int8_store_put, with the slots required distinct when host copies are given. */
+m2_status mamba2_int8_store_get(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n,
+                                const int32_t* entries, const int32_t* slots, const int32_t* entries_host,
+                                const int32_t* slots_host, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* mamba2_last_error(void);
 

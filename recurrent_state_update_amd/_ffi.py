@@ -25,6 +25,12 @@ class LayerParams(ctypes.Structure):
                 ("conv_b", c_void_p)]
 
 
+class Int8StoreDesc(ctypes.Structure):
+    _fields_ = [("num_entries", c_int32), ("reserved", c_int32), ("codes", c_void_p), ("scales", c_void_p),
+                ("conv", c_void_p), ("codes_bytes", c_uint64), ("scales_bytes", c_uint64),
+                ("conv_bytes", c_uint64)]
+
+
 class Mamba2Error(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
@@ -51,6 +57,12 @@ _SIGS = {
                                          c_uint64, c_void_p]),
     "mamba2_checkpoint_states": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p]),
+    "mamba2_int8_store_size": (c_int32, [c_void_p, c_int32, POINTER(c_uint64), POINTER(c_uint64),
+                                         POINTER(c_uint64)]),
+    "mamba2_int8_store_put": (c_int32, [c_void_p, POINTER(Int8StoreDesc), c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p]),
+    "mamba2_int8_store_get": (c_int32, [c_void_p, POINTER(Int8StoreDesc), c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -11,6 +11,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "int8_store.h"
 #include "kernels.h"
 #include "prefill.h"
 #include "mamba2_pool.h"
@@ -149,11 +150,78 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   return true;
 }
 
+// Dense sizes of an int8 store of num_entries entries for this pool.
+bool int8_store_sizes(const m2_pool* pool, int64_t num_entries, uint64_t* codes, uint64_t* scales, uint64_t* conv) {
+  const m2::LayerShape& sh = pool->sh;
+  uint64_t el;
+  if (!mul_ok((uint64_t)num_entries, (uint64_t)pool->d.num_layers, &el)) return false;
+  return mul_ok(el, (uint64_t)sh.H * sh.P * sh.N, codes) && mul_ok(el, (uint64_t)sh.H * sh.N * 4, scales) &&
+         mul_ok(el, pool->conv_slot_bytes, conv);
+}
+
+// Shared checks and launch of the int8 store's two directions.
+m2_status int8_store_call(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n, const int32_t* slots,
+                          const int32_t* entries, const int32_t* slots_host, const int32_t* entries_host, bool put,
+                          void* stream) {
+  if (!pool || !store) return fail(M2_ERR_ARG, "pool and store must not be NULL");
+  if (layer < -1 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (n < 0) return fail(M2_ERR_ARG, "n is negative");
+  if (store->num_entries < 0) return fail(M2_ERR_ARG, "num_entries is negative");
+  uint64_t cb, sb, vb;
+  if (!int8_store_sizes(pool, store->num_entries, &cb, &sb, &vb)) return fail(M2_ERR_SHAPE, "store size overflows");
+  if (store->codes_bytes != cb || store->scales_bytes != sb || store->conv_bytes != vb)
+    return fail(M2_ERR_SHAPE, "store sizes (%llu, %llu, %llu) differ from the dense sizes (%llu, %llu, %llu)",
+                (unsigned long long)store->codes_bytes, (unsigned long long)store->scales_bytes,
+                (unsigned long long)store->conv_bytes, (unsigned long long)cb, (unsigned long long)sb,
+                (unsigned long long)vb);
+  if (n == 0) return ok();
+  if (!slots || !entries) return fail(M2_ERR_ARG, "slots and entries must not be NULL");
+  if (!store->codes || !store->scales || !store->conv) return fail(M2_ERR_ARG, "a store array is NULL");
+  if (!aligned16(store->codes) || !aligned16(store->scales) || !aligned16(store->conv))
+    return fail(M2_ERR_ALIGN, "store arrays must be 16-byte aligned");
+  if (n > 65535) return fail(M2_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  if (pool->sh.N / 8 > 256) return fail(M2_ERR_UNSUPPORTED, "d_state above 2048 is not supported by the int8 store");
+  if (slots_host && entries_host) {
+    const int S = pool->d.num_slots, E = store->num_entries;
+    std::vector<uint8_t> seen(put ? E : S, 0);
+    for (int i = 0; i < n; ++i) {
+      const int sl = slots_host[i], en = entries_host[i];
+      if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "pair %d: slot %d out of range", i, sl);
+      if (en < 0 || en >= E) return fail(M2_ERR_SLOT, "pair %d: entry %d out of range", i, en);
+      const int d = put ? en : sl;
+      if (seen[d]) return fail(M2_ERR_SLOT, "destination %s %d appears twice", put ? "entry" : "slot", d);
+      seen[d] = 1;
+    }
+  }
+  m2::Int8StoreArgs a;
+  a.ssm = static_cast<char*>(pool->d.ssm_base);
+  a.conv = static_cast<char*>(pool->d.conv_base);
+  a.codes = static_cast<int8_t*>(store->codes);
+  a.scales = static_cast<float*>(store->scales);
+  a.store_conv = static_cast<char*>(store->conv);
+  a.conv_bytes = pool->conv_slot_bytes;
+  a.H = pool->sh.H;
+  a.P = pool->sh.P;
+  a.N = pool->sh.N;
+  a.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  a.num_layers = pool->d.num_layers;
+  a.num_slots = pool->d.num_slots;
+  a.num_entries = store->num_entries;
+  a.l0 = layer < 0 ? 0 : layer;
+  a.slots = slots;
+  a.entries = entries;
+  const int nl = layer < 0 ? pool->d.num_layers : 1;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = put ? m2::launch_int8_put(a, n, nl, hs) : m2::launch_int8_get(a, n, nl, hs);
+  if (e != hipSuccess) return hip_fail(e, put ? "int8 store put launch" : "int8 store get launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t mamba2_abi_version(void) { return 1; }
+int32_t mamba2_abi_version(void) { return 2; }
 
 const char* mamba2_last_error(void) { return g_err.c_str(); }
 
@@ -537,6 +605,27 @@ m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, cons
                                             pool->conv_slot_bytes, (uint64_t)S, l0, nl, n, src, dst, hs);
   if (e != hipSuccess) return hip_fail(e, "checkpoint copy launch");
   return ok();
+}
+
+m2_status mamba2_int8_store_size(const m2_pool* pool, int32_t num_entries, uint64_t* codes_bytes,
+                                 uint64_t* scales_bytes, uint64_t* conv_bytes) {
+  if (!pool || !codes_bytes || !scales_bytes || !conv_bytes) return fail(M2_ERR_ARG, "NULL argument");
+  if (num_entries < 0) return fail(M2_ERR_ARG, "num_entries is negative");
+  if (!int8_store_sizes(pool, num_entries, codes_bytes, scales_bytes, conv_bytes))
+    return fail(M2_ERR_SHAPE, "store size overflows");
+  return ok();
+}
+
+m2_status mamba2_int8_store_put(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n,
+                                const int32_t* slots, const int32_t* entries, const int32_t* slots_host,
+                                const int32_t* entries_host, void* stream) {
+  return int8_store_call(pool, store, layer, n, slots, entries, slots_host, entries_host, true, stream);
+}
+
+m2_status mamba2_int8_store_get(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n,
+                                const int32_t* entries, const int32_t* slots, const int32_t* entries_host,
+                                const int32_t* slots_host, void* stream) {
+  return int8_store_call(pool, store, layer, n, slots, entries, slots_host, entries_host, false, stream);
 }
 
 }  // extern "C"

@@ -12,7 +12,7 @@ from ctypes import byref, c_uint64, c_void_p
 import numpy as np
 import torch
 
-from ._ffi import M2_BF16, M2_F32, LayerParams, Mamba2Error, PoolDesc, check, lib
+from ._ffi import M2_BF16, M2_F32, Int8StoreDesc, LayerParams, Mamba2Error, PoolDesc, check, lib
 
 _DT = {torch.float32: M2_F32, torch.bfloat16: M2_BF16}
 
@@ -168,6 +168,28 @@ class Pool:
         return y
 
     # ------------------------------------------------------------------ checkpoints
+    def int8_store(self, num_entries: int) -> "Int8Store":
+        """A zeroed int8 checkpoint store of num_entries entries for this pool's layers."""
+        return Int8Store(self, num_entries)
+
+    def int8_put(self, store: "Int8Store", layer: int, slots: torch.Tensor, entries: torch.Tensor,
+                 slots_host=None, entries_host=None):
+        """Quantize slot slots[i] into store entry entries[i] (device int32); layer -1 = all layers."""
+        _, s_p = _host_i32(slots_host)
+        _, e_p = _host_i32(entries_host)
+        check(lib().mamba2_int8_store_put(self._h, byref(store.desc), layer, slots.numel(),
+                                          c_void_p(slots.data_ptr()), c_void_p(entries.data_ptr()), s_p, e_p,
+                                          _stream()))
+
+    def int8_get(self, store: "Int8Store", layer: int, entries: torch.Tensor, slots: torch.Tensor,
+                 entries_host=None, slots_host=None):
+        """Restore store entry entries[i] into slot slots[i] (device int32); layer -1 = all layers."""
+        _, e_p = _host_i32(entries_host)
+        _, s_p = _host_i32(slots_host)
+        check(lib().mamba2_int8_store_get(self._h, byref(store.desc), layer, entries.numel(),
+                                          c_void_p(entries.data_ptr()), c_void_p(slots.data_ptr()), e_p, s_p,
+                                          _stream()))
+
     def checkpoint(self, layer: int, src: torch.Tensor, dst: torch.Tensor, src_host=None, dst_host=None):
         """Copy both state objects slot src[i] -> dst[i] (device int32); layer -1 = all layers."""
         _, s_p = _host_i32(src_host)
@@ -176,4 +198,23 @@ class Pool:
                                              c_void_p(dst.data_ptr()), s_p, d_p, _stream()))
 
 
-__all__ = ["Pool", "LayerWeights", "Mamba2Error"]
+class Int8Store:
+    """int8 checkpoint store for a pool: codes int8 [E, L, H, P, N], scales fp32 [E, L, H, N],
+    conv windows [E, L, Cd, W-1] in the pool's conv dtype, allocated on the pool's device."""
+
+    def __init__(self, pool: Pool, num_entries: int):
+        cb, sb, vb = c_uint64(), c_uint64(), c_uint64()
+        check(lib().mamba2_int8_store_size(pool._h, num_entries, byref(cb), byref(sb), byref(vb)))
+        L, H, P, N = pool.num_layers, pool.nheads, pool.head_dim, pool.d_state
+        dev = pool.ssm.device
+        self.codes = torch.zeros((num_entries, L, H, P, N), dtype=torch.int8, device=dev)
+        self.scales = torch.zeros((num_entries, L, H, N), dtype=torch.float32, device=dev)
+        self.conv = torch.zeros((num_entries, L) + tuple(pool.conv.shape[2:]), dtype=pool.conv.dtype, device=dev)
+        for t, b in ((self.codes, cb), (self.scales, sb), (self.conv, vb)):
+            assert t.numel() * t.element_size() == b.value
+        self.num_entries = num_entries
+        self.desc = Int8StoreDesc(num_entries, 0, self.codes.data_ptr(), self.scales.data_ptr(),
+                                  self.conv.data_ptr(), cb.value, sb.value, vb.value)
+
+
+__all__ = ["Pool", "LayerWeights", "Int8Store", "Mamba2Error"]

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from recurrent_state_update_amd import _ffi
-from recurrent_state_update_amd._ffi import LayerParams, PoolDesc, lib
+from recurrent_state_update_amd._ffi import Int8StoreDesc, LayerParams, PoolDesc, lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba2_pool.h")
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
     exported = set(re.findall(r"\bT (mamba2_\w+)", out))
     assert set(names) <= exported
     assert set(_ffi.exported_symbols()) == set(names)
-    assert l.mamba2_abi_version() == 1
+    assert l.mamba2_abi_version() == 2
 
 
 def make_desc(H=128, P=64, N=128, G=8, W=4, L=1, S=4, ssm=1, conv=1, ssm_base=FAKE, conv_base=FAKE):
@@ -245,6 +245,50 @@ def test_checkpoint_validation(pool):
     assert ckpt(pool, [-1], [1]) == SLOT
     assert lib().mamba2_checkpoint_states(pool, 0, -1, FAKE, FAKE, None, None, None) == ARG
     assert lib().mamba2_checkpoint_states(pool, 0, 1, None, FAKE, None, None, None) == ARG
+
+
+def store_desc(pool, E=3, **over):
+    cb, sb, vb = c_uint64(), c_uint64(), c_uint64()
+    assert lib().mamba2_int8_store_size(pool, E, byref(cb), byref(sb), byref(vb)) == 0
+    d = dict(num_entries=E, reserved=0, codes=FAKE, scales=FAKE, conv=FAKE, codes_bytes=cb.value,
+             scales_bytes=sb.value, conv_bytes=vb.value)
+    d.update(over)
+    return Int8StoreDesc(**d)
+
+
+def test_int8_store_sizes_at_the_layer_shape(pool):
+    """Dense sizes: codes 1 byte per state element, one fp32 scale per (head, d_state index), the
+    conv window at the pool's conv dtype; an entry is about half a bf16 slot."""
+    cb, sb, vb = c_uint64(), c_uint64(), c_uint64()
+    assert lib().mamba2_int8_store_size(pool, 5, byref(cb), byref(sb), byref(vb)) == 0
+    H, P, N, Cd, W = 128, 64, 128, 10240, 4
+    assert (cb.value, sb.value, vb.value) == (5 * H * P * N, 5 * H * N * 4, 5 * Cd * (W - 1) * 2)
+    ssm, conv = c_uint64(), c_uint64()
+    assert lib().mamba2_pool_info(pool, byref(ssm), byref(conv)) == 0
+    assert 1.8 < 5 * (ssm.value + conv.value) / (cb.value + sb.value + vb.value) < 2.0
+    assert lib().mamba2_int8_store_size(pool, -1, byref(cb), byref(sb), byref(vb)) == ARG
+
+
+def test_int8_store_validation(pool):
+    put, get = lib().mamba2_int8_store_put, lib().mamba2_int8_store_get
+    i32 = lambda v: (ctypes.c_int32 * len(v))(*v)
+    d = store_desc(pool)
+    assert put(pool, byref(d), 0, 0, FAKE, FAKE, None, None, None) == 0      # nothing to do
+    assert put(pool, None, 0, 1, FAKE, FAKE, None, None, None) == ARG
+    assert put(pool, byref(d), 1, 1, FAKE, FAKE, None, None, None) == ARG   # pool has one layer
+    assert put(pool, byref(d), 0, -1, FAKE, FAKE, None, None, None) == ARG
+    assert put(pool, byref(d), 0, 1, None, FAKE, None, None, None) == ARG
+    bad = store_desc(pool, codes_bytes=d.codes_bytes - 16)
+    assert put(pool, byref(bad), 0, 1, FAKE, FAKE, None, None, None) == SHAPE
+    bad = store_desc(pool, scales=FAKE + 8)
+    assert get(pool, byref(bad), 0, 1, FAKE, FAKE, None, None, None) == ALIGN
+    assert put(pool, byref(d), 0, 70000, FAKE, FAKE, None, None, None) == UNSUP
+    # host copies: ranges, and distinct destinations (entries for put, slots for get)
+    assert put(pool, byref(d), 0, 1, FAKE, FAKE, i32([4]), i32([0]), None) == SLOT    # 4 slots
+    assert put(pool, byref(d), 0, 1, FAKE, FAKE, i32([0]), i32([3]), None) == SLOT    # 3 entries
+    assert put(pool, byref(d), 0, 2, FAKE, FAKE, i32([0, 1]), i32([2, 2]), None) == SLOT
+    assert get(pool, byref(d), 0, 2, FAKE, FAKE, i32([0, 1]), i32([3, 3]), None) == SLOT
+    assert get(pool, byref(d), 0, 1, FAKE, FAKE, i32([-1]), i32([0]), None) == SLOT
 
 
 def test_last_error_is_cleared_by_success(pool):
