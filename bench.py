@@ -7,7 +7,8 @@ permuted slots of a 512-slot bf16 pool: conv-window shift, conv + SiLU,
 softplus, state update, readout, gate, in place on the pool.  Inputs are
 synthetic (seeded, resident in HBM before timing).  A second leg times the
 checkpoint copy (256 slot-to-slot copies of both state objects), which is also
-the measured ceiling of a streaming kernel on the part.  A third times the
+the measured ceiling of a streaming kernel on the part, and the int8 checkpoint
+store (256 slots quantized into entries and restored).  A third times the
 chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
 fourth the mixed continuous batch (32 prefills with checkpoints and 224
 decodes on one stream) and the 2 x 131072-token long context through all 48
@@ -126,6 +127,7 @@ def main() -> int:
                     help="write profiles/decode_traffic.json from the FETCH_SIZE and WRITE_SIZE counter runs and exit")
     ap.add_argument("--no-prefill-workloads", action="store_true",
                     help="skip the mixed-batch and long-context prefill timings")
+    ap.add_argument("--no-int8-store", action="store_true", help="skip the int8 checkpoint-store timing")
     ap.add_argument("--no-checkpoint-copy", action="store_true",
                     help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
@@ -236,6 +238,39 @@ def main() -> int:
         # the copy is also the measured ceiling a streaming kernel reaches on this part
         out["roofline"]["copy_ceiling_gbs"] = gbs
         out["roofline"]["frac_of_copy_ceiling"] = achieved / gbs
+
+    if not args.no_int8_store:
+        # int8 checkpoint store: 256 slots quantized into 256 entries, and restored into the other half
+        n = COPY_PAIRS
+        store = pool.int8_store(n)
+        sl = torch.arange(0, n, device=dev, dtype=torch.int32)
+        ent = torch.arange(0, n, device=dev, dtype=torch.int32)
+        dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
+        ssm_b, conv_b = pool.info()
+        codes_b = ssm_b // 2
+        scales_b = sh.nheads * sh.d_state * 4
+        put_bytes = n * (ssm_b + codes_b + scales_b + 2 * conv_b)       # read state + window, write entry
+        get_bytes = n * (codes_b + scales_b + ssm_b + 2 * conv_b)       # read entry, write state + window
+        res = {}
+        for name, fn, nbytes in (("put", lambda: pool.int8_put(store, 0, sl, ent), put_bytes),
+                                 ("get", lambda: pool.int8_get(store, 0, ent, dst), get_bytes)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 10
+            res[name] = {"ms": t, "states_per_s": n / (t * 1e-3), "bytes_per_launch": nbytes,
+                         "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        res["workload"] = (f"{n} bf16 slots quantized into int8 store entries (put) and restored into fresh "
+                           "slots (get), Nemotron-H layer shape")
+        res["entry_bytes"] = codes_b + scales_b + conv_b
+        res["slot_bytes"] = ssm_b + conv_b
+        out["int8_checkpoint_store"] = res
+        del store
 
     if not args.no_prefill:
         pw = synth.prefill_workload(2)

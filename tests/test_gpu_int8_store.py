@@ -33,9 +33,13 @@ def _i32(v):
     return torch.tensor(v, dtype=torch.int32, device="cuda")
 
 
-@pytest.mark.parametrize("ssm_dtype,layer", [("bf16", -1), ("f32", 1), ("bf16", 0)])
-def test_put_and_get_match_the_oracle_bit_for_bit(ssm_dtype, layer):
-    sh = synth.Shape(4, 32, 64, 2, 4)
+@pytest.mark.parametrize("ssm_dtype,layer,sh", [
+    ("bf16", -1, synth.Shape(4, 32, 64, 2, 4)), ("f32", 1, synth.Shape(4, 32, 64, 2, 4)),
+    ("bf16", 0, synth.Shape(4, 32, 64, 2, 4)),
+    ("f32", -1, synth.Shape(2, 128, 256, 1, 3)),    # 128 rows of 256: more rows than a thread holds
+    ("bf16", 0, synth.Shape(3, 24, 40, 3, 2)),      # d_state 40: 5 column groups, ragged row groups
+], ids=["bf16-all", "f32-layer1", "bf16-layer0", "f32-tall", "bf16-ragged"])
+def test_put_and_get_match_the_oracle_bit_for_bit(ssm_dtype, layer, sh):
     L, S, E = 2, 12, 5
     log(f"case: int8 store {ssm_dtype} layer={layer}")
     rng = np.random.default_rng(60)
