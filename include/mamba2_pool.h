@@ -132,8 +132,11 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              void* y, int64_t y_stride, int32_t y_dtype, void* stream);
 
 /* Bytes of device workspace mamba2_prefill_chunked needs for num_seqs packed
- * sequences totalling total_tokens tokens, at chunk_size, with up to max_ckpt
- * checkpoints per sequence.  Host-only. */
+ * sequences totalling total_tokens tokens at chunk_size, when at most max_ckpt
+ * checkpoints of any one sequence fall inside a chunk (a position that is
+ * neither a multiple of chunk_size rows after the sequence's first row in the
+ * call nor its last row; each such checkpoint adds one chunk).  Pass 0 when
+ * every checkpoint lies on that grid.  Host-only. */
 m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
                                         int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
 
@@ -159,8 +162,10 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  *              start_pos < p <= start_pos + L_s ([SSM-hybrids] "align" mode:
  *              states kept at block-aligned positions); -1 skips it.
  *              Checkpoint slots must be distinct and disjoint from `slots`.
- *              Requires ckpt_interval % chunk_size == 0 and start_pos % chunk_size == 0,
- *              so checkpoints fall on chunk ends.
+ *              Positions need not lie on the chunk grid: a chunk that contains a
+ *              checkpoint position ends there and the next chunk starts after it
+ *              (the pages' "all" mode, one checkpoint every ckpt_interval tokens,
+ *              is max_ckpt columns with every slot given).
  * Device tensors: x, B, C, z, dt, y as in mamba2_decode_step with rows = packed tokens
  * (x, B, C 16-byte aligned with 16-byte multiple row strides).
  * chunk_size: multiple of 16, at most 256.  Chunks start at each sequence's

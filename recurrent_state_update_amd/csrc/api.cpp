@@ -2,6 +2,7 @@
 // prefill chunk tables, and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -116,9 +117,12 @@ struct PrefillLayout {
   uint64_t off_delta, off_dA, off_cstate, off_hin, plane_hin, total;
 };
 
-bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, PrefillLayout* L) {
-  L->nc_max = (uint64_t)(T / Q) + (uint64_t)num_seqs;
-  L->nw_max = (uint64_t)num_seqs + L->nc_max;
+// Workspace regions for up to nc chunks and nw conv-window writes.
+bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, uint64_t nc,
+                    uint64_t nw, PrefillLayout* L) {
+  (void)T;
+  L->nc_max = nc;
+  L->nw_max = nw;
   L->planes = split ? 2 : 1;
   L->meta_bytes = align_up(align_up(num_seqs * sizeof(m2::SeqEntry), 16) + align_up(L->nc_max * sizeof(m2::ChunkEntry), 16) +
                                L->nw_max * sizeof(m2::WindowEntry),
@@ -358,8 +362,12 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
   if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
   if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
     return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
+  // chunks on the grid of chunk_size rows from each sequence's first row, plus one more for each
+  // checkpoint that falls inside a chunk; a conv window per chunk end at most, plus the finals
+  const uint64_t nc = (uint64_t)(total_tokens / chunk_size) + (uint64_t)num_seqs * (1 + (uint64_t)max_ckpt);
   PrefillLayout L;
-  if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, total_tokens, chunk_size, &L))
+  if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, total_tokens, chunk_size, nc,
+                      nc + (uint64_t)num_seqs, &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();
@@ -389,11 +397,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     if (cu_seqlens[s + 1] < cu_seqlens[s]) return fail(M2_ERR_SHAPE, "cu_seqlens decreases at %d", s);
   const int64_t T = cu_seqlens[num_seqs];
   const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
-  if (ckpt_on) {
-    if (!ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
-    if (ckpt_interval % chunk_size != 0)
-      return fail(M2_ERR_ARG, "ckpt_interval %d is not a multiple of chunk_size %d", ckpt_interval, chunk_size);
-  }
+  if (ckpt_on && !ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
   const int S = pool->d.num_slots;
   std::vector<uint8_t> used(S, 0);
   for (int s = 0; s < num_seqs; ++s) {
@@ -403,8 +407,6 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     used[sl] = 1;
     const int sp = start_pos ? start_pos[s] : 0;
     if (sp < 0) return fail(M2_ERR_ARG, "start_pos of sequence %d is negative", s);
-    if (ckpt_on && sp % chunk_size != 0)
-      return fail(M2_ERR_ARG, "start_pos %d of sequence %d is not a multiple of chunk_size", sp, s);
   }
   if (ckpt_on) {
     for (int64_t i = 0; i < (int64_t)num_seqs * max_ckpt; ++i) {
@@ -424,23 +426,17 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   if (m2_status st = check_io(io, 6)) return st;
   if (!m2::prefill_supported(sh.P, sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,32,64,128}");
-  PrefillLayout L;
-  if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, &L))
-    return fail(M2_ERR_SHAPE, "workspace size overflows");
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
-                (unsigned long long)L.total);
 
-  // ---- host tables
+  // ---- host tables.  Chunks run chunk_size rows from each sequence's first row; a checkpoint
+  // position inside a chunk ends that chunk early, so every checkpoint falls on a chunk end.
   std::vector<m2::SeqEntry> seqs(num_seqs);
   std::vector<m2::ChunkEntry> chunks;
   std::vector<m2::WindowEntry> windows;
-  chunks.reserve(L.nc_max);
+  chunks.reserve((size_t)(T / chunk_size) + (size_t)num_seqs);
+  std::vector<std::pair<int, int>> ends;   // (rows into the sequence, checkpoint slot or -1)
   for (int s = 0; s < num_seqs; ++s) {
     const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - cu_seqlens[s];
-    const int sp = start_pos ? start_pos[s] : 0;
+    const int64_t sp = start_pos ? start_pos[s] : 0;
     m2::SeqEntry& e = seqs[s];
     e.t0 = t0;
     e.len = len;
@@ -449,28 +445,45 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     e.chunk0 = (int32_t)chunks.size();
     e.nchunk = 0;
     e.pad0 = e.pad1 = 0;
-    for (int c0 = 0; c0 < len; c0 += chunk_size) {
+    ends.clear();
+    for (int c0 = 0; c0 < len; c0 += chunk_size) ends.push_back({c0 + chunk_size < len ? c0 + chunk_size : len, -1});
+    if (ckpt_on) {
+      // entry k: the k-th multiple p of the interval with start_pos < p <= start_pos + len
+      for (int k = 0; k < max_ckpt; ++k) {
+        const int ck = ckpt_slots[(int64_t)s * max_ckpt + k];
+        const int64_t off = (sp / ckpt_interval + 1 + k) * (int64_t)ckpt_interval - sp;
+        if (ck >= 0 && off <= len) ends.push_back({(int)off, ck});
+      }
+    }
+    std::sort(ends.begin(), ends.end(), [](const std::pair<int, int>& a, const std::pair<int, int>& b) {
+      return a.first != b.first ? a.first < b.first : a.second > b.second;   // a checkpoint first
+    });
+    int prev = 0;
+    for (const auto& en : ends) {
+      if (en.first == prev) continue;   // the same end again (a grid end under a checkpoint)
       m2::ChunkEntry c;
       c.seq = s;
-      c.t0 = t0 + c0;
-      c.len = len - c0 < chunk_size ? len - c0 : chunk_size;
-      c.tau0 = c0;
-      c.ckpt_slot = -1;
-      c.is_last = c0 + chunk_size >= len;
+      c.t0 = t0 + prev;
+      c.len = en.first - prev;
+      c.tau0 = prev;
+      c.ckpt_slot = en.second;
+      c.is_last = en.first == len;
       c.pad0 = c.pad1 = 0;
-      if (ckpt_on) {
-        const int64_t p = (int64_t)sp + c0 + c.len;
-        if (p % ckpt_interval == 0) {
-          const int64_t k = p / ckpt_interval - sp / ckpt_interval - 1;
-          if (k >= 0 && k < max_ckpt) c.ckpt_slot = ckpt_slots[(int64_t)s * max_ckpt + k];
-        }
-      }
-      if (c.ckpt_slot >= 0) windows.push_back({s, c0 + c.len, c.ckpt_slot, 0});
+      if (c.ckpt_slot >= 0) windows.push_back({s, en.first, c.ckpt_slot, 0});
       chunks.push_back(c);
       ++e.nchunk;
+      prev = en.first;
     }
     if (len > 0) windows.push_back({s, len, slots[s], 0});
   }
+  PrefillLayout L;
+  if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, chunks.size(), windows.size(), &L))
+    return fail(M2_ERR_SHAPE, "workspace size overflows");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)L.total);
   if (chunks.empty()) return ok();
 
   // ---- pack the tables; small ones travel in the conv launch's arguments, larger ones are

@@ -150,7 +150,14 @@ class Pool:
             max_ck = ck.shape[1]
             ck_p = ck.ctypes.data_as(c_void_p)
         total = int(cu[-1]) if len(cu) else 0
-        need = self.workspace_size(ns, total, chunk_size, max_ck)
+        off_grid = 0          # the most checkpoints of one sequence that end a chunk early
+        if ckpt_slots is not None and ckpt_interval > 0:
+            for s in range(ns):
+                p0 = int(sp[s]) if sp is not None else 0
+                n = int(cu[s + 1] - cu[s])
+                offs = [(p0 // ckpt_interval + 1 + k) * ckpt_interval - p0 for k in range(max_ck) if ck[s, k] >= 0]
+                off_grid = max(off_grid, sum(1 for o in offs if o < n and o % chunk_size))
+        need = self.workspace_size(ns, total, chunk_size, off_grid)
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=self.ssm.device)
         io = _dtype_code(x)

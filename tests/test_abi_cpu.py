@@ -188,8 +188,15 @@ def test_prefill_validation(pool):
     assert prefill(pool, [0, 5], [0], chunk=512) == UNSUP
     assert prefill(pool, [0, 5], [0], start=[-1]) == ARG
     ck = [[2, 3]]
-    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300) == ARG      # interval % chunk
-    assert prefill(pool, [0, 600], [0], start=[100], ck=ck, max_ck=2, interval=256) == ARG
+    # a checkpoint inside a chunk (position 300 of 600 at chunk 256) ends that chunk: one chunk
+    # more than a workspace sized for checkpoints on the chunk grid holds
+    n = c_uint64()
+    assert lib().mamba2_prefill_workspace_size(pool, 1, 600, 256, 0, byref(n)) == 0
+    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300, ws_bytes=n.value) == WS
+    assert prefill(pool, [0, 600], [0], start=[100], ck=ck, max_ck=2, interval=256, ws_bytes=n.value) == WS
+    n1 = c_uint64()
+    assert lib().mamba2_prefill_workspace_size(pool, 1, 600, 256, 1, byref(n1)) == 0
+    assert n1.value > n.value
     assert prefill(pool, [0, 600], [0], ck=[[0, 3]], max_ck=2, interval=256) == SLOT  # aliases the slot
     assert prefill(pool, [0, 600], [0], ck=[[2, 2]], max_ck=2, interval=256) == SLOT  # repeated
     assert prefill(pool, [0, 600], [0], ck=[[2, 9]], max_ck=2, interval=256) == SLOT  # range

@@ -324,3 +324,77 @@ def test_checkpoint_equals_prefix_prefill_and_restore_replay():
     y_tail = run_prefill(pool, W, [0, L - 256], [3], [1], u[256:], z[256:], dt[256:], "bf16", "f32",
                          chunk=Q, start_pos=[256])
     assert rel_err(host(y_tail), host(y_full[256:])) <= 2e-6
+
+
+def _off_grid_case(ssm_dtype, seed, interval):
+    """Sequences whose start positions and checkpoint interval are off the 64-row chunk grid, with a
+    slot for every multiple of the interval (the pages' "all" mode)."""
+    sh = synth.Shape(8, 64, 128, 2, 4)
+    rng = np.random.default_rng(seed)
+    params = synth.layer_params(rng, sh)
+    lens = np.array([300, 1000, 57, 640], np.int32)
+    start = np.array([100, 0, 30, 7], np.int32)
+    has_init = np.array([1, 0, 1, 1], np.uint8)
+    n = len(lens)
+    slots = np.array([1, 3, 5, 7], np.int32)
+    counts = (start + lens) // interval - start // interval
+    kmax = int(counts.max())
+    ck = np.full((n, kmax), -1, np.int32)
+    free = iter([s for s in range(60) if s not in set(slots.tolist())])
+    for i in range(n):
+        for k in range(counts[i]):
+            ck[i, k] = next(free)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    u, z, dt = synth._tokens(rng, sh, int(cu[-1]), ssm_dtype)
+    ssm0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.nheads, sh.head_dim, sh.d_state)), ssm_dtype)
+    conv0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.conv_dim, sh.conv_kernel - 1)), "bf16")
+    return dict(sh=sh, params=params, lens=lens, has_init=has_init, start=start, slots=slots, ck=ck, cu=cu,
+                u=u, z=z, dt=dt, ssm0=ssm0, conv0=conv0, interval=interval, io=ssm_dtype)
+
+
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_checkpoints_off_the_chunk_grid_match_the_oracle(ssm_dtype):
+    """Start positions and a checkpoint interval (96) off the 64-row chunk grid: every checkpoint
+    ends its chunk early; outputs, final and checkpoint states match the oracle, windows bit-exact."""
+    c = _off_grid_case(ssm_dtype, 400, 96)
+    log(f"case: off-grid checkpoints ssm={ssm_dtype} interval=96 Q=64 ({int((c['ck'] >= 0).sum())} checkpoints)")
+    pool = make_pool(c["sh"], 1, 60, ssm_dtype, "bf16")
+    ref = orc.PoolRef(c["sh"], 1, 60, ssm_dtype, "bf16")
+    for i, s in enumerate(c["slots"]):
+        put_slot(pool, 0, int(s), c["ssm0"][i], c["conv0"][i])
+        ref.ssm[0, s], ref.conv[0, s] = c["ssm0"][i], c["conv0"][i]
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    y = run_prefill(pool, weights(c["params"]), c["cu"], c["slots"], c["has_init"], c["u"], c["z"], c["dt"],
+                    c["io"], ssm_dtype, start_pos=c["start"], chunk=64, interval=96, ckpt=c["ck"])
+    y_ref = orc.prefill(ref, 0, c["params"], c["cu"], c["slots"], c["has_init"], c["start"], c["u"], c["z"],
+                        c["dt"], ssm_dtype, ckpt_interval=96, ckpt_slots=c["ck"])
+    tol = TOL[ssm_dtype]
+    yh = host(y)
+    for i in range(len(c["lens"])):
+        a, b = c["cu"][i], c["cu"][i + 1]
+        assert rel_err(yh[a:b], y_ref[a:b]) <= tol, i
+    written = list(c["slots"]) + [int(s) for s in c["ck"].ravel() if s >= 0]
+    for s in written:
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= tol, s
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+    assert untouched(before_s, pool.ssm, written) and untouched(before_c, pool.conv, written)
+
+
+def test_off_grid_checkpoint_equals_the_prefix_prefill_bit_for_bit():
+    """The checkpoint at 480 of a 1000-token sequence (interval 96, chunk 64) is bit-identical to the
+    final state of a 480-token prefill that asks for the same earlier checkpoints (same chunk ends)."""
+    c = _off_grid_case("f32", 401, 96)
+    sh, W = c["sh"], weights(c["params"])
+    a, b = c["cu"][1], c["cu"][2]
+    u, z, dt = c["u"][a:b], c["z"][a:b], c["dt"][a:b]
+    full = make_pool(sh, 1, 60, "f32", "bf16")
+    ck = np.arange(20, 30, dtype=np.int32).reshape(1, 10)           # positions 96 .. 960
+    run_prefill(full, W, [0, 1000], [1], [0], u, z, dt, "f32", "f32", chunk=64, interval=96, ckpt=ck)
+    pref = make_pool(sh, 1, 60, "f32", "bf16")
+    ckp = np.array([[20, 21, 22, 23, -1]], np.int32)                 # 96 .. 384; 480 is the end
+    run_prefill(pref, W, [0, 480], [1], [0], u[:480], z[:480], dt[:480], "f32", "f32", chunk=64, interval=96,
+                ckpt=ckp)
+    assert torch.equal(full.ssm[0, 24].view(torch.int32), pref.ssm[0, 1].view(torch.int32))
+    assert torch.equal(full.conv[0, 24], pref.conv[0, 1])
+    for s in (20, 21, 22, 23):
+        assert torch.equal(full.ssm[0, s].view(torch.int32), pref.ssm[0, s].view(torch.int32))
