@@ -219,6 +219,37 @@ def ssd_matrix_form(h0, x, Bm, Cm, delta, A: float, D: float):
     return M @ x + D * np.asarray(x) + init
 
 
+def decode_multi(pool: PoolRef, layer: int, params: dict, slots_in, slots_out, u, z, dt, y_dtype: str):
+    """Several decode tokens per sequence (a verified token and its drafts), with the state after
+    every token kept in a slot of its own ([SSM-hybrids]: the conv state widened by num_spec and
+    one extra state block per speculative token, so that the state at whichever token the
+    verifier accepts is at hand).
+
+    Row b starts from slot slots_in[b]; its K tokens u[b, t] (t = 0..K-1) are decode steps in
+    order, each rounding the state it stores as decode does; the state and window after token t
+    go to slot slots_out[b][t] (< 0: not kept).  slots_in itself is left as it was unless it is
+    also an output slot.  Returns out (batch, K, H*P); a padding row (slots_in[b] < 0) reads and
+    writes nothing and its outputs are zero.
+    """
+    s = pool.shape
+    batch, K = len(slots_in), np.asarray(u).shape[1]
+    out = np.zeros((batch, K, s.intermediate))
+    for r, slot in enumerate(slots_in):
+        if slot < 0:
+            continue
+        work = PoolRef(s, 1, 1, pool.ssm_dtype, pool.conv_dtype)
+        work.ssm[0, 0], work.conv[0, 0] = pool.ssm[layer, slot], pool.conv[layer, slot]
+        snaps = []
+        for t in range(K):
+            out[r, t] = decode_step(work, 0, params, [0], np.asarray(u)[r, t:t + 1], np.asarray(z)[r, t:t + 1],
+                                    np.asarray(dt)[r, t:t + 1], y_dtype)[0]
+            snaps.append((work.ssm[0, 0].copy(), work.conv[0, 0].copy()))
+        for t, o in enumerate(slots_out[r]):
+            if o >= 0:
+                pool.ssm[layer, o], pool.conv[layer, o] = snaps[t]
+    return out
+
+
 # --------------------------------------------------------------------------
 # prefill: packed variable-length sequences, chunk boundaries are invisible
 # --------------------------------------------------------------------------

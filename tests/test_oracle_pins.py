@@ -476,3 +476,43 @@ def test_int8_restored_error_evolves_through_the_decay_product():
     delta = np.logaddexp(0.0, dt + params["dt_bias"])
     decay = np.exp((delta * params["A"]).sum(axis=0))
     assert rel_err(finals[1] - finals[0], decay[:, None, None] * err0) < 1e-9
+
+
+# ---------------------------------------------------------------- multi-token (speculative) decode
+def test_multi_token_decode_snapshots_equal_prefill_checkpoints_at_every_token():
+    """K decode tokens with a snapshot after each equal, with fp32 state, a prefill of the same
+    tokens that checkpoints after every token (the prefill keeps the state unrounded between
+    tokens; the difference is fp32 rounding), and the outputs match the prefill's."""
+    shape = synth.Shape(4, 8, 16, 2, 4)
+    rng = np.random.default_rng(51)
+    K = 5
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, K)
+    a = orc.PoolRef(shape, 1, 8, "f32", "f32")
+    a.ssm[0, 0], a.conv[0, 0] = ssm0, conv0
+    y_multi = orc.decode_multi(a, 0, params, [0], [[1, 2, 3, 4, 5]], u[None], z[None], dt[None], "f64")
+    b = orc.PoolRef(shape, 1, 8, "f32", "f32")
+    b.ssm[0, 0], b.conv[0, 0] = ssm0, conv0
+    y_pre = orc.prefill(b, 0, params, [0, K], [0], [1], [0], u, z, dt, "f64", ckpt_interval=1,
+                        ckpt_slots=[[1, 2, 3, 4, 5]])
+    assert rel_err(y_multi[0], y_pre) < 1e-6
+    for t in range(K):
+        assert rel_err(a.ssm[0, 1 + t], b.ssm[0, 1 + t]) < 1e-6
+        assert np.array_equal(a.conv[0, 1 + t], b.conv[0, 1 + t])
+    assert np.array_equal(a.ssm[0, 0], orc.round_to(ssm0, "f32"))     # the input slot is left as it was
+
+
+def test_multi_token_decode_pads_and_skips():
+    shape = synth.TINY
+    rng = np.random.default_rng(52)
+    params, ssm0, conv0, u, z, dt = synth.random_problem(rng, shape, 3)
+    pool = orc.PoolRef(shape, 1, 4, "f32", "f32")
+    pool.ssm[0, 2], pool.conv[0, 2] = ssm0, conv0
+    uu = np.stack([u, u]); zz = np.stack([z, z]); dd = np.stack([dt, dt])
+    y = orc.decode_multi(pool, 0, params, [-1, 2], [[0, 1, 3], [-1, 3, -1]], uu, zz, dd, "f32")
+    assert not y[0].any() and y[1].any()
+    assert not pool.ssm[0, 0].any() and not pool.ssm[0, 1].any()      # the padding row wrote nothing
+    ref = orc.PoolRef(shape, 1, 1, "f32", "f32")
+    ref.ssm[0, 0], ref.conv[0, 0] = ssm0, conv0
+    for t in range(2):
+        orc.decode_step(ref, 0, params, [0], u[t:t + 1], z[t:t + 1], dt[t:t + 1], "f32")
+    assert np.array_equal(pool.ssm[0, 3], ref.ssm[0, 0])               # the state after token 1
