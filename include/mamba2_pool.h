@@ -131,6 +131,38 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              const void* dt, int64_t dt_stride, int32_t io_dtype,
                              void* y, int64_t y_stride, int32_t y_dtype, void* stream);
 
+/* Several decode tokens per sequence in one call: a verified token and its
+ * drafts under speculative decoding, where the verifier may accept any prefix
+ * of the drafts, so the state after every token has to survive
+ * ([SSM-hybrids]: the conv state widened by num_spec columns and one state
+ * block per speculative token).  Row b runs its num_tokens tokens as decode
+ * steps in order from the state and window of slots_in[b] (left as they are
+ * unless also an output slot); the state and window after token t are written
+ * to slot slots_out[b*num_tokens + t], so accepting t+1 tokens means switching
+ * the sequence to that slot.  The states, windows and outputs equal
+ * num_tokens calls of mamba2_decode_step.
+ *   num_tokens 1..8.
+ *   slots_in   device int32[batch]; -1 (or any slot out of range) marks a
+ *              padding row: nothing is read or written and its outputs are zero.
+ *   slots_out  device int32[batch*num_tokens]; an entry out of range (e.g. -1)
+ *              keeps no snapshot of that token.
+ *   slots_in_host, slots_out_host optional host copies; when both are given the
+ *              call checks ranges, distinct input slots, distinct output slots,
+ *              and that no output slot is another row's input slot, and returns
+ *              M2_ERR_SLOT otherwise.
+ *   x, B, C, z, dt, y: as in mamba2_decode_step with batch*num_tokens rows,
+ *              row b*num_tokens + t holding token t of sequence b.
+ * Errors: as mamba2_decode_step, plus M2_ERR_UNSUPPORTED for num_tokens outside
+ * 1..8 or batch > 65535. */
+m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_params* params,
+                              int32_t batch, int32_t num_tokens, const int32_t* slots_in,
+                              const int32_t* slots_out, const int32_t* slots_in_host,
+                              const int32_t* slots_out_host, const void* x, int64_t x_stride,
+                              const void* B, int64_t B_stride, const void* C, int64_t C_stride,
+                              const void* z, int64_t z_stride, const void* dt, int64_t dt_stride,
+                              int32_t io_dtype, void* y, int64_t y_stride, int32_t y_dtype,
+                              void* stream);
+
 /* Bytes of device workspace mamba2_prefill_chunked needs for num_seqs packed
  * sequences totalling total_tokens tokens at chunk_size, when at most max_ckpt
  * checkpoints of any one sequence fall inside a chunk (a position that is

@@ -57,6 +57,10 @@ _SIGS = {
                                          c_uint64, c_void_p]),
     "mamba2_checkpoint_states": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p]),
+    "mamba2_decode_multi": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_int32, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                      c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64,
+                                      c_int32, c_void_p]),
     "mamba2_int8_store_size": (c_int32, [c_void_p, c_int32, POINTER(c_uint64), POINTER(c_uint64),
                                          POINTER(c_uint64)]),
     "mamba2_int8_store_put": (c_int32, [c_void_p, POINTER(Int8StoreDesc), c_int32, c_int32, c_void_p, c_void_p,

@@ -15,6 +15,7 @@
 #include "int8_store.h"
 #include "kernels.h"
 #include "prefill.h"
+#include "spec_decode.h"
 #include "mamba2_pool.h"
 
 struct m2_pool {
@@ -639,6 +640,91 @@ m2_status mamba2_int8_store_get(m2_pool* pool, const m2_int8_store* store, int32
                                 const int32_t* entries, const int32_t* slots, const int32_t* entries_host,
                                 const int32_t* slots_host, void* stream) {
   return int8_store_call(pool, store, layer, n, slots, entries, slots_host, entries_host, false, stream);
+}
+
+m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t batch,
+                              int32_t num_tokens, const int32_t* slots_in, const int32_t* slots_out,
+                              const int32_t* slots_in_host, const int32_t* slots_out_host, const void* x,
+                              int64_t x_stride, const void* B, int64_t B_stride, const void* C, int64_t C_stride,
+                              const void* z, int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype,
+                              void* y, int64_t y_stride, int32_t y_dtype, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  const m2::LayerShape& sh = pool->sh;
+  if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
+  if (num_tokens < 1 || num_tokens > m2::kMaxDecodeTokens)
+    return fail(M2_ERR_UNSUPPORTED, "num_tokens must be in [1, %d], got %d", m2::kMaxDecodeTokens, num_tokens);
+  if (m2_status st = check_params(pool, params)) return st;
+  if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
+  if (batch == 0) return ok();
+  if (!slots_in || !slots_out) return fail(M2_ERR_ARG, "slots_in and slots_out must not be NULL");
+  const int ies = esize(io_dtype);
+  const int GN = sh.G * sh.N;
+  const IoCheck io[] = {{"x", x, x_stride, sh.I, ies, true},        {"B", B, B_stride, GN, ies, true},
+                        {"C", C, C_stride, GN, ies, true},          {"z", z, z_stride, sh.I, ies, false},
+                        {"dt", dt, dt_stride, sh.H, ies, false},    {"y", y, y_stride, sh.I, esize(y_dtype), false}};
+  if (m2_status st = check_io(io, 6)) return st;
+  if (!m2::decode_supported(pool->d.ssm_dtype == M2_BF16, sh.N, sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "decode supports d_state in {16,32,64,128,256}, got %d", sh.N);
+  if ((int64_t)batch > 65535) return fail(M2_ERR_UNSUPPORTED, "at most 65535 sequences per multi-token call");
+  if (slots_in_host && slots_out_host) {
+    const int S = pool->d.num_slots;
+    std::vector<int> in_row(S, -1);   // the row that reads each slot
+    for (int i = 0; i < batch; ++i) {
+      const int s = slots_in_host[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= S) return fail(M2_ERR_SLOT, "input slot %d of row %d out of range", s, i);
+      if (in_row[s] >= 0) return fail(M2_ERR_SLOT, "input slot %d appears twice", s);
+      in_row[s] = i;
+    }
+    std::vector<uint8_t> written(S, 0);
+    for (int64_t i = 0; i < (int64_t)batch * num_tokens; ++i) {
+      const int o = slots_out_host[i];
+      if (o == -1) continue;
+      const int row = (int)(i / num_tokens);
+      if (o < 0 || o >= S) return fail(M2_ERR_SLOT, "output slot %d of row %d out of range", o, row);
+      if (written[o]) return fail(M2_ERR_SLOT, "output slot %d appears twice", o);
+      if (in_row[o] >= 0 && in_row[o] != row)
+        return fail(M2_ERR_SLOT, "output slot %d of row %d is the input slot of row %d", o, row, in_row[o]);
+      written[o] = 1;
+    }
+  }
+  m2::MultiDecodeParams m;
+  m2::DecodeParams& p = m.d;
+  p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
+  p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
+  p.num_slots = pool->d.num_slots;
+  p.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
+  p.io_bf16 = io_dtype == M2_BF16;
+  p.y_bf16 = y_dtype == M2_BF16;
+  p.H = sh.H;
+  p.P = sh.P;
+  p.G = sh.G;
+  p.I = sh.I;
+  p.slots = slots_in;
+  p.x = x;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.dt = dt;
+  p.x_stride = x_stride;
+  p.B_stride = B_stride;
+  p.C_stride = C_stride;
+  p.z_stride = z_stride;
+  p.dt_stride = dt_stride;
+  p.y = y;
+  p.y_stride = y_stride;
+  p.A = params->A;
+  p.D = params->D;
+  p.dt_bias = params->dt_bias;
+  p.conv_w = params->conv_w;
+  p.conv_b = params->conv_b;
+  m.slots_out = slots_out;
+  m.K = num_tokens;
+  const hipError_t e = m2::launch_decode_multi(m, sh.N, sh.W, batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -128,6 +128,32 @@ class Pool:
                                        _dtype_code(y), _stream()))
         return y
 
+    def decode_multi(self, layer: int, w: LayerWeights, slots_in: torch.Tensor, slots_out: torch.Tensor,
+                     x, B, C, z, dt, y, slots_in_host=None, slots_out_host=None):
+        """num_tokens = slots_out.shape[1] decode tokens per row of slots_in (device int32), rows
+        b*num_tokens + t of x, B, C, z, dt and y; the state after token t goes to slots_out[b, t]."""
+        if slots_in.dtype != torch.int32 or slots_out.dtype != torch.int32:
+            raise TypeError("slots must be int32")
+        if slots_out.dim() != 2 or slots_out.shape[0] != slots_in.numel() or not slots_out.is_contiguous():
+            raise ValueError("slots_out must be a contiguous [batch, num_tokens] tensor")
+        _, si_p = _host_i32(slots_in_host)
+        _, so_p = _host_i32(None if slots_out_host is None else np.asarray(slots_out_host).reshape(-1))
+        io = _dtype_code(x)
+        for t in (B, C, z, dt):
+            if _dtype_code(t) != io:
+                raise TypeError("x, B, C, z and dt must share one dtype")
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba2_decode_multi(self._h, layer, byref(w.struct), slots_in.numel(), slots_out.shape[1],
+                                        c_void_p(slots_in.data_ptr()), c_void_p(slots_out.data_ptr()), si_p, so_p,
+                                        xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, io, yp, ys, _dtype_code(y),
+                                        _stream()))
+        return y
+
     # ------------------------------------------------------------------ prefill
     def workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int, max_ckpt: int = 0) -> int:
         n = c_uint64()
