@@ -8,7 +8,9 @@ softplus, state update, readout, gate, in place on the pool.  Inputs are
 synthetic (seeded, resident in HBM before timing).  A second leg times the
 checkpoint copy (256 slot-to-slot copies of both state objects), which is also
 the measured ceiling of a streaming kernel on the part, and the int8 checkpoint
-store (256 slots quantized into entries and restored).  A third times the
+store (256 slots quantized into entries and restored), and the multi-token
+(speculative) decode of the same 256 sequences with 4 tokens each.  A third
+times the
 chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
 fourth the mixed continuous batch (32 prefills with checkpoints and 224
 decodes on one stream) and the 2 x 131072-token long context through all 48
@@ -128,6 +130,7 @@ def main() -> int:
     ap.add_argument("--no-prefill-workloads", action="store_true",
                     help="skip the mixed-batch and long-context prefill timings")
     ap.add_argument("--no-int8-store", action="store_true", help="skip the int8 checkpoint-store timing")
+    ap.add_argument("--no-multi-decode", action="store_true", help="skip the multi-token decode timing")
     ap.add_argument("--no-checkpoint-copy", action="store_true",
                     help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
@@ -272,6 +275,9 @@ def main() -> int:
         out["int8_checkpoint_store"] = res
         del store
 
+    if not args.no_multi_decode:
+        out["multi_token_decode"] = multi_token_decode(dev, stream, e0, e1, w, ms)
+
     if not args.no_prefill:
         pw = synth.prefill_workload(2)
         psh = pw["shape"]
@@ -326,6 +332,51 @@ def main() -> int:
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+def multi_token_decode(dev, stream, e0, e1, w, single_ms) -> dict:
+    """Speculative decode step: the 256 sequences of the decode workload with 4 tokens each (a
+    verified token and 3 drafts), the state after every token kept in a slot of its own (a
+    1280-slot bf16 pool).  Algorithmic bytes per sequence: one state and window read, four written,
+    and the io of four tokens."""
+    import torch
+
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+    sh = w["shape"]
+    K, n = 4, len(w["slots"])
+    gen = torch.Generator(device=dev).manual_seed(11)
+    pool = Pool.allocate(1, n * (K + 1), sh.nheads, sh.head_dim, sh.d_state, sh.n_groups, sh.conv_kernel,
+                         torch.bfloat16, torch.bfloat16, dev)
+    pool.ssm.normal_(0.0, 0.1, generator=gen)
+    pool.conv.normal_(0.0, 0.1, generator=gen)
+    perm = torch.randperm(n * (K + 1), generator=gen, device=dev).to(torch.int32)
+    ins, outs = perm[:n].contiguous(), perm[n:].reshape(n, K).contiguous()
+    u = torch.randn((n * K, sh.conv_dim), generator=gen, device=dev).bfloat16()
+    z = torch.randn((n * K, sh.intermediate), generator=gen, device=dev).bfloat16()
+    dt = torch.randn((n * K, sh.nheads), generator=gen, device=dev).bfloat16()
+    y = torch.empty((n * K, sh.intermediate), dtype=torch.bfloat16, device=dev)
+    W = LayerWeights.from_numpy(w["params"], dev)
+    x, B, C = pool.split_xbc(u)
+    step = lambda: pool.decode_multi(0, W, ins, outs, x, B, C, z, dt, y)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(50):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 50
+    ssm_b, conv_b = pool.info()
+    io = (sh.conv_dim + sh.intermediate + sh.nheads + sh.intermediate) * 2
+    nbytes = n * ((1 + K) * (ssm_b + conv_b) + K * io)
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": f"{n} sequences x {K} tokens (a verified token and {K - 1} drafts), state after every "
+                        "token kept, Nemotron-H layer shape, bf16 state",
+            "ms": t, "tokens_per_s": n * K / (t * 1e-3), "bytes_per_launch": nbytes,
+            "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "speedup_vs_single_steps": K * single_ms / t}
 
 
 def prefill_workloads(dev, stream, e0, e1) -> dict:
