@@ -270,18 +270,23 @@ __device__ __forceinline__ void dt_block(const PrefillParams& a, const ChunkEntr
 }
 
 // ------------------------------------------------------------------ 1b. conv
-// One-dimensional grid over (chunk, 64 channels), channel block fastest, so that workgroups
-// running together read neighbouring pieces of the same token rows; 256 threads.  Thread
-// (octet o, group t) convolves channels 8o .. 8o+7 over tokens 8t .. 8t+7 of the chunk: the
+// One-dimensional grid over (chunk, 64-token part, 256 channels), channel block fastest, so that
+// workgroups running together read neighbouring pieces of the same token rows; 256 threads.
+// Thread (octet o, group t) convolves channels 8o .. 8o+7 over tokens 8t .. 8t+7 of its part: the
 // W-1 halo rows and its 8 rows are requested together (16-byte loads), the taps and SiLU run in
 // fp32, and the results are rounded to the operand planes.  B and C rows go out straight from
-// registers (eight lanes cover 128 contiguous bytes of a row); x and B also go into a
+// registers (32 lanes cover 512 contiguous bytes of a row); x and B also go into a
 // channel-major LDS tile, each thread's block transposed in registers so that it writes 8-byte
 // runs of 4 tokens, from which the transposed planes are written with consecutive lanes
 // on consecutive 16-byte pieces of one row.  In a channel row, token group t sits at position
 // t ^ (row / 8 % 8): the eight channel octets of one token group then fall in distinct banks.
-constexpr int kConvCB = 64;
-constexpr int kConvLD = 256 + 8;   // u16 pitch of a channel row of the LDS tile (16-byte aligned)
+// A conv workgroup covers 256 channels x 64 tokens: 512-byte pieces of each input row, and one
+// 64-token block of the transposed planes per channel (measured: 64 channels x 256 tokens 7%
+// slower, 128 x 128 2% slower).
+constexpr int kConvCB = 256;
+constexpr int kConvTQ = 64 * 256 / kConvCB;   // tokens per workgroup
+constexpr int kConvNH = 256 / kConvTQ;        // workgroups per (chunk, channel block)
+constexpr int kConvLD = kConvTQ + 8;   // u16 pitch of a channel row of the LDS tile (16-byte aligned)
 __device__ __forceinline__ int conv_tpos(int row, int grp) { return 8 * (grp ^ ((row >> 3) & 7)); }
 
 template <bool SPLIT> struct ConvLds {
@@ -339,20 +344,22 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs args) {
   }
   const int bx = blockIdx.x - ndt;
   const int ncb = (a.sh.Cd + CB - 1) / CB;
-  if (bx >= a.num_chunks * ncb) {   // trailing workgroup (inline tables only)
+  if (bx >= a.num_chunks * ncb * kConvNH) {   // trailing workgroup (inline tables only)
     table_copy_block(a);
     return;
   }
-  const int64_t chunk = bx / ncb;
+  const int64_t chunk = bx / (ncb * kConvNH);
+  const int rem = bx % (ncb * kConvNH);
+  const int tq0 = (rem / ncb) * kConvTQ;   // first token of this workgroup inside the chunk
   const ChunkEntry ch = load_uniform(&chunks[chunk]);
   const SeqEntry sq = load_uniform(&seqs[ch.seq]);
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, P = a.sh.P, N = a.sh.N, H = a.sh.H, G = a.sh.G;
   const int Q = a.Q, len = ch.len;
-  const int c0 = (bx % ncb) * CB;
+  const int c0 = (rem % ncb) * CB;
   const int tid = threadIdx.x;
-  const int oc = tid % (CB / 8), tg = tid / (CB / 8);   // 8 octets x 32 token groups
+  const int oc = tid % (CB / 8), tg = tid / (CB / 8);   // 32 channel octets x 8 token groups
   const int c = c0 + 8 * oc;
-  const int j0 = 8 * tg;
+  const int j0 = tq0 + 8 * tg;
   if (c < Cd && j0 < len) {
     const void* src;
     int64_t col, stride;
@@ -449,14 +456,15 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs args) {
   if (c0 >= I + GN) return;   // C channels only: nothing transposed (uniform per workgroup)
   __syncthreads();
   // x and B transposed: lane per 8-token group, consecutive lanes along one channel row
-  const int ngr = (len + 7) / 8;
+  const int ngr = len > tq0 ? (min(len - tq0, kConvTQ) + 7) / 8 : 0;
   for (int idx = tid; idx < CB * ngr; idx += 256) {
     const int g = idx % ngr, ccl = idx / ngr;
+    const int tg8 = tq0 + 8 * g;
     const int cc = c0 + ccl;
     if (cc >= I + GN) continue;
     u16* dst;
     int64_t pstride;
-    const int QB = (Q + kPB - 1) / kPB, blk = (8 * g) / kPB, off = (8 * g) % kPB;
+    const int QB = (Q + kPB - 1) / kPB, blk = tg8 / kPB, off = tg8 % kPB;
     if (cc < I) {
       const int h = cc / P, p = cc % P;
       dst = a.xT + (((chunk * H + h) * QB + blk) * P + p) * kPB + off;
@@ -1783,11 +1791,17 @@ static int group_parts(const PrefillParams& a) {
 
 template <bool SPLIT, int P, int N>
 static hipError_t launch_states_and_outputs(const PrefillParams& a, hipStream_t s) {
-  // two heads of a group per workgroup share the staged B blocks (one for hi/lo planes)
-  if (!SPLIT && (a.sh.H / a.sh.G) % 2 == 0)
-    hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 2>), dim3((a.num_chunks + a.num_windows) * (a.sh.H / 2)),
-                       dim3(kStateThreads), 0, s, a);
-  else
+  // two heads of a group per workgroup share the staged B blocks; one with hi/lo planes (two
+  // measured no faster there)
+  bool two = false;
+  if constexpr (!SPLIT) {
+    if ((a.sh.H / a.sh.G) % 2 == 0) {
+      two = true;
+      hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 2>), dim3((a.num_chunks + a.num_windows) * (a.sh.H / 2)),
+                         dim3(kStateThreads), 0, s, a);
+    }
+  }
+  if (!two)
     hipLaunchKernelGGL((chunk_state_kernel<SPLIT, P, N, 1>), dim3((a.num_chunks + a.num_windows) * a.sh.H),
                        dim3(kStateThreads), 0, s, a);
   const dim3 gp(a.num_seqs, a.sh.H, (P * N / 8 + 255) / 256);
@@ -1850,9 +1864,9 @@ hipError_t launch_prefill(const PrefillParams& a, const InlineTables* inl, hipSt
   ConvArgs ca;
   ca.p = a;
   if (a.tab_inline > 0) memcpy(&ca.t, inl, (size_t)a.tab_inline);
-  // Delta/cumsum workgroups first, then (chunk, 64 channels) with the channel block fastest, then
-  // the table copy
-  const unsigned per_chunk = (unsigned)((a.sh.H + 3) / 4 + (a.sh.Cd + kConvCB - 1) / kConvCB);
+  // Delta/cumsum workgroups first, then (chunk, token part, channel block) with the channel block
+  // fastest, then the table copy
+  const unsigned per_chunk = (unsigned)((a.sh.H + 3) / 4 + (a.sh.Cd + kConvCB - 1) / kConvCB * kConvNH);
   const dim3 gc((unsigned)a.num_chunks * per_chunk + (a.tab_inline > 0 ? 1u : 0u));
   const bool split = !a.ssm_bf16;
   hipError_t ea = hipSuccess;
