@@ -254,6 +254,35 @@ def test_checkpoint_validation(pool):
     assert lib().mamba2_checkpoint_states(pool, 0, 1, None, FAKE, None, None, None) == ARG
 
 
+def decode_multi(h, **kw):
+    a = dict(layer=0, params=byref(PARAMS), batch=2, k=4, si=FAKE, so=FAKE, si_h=None, so_h=None, x=FAKE,
+             xs=8192, B=FAKE, Bs=1024, C=FAKE, Cs=1024, z=FAKE, zs=8192, dt=FAKE, dts=128, io=1, y=FAKE, ys=8192,
+             yd=1)
+    a.update(kw)
+    return lib().mamba2_decode_multi(h, a["layer"], a["params"], a["batch"], a["k"], a["si"], a["so"], a["si_h"],
+                                     a["so_h"], a["x"], a["xs"], a["B"], a["Bs"], a["C"], a["Cs"], a["z"], a["zs"],
+                                     a["dt"], a["dts"], a["io"], a["y"], a["ys"], a["yd"], None)
+
+
+def test_multi_token_decode_validation(pool):
+    i32 = lambda v: (ctypes.c_int32 * len(v))(*v)
+    assert decode_multi(pool, batch=0) == 0
+    assert decode_multi(pool, k=0) == UNSUP
+    assert decode_multi(pool, k=9) == UNSUP
+    assert decode_multi(pool, batch=70000) == UNSUP
+    assert decode_multi(pool, layer=1) == ARG
+    assert decode_multi(pool, si=None) == ARG
+    assert decode_multi(pool, so=None) == ARG
+    assert decode_multi(pool, io=4) == DTYPE
+    assert decode_multi(pool, x=FAKE + 8) == ALIGN
+    # host copies (4 slots in the pool): an output that is another row's input, an output twice,
+    # an input twice, out of range
+    assert decode_multi(pool, k=2, si_h=i32([0, 1]), so_h=i32([2, 1, 3, -1])) == SLOT
+    assert decode_multi(pool, k=2, si_h=i32([0, 1]), so_h=i32([2, 3, 3, -1])) == SLOT
+    assert decode_multi(pool, k=2, si_h=i32([0, 0]), so_h=i32([2, -1, 3, -1])) == SLOT
+    assert decode_multi(pool, k=2, si_h=i32([0, 1]), so_h=i32([2, 9, -1, -1])) == SLOT
+
+
 def store_desc(pool, E=3, **over):
     cb, sb, vb = c_uint64(), c_uint64(), c_uint64()
     assert lib().mamba2_int8_store_size(pool, E, byref(cb), byref(sb), byref(vb)) == 0

@@ -178,3 +178,43 @@ def test_decode_other_shapes(shape, ssm_dtype):
         assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= TOL[ssm_dtype]
         assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s])
     assert untouched(before_s, pool.ssm, slots) and untouched(before_c, pool.conv, slots)
+
+
+def test_batch_above_the_grid_row_limit_is_split_into_launches():
+    """70,000 rows (more than one launch's 65,535 grid rows): live rows on both sides of the split
+    match the oracle; the padding rows between them are zero and touch nothing."""
+    sh = synth.TINY
+    rng = np.random.default_rng(6)
+    params = synth.layer_params(rng, sh)
+    pool = make_pool(sh, 1, 8, "f32", "f32")
+    n = 70000
+    live = {3: 1, 65534: 2, 65535: 5, 69999: 6}            # row -> slot
+    slots = np.full(n, -1, np.int32)
+    ref = orc.PoolRef(sh, 1, 8, "f32", "f32")
+    for r, s in live.items():
+        slots[r] = s
+        st = synth.cast_exact(rng.normal(0, 0.1, (sh.nheads, sh.head_dim, sh.d_state)), "f32")
+        cv = synth.cast_exact(rng.normal(0, 0.1, (sh.conv_dim, sh.conv_kernel - 1)), "f32")
+        put_slot(pool, 0, s, st, cv)
+        ref.ssm[0, s], ref.conv[0, s] = st, cv
+    log(f"case: decode of {n} rows, {len(live)} live, TINY shape")
+    before_s = raw_bytes(pool.ssm)
+    u = torch.randn((n, sh.conv_dim), device="cuda")
+    z = torch.randn((n, sh.intermediate), device="cuda")
+    dt = torch.randn((n, sh.nheads), device="cuda")
+    y = torch.full((n, sh.intermediate), 7.0, device="cuda")
+    x, B, C = pool.split_xbc(u)
+    pool.decode_step(0, weights(params), torch.from_numpy(slots).cuda(), x, B, C, z, dt, y, slots_host=slots)
+    torch.cuda.synchronize()
+    rows = sorted(live)
+    y_ref = orc.decode_step(ref, 0, params, [live[r] for r in rows], host(u[rows]), host(z[rows]), host(dt[rows]),
+                            "f32")
+    assert rel_err(host(y[rows]), y_ref) <= TOL["f32"]
+    pad = torch.ones(n, dtype=torch.bool, device="cuda")
+    pad[rows] = False
+    assert not bool(y[pad].any())
+    for r in rows:
+        s = live[r]
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= TOL["f32"]
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s])
+    assert untouched(before_s, pool.ssm, list(live.values()))
