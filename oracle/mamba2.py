@@ -48,13 +48,18 @@ Readings where the pages are silent (each also listed in the design notes):
 
 Checkpoints may also be held in an int8 store apart from the pool ([SSM-hybrids],
 SGLang int8 checkpoint passage): see int8_quantize below for the arithmetic.
+Several decode tokens per sequence with a snapshot after each (speculative decode):
+decode_multi.  A second recurrent family on the same kind of pool, Mamba1 with a (D, N)
+state: Mamba1PoolRef and mamba1_decode_step.
 
 Parity pins live in the test suite (matrix form of [notes] "Mamba and
 Attention", constant-input closed form, scipy lfilter scalar case,
 np.convolve conv, torch bf16 casts, byte counts printed on the pages; for the
 int8 store: states built from known codes and power-of-two scales, halves
 rounding to even, the half-step error bound, the page's ~2x capacity, and the
-restored error evolving through the decay product).
+restored error evolving through the decay product; for multi-token decode: a prefill
+that checkpoints after every token; for Mamba1: equality with the Mamba2 step when
+the decay does not depend on the state index, and the constant-input closed form).
 """
 from __future__ import annotations
 
@@ -406,3 +411,47 @@ def int8_store_get(store: Int8StoreRef, pool: PoolRef, layer: int, entries, slot
         for e, s in zip(entries, slots):
             pool.ssm[l, s] = int8_dequantize(store.codes[e, l], store.scales[e, l], pool.ssm_dtype)
             pool.conv[l, s] = store.conv[e, l]
+
+
+# --------------------------------------------------------------------------
+# a second recurrent family on the same pool: Mamba1
+# --------------------------------------------------------------------------
+# [notes] "Mamba" gives the recurrence h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t,
+# y_t = C_t h_t; the vLLM state-shape table on the same page gives Mamba1's shapes: a
+# conv state (D, W-1) and a recurrent state (D, N).  Read with those shapes, A is a
+# (D, N) matrix of negative entries (one decay per channel and state index), Delta a
+# per-channel vector (softplus of dt + dt_bias), B_t and C_t length-N vectors shared by
+# all channels, and the short conv runs over the D channels of x only (B, C and dt are
+# taken as given per token, after whatever produced them).  The D skip term and the
+# SiLU(z) gate are as in the Mamba2 path.
+
+class Mamba1PoolRef:
+    """Oracle copy of a Mamba1 slot pool: ssm[layer, slot, D, N], conv[layer, slot, D, W-1]."""
+
+    def __init__(self, d_inner: int, d_state: int, conv_kernel: int, num_layers: int, num_slots: int,
+                 ssm_dtype: str, conv_dtype: str):
+        self.d_inner, self.d_state, self.conv_kernel = d_inner, d_state, conv_kernel
+        self.ssm_dtype, self.conv_dtype = ssm_dtype, conv_dtype
+        self.ssm = np.zeros((num_layers, num_slots, d_inner, d_state))
+        self.conv = np.zeros((num_layers, num_slots, d_inner, conv_kernel - 1))
+
+
+def mamba1_decode_step(pool: Mamba1PoolRef, layer: int, params: dict, slots, u, z, dt, Bm, Cm, y_dtype: str):
+    """One Mamba1 decode token per batch row, in place on the pool.  params: A (D, N) < 0,
+    D (D), dt_bias (D), conv_w (D, W), conv_b (D).  Rows: u, z, dt (batch, D); Bm, Cm (batch, N).
+    Returns out (batch, D) rounded to y_dtype; slots[b] < 0 is a padding row (zero output)."""
+    A, Dk, dt_bias, w, b = (_f64(params[k]) for k in ("A", "D", "dt_bias", "conv_w", "conv_b"))
+    out = np.zeros((len(slots), pool.d_inner))
+    for r, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        window = np.concatenate([pool.conv[layer, slot], _f64(u[r])[:, None]], axis=1)
+        x = silu(b + np.sum(w * window, axis=1))
+        delta = softplus(_f64(dt[r]) + dt_bias)
+        h = pool.ssm[layer, slot]
+        h_new = np.exp(delta[:, None] * A) * h + (delta * x)[:, None] * _f64(Bm[r])[None, :]
+        y = h_new @ _f64(Cm[r]) + Dk * x
+        out[r] = y * silu(_f64(z[r]))
+        pool.ssm[layer, slot] = round_to(h_new, pool.ssm_dtype)
+        pool.conv[layer, slot] = round_to(window[:, 1:], pool.conv_dtype)
+    return round_to(out, y_dtype)
