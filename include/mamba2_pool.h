@@ -52,6 +52,12 @@ typedef enum m2_status {
 
 typedef enum m2_dtype { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
 
+/* State families a pool can hold ([sizing] and the vLLM state-shape table of [notes]). */
+typedef enum m2_family {
+  M2_FAMILY_MAMBA2 = 0, /* temporal state (H, P, N), conv over [x | B | C] */
+  M2_FAMILY_MAMBA1 = 1  /* temporal state (D, N), conv over the D channels of x */
+} m2_family;
+
 /* Pool descriptor.  A pool is two dense caller-owned device tensors, one per
  * state object, indexed [layer, slot, ...] ([SSM-hybrids], MambaPool passage):
  *   ssm_base : [num_layers][num_slots][nheads][head_dim][d_state]   of ssm_dtype
@@ -59,7 +65,9 @@ typedef enum m2_dtype { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
  * with d_conv = nheads*head_dim + 2*n_groups*d_state; the conv window column
  * conv_kernel-2 is the newest input.  ssm_bytes / conv_bytes must equal the
  * dense sizes exactly.  Requirements: nheads % n_groups == 0, head_dim and
- * d_state multiples of 8, 2 <= conv_kernel <= 4, bases 16-byte aligned. */
+ * d_state multiples of 8, 2 <= conv_kernel <= 4, bases 16-byte aligned.
+ * family M2_FAMILY_MAMBA1: nheads = D (a multiple of 8), head_dim = 1,
+ * n_groups = 1, so the state is [D][N] and d_conv = D. */
 typedef struct m2_pool_desc {
   int32_t num_layers;
   int32_t num_slots;
@@ -70,7 +78,7 @@ typedef struct m2_pool_desc {
   int32_t conv_kernel;
   int32_t ssm_dtype;  /* m2_dtype */
   int32_t conv_dtype; /* m2_dtype */
-  int32_t reserved;
+  int32_t family;     /* m2_family; 0 (Mamba2) for every entry point above the Mamba1 one */
   void* ssm_base;
   void* conv_base;
   uint64_t ssm_bytes;
@@ -282,6 +290,26 @@ m2_status mamba2_int8_store_put(m2_pool* pool, const m2_int8_store* store, int32
 m2_status mamba2_int8_store_get(m2_pool* pool, const m2_int8_store* store, int32_t layer, int32_t n,
                                 const int32_t* entries, const int32_t* slots, const int32_t* entries_host,
                                 const int32_t* slots_host, void* stream);
+
+/* One Mamba1 decode token per batch row on a Mamba1 pool, in place: the
+ * recurrence of [notes] ("Mamba": h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t,
+ * y_t = C_t h_t) with the Mamba1 shapes of the vLLM state-shape table on the
+ * same page: per channel d and state index n,
+ *   x = SiLU(conv_b + sum_k conv_w[d][k] * window_k)     (window over x' only)
+ *   Delta_d = softplus(dt_d + dt_bias_d)
+ *   h'[d][n] = exp(Delta_d * A[d][n]) h[d][n] + Delta_d * x_d * B[n]
+ *   y_d = sum_n C[n] h'[d][n] + D_d x_d;  out_d = y_d * SiLU(z_d)
+ * params: A fp32 [D][N] (negative), D, dt_bias, conv_b [D], conv_w [D][W].
+ * Rows: x [batch][D] (raw, before the conv), B and C [batch][N] (taken as
+ * given), z and dt [batch][D] of io_dtype; y [batch][D].  slots, slots_host,
+ * padding rows and alignment as in mamba2_decode_step.
+ * Errors: as mamba2_decode_step; M2_ERR_UNSUPPORTED for a Mamba2 pool or
+ * d_state outside {8, 16, 32, 64, 128, 256}. */
+m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t batch,
+                             const int32_t* slots, const int32_t* slots_host, const void* x, int64_t x_stride,
+                             const void* B, int64_t B_stride, const void* C, int64_t C_stride, const void* z,
+                             int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
+                             int64_t y_stride, int32_t y_dtype, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* mamba2_last_error(void);

@@ -16,7 +16,7 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [("num_layers", c_int32), ("num_slots", c_int32), ("nheads", c_int32),
                 ("head_dim", c_int32), ("d_state", c_int32), ("n_groups", c_int32),
                 ("conv_kernel", c_int32), ("ssm_dtype", c_int32), ("conv_dtype", c_int32),
-                ("reserved", c_int32), ("ssm_base", c_void_p), ("conv_base", c_void_p),
+                ("family", c_int32), ("ssm_base", c_void_p), ("conv_base", c_void_p),
                 ("ssm_bytes", c_uint64), ("conv_bytes", c_uint64)]
 
 
@@ -61,6 +61,9 @@ _SIGS = {
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                       c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64,
                                       c_int32, c_void_p]),
+    "mamba1_decode_step": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p, c_void_p,
+                                     c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                     c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32, c_void_p]),
     "mamba2_int8_store_size": (c_int32, [c_void_p, c_int32, POINTER(c_uint64), POINTER(c_uint64),
                                          POINTER(c_uint64)]),
     "mamba2_int8_store_put": (c_int32, [c_void_p, POINTER(Int8StoreDesc), c_int32, c_int32, c_void_p, c_void_p,

@@ -14,6 +14,7 @@
 
 #include "int8_store.h"
 #include "kernels.h"
+#include "mamba1.h"
 #include "prefill.h"
 #include "spec_decode.h"
 #include "mamba2_pool.h"
@@ -102,8 +103,15 @@ m2::LayerShape make_shape(const m2_pool_desc& d) {
   s.G = d.n_groups;
   s.W = d.conv_kernel;
   s.I = d.nheads * d.head_dim;
-  s.Cd = s.I + 2 * d.n_groups * d.d_state;
+  // Mamba1: the conv runs over x only
+  s.Cd = d.family == M2_FAMILY_MAMBA1 ? s.I : s.I + 2 * d.n_groups * d.d_state;
   return s;
+}
+
+m2_status require_family(const m2_pool* pool, int family, const char* what) {
+  if (pool->d.family != family)
+    return fail(M2_ERR_UNSUPPORTED, "%s needs a %s pool", what, family == M2_FAMILY_MAMBA1 ? "Mamba1" : "Mamba2");
+  return M2_OK;
 }
 
 m2_status hip_fail(hipError_t e, const char* what) {
@@ -239,10 +247,19 @@ m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out) {
     return fail(M2_ERR_ARG, "layer, slot, head, head_dim, d_state and group counts must be positive");
   if (d.conv_kernel < 2 || d.conv_kernel > 4)
     return fail(M2_ERR_UNSUPPORTED, "conv_kernel %d outside the supported range 2..4", d.conv_kernel);
-  if (d.nheads % d.n_groups != 0)
-    return fail(M2_ERR_SHAPE, "nheads %d is not a multiple of n_groups %d", d.nheads, d.n_groups);
-  if (d.head_dim % 8 != 0 || d.d_state % 8 != 0)
-    return fail(M2_ERR_SHAPE, "head_dim and d_state must be multiples of 8");
+  if (d.family != M2_FAMILY_MAMBA2 && d.family != M2_FAMILY_MAMBA1)
+    return fail(M2_ERR_ARG, "family %d is neither Mamba2 (0) nor Mamba1 (1)", d.family);
+  if (d.family == M2_FAMILY_MAMBA1) {
+    if (d.head_dim != 1 || d.n_groups != 1)
+      return fail(M2_ERR_SHAPE, "a Mamba1 pool has head_dim 1 and n_groups 1 (nheads = D channels)");
+    if (d.nheads % 8 != 0 || d.d_state % 8 != 0)
+      return fail(M2_ERR_SHAPE, "a Mamba1 pool needs D and d_state multiples of 8");
+  } else {
+    if (d.nheads % d.n_groups != 0)
+      return fail(M2_ERR_SHAPE, "nheads %d is not a multiple of n_groups %d", d.nheads, d.n_groups);
+    if (d.head_dim % 8 != 0 || d.d_state % 8 != 0)
+      return fail(M2_ERR_SHAPE, "head_dim and d_state must be multiples of 8");
+  }
   if (!dtype_ok(d.ssm_dtype) || !dtype_ok(d.conv_dtype)) return fail(M2_ERR_DTYPE, "ssm/conv dtype must be F32 or BF16");
   if (!d.ssm_base || !d.conv_base) return fail(M2_ERR_ARG, "ssm_base and conv_base must not be NULL");
   if (!aligned16(d.ssm_base) || !aligned16(d.conv_base))
@@ -293,6 +310,7 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
                              int64_t y_stride, int32_t y_dtype, void* stream) {
   if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA2, "mamba2_decode_step")) return st;
   const m2::LayerShape& sh = pool->sh;
   if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
   if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
@@ -360,6 +378,7 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
 m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
                                         int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes) {
   if (!pool || !bytes) return fail(M2_ERR_ARG, "NULL argument");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA2, "mamba2_prefill_workspace_size")) return st;
   if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
   if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
     return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
@@ -383,6 +402,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
                                  const int32_t* ckpt_slots, int32_t max_ckpt, void* workspace,
                                  uint64_t workspace_bytes, void* stream) {
   if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA2, "mamba2_prefill_chunked")) return st;
   const m2::LayerShape& sh = pool->sh;
   if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
   if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
@@ -649,6 +669,7 @@ m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_param
                               const void* z, int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype,
                               void* y, int64_t y_stride, int32_t y_dtype, void* stream) {
   if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA2, "mamba2_decode_multi")) return st;
   const m2::LayerShape& sh = pool->sh;
   if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
   if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
@@ -724,6 +745,74 @@ m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_param
   m.K = num_tokens;
   const hipError_t e = m2::launch_decode_multi(m, sh.N, sh.W, batch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
+  return ok();
+}
+
+m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t batch,
+                             const int32_t* slots, const int32_t* slots_host, const void* x, int64_t x_stride,
+                             const void* B, int64_t B_stride, const void* C, int64_t C_stride, const void* z,
+                             int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
+                             int64_t y_stride, int32_t y_dtype, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA1, "mamba1_decode_step")) return st;
+  const m2::LayerShape& sh = pool->sh;
+  if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
+  if (m2_status st = check_params(pool, params)) return st;
+  if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
+  if (batch == 0) return ok();
+  if (!slots) return fail(M2_ERR_ARG, "slots is NULL");
+  const int ies = esize(io_dtype);
+  const int D = sh.H;
+  const IoCheck io[] = {{"x", x, x_stride, D, ies, false},      {"B", B, B_stride, sh.N, ies, false},
+                        {"C", C, C_stride, sh.N, ies, false},   {"z", z, z_stride, D, ies, false},
+                        {"dt", dt, dt_stride, D, ies, false},   {"y", y, y_stride, D, esize(y_dtype), false}};
+  if (m2_status st = check_io(io, 6)) return st;
+  if (!m2::mamba1_supported(sh.N, sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "Mamba1 decode supports d_state in {8,16,32,64,128,256}, got %d", sh.N);
+  if (slots_host) {
+    std::vector<uint8_t> seen(pool->d.num_slots, 0);
+    for (int i = 0; i < batch; ++i) {
+      const int s = slots_host[i];
+      if (s == -1) continue;
+      if (s < 0 || s >= pool->d.num_slots) return fail(M2_ERR_SLOT, "slot %d of row %d out of range", s, i);
+      if (seen[s]) return fail(M2_ERR_SLOT, "slot %d appears twice", s);
+      seen[s] = 1;
+    }
+  }
+  m2::Mamba1Params p;
+  p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
+  p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
+  p.num_slots = pool->d.num_slots;
+  p.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
+  p.io_bf16 = io_dtype == M2_BF16;
+  p.y_bf16 = y_dtype == M2_BF16;
+  p.D = D;
+  p.x_stride = x_stride;
+  p.B_stride = B_stride;
+  p.C_stride = C_stride;
+  p.z_stride = z_stride;
+  p.dt_stride = dt_stride;
+  p.y_stride = y_stride;
+  p.A = params->A;
+  p.Dk = params->D;
+  p.dt_bias = params->dt_bias;
+  p.conv_w = params->conv_w;
+  p.conv_b = params->conv_b;
+  const int kMaxRows = 65535;   // grid.y limit
+  for (int r0 = 0; r0 < batch; r0 += kMaxRows) {
+    const int nb = batch - r0 < kMaxRows ? batch - r0 : kMaxRows;
+    p.slots = slots + r0;
+    p.x = static_cast<const char*>(x) + (int64_t)r0 * x_stride * ies;
+    p.B = static_cast<const char*>(B) + (int64_t)r0 * B_stride * ies;
+    p.C = static_cast<const char*>(C) + (int64_t)r0 * C_stride * ies;
+    p.z = static_cast<const char*>(z) + (int64_t)r0 * z_stride * ies;
+    p.dt = static_cast<const char*>(dt) + (int64_t)r0 * dt_stride * ies;
+    p.y = static_cast<char*>(y) + (int64_t)r0 * y_stride * esize(y_dtype);
+    const hipError_t e = m2::launch_mamba1_decode(p, sh.N, sh.W, nb, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "Mamba1 decode launch");
+  }
   return ok();
 }
 

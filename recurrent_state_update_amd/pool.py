@@ -61,17 +61,18 @@ class Pool:
     """Slot pool over caller-owned tensors ssm [L, S, H, P, N] and conv [L, S, Cd, W-1]."""
 
     def __init__(self, ssm: torch.Tensor, conv: torch.Tensor, nheads: int, head_dim: int, d_state: int,
-                 n_groups: int, conv_kernel: int):
+                 n_groups: int, conv_kernel: int, family: int = 0):
         if not (ssm.is_contiguous() and conv.is_contiguous()):
             raise ValueError("pool tensors must be contiguous")
         self.ssm, self.conv = ssm, conv
         self.nheads, self.head_dim, self.d_state = nheads, head_dim, d_state
         self.n_groups, self.conv_kernel = n_groups, conv_kernel
+        self.family = family               # 0: Mamba2, 1: Mamba1 (nheads = D channels, head_dim 1)
         self.intermediate = nheads * head_dim
-        self.conv_dim = self.intermediate + 2 * n_groups * d_state
+        self.conv_dim = self.intermediate + (0 if family == 1 else 2 * n_groups * d_state)
         self.num_layers, self.num_slots = ssm.shape[0], ssm.shape[1]
         desc = PoolDesc(self.num_layers, self.num_slots, nheads, head_dim, d_state, n_groups, conv_kernel,
-                        _dtype_code(ssm), _dtype_code(conv), 0, ssm.data_ptr(), conv.data_ptr(),
+                        _dtype_code(ssm), _dtype_code(conv), family, ssm.data_ptr(), conv.data_ptr(),
                         ssm.numel() * ssm.element_size(), conv.numel() * conv.element_size())
         h = c_void_p()
         check(lib().mamba2_pool_create(byref(desc), byref(h)))
@@ -84,6 +85,36 @@ class Pool:
         ssm = torch.zeros((num_layers, num_slots, nheads, head_dim, d_state), dtype=ssm_dtype, device=device)
         conv = torch.zeros((num_layers, num_slots, cd, conv_kernel - 1), dtype=conv_dtype, device=device)
         return cls(ssm, conv, nheads, head_dim, d_state, n_groups, conv_kernel)
+
+    @classmethod
+    def allocate_mamba1(cls, num_layers, num_slots, d_inner, d_state, conv_kernel, ssm_dtype=torch.bfloat16,
+                        conv_dtype=torch.bfloat16, device="cuda"):
+        """A Mamba1 pool: ssm [L, S, D, 1, N] (the (D, N) state) and conv [L, S, D, W-1]."""
+        ssm = torch.zeros((num_layers, num_slots, d_inner, 1, d_state), dtype=ssm_dtype, device=device)
+        conv = torch.zeros((num_layers, num_slots, d_inner, conv_kernel - 1), dtype=conv_dtype, device=device)
+        return cls(ssm, conv, d_inner, 1, d_state, 1, conv_kernel, family=1)
+
+    def mamba1_decode_step(self, layer: int, w: LayerWeights, slots: torch.Tensor, x, B, C, z, dt, y,
+                           slots_host=None):
+        """One Mamba1 token per row of slots (device int32): x, z, dt rows of D, B and C rows of N;
+        w.A is the (D, N) decay matrix."""
+        if slots.dtype != torch.int32:
+            raise TypeError("slots must be int32")
+        _, sh_ptr = _host_i32(slots_host)
+        io = _dtype_code(x)
+        for t in (B, C, z, dt):
+            if _dtype_code(t) != io:
+                raise TypeError("x, B, C, z and dt must share one dtype")
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba1_decode_step(self._h, layer, byref(w.struct), slots.numel(), c_void_p(slots.data_ptr()),
+                                       sh_ptr, xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, io, yp, ys,
+                                       _dtype_code(y), _stream()))
+        return y
 
     def close(self):
         if getattr(self, "_h", None):

@@ -95,6 +95,28 @@ def layer_params(rng: np.random.Generator, shape: Shape) -> dict:
             dict(A=A, D=D, dt_bias=dt_bias, conv_w=conv_w, conv_b=conv_b).items()}
 
 
+# A Mamba1 layer for the second state family of the pool: D channels, state size N, conv W
+# (d_inner 8192, d_state 16, conv 4: the width of the 7B-class Mamba1 models).
+MAMBA1_D, MAMBA1_N, MAMBA1_W = 8192, 16, 4
+
+
+def mamba1_layer_params(rng: np.random.Generator, D: int, N: int, W: int) -> dict:
+    """Mamba1 parameters drawn in a fixed order, fp32-exact float64: A (D, N) < 0, D, dt_bias,
+    conv_b (D), conv_w (D, W); same value ranges as the Mamba2 layer."""
+    dt_bias = rng.uniform(-4.0, -2.0, D)
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), (D, N)))
+    Dk = rng.standard_normal(D)
+    conv_w = rng.uniform(-0.5, 0.5, (D, W))
+    conv_b = rng.uniform(-0.5, 0.5, D)
+    return {k: cast_exact(v, "f32").astype(np.float64) for k, v in
+            dict(A=A, D=Dk, dt_bias=dt_bias, conv_w=conv_w, conv_b=conv_b).items()}
+
+
+def mamba1_tokens(rng: np.random.Generator, n: int, D: int, N: int, io_dtype: str):
+    """n Mamba1 token rows: raw x (D), z (D), dt (D), B (N), C (N), N(0, 1), io-dtype exact."""
+    return tuple(cast_exact(rng.standard_normal(s), io_dtype) for s in ((n, D), (n, D), (n, D), (n, N), (n, N)))
+
+
 def sentinel_bytes(rng: np.random.Generator, nbytes: int) -> np.ndarray:
     return rng.integers(0, 256, nbytes, dtype=np.uint8)
 

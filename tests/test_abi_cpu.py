@@ -29,7 +29,7 @@ FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba2_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba[12]_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(l, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _ffi.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (mamba2_\w+)", out))
+    exported = set(re.findall(r"\bT (mamba[12]_\w+)", out))
     assert set(names) <= exported
     assert set(_ffi.exported_symbols()) == set(names)
     assert l.mamba2_abi_version() == 2
@@ -281,6 +281,36 @@ def test_multi_token_decode_validation(pool):
     assert decode_multi(pool, k=2, si_h=i32([0, 1]), so_h=i32([2, 3, 3, -1])) == SLOT
     assert decode_multi(pool, k=2, si_h=i32([0, 0]), so_h=i32([2, -1, 3, -1])) == SLOT
     assert decode_multi(pool, k=2, si_h=i32([0, 1]), so_h=i32([2, 9, -1, -1])) == SLOT
+
+
+def test_mamba1_pool_family():
+    """A Mamba1 pool holds a (D, N) state and a (D, W-1) window; the Mamba2 entry points refuse it
+    and the Mamba1 decode refuses a Mamba2 pool."""
+    D, N, W, S = 64, 16, 4, 4
+    d = PoolDesc(1, S, D, 1, N, 1, W, 1, 1, 1, FAKE, FAKE, S * D * N * 2, S * D * (W - 1) * 2)
+    st, h = create(d)
+    assert st == 0, lib().mamba2_last_error()
+    a, b = c_uint64(), c_uint64()
+    assert lib().mamba2_pool_info(h, byref(a), byref(b)) == 0
+    assert (a.value, b.value) == (D * N * 2, D * (W - 1) * 2)
+    n = c_uint64()
+    assert lib().mamba2_prefill_workspace_size(h, 1, 100, 64, 0, byref(n)) == UNSUP
+    assert decode(h) == UNSUP
+    assert decode_multi(h) == UNSUP
+    m1 = lambda hh, **kw: lib().mamba1_decode_step(hh, kw.get("layer", 0), byref(PARAMS), kw.get("batch", 2), FAKE,
+                                                  None, FAKE, D, FAKE, N, FAKE, N, FAKE, D, FAKE, D, 1, FAKE, D, 1,
+                                                  None)
+    assert m1(h, batch=0) == 0
+    assert m1(h, layer=1) == ARG
+    lib().mamba2_pool_destroy(h)
+    st, h2 = create(make_desc())                      # a Mamba2 pool
+    assert st == 0
+    assert m1(h2, batch=0) == UNSUP
+    lib().mamba2_pool_destroy(h2)
+    bad = PoolDesc(1, S, D, 2, N, 1, W, 1, 1, 1, FAKE, FAKE, S * D * 2 * N * 2, S * D * 2 * (W - 1) * 2)
+    assert create(bad)[0] == SHAPE                    # head_dim must be 1
+    bad = PoolDesc(1, S, D, 1, N, 1, W, 1, 1, 7, FAKE, FAKE, S * D * N * 2, S * D * (W - 1) * 2)
+    assert create(bad)[0] == ARG                      # unknown family
 
 
 def store_desc(pool, E=3, **over):
