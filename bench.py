@@ -9,7 +9,8 @@ synthetic (seeded, resident in HBM before timing).  A second leg times the
 checkpoint copy (256 slot-to-slot copies of both state objects), which is also
 the measured ceiling of a streaming kernel on the part, and the int8 checkpoint
 store (256 slots quantized into entries and restored), and the multi-token
-(speculative) decode of the same 256 sequences with 4 tokens each.  A third
+(speculative) decode of the same 256 sequences with 4 tokens each, and a Mamba1
+decode step (the pool's second state family, D = 8192, N = 16).  A third
 times the
 chunked prefill of one 8192-token sequence (chunk 256) at the same shape; a
 fourth the mixed continuous batch (32 prefills with checkpoints and 224
@@ -131,6 +132,7 @@ def main() -> int:
                     help="skip the mixed-batch and long-context prefill timings")
     ap.add_argument("--no-int8-store", action="store_true", help="skip the int8 checkpoint-store timing")
     ap.add_argument("--no-multi-decode", action="store_true", help="skip the multi-token decode timing")
+    ap.add_argument("--no-mamba1", action="store_true", help="skip the Mamba1 decode timing")
     ap.add_argument("--no-checkpoint-copy", action="store_true",
                     help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
@@ -278,6 +280,9 @@ def main() -> int:
     if not args.no_multi_decode:
         out["multi_token_decode"] = multi_token_decode(dev, stream, e0, e1, w, ms)
 
+    if not args.no_mamba1:
+        out["mamba1_decode"] = mamba1_decode(dev, stream, e0, e1)
+
     if not args.no_prefill:
         pw = synth.prefill_workload(2)
         psh = pw["shape"]
@@ -377,6 +382,46 @@ def multi_token_decode(dev, stream, e0, e1, w, single_ms) -> dict:
             "ms": t, "tokens_per_s": n * K / (t * 1e-3), "bytes_per_launch": nbytes,
             "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "speedup_vs_single_steps": K * single_ms / t}
+
+
+def mamba1_decode(dev, stream, e0, e1) -> dict:
+    """The pool's second state family: a Mamba1 decode step (D = 8192, N = 16, conv 4) for 256
+    sequences at permuted slots of a 512-slot bf16 pool.  Algorithmic bytes per sequence: the
+    (D, N) state and the (D, 3) window read and written, x, z, dt, B, C in and y out."""
+    import torch
+
+    from recurrent_state_update_amd import synth
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+    D, N, Wd = synth.MAMBA1_D, synth.MAMBA1_N, synth.MAMBA1_W
+    n = 256
+    rng = np.random.default_rng(12)
+    gen = torch.Generator(device=dev).manual_seed(12)
+    pool = Pool.allocate_mamba1(1, 2 * n, D, N, Wd, torch.bfloat16, torch.bfloat16, dev)
+    pool.ssm.normal_(0.0, 0.1, generator=gen)
+    pool.conv.normal_(0.0, 0.1, generator=gen)
+    W = LayerWeights.from_numpy(synth.mamba1_layer_params(rng, D, N, Wd), dev)
+    sl = torch.from_numpy(rng.permutation(2 * n)[:n].astype(np.int32)).to(dev)
+    x, z, dt = (torch.randn((n, D), generator=gen, device=dev).bfloat16() for _ in range(3))
+    B, C = (torch.randn((n, N), generator=gen, device=dev).bfloat16() for _ in range(2))
+    y = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
+    step = lambda: pool.mamba1_decode_step(0, W, sl, x, B, C, z, dt, y)
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(200):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 200
+    ssm_b, conv_b = pool.info()
+    per_seq = 2 * (ssm_b + conv_b) + (3 * D + 2 * N) * 2 + D * 2
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": f"Mamba1 decode step, D={D}, N={N}, conv {Wd}, {n} sequences at permuted slots of a "
+                        f"{2 * n}-slot bf16 pool",
+            "ms": t, "tokens_per_s": n / (t * 1e-3), "bytes_per_launch": n * per_seq,
+            "gbs": n * per_seq / (t * 1e-3) / 1e9, "hbm_frac": n * per_seq / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def prefill_workloads(dev, stream, e0, e1) -> dict:
