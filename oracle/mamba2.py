@@ -455,3 +455,43 @@ def mamba1_decode_step(pool: Mamba1PoolRef, layer: int, params: dict, slots, u, 
         pool.ssm[layer, slot] = round_to(h_new, pool.ssm_dtype)
         pool.conv[layer, slot] = round_to(window[:, 1:], pool.conv_dtype)
     return round_to(out, y_dtype)
+
+
+def mamba1_prefill(pool: Mamba1PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init, start_pos,
+                   u, z, dt, Bm, Cm, y_dtype: str, ckpt_interval: int = 0, ckpt_slots=None):
+    """Mamba1 prefill of packed sequences: the token-by-token recurrence of mamba1_decode_step with
+    the state kept unrounded between tokens; only the final state (slots[s]) and the checkpoint
+    states are rounded to the ssm dtype, as in the Mamba2 prefill.  Rows: u, z, dt (T, D); Bm, Cm
+    (T, N).  Checkpoint entry k of sequence s takes the state and window after absolute position
+    p, the k-th multiple of ckpt_interval with start_pos < p <= start_pos + L."""
+    A, Dk, dt_bias, w, b = (_f64(params[k]) for k in ("A", "D", "dt_bias", "conv_w", "conv_b"))
+    W = pool.conv_kernel
+    out = np.zeros((int(cu_seqlens[-1]), pool.d_inner))
+    for s, slot in enumerate(slots):
+        t0, t1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        if t1 == t0:
+            continue
+        sp = int(start_pos[s]) if start_pos is not None else 0
+        if has_init[s]:
+            h = pool.ssm[layer, slot].copy()
+            stream = list(pool.conv[layer, slot].T)         # W-1 rows of D, oldest first
+        else:
+            h = np.zeros((pool.d_inner, pool.d_state))
+            stream = [np.zeros(pool.d_inner) for _ in range(W - 1)]
+        for t in range(t0, t1):
+            stream.append(_f64(u[t]))
+            window = np.stack(stream[-W:], axis=1)
+            x = silu(b + np.sum(w * window, axis=1))
+            delta = softplus(_f64(dt[t]) + dt_bias)
+            h = np.exp(delta[:, None] * A) * h + (delta * x)[:, None] * _f64(Bm[t])[None, :]
+            out[t] = (h @ _f64(Cm[t]) + Dk * x) * silu(_f64(z[t]))
+            p = sp + (t - t0) + 1
+            if ckpt_interval > 0 and ckpt_slots is not None and p % ckpt_interval == 0:
+                k = p // ckpt_interval - sp // ckpt_interval - 1
+                if 0 <= k < len(ckpt_slots[s]) and ckpt_slots[s][k] >= 0:
+                    pool.ssm[layer, ckpt_slots[s][k]] = round_to(h, pool.ssm_dtype)
+                    pool.conv[layer, ckpt_slots[s][k]] = round_to(np.stack(stream[-(W - 1):], axis=1),
+                                                                  pool.conv_dtype)
+        pool.ssm[layer, slot] = round_to(h, pool.ssm_dtype)
+        pool.conv[layer, slot] = round_to(np.stack(stream[-(W - 1):], axis=1), pool.conv_dtype)
+    return round_to(out, y_dtype)

@@ -582,3 +582,38 @@ def test_mamba1_constant_input_closed_form_per_channel_and_state_index():
     assert rel_err(pool.ssm[0, 0], hT) < 1e-12
     yT = (hT @ Ct + p["D"] * x) * (z / (1 + np.exp(-z)))
     assert rel_err(y[0], yT) < 1e-12
+
+
+def test_mamba1_prefill_equals_decode_steps_and_the_decay_product():
+    """A Mamba1 prefill equals the same tokens as decode steps (fp64 storage: no rounding between
+    tokens either way), checkpoints included, and a perturbation of the initial state evolves
+    through the product of the decays exp(sum_t Delta_t[d] A[d, n])."""
+    rng = np.random.default_rng(63)
+    D, N, W, L = 8, 8, 3, 21
+    p = _m1_params(rng, D, N, W)
+    u, z, dt = rng.normal(0, 1, (L, D)), rng.normal(0, 1, (L, D)), rng.normal(0, 1, (L, D))
+    Bm, Cm = rng.normal(0, 1, (L, N)), rng.normal(0, 1, (L, N))
+    h0, w0 = rng.normal(0, 0.1, (D, N)), rng.normal(0, 0.1, (D, W - 1))
+    pre = orc.Mamba1PoolRef(D, N, W, 1, 6, "f64", "f64")
+    pre.ssm[0, 1], pre.conv[0, 1] = h0, w0
+    y_pre = orc.mamba1_prefill(pre, 0, p, [0, L], [1], [1], [3], u, z, dt, Bm, Cm, "f64", ckpt_interval=6,
+                               ckpt_slots=[[2, 3, 4]])
+    dec = orc.Mamba1PoolRef(D, N, W, 1, 1, "f64", "f64")
+    dec.ssm[0, 0], dec.conv[0, 0] = h0, w0
+    snaps = {}
+    for t in range(L):
+        y = orc.mamba1_decode_step(dec, 0, p, [0], u[t:t + 1], z[t:t + 1], dt[t:t + 1], Bm[t:t + 1], Cm[t:t + 1],
+                                   "f64")
+        assert rel_err(y[0], y_pre[t]) < 1e-12, t
+        snaps[3 + t + 1] = (dec.ssm[0, 0].copy(), dec.conv[0, 0].copy())
+    assert rel_err(pre.ssm[0, 1], dec.ssm[0, 0]) < 1e-12
+    for k, pos in enumerate((6, 12, 18)):                       # multiples of 6 in (3, 24]
+        assert rel_err(pre.ssm[0, 2 + k], snaps[pos][0]) < 1e-12
+        assert np.array_equal(pre.conv[0, 2 + k], snaps[pos][1])
+    dlt = rng.normal(0, 0.01, (D, N))
+    pre2 = orc.Mamba1PoolRef(D, N, W, 1, 6, "f64", "f64")
+    pre2.ssm[0, 1], pre2.conv[0, 1] = h0 + dlt, w0
+    orc.mamba1_prefill(pre2, 0, p, [0, L], [1], [1], [3], u, z, dt, Bm, Cm, "f64")
+    delta = np.logaddexp(0.0, dt + p["dt_bias"])                 # (L, D)
+    decay = np.exp(delta.sum(axis=0)[:, None] * p["A"])         # prod_t exp(Delta_t[d] A[d, n])
+    assert rel_err(pre2.ssm[0, 1] - pre.ssm[0, 1], decay * dlt) < 1e-9
