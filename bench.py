@@ -132,7 +132,7 @@ def main() -> int:
                     help="skip the mixed-batch and long-context prefill timings")
     ap.add_argument("--no-int8-store", action="store_true", help="skip the int8 checkpoint-store timing")
     ap.add_argument("--no-multi-decode", action="store_true", help="skip the multi-token decode timing")
-    ap.add_argument("--no-mamba1", action="store_true", help="skip the Mamba1 decode timing")
+    ap.add_argument("--no-mamba1", action="store_true", help="skip the Mamba1 decode and prefill timings")
     ap.add_argument("--no-checkpoint-copy", action="store_true",
                     help="skip the checkpoint-copy timing (also the known-size copy that scales the byte counters)")
     args = ap.parse_args()
@@ -282,6 +282,7 @@ def main() -> int:
 
     if not args.no_mamba1:
         out["mamba1_decode"] = mamba1_decode(dev, stream, e0, e1)
+        out["mamba1_prefill"] = mamba1_prefill_leg(dev, stream, e0, e1)
 
     if not args.no_prefill:
         pw = synth.prefill_workload(2)
@@ -422,6 +423,50 @@ def mamba1_decode(dev, stream, e0, e1) -> dict:
                         f"{2 * n}-slot bf16 pool",
             "ms": t, "tokens_per_s": n / (t * 1e-3), "bytes_per_launch": n * per_seq,
             "gbs": n * per_seq / (t * 1e-3) / 1e9, "hbm_frac": n * per_seq / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def mamba1_prefill_leg(dev, stream, e0, e1) -> dict:
+    """Mamba1 prefill (D = 8192, N = 16, conv 4, bf16 state and rows, chunk 256) of 8 sequences of
+    1024 rows from zero states.  Algorithmic bytes per row: x, z, dt and y of D and B, C of N at
+    2 bytes; the (D, N) state and window written once per sequence.  The recurrence takes one
+    exponential per (row, channel, state index), twice (chunk end states, then the outputs)."""
+    import torch
+
+    from recurrent_state_update_amd import synth
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+    D, N, Wd = synth.MAMBA1_D, synth.MAMBA1_N, synth.MAMBA1_W
+    ns, ln, Q = 8, 1024, 256
+    T = ns * ln
+    rng = np.random.default_rng(13)
+    gen = torch.Generator(device=dev).manual_seed(13)
+    pool = Pool.allocate_mamba1(1, ns, D, N, Wd, torch.bfloat16, torch.bfloat16, dev)
+    W = LayerWeights.from_numpy(synth.mamba1_layer_params(rng, D, N, Wd), dev)
+    x, z, dt = (torch.randn((T, D), generator=gen, device=dev).bfloat16() for _ in range(3))
+    B, C = (torch.randn((T, N), generator=gen, device=dev).bfloat16() for _ in range(2))
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    cu = np.arange(ns + 1, dtype=np.int32) * ln
+    slots = np.arange(ns, dtype=np.int32)
+    zeros = np.zeros(ns, np.uint8)
+    ws = torch.empty(pool.mamba1_workspace_size(ns, T, Q), dtype=torch.uint8, device=dev)
+    step = lambda: pool.mamba1_prefill(0, W, cu, slots, zeros, x, B, C, z, dt, y, chunk_size=Q, workspace=ws)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(20):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 20
+    ssm_b, conv_b = pool.info()
+    nbytes = T * (4 * D + 2 * N) * 2 + ns * (ssm_b + conv_b)
+    del pool, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"Mamba1 prefill, D={D}, N={N}, conv {Wd}, {ns} sequences x {ln} rows from zero "
+                        f"states, chunk {Q}, bf16 state and rows",
+            "ms": t, "tokens_per_s": T / (t * 1e-3), "bytes_per_launch": nbytes,
+            "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "exp_per_s": 2 * T * D * N / (t * 1e-3)}
 
 
 def prefill_workloads(dev, stream, e0, e1) -> dict:

@@ -311,6 +311,32 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
                              int64_t y_stride, int32_t y_dtype, void* stream);
 
+/* Workspace bytes mamba1_prefill needs (same arguments as
+ * mamba2_prefill_workspace_size; max_ckpt is the width of the checkpoint table). */
+m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
+                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
+
+/* Mamba1 prefill of packed sequences on a Mamba1 pool: the recurrence of
+ * mamba1_decode_step over each sequence's rows, the state kept in fp32 between
+ * tokens and rounded only into the final slot and the checkpoint slots (the
+ * Mamba2 prefill's rules: cu_seqlens, slots, has_initial_state, start_pos,
+ * ckpt_interval, ckpt_slots [num_seqs][max_ckpt] -- any interval and start
+ * position).  Rows: x, z, dt [T][D] (x raw, before the conv), B, C [T][N]
+ * (16-byte aligned with 16-byte multiple row strides), y [T][D].  The work
+ * runs in chunks of chunk_size rows (16..4096): each chunk's end state from
+ * zero, a pass through each sequence's chunks, then every chunk again from its
+ * entering state.  workspace: at least mamba1_prefill_workspace_size(...)
+ * bytes, 256-byte aligned.  The launch tables go through the pool's pinned
+ * staging buffer (the call may wait for the previous upload on the host). */
+m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t num_seqs,
+                         const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_initial_state,
+                         const int32_t* start_pos, const void* x, int64_t x_stride, const void* B,
+                         int64_t B_stride, const void* C, int64_t C_stride, const void* z, int64_t z_stride,
+                         const void* dt, int64_t dt_stride, int32_t io_dtype, void* y, int64_t y_stride,
+                         int32_t y_dtype, int32_t chunk_size, int32_t ckpt_interval,
+                         const int32_t* ckpt_slots, int32_t max_ckpt, void* workspace,
+                         uint64_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* mamba2_last_error(void);
 

@@ -64,6 +64,13 @@ _SIGS = {
     "mamba1_decode_step": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p, c_void_p,
                                      c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                      c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32, c_void_p]),
+    "mamba1_prefill_workspace_size": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                                POINTER(c_uint64)]),
+    "mamba1_prefill": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                 c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
+                                 c_int64, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p,
+                                 c_uint64, c_void_p]),
     "mamba2_int8_store_size": (c_int32, [c_void_p, c_int32, POINTER(c_uint64), POINTER(c_uint64),
                                          POINTER(c_uint64)]),
     "mamba2_int8_store_put": (c_int32, [c_void_p, POINTER(Int8StoreDesc), c_int32, c_int32, c_void_p, c_void_p,

@@ -118,6 +118,38 @@ m2_status hip_fail(hipError_t e, const char* what) {
   return fail(M2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Copy `bytes` of host data, written into the buffer by fill(), to device memory at dst on the
+// stream, through the pool's pinned staging buffer: one host-to-device copy, the buffer reused
+// once the previous copy has completed (the call may wait for that on the host).
+template <typename F>
+m2_status staged_upload(m2_pool* pool, void* dst, size_t bytes, hipStream_t hs, F fill) {
+  std::lock_guard<std::mutex> lock(pool->mu);
+  hipError_t e;
+  if (pool->staging_pending) {
+    if ((e = hipEventSynchronize(pool->staging_done)) != hipSuccess) return hip_fail(e, "staging wait");
+    pool->staging_pending = false;
+  }
+  if (pool->staging_bytes < bytes) {
+    if (pool->staging) (void)hipHostFree(pool->staging);
+    pool->staging = nullptr;
+    pool->staging_bytes = 0;
+    if ((e = hipHostMalloc(&pool->staging, bytes, hipHostMallocDefault)) != hipSuccess)
+      return hip_fail(e, "pinned staging allocation");
+    pool->staging_bytes = bytes;
+  }
+  if (!pool->staging_done) {
+    if ((e = hipEventCreateWithFlags(&pool->staging_done, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "staging event");
+  }
+  char* st = static_cast<char*>(pool->staging);
+  memset(st, 0, bytes);
+  fill(st);
+  if ((e = hipMemcpyAsync(dst, st, bytes, hipMemcpyHostToDevice, hs)) != hipSuccess) return hip_fail(e, "table upload");
+  if ((e = hipEventRecord(pool->staging_done, hs)) != hipSuccess) return hip_fail(e, "staging event record");
+  pool->staging_pending = true;
+  return M2_OK;
+}
+
 // Prefill tables and workspace carving.
 struct PrefillLayout {
   uint64_t nc_max, nw_max, planes;
@@ -228,6 +260,27 @@ m2_status int8_store_call(m2_pool* pool, const m2_int8_store* store, int32_t lay
   const hipError_t e = put ? m2::launch_int8_put(a, n, nl, hs) : m2::launch_int8_get(a, n, nl, hs);
   if (e != hipSuccess) return hip_fail(e, put ? "int8 store put launch" : "int8 store get launch");
   return ok();
+}
+
+// Mamba1 prefill workspace: tables, then each chunk's end state and sum of Delta, the state
+// entering each chunk, and each sequence's initial window.
+struct M1Layout {
+  uint64_t off_chunks, off_ck, tab_bytes, off_S, off_SD, off_Hin, off_W0, total;
+};
+
+bool m1_layout(const m2::LayerShape& sh, int64_t num_seqs, int64_t nc, int64_t nck, M1Layout* L) {
+  uint64_t v, dn;
+  L->off_chunks = align_up((uint64_t)num_seqs * sizeof(m2::M1Seq), 16);
+  L->off_ck = align_up(L->off_chunks + (uint64_t)nc * sizeof(m2::M1Chunk), 16);
+  L->tab_bytes = align_up(L->off_ck + (uint64_t)nck * 4, 16);
+  if (!mul_ok((uint64_t)sh.H, (uint64_t)sh.N, &dn)) return false;
+  L->off_S = align_up(L->tab_bytes, 256);
+  if (!mul_ok((uint64_t)nc, dn * 4, &v)) return false;
+  L->off_SD = align_up(L->off_S + v, 256);
+  L->off_Hin = align_up(L->off_SD + (uint64_t)nc * sh.H * 4, 256);
+  L->off_W0 = align_up(L->off_Hin + v, 256);
+  L->total = align_up(L->off_W0 + (uint64_t)num_seqs * sh.H * (sh.W - 1) * 4, 256);
+  return true;
 }
 
 }  // namespace
@@ -516,41 +569,17 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool tab_inline = tab_bytes <= (size_t)m2::kInlineTableBytes;
+  auto pack = [&](char* tab) {
+    memcpy(tab, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
+    memcpy(tab + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
+    memcpy(tab + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
+  };
   m2::InlineTables inl;
-  char* tab = reinterpret_cast<char*>(inl.w);
-  std::unique_lock<std::mutex> lock(pool->mu, std::defer_lock);
-  if (!tab_inline) {
-    lock.lock();
-    hipError_t e;
-    if (pool->staging_pending) {
-      if ((e = hipEventSynchronize(pool->staging_done)) != hipSuccess) return hip_fail(e, "staging wait");
-      pool->staging_pending = false;
-    }
-    if (pool->staging_bytes < tab_bytes) {
-      if (pool->staging) (void)hipHostFree(pool->staging);
-      pool->staging = nullptr;
-      pool->staging_bytes = 0;
-      if ((e = hipHostMalloc(&pool->staging, tab_bytes, hipHostMallocDefault)) != hipSuccess)
-        return hip_fail(e, "pinned staging allocation");
-      pool->staging_bytes = tab_bytes;
-    }
-    if (!pool->staging_done) {
-      if ((e = hipEventCreateWithFlags(&pool->staging_done, hipEventDisableTiming)) != hipSuccess)
-        return hip_fail(e, "staging event");
-    }
-    tab = static_cast<char*>(pool->staging);
-  }
-  memset(tab, 0, tab_bytes);
-  memcpy(tab, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
-  memcpy(tab + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
-  memcpy(tab + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
-  if (!tab_inline) {
-    hipError_t e;
-    if ((e = hipMemcpyAsync(ws, tab, tab_bytes, hipMemcpyHostToDevice, hs)) != hipSuccess)
-      return hip_fail(e, "table upload");
-    if ((e = hipEventRecord(pool->staging_done, hs)) != hipSuccess) return hip_fail(e, "staging event record");
-    pool->staging_pending = true;
-    lock.unlock();
+  if (tab_inline) {
+    memset(inl.w, 0, tab_bytes);
+    pack(reinterpret_cast<char*>(inl.w));
+  } else if (m2_status st = staged_upload(pool, ws, tab_bytes, hs, pack)) {
+    return st;
   }
 
   m2::PrefillParams p;
@@ -813,6 +842,140 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
     const hipError_t e = m2::launch_mamba1_decode(p, sh.N, sh.W, nb, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "Mamba1 decode launch");
   }
+  return ok();
+}
+
+m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
+                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes) {
+  if (!pool || !bytes) return fail(M2_ERR_ARG, "NULL argument");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA1, "mamba1_prefill_workspace_size")) return st;
+  if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
+  if (chunk_size < 16 || chunk_size > 4096) return fail(M2_ERR_UNSUPPORTED, "chunk_size must be in [16, 4096]");
+  M1Layout L;
+  if (!m1_layout(pool->sh, num_seqs, (int64_t)total_tokens / chunk_size + num_seqs, (int64_t)num_seqs * max_ckpt, &L))
+    return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
+  *bytes = L.total;
+  return ok();
+}
+
+m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t num_seqs,
+                         const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_init,
+                         const int32_t* start_pos, const void* x, int64_t x_stride, const void* B, int64_t B_stride,
+                         const void* C, int64_t C_stride, const void* z, int64_t z_stride, const void* dt,
+                         int64_t dt_stride, int32_t io_dtype, void* y, int64_t y_stride, int32_t y_dtype,
+                         int32_t chunk_size, int32_t ckpt_interval, const int32_t* ckpt_slots, int32_t max_ckpt,
+                         void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  if (m2_status st = require_family(pool, M2_FAMILY_MAMBA1, "mamba1_prefill")) return st;
+  const m2::LayerShape& sh = pool->sh;
+  if (layer < 0 || layer >= pool->d.num_layers) return fail(M2_ERR_ARG, "layer %d out of range", layer);
+  if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
+  if (m2_status st = check_params(pool, params)) return st;
+  if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
+  if (chunk_size < 16 || chunk_size > 4096) return fail(M2_ERR_UNSUPPORTED, "chunk_size must be in [16, 4096]");
+  if (ckpt_interval < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative checkpoint interval or count");
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens || !slots || !has_init) return fail(M2_ERR_ARG, "cu_seqlens, slots and has_initial_state are required");
+  if (cu_seqlens[0] != 0) return fail(M2_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < num_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return fail(M2_ERR_SHAPE, "cu_seqlens decreases at %d", s);
+  const int64_t T = cu_seqlens[num_seqs];
+  const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
+  if (ckpt_on && !ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
+  const int S = pool->d.num_slots;
+  std::vector<uint8_t> used(S, 0);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int sl = slots[s];
+    if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "slot %d of sequence %d out of range", sl, s);
+    if (used[sl]) return fail(M2_ERR_SLOT, "slot %d appears twice", sl);
+    used[sl] = 1;
+    if (start_pos && start_pos[s] < 0) return fail(M2_ERR_ARG, "start_pos of sequence %d is negative", s);
+  }
+  if (ckpt_on) {
+    for (int64_t i = 0; i < (int64_t)num_seqs * max_ckpt; ++i) {
+      const int sl = ckpt_slots[i];
+      if (sl == -1) continue;
+      if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "checkpoint slot %d out of range", sl);
+      if (used[sl]) return fail(M2_ERR_SLOT, "checkpoint slot %d repeats or aliases a sequence slot", sl);
+      used[sl] = 1;
+    }
+  }
+  if (T == 0) return ok();
+  const int ies = esize(io_dtype);
+  const int D = sh.H;
+  const IoCheck io[] = {{"x", x, x_stride, D, ies, false},      {"B", B, B_stride, sh.N, ies, true},
+                        {"C", C, C_stride, sh.N, ies, true},    {"z", z, z_stride, D, ies, false},
+                        {"dt", dt, dt_stride, D, ies, false},   {"y", y, y_stride, D, esize(y_dtype), false}};
+  if (m2_status st = check_io(io, 6)) return st;
+  if (!m2::mamba1_supported(sh.N, sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "Mamba1 prefill supports d_state in {8,16,32,64,128,256}, got %d", sh.N);
+  // tables: chunks of chunk_size rows from each sequence's first row
+  std::vector<m2::M1Seq> seqs(num_seqs);
+  std::vector<m2::M1Chunk> chunks;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - t0;
+    seqs[s] = m2::M1Seq{t0, len, slots[s], has_init[s] ? 1 : 0, start_pos ? start_pos[s] : 0,
+                        s * (ckpt_on ? max_ckpt : 0), ckpt_on ? max_ckpt : 0, (int32_t)chunks.size()};
+    for (int c0 = 0; c0 < len; c0 += chunk_size)
+      chunks.push_back(m2::M1Chunk{s, t0 + c0, len - c0 < chunk_size ? len - c0 : chunk_size, c0});
+  }
+  if (chunks.size() > 65535 || num_seqs > 65535)
+    return fail(M2_ERR_UNSUPPORTED, "%zu chunks and %d sequences: at most 65535 of each (raise chunk_size)",
+                chunks.size(), num_seqs);
+  const int64_t nck = ckpt_on ? (int64_t)num_seqs * max_ckpt : 0;
+  M1Layout L;
+  if (!m1_layout(sh, num_seqs, (int64_t)chunks.size(), nck, &L)) return fail(M2_ERR_SHAPE, "workspace size overflows");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
+                (unsigned long long)L.total);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (m2_status st = staged_upload(pool, ws, L.tab_bytes, hs, [&](char* t) {
+        memcpy(t, seqs.data(), seqs.size() * sizeof(m2::M1Seq));
+        memcpy(t + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::M1Chunk));
+        if (nck) memcpy(t + L.off_ck, ckpt_slots, (size_t)nck * 4);
+      }))
+    return st;
+  m2::Mamba1PrefillParams p;
+  p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
+  p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
+  p.num_slots = S;
+  p.ssm_bf16 = pool->d.ssm_dtype == M2_BF16;
+  p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
+  p.io_bf16 = io_dtype == M2_BF16;
+  p.y_bf16 = y_dtype == M2_BF16;
+  p.D = D;
+  p.x = x;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.dt = dt;
+  p.x_stride = x_stride;
+  p.B_stride = B_stride;
+  p.C_stride = C_stride;
+  p.z_stride = z_stride;
+  p.dt_stride = dt_stride;
+  p.y = y;
+  p.y_stride = y_stride;
+  p.A = params->A;
+  p.Dk = params->D;
+  p.dt_bias = params->dt_bias;
+  p.conv_w = params->conv_w;
+  p.conv_b = params->conv_b;
+  p.num_seqs = num_seqs;
+  p.num_chunks = (int)chunks.size();
+  p.ckpt_interval = ckpt_on ? ckpt_interval : 0;
+  p.seqs = reinterpret_cast<const m2::M1Seq*>(ws);
+  p.chunks = reinterpret_cast<const m2::M1Chunk*>(ws + L.off_chunks);
+  p.ck = reinterpret_cast<const int32_t*>(ws + L.off_ck);
+  p.S = reinterpret_cast<float*>(ws + L.off_S);
+  p.SD = reinterpret_cast<float*>(ws + L.off_SD);
+  p.Hin = reinterpret_cast<float*>(ws + L.off_Hin);
+  p.Win0 = reinterpret_cast<float*>(ws + L.off_W0);
+  const hipError_t e = m2::launch_mamba1_prefill(p, sh.N, sh.W, hs);
+  if (e != hipSuccess) return hip_fail(e, "Mamba1 prefill launch");
   return ok();
 }
 

@@ -29,3 +29,45 @@ hipError_t launch_mamba1_decode(const Mamba1Params& p, int N, int W, int batch, 
 bool mamba1_supported(int N, int W);
 
 }  // namespace m2
+
+namespace m2 {
+
+// Mamba1 prefill over packed sequences, in chunks of Q tokens from each sequence's first row.
+struct M1Seq {      // one per sequence
+  int32_t t0, len, slot, has_init, start_pos, ck0, nck, chunk0;
+};
+struct M1Chunk {    // one per chunk
+  int32_t seq, t0, len, tau0;   // packed start row, rows, offset inside the sequence
+};
+struct Mamba1PrefillParams {
+  void* ssm;            // [num_slots][D][N] of one layer
+  void* conv;           // [num_slots][D][W-1] of one layer
+  int num_slots;
+  int ssm_bf16, conv_bf16, io_bf16, y_bf16;
+  int D;
+  const void* x;
+  const void* B;
+  const void* C;
+  const void* z;
+  const void* dt;
+  int64_t x_stride, B_stride, C_stride, z_stride, dt_stride;
+  void* y;
+  int64_t y_stride;
+  const float* A;
+  const float* Dk;
+  const float* dt_bias;
+  const float* conv_w;
+  const float* conv_b;
+  int num_seqs, num_chunks, ckpt_interval;
+  const M1Seq* seqs;        // workspace tables
+  const M1Chunk* chunks;
+  const int32_t* ck;        // checkpoint slots, sequence s at ck[seqs[s].ck0 ...]
+  float* S;                 // [chunks][D][N] each chunk's end state from a zero state
+  float* SD;                // [chunks][D] each chunk's sum of Delta per channel
+  float* Hin;               // [chunks][D][N] the state entering each chunk
+  float* Win0;              // [seqs][D][W-1] each sequence's initial window, read once by launch (1)
+                            // (launch (3) writes the final window into the same slot)
+};
+hipError_t launch_mamba1_prefill(const Mamba1PrefillParams& p, int N, int W, hipStream_t s);
+
+}  // namespace m2

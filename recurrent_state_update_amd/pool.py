@@ -116,6 +116,49 @@ class Pool:
                                        _dtype_code(y), _stream()))
         return y
 
+    def mamba1_workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int = 256,
+                              max_ckpt: int = 0) -> int:
+        n = c_uint64()
+        check(lib().mamba1_prefill_workspace_size(self._h, num_seqs, total_tokens, chunk_size, max_ckpt,
+                                                  byref(n)))
+        return n.value
+
+    def mamba1_prefill(self, layer: int, w: LayerWeights, cu_seqlens, slots, has_init, x, B, C, z, dt, y,
+                       start_pos=None, chunk_size: int = 256, ckpt_interval: int = 0, ckpt_slots=None,
+                       workspace: torch.Tensor | None = None):
+        """Mamba1 prefill of packed sequences (rows x, z, dt of D; B, C of N); cu_seqlens, slots,
+        has_init, start_pos and ckpt_slots [num_seqs][max_ckpt] are host arrays."""
+        cu, _ = _host_i32(cu_seqlens)
+        sl, sl_p = _host_i32(slots)
+        hi = np.ascontiguousarray(np.asarray(has_init, dtype=np.uint8))
+        sp, sp_p = _host_i32(start_pos)   # sp keeps the array alive through the call
+        ns = len(sl)
+        max_ck, ck_p = 0, None
+        if ckpt_slots is not None:
+            ck = np.ascontiguousarray(np.asarray(ckpt_slots, dtype=np.int32).reshape(ns, -1))
+            max_ck = ck.shape[1]
+            ck_p = ck.ctypes.data_as(c_void_p)
+        total = int(cu[-1]) if len(cu) else 0
+        if workspace is None:
+            workspace = torch.empty(self.mamba1_workspace_size(ns, total, chunk_size, max_ck), dtype=torch.uint8,
+                                    device=self.ssm.device)
+        io = _dtype_code(x)
+        for t in (B, C, z, dt):
+            if _dtype_code(t) != io:
+                raise TypeError("x, B, C, z and dt must share one dtype")
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba1_prefill(
+            self._h, layer, byref(w.struct), ns, cu.ctypes.data_as(c_void_p), sl_p,
+            hi.ctypes.data_as(c_void_p), sp_p, xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, io, yp, ys,
+            _dtype_code(y), chunk_size, ckpt_interval, ck_p, max_ck, c_void_p(workspace.data_ptr()),
+            workspace.numel(), _stream()))
+        return y
+
     def close(self):
         if getattr(self, "_h", None):
             lib().mamba2_pool_destroy(self._h)

@@ -367,3 +367,54 @@ def test_last_error_is_cleared_by_success(pool):
 
 def test_destroy_null_is_noop():
     lib().mamba2_pool_destroy(None)
+
+
+def test_mamba1_prefill_validation():
+    """Mamba1 prefill: sizing, family, slot, shape and workspace errors, all raised on the host
+    before any device work (the too-small workspace is the last check before the table upload)."""
+    D, N, W, S = 64, 16, 4, 6
+    i32 = lambda v: np.ascontiguousarray(np.asarray(v, dtype=np.int32))
+    st, h = create(PoolDesc(1, S, D, 1, N, 1, W, 1, 1, 1, FAKE, FAKE, S * D * N * 2, S * D * (W - 1) * 2))
+    assert st == 0, lib().mamba2_last_error()
+    n0, n1, n2 = c_uint64(), c_uint64(), c_uint64()
+    assert lib().mamba1_prefill_workspace_size(h, 2, 100, 32, 0, byref(n0)) == 0
+    assert lib().mamba1_prefill_workspace_size(h, 2, 1000, 32, 0, byref(n1)) == 0
+    assert lib().mamba1_prefill_workspace_size(h, 2, 1000, 32, 4, byref(n2)) == 0
+    # end state and entering state per chunk (2 x D N fp32) dominate the growth
+    assert n1.value - n0.value >= (1000 // 32 - 100 // 32) * 2 * D * N * 4
+    assert n2.value >= n1.value and n0.value % 256 == 0
+    assert lib().mamba1_prefill_workspace_size(h, 2, 100, 8, 0, byref(n0)) == UNSUP
+    assert lib().mamba2_prefill_workspace_size(h, 2, 100, 64, 0, byref(n0)) == UNSUP
+
+    def call(hh=None, **kw):
+        cu = i32(kw.get("cu", [0, 40, 100]))
+        sl = i32(kw.get("slots", [0, 1]))
+        hi = np.asarray(kw.get("has_init", [1, 0]), dtype=np.uint8)
+        ck = kw.get("ck")
+        ck_p = ck.ctypes.data_as(c_void_p) if ck is not None else None
+        return lib().mamba1_prefill(
+            hh or h, kw.get("layer", 0), byref(PARAMS), len(sl), cu.ctypes.data_as(c_void_p),
+            sl.ctypes.data_as(c_void_p), hi.ctypes.data_as(c_void_p), None, FAKE, D, kw.get("B", FAKE),
+            kw.get("Bs", N), FAKE, N, FAKE, D, FAKE, D, 1, FAKE, D, 1, kw.get("chunk", 32),
+            kw.get("interval", 0), ck_p, ck.shape[1] if ck is not None else 0, kw.get("ws", FAKE),
+            kw.get("ws_bytes", 64), None)
+
+    assert call() == WS                                   # 64 bytes is far too small
+    assert call(ws=FAKE + 16, ws_bytes=1 << 40) == WS     # misaligned
+    assert call(cu=[0, 0, 0]) == 0                        # no rows: nothing to do
+    assert call(layer=1) == ARG
+    assert call(chunk=8) == UNSUP
+    assert call(slots=[0, 0]) == SLOT
+    assert call(slots=[0, 6]) == SLOT
+    assert call(cu=[0, 50, 40]) == SHAPE
+    assert call(cu=[1, 50, 60]) == SHAPE
+    assert call(B=FAKE + 4) == ALIGN
+    assert call(Bs=N + 2) == ALIGN
+    assert call(interval=16, ck=i32([[2, 3], [1, -1]])) == SLOT     # aliases sequence 1's slot
+    assert call(interval=16, ck=i32([[2, 3], [3, -1]])) == SLOT     # repeats
+    assert call(interval=16, ck=i32([[2, 3], [4, -1]])) == WS       # valid up to the workspace
+    st, h2 = create(make_desc())
+    assert st == 0
+    assert call(h2) == UNSUP                                         # a Mamba2 pool
+    lib().mamba2_pool_destroy(h2)
+    lib().mamba2_pool_destroy(h)
