@@ -65,8 +65,8 @@ struct Mamba1PrefillParams {
   float* S;                 // [chunks][D][N] each chunk's end state from a zero state
   float* SD;                // [chunks][D] each chunk's sum of Delta per channel
   float* Hin;               // [chunks][D][N] the state entering each chunk
-  float* Win0;              // [seqs][D][W-1] each sequence's initial window, read once by launch (1)
-                            // (launch (3) writes the final window into the same slot)
+  float* Win0;              // [seqs][D][W-1] the initial window of each sequence of several chunks,
+                            // copied by launch (1) for launch (3), whose last chunk rewrites the slot
 };
 hipError_t launch_mamba1_prefill(const Mamba1PrefillParams& p, int N, int W, hipStream_t s);
 

@@ -143,138 +143,224 @@ hipError_t launch_mamba1_decode(const Mamba1Params& p, int N, int W, int batch, 
 }  // namespace m2
 
 // ============================================================================ prefill
-// Three launches: (1) each chunk's end state from a zero state and its per-channel sum of Delta,
-// all chunks at once; (2) per (sequence, channel, state index) the pass through the sequence's
-// chunks, h <- exp(A sum Delta) h + S_c, writing the state entering each chunk; (3) each chunk's
-// tokens again from its entering state, with the outputs, the checkpoint states at their tokens
-// and the final state.  Launches (1) and (3) give a channel's state values to N/8 lanes of one
-// wave, run the token recurrence in fp32 registers (inputs of the next token requested before the
-// current one is computed) and reduce h C over the channel's lanes with xor shuffles.
+// Three launches: (1) the end state from a zero state and the per-channel sum of Delta of every
+// chunk that is not its sequence's last (a last chunk's end state feeds nothing), all at once;
+// (2) per (sequence, channel, state index) the pass through the sequence's chunks,
+// h <- exp(A sum Delta) h + S_c, writing the state entering each chunk; (3) every chunk again
+// from its entering state, with the outputs, the checkpoint states at their tokens and the final
+// state.  Launches (1) and (3) take a 256-thread workgroup per (chunk, block of channels) and walk
+// the chunk in blocks of TB tokens: the raw rows of the block are loaded cooperatively (the next
+// block's requested while the current one runs), each (token, channel) gets its conv, Delta,
+// Delta x, D x and silu(z) once, into LDS, and then the recurrence runs with a channel's state
+// values spread over N/8 lanes in fp32 registers, h C reduced with xor shuffles.
 namespace m2 {
 
-constexpr int kM1PThreads = 64;
 constexpr int kM1PV = 8;   // state values per lane
 
-template <int W> struct M1Tok {   // one token's inputs for one lane
-  float u, dt, z;
-  float B[kM1PV], C[kM1PV];
-};
+constexpr int kM1Ring = 16;   // rows of the raw-x ring: a token block and the W-1 rows before it
+template <int N, int W> constexpr int m1_tb() { return N / kM1PV == 1 ? 8 : kM1Ring - (W - 1); }
 
-template <bool OUT, int N, int W>
-__device__ __forceinline__ void m1_load_tok(const Mamba1PrefillParams& a, int64_t row, int d, int n0,
-                                            M1Tok<W>& t) {
-  t.u = load_any(a.x, row * a.x_stride + d, a.io_bf16);
-  t.dt = load_any(a.dt, row * a.dt_stride + d, a.io_bf16);
-  load8_any(a.B, row * a.B_stride + n0, a.io_bf16, t.B);
-  if (OUT) {
-    t.z = load_any(a.z, row * a.z_stride + d, a.io_bf16);
-    load8_any(a.C, row * a.C_stride + n0, a.io_bf16, t.C);
-  }
+// log(1 + e^v) from the hardware exp2 and log2.  Above 20 the value is v to fp32 resolution;
+// below, with e = e^v and u = 1 + e rounded, log(u) e / (u - 1) cancels the rounding of u
+// (Goldberg's log1p identity), and is e itself when u rounds to 1.
+__device__ __forceinline__ float m1_softplus(float v) {
+  if (v > 20.f) return v;
+  const float e = __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
+  const float u = 1.f + e;
+  const float um1 = u - 1.f;
+  return um1 == 0.f ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * __builtin_amdgcn_rcpf(um1);
 }
 
-// OUT = false: launch (1); OUT = true: launch (3).
-template <typename TS, bool OUT, int N, int W>
-__global__ __launch_bounds__(kM1PThreads) void mamba1_chunk_kernel(Mamba1PrefillParams a) {
-  constexpr int LPC = N / kM1PV;
-  constexpr int CPW = kM1PThreads / LPC;
+template <typename TI> __device__ __forceinline__ float m1_ld(const void* p, int64_t i) {
+  return to_f32(static_cast<const TI*>(p)[i]);
+}
+
+// OUT = false: launch (1); OUT = true: launch (3).  TI: the dtype of the x, z, dt, B, C rows.
+template <typename TS, typename TI, bool OUT, int N, int W>
+__global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a) {
+  constexpr int LPC = N / kM1PV;             // recurrence lanes per channel
+  constexpr int CPW = 256 / LPC;             // channels per workgroup
+  constexpr int TB = m1_tb<N, W>();          // tokens per block
+  constexpr int R = kM1Ring;
+  static_assert(TB + W - 1 <= R, "ring too short");
+  constexpr int RS = 256 / CPW;              // staging: row step of one thread
+  constexpr int PP = (TB + RS - 1) / RS;     // staging: (token, channel) pairs per thread
+  constexpr int BPT = (TB * N + 255) / 256;  // staging: B (and C) values per thread
+  constexpr int NO = OUT ? TB : 1;
+  __shared__ float xs[R][CPW];
+  __shared__ float s_dl[TB][CPW], s_dx[TB][CPW];
+  __shared__ float s_dy[NO][CPW], s_sz[NO][CPW];
+  __shared__ __align__(16) float s_B[TB][N];
+  __shared__ __align__(16) float s_C[NO][N];
+
   const int ci = blockIdx.y;
   const M1Chunk ch = a.chunks[ci];
   const M1Seq sq = a.seqs[ch.seq];
-  const int lane = threadIdx.x;
-  const int c = lane / LPC, sub = lane % LPC;
-  const int d = blockIdx.x * CPW + c;
+  const bool first = ch.tau0 == 0, last = ch.tau0 + ch.len == sq.len;
+  if (!OUT && last) return;
+  const int tid = threadIdx.x, D = a.D, d0 = blockIdx.x * CPW;
+
+  // staging role: channel pc, rows pr0, pr0 + RS, ...
+  const int pc = tid % CPW, pr0 = tid / CPW;
+  const int pd = d0 + pc;
+  const bool pon = pd < D;
+  const int pdd = pon ? pd : 0;
+  float w[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) w[k] = a.conv_w[(int64_t)pdd * W + k];
+  const float cb = a.conv_b[pdd], bias = a.dt_bias[pdd];
+  const float Dd = OUT ? a.Dk[pdd] : 0.f;
+
+  // the W-1 raw inputs before the chunk: earlier rows of the sequence, else the slot's window
+  // (launch (1) copies a first chunk's window aside for launch (3), whose last chunk rewrites the
+  // slot's window while the first may still be reading it; a chunk that is both reads the slot)
+  if (pr0 == 0) {
+    float* const w0 = a.Win0 + ((int64_t)ch.seq * D + pdd) * (W - 1);
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) {
+      const int tau = ch.tau0 - (W - 1) + k;
+      float v;
+      if (tau >= 0) v = m1_ld<TI>(a.x, (int64_t)(sq.t0 + tau) * a.x_stride + pdd);
+      else if (OUT && !last) v = w0[k];
+      else if (sq.has_init) v = load_any(a.conv, ((int64_t)sq.slot * D + pdd) * (W - 1) + k, a.conv_bf16);
+      else v = 0.f;
+      xs[k][pc] = v;
+      if (!OUT && first && pon) w0[k] = v;
+    }
+  }
+
+  // recurrence role: channel rc, state values n0 .. n0+7
+  const int rc = tid / LPC, sub = tid % LPC;
+  const int rd = d0 + rc;
+  const bool ron = rd < D;
+  const int rdd = ron ? rd : 0;
   const int n0 = sub * kM1PV;
-  const bool on = d < a.D;
-  const int dd = on ? d : 0;   // lanes past D run on channel 0 and store nothing
-  const int D = a.D;
   const float kLog2e = 1.4426950408889634f;
   float A2[kM1PV], h[kM1PV];
 #pragma unroll
-  for (int e = 0; e < kM1PV; ++e) A2[e] = a.A[(int64_t)dd * N + n0 + e] * kLog2e;
+  for (int e = 0; e < kM1PV; ++e) A2[e] = a.A[(int64_t)rdd * N + n0 + e] * kLog2e;
   if (OUT) {
-    const float* hin = a.Hin + ((int64_t)ci * D + dd) * N + n0;
+    const float* hin = a.Hin + ((int64_t)ci * D + rdd) * N + n0;
 #pragma unroll
     for (int e = 0; e < kM1PV; ++e) h[e] = hin[e];
   } else {
 #pragma unroll
     for (int e = 0; e < kM1PV; ++e) h[e] = 0.f;
   }
-  float w[W];
-#pragma unroll
-  for (int k = 0; k < W; ++k) w[k] = a.conv_w[(int64_t)dd * W + k];
-  const float cb = a.conv_b[dd], bias = a.dt_bias[dd], Dd = a.Dk[dd];
-  // the W-1 raw inputs before the chunk: earlier rows of the sequence, else the slot's window
-  float win[W - 1];
-  float* const w0 = a.Win0 + ((int64_t)ch.seq * D + dd) * (W - 1);
-#pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
-    const int tau = ch.tau0 - (W - 1) + k;
-    if (tau >= 0) win[k] = load_any(a.x, (int64_t)(sq.t0 + tau) * a.x_stride + dd, a.io_bf16);
-    else if (OUT) win[k] = w0[W - 1 + tau];   // the slot's window, as launch (1) read it
-    else if (sq.has_init) win[k] = load_any(a.conv, ((int64_t)sq.slot * D + dd) * (W - 1) + (W - 1 + tau), a.conv_bf16);
-    else win[k] = 0.f;
-  }
-  if (!OUT && ch.tau0 == 0 && on && sub == 0) {
-#pragma unroll
-    for (int k = 0; k < W - 1; ++k) w0[k] = win[k];
-  }
-  auto store_state = [&](int slot) {
-    TS* st = static_cast<TS*>(a.ssm) + ((int64_t)slot * D + d) * N + n0;
+  // state and window after chunk token q (the window's raw rows are in the ring)
+  auto store_state = [&](int slot, int q) {
+    TS* st = static_cast<TS*>(a.ssm) + ((int64_t)slot * D + rd) * N + n0;
 #pragma unroll
     for (int e = 0; e < kM1PV; ++e) st[e] = from_f32<TS>(h[e]);
     if (sub == 0) {
 #pragma unroll
-      for (int k = 0; k < W - 1; ++k) store_any(a.conv, ((int64_t)slot * D + d) * (W - 1) + k, win[k], a.conv_bf16);
+      for (int k = 0; k < W - 1; ++k)
+        store_any(a.conv, ((int64_t)slot * D + rd) * (W - 1) + k, xs[(q + 1 + k) & (R - 1)][rc], a.conv_bf16);
     }
   };
-  float sumd = 0.f;
-  M1Tok<W> cur, nxt;
-  if (ch.len > 0) m1_load_tok<OUT, N, W>(a, ch.t0, dd, n0, nxt);
-  for (int t = 0; t < ch.len; ++t) {
-    cur = nxt;
-    if (t + 1 < ch.len) m1_load_tok<OUT, N, W>(a, ch.t0 + t + 1, dd, n0, nxt);
-    float v = cb;
+
+  float px[PP], pdt[PP], pz[OUT ? PP : 1], pB[BPT], pC[OUT ? BPT : 1];
+  auto fetch = [&](int r0, int nb) {
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) v += w[k] * win[k];
-    v += w[W - 1] * cur.u;
-#pragma unroll
-    for (int k = 0; k < W - 2; ++k) win[k] = win[k + 1];
-    win[W - 2] = cur.u;
-    const float xv = silu(v);
-    const float dl = softplus(cur.dt + bias);
-    const float dx = dl * xv;
-    sumd += dl;
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < kM1PV; ++e) {
-      h[e] = __builtin_amdgcn_exp2f(dl * A2[e]) * h[e] + dx * cur.B[e];
-      if (OUT) part += h[e] * cur.C[e];
+    for (int m = 0; m < PP; ++m) {
+      const int r = pr0 + m * RS;
+      if (r < nb && pon) {
+        const int64_t row = ch.t0 + r0 + r;
+        px[m] = m1_ld<TI>(a.x, row * a.x_stride + pd);
+        pdt[m] = m1_ld<TI>(a.dt, row * a.dt_stride + pd);
+        if (OUT) pz[m] = m1_ld<TI>(a.z, row * a.z_stride + pd);
+      }
     }
-    if (OUT) {
 #pragma unroll
-      for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
-      if (on && sub == 0)
-        store_any(a.y, (int64_t)(ch.t0 + t) * a.y_stride + d, (part + Dd * xv) * silu(cur.z), a.y_bf16);
-      if (a.ckpt_interval > 0 && on) {
-        const int64_t p = (int64_t)sq.start_pos + ch.tau0 + t + 1;
-        if (p % a.ckpt_interval == 0) {
-          const int64_t k = p / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
-          if (k >= 0 && k < sq.nck) {
-            const int slot = a.ck[sq.ck0 + k];
-            if (slot >= 0 && slot < a.num_slots) store_state(slot);
+    for (int m = 0; m < BPT; ++m) {
+      const int i = tid + 256 * m, r = i / N, n = i % N;
+      if (r < nb) {
+        const int64_t row = ch.t0 + r0 + r;
+        pB[m] = m1_ld<TI>(a.B, row * a.B_stride + n);
+        if (OUT) pC[m] = m1_ld<TI>(a.C, row * a.C_stride + n);
+      }
+    }
+  };
+
+  float sumd = 0.f;
+  fetch(0, ch.len < TB ? ch.len : TB);
+  for (int r0 = 0; r0 < ch.len; r0 += TB) {
+    const int nb = ch.len - r0 < TB ? ch.len - r0 : TB;
+    // stage the block's raw rows (rows past nb are left alone: the ring still holds older rows
+    // that the final window may need)
+#pragma unroll
+    for (int m = 0; m < PP; ++m) {
+      const int r = pr0 + m * RS;
+      if (r < nb) xs[(r0 + r + W - 1) & (R - 1)][pc] = pon ? px[m] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < BPT; ++m) {
+      const int i = tid + 256 * m, r = i / N;
+      if (r < nb) {
+        s_B[r][i % N] = pB[m];
+        if (OUT) s_C[r][i % N] = pC[m];
+      }
+    }
+    __syncthreads();
+    // per (token, channel): conv over the ring, Delta, Delta x, D x, silu(z)
+#pragma unroll
+    for (int m = 0; m < PP; ++m) {
+      const int r = pr0 + m * RS;
+      if (r < nb) {
+        float v = cb;
+#pragma unroll
+        for (int k = 0; k < W; ++k) v += w[k] * xs[(r0 + r + k) & (R - 1)][pc];
+        const float xv = silu(v);
+        const float dl = m1_softplus((pon ? pdt[m] : 0.f) + bias);
+        s_dl[r][pc] = dl;
+        s_dx[r][pc] = dl * xv;
+        if (OUT) {
+          s_dy[r][pc] = Dd * xv;
+          s_sz[r][pc] = silu(pon ? pz[m] : 0.f);
+        }
+      }
+    }
+    if (r0 + TB < ch.len) fetch(r0 + TB, ch.len - r0 - TB < TB ? ch.len - r0 - TB : TB);
+    __syncthreads();
+    for (int t = 0; t < nb; ++t) {
+      const float dl = s_dl[t][rc], dx = s_dx[t][rc];
+      float Bv[kM1PV];
+#pragma unroll
+      for (int e = 0; e < kM1PV; ++e) Bv[e] = s_B[t][n0 + e];
+#pragma unroll
+      for (int e = 0; e < kM1PV; ++e) h[e] = __builtin_amdgcn_exp2f(dl * A2[e]) * h[e] + dx * Bv[e];
+      if (!OUT) {
+        sumd += dl;
+      } else {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < kM1PV; ++e) part += h[e] * s_C[t][n0 + e];
+#pragma unroll
+        for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
+        if (ron && sub == 0)
+          store_any(a.y, (int64_t)(ch.t0 + r0 + t) * a.y_stride + rd, (part + s_dy[t][rc]) * s_sz[t][rc], a.y_bf16);
+        if (a.ckpt_interval > 0 && ron) {
+          const int64_t p = (int64_t)sq.start_pos + ch.tau0 + r0 + t + 1;
+          if (p % a.ckpt_interval == 0) {
+            const int64_t k = p / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
+            if (k >= 0 && k < sq.nck) {
+              const int slot = a.ck[sq.ck0 + k];
+              if (slot >= 0 && slot < a.num_slots) store_state(slot, r0 + t);
+            }
           }
         }
       }
     }
+    __syncthreads();
   }
-  if (!on) return;
+  if (!ron) return;
   if (OUT) {
-    if (ch.tau0 + ch.len == sq.len) store_state(sq.slot);
+    if (last) store_state(sq.slot, ch.len - 1);
   } else {
-    float* s = a.S + ((int64_t)ci * D + d) * N + n0;
+    float* s = a.S + ((int64_t)ci * D + rd) * N + n0;
 #pragma unroll
     for (int e = 0; e < kM1PV; ++e) s[e] = h[e];
-    if (sub == 0) a.SD[(int64_t)ci * D + d] = sumd;
+    if (sub == 0) a.SD[(int64_t)ci * D + rd] = sumd;
   }
 }
 
@@ -288,20 +374,22 @@ __global__ __launch_bounds__(256) void mamba1_pass_kernel(Mamba1PrefillParams a,
   const int d = (int)(i / N);
   float h = sq.has_init ? to_f32(static_cast<const TS*>(a.ssm)[(int64_t)sq.slot * DN + i]) : 0.f;
   const float A2 = a.A[i] * 1.4426950408889634f;
-  for (int cj = sq.chunk0; cj < a.num_chunks && a.chunks[cj].seq == (int)blockIdx.y; ++cj) {
+  for (int cj = sq.chunk0;; ++cj) {
     a.Hin[(int64_t)cj * DN + i] = h;
+    const M1Chunk c = a.chunks[cj];
+    if (c.tau0 + c.len == sq.len) break;
     h = __builtin_amdgcn_exp2f(A2 * a.SD[(int64_t)cj * a.D + d]) * h + a.S[(int64_t)cj * DN + i];
   }
 }
 
-template <typename TS, int N>
+template <typename TS, typename TI, int N>
 static hipError_t launch_m1p_n(const Mamba1PrefillParams& a, int W, hipStream_t s) {
-  constexpr int CPW = kM1PThreads / (N / kM1PV);
+  constexpr int CPW = 256 / (N / kM1PV);
   const dim3 gc((a.D + CPW - 1) / CPW, a.num_chunks), gp((unsigned)(((int64_t)a.D * N + 255) / 256), a.num_seqs);
-#define M1P_W(WW)                                                                                   \
-  hipLaunchKernelGGL((mamba1_chunk_kernel<TS, false, N, WW>), gc, dim3(kM1PThreads), 0, s, a);      \
-  hipLaunchKernelGGL((mamba1_pass_kernel<TS>), gp, dim3(256), 0, s, a, N);                          \
-  hipLaunchKernelGGL((mamba1_chunk_kernel<TS, true, N, WW>), gc, dim3(kM1PThreads), 0, s, a);
+#define M1P_W(WW)                                                                               \
+  hipLaunchKernelGGL((mamba1_chunk_kernel<TS, TI, false, N, WW>), gc, dim3(256), 0, s, a);          \
+  hipLaunchKernelGGL((mamba1_pass_kernel<TS>), gp, dim3(256), 0, s, a, N);                      \
+  hipLaunchKernelGGL((mamba1_chunk_kernel<TS, TI, true, N, WW>), gc, dim3(256), 0, s, a);
   switch (W) {
     case 2: M1P_W(2) break;
     case 3: M1P_W(3) break;
@@ -312,22 +400,23 @@ static hipError_t launch_m1p_n(const Mamba1PrefillParams& a, int W, hipStream_t 
   return hipGetLastError();
 }
 
-template <typename TS>
+template <typename TS, typename TI>
 static hipError_t launch_m1p(const Mamba1PrefillParams& a, int N, int W, hipStream_t s) {
   switch (N) {
-    case 8: return launch_m1p_n<TS, 8>(a, W, s);
-    case 16: return launch_m1p_n<TS, 16>(a, W, s);
-    case 32: return launch_m1p_n<TS, 32>(a, W, s);
-    case 64: return launch_m1p_n<TS, 64>(a, W, s);
-    case 128: return launch_m1p_n<TS, 128>(a, W, s);
-    case 256: return launch_m1p_n<TS, 256>(a, W, s);
+    case 8: return launch_m1p_n<TS, TI, 8>(a, W, s);
+    case 16: return launch_m1p_n<TS, TI, 16>(a, W, s);
+    case 32: return launch_m1p_n<TS, TI, 32>(a, W, s);
+    case 64: return launch_m1p_n<TS, TI, 64>(a, W, s);
+    case 128: return launch_m1p_n<TS, TI, 128>(a, W, s);
+    case 256: return launch_m1p_n<TS, TI, 256>(a, W, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_mamba1_prefill(const Mamba1PrefillParams& a, int N, int W, hipStream_t s) {
   if (a.num_chunks == 0) return hipSuccess;
-  return a.ssm_bf16 ? launch_m1p<bf16>(a, N, W, s) : launch_m1p<float>(a, N, W, s);
+  if (a.ssm_bf16) return a.io_bf16 ? launch_m1p<bf16, bf16>(a, N, W, s) : launch_m1p<bf16, float>(a, N, W, s);
+  return a.io_bf16 ? launch_m1p<float, bf16>(a, N, W, s) : launch_m1p<float, float>(a, N, W, s);
 }
 
 }  // namespace m2
