@@ -75,10 +75,12 @@ def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
     import glob
 
     def per_dispatch(d, part):
+        # part: a substring of the kernel name, or a tuple of alternatives (mangled and demangled)
+        parts = part if isinstance(part, tuple) else (part,)
         acc, names = {}, set()
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
         for r in csv.DictReader(open(f)):
-            if part in r["Kernel_Name"]:
+            if any(p in r["Kernel_Name"] for p in parts):
                 acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
                 names.add(r["Kernel_Name"])
         return list(acc.values()), sorted(names)
@@ -88,7 +90,8 @@ def write_traffic_record(root: str, fetch_dir: str, write_dir: str) -> dict:
     cp_f = [v for v in per_dispatch(fetch_dir, "slot_copy_kernel")[0] if v > 10000]   # the timed copies
     cp_w = [v for v in per_dispatch(write_dir, "slot_copy_kernel")[0] if v > 10000]
     fs, ws = known / avg(cp_f), known / avg(cp_w)
-    dec_f, dec_w = per_dispatch(fetch_dir, "decode_kernel")[0], per_dispatch(write_dir, "decode_kernel")[0]
+    dec_name = ("_ZN2m213decode_kernel", "m2::decode_kernel<")   # not the Mamba1 or multi-token decode
+    dec_f, dec_w = per_dispatch(fetch_dir, dec_name)[0], per_dispatch(write_dir, dec_name)[0]
     dec = {"kernel": "decode_kernel<bf16, N=128, W=4>", "workload": "decode step, 256 sequences, Nemotron-H layer shape",
            "source_sha256": source_sha(root, DECODE_SOURCES), "sources": DECODE_SOURCES,
            "fetch_kib_per_launch": avg(dec_f), "write_kib_per_launch": avg(dec_w), "fetch_scale": fs,

@@ -379,6 +379,13 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
   if (m2_status st = check_io(io, 6)) return st;
   if (!m2::decode_supported(pool->d.ssm_dtype == M2_BF16, sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "decode supports d_state in {16,32,64,128,256}, got %d", sh.N);
+  {
+    // the decode workgroup keeps its group's x and gate rows, B, C, Delta and alpha in LDS (fp32)
+    const int64_t hpg = sh.H / sh.G;
+    if (4 * (2 * hpg * sh.P + 2 * sh.N + 2 * hpg) > 65536)
+      return fail(M2_ERR_UNSUPPORTED, "decode needs (H/G)*head_dim <= %d per group, got %lld",
+                  (int)((65536 / 4 - 2 * sh.N - 2 * hpg) / 2), (long long)(hpg * sh.P));
+  }
   if (slots_host) {
     std::vector<uint8_t> seen(pool->d.num_slots, 0);
     for (int i = 0; i < batch; ++i) {

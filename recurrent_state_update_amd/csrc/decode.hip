@@ -4,7 +4,7 @@
 // Phase 1 shifts the conv window of the group's channels (x of its heads,
 // then its B and C), applies the depthwise conv and SiLU, and stages the
 // activations in LDS, together with Delta = softplus(dt + dt_bias) and
-// alpha = exp(Delta * A) for its heads.  Phase 2 streams the (P, N) state of
+// alpha = exp(Delta * A) for its heads and the gate SiLU(z) of its rows.  Phase 2 streams the (P, N) state of
 // each head through HBM with 16-byte loads: every lane owns one 16-byte
 // column slice of a state row, updates h' = alpha h + Delta x B, accumulates
 // h' C, and writes h' back rounded to the state dtype.  The reduction over N
@@ -96,6 +96,7 @@ void decode_kernel(DecodeParams a) {
   float* s_act = smem;                  // [x of the group's heads | B_g | C_g]
   float* s_delta = smem + nx + 2 * N;   // [hpg]
   float* s_alpha = s_delta + hpg;       // [hpg]
+  float* s_gate = s_alpha + hpg;        // [nx] SiLU(z) of the group's rows
 
   // ---------------------------------------------------------------- state geometry
   const int sub = lane % LPR;
@@ -126,8 +127,19 @@ void decode_kernel(DecodeParams a) {
   // the conv phase so that its latency overlaps it
   vec_t data[U], next[U];
   if (ntile > 0) load_tile(0, next);
-  // ---------------------------------------------------------------- conv
+  // ---------------------------------------------------------------- gate
+  // SiLU(z) of the group's rows goes to LDS here, by the threads the conv pass leaves idle (all
+  // threads when it leaves none), so that the state loop issues no global load besides the
+  // state: a z load there would wait for the prefetched tile ahead of it in the memory counter.
   const int nch = nx + 2 * N;
+  {
+    const int nconv = (nch + 7) / 8 < (int)blockDim.x ? (nch + 7) / 8 : (int)blockDim.x;
+    const int zn = nconv < (int)blockDim.x ? (int)blockDim.x - nconv : (int)blockDim.x;
+    const int zt = nconv < (int)blockDim.x ? tid - nconv : tid;
+    for (int i = zt; zt >= 0 && i < nx; i += zn)
+      s_gate[i] = silu(load_any(a.z, b * a.z_stride + g * nx + i, a.io_bf16));
+  }
+  // ---------------------------------------------------------------- conv
   for (int ck = tid * 8; ck < nch; ck += blockDim.x * 8) {
     const void* src;
     int64_t si;
@@ -262,8 +274,7 @@ void decode_kernel(DecodeParams a) {
         if (row < P) {
           const int64_t ci = (int64_t)h * P + row;
           const float yv = acc[k] + Dh * xs[row];
-          const float zv = load_any(a.z, b * a.z_stride + ci, a.io_bf16);
-          store_any(a.y, b * a.y_stride + ci, yv * silu(zv), a.y_bf16);
+          store_any(a.y, b * a.y_stride + ci, yv * s_gate[hl * P + row], a.y_bf16);
         }
       }
     }
@@ -273,7 +284,7 @@ void decode_kernel(DecodeParams a) {
 template <typename TS, int N>
 static hipError_t launch_w(const DecodeParams& p, int W, int batch, hipStream_t s) {
   const int hpg = p.H / p.G;
-  const size_t lds = sizeof(float) * (hpg * p.P + 2 * N + 2 * hpg);
+  const size_t lds = sizeof(float) * (2 * hpg * p.P + 2 * N + 2 * hpg);
   const dim3 grid(p.G, batch), block(kDecodeThreads);
   switch (W) {
     case 2: hipLaunchKernelGGL((decode_kernel<TS, N, 2>), grid, block, lds, s, p); break;

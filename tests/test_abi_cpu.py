@@ -159,6 +159,16 @@ def test_decode_rejects_unsupported_state_size():
     lib().mamba2_pool_destroy(h)
 
 
+def test_decode_rejects_a_group_too_wide_for_the_workgroup_lds():
+    """The decode workgroup holds its group's x and gate rows in LDS (64 KiB budget): one group of
+    128 heads of 128 rows (16384 per group) is refused before anything is launched."""
+    st, h = create(make_desc(H=128, P=128, N=128, G=1))
+    assert st == 0
+    assert decode(h, xs=16384, Bs=128, Cs=128, zs=16384, ys=16384) == UNSUP
+    assert "per group" in lib().mamba2_last_error().decode()
+    lib().mamba2_pool_destroy(h)
+
+
 def prefill(h, cu, slots, has_init=None, start=None, ck=None, max_ck=0, interval=0, chunk=256,
             ws=FAKE, ws_bytes=1 << 40, **kw):
     n = len(slots)
