@@ -99,7 +99,7 @@ def test_mamba1_decode_at_the_7b_width_256_of_512_slots():
 
 
 def _m1_prefill_case(D, N, W, ssm_dtype, Q, lens, has_init, start_pos, interval, ck, seed, L=2, S=16,
-                     layer=1, slots=None, draw_rows=0):
+                     layer=1, slots=None, draw_rows=0, io=None):
     """Run one Mamba1 prefill on the GPU and on the oracle from the same seeded pool and rows."""
     rng = np.random.default_rng(seed)
     params = synth.mamba1_layer_params(rng, D, N, W)
@@ -116,7 +116,7 @@ def _m1_prefill_case(D, N, W, ssm_dtype, Q, lens, has_init, start_pos, interval,
     before_s, before_c = _raw(pool.ssm), _raw(pool.conv)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
-    io = ssm_dtype
+    io = io or ssm_dtype
     x, z, dt, Bm, Cm = (r[:T] for r in synth.mamba1_tokens(rng, max(T, draw_rows), D, N, io))
     y = torch.full((T, D), float("nan"), dtype=TD[ssm_dtype], device="cuda")
     pool.mamba1_prefill(layer, weights(params), cu, slots, has_init, dev(x, io), dev(Bm, io), dev(Cm, io),
@@ -168,6 +168,22 @@ def test_mamba1_prefill_matches_the_oracle(D, N, W, ssm_dtype, Q):
     live[1, sorted(written)] = True
     for t, b in ((pool.ssm, before_s), (pool.conv, before_c)):
         assert torch.equal(t.view(torch.uint8).view(2, 16, -1)[~live], b.view(2, 16, -1)[~live])
+
+
+@pytest.mark.parametrize("ssm_dtype,io", [("f32", "bf16"), ("bf16", "f32")])
+def test_mamba1_prefill_with_rows_in_the_other_dtype(ssm_dtype, io):
+    """Rows in bf16 with an fp32 state and the reverse (y in the state dtype): outputs, final and
+    checkpoint states against the oracle."""
+    D, N, W = 64, 32, 4
+    lens = [90, 1, 40]
+    ck = np.array([[9, 10, -1], [-1, -1, -1], [11, -1, -1]], np.int32)
+    log(f"case: Mamba1 prefill ssm={ssm_dtype} io={io}")
+    pool, ref, y, y_ref, _, _ = _m1_prefill_case(D, N, W, ssm_dtype, 32, lens, [1, 0, 1],
+                                                 np.array([0, 3, 0], np.int32), 32, ck, 940, io=io)
+    assert rel_err(y, y_ref) <= TOL[ssm_dtype]
+    for s in (3, 4, 5, 9, 10, 11):
+        assert rel_err(host(pool.ssm[1, s, :, 0]), ref.ssm[1, s]) <= TOL[ssm_dtype], s
+        assert np.array_equal(host(pool.conv[1, s]), ref.conv[1, s]), s
 
 
 def test_mamba1_prefill_chunk_size_and_batch_invariance():
