@@ -5,7 +5,7 @@
 // and state index exp(Delta_d A[d][n]), B and C shared by all channels, the
 // short conv over the D channels of x.
 //
-// One workgroup of 256 threads covers a block of channels of one sequence.
+// One workgroup of 1024 threads covers a block of channels of one sequence.
 // Phase 1: one thread per channel shifts the conv window, convolves, applies
 // SiLU and softplus, and stages x_d and Delta_d in LDS with the row's B and C.
 // Phase 2: a channel's N state values are split over N/VEC lanes, each with one
@@ -18,7 +18,7 @@
 
 namespace m2 {
 
-constexpr int kM1Threads = 256;
+constexpr int kM1Threads = 1024;
 
 template <typename T> struct M1Vec;
 template <> struct M1Vec<float> { typedef floatx4 type; };
