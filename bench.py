@@ -144,7 +144,7 @@ def main() -> int:
         print(json.dumps(rec))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the decode step shards by "
               "sequence and needs no collective); run with --gpus 1", file=sys.stderr)
         return 2
 
