@@ -50,7 +50,8 @@ Checkpoints may also be held in an int8 store apart from the pool ([SSM-hybrids]
 SGLang int8 checkpoint passage): see int8_quantize below for the arithmetic.
 Several decode tokens per sequence with a snapshot after each (speculative decode):
 decode_multi.  A second recurrent family on the same kind of pool, Mamba1 with a (D, N)
-state: Mamba1PoolRef and mamba1_decode_step.
+state: Mamba1PoolRef, mamba1_decode_step and mamba1_prefill (the same token recurrence
+over packed sequences with the prefill's rounding and checkpoint rules).
 
 Parity pins live in the test suite (matrix form of [notes] "Mamba and
 Attention", constant-input closed form, scipy lfilter scalar case,
@@ -59,7 +60,9 @@ int8 store: states built from known codes and power-of-two scales, halves
 rounding to even, the half-step error bound, the page's ~2x capacity, and the
 restored error evolving through the decay product; for multi-token decode: a prefill
 that checkpoints after every token; for Mamba1: equality with the Mamba2 step when
-the decay does not depend on the state index, and the constant-input closed form).
+the decay does not depend on the state index, the constant-input closed form, and a
+prefill equal to its rows as decode steps with an initial-state perturbation evolving
+through the product of the decays).
 """
 from __future__ import annotations
 
