@@ -1,4 +1,4 @@
-"""GPU parity of the Mamba1 decode step (the pool's second state family) against the oracle."""
+"""GPU parity of the Mamba1 decode step and prefill (the pool's second state family) against the oracle."""
 import numpy as np
 import pytest
 import torch
