@@ -379,13 +379,9 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
   if (m2_status st = check_io(io, 6)) return st;
   if (!m2::decode_supported(pool->d.ssm_dtype == M2_BF16, sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "decode supports d_state in {16,32,64,128,256}, got %d", sh.N);
-  {
-    // the decode workgroup keeps its group's x and gate rows, B, C, Delta and alpha in LDS (fp32)
-    const int64_t hpg = sh.H / sh.G;
-    if (4 * (2 * hpg * sh.P + 2 * sh.N + 2 * hpg) > 65536)
-      return fail(M2_ERR_UNSUPPORTED, "decode needs (H/G)*head_dim <= %d per group, got %lld",
-                  (int)((65536 / 4 - 2 * sh.N - 2 * hpg) / 2), (long long)(hpg * sh.P));
-  }
+  if (m2::decode_lds_bytes(sh.H / sh.G, sh.P, sh.N) > m2::kMaxLdsBytes)
+    return fail(M2_ERR_UNSUPPORTED, "decode: a group of %d heads x %d rows needs more LDS per workgroup than %zu bytes",
+                sh.H / sh.G, sh.P, m2::kMaxLdsBytes);
   if (slots_host) {
     std::vector<uint8_t> seen(pool->d.num_slots, 0);
     for (int i = 0; i < batch; ++i) {
@@ -711,6 +707,9 @@ m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_param
   if (batch < 0) return fail(M2_ERR_ARG, "batch %d is negative", batch);
   if (num_tokens < 1 || num_tokens > m2::kMaxDecodeTokens)
     return fail(M2_ERR_UNSUPPORTED, "num_tokens must be in [1, %d], got %d", m2::kMaxDecodeTokens, num_tokens);
+  if (m2::multi_decode_lds_bytes(pool->sh.H / pool->sh.G, pool->sh.P, pool->sh.N, num_tokens) > m2::kMaxLdsBytes)
+    return fail(M2_ERR_UNSUPPORTED, "multi-token decode: %d tokens of a %d-head x %d-row group need more LDS per "
+                "workgroup than %zu bytes", num_tokens, pool->sh.H / pool->sh.G, pool->sh.P, m2::kMaxLdsBytes);
   if (m2_status st = check_params(pool, params)) return st;
   if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
   if (batch == 0) return ok();

@@ -284,14 +284,24 @@ void decode_kernel(DecodeParams a) {
 template <typename TS, int N>
 static hipError_t launch_w(const DecodeParams& p, int W, int batch, hipStream_t s) {
   const int hpg = p.H / p.G;
-  const size_t lds = sizeof(float) * (2 * hpg * p.P + 2 * N + 2 * hpg);
+  const size_t lds = decode_lds_bytes(hpg, p.P, N);
   const dim3 grid(p.G, batch), block(kDecodeThreads);
+#define D_LAUNCH(WW)                                                                                      \
+  {                                                                                                       \
+    if (lds > 65536) {                                                                                    \
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<TS, N, WW>),  \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
+      if (e != hipSuccess) return e;                                                                      \
+    }                                                                                                     \
+    hipLaunchKernelGGL((decode_kernel<TS, N, WW>), grid, block, lds, s, p);                              \
+  }
   switch (W) {
-    case 2: hipLaunchKernelGGL((decode_kernel<TS, N, 2>), grid, block, lds, s, p); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<TS, N, 3>), grid, block, lds, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<TS, N, 4>), grid, block, lds, s, p); break;
+    case 2: D_LAUNCH(2) break;
+    case 3: D_LAUNCH(3) break;
+    case 4: D_LAUNCH(4) break;
     default: return hipErrorInvalidValue;
   }
+#undef D_LAUNCH
   return hipGetLastError();
 }
 

@@ -35,6 +35,12 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams& p, int N, int W, int batch, hipStream_t s);
 bool decode_supported(int ssm_bf16, int N, int W);
+// LDS of one decode workgroup: its group's x and gate rows, B, C, Delta and alpha (fp32).  Up to
+// kMaxLdsBytes per workgroup on gfx950 (above 64 KiB the launch raises the kernel's limit).
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+inline size_t decode_lds_bytes(int hpg, int P, int N) {
+  return sizeof(float) * (2 * (size_t)hpg * P + 2 * (size_t)N + 2 * (size_t)hpg);
+}
 
 // Slot-to-slot copy of both state objects in one launch: for each object, bytes_per_slot bytes at
 // base + layer*num_slots*bytes_per_slot + slot*bytes_per_slot, for layers [l0, l0+nl).  Byte

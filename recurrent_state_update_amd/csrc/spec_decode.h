@@ -15,5 +15,11 @@ struct MultiDecodeParams {
   int K;
 };
 hipError_t launch_decode_multi(const MultiDecodeParams& p, int N, int W, int batch, hipStream_t s);
+// LDS of one multi-token workgroup: per token the group's activations, Delta, alpha and gate rows,
+// and the output slots (at most kMaxLdsBytes).
+inline size_t multi_decode_lds_bytes(int hpg, int P, int N, int K) {
+  return sizeof(float) * ((size_t)K * (2 * (size_t)hpg * P + 2 * (size_t)N) + 2 * (size_t)K * hpg) +
+         sizeof(int) * (size_t)K;
+}
 
 }  // namespace m2

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kMultiThreads) void decode_multi_kernel(MultiDecode
   float* s_delta = smem + K * nch;         // [K][hpg]
   float* s_alpha = s_delta + K * hpg;      // [K][hpg]
   int* s_out = reinterpret_cast<int*>(s_alpha + K * hpg);   // [K] output slot per token (-1: none)
+  float* s_gate = reinterpret_cast<float*>(s_out + K);      // [K][nx] SiLU(z) of the group's rows
 
   if (tid < K) {
     const int o = m.slots_out[(int64_t)b * K + tid];
@@ -125,6 +126,20 @@ __global__ __launch_bounds__(kMultiThreads) void decode_multi_kernel(MultiDecode
   };
   vec_t data[U], next[U];
   if (ntile > 0) load_tile(0, next);
+
+  // ---------------------------------------------------------------- gate
+  // SiLU(z) of the group's rows for every token goes to LDS here, by the threads the conv pass
+  // leaves idle (all threads when it leaves none): a z load in the state loop would be issued
+  // after the next tile's state loads and, the memory counter being in order, wait for them.
+  {
+    const int nconv = (nch + 3) / 4 < (int)blockDim.x ? (nch + 3) / 4 : (int)blockDim.x;
+    const int zn = nconv < (int)blockDim.x ? (int)blockDim.x - nconv : (int)blockDim.x;
+    const int zt = nconv < (int)blockDim.x ? tid - nconv : tid;
+    for (int i = zt; zt >= 0 && i < K * nx; i += zn) {
+      const int t = i / nx, c = i - t * nx;
+      s_gate[i] = silu(load_any(a.z, (int64_t)(b * K + t) * a.z_stride + (int64_t)g * nx + c, a.io_bf16));
+    }
+  }
 
   // ---------------------------------------------------------------- conv over the K tokens
   // four channels per thread (what stays live across the token loop is their taps and windows)
@@ -288,8 +303,7 @@ __global__ __launch_bounds__(kMultiThreads) void decode_multi_kernel(MultiDecode
           if (row < P) {
             const int64_t ci = (int64_t)h * P + row;
             const float yv = acc[k] + Dh * xs[row];
-            const float zv = load_any(a.z, (int64_t)(b * K + t) * a.z_stride + ci, a.io_bf16);
-            store_any(a.y, (int64_t)(b * K + t) * a.y_stride + ci, yv * silu(zv), a.y_bf16);
+            store_any(a.y, (int64_t)(b * K + t) * a.y_stride + ci, yv * s_gate[t * nx + hl * P + row], a.y_bf16);
           }
         }
       }
@@ -301,14 +315,24 @@ template <typename TS, int N>
 static hipError_t launch_mw(const MultiDecodeParams& p, int W, int batch, hipStream_t s) {
   const DecodeParams& d = p.d;
   const int hpg = d.H / d.G;
-  const size_t lds = sizeof(float) * (p.K * (hpg * d.P + 2 * N) + 2 * p.K * hpg) + sizeof(int) * p.K;
+  const size_t lds = multi_decode_lds_bytes(hpg, d.P, N, p.K);
   const dim3 grid(d.G, batch), block(kMultiThreads);
+#define MW_LAUNCH(WW)                                                                                         \
+  {                                                                                                           \
+    if (lds > 65536) {                                                                                        \
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_multi_kernel<TS, N, WW>), \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);         \
+      if (e != hipSuccess) return e;                                                                          \
+    }                                                                                                         \
+    hipLaunchKernelGGL((decode_multi_kernel<TS, N, WW>), grid, block, lds, s, p);                            \
+  }
   switch (W) {
-    case 2: hipLaunchKernelGGL((decode_multi_kernel<TS, N, 2>), grid, block, lds, s, p); break;
-    case 3: hipLaunchKernelGGL((decode_multi_kernel<TS, N, 3>), grid, block, lds, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_multi_kernel<TS, N, 4>), grid, block, lds, s, p); break;
+    case 2: MW_LAUNCH(2) break;
+    case 3: MW_LAUNCH(3) break;
+    case 4: MW_LAUNCH(4) break;
     default: return hipErrorInvalidValue;
   }
+#undef MW_LAUNCH
   return hipGetLastError();
 }
 

@@ -160,12 +160,18 @@ def test_decode_rejects_unsupported_state_size():
 
 
 def test_decode_rejects_a_group_too_wide_for_the_workgroup_lds():
-    """The decode workgroup holds its group's x and gate rows in LDS (64 KiB budget): one group of
-    128 heads of 128 rows (16384 per group) is refused before anything is launched."""
-    st, h = create(make_desc(H=128, P=128, N=128, G=1))
+    """The decode workgroup holds its group's x and gate rows in LDS (160 KiB per workgroup): one
+    group of 256 heads of 128 rows (32768 per group, 256 KiB) is refused before anything is
+    launched; the multi-token decode's per-token share is checked the same way."""
+    st, h = create(make_desc(H=256, P=128, N=128, G=1))
     assert st == 0
-    assert decode(h, xs=16384, Bs=128, Cs=128, zs=16384, ys=16384) == UNSUP
-    assert "per group" in lib().mamba2_last_error().decode()
+    assert decode(h, xs=32768, Bs=128, Cs=128, zs=32768, dts=256, ys=32768) == UNSUP
+    assert "LDS" in lib().mamba2_last_error().decode()
+    lib().mamba2_pool_destroy(h)
+    st, h = create(make_desc(H=128, P=64, N=128, G=1))   # 8192 rows: decode fits, 8 tokens do not
+    assert st == 0
+    assert decode_multi(h, k=8, xs=8192, Bs=128, Cs=128, zs=8192, ys=8192) == UNSUP
+    assert "LDS" in lib().mamba2_last_error().decode()
     lib().mamba2_pool_destroy(h)
 
 
