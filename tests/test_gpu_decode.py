@@ -143,8 +143,9 @@ def test_fp32_state_decode_at_8b_shape():
 
 
 # (heads, head_dim, d_state, groups, conv kernel): every supported d_state, head_dim other than 64,
-# group counts other than a power of two and every conv width
-DECODE_SHAPES = [(4, 32, 32, 2, 2), (6, 64, 64, 3, 3), (4, 128, 256, 1, 4), (8, 16, 16, 4, 4)]
+# group counts other than a power of two, every conv width, and one group of 128 heads (a
+# workgroup with 67.6 KB of LDS, above the default 64 KiB limit)
+DECODE_SHAPES = [(4, 32, 32, 2, 2), (6, 64, 64, 3, 3), (4, 128, 256, 1, 4), (8, 16, 16, 4, 4), (128, 64, 128, 1, 4)]
 
 
 @pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda t: "H%dP%dN%dG%dW%d" % t)

@@ -119,13 +119,14 @@ def test_multi_token_decode_rejects_aliasing_host_slots():
                               slots_out_host=outs)
 
 
-def test_layer_shape_256_sequences_4_tokens_equals_single_steps():
-    """The Nemotron-H layer shape at the benchmark's size: 256 sequences of a 1280-slot bf16 pool,
-    4 tokens each (a verified token and 3 drafts), against 4 single-step launches over all rows."""
+@pytest.mark.parametrize("K,n", [(4, 256), (8, 64)])
+def test_layer_shape_equals_single_steps(K, n):
+    """The Nemotron-H layer shape: 256 sequences of a 1280-slot bf16 pool with 4 tokens each (a
+    verified token and 3 drafts; the benchmark's size), and 64 sequences with 8 tokens (75 KB of
+    LDS per workgroup, above the default 64 KiB), against K single-step launches over all rows."""
     w = synth.decode_workload(1)
     sh = w["shape"]
-    K, n = 4, 256
-    log("case: multi-token decode, 256 sequences x 4 tokens, Nemotron-H layer shape")
+    log(f"case: multi-token decode, {n} sequences x {K} tokens, Nemotron-H layer shape")
     g = torch.Generator(device="cuda")
     g.manual_seed(75)
     pool = make_pool(sh, 1, 1280, "bf16", "bf16", sentinel_seed=76)
