@@ -434,3 +434,42 @@ def test_mamba1_prefill_validation():
     assert call(h2) == UNSUP                                         # a Mamba2 pool
     lib().mamba2_pool_destroy(h2)
     lib().mamba2_pool_destroy(h)
+
+
+def test_header_is_plain_c_and_links_against_the_library(tmp_path):
+    """include/mamba2_pool.h compiles as C99 (no C++ in the ABI), and a C program that calls the
+    host-only entry points through it links against libmamba2pool.so and runs without a GPU."""
+    prog = tmp_path / "abi.c"
+    prog.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "mamba2_pool.h"
+int main(void) {
+  if (mamba2_abi_version() != 2) return 1;
+  m2_pool_desc d;
+  memset(&d, 0, sizeof d);
+  d.num_layers = 1; d.num_slots = 2; d.nheads = 4; d.head_dim = 8; d.d_state = 16; d.n_groups = 1;
+  d.conv_kernel = 4; d.ssm_dtype = M2_BF16; d.conv_dtype = M2_BF16;
+  d.ssm_base = (void*)0x7F0000000000ull; d.conv_base = (void*)0x7F0000000000ull;
+  d.ssm_bytes = 1ull * 2 * 4 * 8 * 16 * 2; d.conv_bytes = 1ull * 2 * (4 * 8 + 2 * 16) * 3 * 2;
+  m2_pool* p = 0;
+  if (mamba2_pool_create(&d, &p) != M2_OK) { printf("%s\n", mamba2_last_error()); return 2; }
+  uint64_t s = 0, c = 0;
+  if (mamba2_pool_info(p, &s, &c) != M2_OK || s != 4 * 8 * 16 * 2 || c != 64 * 3 * 2) return 3;
+  d.nheads = 3;                                          /* not a multiple of n_groups = 2 below */
+  d.n_groups = 2;
+  m2_pool* q = 0;
+  if (mamba2_pool_create(&d, &q) == M2_OK || strlen(mamba2_last_error()) == 0) return 4;
+  mamba2_pool_destroy(p);
+  printf("ok\n");
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    lib_dir = os.path.dirname(_ffi.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(prog),
+                        "-L", lib_dir, "-lmamba2pool", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
