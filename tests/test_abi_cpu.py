@@ -11,6 +11,7 @@ import json
 import os
 import re
 import subprocess
+import sys
 from ctypes import byref, c_uint64, c_void_p
 
 import numpy as np
@@ -473,3 +474,20 @@ int main(void) {
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With the shared library absent the binding raises instead of falling back to anything: run
+    in a fresh interpreter whose library path points at a file that does not exist."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from recurrent_state_update_amd import _ffi\n"
+            "_ffi.LIB_PATH = %r\n"
+            "try:\n"
+            "    _ffi.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n") % (ROOT, str(tmp_path / "missing.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "not built" in r.stdout
