@@ -312,14 +312,19 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              int64_t y_stride, int32_t y_dtype, void* stream);
 
 /* Workspace bytes mamba1_prefill needs (same arguments as
- * mamba2_prefill_workspace_size; max_ckpt is the width of the checkpoint table). */
+ * mamba2_prefill_workspace_size; max_ckpt is the width of the checkpoint table).
+ * Errors: M2_ERR_ARG (NULL, negative counts), M2_ERR_UNSUPPORTED (a Mamba2
+ * pool, chunk_size outside 16..4096), M2_ERR_SHAPE (size overflow). */
 m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
                                         int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
 
 /* Mamba1 prefill of packed sequences on a Mamba1 pool: the recurrence of
- * mamba1_decode_step over each sequence's rows, the state kept in fp32 between
- * tokens and rounded only into the final slot and the checkpoint slots (the
- * Mamba2 prefill's rules: cu_seqlens, slots, has_initial_state, start_pos,
+ * mamba1_decode_step ([notes] "Mamba" equations, Mamba1 shapes of the same
+ * page's state-shape table) over each sequence's rows, with the prefill and
+ * checkpoint behaviour [SSM-hybrids] describes for hybrid models (the
+ * chunked-prefill handoff and SGLang checkpoint passages).  The state is kept
+ * in fp32 between tokens and rounded only into the final slot and the
+ * checkpoint slots (the Mamba2 prefill's rules: cu_seqlens, slots, has_initial_state, start_pos,
  * ckpt_interval, ckpt_slots [num_seqs][max_ckpt] -- any interval and start
  * position).  Rows: x, z, dt [T][D] (x raw, before the conv), B, C [T][N]
  * (16-byte aligned with 16-byte multiple row strides), y [T][D].  The work
@@ -327,7 +332,12 @@ m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  * zero, a pass through each sequence's chunks, then every chunk again from its
  * entering state.  workspace: at least mamba1_prefill_workspace_size(...)
  * bytes, 256-byte aligned.  The launch tables go through the pool's pinned
- * staging buffer (the call may wait for the previous upload on the host). */
+ * staging buffer (the call may wait for the previous upload on the host).
+ * Errors: as mamba2_prefill_chunked (slot range, repeats and aliasing
+ * M2_ERR_SLOT; cu_seqlens M2_ERR_SHAPE; alignment M2_ERR_ALIGN; workspace
+ * M2_ERR_WORKSPACE), plus M2_ERR_UNSUPPORTED for a Mamba2 pool, d_state
+ * outside {8, 16, 32, 64, 128, 256} or more than 65535 chunks or sequences.
+ * On any error nothing is enqueued. */
 m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* params, int32_t num_seqs,
                          const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_initial_state,
                          const int32_t* start_pos, const void* x, int64_t x_stride, const void* B,
