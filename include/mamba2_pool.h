@@ -131,7 +131,12 @@ m2_status mamba2_pool_info(const m2_pool* pool, uint64_t* ssm_bytes_per_slot_lay
  *   z [batch][H*P], dt [batch][H] of io_dtype.
  *   y [batch][H*P] of y_dtype: out = (C h + D x) * SiLU(z), written for every row.
  * x, B, C must be 16-byte aligned with 16-byte multiple row strides.
- * Duplicated slots in one call race; pass slots_host to have them rejected. */
+ * Duplicated slots in one call race; pass slots_host to have them rejected.
+ * Errors: M2_ERR_ARG (NULL pool, params or slots, layer or batch out of
+ * range), M2_ERR_DTYPE, M2_ERR_ALIGN, M2_ERR_SLOT (with slots_host),
+ * M2_ERR_UNSUPPORTED (a Mamba1 pool, d_state outside {16, 32, 64, 128, 256},
+ * or a group of heads whose rows need more than 160 KiB of LDS), M2_ERR_HIP
+ * (launch failure).  On any error nothing is enqueued. */
 m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params* params,
                              int32_t batch, const int32_t* slots, const int32_t* slots_host,
                              const void* x, int64_t x_stride, const void* B, int64_t B_stride,
@@ -161,7 +166,8 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
  *   x, B, C, z, dt, y: as in mamba2_decode_step with batch*num_tokens rows,
  *              row b*num_tokens + t holding token t of sequence b.
  * Errors: as mamba2_decode_step, plus M2_ERR_UNSUPPORTED for num_tokens outside
- * 1..8 or batch > 65535. */
+ * 1..8, batch > 65535, or num_tokens whose per-token rows of one group need
+ * more than 160 KiB of LDS. */
 m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_params* params,
                               int32_t batch, int32_t num_tokens, const int32_t* slots_in,
                               const int32_t* slots_out, const int32_t* slots_in_host,
