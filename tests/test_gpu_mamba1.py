@@ -249,3 +249,20 @@ def test_mamba1_prefill_at_the_7b_width():
     for s in (0, 1, 2, 3, 8, 9, 10):
         assert rel_err(host(pool.ssm[0, s, :, 0]), ref.ssm[0, s]) <= TOL["bf16"], s
         assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+
+
+def test_mamba1_prefill_at_the_largest_chunk_size():
+    """chunk_size 4096 (the upper bound): a 5000-row sequence (two chunks, the second partial) and a
+    4096-row one (one full chunk), seeded, with checkpoints every 1000 positions, against the oracle."""
+    D, N, W = 32, 16, 4
+    lens = [5000, 4096]
+    ck = np.full((2, 6), -1, np.int32)
+    ck[0, :5] = [8, 9, 10, 11, 12]                    # positions 1000 .. 5000 of sequence 0
+    ck[1, :4] = [13, 14, 15, 2]                       # positions 1000 .. 4000 of sequence 1
+    log("case: Mamba1 prefill chunk 4096, lens 5000 and 4096")
+    pool, ref, y, y_ref, _, _ = _m1_prefill_case(D, N, W, "f32", 4096, lens, [1, 1], np.array([0, 0], np.int32),
+                                                 1000, ck, 990, L=1, S=16, layer=0, slots=[0, 1])
+    assert rel_err(y, y_ref) <= TOL["f32"]
+    for s in (0, 1, 2, 8, 9, 10, 11, 12, 13, 14, 15):
+        assert rel_err(host(pool.ssm[0, s, :, 0]), ref.ssm[0, s]) <= TOL["f32"], s
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
