@@ -1,6 +1,6 @@
 """CPU oracle (test infrastructure only; see oracle/mamba2.py)."""
-from .mamba2 import (PoolRef, checkpoint_states, conv_tokens, decode_step, prefill, round_to,
-                     silu, softplus, ssd_matrix_form, ssm_scan)
+from .mamba2 import (PoolRef, conv_tokens, decode_step, prefill, round_to, silu, softplus, ssd_matrix_form,
+                     ssm_scan)
 
-__all__ = ["PoolRef", "checkpoint_states", "conv_tokens", "decode_step", "prefill", "round_to",
-           "silu", "softplus", "ssd_matrix_form", "ssm_scan"]
+__all__ = ["PoolRef", "conv_tokens", "decode_step", "prefill", "round_to", "silu", "softplus", "ssd_matrix_form",
+           "ssm_scan"]

@@ -341,15 +341,6 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
     return round_to(out, y_dtype)
 
 
-def checkpoint_states(pool: PoolRef, layer: int, src, dst):
-    """Copy both state objects of slot src[i] into slot dst[i] (layer < 0: every layer)."""
-    layers = range(pool.ssm.shape[0]) if layer < 0 else [layer]
-    for l in layers:
-        for a, b in zip(src, dst):
-            pool.ssm[l, b] = pool.ssm[l, a]
-            pool.conv[l, b] = pool.conv[l, a]
-
-
 # --------------------------------------------------------------------------
 # int8 checkpoint store
 # --------------------------------------------------------------------------

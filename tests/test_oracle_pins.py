@@ -304,6 +304,52 @@ def test_checkpoints_equal_prefix_prefills():
     assert np.array_equal(pool2.ssm[0, 1], ref.ssm[0, 0])      # absolute position 8
 
 
+@pytest.mark.parametrize("shape,heads", [
+    (synth.Shape(6, 4, 8, 3, 4), [5, 0, 3]),         # three groups of two heads, one head of each, unsorted
+    (synth.Shape(8, 8, 16, 2, 3), [7, 1, 2]),        # two groups of four heads
+    (synth.Shape(4, 8, 8, 2, 2), [2]),               # a single head of the second group
+])
+def test_head_subset_prefill_equals_full_prefill(shape, heads):
+    """prefill(heads=...) runs the recurrence of the chosen heads only; their output columns,
+    final states and checkpoint states equal those of the full-head call, heads of other groups
+    included (the group map, the x, B, C channel selection and the z columns), and nothing else
+    of the states is written."""
+    rng = np.random.default_rng(71)
+    lens = [13, 1, 22]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    params, _, _, u, z, dt = synth.random_problem(rng, shape, T)
+    slots, has_init, start = [1, 4, 6], [1, 0, 1], [5, 0, 8]
+    ck = np.array([[2, 3, -1], [-1, -1, -1], [5, 7, 0]])
+    nslot = 10
+
+    def run(heads_arg):
+        pool = _fresh(shape, nslot, "f32")
+        r = np.random.default_rng(72)
+        pool.ssm[0] = r.standard_normal(pool.ssm[0].shape)
+        pool.conv[0] = r.standard_normal(pool.conv[0].shape)
+        before = pool.ssm.copy()
+        y = orc.prefill(pool, 0, params, cu, slots, has_init, start, u, z, dt, "f64", ckpt_interval=4,
+                        ckpt_slots=ck, heads=heads_arg)
+        return pool, before, y
+
+    full, _, y_full = run(None)
+    sub, before, y_sub = run(heads)
+    H, P = shape.nheads, shape.head_dim
+    other = [h for h in range(H) if h not in heads]
+    ys, yf = y_sub.reshape(T, H, P), y_full.reshape(T, H, P)
+    assert rel_err(ys[:, heads], yf[:, heads]) <= 1e-12
+    assert np.all(np.isnan(ys[:, other]))
+    written = set(slots) | {int(c) for c in ck.ravel() if c >= 0}
+    assert len(written) == 8                     # three finals and five checkpoints, all distinct
+    for s in written:
+        assert rel_err(sub.ssm[0, s][heads], full.ssm[0, s][heads]) <= 1e-12
+        assert np.array_equal(sub.ssm[0, s][other], before[0, s][other])    # other heads untouched
+        assert np.array_equal(sub.conv[0, s], full.conv[0, s])              # windows in full
+    for s in set(range(nslot)) - written:
+        assert np.array_equal(sub.ssm[0, s], before[0, s])
+
+
 def test_padding_rows_and_fresh_sequences_do_not_read_slots():
     shape = synth.TINY
     rng = np.random.default_rng(61)
