@@ -17,10 +17,12 @@ fourth the mixed continuous batch (32 prefills with checkpoints and 224
 decodes on one stream) and the 2 x 131072-token long context through all 48
 layer calls with fp32 state.
 
-Prints one JSON line.  `roofline.achieved` is the algorithmic bytes of one
-decode launch divided by its average duration, timed with HIP events on the
-stream the kernel runs on.  `cpu_baseline` is the fp64 CPU oracle on a bounded
-sample of the same decode step, single-threaded.
+Prints one JSON line.  The decode step is timed last, after the other legs,
+so that the GPU runs at its steady clocks.  `roofline.achieved` is the
+algorithmic bytes of one decode launch divided by its average duration, timed
+with HIP events on the stream the kernel runs on.  `cpu_baseline` is the fp64
+CPU oracle on bounded samples of the decode step and of the two prefill
+workloads, single-threaded, with the host's core count.
 """
 from __future__ import annotations
 
@@ -126,7 +128,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0, help="budget of the decode part of the CPU-oracle baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--write-traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -173,11 +175,31 @@ def main() -> int:
     def step():
         pool.decode_step(0, W, sl, x, B, C, z, dt, y)
 
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    legs = {}
+    # The other legs run first: the GPU reaches its steady clocks only after some 15 ms of
+    # continuous work (a cold start measured 201-202 us per decode step over the first 60 steps,
+    # 192 us afterwards), and the decode step is timed right after them.
+    if not args.no_checkpoint_copy:
+        legs["checkpoint_copy"] = checkpoint_copy_leg(pool, dev, stream, e0, e1)
+    if not args.no_int8_store:
+        legs["int8_checkpoint_store"] = int8_store_leg(pool, sh, dev, stream, e0, e1)
+    if not args.no_multi_decode:
+        legs["multi_token_decode"] = multi_token_decode(dev, stream, e0, e1, w)
+    if not args.no_mamba1:
+        legs["mamba1_decode"] = mamba1_decode(dev, stream, e0, e1)
+        legs["mamba1_prefill"] = mamba1_prefill_leg(dev, stream, e0, e1)
+    pw = None
+    if not args.no_prefill:
+        pw = synth.prefill_workload(2)
+        legs["prefill"] = prefill_leg(pw, dev, stream, e0, e1)
+        if not args.no_prefill_workloads:
+            legs["prefill_workloads"] = prefill_workloads(dev, stream, e0, e1)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -220,130 +242,137 @@ def main() -> int:
         },
     }
 
-    if not args.no_checkpoint_copy:
-        # checkpoint copy: COPY_PAIRS slot pairs, both state objects, slots [0, 256) -> [256, 512)
-        n = COPY_PAIRS
-        src = torch.arange(0, n, device=dev, dtype=torch.int32)
-        dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
-        for _ in range(2):
-            pool.checkpoint(0, src, dst)
-        torch.cuda.synchronize()
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            pool.checkpoint(0, src, dst)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / reps
-        ssm_b, conv_b = pool.info()
-        moved = 2 * n * (ssm_b + conv_b)
-        gbs = moved / (cms * 1e-3) / 1e9
-        out["checkpoint_copy"] = {
-            "workload": f"{n} slot-to-slot copies of both state objects (bf16, {ssm_b + conv_b} B per slot)",
-            "ms": cms, "copies_per_s": n / (cms * 1e-3), "bytes_per_launch": moved, "gbs": gbs,
-            "hbm_frac": gbs / HBM_PEAK_GBS,
-        }
+    if "checkpoint_copy" in legs:
         # the copy is also the measured ceiling a streaming kernel reaches on this part
-        out["roofline"]["copy_ceiling_gbs"] = gbs
-        out["roofline"]["frac_of_copy_ceiling"] = achieved / gbs
-
-    if not args.no_int8_store:
-        # int8 checkpoint store: 256 slots quantized into 256 entries, and restored into the other half
-        n = COPY_PAIRS
-        store = pool.int8_store(n)
-        sl = torch.arange(0, n, device=dev, dtype=torch.int32)
-        ent = torch.arange(0, n, device=dev, dtype=torch.int32)
-        dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
-        ssm_b, conv_b = pool.info()
-        codes_b = ssm_b // 2
-        scales_b = sh.nheads * sh.d_state * 4
-        put_bytes = n * (ssm_b + codes_b + scales_b + 2 * conv_b)       # read state + window, write entry
-        get_bytes = n * (codes_b + scales_b + ssm_b + 2 * conv_b)       # read entry, write state + window
-        res = {}
-        for name, fn, nbytes in (("put", lambda: pool.int8_put(store, 0, sl, ent), put_bytes),
-                                 ("get", lambda: pool.int8_get(store, 0, ent, dst), get_bytes)):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(10):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) / 10
-            res[name] = {"ms": t, "states_per_s": n / (t * 1e-3), "bytes_per_launch": nbytes,
-                         "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        res["workload"] = (f"{n} bf16 slots quantized into int8 store entries (put) and restored into fresh "
-                           "slots (get), Nemotron-H layer shape")
-        res["entry_bytes"] = codes_b + scales_b + conv_b
-        res["slot_bytes"] = ssm_b + conv_b
-        out["int8_checkpoint_store"] = res
-        del store
-
-    if not args.no_multi_decode:
-        out["multi_token_decode"] = multi_token_decode(dev, stream, e0, e1, w, ms)
-
-    if not args.no_mamba1:
-        out["mamba1_decode"] = mamba1_decode(dev, stream, e0, e1)
-        out["mamba1_prefill"] = mamba1_prefill_leg(dev, stream, e0, e1)
-
-    if not args.no_prefill:
-        pw = synth.prefill_workload(2)
-        psh = pw["shape"]
-        ppool = Pool.allocate(1, 32, psh.nheads, psh.head_dim, psh.d_state, psh.n_groups, psh.conv_kernel,
-                              torch.bfloat16, torch.bfloat16, dev)
-        PW = LayerWeights.from_numpy(pw["params"], dev)
-        pu = synth.to_torch(pw["u"], "bf16").to(dev)
-        pz = synth.to_torch(pw["z"], "bf16").to(dev)
-        pdt = synth.to_torch(pw["dt"], "bf16").to(dev)
-        T = pu.shape[0]
-        py = torch.empty((T, psh.intermediate), dtype=torch.bfloat16, device=dev)
-        px, pB, pC = ppool.split_xbc(pu)
-        ws = torch.empty(ppool.workspace_size(1, T, pw["chunk"]), dtype=torch.uint8, device=dev)
-
-        def pstep():
-            ppool.prefill(0, PW, pw["cu_seqlens"], [17], [0], px, pB, pC, pz, pdt, py,
-                          chunk_size=pw["chunk"], workspace=ws)
-
-        for _ in range(3):
-            pstep()
-        torch.cuda.synchronize()
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            pstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        pms = e0.elapsed_time(e1) / reps
-        flops = prefill_dense_flops_per_token(psh, pw["chunk"]) * T
-        io_bytes = T * (psh.conv_dim + psh.intermediate + psh.nheads + psh.intermediate) * 2 \
-            + psh.nheads * psh.head_dim * psh.d_state * 2 + psh.conv_dim * 3 * 2
-        out["prefill"] = {
-            "workload": "chunked prefill of one 8192-token sequence, chunk 256, same layer shape, bf16 state",
-            "ms": pms, "tokens_per_s": T / (pms * 1e-3),
-            "mfma_dense_tflops": flops / (pms * 1e-3) / 1e12,
-            "mfma_frac": flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "hbm_algorithmic_gbs": io_bytes / (pms * 1e-3) / 1e9,
-            "hbm_frac": io_bytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        }
-        # bytes the kernels move per call, intermediates included, from the committed counter record
-        ptraffic = measured_traffic(ROOT, "prefill_traffic.json", PREFILL_SOURCES, "traffic_bytes_per_call")
-        out["prefill"]["traffic"] = ptraffic
-        if ptraffic is not None:
-            out["prefill"]["traffic_gbs"] = ptraffic / (pms * 1e-3) / 1e9
-            out["prefill"]["traffic_frac"] = ptraffic / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS
-        del ppool, ws
-        if not args.no_prefill_workloads:
-            out["prefill_workloads"] = prefill_workloads(dev, stream, e0, e1)
+        out["roofline"]["copy_ceiling_gbs"] = legs["checkpoint_copy"]["gbs"]
+        out["roofline"]["frac_of_copy_ceiling"] = achieved / legs["checkpoint_copy"]["gbs"]
+    if "multi_token_decode" in legs:
+        legs["multi_token_decode"]["speedup_vs_single_steps"] = 4 * ms / legs["multi_token_decode"]["ms"]
+    out.update(legs)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, pw, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
     return 0
 
 
-def multi_token_decode(dev, stream, e0, e1, w, single_ms) -> dict:
+def checkpoint_copy_leg(pool, dev, stream, e0, e1) -> dict:
+    """COPY_PAIRS slot-to-slot copies of both state objects, slots [0, 256) -> [256, 512) of the
+    decode pool; also the measured streaming ceiling of the part (a copy of known size)."""
+    import torch
+    n = COPY_PAIRS
+    src = torch.arange(0, n, device=dev, dtype=torch.int32)
+    dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
+    for _ in range(2):
+        pool.checkpoint(0, src, dst)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        pool.checkpoint(0, src, dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cms = e0.elapsed_time(e1) / reps
+    ssm_b, conv_b = pool.info()
+    moved = 2 * n * (ssm_b + conv_b)
+    gbs = moved / (cms * 1e-3) / 1e9
+    return {"workload": f"{n} slot-to-slot copies of both state objects (bf16, {ssm_b + conv_b} B per slot)",
+            "ms": cms, "copies_per_s": n / (cms * 1e-3), "bytes_per_launch": moved, "gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def int8_store_leg(pool, sh, dev, stream, e0, e1) -> dict:
+    """int8 checkpoint store: 256 slots quantized into 256 entries, and restored into the other half."""
+    import torch
+    n = COPY_PAIRS
+    store = pool.int8_store(n)
+    sl = torch.arange(0, n, device=dev, dtype=torch.int32)
+    ent = torch.arange(0, n, device=dev, dtype=torch.int32)
+    dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
+    ssm_b, conv_b = pool.info()
+    codes_b = ssm_b // 2
+    scales_b = sh.nheads * sh.d_state * 4
+    put_bytes = n * (ssm_b + codes_b + scales_b + 2 * conv_b)       # read state + window, write entry
+    get_bytes = n * (codes_b + scales_b + ssm_b + 2 * conv_b)       # read entry, write state + window
+    res = {}
+    for name, fn, nbytes in (("put", lambda: pool.int8_put(store, 0, sl, ent), put_bytes),
+                             ("get", lambda: pool.int8_get(store, 0, ent, dst), get_bytes)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 10
+        res[name] = {"ms": t, "states_per_s": n / (t * 1e-3), "bytes_per_launch": nbytes,
+                     "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res["workload"] = (f"{n} bf16 slots quantized into int8 store entries (put) and restored into fresh "
+                       "slots (get), Nemotron-H layer shape")
+    res["entry_bytes"] = codes_b + scales_b + conv_b
+    res["slot_bytes"] = ssm_b + conv_b
+    del store
+    return res
+
+
+def prefill_leg(pw, dev, stream, e0, e1) -> dict:
+    """Chunked prefill of one 8192-token sequence (chunk 256) at the Nemotron-H layer shape, bf16
+    state, zero initial state, final state and window into slot 17."""
+    import torch
+
+    from recurrent_state_update_amd import synth
+    from recurrent_state_update_amd.pool import LayerWeights, Pool
+    psh = pw["shape"]
+    ppool = Pool.allocate(1, 32, psh.nheads, psh.head_dim, psh.d_state, psh.n_groups, psh.conv_kernel,
+                          torch.bfloat16, torch.bfloat16, dev)
+    PW = LayerWeights.from_numpy(pw["params"], dev)
+    pu = synth.to_torch(pw["u"], "bf16").to(dev)
+    pz = synth.to_torch(pw["z"], "bf16").to(dev)
+    pdt = synth.to_torch(pw["dt"], "bf16").to(dev)
+    T = pu.shape[0]
+    py = torch.empty((T, psh.intermediate), dtype=torch.bfloat16, device=dev)
+    px, pB, pC = ppool.split_xbc(pu)
+    ws = torch.empty(ppool.workspace_size(pw["cu_seqlens"], pw["chunk"]), dtype=torch.uint8, device=dev)
+
+    def pstep():
+        ppool.prefill(0, PW, pw["cu_seqlens"], [17], [0], px, pB, pC, pz, pdt, py,
+                      chunk_size=pw["chunk"], workspace=ws)
+
+    for _ in range(3):
+        pstep()
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        pstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pms = e0.elapsed_time(e1) / reps
+    flops = prefill_dense_flops_per_token(psh, pw["chunk"]) * T
+    io_bytes = T * (psh.conv_dim + psh.intermediate + psh.nheads + psh.intermediate) * 2 \
+        + psh.nheads * psh.head_dim * psh.d_state * 2 + psh.conv_dim * 3 * 2
+    res = {
+        "workload": "chunked prefill of one 8192-token sequence, chunk 256, same layer shape, bf16 state",
+        "ms": pms, "tokens_per_s": T / (pms * 1e-3),
+        "mfma_dense_tflops": flops / (pms * 1e-3) / 1e12,
+        "mfma_frac": flops / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "hbm_algorithmic_gbs": io_bytes / (pms * 1e-3) / 1e9,
+        "hbm_frac": io_bytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    # bytes the kernels move per call, intermediates included, from the committed counter record
+    ptraffic = measured_traffic(ROOT, "prefill_traffic.json", PREFILL_SOURCES, "traffic_bytes_per_call")
+    res["traffic"] = ptraffic
+    if ptraffic is not None:
+        res["traffic_gbs"] = ptraffic / (pms * 1e-3) / 1e9
+        res["traffic_frac"] = ptraffic / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    del ppool, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def multi_token_decode(dev, stream, e0, e1, w) -> dict:
     """Speculative decode step: the 256 sequences of the decode workload with 4 tokens each (a
     verified token and 3 drafts), the state after every token kept in a slot of its own (a
     1280-slot bf16 pool).  Algorithmic bytes per sequence: one state and window read, four written,
@@ -384,8 +413,7 @@ def multi_token_decode(dev, stream, e0, e1, w, single_ms) -> dict:
     return {"workload": f"{n} sequences x {K} tokens (a verified token and {K - 1} drafts), state after every "
                         "token kept, Nemotron-H layer shape, bf16 state",
             "ms": t, "tokens_per_s": n * K / (t * 1e-3), "bytes_per_launch": nbytes,
-            "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "speedup_vs_single_steps": K * single_ms / t}
+            "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def mamba1_decode(dev, stream, e0, e1) -> dict:
@@ -516,7 +544,7 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
     du, dz, ddt, dy = tokens(nd, torch.bfloat16)
     dx, dB, dC = pool.split_xbc(du)
     dsl = torch.from_numpy(d_slots).to(dev)
-    ws = torch.empty(pool.workspace_size(len(lens), T, 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(pool.workspace_size(cu, 256, ckpt_interval=1024, ckpt_slots=ck), dtype=torch.uint8, device=dev)
 
     def pre():
         pool.prefill(0, W, cu, p_slots, np.zeros(len(lens), np.uint8), x, B, C, z, dt, y, chunk_size=256,
@@ -546,7 +574,7 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
     Ws = [LayerWeights.from_numpy(synth.long_layer_params(layer), dev) for layer in range(nl)]
     u, z, dt, y = tokens(T, torch.float32)
     x, B, C = pool.split_xbc(u)
-    ws = torch.empty(pool.workspace_size(lw["seqs"], T, lw["chunk"]), dtype=torch.uint8, device=dev)
+    ws = torch.empty(pool.workspace_size(lw["cu_seqlens"], lw["chunk"]), dtype=torch.uint8, device=dev)
 
     def stack():
         for layer in range(nl):
@@ -563,29 +591,56 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
     return res
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
-    """The fp64 CPU oracle on the same decode step, single-threaded, for about budget_s seconds."""
+def cpu_baseline(w, pw, budget_s: float) -> dict:
+    """The fp64 CPU oracle, as it stands, on bounded samples of the benchmark workloads, on one host
+    thread (numpy with its thread pool limited to one): the decode step at the Nemotron-H layer
+    shape (whole 256-sequence steps, repeated while the budget lasts), and the prefill of one
+    8192-token sequence and of the 2 x 131072-token fp32-state long context, each on its first 256
+    tokens with all 128 heads (the oracle's cost per token does not depend on the position)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import mamba2 as orc
+    from recurrent_state_update_amd import synth
+    host_cores = len(os.sched_getaffinity(0))
     sh = w["shape"]
     n = len(w["slots"])
-    done = 0
-    t0 = time.perf_counter()
+    per = {}
     with threadpool_limits(limits=1):
-        while True:
-            ref = orc.PoolRef(sh, 1, 16, "bf16", "bf16")
-            lo = done % n
-            idx = np.arange(lo, min(lo + 16, n))
-            ref.ssm[0, :len(idx)], ref.conv[0, :len(idx)] = w["ssm0"][idx], w["conv0"][idx]
+        done, el = 0, 0.0
+        while el < budget_s:
+            # 16 sequences of the step at a time; the oracle's pool copy is set up outside the timing
+            idx = np.arange(done % n, min(done % n + 16, n))
+            ref = orc.PoolRef(sh, 1, len(idx), "bf16", "bf16")
+            ref.ssm[0], ref.conv[0] = w["ssm0"][idx], w["conv0"][idx]
+            t0 = time.perf_counter()
             orc.decode_step(ref, 0, w["params"], np.arange(len(idx)), w["u"][idx], w["z"][idx], w["dt"][idx], "bf16")
+            el += time.perf_counter() - t0
             done += len(idx)
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode tokens (sequences of the same 256-sequence step, 16 at a time) "
-                      f"in {el:.1f} s on one host thread, numpy fp64"}
+        per["decode_256seq"] = {"tokens_per_s": done / el, "seconds": el,
+                                "sample": f"{done} decode tokens of the 256-sequence step, 16 sequences per call"}
+        k = 256
+        if pw is not None:
+            ref = orc.PoolRef(pw["shape"], 1, 32, "bf16", "bf16")
+            t0 = time.perf_counter()
+            orc.prefill(ref, 0, pw["params"], [0, k], [17], [0], [0], pw["u"][:k], pw["z"][:k], pw["dt"][:k], "bf16")
+            el = time.perf_counter() - t0
+            per["prefill_8192tok"] = {"tokens_per_s": k / el, "seconds": el,
+                                      "sample": f"first {k} of the 8192 tokens, all 128 heads, bf16 state"}
+        lw = synth.long_workload()
+        bu, bz, bdt = synth.long_token_block(0)
+        ref = orc.PoolRef(lw["shape"], 1, 1, "f32", "bf16")
+        t0 = time.perf_counter()
+        orc.prefill(ref, 0, synth.long_layer_params(0), [0, k], [0], [0], [0], bu[:k], bz[:k], bdt[:k], "f32")
+        el = time.perf_counter() - t0
+        per["long_context_fp32"] = {"tokens_per_s": k / el, "seconds": el,
+                                    "sample": f"first {k} tokens of sequence 0 in layer 0, all 128 heads, fp32 "
+                                              "state; the whole workload is 2 x 131072 tokens x 48 layers"}
+    d = per["decode_256seq"]
+    return {"value": d["tokens_per_s"], "unit": "tokens/s", "cores": 1, "threads": 1, "workers": 1,
+            "host_cores": host_cores, "kind": "oracle",
+            "sample": f"{d['sample']} ({d['seconds']:.1f} s) on one host thread, numpy fp64; per-workload "
+                      "samples in per_workload",
+            "per_workload": per}
 
 
 if __name__ == "__main__":

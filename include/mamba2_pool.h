@@ -85,7 +85,7 @@ typedef struct m2_pool_desc {
   uint64_t conv_bytes;
 } m2_pool_desc;
 
-/* Opaque host-side handle; holds the descriptor, no device memory. */
+/* Opaque host-side handle; holds the descriptor, no device or pinned host memory. */
 typedef struct m2_pool m2_pool;
 
 /* Per-layer parameters, fp32 device arrays:
@@ -177,14 +177,19 @@ m2_status mamba2_decode_multi(m2_pool* pool, int32_t layer, const m2_layer_param
                               int32_t io_dtype, void* y, int64_t y_stride, int32_t y_dtype,
                               void* stream);
 
-/* Bytes of device workspace mamba2_prefill_chunked needs for num_seqs packed
- * sequences totalling total_tokens tokens at chunk_size, when at most max_ckpt
- * checkpoints of any one sequence fall inside a chunk (a position that is
- * neither a multiple of chunk_size rows after the sequence's first row in the
- * call nor its last row; each such checkpoint adds one chunk).  Pass 0 when
- * every checkpoint lies on that grid.  Host-only. */
-m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
-                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
+/* Bytes of device workspace mamba2_prefill_chunked needs for a call with these
+ * per-sequence host arguments (the same values the call takes: cu_seqlens
+ * [num_seqs+1], start_pos [num_seqs] or NULL, chunk_size, ckpt_interval and the
+ * checkpoint table ckpt_slots [num_seqs][max_ckpt] or NULL).  The library builds
+ * the call's chunk table from them, so checkpoints that end a chunk early are
+ * counted exactly; a workspace sized for one call fits every call whose chunk
+ * table is no larger.  Host-only.
+ * Errors: M2_ERR_ARG (NULL pool or bytes, negative counts, cu_seqlens or
+ * ckpt_slots missing where needed), M2_ERR_SHAPE (cu_seqlens[0] != 0 or
+ * decreasing; size overflow), M2_ERR_UNSUPPORTED (a Mamba1 pool, chunk_size). */
+m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, const int32_t* cu_seqlens,
+                                        const int32_t* start_pos, int32_t chunk_size, int32_t ckpt_interval,
+                                        const int32_t* ckpt_slots, int32_t max_ckpt, uint64_t* bytes);
 
 /* Chunked (SSD) prefill of packed variable-length sequences.  Each chunk's
  * own contribution is a causally masked matrix product, and a short scan over
@@ -218,11 +223,10 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  * first row.  workspace: device memory of at least
  * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch
  * and not read across calls.  Sequences with zero length leave their slot untouched.
- * Launch tables (32 bytes per sequence and per chunk, 16 per conv window written)
- * of up to 3072 bytes travel in the first kernel's arguments, so the call enqueues
- * no copy and never blocks; larger tables go through a pinned host buffer owned by
- * the pool handle, and the call may then wait on the host for the previous such
- * upload to finish before it reuses the buffer.
+ * Launch tables (32 bytes per sequence and per chunk, 16 per checkpoint window)
+ * travel in kernel arguments: up to 3072 bytes in the first kernel's, more in
+ * those of small upload launches ahead of it.  The call allocates nothing, enqueues
+ * no host-to-device copy and never waits on the host.
  * With fp32 SSM state the contractions run in split-bf16 (three products)
  * for fp32-level accuracy; with bf16 state they run in bf16 with fp32 accumulate. */
 m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_params* params,
@@ -337,8 +341,8 @@ m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  * runs in chunks of chunk_size rows (16..4096): each chunk's end state from
  * zero, a pass through each sequence's chunks, then every chunk again from its
  * entering state.  workspace: at least mamba1_prefill_workspace_size(...)
- * bytes, 256-byte aligned.  The launch tables go through the pool's pinned
- * staging buffer (the call may wait for the previous upload on the host).
+ * bytes, 256-byte aligned.  The launch tables travel in the arguments of small
+ * upload launches (no allocation, no host-to-device copy, no host wait).
  * Errors: as mamba2_prefill_chunked (slot range, repeats and aliasing
  * M2_ERR_SLOT; cu_seqlens M2_ERR_SHAPE; alignment M2_ERR_ALIGN; workspace
  * M2_ERR_WORKSPACE), plus M2_ERR_UNSUPPORTED for a Mamba2 pool, d_state

@@ -299,7 +299,7 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
     gsel = np.array([gpos[g] for g in groups])
     A, D, dt_bias = (_f64(params[k])[heads] for k in ("A", "D", "dt_bias"))
     T = int(cu_seqlens[-1])
-    out = np.full((T, I), np.nan)
+    outs = np.zeros((T, len(heads), P))                          # outputs of the chosen heads
     for sq in range(len(slots)):
         t0, t1 = int(cu_seqlens[sq]), int(cu_seqlens[sq + 1])
         L = t1 - t0
@@ -327,8 +327,7 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
         for t in range(L):
             h = alpha[t][:, None, None] * h + (delta[t][:, None] * x[t])[:, :, None] * Bm[t][:, None, :]
             y = np.einsum("hpn,hn->hp", h, Cm[t]) + D[:, None] * x[t]
-            row = out[t0 + t].reshape(H, P)
-            row[heads] = y * zs[t]
+            outs[t0 + t] = y * zs[t]
             p = sp + t + 1
             if ckpt_interval and p % ckpt_interval == 0:
                 k = p // ckpt_interval - sp // ckpt_interval - 1
@@ -338,7 +337,9 @@ def prefill(pool: PoolRef, layer: int, params: dict, cu_seqlens, slots, has_init
                     pool.conv[layer, dst] = round_to(stream[t + 1:t + W].T, pool.conv_dtype)
         pool.ssm[layer, slot][heads] = round_to(h, pool.ssm_dtype)
         pool.conv[layer, slot] = round_to(stream[L:L + W - 1].T, pool.conv_dtype)
-    return round_to(out, y_dtype)
+    out = np.full((T, H, P), np.nan)
+    out[:, heads] = round_to(outs, y_dtype)
+    return out.reshape(T, I)
 
 
 # --------------------------------------------------------------------------

@@ -48,8 +48,8 @@ _SIGS = {
     "mamba2_decode_step": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p, c_void_p,
                                      c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                      c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32, c_void_p]),
-    "mamba2_prefill_workspace_size": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
-                                                POINTER(c_uint64)]),
+    "mamba2_prefill_workspace_size": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                                c_int32, POINTER(c_uint64)]),
     "mamba2_prefill_chunked": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                          c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,

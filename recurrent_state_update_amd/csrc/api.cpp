@@ -7,7 +7,6 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -24,12 +23,6 @@ struct m2_pool {
   m2::LayerShape sh;
   uint64_t ssm_slot_bytes;   // one slot, one layer
   uint64_t conv_slot_bytes;
-  // pinned host staging for the prefill tables, reused across calls
-  std::mutex mu;
-  void* staging = nullptr;
-  size_t staging_bytes = 0;
-  hipEvent_t staging_done = nullptr;
-  bool staging_pending = false;
 };
 
 namespace {
@@ -118,38 +111,6 @@ m2_status hip_fail(hipError_t e, const char* what) {
   return fail(M2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Copy `bytes` of host data, written into the buffer by fill(), to device memory at dst on the
-// stream, through the pool's pinned staging buffer: one host-to-device copy, the buffer reused
-// once the previous copy has completed (the call may wait for that on the host).
-template <typename F>
-m2_status staged_upload(m2_pool* pool, void* dst, size_t bytes, hipStream_t hs, F fill) {
-  std::lock_guard<std::mutex> lock(pool->mu);
-  hipError_t e;
-  if (pool->staging_pending) {
-    if ((e = hipEventSynchronize(pool->staging_done)) != hipSuccess) return hip_fail(e, "staging wait");
-    pool->staging_pending = false;
-  }
-  if (pool->staging_bytes < bytes) {
-    if (pool->staging) (void)hipHostFree(pool->staging);
-    pool->staging = nullptr;
-    pool->staging_bytes = 0;
-    if ((e = hipHostMalloc(&pool->staging, bytes, hipHostMallocDefault)) != hipSuccess)
-      return hip_fail(e, "pinned staging allocation");
-    pool->staging_bytes = bytes;
-  }
-  if (!pool->staging_done) {
-    if ((e = hipEventCreateWithFlags(&pool->staging_done, hipEventDisableTiming)) != hipSuccess)
-      return hip_fail(e, "staging event");
-  }
-  char* st = static_cast<char*>(pool->staging);
-  memset(st, 0, bytes);
-  fill(st);
-  if ((e = hipMemcpyAsync(dst, st, bytes, hipMemcpyHostToDevice, hs)) != hipSuccess) return hip_fail(e, "table upload");
-  if ((e = hipEventRecord(pool->staging_done, hs)) != hipSuccess) return hip_fail(e, "staging event record");
-  pool->staging_pending = true;
-  return M2_OK;
-}
-
 // Prefill tables and workspace carving.
 struct PrefillLayout {
   uint64_t nc_max, nw_max, planes;
@@ -193,6 +154,85 @@ bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int6
   if (!mul_ok(L->plane_hin, 2 * L->planes, &v)) return false;
   L->total = align_up(L->off_hin + v, 256);
   return true;
+}
+
+// Checks of the per-sequence host arguments shared by the prefill and its workspace query.
+m2_status check_prefill_seqs(int32_t num_seqs, const int32_t* cu_seqlens, const int32_t* start_pos,
+                             int32_t chunk_size, int32_t ckpt_interval, const int32_t* ckpt_slots, int32_t max_ckpt) {
+  if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
+  if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
+    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
+  if (ckpt_interval < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative checkpoint interval or count");
+  if (num_seqs == 0) return M2_OK;
+  if (!cu_seqlens) return fail(M2_ERR_ARG, "cu_seqlens is required");
+  if (cu_seqlens[0] != 0) return fail(M2_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < num_seqs; ++s) {
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return fail(M2_ERR_SHAPE, "cu_seqlens decreases at %d", s);
+    if (start_pos && start_pos[s] < 0) return fail(M2_ERR_ARG, "start_pos of sequence %d is negative", s);
+  }
+  if (ckpt_interval > 0 && max_ckpt > 0 && !ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
+  return M2_OK;
+}
+
+// The launch tables of a prefill call.  Chunks run chunk_size rows from each sequence's first row; a
+// checkpoint position inside a chunk ends that chunk early, so every checkpoint falls on a chunk end.
+// slots and has_init may be NULL (a size query): the entries then hold -1 and 0.
+struct PrefillTables {
+  std::vector<m2::SeqEntry> seqs;
+  std::vector<m2::ChunkEntry> chunks;
+  std::vector<m2::WindowEntry> windows;   // checkpoint conv windows (final windows are per sequence)
+};
+
+void build_prefill_tables(int num_seqs, const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_init,
+                          const int32_t* start_pos, int chunk_size, int ckpt_interval, const int32_t* ckpt_slots,
+                          int max_ckpt, PrefillTables* t) {
+  const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
+  t->seqs.assign(num_seqs, m2::SeqEntry{});
+  t->chunks.clear();
+  t->windows.clear();
+  t->chunks.reserve((size_t)(cu_seqlens[num_seqs] / chunk_size) + (size_t)num_seqs);
+  std::vector<std::pair<int, int>> ends;   // (rows into the sequence, checkpoint slot or -1)
+  for (int s = 0; s < num_seqs; ++s) {
+    const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - cu_seqlens[s];
+    const int64_t sp = start_pos ? start_pos[s] : 0;
+    m2::SeqEntry& e = t->seqs[s];
+    e.t0 = t0;
+    e.len = len;
+    e.slot = slots ? slots[s] : -1;
+    e.has_init = has_init && has_init[s] ? 1 : 0;
+    e.chunk0 = (int32_t)t->chunks.size();
+    e.nchunk = 0;
+    e.pad0 = e.pad1 = 0;
+    ends.clear();
+    for (int c0 = 0; c0 < len; c0 += chunk_size) ends.push_back({c0 + chunk_size < len ? c0 + chunk_size : len, -1});
+    if (ckpt_on) {
+      // entry k: the k-th multiple p of the interval with start_pos < p <= start_pos + len
+      for (int k = 0; k < max_ckpt; ++k) {
+        const int ck = ckpt_slots[(int64_t)s * max_ckpt + k];
+        const int64_t off = (sp / ckpt_interval + 1 + k) * (int64_t)ckpt_interval - sp;
+        if (ck >= 0 && off <= len) ends.push_back({(int)off, ck});
+      }
+    }
+    std::sort(ends.begin(), ends.end(), [](const std::pair<int, int>& a, const std::pair<int, int>& b) {
+      return a.first != b.first ? a.first < b.first : a.second > b.second;   // a checkpoint first
+    });
+    int prev = 0;
+    for (const auto& en : ends) {
+      if (en.first == prev) continue;   // the same end again (a grid end under a checkpoint)
+      m2::ChunkEntry c;
+      c.seq = s;
+      c.t0 = t0 + prev;
+      c.len = en.first - prev;
+      c.tau0 = prev;
+      c.ckpt_slot = en.second;
+      c.is_last = en.first == len;
+      c.pad0 = c.pad1 = 0;
+      if (c.ckpt_slot >= 0) t->windows.push_back({s, en.first, c.ckpt_slot, 0});
+      t->chunks.push_back(c);
+      ++e.nchunk;
+      prev = en.first;
+    }
+  }
 }
 
 // Dense sizes of an int8 store of num_entries entries for this pool.
@@ -287,7 +327,7 @@ bool m1_layout(const m2::LayerShape& sh, int64_t num_seqs, int64_t nc, int64_t n
 
 extern "C" {
 
-int32_t mamba2_abi_version(void) { return 2; }
+int32_t mamba2_abi_version(void) { return 3; }
 
 const char* mamba2_last_error(void) { return g_err.c_str(); }
 
@@ -340,15 +380,7 @@ m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out) {
   return ok();
 }
 
-void mamba2_pool_destroy(m2_pool* pool) {
-  if (!pool) return;
-  if (pool->staging_done) {
-    if (pool->staging_pending) (void)hipEventSynchronize(pool->staging_done);
-    (void)hipEventDestroy(pool->staging_done);
-  }
-  if (pool->staging) (void)hipHostFree(pool->staging);
-  delete pool;
-}
+void mamba2_pool_destroy(m2_pool* pool) { delete pool; }
 
 m2_status mamba2_pool_info(const m2_pool* pool, uint64_t* ssm_bytes, uint64_t* conv_bytes) {
   if (!pool || !ssm_bytes || !conv_bytes) return fail(M2_ERR_ARG, "NULL argument");
@@ -431,19 +463,22 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
   return ok();
 }
 
-m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
-                                        int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes) {
+m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, const int32_t* cu_seqlens,
+                                        const int32_t* start_pos, int32_t chunk_size, int32_t ckpt_interval,
+                                        const int32_t* ckpt_slots, int32_t max_ckpt, uint64_t* bytes) {
   if (!pool || !bytes) return fail(M2_ERR_ARG, "NULL argument");
   if (m2_status st = require_family(pool, M2_FAMILY_MAMBA2, "mamba2_prefill_workspace_size")) return st;
-  if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
-  if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
-    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
-  // chunks on the grid of chunk_size rows from each sequence's first row, plus one more for each
-  // checkpoint that falls inside a chunk; a conv window per chunk end at most, plus the finals
-  const uint64_t nc = (uint64_t)(total_tokens / chunk_size) + (uint64_t)num_seqs * (1 + (uint64_t)max_ckpt);
+  if (m2_status st = check_prefill_seqs(num_seqs, cu_seqlens, start_pos, chunk_size, ckpt_interval, ckpt_slots,
+                                        max_ckpt))
+    return st;
+  *bytes = 0;
+  if (num_seqs == 0 || cu_seqlens[num_seqs] == 0) return ok();
+  PrefillTables t;
+  build_prefill_tables(num_seqs, cu_seqlens, nullptr, nullptr, start_pos, chunk_size, ckpt_interval, ckpt_slots,
+                       max_ckpt, &t);
   PrefillLayout L;
-  if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, total_tokens, chunk_size, nc,
-                      nc + (uint64_t)num_seqs, &L))
+  if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, cu_seqlens[num_seqs], chunk_size,
+                      t.chunks.size(), t.windows.size(), &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();
@@ -464,17 +499,13 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
   if (m2_status st = check_params(pool, params)) return st;
   if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
-  if (chunk_size < 16 || chunk_size > 256 || chunk_size % 16 != 0)
-    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be a multiple of 16 in [16, 256], got %d", chunk_size);
-  if (ckpt_interval < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative checkpoint interval or count");
+  if (m2_status st = check_prefill_seqs(num_seqs, cu_seqlens, start_pos, chunk_size, ckpt_interval, ckpt_slots,
+                                        max_ckpt))
+    return st;
   if (num_seqs == 0) return ok();
-  if (!cu_seqlens || !slots || !has_init) return fail(M2_ERR_ARG, "cu_seqlens, slots and has_initial_state are required");
-  if (cu_seqlens[0] != 0) return fail(M2_ERR_SHAPE, "cu_seqlens[0] must be 0");
-  for (int s = 0; s < num_seqs; ++s)
-    if (cu_seqlens[s + 1] < cu_seqlens[s]) return fail(M2_ERR_SHAPE, "cu_seqlens decreases at %d", s);
+  if (!slots || !has_init) return fail(M2_ERR_ARG, "slots and has_initial_state are required");
   const int64_t T = cu_seqlens[num_seqs];
   const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
-  if (ckpt_on && !ckpt_slots) return fail(M2_ERR_ARG, "ckpt_slots is NULL");
   const int S = pool->d.num_slots;
   std::vector<uint8_t> used(S, 0);
   for (int s = 0; s < num_seqs; ++s) {
@@ -482,8 +513,6 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     if (sl < 0 || sl >= S) return fail(M2_ERR_SLOT, "slot %d of sequence %d out of range", sl, s);
     if (used[sl]) return fail(M2_ERR_SLOT, "slot %d appears twice", sl);
     used[sl] = 1;
-    const int sp = start_pos ? start_pos[s] : 0;
-    if (sp < 0) return fail(M2_ERR_ARG, "start_pos of sequence %d is negative", s);
   }
   if (ckpt_on) {
     for (int64_t i = 0; i < (int64_t)num_seqs * max_ckpt; ++i) {
@@ -504,55 +533,12 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   if (!m2::prefill_supported(sh.P, sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,32,64,128}");
 
-  // ---- host tables.  Chunks run chunk_size rows from each sequence's first row; a checkpoint
-  // position inside a chunk ends that chunk early, so every checkpoint falls on a chunk end.
-  std::vector<m2::SeqEntry> seqs(num_seqs);
-  std::vector<m2::ChunkEntry> chunks;
-  std::vector<m2::WindowEntry> windows;
-  chunks.reserve((size_t)(T / chunk_size) + (size_t)num_seqs);
-  std::vector<std::pair<int, int>> ends;   // (rows into the sequence, checkpoint slot or -1)
-  for (int s = 0; s < num_seqs; ++s) {
-    const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - cu_seqlens[s];
-    const int64_t sp = start_pos ? start_pos[s] : 0;
-    m2::SeqEntry& e = seqs[s];
-    e.t0 = t0;
-    e.len = len;
-    e.slot = slots[s];
-    e.has_init = has_init[s] ? 1 : 0;
-    e.chunk0 = (int32_t)chunks.size();
-    e.nchunk = 0;
-    e.pad0 = e.pad1 = 0;
-    ends.clear();
-    for (int c0 = 0; c0 < len; c0 += chunk_size) ends.push_back({c0 + chunk_size < len ? c0 + chunk_size : len, -1});
-    if (ckpt_on) {
-      // entry k: the k-th multiple p of the interval with start_pos < p <= start_pos + len
-      for (int k = 0; k < max_ckpt; ++k) {
-        const int ck = ckpt_slots[(int64_t)s * max_ckpt + k];
-        const int64_t off = (sp / ckpt_interval + 1 + k) * (int64_t)ckpt_interval - sp;
-        if (ck >= 0 && off <= len) ends.push_back({(int)off, ck});
-      }
-    }
-    std::sort(ends.begin(), ends.end(), [](const std::pair<int, int>& a, const std::pair<int, int>& b) {
-      return a.first != b.first ? a.first < b.first : a.second > b.second;   // a checkpoint first
-    });
-    int prev = 0;
-    for (const auto& en : ends) {
-      if (en.first == prev) continue;   // the same end again (a grid end under a checkpoint)
-      m2::ChunkEntry c;
-      c.seq = s;
-      c.t0 = t0 + prev;
-      c.len = en.first - prev;
-      c.tau0 = prev;
-      c.ckpt_slot = en.second;
-      c.is_last = en.first == len;
-      c.pad0 = c.pad1 = 0;
-      if (c.ckpt_slot >= 0) windows.push_back({s, en.first, c.ckpt_slot, 0});
-      chunks.push_back(c);
-      ++e.nchunk;
-      prev = en.first;
-    }
-    if (len > 0) windows.push_back({s, len, slots[s], 0});
-  }
+  PrefillTables t;
+  build_prefill_tables(num_seqs, cu_seqlens, slots, has_init, start_pos, chunk_size, ckpt_interval, ckpt_slots,
+                       max_ckpt, &t);
+  const std::vector<m2::SeqEntry>& seqs = t.seqs;
+  const std::vector<m2::ChunkEntry>& chunks = t.chunks;
+  const std::vector<m2::WindowEntry>& windows = t.windows;
   PrefillLayout L;
   if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, chunks.size(), windows.size(), &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows");
@@ -563,8 +549,8 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
                 (unsigned long long)L.total);
   if (chunks.empty()) return ok();
 
-  // ---- pack the tables; small ones travel in the conv launch's arguments, larger ones are
-  // uploaded through pinned staging (one host-to-device copy)
+  // ---- pack the tables; small ones travel in the conv launch's arguments, larger ones in the
+  // arguments of upload launches ahead of it (no host-to-device copy, no host wait)
   const size_t tab_chunks = align_up(seqs.size() * sizeof(m2::SeqEntry), 16);
   const size_t tab_windows = tab_chunks + align_up(chunks.size() * sizeof(m2::ChunkEntry), 16);
   const size_t tab_bytes = align_up(tab_windows + windows.size() * sizeof(m2::WindowEntry), 16);
@@ -572,17 +558,17 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool tab_inline = tab_bytes <= (size_t)m2::kInlineTableBytes;
-  auto pack = [&](char* tab) {
-    memcpy(tab, seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
-    memcpy(tab + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
-    memcpy(tab + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
-  };
+  std::vector<char> packed(tab_bytes, 0);
+  memcpy(packed.data(), seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
+  memcpy(packed.data() + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
+  if (!windows.empty())
+    memcpy(packed.data() + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
   m2::InlineTables inl;
   if (tab_inline) {
-    memset(inl.w, 0, tab_bytes);
-    pack(reinterpret_cast<char*>(inl.w));
-  } else if (m2_status st = staged_upload(pool, ws, tab_bytes, hs, pack)) {
-    return st;
+    memcpy(inl.w, packed.data(), tab_bytes);
+  } else {
+    const hipError_t eu = m2::launch_table_upload(ws, packed.data(), tab_bytes, hs);
+    if (eu != hipSuccess) return hip_fail(eu, "table upload");
   }
 
   m2::PrefillParams p;
@@ -938,12 +924,14 @@ m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* pa
                 (unsigned long long)L.total);
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (m2_status st = staged_upload(pool, ws, L.tab_bytes, hs, [&](char* t) {
-        memcpy(t, seqs.data(), seqs.size() * sizeof(m2::M1Seq));
-        memcpy(t + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::M1Chunk));
-        if (nck) memcpy(t + L.off_ck, ckpt_slots, (size_t)nck * 4);
-      }))
-    return st;
+  {
+    std::vector<char> t(L.tab_bytes, 0);
+    memcpy(t.data(), seqs.data(), seqs.size() * sizeof(m2::M1Seq));
+    memcpy(t.data() + L.off_chunks, chunks.data(), chunks.size() * sizeof(m2::M1Chunk));
+    if (nck) memcpy(t.data() + L.off_ck, ckpt_slots, (size_t)nck * 4);
+    const hipError_t eu = m2::launch_table_upload(ws, t.data(), L.tab_bytes, hs);
+    if (eu != hipSuccess) return hip_fail(eu, "table upload");
+  }
   m2::Mamba1PrefillParams p;
   p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
   p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;

@@ -1,8 +1,9 @@
-// Bit-exact slot-to-slot copy of both pool state objects, gfx950.
+// Bit-exact slot-to-slot copy of both pool state objects, gfx950; and the launch that carries
+// host-built tables to device memory inside its own kernel arguments.
 //
-// A cached state is copied into a fresh slot rather than shared, because the
-// recurrence overwrites its slot in place ("Hybrid SSM / Mamba models and
-// non-KV state", mlinterviewnotes.com ch. 7.3, SGLang checkpoint passage).
+// A kept state needs a slot of its own: the live slot is updated in place by the next token, so
+// the two cannot share storage ("Hybrid SSM / Mamba models and non-KV state",
+// mlinterviewnotes.com ch. 7.3, SGLang checkpoint passage).
 // One launch covers both objects: workgroups [0, groups of the SSM state) copy
 // the SSM state, the rest the conv window, of one (pair, layer) each.  Each lane
 // moves one 16-byte piece with a non-temporal load and store (the copy is
@@ -11,6 +12,9 @@
 // small workgroups stream fastest (8 KiB per 512-thread workgroup 6.33 TB/s;
 // 32 KiB 5.73; 128 KiB with the next span's loads issued before the current
 // span's stores 5.26).
+#include <cstddef>
+#include <cstring>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -67,6 +71,44 @@ hipError_t launch_slot_copy(void* ssm_base, uint64_t ssm_bytes_per_slot, void* c
   const dim3 grid(o0.groups + o1.groups, (unsigned)n, (unsigned)nl);
   hipLaunchKernelGGL(slot_copy_kernel, grid, dim3(kCopyThreads), 0, s, o0, o1, l0, (int)num_slots, src, dst);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ tables through kernel arguments
+// Host-built launch tables reach device memory without a host-to-device copy: each launch carries
+// up to kUploadBytes of them in its kernel arguments and writes them to dst.  No pinned host
+// buffer, no allocation and no host wait are involved, and the launches order with the rest of
+// the work on the stream.
+constexpr int kUploadBytes = 3072;
+struct alignas(16) UploadArgs {
+  unsigned char* dst;
+  int32_t bytes;   // a multiple of 16, at most kUploadBytes
+  int32_t pad[1];
+  unsigned char data[kUploadBytes];
+};
+
+__global__ __launch_bounds__(256) void table_upload_kernel(UploadArgs a) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) i32x4 kquad;
+  kquad* src = reinterpret_cast<kquad*>((const __attribute__((address_space(4))) unsigned char*)
+                                            __builtin_amdgcn_kernarg_segment_ptr() + offsetof(UploadArgs, data));
+  i32x4* dst = reinterpret_cast<i32x4*>(a.dst);
+  for (int i = threadIdx.x; i < a.bytes / 16; i += blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_table_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes % 16 != 0) return hipErrorInvalidValue;
+  UploadArgs a;
+  for (size_t off = 0; off < bytes; off += kUploadBytes) {
+    const size_t n = bytes - off < (size_t)kUploadBytes ? bytes - off : (size_t)kUploadBytes;
+    a.dst = static_cast<unsigned char*>(dst) + off;
+    a.bytes = (int32_t)n;
+    a.pad[0] = 0;
+    memcpy(a.data, static_cast<const unsigned char*>(src) + off, n);
+    hipLaunchKernelGGL(table_upload_kernel, dim3(1), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace m2

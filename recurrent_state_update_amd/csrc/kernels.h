@@ -49,4 +49,9 @@ hipError_t launch_slot_copy(void* ssm_base, uint64_t ssm_bytes_per_slot, void* c
                             uint64_t conv_bytes_per_slot, uint64_t num_slots, int l0, int nl, int n,
                             const int32_t* src, const int32_t* dst, hipStream_t s);
 
+// Copy `bytes` (a multiple of 16) of host data to device memory at dst, ordered on stream s, by
+// kernel launches that carry the data in their arguments (no host-to-device copy, no pinned
+// buffer, no host wait).
+hipError_t launch_table_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+
 }  // namespace m2

@@ -13,7 +13,7 @@ struct ChunkEntry {   // one per chunk
   int32_t seq, t0, len, tau0;       // packed start row, rows in chunk, offset inside the sequence
   int32_t ckpt_slot, is_last, pad0, pad1;
 };
-struct WindowEntry {  // one conv-window write: window after `tau` rows of sequence `seq` -> slot
+struct WindowEntry {  // one checkpoint conv-window write: window after `tau` rows of sequence `seq` -> slot
   int32_t seq, tau, slot, pad;
 };
 

@@ -17,10 +17,10 @@
 //                         workgroups compute Delta = softplus(dt + dt_bias) and the chunk-local
 //                         cumsum of Delta*A
 //   2. chunk_state_kernel per (chunk, head): the chunk's end state from a zero state (MFMA); its
-//                         trailing workgroups write the final and checkpoint conv windows
+//                         trailing workgroups write the checkpoint conv windows
 //   3. state_pass_kernel  per (sequence, head): the affine step through the sequence's chunks ->
 //                         state entering each chunk (operand planes), checkpoint and final
-//                         states into their slots
+//                         states into their slots; the final conv windows
 //   4. chunk_out_group_kernel  per (chunk, group): outputs (MFMA) of the group's heads in turn,
 //                         C B^T formed once; chunk_out_kernel per (chunk, head) for hi/lo planes
 //                         and head_dim 128
@@ -504,12 +504,13 @@ __device__ __forceinline__ void store_state_tile(void* pool, int64_t base, int N
 }
 
 // ------------------------------------------------------------------ 2a. conv windows
-// Run by the trailing workgroups of the chunk-state launch (after the conv has read the initial
-// windows): for window entry w, the raw inputs of the W-1 rows before position tau (from the
-// slot's window, or zeros, before the sequence start) into the entry's slot.
-__device__ __forceinline__ void window_block(const PrefillParams& a, int w, int c_first, int c_step) {
-  const WindowEntry we = load_uniform(&a.windows[w]);
-  const SeqEntry sq = load_uniform(&a.seqs[we.seq]);
+// The raw inputs of the W-1 rows before position tau of sequence we.seq (from the slot's window,
+// or zeros, before the sequence start) into slot we.slot, channels c_first, c_first + c_step, ...
+// Checkpoint windows are written by the trailing workgroups of the chunk-state launch, after the
+// conv launch has read every initial window; final windows, which overwrite the sequence's own
+// slot, by the state-pass launch, after every checkpoint window that reads the initial window.
+__device__ __forceinline__ void window_write(const PrefillParams& a, const WindowEntry& we, const SeqEntry& sq,
+                                             int c_first, int c_step) {
   const int Cd = a.sh.Cd, I = a.sh.I, GN = a.sh.G * a.sh.N, W1 = a.sh.W - 1;
   for (int c = c_first; c < Cd; c += c_step) {
     const void* src;
@@ -580,7 +581,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
   const int nmain = a.num_chunks * nh;
   if ((int)blockIdx.x >= nmain) {   // trailing workgroups: conv windows, nh per window
     const int w = blockIdx.x - nmain;
-    window_block(a, w / nh, (w % nh) * kStateThreads + threadIdx.x, nh * kStateThreads);
+    const WindowEntry we = load_uniform(&a.windows[w / nh]);
+    window_write(a, we, load_uniform(&a.seqs[we.seq]), (w % nh) * kStateThreads + threadIdx.x, nh * kStateThreads);
     return;
   }
   // The workgroups of one (chunk, group) read the same B blocks: consecutive logical indices,
@@ -733,7 +735,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(PrefillParam
 }
 
 // ------------------------------------------------------------------ 3. pass over each sequence's chunks
-// Per (sequence, head, 2048 state elements), 256 threads of 8 elements each: the affine step
+// Per (sequence, head, 2048 state elements), 256 threads of 8 elements each (part 0 also writes the
+// sequence's final conv window): the affine step
 //   h <- exp(a_last(c)) h + S_c
 // through the sequence's chunks from its initial state (the slot's, or zero).  Before each chunk
 // the state entering it goes out as the output kernel's bf16 operand planes; after a chunk that
@@ -745,6 +748,10 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillParams a) {
   const SeqEntry sq = load_uniform(&a.seqs[blockIdx.x]);
   if (sq.nchunk == 0) return;
   const int h = blockIdx.y, H = a.sh.H;
+  if (blockIdx.z == 0) {   // the final conv window, spread over the sequence's H workgroups of part 0
+    const WindowEntry we = {(int32_t)blockIdx.x, sq.len, sq.slot, 0};
+    window_write(a, we, sq, h * 256 + threadIdx.x, H * 256);
+  }
   const int PN = a.sh.P * a.sh.N;
   const int e8 = (blockIdx.z * 256 + threadIdx.x) * 8;
   if (e8 >= PN) return;

@@ -229,9 +229,19 @@ class Pool:
         return y
 
     # ------------------------------------------------------------------ prefill
-    def workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int, max_ckpt: int = 0) -> int:
+    def workspace_size(self, cu_seqlens, chunk_size: int = 256, start_pos=None, ckpt_interval: int = 0,
+                       ckpt_slots=None) -> int:
+        """Workspace bytes of a prefill call with these host arguments (the library counts the chunks)."""
+        cu, cu_p = _host_i32(cu_seqlens)
+        ns = len(cu) - 1
+        _, sp_p = _host_i32(start_pos)
+        ck_p, max_ck = None, 0
+        if ckpt_slots is not None:
+            ck = np.ascontiguousarray(np.asarray(ckpt_slots, dtype=np.int32).reshape(ns, -1))
+            ck_p, max_ck = ck.ctypes.data_as(c_void_p), ck.shape[1]
         n = c_uint64()
-        check(lib().mamba2_prefill_workspace_size(self._h, num_seqs, total_tokens, chunk_size, max_ckpt, byref(n)))
+        check(lib().mamba2_prefill_workspace_size(self._h, ns, cu_p, sp_p, chunk_size, ckpt_interval, ck_p, max_ck,
+                                                  byref(n)))
         return n.value
 
     def prefill(self, layer: int, w: LayerWeights, cu_seqlens, slots, has_init, x, B, C, z, dt, y,
@@ -249,17 +259,9 @@ class Pool:
             ck = np.ascontiguousarray(np.asarray(ckpt_slots, dtype=np.int32).reshape(ns, -1))
             max_ck = ck.shape[1]
             ck_p = ck.ctypes.data_as(c_void_p)
-        total = int(cu[-1]) if len(cu) else 0
-        off_grid = 0          # the most checkpoints of one sequence that end a chunk early
-        if ckpt_slots is not None and ckpt_interval > 0:
-            for s in range(ns):
-                p0 = int(sp[s]) if sp is not None else 0
-                n = int(cu[s + 1] - cu[s])
-                offs = [(p0 // ckpt_interval + 1 + k) * ckpt_interval - p0 for k in range(max_ck) if ck[s, k] >= 0]
-                off_grid = max(off_grid, sum(1 for o in offs if o < n and o % chunk_size))
-        need = self.workspace_size(ns, total, chunk_size, off_grid)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=self.ssm.device)
+            need = self.workspace_size(cu, chunk_size, sp, ckpt_interval, ckpt_slots)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.ssm.device)
         io = _dtype_code(x)
         xp, xs = _rows(x, "x")
         bp, bs = _rows(B, "B")

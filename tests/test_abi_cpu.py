@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
     exported = set(re.findall(r"\bT (mamba[12]_\w+)", out))
     assert set(names) <= exported
     assert set(_ffi.exported_symbols()) == set(names)
-    assert l.mamba2_abi_version() == 2
+    assert l.mamba2_abi_version() == 3
 
 
 def make_desc(H=128, P=64, N=128, G=8, W=4, L=1, S=4, ssm=1, conv=1, ssm_base=FAKE, conv_base=FAKE):
@@ -206,14 +206,16 @@ def test_prefill_validation(pool):
     assert prefill(pool, [0, 5], [0], start=[-1]) == ARG
     ck = [[2, 3]]
     # a checkpoint inside a chunk (position 300 of 600 at chunk 256) ends that chunk: one chunk
-    # more than a workspace sized for checkpoints on the chunk grid holds
-    n = c_uint64()
-    assert lib().mamba2_prefill_workspace_size(pool, 1, 600, 256, 0, byref(n)) == 0
-    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300, ws_bytes=n.value) == WS
-    assert prefill(pool, [0, 600], [0], start=[100], ck=ck, max_ck=2, interval=256, ws_bytes=n.value) == WS
-    n1 = c_uint64()
-    assert lib().mamba2_prefill_workspace_size(pool, 1, 600, 256, 1, byref(n1)) == 0
-    assert n1.value > n.value
+    # more than a workspace sized for checkpoints on the chunk grid holds; the library's own size
+    # query, given the same host arguments, counts it
+    n = wsize(pool, [0, 600])
+    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300, ws_bytes=n) == WS
+    assert prefill(pool, [0, 600], [0], start=[100], ck=ck, max_ck=2, interval=256, ws_bytes=n) == WS
+    n1 = wsize(pool, [0, 600], ck=ck, interval=300)
+    assert n1 > n
+    assert prefill(pool, [0, 600], [0], ck=ck, max_ck=2, interval=300, ws_bytes=n1 - 1) == WS
+    assert wsize(pool, [0, 600], start=[100], ck=ck, interval=256) > n1     # 256 and 512 both inside chunks
+    assert wsize(pool, [0, 600], ck=ck, interval=256) == n           # 256 and 512: on the grid
     assert prefill(pool, [0, 600], [0], ck=[[0, 3]], max_ck=2, interval=256) == SLOT  # aliases the slot
     assert prefill(pool, [0, 600], [0], ck=[[2, 2]], max_ck=2, interval=256) == SLOT  # repeated
     assert prefill(pool, [0, 600], [0], ck=[[2, 9]], max_ck=2, interval=256) == SLOT  # range
@@ -227,11 +229,25 @@ def test_prefill_validation(pool):
     assert prefill(pool, [0, 5], [0], layer=3) == ARG
 
 
+def wsize(pool, cu, start=None, chunk=256, interval=0, ck=None, expect=0):
+    """mamba2_prefill_workspace_size through the C ABI with the call's host arguments."""
+    n = c_uint64()
+    cu_a = np.asarray(cu, np.int32)
+    sp = None if start is None else np.asarray(start, np.int32)
+    cka = None if ck is None else np.ascontiguousarray(np.asarray(ck, np.int32))
+    st = lib().mamba2_prefill_workspace_size(
+        pool, len(cu_a) - 1, cu_a.ctypes.data_as(c_void_p), None if sp is None else sp.ctypes.data_as(c_void_p),
+        chunk, interval, None if cka is None else cka.ctypes.data_as(c_void_p), 0 if cka is None else cka.shape[1],
+        byref(n))
+    assert st == expect, lib().mamba2_last_error()
+    return n.value
+
+
 def test_workspace_size_formula(pool):
     n = c_uint64()
-    assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 256, 0, byref(n)) == 0
+    n.value = wsize(pool, [0, 8192])
     H, P, N, G, T, Q = 128, 64, 128, 8, 8192, 256
-    nc = T // Q + 1
+    nc = T // Q                                  # the exact chunk count of the call
     planes = 1                                   # bf16 state: single bf16 operand planes
     acts = nc * Q * (H * P + 3 * G * N) * 2 * planes
     vecs = 2 * H * T * 4                         # Delta and its chunk-local cumsum
@@ -239,8 +255,13 @@ def test_workspace_size_formula(pool):
     hin = nc * H * P * N * 2 * planes            # state entering each chunk, operand planes
     total = acts + vecs + cstates + hin
     assert total <= n.value < total + 64 * 1024
-    assert lib().mamba2_prefill_workspace_size(pool, 1, 8192, 20, 0, byref(n)) == UNSUP
-    assert lib().mamba2_prefill_workspace_size(pool, -1, 8192, 256, 0, byref(n)) == ARG
+    wsize(pool, [0, 8192], chunk=20, expect=UNSUP)
+    assert lib().mamba2_prefill_workspace_size(pool, -1, None, None, 256, 0, None, 0, byref(n)) == ARG
+    wsize(pool, [1, 8192], expect=SHAPE)
+    wsize(pool, [0, 8192, 100], expect=SHAPE)
+    wsize(pool, [0, 8192], ck=None, interval=256, expect=0)            # no table: no checkpoints
+    assert lib().mamba2_prefill_workspace_size(pool, 1, None, None, 256, 0, None, 0, byref(n)) == ARG
+    assert wsize(pool, [0, 0]) == 0
 
 
 def test_prefill_rejects_unsupported_head_dim():
@@ -310,8 +331,7 @@ def test_mamba1_pool_family():
     a, b = c_uint64(), c_uint64()
     assert lib().mamba2_pool_info(h, byref(a), byref(b)) == 0
     assert (a.value, b.value) == (D * N * 2, D * (W - 1) * 2)
-    n = c_uint64()
-    assert lib().mamba2_prefill_workspace_size(h, 1, 100, 64, 0, byref(n)) == UNSUP
+    wsize(h, [0, 100], chunk=64, expect=UNSUP)
     assert decode(h) == UNSUP
     assert decode_multi(h) == UNSUP
     m1 = lambda hh, **kw: lib().mamba1_decode_step(hh, kw.get("layer", 0), byref(PARAMS), kw.get("batch", 2), FAKE,
@@ -401,7 +421,7 @@ def test_mamba1_prefill_validation():
     assert n1.value - n0.value >= (1000 // 32 - 100 // 32) * 2 * D * N * 4
     assert n2.value >= n1.value and n0.value % 256 == 0
     assert lib().mamba1_prefill_workspace_size(h, 2, 100, 8, 0, byref(n0)) == UNSUP
-    assert lib().mamba2_prefill_workspace_size(h, 2, 100, 64, 0, byref(n0)) == UNSUP
+    wsize(h, [0, 50, 100], chunk=64, expect=UNSUP)
 
     def call(hh=None, **kw):
         cu = i32(kw.get("cu", [0, 40, 100]))
@@ -446,7 +466,7 @@ def test_header_is_plain_c_and_links_against_the_library(tmp_path):
 #include <string.h>
 #include "mamba2_pool.h"
 int main(void) {
-  if (mamba2_abi_version() != 2) return 1;
+  if (mamba2_abi_version() != 3) return 1;
   m2_pool_desc d;
   memset(&d, 0, sizeof d);
   d.num_layers = 1; d.num_slots = 2; d.nheads = 4; d.head_dim = 8; d.d_state = 16; d.n_groups = 1;
@@ -461,6 +481,13 @@ int main(void) {
   d.n_groups = 2;
   m2_pool* q = 0;
   if (mamba2_pool_create(&d, &q) == M2_OK || strlen(mamba2_last_error()) == 0) return 4;
+  /* workspace of a 600-row prefill at chunk 256, without and with checkpoints at 300 and 600:
+     the one at 300 ends a chunk early, and the library counts it from the same host arguments */
+  int32_t cu[2] = {0, 600}, ck[2] = {1, -1};
+  uint64_t w0 = 0, w1 = 0, w2 = 0;
+  if (mamba2_prefill_workspace_size(p, 1, cu, NULL, 256, 0, NULL, 0, &w0) != M2_OK || w0 == 0) return 5;
+  if (mamba2_prefill_workspace_size(p, 1, cu, NULL, 256, 300, ck, 2, &w1) != M2_OK || w1 <= w0) return 6;
+  if (mamba2_prefill_workspace_size(p, 1, cu, NULL, 256, 512, ck, 2, &w2) != M2_OK || w2 >= w1) return 7;
   mamba2_pool_destroy(p);
   printf("ok\n");
   return 0;

@@ -230,7 +230,7 @@ def test_mamba1_prefill_then_decode_continues_the_sequence():
                                 dev(z[r], "f32"), dev(dt[r], "f32"), yd, slots_host=[2])
         assert rel_err(host(yd)[0], y_ref[t]) <= TOL["f32"], t
     assert rel_err(host(pool.ssm[0, 2, :, 0]), ref.ssm[0, 2]) <= TOL["f32"]
-    assert rel_err(host(pool.conv[0, 2]), ref.conv[0, 2]) <= 1e-6
+    assert np.array_equal(host(pool.conv[0, 2]), ref.conv[0, 2])    # windows are copies: bit for bit
 
 
 def test_mamba1_prefill_at_the_7b_width():

@@ -261,13 +261,13 @@ def test_prefill_is_batch_invariant_and_deterministic(ssm_dtype):
 
 @pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
 def test_large_tables_take_the_upload_path_with_identical_results(ssm_dtype):
-    """Small launch tables ride in the first kernel's arguments; 100 extra empty sequences push them
-    past that room, onto the staged upload.  The real sequences' outputs and states are bit-identical
-    either way, and the empty sequences' slots stay untouched."""
+    """Small launch tables ride in the first kernel's arguments; 300 extra empty sequences push them
+    past that room (about 10 KB), onto several upload launches.  The real sequences' outputs and
+    states are bit-identical either way, and the empty sequences' slots stay untouched."""
     c = _varlen_case(ssm_dtype, 64, seed=501)
     sh = c["sh"]
     W = weights(c["params"])
-    n, extra = len(c["lens"]), 100
+    n, extra = len(c["lens"]), 300
     bits = torch.int16 if ssm_dtype == "bf16" else torch.int32
 
     def run(pad):
@@ -398,3 +398,48 @@ def test_off_grid_checkpoint_equals_the_prefix_prefill_bit_for_bit():
     assert torch.equal(full.conv[0, 24], pref.conv[0, 1])
     for s in (20, 21, 22, 23):
         assert torch.equal(full.ssm[0, s].view(torch.int32), pref.ssm[0, s].view(torch.int32))
+
+
+@pytest.mark.parametrize("ssm_dtype", ["bf16", "f32"])
+def test_checkpoint_windows_next_to_the_start_read_the_initial_window(ssm_dtype):
+    """Checkpoints one and two rows after a seeded sequence's first row (start positions interval-1
+    and interval-2): their conv windows take W-1-tau values from the slot's initial window, which
+    the same call overwrites with the final window.  Every window equals the oracle's bit for bit,
+    states and outputs within tolerance."""
+    sh = synth.Shape(8, 64, 64, 2, 4)
+    rng = np.random.default_rng(501)
+    params = synth.layer_params(rng, sh)
+    interval, Q = 64, 64
+    lens = np.array([100, 70, 3, 130, 1], np.int32)
+    start = np.array([interval - 1, interval - 2, 2 * interval - 1, 3 * interval - 2, interval - 1], np.int32)
+    n = len(lens)
+    has_init = np.ones(n, np.uint8)
+    slots = np.array([2, 4, 6, 8, 10], np.int32)
+    counts = (start + lens) // interval - start // interval
+    ck = np.full((n, int(counts.max())), -1, np.int32)
+    free = iter([s for s in range(40) if s not in set(slots.tolist())])
+    for i in range(n):
+        for k in range(counts[i]):
+            ck[i, k] = next(free)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    u, z, dt = synth._tokens(rng, sh, int(cu[-1]), ssm_dtype)
+    ssm0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.nheads, sh.head_dim, sh.d_state)), ssm_dtype)
+    conv0 = synth.cast_exact(rng.normal(0, 0.1, (n, sh.conv_dim, sh.conv_kernel - 1)), "bf16")
+    log(f"case: checkpoints next to the start, ssm={ssm_dtype}, {int((ck >= 0).sum())} checkpoints")
+    pool = make_pool(sh, 1, 40, ssm_dtype, "bf16")
+    ref = orc.PoolRef(sh, 1, 40, ssm_dtype, "bf16")
+    for i, s in enumerate(slots):
+        put_slot(pool, 0, int(s), ssm0[i], conv0[i])
+        ref.ssm[0, s], ref.conv[0, s] = ssm0[i], conv0[i]
+    before_s, before_c = raw_bytes(pool.ssm), raw_bytes(pool.conv)
+    y = run_prefill(pool, weights(params), cu, slots, has_init, u, z, dt, ssm_dtype, ssm_dtype, start_pos=start,
+                    chunk=Q, interval=interval, ckpt=ck)
+    y_ref = orc.prefill(ref, 0, params, cu, slots, has_init, start, u, z, dt, ssm_dtype, ckpt_interval=interval,
+                        ckpt_slots=ck)
+    tol = TOL[ssm_dtype]
+    assert rel_err(host(y), y_ref) <= tol
+    written = list(slots) + [int(s) for s in ck.ravel() if s >= 0]
+    for s in written:
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+        assert rel_err(host(pool.ssm[0, s]), ref.ssm[0, s]) <= tol, s
+    assert untouched(before_s, pool.ssm, written) and untouched(before_c, pool.conv, written)
