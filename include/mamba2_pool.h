@@ -17,7 +17,8 @@
  *
  * Conventions for every entry point:
  *  - All device pointers are caller-owned device memory; the library never
- *    allocates device memory and never frees caller memory.
+ *    allocates device memory (the one exception is the static scratch array
+ *    of mamba2_prefill_chunked_noalloc) and never frees caller memory.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *    void*; NULL = the default stream).  Pointers must stay valid until the
  *    stream has completed the work.  Host pointers are read before return.
@@ -239,6 +240,29 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
                                  int32_t chunk_size, int32_t ckpt_interval, const int32_t* ckpt_slots,
                                  int32_t max_ckpt, void* workspace, uint64_t workspace_bytes,
                                  void* stream);
+
+/* mamba2_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  The scratch comes from a static device array
+ * of 64 MiB (67,108,864 bytes) that every GPU the library runs on holds from
+ * library load until the process ends; the call itself allocates no device or
+ * pinned memory (its host-side launch tables are built in ordinary host memory).
+ * Arguments, results and errors are those of mamba2_prefill_chunked, plus
+ * M2_ERR_WORKSPACE when mamba2_prefill_workspace_size for the same arguments
+ * exceeds 64 MiB (at the 8B-hybrid layer shape, bf16 state, chunk 256: about
+ * 1.5k tokens), and M2_ERR_HIP if the array's address cannot be looked up.
+ * All calls on one GPU share that GPU's array and nothing in it survives a call:
+ * calls that overlap in time on one GPU (two streams, or two threads) race and
+ * must not be issued. */
+m2_status mamba2_prefill_chunked_noalloc(m2_pool* pool, int32_t layer, const m2_layer_params* params,
+                                         int32_t num_seqs, const int32_t* cu_seqlens, const int32_t* slots,
+                                         const uint8_t* has_initial_state, const int32_t* start_pos,
+                                         const void* x, int64_t x_stride, const void* B, int64_t B_stride,
+                                         const void* C, int64_t C_stride, const void* z, int64_t z_stride,
+                                         const void* dt, int64_t dt_stride, int32_t io_dtype,
+                                         void* y, int64_t y_stride, int32_t y_dtype,
+                                         int32_t chunk_size, int32_t ckpt_interval, const int32_t* ckpt_slots,
+                                         int32_t max_ckpt, void* stream);
 
 /* Copy both state objects of slot src[i] into slot dst[i], bit-exact.  A
  * cached state is copied to a fresh slot instead of being shared, since the

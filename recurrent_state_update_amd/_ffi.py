@@ -55,6 +55,11 @@ _SIGS = {
                                          c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p,
                                          c_int64, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                                          c_uint64, c_void_p]),
+    "mamba2_prefill_chunked_noalloc": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int64,
+                                                 c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_int32,
+                                                 c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                                 c_void_p]),
     "mamba2_checkpoint_states": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p]),
     "mamba2_decode_multi": (c_int32, [c_void_p, c_int32, POINTER(LayerParams), c_int32, c_int32, c_void_p,

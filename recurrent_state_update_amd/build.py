@@ -20,7 +20,8 @@ LIB = os.path.join(HERE, "libmamba2pool.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "decode.hip", "ckpt.hip", "prefill.hip", "int8_store.hip", "spec_decode.hip", "mamba1.hip"]
+SOURCES = ["api.cpp", "decode.hip", "ckpt.hip", "prefill.hip", "int8_store.hip", "spec_decode.hip", "mamba1.hip",
+           "noalloc.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -627,6 +627,33 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   return ok();
 }
 
+m2_status mamba2_prefill_chunked_noalloc(m2_pool* pool, int32_t layer, const m2_layer_params* params,
+                                         int32_t num_seqs, const int32_t* cu_seqlens, const int32_t* slots,
+                                         const uint8_t* has_init, const int32_t* start_pos, const void* x,
+                                         int64_t x_stride, const void* B, int64_t B_stride, const void* C,
+                                         int64_t C_stride, const void* z, int64_t z_stride, const void* dt,
+                                         int64_t dt_stride, int32_t io_dtype, void* y, int64_t y_stride,
+                                         int32_t y_dtype, int32_t chunk_size, int32_t ckpt_interval,
+                                         const int32_t* ckpt_slots, int32_t max_ckpt, void* stream) {
+  if (!pool) return fail(M2_ERR_ARG, "pool is NULL");
+  uint64_t need = 0;
+  if (m2_status st = mamba2_prefill_workspace_size(pool, num_seqs, cu_seqlens, start_pos, chunk_size, ckpt_interval,
+                                                   ckpt_slots, max_ckpt, &need))
+    return st;
+  if (need > m2::kNoAllocScratchBytes)
+    return fail(M2_ERR_WORKSPACE, "the call needs %llu bytes of scratch; the static scratch holds %llu",
+                (unsigned long long)need, (unsigned long long)m2::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = m2::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  }
+  return mamba2_prefill_chunked(pool, layer, params, num_seqs, cu_seqlens, slots, has_init, start_pos, x, x_stride,
+                                B, B_stride, C, C_stride, z, z_stride, dt, dt_stride, io_dtype, y, y_stride, y_dtype,
+                                chunk_size, ckpt_interval, ckpt_slots, max_ckpt, scratch,
+                                need > 0 ? m2::kNoAllocScratchBytes : 0, stream);
+}
+
 m2_status mamba2_checkpoint_states(m2_pool* pool, int32_t layer, int32_t n, const int32_t* src, const int32_t* dst,
                                    const int32_t* src_host, const int32_t* dst_host, void* stream) {
   if (!pool) return fail(M2_ERR_ARG, "pool is NULL");

@@ -54,4 +54,10 @@ hipError_t launch_slot_copy(void* ssm_base, uint64_t ssm_bytes_per_slot, void* c
 // buffer, no host wait).
 hipError_t launch_table_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
 
+// The prefill scratch of the entry point that allocates nothing: a file-scope device array of
+// kNoAllocScratchBytes per GPU.  *ptr receives its device address on the current device (looked
+// up once per device).
+constexpr uint64_t kNoAllocScratchBytes = 64ull << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace m2

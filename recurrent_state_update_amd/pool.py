@@ -276,6 +276,30 @@ class Pool:
             workspace.numel(), _stream()))
         return y
 
+    def prefill_noalloc(self, layer: int, w: LayerWeights, cu_seqlens, slots, has_init, x, B, C, z, dt, y,
+                        start_pos=None, chunk_size: int = 256, ckpt_interval: int = 0, ckpt_slots=None):
+        """prefill() with its scratch in the library's static per-GPU array instead of a workspace."""
+        cu, _ = _host_i32(cu_seqlens)
+        sl, sl_p = _host_i32(slots)
+        hi = np.ascontiguousarray(np.asarray(has_init, dtype=np.uint8))
+        _, sp_p = _host_i32(start_pos)
+        ns = len(sl)
+        max_ck, ck_p = 0, None
+        if ckpt_slots is not None:
+            ck = np.ascontiguousarray(np.asarray(ckpt_slots, dtype=np.int32).reshape(ns, -1))
+            max_ck, ck_p = ck.shape[1], ck.ctypes.data_as(c_void_p)
+        xp, xs = _rows(x, "x")
+        bp, bs = _rows(B, "B")
+        cp, cs = _rows(C, "C")
+        zp, zs = _rows(z, "z")
+        dp, ds = _rows(dt, "dt")
+        yp, ys = _rows(y, "y")
+        check(lib().mamba2_prefill_chunked_noalloc(
+            self._h, layer, byref(w.struct), ns, cu.ctypes.data_as(c_void_p), sl_p, hi.ctypes.data_as(c_void_p),
+            sp_p, xp, xs, bp, bs, cp, cs, zp, zs, dp, ds, _dtype_code(x), yp, ys, _dtype_code(y), chunk_size,
+            ckpt_interval, ck_p, max_ck, _stream()))
+        return y
+
     # ------------------------------------------------------------------ checkpoints
     def int8_store(self, num_entries: int) -> "Int8Store":
         """A zeroed int8 checkpoint store of num_entries entries for this pool's layers."""
