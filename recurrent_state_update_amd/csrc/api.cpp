@@ -447,7 +447,7 @@ m2_status mamba2_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
   p.dt_bias = params->dt_bias;
   p.conv_w = params->conv_w;
   p.conv_b = params->conv_b;
-  const int kMaxRows = 65535;   // grid.y limit
+  const int kMaxRows = 65535;   // rows per launch
   for (int r0 = 0; r0 < batch; r0 += kMaxRows) {
     const int nb = batch - r0 < kMaxRows ? batch - r0 : kMaxRows;
     p.slots = slots + r0;

@@ -1,6 +1,6 @@
 // Fused Mamba2 decode step over a slot pool, gfx950.
 //
-// One workgroup of 512 threads (eight wave64s) per (sequence row, group).
+// One workgroup of 512 threads (eight wave64s) per (sequence row, group), rows fastest in the grid.
 // Phase 1 shifts the conv window of the group's channels (x of its heads,
 // then its B and C), applies the depthwise conv and SiLU, and stages the
 // activations in LDS, together with Delta = softplus(dt + dt_bias) and
@@ -77,8 +77,8 @@ void decode_kernel(DecodeParams a) {
   constexpr int MF = U > LPR ? U / LPR : 1;             // row sums held per lane at the end
   constexpr int DUP = U < LPR ? LPR / U : 1;            // lanes holding the same row sum
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = blockIdx.x;   // rows fastest: consecutive workgroups (dealt round-robin over the XCDs) take
+  const int g = blockIdx.y;   // the same group of different rows (measured 0.8% faster than groups fastest)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -285,7 +285,7 @@ template <typename TS, int N>
 static hipError_t launch_w(const DecodeParams& p, int W, int batch, hipStream_t s) {
   const int hpg = p.H / p.G;
   const size_t lds = decode_lds_bytes(hpg, p.P, N);
-  const dim3 grid(p.G, batch), block(kDecodeThreads);
+  const dim3 grid(batch, p.G), block(kDecodeThreads);
 #define D_LAUNCH(WW)                                                                                      \
   {                                                                                                       \
     if (lds > 65536) {                                                                                    \

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kMultiThreads) void decode_multi_kernel(MultiDecode
   constexpr int MF = U > LPR ? U / LPR : 1;
   constexpr int DUP = U < LPR ? LPR / U : 1;
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = blockIdx.x;   // rows fastest in the grid, as in the single-token decode
+  const int g = blockIdx.y;
   const int K = m.K;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -316,7 +316,7 @@ static hipError_t launch_mw(const MultiDecodeParams& p, int W, int batch, hipStr
   const DecodeParams& d = p.d;
   const int hpg = d.H / d.G;
   const size_t lds = multi_decode_lds_bytes(hpg, d.P, N, p.K);
-  const dim3 grid(d.G, batch), block(kMultiThreads);
+  const dim3 grid(batch, d.G), block(kMultiThreads);
 #define MW_LAUNCH(WW)                                                                                         \
   {                                                                                                           \
     if (lds > 65536) {                                                                                        \
