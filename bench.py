@@ -59,7 +59,7 @@ DECODE_SOURCES = ["recurrent_state_update_amd/csrc/decode.hip", "recurrent_state
 PREFILL_SOURCES = ["recurrent_state_update_amd/csrc/prefill.hip", "recurrent_state_update_amd/csrc/prefill.h",
                    "recurrent_state_update_amd/csrc/device_common.h", "recurrent_state_update_amd/csrc/kernels.h",
                    "recurrent_state_update_amd/csrc/ckpt.hip"]
-PREFILL_KERNELS = ["conv_kernel", "chunk_state_kernel", "state_pass_kernel", "chunk_out"]
+PREFILL_KERNELS = ["bc_kernel", "walk_kernel"]
 COPY_PAIRS = 256      # slot pairs per timed checkpoint copy (the decode pool's 512 slots, halves swapped)
 
 

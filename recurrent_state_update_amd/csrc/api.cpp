@@ -113,46 +113,32 @@ m2_status hip_fail(hipError_t e, const char* what) {
 
 // Prefill tables and workspace carving.
 struct PrefillLayout {
-  uint64_t nc_max, nw_max, planes;
-  uint64_t meta_bytes;   // the packed tables (sequences, chunks, windows) at the start
-  uint64_t off_xT, off_Bt, off_Br, off_Cr, plane_xT, plane_Bt, plane_Br, plane_Cr;
-  uint64_t off_delta, off_dA, off_cstate, off_hin, plane_hin, total;
+  uint64_t meta_bytes;   // the packed tables (sequences, chunks) at the start
+  uint64_t QC, NP, planes;
+  uint64_t off_delta, off_dA, off_Cf, off_Btf, off_Gf, plane_Cf, plane_Btf, total;
 };
 
-// Workspace regions for up to nc chunks and nw conv-window writes.
+// Workspace regions for nc chunks of at most Q tokens over T packed tokens.
 bool prefill_layout(const m2::LayerShape& sh, bool split, int64_t num_seqs, int64_t T, int64_t Q, uint64_t nc,
-                    uint64_t nw, PrefillLayout* L) {
-  (void)T;
-  L->nc_max = nc;
-  L->nw_max = nw;
+                    PrefillLayout* L) {
   L->planes = split ? 2 : 1;
-  L->meta_bytes = align_up(align_up(num_seqs * sizeof(m2::SeqEntry), 16) + align_up(L->nc_max * sizeof(m2::ChunkEntry), 16) +
-                               L->nw_max * sizeof(m2::WindowEntry),
-                           256);
-  const uint64_t rows = L->nc_max * (uint64_t)Q;          // chunk-blocked rows
-  uint64_t v;
-  const uint64_t brows = L->nc_max * (uint64_t)((Q + m2::kPB - 1) / m2::kPB * m2::kPB);   // whole blocks
-  if (!mul_ok(brows, (uint64_t)sh.H * sh.P, &L->plane_xT)) return false;
-  if (!mul_ok(brows, (uint64_t)sh.G * sh.N, &L->plane_Bt)) return false;
-  if (!mul_ok(rows, (uint64_t)sh.G * sh.N, &L->plane_Br)) return false;
-  L->plane_Cr = L->plane_Br;
-  uint64_t off = L->meta_bytes;
-  const uint64_t planes[4] = {L->plane_xT, L->plane_Bt, L->plane_Br, L->plane_Cr};
-  uint64_t* offs[4] = {&L->off_xT, &L->off_Bt, &L->off_Br, &L->off_Cr};
-  for (int i = 0; i < 4; ++i) {
-    if (!mul_ok(planes[i], 2 * L->planes, &v)) return false;
-    *offs[i] = off;
-    off = align_up(off + v, 256);
-  }
+  L->QC = (uint64_t)(Q + 31) / 32 * 32;
+  L->NP = sh.N < 32 ? 32 : (uint64_t)sh.N;
+  L->meta_bytes = align_up(align_up(num_seqs * sizeof(m2::SeqEntry), 16) + nc * sizeof(m2::ChunkEntry), 256);
+  uint64_t v, cg;
+  if (!mul_ok(nc, (uint64_t)sh.G, &cg)) return false;
   if (!mul_ok((uint64_t)T, (uint64_t)sh.H * 4, &v)) return false;
-  L->off_delta = off;
+  L->off_delta = L->meta_bytes;
   L->off_dA = align_up(L->off_delta + v, 256);
-  L->off_cstate = align_up(L->off_dA + v, 256);
-  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N * (split ? 4 : 2), &v)) return false;   // chunk end states
-  L->off_hin = align_up(L->off_cstate + v, 256);
-  if (!mul_ok(L->nc_max, (uint64_t)sh.H * sh.P * sh.N, &L->plane_hin)) return false;
-  if (!mul_ok(L->plane_hin, 2 * L->planes, &v)) return false;
-  L->total = align_up(L->off_hin + v, 256);
+  L->off_Cf = align_up(L->off_dA + v, 256);
+  if (!mul_ok(cg, L->QC * L->NP, &L->plane_Cf)) return false;
+  if (!mul_ok(L->plane_Cf, 2 * L->planes, &v)) return false;
+  L->off_Btf = align_up(L->off_Cf + v, 256);
+  if (!mul_ok(cg, L->QC * (uint64_t)sh.N, &L->plane_Btf)) return false;
+  if (!mul_ok(L->plane_Btf, 2 * L->planes, &v)) return false;
+  L->off_Gf = align_up(L->off_Btf + v, 256);
+  if (!mul_ok(cg, (uint64_t)m2::kGPairs * 64 * 8 * (split ? 4 : 2), &v)) return false;
+  L->total = align_up(L->off_Gf + v, 256);
   return true;
 }
 
@@ -180,7 +166,6 @@ m2_status check_prefill_seqs(int32_t num_seqs, const int32_t* cu_seqlens, const 
 struct PrefillTables {
   std::vector<m2::SeqEntry> seqs;
   std::vector<m2::ChunkEntry> chunks;
-  std::vector<m2::WindowEntry> windows;   // checkpoint conv windows (final windows are per sequence)
 };
 
 void build_prefill_tables(int num_seqs, const int32_t* cu_seqlens, const int32_t* slots, const uint8_t* has_init,
@@ -189,7 +174,6 @@ void build_prefill_tables(int num_seqs, const int32_t* cu_seqlens, const int32_t
   const bool ckpt_on = ckpt_interval > 0 && max_ckpt > 0;
   t->seqs.assign(num_seqs, m2::SeqEntry{});
   t->chunks.clear();
-  t->windows.clear();
   t->chunks.reserve((size_t)(cu_seqlens[num_seqs] / chunk_size) + (size_t)num_seqs);
   std::vector<std::pair<int, int>> ends;   // (rows into the sequence, checkpoint slot or -1)
   for (int s = 0; s < num_seqs; ++s) {
@@ -227,7 +211,6 @@ void build_prefill_tables(int num_seqs, const int32_t* cu_seqlens, const int32_t
       c.ckpt_slot = en.second;
       c.is_last = en.first == len;
       c.pad0 = c.pad1 = 0;
-      if (c.ckpt_slot >= 0) t->windows.push_back({s, en.first, c.ckpt_slot, 0});
       t->chunks.push_back(c);
       ++e.nchunk;
       prev = en.first;
@@ -478,7 +461,7 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, c
                        max_ckpt, &t);
   PrefillLayout L;
   if (!prefill_layout(pool->sh, pool->d.ssm_dtype == M2_F32, num_seqs, cu_seqlens[num_seqs], chunk_size,
-                      t.chunks.size(), t.windows.size(), &L))
+                      t.chunks.size(), &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();
@@ -538,9 +521,8 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
                        max_ckpt, &t);
   const std::vector<m2::SeqEntry>& seqs = t.seqs;
   const std::vector<m2::ChunkEntry>& chunks = t.chunks;
-  const std::vector<m2::WindowEntry>& windows = t.windows;
   PrefillLayout L;
-  if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, chunks.size(), windows.size(), &L))
+  if (!prefill_layout(sh, pool->d.ssm_dtype == M2_F32, num_seqs, T, chunk_size, chunks.size(), &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(M2_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
@@ -548,12 +530,13 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
                 (unsigned long long)L.total);
   if (chunks.empty()) return ok();
+  if ((int64_t)num_seqs * sh.H * (sh.P / m2::prefill_part(sh.P)) > INT32_MAX || (int64_t)chunks.size() * sh.G > INT32_MAX)
+    return fail(M2_ERR_UNSUPPORTED, "too many sequences or chunks for one launch");
 
-  // ---- pack the tables; small ones travel in the conv launch's arguments, larger ones in the
+  // ---- pack the tables; small ones travel in the first launch's arguments, larger ones in the
   // arguments of upload launches ahead of it (no host-to-device copy, no host wait)
   const size_t tab_chunks = align_up(seqs.size() * sizeof(m2::SeqEntry), 16);
-  const size_t tab_windows = tab_chunks + align_up(chunks.size() * sizeof(m2::ChunkEntry), 16);
-  const size_t tab_bytes = align_up(tab_windows + windows.size() * sizeof(m2::WindowEntry), 16);
+  const size_t tab_bytes = align_up(tab_chunks + chunks.size() * sizeof(m2::ChunkEntry), 16);
   if (tab_bytes > L.meta_bytes) return fail(M2_ERR_WORKSPACE, "table packing exceeds its workspace region");
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -561,8 +544,6 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   std::vector<char> packed(tab_bytes, 0);
   memcpy(packed.data(), seqs.data(), seqs.size() * sizeof(m2::SeqEntry));
   memcpy(packed.data() + tab_chunks, chunks.data(), chunks.size() * sizeof(m2::ChunkEntry));
-  if (!windows.empty())
-    memcpy(packed.data() + tab_windows, windows.data(), windows.size() * sizeof(m2::WindowEntry));
   m2::InlineTables inl;
   if (tab_inline) {
     memcpy(inl.w, packed.data(), tab_bytes);
@@ -571,6 +552,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     if (eu != hipSuccess) return hip_fail(eu, "table upload");
   }
 
+  const int yes = esize(y_dtype);
   m2::PrefillParams p;
   p.ssm = static_cast<char*>(pool->d.ssm_base) + (uint64_t)layer * pool->d.num_slots * pool->ssm_slot_bytes;
   p.conv = static_cast<char*>(pool->d.conv_base) + (uint64_t)layer * pool->d.num_slots * pool->conv_slot_bytes;
@@ -578,19 +560,19 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
   p.io_bf16 = io_dtype == M2_BF16;
   p.y_bf16 = y_dtype == M2_BF16;
-  p.zy_vec = aligned16(z) && aligned16(y) && (z_stride * ies) % 16 == 0 && (y_stride * esize(y_dtype)) % 16 == 0 &&
-             z_stride < ((int64_t)1 << 22) && y_stride < ((int64_t)1 << 22);
+  // z and y in 4-element pieces: bases and row pitches aligned to 4 elements
+  p.zy_vec = (reinterpret_cast<uintptr_t>(z) % (4 * ies)) == 0 && (reinterpret_cast<uintptr_t>(y) % (4 * yes)) == 0 &&
+             z_stride % 4 == 0 && y_stride % 4 == 0;
   p.sh = sh;
   p.Q = chunk_size;
+  p.QC = (int)L.QC;
+  p.nparts = sh.P / m2::prefill_part(sh.P);
   p.num_seqs = num_seqs;
   p.num_chunks = (int)chunks.size();
-  p.num_windows = (int)windows.size();
   p.total_tokens = (int)T;
   p.seqs = reinterpret_cast<const m2::SeqEntry*>(ws);
   p.chunks = reinterpret_cast<const m2::ChunkEntry*>(ws + tab_chunks);
-  p.windows = reinterpret_cast<const m2::WindowEntry*>(ws + tab_windows);
   p.tab_chunks = (int)tab_chunks;
-  p.tab_windows = (int)tab_windows;
   p.tab_inline = tab_inline ? (int)tab_bytes : 0;
   p.x = x;
   p.B = B;
@@ -609,19 +591,13 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.dt_bias = params->dt_bias;
   p.conv_w = params->conv_w;
   p.conv_b = params->conv_b;
-  p.xT = reinterpret_cast<uint16_t*>(ws + L.off_xT);
-  p.Bt = reinterpret_cast<uint16_t*>(ws + L.off_Bt);
-  p.Br = reinterpret_cast<uint16_t*>(ws + L.off_Br);
-  p.Cr = reinterpret_cast<uint16_t*>(ws + L.off_Cr);
-  p.xT_plane = (int64_t)L.plane_xT;
-  p.Bt_plane = (int64_t)L.plane_Bt;
-  p.Br_plane = (int64_t)L.plane_Br;
-  p.Cr_plane = (int64_t)L.plane_Cr;
   p.delta = reinterpret_cast<float*>(ws + L.off_delta);
   p.dA = reinterpret_cast<float*>(ws + L.off_dA);
-  p.cstate = ws + L.off_cstate;
-  p.hin = reinterpret_cast<uint16_t*>(ws + L.off_hin);
-  p.hin_plane = (int64_t)L.plane_hin;
+  p.Cf = reinterpret_cast<uint16_t*>(ws + L.off_Cf);
+  p.Btf = reinterpret_cast<uint16_t*>(ws + L.off_Btf);
+  p.Gf = ws + L.off_Gf;
+  p.Cf_plane = (int64_t)L.plane_Cf;
+  p.Btf_plane = (int64_t)L.plane_Btf;
   const hipError_t e = m2::launch_prefill(p, tab_inline ? &inl : nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();

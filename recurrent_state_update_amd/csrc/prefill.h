@@ -13,26 +13,30 @@ struct ChunkEntry {   // one per chunk
   int32_t seq, t0, len, tau0;       // packed start row, rows in chunk, offset inside the sequence
   int32_t ckpt_slot, is_last, pad0, pad1;
 };
-struct WindowEntry {  // one checkpoint conv-window write: window after `tau` rows of sequence `seq` -> slot
-  int32_t seq, tau, slot, pad;
-};
 
-constexpr int kPB = 64;   // tokens per block of the transposed operand planes
+// Row tiles (16 tokens) of a chunk of at most 256 tokens, and the (row tile, 32-token K-step)
+// pairs on or below the diagonal whose C B^T blocks the output product needs: row tile rt takes
+// K-steps 0 .. rt/2, so there are 72 pairs; pair (rt, k) is stored at index pair_index(rt, k).
+constexpr int kMaxRowTiles = 16;
+constexpr int kGPairs = 72;
+__host__ __device__ constexpr int pair_index(int rt, int k) {
+  return (rt & 1) ? ((rt >> 1) + 1) * ((rt >> 1) + 1) + k : (rt >> 1) * ((rt >> 1) + 1) + k;
+}
 
 struct PrefillParams {
   void* ssm;
   void* conv;
   int ssm_bf16, conv_bf16, io_bf16, y_bf16;
-  int zy_vec;          // z and y rows allow 16-byte vector access (aligned bases and row pitches), and
-                       // offsets inside a chunk's rows fit in 32 bits
+  int zy_vec;          // z and y allow 4-element vector access (aligned bases and row pitches)
   LayerShape sh;
-  int Q;               // chunk size
-  int num_seqs, num_chunks, num_windows, total_tokens;
+  int Q;               // chunk size (multiple of 16, at most 256)
+  int QC;              // token capacity of a chunk's operand rows: Q rounded up to 32
+  int nparts;          // head_dim parts per head in the walk (head_dim / part width)
+  int num_seqs, num_chunks, total_tokens;
   const SeqEntry* seqs;        // the tables, packed in this order at the start of the workspace
   const ChunkEntry* chunks;
-  const WindowEntry* windows;
-  int tab_chunks, tab_windows;   // byte offsets of the chunk and window tables from the sequence table
-  int tab_inline;              // > 0: the tables (this many bytes) ride in the conv launch's arguments
+  int tab_chunks;              // byte offset of the chunk table from the sequence table
+  int tab_inline;              // > 0: the tables (this many bytes) ride in the first launch's arguments
                                // and that launch writes them to the workspace; 0: already there
   const void* x;
   const void* B;
@@ -47,30 +51,24 @@ struct PrefillParams {
   const float* dt_bias;
   const float* conv_w;
   const float* conv_b;
-  // workspace arrays.  Post-conv activations as bf16 operand planes (one plane, or hi and lo
-  // planes for fp32-faithful products), chunk-blocked with Q rows per chunk:
-  // x and B transposed in blocks of kPB tokens (QB = ceil(Q / kPB) blocks per chunk), each
-  // block contiguous: [planes][chunks][H][QB][P][kPB] and [planes][chunks][G][QB][N][kPB]
-  uint16_t* xT;
-  uint16_t* Bt;
-  uint16_t* Br;          // [planes][chunks][Q][G*N]    B, channels contiguous
-  uint16_t* Cr;          // [planes][chunks][Q][G*N]    C, channels contiguous
-  int64_t xT_plane, Bt_plane, Br_plane, Cr_plane;   // elements per plane
-  float* delta;          // [H][T]
+  // workspace arrays, per chunk and group: the post-conv B and C rows as bf16 operand planes (one
+  // plane, or hi and lo planes for fp32-faithful products) in the order the output and state
+  // products read them, and the C B^T blocks of the causal pairs
+  float* delta;          // [H][T] Delta = softplus(dt + dt_bias)
   float* dA;             // [H][T] chunk-local inclusive cumsum of Delta*A
-  void* cstate;          // [chunks][H][P][N]: each chunk's end state from a zero state; fp32 with
-                         // hi/lo planes, bf16 otherwise
-  uint16_t* hin;         // [planes][chunks][H][P][N]: state entering each chunk, bf16 operand planes
-  int64_t hin_plane;     // elements per plane
+  uint16_t* Cf;          // [planes][chunks][G][QC][NP]  C rows, d_state permuted inside 32-blocks
+  uint16_t* Btf;         // [planes][chunks][G][N][QC]   B transposed, tokens permuted inside 32-blocks
+  void* Gf;              // [chunks][G][kGPairs][64 lanes][8]: bf16 with bf16 state, fp32 with fp32 state
+  int64_t Cf_plane, Btf_plane;   // elements per plane
 };
-// Tables of up to kInlineTableBytes travel inside the conv launch's kernel arguments: its
+// Tables of up to kInlineTableBytes travel inside the first launch's kernel arguments: its
 // workgroups read them from there and one extra workgroup writes them to the workspace for the
-// later launches, so a call needs no host-to-device copy.
+// later launch, so a call needs no host-to-device copy.
 constexpr int kInlineTableBytes = 3072;
 struct alignas(16) InlineTables {
   int32_t w[kInlineTableBytes / 4];
 };
-struct ConvArgs {   // the conv launch's one kernel argument
+struct BcArgs {   // the first launch's one kernel argument
   PrefillParams p;
   InlineTables t;
 };
@@ -78,5 +76,7 @@ struct ConvArgs {   // the conv launch's one kernel argument
 // `inl` holds the packed tables when p.tab_inline > 0 (else it may be NULL).
 hipError_t launch_prefill(const PrefillParams& p, const InlineTables* inl, hipStream_t s);
 bool prefill_supported(int P, int N, int W);
+// head_dim part width of the walk for head_dim P
+inline int prefill_part(int P) { return P < 32 ? P : 32; }
 
 }  // namespace m2

@@ -249,12 +249,12 @@ def test_workspace_size_formula(pool):
     H, P, N, G, T, Q = 128, 64, 128, 8, 8192, 256
     nc = T // Q                                  # the exact chunk count of the call
     planes = 1                                   # bf16 state: single bf16 operand planes
-    acts = nc * Q * (H * P + 3 * G * N) * 2 * planes
+    bc = nc * G * Q * 2 * N * 2 * planes         # post-conv C rows and B columns per (chunk, group)
     vecs = 2 * H * T * 4                         # Delta and its chunk-local cumsum
-    cstates = nc * H * P * N * 2                 # chunk end states (bf16 with bf16 state)
-    hin = nc * H * P * N * 2 * planes            # state entering each chunk, operand planes
-    total = acts + vecs + cstates + hin
+    cbt = nc * G * 72 * 64 * 8 * 2               # C B^T of the 72 causal (row tile, K-step) pairs, bf16
+    total = bc + vecs + cbt
     assert total <= n.value < total + 64 * 1024
+    assert n.value < 64 * 1024 * 1024            # fits the static scratch of the no-allocation prefill
     wsize(pool, [0, 8192], chunk=20, expect=UNSUP)
     assert lib().mamba2_prefill_workspace_size(pool, -1, None, None, 256, 0, None, 0, byref(n)) == ARG
     wsize(pool, [1, 8192], expect=SHAPE)
