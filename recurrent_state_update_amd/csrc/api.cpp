@@ -530,7 +530,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
     return fail(M2_ERR_WORKSPACE, "workspace has %llu bytes, needs %llu", (unsigned long long)workspace_bytes,
                 (unsigned long long)L.total);
   if (chunks.empty()) return ok();
-  if ((int64_t)num_seqs * sh.H * (sh.P / m2::prefill_part(sh.P)) > INT32_MAX || (int64_t)chunks.size() * sh.G > INT32_MAX)
+  if ((int64_t)num_seqs * sh.H * (sh.P / m2::prefill_part(sh.P, pool->d.ssm_dtype == M2_F32)) > INT32_MAX || (int64_t)chunks.size() * sh.G > INT32_MAX)
     return fail(M2_ERR_UNSUPPORTED, "too many sequences or chunks for one launch");
 
   // ---- pack the tables; small ones travel in the first launch's arguments, larger ones in the
@@ -566,7 +566,7 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.sh = sh;
   p.Q = chunk_size;
   p.QC = (int)L.QC;
-  p.nparts = sh.P / m2::prefill_part(sh.P);
+  p.nparts = sh.P / m2::prefill_part(sh.P, pool->d.ssm_dtype == M2_F32);
   p.num_seqs = num_seqs;
   p.num_chunks = (int)chunks.size();
   p.total_tokens = (int)T;

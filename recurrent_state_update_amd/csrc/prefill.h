@@ -76,7 +76,8 @@ struct BcArgs {   // the first launch's one kernel argument
 // `inl` holds the packed tables when p.tab_inline > 0 (else it may be NULL).
 hipError_t launch_prefill(const PrefillParams& p, const InlineTables* inl, hipStream_t s);
 bool prefill_supported(int P, int N, int W);
-// head_dim part width of the walk for head_dim P
-inline int prefill_part(int P) { return P < 32 ? P : 32; }
+// head_dim part width of the walk for head_dim P: 32 channels with a bf16 state, 16 with an fp32
+// state (whose fp32-faithful operands take twice the registers)
+inline int prefill_part(int P, bool fp32_state) { return fp32_state || P < 32 ? 16 : 32; }
 
 }  // namespace m2

@@ -89,6 +89,16 @@ __device__ __forceinline__ void split2(float v, u16& hi, u16& lo) {
   lo = bits_of(from_f32<bf16>(v - static_cast<float>(h)));
 }
 
+// Two fp32 values -> two bf16 (round to nearest even) in one word, `lo` in the low half (one
+// v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2v));
+}
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // A fragment from bf16 planes in LDS: row `row`, K positions kb + kmap(q, 0..7).
 template <bool SPLIT>
 __device__ __forceinline__ Frag<SPLIT> lds_frag(const u16* base, int64_t plane, int ld, int row, int kb, int q) {
@@ -131,6 +141,22 @@ constexpr int kThreads = 512;
 __device__ __forceinline__ const __attribute__((address_space(4))) unsigned char* arg_tables() {
   typedef const __attribute__((address_space(4))) unsigned char kbyte;
   return (kbyte*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(BcArgs, t);
+}
+
+// The walk's PrefillParams argument, read through a pointer the compiler cannot see through:
+// fields needed only on rare paths (checkpoints, the end of a sequence) are loaded there instead
+// of being held in scalar registers across the whole chunk loop.  (Accesses through pointers read
+// this way are flat ones, so the chunk loop's own accesses keep using the argument itself.)
+__device__ __forceinline__ PrefillParams opaque_params() {
+  typedef const __attribute__((address_space(4))) uint32_t ConstWord;
+  ConstWord* p = (ConstWord*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  // a word-wise copy: only the words a caller reads survive, as scalar loads
+  PrefillParams r;
+  uint32_t* d = reinterpret_cast<uint32_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(PrefillParams) / 4); ++i) d[i] = p[i];
+  return r;
 }
 
 // One workgroup of the first launch: copy the tables from the kernel arguments to the workspace,
@@ -459,19 +485,23 @@ template <bool SPLIT, int PP, int N> struct WalkLds {
   static constexpr int NP = N < 32 ? 32 : N;
   static constexpr int NPL = SPLIT ? 2 : 1;
   static constexpr int RING = kMaxRowTiles * 16 + 8;   // raw rows kept: a chunk and the 3 rows before it
+  static constexpr int MIRROR = 11;                    // ring rows 0..10 are also kept past its end, so
+                                                       // 11 consecutive rows never wrap
   static constexpr int LDR = PP + 4;                   // fp32 pitch of a raw row
   static constexpr int LDX = kMaxRowTiles * 16 + 4;    // u16 pitch of an x^T row (tokens)
   static constexpr int LDH = NP + 4;                   // u16 pitch of a state row
   static constexpr int XPL = PP * LDX;                 // u16 per plane
   static constexpr int HPL = PP * LDH;
-  static constexpr int OFF_RAW = 0;                    // byte offsets
-  static constexpr int OFF_XT = OFF_RAW + RING * LDR * 4;
-  static constexpr int OFF_XW = OFF_XT + NPL * XPL * 2;
-  static constexpr int OFF_XC = OFF_XW + NPL * XPL * 2;   // (c x)^T: x scaled by its column factor
-  static constexpr int OFF_H = OFF_XC + NPL * XPL * 2;
-  static constexpr int OFF_TAB = (OFF_H + NPL * HPL * 2 + 15) / 16 * 16;   // sA2, sB2, sCw, sWs
+  // byte offsets: the arrays read at fixed positions (tables, taps, state rows, planes) first, so
+  // their addresses fit the 16-bit offsets of LDS instructions; the raw-row ring last
+  static constexpr int OFF_TAB = 0;                                        // sA2, sB2, sCw, sWs
   static constexpr int OFF_TAPS = OFF_TAB + 4 * 256 * 4;                  // taps [PP][4], bias [PP]
-  static constexpr int BYTES = OFF_TAPS + PP * 5 * 4;
+  static constexpr int OFF_H = (OFF_TAPS + PP * 5 * 4 + 15) / 16 * 16;
+  static constexpr int OFF_XC = OFF_H + NPL * HPL * 2;                    // (c x)^T: x scaled by its column factor
+  static constexpr int OFF_XT = OFF_XC + NPL * XPL * 2;
+  static constexpr int OFF_XW = OFF_XT + NPL * XPL * 2;
+  static constexpr int OFF_RAW = OFF_XW + NPL * XPL * 2;
+  static constexpr int BYTES = OFF_RAW + (RING + MIRROR) * LDR * 4;
   static constexpr bool FITS = BYTES <= 160 * 1024;
 };
 
@@ -506,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   if (sq.nchunk == 0) return;
   const int c0 = h * P + part * PP;   // first x channel and output column of this part
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), q = lane >> 4, l16 = lane & 15;
-  const int W1 = a.sh.W - 1, I = a.sh.I, GN = G * N, QC = a.QC;
+  const int W1 = a.sh.W - 1, QC = a.QC;
   const int64_t T = a.total_tokens;
   const float Dh = load_uniform(&a.D[h]);
   const bool bc_windows = hh == 0 && part == 0;   // this workgroup also writes the group's B/C windows
@@ -529,14 +559,16 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   }
   // the state: wave w holds columns 16w .. 16w+15 for all PT row tiles (lane: rows 4q + r, column l16)
   const bool st_on = wave < NT;
-  TS* const head_state = static_cast<TS*>(a.ssm) + ((int64_t)sq.slot * H + h) * P * N + (int64_t)part * PP * N;
   floatx4 accS[PT];
+  {
+    const TS* const init = static_cast<const TS*>(a.ssm) + ((int64_t)sq.slot * H + h) * P * N + (int64_t)part * PP * N;
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    accS[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (sq.has_init && st_on) {
+    for (int pt = 0; pt < PT; ++pt) {
+      accS[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (sq.has_init && st_on) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accS[pt][r] = to_f32(head_state[(pt * 16 + 4 * q + r) * N + wave * 16 + l16]);
+        for (int r = 0; r < 4; ++r) accS[pt][r] = to_f32(init[(pt * 16 + 4 * q + r) * N + wave * 16 + l16]);
+      }
     }
   }
 
@@ -545,26 +577,28 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   constexpr int RIT = (kMaxRowTiles * 16 * OCT + kThreads - 1) / kThreads;
   Raw8<IOBF> praw[RIT];
   float pd = 0.f, pa = 0.f, pr = 0.f;
-  auto prefetch = [&](int cidx) {
-    const ChunkEntry nc = load_uniform(&a.chunks[cidx]);
+  auto prefetch_raw = [&](const PrefillParams& ap, const ChunkEntry& nc) {
 #pragma unroll
     for (int it = 0; it < RIT; ++it) {
       const int idx = min(tid + it * kThreads, kMaxRowTiles * 16 * OCT - 1);
       const int row = idx / OCT, o = idx % OCT;
-      praw[it].load(a.x, (int64_t)(nc.t0 + (row < nc.len ? row : 0)) * a.x_stride + c0 + 8 * o);
+      praw[it].load(ap.x, (int64_t)(nc.t0 + (row < nc.len ? row : 0)) * ap.x_stride + c0 + 8 * o);
     }
+  };
+  auto prefetch_tok = [&](const PrefillParams& ap, const ChunkEntry& nc) {
     const int j = min(tid & 255, nc.len - 1);
-    const float* dAh = a.dA + (int64_t)h * T + nc.t0;
-    pd = a.delta[(int64_t)h * T + nc.t0 + j];
+    const float* dAh = ap.dA + (int64_t)h * T + nc.t0;
+    pd = ap.delta[(int64_t)h * T + nc.t0 + j];
     pa = dAh[j];
     pr = dAh[min(j | 31, nc.len - 1)];
   };
-  prefetch(sq.chunk0);
+  const ChunkEntry first = load_uniform(&a.chunks[sq.chunk0]);
+  prefetch_raw(a, first);
+  prefetch_tok(a, first);
   __builtin_amdgcn_sched_barrier(0);
 
   const int rts[2] = {wave, kMaxRowTiles - 1 - wave};
-  const int m0 = wave >> 1;
-  const int mt[2] = {m0, 7 - m0};   // K-steps below each row tile; K-step mt[t] holds its diagonal
+  const int m0 = wave >> 1;           // K-steps below row tile 0 (7 - m0 below row tile 1)
 
   // ---- the output product's operands of a chunk, requested a chunk ahead (after the previous
   // chunk's outputs, while its state product runs): C columns and C B^T blocks of this wave's row
@@ -575,14 +609,15 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   Frag<SPLIT> gb[7], gd[2];
   ZQuad zr[2][PT];
   // Every load is issued unconditionally (row tiles past the chunk read row tile 0 instead): the
-  // in-order memory counter then lets each later wait cover exactly the loads it needs.
-  auto load_ops = [&](int cidx) {
-    const ChunkEntry nc = load_uniform(&a.chunks[cidx]);
+  // in-order memory counter then lets each later wait cover exactly the loads it needs.  The loads
+  // come in steps, spread over the previous chunk's state product: step 0 / 1 is the diagonal
+  // block and z of tile 0 / 1, step 2 + k is C B^T slot k.
+  auto load_op = [&](const PrefillParams& ap, int step, int cidx, const ChunkEntry& nc) {
     const int64_t cgn = (int64_t)cidx * G + g;
     const bool v0 = rts[0] * 16 < nc.len, v1 = rts[1] * 16 < nc.len;
     const int rv[2] = {v0 ? rts[0] : 0, v1 ? rts[1] : 0};   // the row tile each load reads
     auto load_g = [&](int rt, int k, Frag<SPLIT>& dst) {
-      const u16* const gp = static_cast<const u16*>(a.Gf) + ((cgn * kGPairs + pair_index(rt, k)) * 64 + lane) * 8 * NPL;
+      const u16* const gp = static_cast<const u16*>(ap.Gf) + ((cgn * kGPairs + pair_index(rt, k)) * 64 + lane) * 8 * NPL;
       const u16x8 hi = *reinterpret_cast<const u16x8*>(gp);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst.hi[e] = bf_of(hi[e]);
@@ -592,8 +627,8 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         for (int e = 0; e < 8; ++e) dst.lo[e] = bf_of(lo[e]);
       }
     };
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    if (step < 2) {
+      const int t = step;
       const int i = rv[t] * 16 + l16;
       load_g(rv[t], rv[t] >> 1, gd[t]);
       const int64_t row = nc.t0 + (i < nc.len ? i : 0);
@@ -601,32 +636,30 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       for (int pt = 0; pt < PT; ++pt) {
         const int col = c0 + pt * 16 + 4 * q;
         if constexpr (ZYV) {
-          if constexpr (IOBF) zr[t][pt] = *reinterpret_cast<const u16x4*>(static_cast<const u16*>(a.z) + row * a.z_stride + col);
-          else zr[t][pt] = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a.z) + row * a.z_stride + col);
+          if constexpr (IOBF) zr[t][pt] = *reinterpret_cast<const u16x4*>(static_cast<const u16*>(ap.z) + row * ap.z_stride + col);
+          else zr[t][pt] = *reinterpret_cast<const floatx4*>(static_cast<const float*>(ap.z) + row * ap.z_stride + col);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            if constexpr (IOBF) zr[t][pt][r] = static_cast<const u16*>(a.z)[row * a.z_stride + col + r];
-            else zr[t][pt][r] = static_cast<const float*>(a.z)[row * a.z_stride + col + r];
+            if constexpr (IOBF) zr[t][pt][r] = static_cast<const u16*>(ap.z)[row * ap.z_stride + col + r];
+            else zr[t][pt][r] = static_cast<const float*>(ap.z)[row * ap.z_stride + col + r];
           }
         }
       }
-    }
-#pragma unroll
-    for (int k = 0; k < 7; ++k) {
+    } else {
       // slot k: a below-diagonal block of tile 0 (k < m0) or of tile 1 (K-step 6 - k)
+      const int k = step - 2;
       const int rt = k < m0 ? rv[0] : rv[1];
       const int kk = k < m0 ? k : 6 - k;
       load_g(rt, min(kk, rt >> 1), gb[k]);
     }
   };
-  load_ops(sq.chunk0);
-  // the C columns of this wave's row tiles (requested at the start of each chunk's conv phase)
-  auto load_c = [&](int cidx) {
-    const ChunkEntry nc = load_uniform(&a.chunks[cidx]);
-    const u16* const cfb = a.Cf + ((int64_t)cidx * G + g) * QC * NP;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+  for (int st = 0; st < 9; ++st) load_op(a, st, sq.chunk0, first);
+  // the C columns of this wave's row tiles (requested at the start of each chunk's conv phase)
+  auto load_c = [&](const PrefillParams& ap, int t, int cidx, const ChunkEntry& nc) {
+    const u16* const cfb = ap.Cf + ((int64_t)cidx * G + g) * QC * NP;
+    {
       const int i = (rts[t] * 16 < nc.len ? rts[t] : 0) * 16 + l16;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
@@ -635,9 +668,42 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) cfr[t][ks].hi[e] = bf_of(hi[e]);
         if (SPLIT) {
-          const u16x8 lo = *reinterpret_cast<const u16x8*>(p + a.Cf_plane);
+          const u16x8 lo = *reinterpret_cast<const u16x8*>(p + ap.Cf_plane);
 #pragma unroll
           for (int e = 0; e < 8; ++e) cfr[t][ks].lo[e] = bf_of(lo[e]);
+        }
+      }
+    }
+  };
+
+  // A chunk's gated outputs stay in registers until the next chunk's conv phase issues their
+  // stores (lane: channels c0 + 16 pt + 4q .. +3 of packed row yrow[t], -1 for none).  The waits
+  // then see only loads in flight, except the first wait of the output phase, by which time the
+  // stores issued before the conv have long completed: loads and stores share one counter, and
+  // any wait while both are in flight has to wait for all of them.
+  floatx4 ys[2][PT];
+  int yrow[2] = {-1, -1};
+  auto store_y = [&](const PrefillParams& ap) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (yrow[t] < 0) continue;
+      const int64_t row = yrow[t];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int col = c0 + pt * 16 + 4 * q;
+        const floatx4 yv = ys[t][pt];
+        if constexpr (ZYV) {
+          if (ap.y_bf16) {
+            u16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = bits_of(from_f32<bf16>(yv[r]));
+            *reinterpret_cast<u16x4*>(static_cast<u16*>(ap.y) + row * ap.y_stride + col) = o;
+          } else {
+            *reinterpret_cast<floatx4*>(static_cast<float*>(ap.y) + row * ap.y_stride + col) = yv;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) store_any(ap.y, row * ap.y_stride + col + r, yv[r], ap.y_bf16);
         }
       }
     }
@@ -646,19 +712,30 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   for (int kc = 0; kc < sq.nchunk; ++kc) {
     const int cidx = sq.chunk0 + kc;
     const ChunkEntry ch = load_uniform(&a.chunks[cidx]);
+    const int cnext = sq.chunk0 + min(kc + 1, sq.nchunk - 1);   // past the last chunk: itself again
+    const ChunkEntry nx = load_uniform(&a.chunks[cnext]);
     const int len = ch.len;
     const float alast = load_uniform(&a.dA[(int64_t)h * T + ch.t0 + len - 1]);
     const int64_t cg = (int64_t)cidx * G + g;
 
-    // ---- A. raw rows into the ring, token tables
+    // ---- A. raw rows into the ring (zeros for the rows past the chunk, so that every conv output
+    // there is finite and the zero token weights past the chunk cancel it), token tables
 #pragma unroll
     for (int it = 0; it < RIT; ++it) {
       const int idx = tid + it * kThreads;
       const int row = idx / OCT, o = idx % OCT;
-      if (idx < kMaxRowTiles * 16 * OCT && row < len) {
-        float* d = sRaw + ((ch.tau0 + row) % RING) * LDR + 8 * o;
-        *reinterpret_cast<floatx4*>(d) = floatx4{praw[it].at(0), praw[it].at(1), praw[it].at(2), praw[it].at(3)};
-        *reinterpret_cast<floatx4*>(d + 4) = floatx4{praw[it].at(4), praw[it].at(5), praw[it].at(6), praw[it].at(7)};
+      if (idx < kMaxRowTiles * 16 * OCT) {
+        const int pos = (ch.tau0 + row) % RING;
+        const bool in = row < len;
+        const floatx4 v0 = in ? floatx4{praw[it].at(0), praw[it].at(1), praw[it].at(2), praw[it].at(3)} : floatx4{0.f, 0.f, 0.f, 0.f};
+        const floatx4 v1 = in ? floatx4{praw[it].at(4), praw[it].at(5), praw[it].at(6), praw[it].at(7)} : floatx4{0.f, 0.f, 0.f, 0.f};
+        float* d = sRaw + pos * LDR + 8 * o;
+        *reinterpret_cast<floatx4*>(d) = v0;
+        *reinterpret_cast<floatx4*>(d + 4) = v1;
+        if (pos < L::MIRROR) {
+          *reinterpret_cast<floatx4*>(d + RING * LDR) = v0;
+          *reinterpret_cast<floatx4*>(d + RING * LDR + 4) = v1;
+        }
       }
     }
     if (tid < 256) {
@@ -672,7 +749,9 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 
     const bool vt[2] = {rts[0] * 16 < len, rts[1] * 16 < len};
     __builtin_amdgcn_sched_barrier(0);
-    load_c(cidx);
+    load_c(a, 0, cidx, ch);   // tile 1's C columns follow under tile 0's products
+    __builtin_amdgcn_sched_barrier(0);
+    store_y(a);   // the previous chunk's outputs
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- B. conv of the part's x channels: thread (channel pair cp, token octet to)
@@ -681,53 +760,53 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       const int cp = tid % NCP, to = tid / NCP;
       if (to < kMaxRowTiles * 2) {
         const int j0 = 8 * to, cl = 2 * cp;
-        float rw[11][2];   // raw rows j0-3 .. j0+7 of the two channels (unused past the chunk)
+        float rw[11][2];   // raw rows j0-3 .. j0+7 of the two channels (zeros past the chunk)
         {
-          int row = (ch.tau0 + j0 - 3 + RING) % RING;
+          const float* src = sRaw + ((ch.tau0 + j0 - 3 + RING) % RING) * LDR + cl;   // mirrored: no wrap
 #pragma unroll
           for (int k = 0; k < 11; ++k) {
-            const float* src = sRaw + row * LDR + cl;
-            rw[k][0] = src[0];
-            rw[k][1] = src[1];
-            row = row + 1 == RING ? 0 : row + 1;
+            rw[k][0] = src[k * LDR];
+            rw[k][1] = src[k * LDR + 1];
           }
         }
-        const bool any = j0 < len;
-        // per channel: x, (w x) and (c x) of the 8 tokens, each as one plane's 8-token piece
+        // per channel: x, (w x) and (c x) of the 8 tokens, each as one plane's 8-token piece (past
+        // the chunk x is finite and both weights are zero)
+        const floatx4 ws0 = *reinterpret_cast<const floatx4*>(sWs + j0), ws1 = *reinterpret_cast<const floatx4*>(sWs + j0 + 4);
+        const floatx4 cw0 = *reinterpret_cast<const floatx4*>(sCw + j0), cw1 = *reinterpret_cast<const floatx4*>(sCw + j0 + 4);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const floatx4 w4 = *reinterpret_cast<const floatx4*>(sTap + (cl + e) * 4);
           const float b = sBias[cl + e];
-          u16x8 xh, xl, wh, wl, ch8, cl8;
+          float xv[8], wv[8], cv[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
             float x = b;
 #pragma unroll
             for (int k = 0; k < 4; ++k) x += w4[k] * rw[r + k][e];
-            x = (any && j0 + r < len) ? silu(x) : 0.f;
-            const float vals[3] = {x, x * sWs[j0 + r], x * sCw[j0 + r]};
-#pragma unroll
-            for (int pl3 = 0; pl3 < 3; ++pl3) {
-              u16 hi, lo = 0;
-              if (SPLIT) split2(vals[pl3], hi, lo);
-              else hi = bits_of(from_f32<bf16>(vals[pl3]));
-              if (pl3 == 0) { xh[r] = hi; xl[r] = lo; }
-              else if (pl3 == 1) { wh[r] = hi; wl[r] = lo; }
-              else { ch8[r] = hi; cl8[r] = lo; }
-            }
+            x = silu(x);
+            xv[r] = x;
+            wv[r] = x * (r < 4 ? ws0[r] : ws1[r - 4]);
+            cv[r] = x * (r < 4 ? cw0[r] : cw1[r - 4]);
           }
-          auto put = [&](u16* base, const u16x8& h8, const u16x8& l8) {
-            u16* d = base + (cl + e) * LDX + j0;
-            *reinterpret_cast<u16x4*>(d) = u16x4{h8[0], h8[1], h8[2], h8[3]};
-            *reinterpret_cast<u16x4*>(d + 4) = u16x4{h8[4], h8[5], h8[6], h8[7]};
+          auto put = [&](u16* base, const float (&v)[8]) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              hw[m] = pack_bf16x2(v[2 * m], v[2 * m + 1]);
+              if (SPLIT) lw[m] = pack_bf16x2(v[2 * m] - lo_f32(hw[m]), v[2 * m + 1] - hi_f32(hw[m]));
+            }
+            uint32_t* d = reinterpret_cast<uint32_t*>(base + (cl + e) * LDX + j0);
+            *reinterpret_cast<uint2*>(d) = uint2{hw[0], hw[1]};
+            *reinterpret_cast<uint2*>(d + 2) = uint2{hw[2], hw[3]};
             if (SPLIT) {
-              *reinterpret_cast<u16x4*>(d + L::XPL) = u16x4{l8[0], l8[1], l8[2], l8[3]};
-              *reinterpret_cast<u16x4*>(d + L::XPL + 4) = u16x4{l8[4], l8[5], l8[6], l8[7]};
+              uint32_t* dl = reinterpret_cast<uint32_t*>(base + L::XPL + (cl + e) * LDX + j0);
+              *reinterpret_cast<uint2*>(dl) = uint2{lw[0], lw[1]};
+              *reinterpret_cast<uint2*>(dl + 2) = uint2{lw[2], lw[3]};
             }
           };
-          put(sXT, xh, xl);
-          put(sXW, wh, wl);
-          put(sXC, ch8, cl8);
+          put(sXT, xv);
+          put(sXW, wv);
+          put(sXC, cv);
         }
       }
     }
@@ -753,29 +832,39 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     const int nkb = (len + 31) / 32;
     Frag<SPLIT> bt[kMaxRowTiles / 2];
     const u16* const btb = a.Btf + (cg * N + (st_on ? wave : 0) * 16 + l16) * QC + 8 * q;
-    auto load_bt = [&]() {   // unconditional: K-steps past the chunk read its last K-step again
+    // K-steps k0 .. k1-1, unconditional: K-steps past the chunk read its last K-step again
+    auto load_bt = [&](const PrefillParams& ap, int k0, int k1) {
 #pragma unroll
-      for (int kb = 0; kb < kMaxRowTiles / 2; ++kb) {
+      for (int kb = k0; kb < k1; ++kb) {
         const int kr = min(kb, nkb - 1);
         const u16x8 hi = *reinterpret_cast<const u16x8*>(btb + 32 * kr);
 #pragma unroll
         for (int e = 0; e < 8; ++e) bt[kb].hi[e] = bf_of(hi[e]);
         if (SPLIT) {
-          const u16x8 lo = *reinterpret_cast<const u16x8*>(btb + a.Btf_plane + 32 * kr);
+          const u16x8 lo = *reinterpret_cast<const u16x8*>(btb + ap.Btf_plane + 32 * kr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) bt[kb].lo[e] = bf_of(lo[e]);
         }
       }
     };
-    const int cnext = sq.chunk0 + min(kc + 1, sq.nchunk - 1);   // past the last chunk: itself again
-    __builtin_amdgcn_sched_barrier(0);
-    if (!SPLIT) load_bt();
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- C. outputs of this wave's row tiles
+    // ---- C. outputs of this wave's row tiles, one copy of the code per number of K-steps below
+    // tile 0, so the K-step loops have fixed trip counts.
+    auto phase_c = [&](auto m0c) {
+    constexpr int M0 = decltype(m0c)::value;
+    constexpr int MT[2] = {M0, 7 - M0};   // K-steps below each row tile; K-step MT[t] holds its diagonal
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (!vt[t]) continue;
+      if (!vt[t]) {
+        yrow[t] = -1;
+        if (t == 0) {
+          load_c(a, 1, cidx, ch);
+          if (!SPLIT) load_bt(a, 0, 8);
+        } else if (SPLIT) {
+          load_bt(a, 0, 4);
+        }
+        continue;
+      }
       const int rt = rts[t];
       const int i = rt * 16 + l16;
       const float a2i = sA2[i];
@@ -791,10 +880,19 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         for (int ks = 0; ks < NK; ++ks)
           acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sH, L::HPL, LDH, pt * 16 + l16, 32 * ks, q), cfr[t][ks], acc[pt]);
       }
+      // the next operands, requested under this tile's products: tile 1's C columns and the state
+      // product's B^T (bf16: all of it; fp32-faithful planes: half here, half at its start)
+      __builtin_amdgcn_sched_barrier(0);
+      if (t == 0) {
+        load_c(a, 1, cidx, ch);
+        if (!SPLIT) load_bt(a, 0, 8);
+      } else if (SPLIT) {
+        load_bt(a, 0, 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float aprev = 0.f;
 #pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        if (k >= mt[t]) break;
+      for (int k = 0; k < MT[t]; ++k) {
         const int jk = 32 * k;
         const float aR = sA2[jk + 31];
         const float sk = fast_exp2(aR - aprev);
@@ -818,7 +916,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       // the causal mask and D on the diagonal; the other half lies entirely below the tile (odd
       // tiles) or entirely above it (even tiles)
       {
-        const int jk = 32 * mt[t];
+        const int jk = 32 * MT[t];
         const int dsel = l16 - 4 * q;
         const floatx4 bd = *reinterpret_cast<const floatx4*>(&sB2[16 * rt + 4 * q]);
         float gv[8];
@@ -849,74 +947,59 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         for (int pt = 0; pt < PT; ++pt)
           acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXT, L::XPL, LDX, pt * 16 + l16, jk, q), mf, acc[pt]);
       }
-      // gate and store: lane holds channels c0 + 16 pt + 4q .. +3 of token i
-      if (i < len) {
-        const int64_t row = ch.t0 + i;
+      // the gate: lane holds channels c0 + 16 pt + 4q .. +3 of token i
+      yrow[t] = i < len ? ch.t0 + i : -1;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const int col = c0 + pt * 16 + 4 * q;
-          float zv[4];
+      for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if constexpr (IOBF) zv[r] = f_of(zr[t][pt][r]);
-            else zv[r] = zr[t][pt][r];
-          }
-          float yv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) yv[r] = acc[pt][r] * silu(zv[r]);
-          if constexpr (ZYV) {
-            if (a.y_bf16) {
-              u16x4 o;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[r] = bits_of(from_f32<bf16>(yv[r]));
-              *reinterpret_cast<u16x4*>(static_cast<u16*>(a.y) + row * a.y_stride + col) = o;
-            } else {
-              *reinterpret_cast<floatx4*>(static_cast<float*>(a.y) + row * a.y_stride + col) =
-                  floatx4{yv[0], yv[1], yv[2], yv[3]};
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) store_any(a.y, row * a.y_stride + col + r, yv[r], a.y_bf16);
-          }
+        for (int r = 0; r < 4; ++r) {
+          float zv;
+          if constexpr (IOBF) zv = f_of(zr[t][pt][r]);
+          else zv = zr[t][pt][r];
+          ys[t][pt][r] = acc[pt][r] * silu(zv);
         }
       }
     }
+    };
+    switch (m0) {
+      case 0: phase_c(std::integral_constant<int, 0>{}); break;
+      case 1: phase_c(std::integral_constant<int, 1>{}); break;
+      case 2: phase_c(std::integral_constant<int, 2>{}); break;
+      default: phase_c(std::integral_constant<int, 3>{}); break;
+    }
 
-    // Loads and stores share the in-order memory counter, and the compiler treats it as out of
-    // order (waits for everything) while stores of the wave are in flight.  So the output stores
-    // are drained here, once, and only then the next chunk's rows and operands are requested: the
-    // waits for them, one chunk later, see loads only and cover exactly what they need.
-    __builtin_amdgcn_s_waitcnt(0);
-    // issued in the order the next chunk consumes them (the scheduler may not reorder across the
-    // barriers): its raw rows and token values, then its C B^T blocks and z
-    __builtin_amdgcn_sched_barrier(0);
-    prefetch(cnext);
-    __builtin_amdgcn_sched_barrier(0);
-    load_ops(cnext);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- D. the state: h <- exp(a_last) h + (w x)^T B over the chunk's tokens
-    if (SPLIT) load_bt();
-    if (st_on) {
-      const float dec = fast_exp2(alast * kLog2e);
+    // ---- D. the state: h <- exp(a_last) h + (w x)^T B over the chunk's tokens.  Between its
+    // K-steps the next chunk's loads are issued, in the order that chunk consumes them (raw rows
+    // and token values, then the output operands), so the memory pipeline drains under the MFMAs.
+    if (SPLIT) load_bt(a, 4, 8);
+    const float dec = fast_exp2(alast * kLog2e);
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accS[pt][r] *= dec;
+      for (int r = 0; r < 4; ++r) accS[pt][r] *= dec;
+    // every K-step, also past a short chunk's end: there the (w x) rows are zeros and the B^T
+    // operand repeats the last K-step, so the products add nothing and no branch is needed
 #pragma unroll
-      for (int kb = 0; kb < kMaxRowTiles / 2; ++kb) {
-        if (kb < nkb) {
+    for (int kb = 0; kb < kMaxRowTiles / 2; ++kb) {
+      if (st_on) {
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-            accS[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXW, L::XPL, LDX, pt * 16 + l16, 32 * kb, q), bt[kb], accS[pt]);
-        }
+        for (int pt = 0; pt < PT; ++pt)
+          accS[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXW, L::XPL, LDX, pt * 16 + l16, 32 * kb, q), bt[kb], accS[pt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb == 0) prefetch_raw(a, nx);
+      if (kb == 1) prefetch_tok(a, nx);
+      if (kb >= 1) load_op(a, kb - 1, cnext, nx);
+      if (kb == 7) load_op(a, 7, cnext, nx), load_op(a, 8, cnext, nx);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- E. a checkpoint after this chunk: the state (rounded) and the raw-input window
     if (ch.ckpt_slot >= 0) {
+      const PrefillParams ar = opaque_params();
+      const SeqEntry sqr = load_uniform(&ar.seqs[s]);
       if (st_on) {
-        TS* const dst = static_cast<TS*>(a.ssm) + ((int64_t)ch.ckpt_slot * H + h) * P * N + (int64_t)part * PP * N;
+        TS* const dst = static_cast<TS*>(ar.ssm) + ((int64_t)ch.ckpt_slot * H + h) * P * N + (int64_t)part * PP * N;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
@@ -925,21 +1008,22 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       const int tau = ch.tau0 + len;
       for (int i = tid; i < W1 * PP; i += kThreads) {
         const int kk = i / PP, cl = i % PP;
-        window_store(a, ch.ckpt_slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
+        window_store(ar, ch.ckpt_slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
       }
       if (bc_windows) {
+        const int I = ar.sh.I, GN = ar.sh.G * N;
         for (int i = tid; i < W1 * 2 * N; i += kThreads) {
           const int kk = i / (2 * N), cl = i % (2 * N);
           const bool isC = cl >= N;
           const int n = cl % N, cc = I + (isC ? GN : 0) + g * N + n, off = tau - W1 + kk;
           float v;
           if (off >= 0) {
-            v = isC ? load_any(a.C, (int64_t)(sq.t0 + off) * a.C_stride + g * N + n, a.io_bf16)
-                    : load_any(a.B, (int64_t)(sq.t0 + off) * a.B_stride + g * N + n, a.io_bf16);
+            v = isC ? load_any(ar.C, (int64_t)(sqr.t0 + off) * ar.C_stride + g * N + n, ar.io_bf16)
+                    : load_any(ar.B, (int64_t)(sqr.t0 + off) * ar.B_stride + g * N + n, ar.io_bf16);
           } else {
-            v = sq.has_init ? window_value(a, sq.slot, cc, W1 + off) : 0.f;
+            v = sqr.has_init ? window_value(ar, sqr.slot, cc, W1 + off) : 0.f;
           }
-          window_store(a, ch.ckpt_slot, cc, kk, v);
+          window_store(ar, ch.ckpt_slot, cc, kk, v);
         }
       }
       // drain the checkpoint stores (this also waits for the next chunk's prefetches, on
@@ -949,18 +1033,22 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     lds_sync();   // every read of this chunk's LDS rows is done
   }
 
+  store_y(a);   // the last chunk's outputs
   // ---- the final state and window into the sequence's slot
+  const PrefillParams ar = opaque_params();
+  const SeqEntry sqr = load_uniform(&ar.seqs[s]);
   if (st_on) {
+    TS* const head_state = static_cast<TS*>(ar.ssm) + ((int64_t)sqr.slot * H + h) * P * N + (int64_t)part * PP * N;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) head_state[(pt * 16 + 4 * q + r) * N + wave * 16 + l16] = from_f32<TS>(accS[pt][r]);
   }
   {
-    const int tau = sq.len;
+    const int tau = sqr.len;
     for (int i = tid; i < W1 * PP; i += kThreads) {
       const int kk = i / PP, cl = i % PP;
-      window_store(a, sq.slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
+      window_store(ar, sqr.slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
     }
   }
   if (bc_windows) {
@@ -968,7 +1056,8 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     // than W-1 rows), so every value is read before any is written
     constexpr int BIT = (3 * 2 * N + kThreads - 1) / kThreads;
     float vals[BIT];
-    const int tau = sq.len;
+    const int I = ar.sh.I, GN = ar.sh.G * N;
+    const int tau = sqr.len;
 #pragma unroll
     for (int b = 0; b < BIT; ++b) {
       const int i = tid + b * kThreads;
@@ -978,10 +1067,10 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         const bool isC = cl >= N;
         const int n = cl % N, cc = I + (isC ? GN : 0) + g * N + n, off = tau - W1 + kk;
         if (off >= 0) {
-          vals[b] = isC ? load_any(a.C, (int64_t)(sq.t0 + off) * a.C_stride + g * N + n, a.io_bf16)
-                        : load_any(a.B, (int64_t)(sq.t0 + off) * a.B_stride + g * N + n, a.io_bf16);
-        } else if (sq.has_init) {
-          vals[b] = window_value(a, sq.slot, cc, W1 + off);
+          vals[b] = isC ? load_any(ar.C, (int64_t)(sqr.t0 + off) * ar.C_stride + g * N + n, ar.io_bf16)
+                        : load_any(ar.B, (int64_t)(sqr.t0 + off) * ar.B_stride + g * N + n, ar.io_bf16);
+        } else if (sqr.has_init) {
+          vals[b] = window_value(ar, sqr.slot, cc, W1 + off);
         }
       }
     }
@@ -992,7 +1081,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       if (i < W1 * 2 * N) {
         const int kk = i / (2 * N), cl = i % (2 * N);
         const bool isC = cl >= N;
-        window_store(a, sq.slot, I + (isC ? GN : 0) + g * N + cl % N, kk, vals[b]);
+        window_store(ar, sqr.slot, I + (isC ? GN : 0) + g * N + cl % N, kk, vals[b]);
       }
     }
   }
@@ -1037,9 +1126,13 @@ template <bool SPLIT, int N>
 static hipError_t launch_sn(const PrefillParams& p, const InlineTables* inl, hipStream_t s) {
   hipError_t e = p.io_bf16 ? launch_bc<SPLIT, N, true>(p, inl, s) : launch_bc<SPLIT, N, false>(p, inl, s);
   if (e != hipSuccess) return e;
-  if (prefill_part(p.sh.P) == 16)
+  if constexpr (SPLIT) {
     return p.io_bf16 ? launch_walk<SPLIT, 16, N, true>(p, s) : launch_walk<SPLIT, 16, N, false>(p, s);
-  return p.io_bf16 ? launch_walk<SPLIT, 32, N, true>(p, s) : launch_walk<SPLIT, 32, N, false>(p, s);
+  } else {
+    if (prefill_part(p.sh.P, false) == 16)
+      return p.io_bf16 ? launch_walk<SPLIT, 16, N, true>(p, s) : launch_walk<SPLIT, 16, N, false>(p, s);
+    return p.io_bf16 ? launch_walk<SPLIT, 32, N, true>(p, s) : launch_walk<SPLIT, 32, N, false>(p, s);
+  }
 }
 
 template <int N>
@@ -1057,7 +1150,7 @@ hipError_t launch_prefill(const PrefillParams& p, const InlineTables* inl, hipSt
   if (p.num_chunks == 0) return hipSuccess;
   if (p.tab_inline < 0 || p.tab_inline > kInlineTableBytes || p.tab_inline % 16 != 0 || (p.tab_inline > 0 && !inl))
     return hipErrorInvalidValue;
-  if (!prefill_supported(p.sh.P, p.sh.N, p.sh.W) || p.nparts * prefill_part(p.sh.P) != p.sh.P || p.Q > 256 ||
+  if (!prefill_supported(p.sh.P, p.sh.N, p.sh.W) || p.nparts * prefill_part(p.sh.P, !p.ssm_bf16) != p.sh.P || p.Q > 256 ||
       p.QC % 32 != 0 || p.QC < p.Q)
     return hipErrorInvalidValue;
   switch (p.sh.N) {
