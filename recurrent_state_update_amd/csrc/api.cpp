@@ -216,6 +216,20 @@ void build_prefill_tables(int num_seqs, const int32_t* cu_seqlens, const int32_t
       prev = en.first;
     }
   }
+  // The walk launch takes the sequences in table order: longest first, so the long walks start
+  // early and the short ones fill in behind them.  (Chunks keep their order; each names its entry.)
+  std::vector<int> order(num_seqs);
+  for (int s = 0; s < num_seqs; ++s) order[s] = s;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return t->seqs[x].nchunk > t->seqs[y].nchunk; });
+  std::vector<int> where(num_seqs);
+  std::vector<m2::SeqEntry> sorted(num_seqs);
+  for (int k = 0; k < num_seqs; ++k) {
+    sorted[k] = t->seqs[order[k]];
+    where[order[k]] = k;
+  }
+  t->seqs.swap(sorted);
+  for (m2::ChunkEntry& c : t->chunks) c.seq = where[c.seq];
 }
 
 // Dense sizes of an int8 store of num_entries entries for this pool.

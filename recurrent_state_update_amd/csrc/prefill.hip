@@ -127,11 +127,14 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 // Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups round-robin over
-// the 8 XCDs, each with its own L2).  This maps b to a logical index so that every XCD receives
-// one contiguous range of logical indices (a bijection on [0, n)).
-__device__ __forceinline__ int xcd_contiguous(int b, int n) {
-  const int x = b % 8, full = n / 8, rem = n % 8;
-  return x * full + min(x, rem) + b / 8;
+// the 8 XCDs, each with its own L2).  This maps b to a logical index in units of `unit`
+// consecutive indices: unit u runs on XCD u % 8, and each XCD takes its units in order, so work
+// listed first starts first on every XCD (a tail of fewer than 8 units keeps the dispatch order).
+// A bijection on [0, n), n a multiple of `unit`.
+__device__ __forceinline__ int xcd_units(int b, int n, int unit) {
+  const int x = b % 8, j = b / 8, rounds = n / (8 * unit);
+  if (j >= rounds * unit) return b;
+  return (8 * (j / unit) + x) * unit + j % unit;
 }
 
 constexpr int kThreads = 512;
@@ -233,7 +236,8 @@ template <bool SPLIT, int N> struct BcLds {
   static constexpr int NPL = SPLIT ? 2 : 1;
   static constexpr int LDB = NP + 4;                       // u16 pitch of the post-conv B rows
   static constexpr int PLANE = kMaxRowTiles * 16 * LDB;   // u16
-  static constexpr int BYTES = NPL * PLANE * 2;
+  static constexpr int OFF_TAPS = NPL * PLANE * 2;         // bytes: taps [2N][4], then bias [2N]
+  static constexpr int BYTES = OFF_TAPS + 2 * N * 5 * 4;
 };
 
 template <bool SPLIT, int N, bool IOBF>
@@ -262,94 +266,136 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
   const int64_t cg = (int64_t)c * G + g;
   u16* const cf = a.Cf + cg * QC * NP;
 
-  // a. conv + SiLU: octets [0, NP/8) are B channels, [NP/8, NP/4) C channels (past N: zeros)
-  constexpr int OCT = NP / 8;
-  const int ntb = (len + 7) / 8;
-  for (int item = tid; item < 2 * OCT * ntb; item += kThreads) {
-    const int o = item % (2 * OCT), tb = item / (2 * OCT);
-    const bool isC = o >= OCT;
-    const int n0 = (o % OCT) * 8, j0 = tb * 8;
-    float v[8][8];
-    if (n0 < N) {
-      const void* src = isC ? a.C : a.B;
-      const int64_t stride = isC ? a.C_stride : a.B_stride;
-      const int64_t col = (int64_t)g * N + n0;
-      const int cc = I + (isC ? GN : 0) + g * N + n0;
-      Raw8<IOBF> raw[11];   // rows j0 - 3 .. j0 + 7 of the chunk
+  // Requests first, work second: the step sizes' dt values, the group's conv taps (to LDS), and
+  // the raw B/C rows of this thread's conv items all go out before any of them is waited for.
+  // b0. dt of the wave's heads (wave w: heads w, w + 8, ...; lane l: tokens 4l .. 4l+3), two heads
+  // at a time
+  const int hpg = a.sh.H / G;
+  constexpr int HB = 2;
+  // raw values (converted when used, so no load waits for its own result)
+  typedef typename std::conditional<IOBF, u16, float>::type DtRaw;
+  DtRaw dtv[HB][4];
+  auto load_dt = [&](int hh0) {
 #pragma unroll
-      for (int k = 0; k < 11; ++k) {
-        const int jj = j0 - 3 + k, tau = ch.tau0 + jj;
-        if (tau >= 0 && jj < len) {
-          raw[k].load(src, (int64_t)(sq.t0 + tau) * stride + col);
-        } else {
-          raw[k].zero();
-        }
+    for (int b = 0; b < HB; ++b) {
+      const int hh = min(hh0 + 8 * b, hpg - 1), h = g * hpg + hh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = min(lane * 4 + e, len - 1);
+        dtv[b][e] = static_cast<const DtRaw*>(a.dt)[(int64_t)(ch.t0 + i) * a.dt_stride + h];
       }
-      float wt[8][4], bias[8];
+    }
+  };
+  load_dt(wave);
+  // a1. conv + SiLU: thread (octet o, token blocks tb0 + TBS m); octets [0, OCT) are B channels,
+  // [OCT, 2 OCT) C channels (past N: zeros); rows outside the sequence or past the chunk read a
+  // valid row and are replaced by zeros (or the slot's window before the sequence)
+  constexpr int OCT = NP / 8, NOCT = 2 * OCT, TBS = kThreads / NOCT;
+  constexpr int NIT = (kMaxRowTiles * 2 + TBS - 1) / TBS;
+  constexpr int PRE = IOBF ? NIT : 1;   // items whose rows are requested ahead (fp32 rows: one)
+  const int ntb = (len + 7) / 8;
+  const int o = tid % NOCT, tb0 = tid / NOCT;
+  const bool isC = o >= OCT;
+  const int n0 = (o % OCT) * 8;
+  const bool chan_ok = n0 < N;
+  const void* const src = isC ? a.C : a.B;
+  const int64_t stride = isC ? a.C_stride : a.B_stride;
+  const int64_t col = (int64_t)g * N + (chan_ok ? n0 : 0);
+  Raw8<IOBF> raw[PRE][11];
+  auto load_rows = [&](int m, Raw8<IOBF> (&r)[11]) {
+    const int j0 = 8 * (tb0 + TBS * m);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) taps4(a, cc + e, wt[e], bias[e]);
-      float halo[3][8];   // rows before the sequence: the slot's window, or zeros
+    for (int k = 0; k < 11; ++k) {
+      const int jj = j0 - 3 + k, tau = ch.tau0 + jj;
+      const bool ok = tau >= 0 && jj < len;
+      r[k].load(src, (int64_t)(sq.t0 + (ok ? tau : ch.tau0)) * stride + col);
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < PRE; ++m) load_rows(m, raw[m]);
+  // the conv taps and bias of the group's B and C channels, to LDS (requested after the rows)
+  float* const sTap = reinterpret_cast<float*>(bc_smem + L::OFF_TAPS);
+  for (int i = tid; i < 2 * N; i += kThreads) {
+    const int cc = I + (i >= N ? GN : 0) + g * N + i % N;
+    float w[4], b;
+    taps4(a, cc, w, b);
+    *reinterpret_cast<floatx4*>(sTap + 4 * i) = floatx4{w[0], w[1], w[2], w[3]};
+    sTap[8 * N + i] = b;
+  }
+  __syncthreads();   // the taps in LDS
+  const int cc0 = I + (isC ? GN : 0) + g * N + n0;
+  float wt[8][4], bias[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int ci = (isC ? N : 0) + (chan_ok ? n0 + e : 0);
+    const floatx4 w4 = *reinterpret_cast<const floatx4*>(sTap + 4 * ci);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wt[e][k] = w4[k];
+    bias[e] = sTap[8 * N + ci];
+  }
+#pragma unroll
+  for (int m = 0; m < NIT; ++m) {
+    const int tb = tb0 + TBS * m, j0 = 8 * tb;
+    if (tb >= ntb) break;
+    Raw8<IOBF> rr[11];
+    if (PRE == NIT) {
+#pragma unroll
+      for (int k = 0; k < 11; ++k) rr[k] = raw[PRE == NIT ? m : 0][k];
+    } else {
+      load_rows(m, rr);
+    }
+    float xr[11][8];   // the raw rows: zeros outside the sequence or past the chunk
+#pragma unroll
+    for (int k = 0; k < 11; ++k) {
+      const int jj = j0 - 3 + k, tau = ch.tau0 + jj;
+      const bool ok = tau >= 0 && jj < len;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xr[k][e] = ok ? rr[k].at(e) : 0.f;
+    }
+    if (ch.tau0 + j0 < 3 && sq.has_init && chan_ok) {   // rare: rows before the sequence, from the slot's window
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
+        const int tau = ch.tau0 + j0 - 3 + k;
+        if (tau < 0 && tau >= -W1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) halo[k][e] = raw[k].at(e);
-      }
-      if (ch.tau0 + j0 < 3) {   // rare: the item starts next to the sequence start
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const int tau = ch.tau0 + j0 - 3 + k;
-          if (tau < 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              halo[k][e] = (sq.has_init && tau >= -W1) ? window_value(a, sq.slot, cc + e, W1 + tau) : 0.f;
-          }
+          for (int e = 0; e < 8; ++e) xr[k][e] = window_value(a, sq.slot, cc0 + e, W1 + tau);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = bias[e];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) x += wt[e][k] * (r + k < 3 ? halo[r + k][e] : raw[r + k].at(e));
-          v[r][e] = j0 + r < len ? silu(x) : 0.f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[r][e] = 0.f;
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      u16x8 hv, lv;
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        u16 hi, lo = 0;
-        if (SPLIT) split2(v[r][e], hi, lo);
-        else hi = bits_of(from_f32<bf16>(v[r][e]));
-        hv[e] = hi;
-        lv[e] = lo;
+        float x = bias[e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x += wt[e][k] * xr[r + k][e];
+        v[e] = (chan_ok && j0 + r < len) ? silu(x) : 0.f;
+      }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        hw[mm] = pack_bf16x2(v[2 * mm], v[2 * mm + 1]);
+        if (SPLIT) lw[mm] = pack_bf16x2(v[2 * mm] - lo_f32(hw[mm]), v[2 * mm + 1] - hi_f32(hw[mm]));
       }
       const int j = j0 + r;
       if (!isC) {
 #pragma unroll
         for (int pl = 0; pl < NPL; ++pl) {
-          const u16x8 x = pl == 0 ? hv : lv;
-          u16* d = sB + pl * L::PLANE + j * LDB + n0;
-          *reinterpret_cast<u16x4*>(d) = u16x4{x[0], x[1], x[2], x[3]};
-          *reinterpret_cast<u16x4*>(d + 4) = u16x4{x[4], x[5], x[6], x[7]};
+          const uint32_t* x = pl == 0 ? hw : lw;
+          uint32_t* d = reinterpret_cast<uint32_t*>(sB + pl * L::PLANE + j * LDB + n0);
+          *reinterpret_cast<uint2*>(d) = uint2{x[0], x[1]};
+          *reinterpret_cast<uint2*>(d + 2) = uint2{x[2], x[3]};
         }
       } else {
         // channels n0 .. n0+3 and n0+4 .. n0+7 land at two 4-element runs of the permuted row
         const int p0 = (n0 & ~31) + perm32(n0 & 31), p1 = (n0 & ~31) + perm32((n0 + 4) & 31);
 #pragma unroll
         for (int pl = 0; pl < NPL; ++pl) {
-          const u16x8 x = pl == 0 ? hv : lv;
+          const uint32_t* x = pl == 0 ? hw : lw;
           u16* d = cf + pl * a.Cf_plane + (int64_t)j * NP;
-          *reinterpret_cast<u16x4*>(d + p0) = u16x4{x[0], x[1], x[2], x[3]};
-          *reinterpret_cast<u16x4*>(d + p1) = u16x4{x[4], x[5], x[6], x[7]};
+          *reinterpret_cast<uint2*>(d + p0) = uint2{x[0], x[1]};
+          *reinterpret_cast<uint2*>(d + p1) = uint2{x[2], x[3]};
         }
       }
     }
@@ -363,32 +409,40 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
 
   // b. Delta and the chunk-local cumsum for the group's heads; lane l owns tokens 4l .. 4l+3
   {
-    const int hpg = a.sh.H / G;
     const int64_t T = a.total_tokens;
-    for (int hh = wave; hh < hpg; hh += kThreads / 64) {
-      const int h = g * hpg + hh;
-      const float A = a.A[h], bias = a.dt_bias[h];
-      float d[4], s[4], run = 0.f;
+    for (int hh0 = wave; hh0 < hpg; hh0 += 8 * HB) {
+      if (hh0 != wave) load_dt(hh0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = lane * 4 + e;
-        d[e] = i < len ? softplus(load_any(a.dt, (int64_t)(ch.t0 + i) * a.dt_stride + h, a.io_bf16) + bias) : 0.f;
-        run += d[e] * A;
-        s[e] = run;
-      }
-      float incl = run;
+      for (int b = 0; b < HB; ++b) {
+        const int hh = hh0 + 8 * b;
+        if (hh >= hpg) break;
+        const int h = g * hpg + hh;
+        const float A = a.A[h], dtb = a.dt_bias[h];
+        float d[4], sc[4], run = 0.f;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      const float excl = incl - run;
+        for (int e = 0; e < 4; ++e) {
+          const int i = lane * 4 + e;
+          float dt;
+          if constexpr (IOBF) dt = f_of(dtv[b][e]);
+          else dt = dtv[b][e];
+          d[e] = i < len ? softplus(dt + dtb) : 0.f;
+          run += d[e] * A;
+          sc[e] = run;
+        }
+        float incl = run;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = lane * 4 + e;
-        if (i < len) {
-          a.delta[(int64_t)h * T + ch.t0 + i] = d[e];
-          a.dA[(int64_t)h * T + ch.t0 + i] = excl + s[e];
+        for (int off = 1; off < 64; off <<= 1) {
+          const float t = __shfl_up(incl, off);
+          if (lane >= off) incl += t;
+        }
+        const float excl = incl - run;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = lane * 4 + e;
+          if (i < len) {
+            a.delta[(int64_t)h * T + ch.t0 + i] = d[e];
+            a.dA[(int64_t)h * T + ch.t0 + i] = excl + sc[e];
+          }
         }
       }
     }
@@ -526,9 +580,10 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   float* const sBias = sTap + PP * 4;
 
   const int H = a.sh.H, P = a.sh.P, G = a.sh.G, hpg = H / G, nparts = a.nparts;
-  // the workgroups of one (sequence, group) take consecutive logical indices on one XCD, so the
-  // group's C, B^T and C B^T blocks of a chunk come from memory once for its heads
-  const int lg = xcd_contiguous(blockIdx.x, gridDim.x);
+  // the workgroups of one (sequence, group) run on one XCD, so the group's C, B^T and C B^T blocks
+  // of a chunk come from memory once for its heads; the (sequence, group) units are dealt over the
+  // XCDs in table order (longest sequences first)
+  const int lg = xcd_units(blockIdx.x, gridDim.x, hpg * nparts);
   const int part = lg % nparts, rest = lg / nparts;
   const int hh = rest % hpg, g = (rest / hpg) % G, s = rest / H;
   const int h = g * hpg + hh;
