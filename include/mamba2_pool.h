@@ -193,10 +193,11 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, c
                                         const int32_t* ckpt_slots, int32_t max_ckpt, uint64_t* bytes);
 
 /* Chunked (SSD) prefill of packed variable-length sequences.  Each chunk's
- * own contribution is a causally masked matrix product, and a short scan over
- * chunk states links the chunks ([SSM-hybrids], the mamba_chunk_scan_combined
- * call site; [notes] "Mamba and Attention": Y = (M o L) X with L the causal
- * mask).  The result equals the token-by-token recurrence up to rounding.
+ * own contribution is a causally masked matrix product, and the state is carried
+ * from each chunk to the next by the affine step ([SSM-hybrids], the
+ * mamba_chunk_scan_combined call site; [notes] "Mamba and Attention":
+ * Y = (M o L) X with L the causal mask).  The result equals the token-by-token
+ * recurrence up to rounding.
  * Host arrays (read before return):
  *   cu_seqlens int32[num_seqs+1], cu_seqlens[0] = 0, non-decreasing;
  *              sequence s owns packed rows [cu_seqlens[s], cu_seqlens[s+1]).
@@ -224,8 +225,7 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, c
  * first row.  workspace: device memory of at least
  * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch
  * and not read across calls.  Sequences with zero length leave their slot untouched.
- * Launch tables (32 bytes per sequence and per chunk, 16 per checkpoint window)
- * travel in kernel arguments: up to 3072 bytes in the first kernel's, more in
+ * Launch tables (32 bytes per sequence and per chunk) travel in kernel arguments: up to 3072 bytes in the first kernel's, more in
  * those of small upload launches ahead of it.  The call allocates nothing, enqueues
  * no host-to-device copy and never waits on the host.
  * With fp32 SSM state the contractions run in split-bf16 (three products)
@@ -249,8 +249,9 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
  * pinned memory (its host-side launch tables are built in ordinary host memory).
  * Arguments, results and errors are those of mamba2_prefill_chunked, plus
  * M2_ERR_WORKSPACE when mamba2_prefill_workspace_size for the same arguments
- * exceeds 64 MiB (at the 8B-hybrid layer shape, bf16 state, chunk 256: about
- * 1.5k tokens), and M2_ERR_HIP if the array's address cannot be looked up.
+ * exceeds 64 MiB (at the 8B-hybrid layer shape, chunk 256: up to 8,960 tokens of
+ * one sequence with bf16 state, 4,735 with fp32 state), and M2_ERR_HIP if the
+ * array's address cannot be looked up.
  * All calls on one GPU share that GPU's array and nothing in it survives a call:
  * calls that overlap in time on one GPU (two streams, or two threads) race and
  * must not be issued. */
