@@ -53,10 +53,13 @@ typedef enum m2_status {
 
 typedef enum m2_dtype { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
 
-/* State families a pool can hold ([sizing] and the vLLM state-shape table of [notes]). */
+/* State families a pool can hold ([sizing] and the state-shape and dtype tables of [notes],
+ * section "MambaSpec"). */
 typedef enum m2_family {
   M2_FAMILY_MAMBA2 = 0, /* temporal state (H, P, N), conv over [x | B | C] */
-  M2_FAMILY_MAMBA1 = 1  /* temporal state (D, N), conv over the D channels of x */
+  M2_FAMILY_MAMBA1 = 1, /* temporal state (D, N), conv over the D channels of x */
+  M2_FAMILY_GDN = 2,    /* temporal state (num_v_heads, head_v_dim, head_k_dim), conv over q, k, v */
+  M2_FAMILY_KDA = 3     /* temporal state (num_heads, head_dim, head_dim), conv over q, k, v */
 } m2_family;
 
 /* Pool descriptor.  A pool is two dense caller-owned device tensors, one per
@@ -68,7 +71,18 @@ typedef enum m2_family {
  * dense sizes exactly.  Requirements: nheads % n_groups == 0, head_dim and
  * d_state multiples of 8, 2 <= conv_kernel <= 4, bases 16-byte aligned.
  * family M2_FAMILY_MAMBA1: nheads = D (a multiple of 8), head_dim = 1,
- * n_groups = 1, so the state is [D][N] and d_conv = D. */
+ * n_groups = 1, so the state is [D][N] and d_conv = D.
+ * family M2_FAMILY_GDN: nheads = num_v_heads, head_dim = head_v_dim,
+ * d_state = head_k_dim, n_groups = num_k_heads (q and k have num_k_heads heads
+ * of head_k_dim, v has num_v_heads of head_v_dim, so d_conv has the formula
+ * above); both objects bf16, the dtypes the [notes] table gives GDN.
+ * family M2_FAMILY_KDA: nheads = num_heads, head_dim = d_state = head_dim,
+ * n_groups = num_heads (q, k and v each num_heads x head_dim: d_conv =
+ * 3 * num_heads * head_dim); conv bf16 and state fp32, as the [notes] table
+ * gives KDA.  GDN and KDA pools hold, copy (mamba2_checkpoint_states) and
+ * quantize (the int8 store) their states; the pages give no recurrence for
+ * either, so the decode and prefill entry points refuse them
+ * (M2_ERR_UNSUPPORTED). */
 typedef struct m2_pool_desc {
   int32_t num_layers;
   int32_t num_slots;
@@ -79,7 +93,7 @@ typedef struct m2_pool_desc {
   int32_t conv_kernel;
   int32_t ssm_dtype;  /* m2_dtype */
   int32_t conv_dtype; /* m2_dtype */
-  int32_t family;     /* m2_family; 0 (Mamba2) for every entry point above the Mamba1 one */
+  int32_t family;     /* m2_family; 0 (Mamba2) for the Mamba2 decode and prefill entry points */
   void* ssm_base;
   void* conv_base;
   uint64_t ssm_bytes;

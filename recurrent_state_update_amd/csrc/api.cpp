@@ -101,9 +101,20 @@ m2::LayerShape make_shape(const m2_pool_desc& d) {
   return s;
 }
 
+const char* family_name(int family) {
+  switch (family) {
+    case M2_FAMILY_MAMBA2: return "Mamba2";
+    case M2_FAMILY_MAMBA1: return "Mamba1";
+    case M2_FAMILY_GDN: return "GDN";
+    case M2_FAMILY_KDA: return "KDA";
+    default: return "unknown";
+  }
+}
+
 m2_status require_family(const m2_pool* pool, int family, const char* what) {
   if (pool->d.family != family)
-    return fail(M2_ERR_UNSUPPORTED, "%s needs a %s pool", what, family == M2_FAMILY_MAMBA1 ? "Mamba1" : "Mamba2");
+    return fail(M2_ERR_UNSUPPORTED, "%s needs a %s pool, not a %s pool", what, family_name(family),
+                family_name(pool->d.family));
   return M2_OK;
 }
 
@@ -337,8 +348,8 @@ m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out) {
     return fail(M2_ERR_ARG, "layer, slot, head, head_dim, d_state and group counts must be positive");
   if (d.conv_kernel < 2 || d.conv_kernel > 4)
     return fail(M2_ERR_UNSUPPORTED, "conv_kernel %d outside the supported range 2..4", d.conv_kernel);
-  if (d.family != M2_FAMILY_MAMBA2 && d.family != M2_FAMILY_MAMBA1)
-    return fail(M2_ERR_ARG, "family %d is neither Mamba2 (0) nor Mamba1 (1)", d.family);
+  if (d.family < M2_FAMILY_MAMBA2 || d.family > M2_FAMILY_KDA)
+    return fail(M2_ERR_ARG, "family %d is none of Mamba2 (0), Mamba1 (1), GDN (2), KDA (3)", d.family);
   if (d.family == M2_FAMILY_MAMBA1) {
     if (d.head_dim != 1 || d.n_groups != 1)
       return fail(M2_ERR_SHAPE, "a Mamba1 pool has head_dim 1 and n_groups 1 (nheads = D channels)");
@@ -350,7 +361,14 @@ m2_status mamba2_pool_create(const m2_pool_desc* desc, m2_pool** out) {
     if (d.head_dim % 8 != 0 || d.d_state % 8 != 0)
       return fail(M2_ERR_SHAPE, "head_dim and d_state must be multiples of 8");
   }
+  if (d.family == M2_FAMILY_KDA && (d.head_dim != d.d_state || d.n_groups != d.nheads))
+    return fail(M2_ERR_SHAPE, "a KDA pool has a square (head_dim, head_dim) state per head and n_groups = nheads "
+                "(got head_dim %d, d_state %d, n_groups %d, nheads %d)", d.head_dim, d.d_state, d.n_groups, d.nheads);
   if (!dtype_ok(d.ssm_dtype) || !dtype_ok(d.conv_dtype)) return fail(M2_ERR_DTYPE, "ssm/conv dtype must be F32 or BF16");
+  if (d.family == M2_FAMILY_GDN && (d.ssm_dtype != M2_BF16 || d.conv_dtype != M2_BF16))
+    return fail(M2_ERR_DTYPE, "a GDN pool keeps both objects in bf16");
+  if (d.family == M2_FAMILY_KDA && (d.ssm_dtype != M2_F32 || d.conv_dtype != M2_BF16))
+    return fail(M2_ERR_DTYPE, "a KDA pool keeps its conv window in bf16 and its state in fp32");
   if (!d.ssm_base || !d.conv_base) return fail(M2_ERR_ARG, "ssm_base and conv_base must not be NULL");
   if (!aligned16(d.ssm_base) || !aligned16(d.conv_base))
     return fail(M2_ERR_ALIGN, "pool bases must be 16-byte aligned");

@@ -67,7 +67,7 @@ class Pool:
         self.ssm, self.conv = ssm, conv
         self.nheads, self.head_dim, self.d_state = nheads, head_dim, d_state
         self.n_groups, self.conv_kernel = n_groups, conv_kernel
-        self.family = family               # 0: Mamba2, 1: Mamba1 (nheads = D channels, head_dim 1)
+        self.family = family               # 0: Mamba2, 1: Mamba1 (nheads = D channels, head_dim 1), 2: GDN, 3: KDA
         self.intermediate = nheads * head_dim
         self.conv_dim = self.intermediate + (0 if family == 1 else 2 * n_groups * d_state)
         self.num_layers, self.num_slots = ssm.shape[0], ssm.shape[1]
@@ -93,6 +93,26 @@ class Pool:
         ssm = torch.zeros((num_layers, num_slots, d_inner, 1, d_state), dtype=ssm_dtype, device=device)
         conv = torch.zeros((num_layers, num_slots, d_inner, conv_kernel - 1), dtype=conv_dtype, device=device)
         return cls(ssm, conv, d_inner, 1, d_state, 1, conv_kernel, family=1)
+
+    @classmethod
+    def allocate_gdn(cls, num_layers, num_slots, num_v_heads, head_v_dim, head_k_dim, num_k_heads, conv_kernel,
+                     device="cuda"):
+        """A GDN pool (state only: the pages give no recurrence): ssm [L, S, Hv, dv, dk] and conv
+        [L, S, Hv*dv + 2*Hk*dk, W-1], both bf16."""
+        cd = num_v_heads * head_v_dim + 2 * num_k_heads * head_k_dim
+        ssm = torch.zeros((num_layers, num_slots, num_v_heads, head_v_dim, head_k_dim), dtype=torch.bfloat16,
+                          device=device)
+        conv = torch.zeros((num_layers, num_slots, cd, conv_kernel - 1), dtype=torch.bfloat16, device=device)
+        return cls(ssm, conv, num_v_heads, head_v_dim, head_k_dim, num_k_heads, conv_kernel, family=2)
+
+    @classmethod
+    def allocate_kda(cls, num_layers, num_slots, num_heads, head_dim, conv_kernel, device="cuda"):
+        """A KDA pool (state only: the pages give no recurrence): ssm [L, S, H, d, d] fp32 and conv
+        [L, S, 3*H*d, W-1] bf16."""
+        ssm = torch.zeros((num_layers, num_slots, num_heads, head_dim, head_dim), dtype=torch.float32, device=device)
+        conv = torch.zeros((num_layers, num_slots, 3 * num_heads * head_dim, conv_kernel - 1), dtype=torch.bfloat16,
+                           device=device)
+        return cls(ssm, conv, num_heads, head_dim, head_dim, num_heads, conv_kernel, family=3)
 
     def mamba1_decode_step(self, layer: int, w: LayerWeights, slots: torch.Tensor, x, B, C, z, dt, y,
                            slots_host=None):

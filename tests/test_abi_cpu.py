@@ -518,3 +518,103 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("raised:") and "not built" in r.stdout
+
+
+# ---- GDN and KDA pools: state only (the pages give no recurrence for either)
+FAMILY_CODE = {"Mamba2": 0, "Mamba1": 1, "GDN": 2, "KDA": 3}
+DT_CODE = {"fp32": 0, "bf16": 1}
+
+
+def mambaspec():
+    return json.load(open(os.path.join(ROOT, "tests", "golden", "mambaspec_state_shapes.json")))
+
+
+def family_desc(family, dims, W=4, L=2, S=5):
+    """A descriptor built from the table's symbols: recurrent shape and dtypes from the MambaSpec
+    entry, the conv channel count D of the q, k, v projections (GDN: 2 Hk dk + Hv dv; KDA: 3 H d)."""
+    spec = mambaspec()
+    f = spec["families"][family]
+    rec = [dims[k] for k in f["recurrent"]]
+    conv_dt, ssm_dt = f["dtypes"]
+    by = spec["dtype_bytes"]
+    if family == "GDN":
+        H, P, N, G = dims["num_v_heads"], dims["head_v_dim"], dims["head_k_dim"], dims["num_k_heads"]
+        D = 2 * G * N + H * P
+    else:
+        H, P, N, G = dims["num_heads"], dims["head_dim"], dims["head_dim"], dims["num_heads"]
+        D = 3 * H * P
+    rec_bytes = int(np.prod(rec)) * by[ssm_dt]
+    conv_bytes = D * (W - 1) * by[conv_dt]
+    d = PoolDesc(L, S, H, P, N, G, W, DT_CODE[ssm_dt], DT_CODE[conv_dt], FAMILY_CODE[family], FAKE, FAKE,
+                 L * S * rec_bytes, L * S * conv_bytes)
+    return d, rec_bytes, conv_bytes
+
+
+GDN_DIMS = [dict(num_v_heads=32, head_v_dim=128, head_k_dim=128, num_k_heads=16),
+            dict(num_v_heads=8, head_v_dim=64, head_k_dim=32, num_k_heads=2)]
+KDA_DIMS = [dict(num_heads=32, head_dim=128), dict(num_heads=4, head_dim=64)]
+
+
+@pytest.mark.parametrize("family,dims", [("GDN", d) for d in GDN_DIMS] + [("KDA", d) for d in KDA_DIMS])
+def test_gdn_and_kda_pools_hold_the_table_byte_counts(family, dims):
+    """pool_info of a GDN or KDA pool equals the MambaSpec table's recurrent shape times its dtype
+    size, and the conv window D x (kernel-1) at the conv dtype; the int8 store of such a pool has
+    one code per state element and one fp32 scale per (head, last state index)."""
+    d, rec_bytes, conv_bytes = family_desc(family, dims)
+    st, h = create(d)
+    assert st == 0, lib().mamba2_last_error()
+    a, b = c_uint64(), c_uint64()
+    assert lib().mamba2_pool_info(h, byref(a), byref(b)) == 0
+    assert (a.value, b.value) == (rec_bytes, conv_bytes)
+    cb, sb, vb = c_uint64(), c_uint64(), c_uint64()
+    assert lib().mamba2_int8_store_size(h, 3, byref(cb), byref(sb), byref(vb)) == 0
+    L = d.num_layers
+    assert cb.value == 3 * L * d.nheads * d.head_dim * d.d_state
+    assert sb.value == 3 * L * d.nheads * d.d_state * 4
+    assert vb.value == 3 * L * conv_bytes
+    lib().mamba2_pool_destroy(h)
+
+
+def test_gdn_and_kda_byte_counts_at_their_published_widths():
+    """The two wide configurations above by hand: a GDN layer with 32 value heads of 128 x 128
+    holds 1 MiB of bf16 state; a KDA layer with 32 heads of 128 x 128 holds 2 MiB of fp32 state."""
+    for family, dims, rec in (("GDN", GDN_DIMS[0], 32 * 128 * 128 * 2), ("KDA", KDA_DIMS[0], 32 * 128 * 128 * 4)):
+        d, rec_bytes, conv_bytes = family_desc(family, dims)
+        assert rec_bytes == rec
+        st, h = create(d)
+        assert st == 0
+        a, b = c_uint64(), c_uint64()
+        assert lib().mamba2_pool_info(h, byref(a), byref(b)) == 0 and a.value == rec
+        lib().mamba2_pool_destroy(h)
+
+
+def test_gdn_and_kda_pools_are_validated_and_refused_by_the_recurrences():
+    d, _, _ = family_desc("KDA", KDA_DIMS[1])
+    st, h = create(d)
+    assert st == 0, lib().mamba2_last_error()
+    assert decode(h) == UNSUP
+    assert decode_multi(h) == UNSUP
+    assert prefill(h, [0, 16], [0]) == UNSUP
+    wsize(h, [0, 100], chunk=64, expect=UNSUP)
+    n = c_uint64()
+    assert lib().mamba1_prefill_workspace_size(h, 2, 100, 32, 0, byref(n)) == UNSUP
+    assert ckpt(h, [0], [5]) == SLOT                # the copy validates any family (it runs on the GPU tests)
+    lib().mamba2_pool_destroy(h)
+    # KDA: square state per head, n_groups = nheads, conv bf16 + state fp32
+    H, P, W, L, S = 4, 64, 4, 2, 5
+    kda = lambda P, N, G, ssm, conv: PoolDesc(L, S, H, P, N, G, W, ssm, conv, 3, FAKE, FAKE,
+                                              L * S * H * P * N * (4 if ssm == 0 else 2),
+                                              L * S * (H * P + 2 * G * N) * (W - 1) * (4 if conv == 0 else 2))
+    assert create(kda(P, 32, H, 0, 1))[0] == SHAPE          # head_dim != d_state
+    assert create(kda(P, P, 2, 0, 1))[0] == SHAPE           # n_groups != nheads
+    assert create(kda(P, P, H, 1, 1))[0] == DTYPE           # bf16 state
+    assert create(kda(P, P, H, 0, 0))[0] == DTYPE           # fp32 conv
+    assert create(kda(P, P, H, 0, 1))[0] == 0
+    # GDN: value heads a multiple of key heads, both objects bf16
+    gdn = lambda H, G, ssm: PoolDesc(L, S, H, 64, 32, G, W, ssm, 1, 2, FAKE, FAKE,
+                                     L * S * H * 64 * 32 * (4 if ssm == 0 else 2), L * S * (H * 64 + 2 * G * 32) * (W - 1) * 2)
+    assert create(gdn(6, 4, 1))[0] == SHAPE                 # 6 value heads over 4 key heads
+    assert create(gdn(8, 2, 0))[0] == DTYPE                 # fp32 state
+    assert create(gdn(8, 2, 1))[0] == 0
+    bad = PoolDesc(L, S, H, 1, 16, 1, W, 1, 1, 4, FAKE, FAKE, L * S * H * 16 * 2, L * S * H * (W - 1) * 2)
+    assert create(bad)[0] == ARG                            # no family 4
