@@ -56,26 +56,46 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
   if (d < D) h = __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(st));
 
   // ---------------------------------------------------------------- phase 1
-  if (tid < CPW && d0 + tid < D) {
-    const int dc = d0 + tid;
-    float win[W - 1];
-    const int64_t woff = ((int64_t)slot * D + dc) * (W - 1);
+  // One copy per (conv dtype, io dtype), chosen once: with the element types known every load of
+  // the phase is issued before the first conversion waits for one.
+  auto phase1 = [&](auto tc, auto ti) {
+    typedef decltype(tc) TC;
+    typedef decltype(ti) TI;
+    if (tid < CPW && d0 + tid < D) {
+      const int dc = d0 + tid;
+      const int64_t woff = ((int64_t)slot * D + dc) * (W - 1);
+      TC* const wp = static_cast<TC*>(a.conv) + woff;
+      TC wr[W - 1];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) win[k] = load_any(a.conv, woff + k, a.conv_bf16);
-    const float u = load_any(a.x, b * a.x_stride + dc, a.io_bf16);
-    float v = a.conv_b[dc];
+      for (int k = 0; k < W - 1; ++k) wr[k] = wp[k];
+      const TI ur = static_cast<const TI*>(a.x)[b * a.x_stride + dc];
+      const TI dtr = static_cast<const TI*>(a.dt)[b * a.dt_stride + dc];
+      float wt[W];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) v += a.conv_w[(int64_t)dc * W + k] * win[k];
-    v += a.conv_w[(int64_t)dc * W + W - 1] * u;
-    s_x[tid] = silu(v);
-    s_dl[tid] = softplus(load_any(a.dt, b * a.dt_stride + dc, a.io_bf16) + a.dt_bias[dc]);
+      for (int k = 0; k < W; ++k) wt[k] = a.conv_w[(int64_t)dc * W + k];
+      const float cb = a.conv_b[dc], dtb = a.dt_bias[dc];
+      const float u = to_f32(ur);
+      float v = cb + wt[W - 1] * u;
 #pragma unroll
-    for (int k = 0; k < W - 2; ++k) store_any(a.conv, woff + k, win[k + 1], a.conv_bf16);
-    store_any(a.conv, woff + W - 2, u, a.conv_bf16);
-  }
-  for (int n = tid; n < N; n += kM1Threads) {
-    s_B[n] = load_any(a.B, b * a.B_stride + n, a.io_bf16);
-    s_C[n] = load_any(a.C, b * a.C_stride + n, a.io_bf16);
+      for (int k = 0; k < W - 1; ++k) v += wt[k] * to_f32(wr[k]);
+      s_x[tid] = silu(v);
+      s_dl[tid] = softplus(to_f32(dtr) + dtb);
+      // the window keeps raw inputs at the conv dtype: shift the stored words, append the input
+#pragma unroll
+      for (int k = 0; k < W - 2; ++k) wp[k] = wr[k + 1];
+      wp[W - 2] = from_f32<TC>(u);
+    }
+    for (int n = tid; n < N; n += kM1Threads) {
+      s_B[n] = to_f32(static_cast<const TI*>(a.B)[b * a.B_stride + n]);
+      s_C[n] = to_f32(static_cast<const TI*>(a.C)[b * a.C_stride + n]);
+    }
+  };
+  if (a.conv_bf16) {
+    if (a.io_bf16) phase1(bf16(), bf16());
+    else phase1(bf16(), 0.f);
+  } else {
+    if (a.io_bf16) phase1(0.f, bf16());
+    else phase1(0.f, 0.f);
   }
   __syncthreads();
 
