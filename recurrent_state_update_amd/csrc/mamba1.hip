@@ -5,7 +5,8 @@
 // and state index exp(Delta_d A[d][n]), B and C shared by all channels, the
 // short conv over the D channels of x.
 //
-// One workgroup of 1024 threads covers a block of channels of one sequence.
+// One workgroup of 1024 threads covers a block of channels of one sequence
+// (with states of at most 32 bytes per channel, two channels per lane group).
 // Phase 1: one thread per channel shifts the conv window, convolves, applies
 // SiLU and softplus, and stages x_d and Delta_d in LDS with the row's B and C.
 // Phase 2: a channel's N state values are split over N/VEC lanes, each with one
@@ -29,13 +30,18 @@ __device__ __forceinline__ int m1_uniform(const int32_t* p) {
   return *(const cint*)p;
 }
 
+template <typename TS, int N> constexpr int m1_passes() { return N * (int)sizeof(TS) <= 32 ? 2 : 1; }
+
 template <typename TS, int N, int W>
 __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params a) {
   typedef typename M1Vec<TS>::type vec_t;
   constexpr int VEC = 16 / sizeof(TS);      // state values per 16-byte access
   constexpr int LPC = N / VEC;              // lanes per channel
   static_assert(LPC >= 1 && LPC <= 64 && (64 % LPC) == 0, "unsupported d_state");
-  constexpr int CPW = kM1Threads / LPC;     // channels per workgroup
+  constexpr int CPP = kM1Threads / LPC;     // channels per pass of the workgroup's lanes
+  constexpr int NPASS = m1_passes<TS, N>(); // passes: with small states a lane holds two channels'
+                                            // values, so twice the bytes are in flight
+  constexpr int CPW = CPP * NPASS;          // channels per workgroup
   __shared__ float s_x[CPW], s_dl[CPW], s_B[N], s_C[N];
 
   const int b = blockIdx.y;
@@ -44,16 +50,20 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
   const int D = a.D;
   const int slot = m1_uniform(a.slots + b);
   if (slot < 0 || slot >= a.num_slots) {   // padding row: no pool access, zero outputs
-    if (tid < CPW && d0 + tid < D) store_any(a.y, b * a.y_stride + d0 + tid, 0.f, a.y_bf16);
+    for (int i = tid; i < CPW; i += kM1Threads)
+      if (d0 + i < D) store_any(a.y, b * a.y_stride + d0 + i, 0.f, a.y_bf16);
     return;
   }
-  // this lane's state values, requested first
+  // this lane's state values (channel c + CPP p of pass p), requested first
   const int c = tid / LPC, sub = tid % LPC;
-  const int d = d0 + c;
   const int n0 = sub * VEC;
-  TS* const st = static_cast<TS*>(a.ssm) + ((int64_t)slot * D + d) * N + n0;
-  vec_t h;
-  if (d < D) h = __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(st));
+  vec_t h[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int d = d0 + CPP * p + c;
+    if (d < D) h[p] = __builtin_nontemporal_load(
+        reinterpret_cast<const vec_t*>(static_cast<TS*>(a.ssm) + ((int64_t)slot * D + d) * N + n0));
+  }
 
   // ---------------------------------------------------------------- phase 1
   // One copy per (conv dtype, io dtype), chosen once: with the element types known every load of
@@ -61,8 +71,9 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
   auto phase1 = [&](auto tc, auto ti) {
     typedef decltype(tc) TC;
     typedef decltype(ti) TI;
-    if (tid < CPW && d0 + tid < D) {
-      const int dc = d0 + tid;
+    for (int ci = tid; ci < CPW; ci += kM1Threads) {
+      if (d0 + ci >= D) break;
+      const int dc = d0 + ci;
       const int64_t woff = ((int64_t)slot * D + dc) * (W - 1);
       TC* const wp = static_cast<TC*>(a.conv) + woff;
       TC wr[W - 1];
@@ -78,8 +89,8 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
       float v = cb + wt[W - 1] * u;
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) v += wt[k] * to_f32(wr[k]);
-      s_x[tid] = silu(v);
-      s_dl[tid] = softplus(to_f32(dtr) + dtb);
+      s_x[ci] = silu(v);
+      s_dl[ci] = softplus(to_f32(dtr) + dtb);
       // the window keeps raw inputs at the conv dtype: shift the stored words, append the input
 #pragma unroll
       for (int k = 0; k < W - 2; ++k) wp[k] = wr[k + 1];
@@ -100,34 +111,38 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
   __syncthreads();
 
   // ---------------------------------------------------------------- phase 2
-  float part = 0.f;
-  if (d < D) {
-    const float x = s_x[c], dl = s_dl[c];
-    const float dx = dl * x;
-    const float* Ar = a.A + (int64_t)d * N + n0;
-    vec_t o;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const float al = __builtin_amdgcn_exp2f(dl * Ar[e] * 1.4426950408889634f);
-      const float hn = al * to_f32(h[e]) + dx * s_B[n0 + e];
-      part += hn * s_C[n0 + e];
-      o[e] = from_f32<TS>(hn);
+  for (int p = 0; p < NPASS; ++p) {
+    const int cc = CPP * p + c, d = d0 + cc;
+    float part = 0.f;
+    if (d < D) {
+      const float x = s_x[cc], dl = s_dl[cc];
+      const float dx = dl * x;
+      const float* Ar = a.A + (int64_t)d * N + n0;
+      vec_t o;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float al = __builtin_amdgcn_exp2f(dl * Ar[e] * 1.4426950408889634f);
+        const float hn = al * to_f32(h[p][e]) + dx * s_B[n0 + e];
+        part += hn * s_C[n0 + e];
+        o[e] = from_f32<TS>(hn);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<vec_t*>(static_cast<TS*>(a.ssm) + ((int64_t)slot * D + d) * N + n0));
     }
-    __builtin_nontemporal_store(o, reinterpret_cast<vec_t*>(st));
-  }
 #pragma unroll
-  for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
-  if (d < D && sub == 0) {
-    const float yv = part + a.Dk[d] * s_x[c];
-    const float zv = load_any(a.z, b * a.z_stride + d, a.io_bf16);
-    store_any(a.y, b * a.y_stride + d, yv * silu(zv), a.y_bf16);
+    for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
+    if (d < D && sub == 0) {
+      const float yv = part + a.Dk[d] * s_x[cc];
+      const float zv = load_any(a.z, b * a.z_stride + d, a.io_bf16);
+      store_any(a.y, b * a.y_stride + d, yv * silu(zv), a.y_bf16);
+    }
   }
 }
 
 template <typename TS, int N>
 static hipError_t launch_m1w(const Mamba1Params& p, int W, int batch, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(TS);
-  constexpr int CPW = kM1Threads / (N / VEC);
+  constexpr int CPW = kM1Threads / (N / VEC) * m1_passes<TS, N>();
   const dim3 grid((p.D + CPW - 1) / CPW, batch), block(kM1Threads);
   switch (W) {
     case 2: hipLaunchKernelGGL((mamba1_decode_kernel<TS, N, 2>), grid, block, 0, s, p); break;
