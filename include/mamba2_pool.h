@@ -234,7 +234,8 @@ m2_status mamba2_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, c
  *              (the pages' "all" mode, one checkpoint every ckpt_interval tokens,
  *              is max_ckpt columns with every slot given).
  * Device tensors: x, B, C, z, dt, y as in mamba2_decode_step with rows = packed tokens
- * (x, B, C 16-byte aligned with 16-byte multiple row strides).
+ * (x, B, C 16-byte aligned with 16-byte multiple row strides; the row strides of x, z
+ * and y below 16 MiB, else M2_ERR_SHAPE).
  * chunk_size: multiple of 16, at most 256.  Chunks start at each sequence's
  * first row.  workspace: device memory of at least
  * mamba2_prefill_workspace_size(...) bytes, 256-byte aligned, used as scratch

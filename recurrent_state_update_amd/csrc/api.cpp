@@ -545,6 +545,10 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
                         {"C", C, C_stride, GN, ies, true},          {"z", z, z_stride, sh.I, ies, false},
                         {"dt", dt, dt_stride, sh.H, ies, false},    {"y", y, y_stride, sh.I, esize(y_dtype), false}};
   if (m2_status st = check_io(io, 6)) return st;
+  // the walk addresses the rows of a chunk with 32-bit byte offsets from the chunk's first row
+  if (x_stride * ies >= (int64_t)1 << 24 || z_stride * ies >= (int64_t)1 << 24 ||
+      y_stride * esize(y_dtype) >= (int64_t)1 << 24)
+    return fail(M2_ERR_SHAPE, "prefill row strides of x, z and y must be below 16 MiB");
   if (!m2::prefill_supported(sh.P, sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "prefill supports head_dim in {16,32,64,128} and d_state in {16,32,64,128}");
 

@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
   // valid row and are replaced by zeros (or the slot's window before the sequence)
   constexpr int OCT = NP / 8, NOCT = 2 * OCT, TBS = kThreads / NOCT;
   constexpr int NIT = (kMaxRowTiles * 2 + TBS - 1) / TBS;
-  constexpr int PRE = IOBF ? NIT : 1;   // items whose rows are requested ahead (fp32 rows: one)
+  constexpr int PRE = 1;   // items whose rows are requested ahead (fp32 rows: one)
   const int ntb = (len + 7) / 8;
   const int o = tid % NOCT, tb0 = tid / NOCT;
   const bool isC = o >= OCT;
@@ -519,43 +519,41 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
 // ------------------------------------------------------------------ 2. the walk over each sequence's chunks
 // One workgroup of 512 threads per (sequence, head, part of PP head_dim channels) walks the
 // sequence's chunks in order with the running state h (PP x N) in fp32 MFMA accumulators, so the
-// state passes from chunk to chunk on chip.  Per chunk:
-//  A. the chunk's raw x rows (prefetched during the previous chunk) go into a ring of raw rows
-//     indexed by sequence offset, so the W-1 rows before the chunk are still there; per-token
-//     tables of the decay factors in log2 units;
-//  B. causal conv + SiLU of the part's x channels -> x^T and (w x)^T (w_j = exp(a_last - a_j)
-//     Delta_j) as bf16 operand planes in LDS, and the entering state h_in -> LDS;
-//  C. outputs, formed transposed, Y^T = h_in^T (exp(a) C)^T + X^T (M o L)^T, two 16-token row
-//     tiles per wave (w and 15 - w), so that a lane holds four consecutive channels of one
-//     token: C h_in from the permuted C rows, then (M o L) X from the C B^T blocks of the causal
-//     pairs masked by the decay (below the diagonal exp(a_i - a_j) = 2^(a2_i - a2_ref) times a
-//     column factor, both <= 1; on the diagonal block the exponent is taken directly, with the
-//     causal mask and D on the diagonal), then the gate y = acc * SiLU(z);
-//  D. h <- exp(a_last) h + (w x)^T B over the chunk's tokens (wave w: state columns 16w ..);
+// state passes from chunk to chunk on chip.  The conv of a chunk runs one step ahead of the
+// chunk's products, into the other of two LDS buffers, so that one barrier per step orders every
+// LDS access.  Step k:
+//  B. causal conv + SiLU of chunk k+1's x channels straight from its raw rows (requested during
+//     step k-1, the W-1 rows before the chunk included) -> x^T, (w x)^T (w_j = exp(a_last - a_j)
+//     Delta_j) and (c x)^T (c_j: the column factors of the output product) as bf16 planes;
+//  C. outputs of chunk k, formed transposed, Y^T = h_in^T (exp(a) C)^T + X^T (M o L)^T, two
+//     16-token row tiles per wave (w and 15 - w), so that a lane holds four consecutive channels
+//     of one token: C h_in from the permuted C rows, then (M o L) X from the C B^T blocks of the
+//     causal pairs masked by the decay (below the diagonal by a recurrence over the K-steps' last
+//     tokens whose factors are all <= 1; on the diagonal block the exponent is taken directly,
+//     with the causal mask and D on the diagonal), then the gate y = acc * SiLU(z);
+//  D. h <- exp(a_last) h + (w x)^T B over chunk k's tokens (wave w: state columns 16w ..), with
+//     the next steps' loads issued between its K-steps;
+//  T. per-token decay tables of chunk k+2 (log2 units) into the third of three table sets;
+//  H. the state leaving chunk k -> the other LDS state buffer (bf16 planes), read by step k+1;
 //  E. after a checkpoint chunk, the state (rounded) and the raw-input window into the slot.
 // After the last chunk the state and the window go to the sequence's slot.  The part-0
 // workgroup of a group's first head also writes the windows of the group's B and C channels.
 template <bool SPLIT, int PP, int N> struct WalkLds {
   static constexpr int NP = N < 32 ? 32 : N;
   static constexpr int NPL = SPLIT ? 2 : 1;
-  static constexpr int RING = kMaxRowTiles * 16 + 8;   // raw rows kept: a chunk and the 3 rows before it
-  static constexpr int MIRROR = 11;                    // ring rows 0..10 are also kept past its end, so
-                                                       // 11 consecutive rows never wrap
-  static constexpr int LDR = PP + 4;                   // fp32 pitch of a raw row
   static constexpr int LDX = kMaxRowTiles * 16 + 4;    // u16 pitch of an x^T row (tokens)
   static constexpr int LDH = NP + 4;                   // u16 pitch of a state row
   static constexpr int XPL = PP * LDX;                 // u16 per plane
   static constexpr int HPL = PP * LDH;
-  // byte offsets: the arrays read at fixed positions (tables, taps, state rows, planes) first, so
-  // their addresses fit the 16-bit offsets of LDS instructions; the raw-row ring last
-  static constexpr int OFF_TAB = 0;                                        // sA2, sB2, sCw, sWs
-  static constexpr int OFF_TAPS = OFF_TAB + 4 * 256 * 4;                  // taps [PP][4], bias [PP]
-  static constexpr int OFF_H = (OFF_TAPS + PP * 5 * 4 + 15) / 16 * 16;
-  static constexpr int OFF_XC = OFF_H + NPL * HPL * 2;                    // (c x)^T: x scaled by its column factor
-  static constexpr int OFF_XT = OFF_XC + NPL * XPL * 2;
-  static constexpr int OFF_XW = OFF_XT + NPL * XPL * 2;
-  static constexpr int OFF_RAW = OFF_XW + NPL * XPL * 2;
-  static constexpr int BYTES = OFF_RAW + (RING + MIRROR) * LDR * 4;
+  static constexpr int TSET = 4 * 256 * 4;             // bytes of a chunk's tables: a2, b2, cw, ws
+  static constexpr int HBUF = NPL * HPL * 2;           // bytes of a state buffer
+  static constexpr int PBUF = 3 * NPL * XPL * 2;       // bytes of a plane buffer: (c x)^T, x^T, (w x)^T
+  static constexpr int OFF_TAB = 0;                                     // three table sets
+  static constexpr int OFF_TAPS = OFF_TAB + 3 * TSET;                   // taps [PP][4], bias [PP]
+  static constexpr int OFF_W0 = OFF_TAPS + PP * 5 * 4;                  // raw rows -3 .. -1 [3][PP]
+  static constexpr int OFF_H = (OFF_W0 + 3 * PP * 4 + 15) / 16 * 16;   // two state buffers
+  static constexpr int OFF_P = OFF_H + 2 * HBUF;                        // two plane buffers
+  static constexpr int BYTES = OFF_P + 2 * PBUF;
   static constexpr bool FITS = BYTES <= 160 * 1024;
 };
 
@@ -565,19 +563,14 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   typedef typename std::conditional<SPLIT, float, bf16>::type TS;
   constexpr int NP = L::NP, NPL = L::NPL, NK = NP / 32, PT = PP / 16;
   constexpr int NT = N / 16;                     // state column tiles (one per wave)
-  constexpr int RING = L::RING, LDR = L::LDR, LDX = L::LDX, LDH = L::LDH;
+  constexpr int LDX = L::LDX, LDH = L::LDH, XPL = L::XPL;
   extern __shared__ __align__(16) unsigned char wk_smem[];
-  float* const sRaw = reinterpret_cast<float*>(wk_smem + L::OFF_RAW);
-  u16* const sXT = reinterpret_cast<u16*>(wk_smem + L::OFF_XT);
-  u16* const sXW = reinterpret_cast<u16*>(wk_smem + L::OFF_XW);
-  u16* const sXC = reinterpret_cast<u16*>(wk_smem + L::OFF_XC);
-  u16* const sH = reinterpret_cast<u16*>(wk_smem + L::OFF_H);
-  float* const sA2 = reinterpret_cast<float*>(wk_smem + L::OFF_TAB);
-  float* const sB2 = sA2 + 256;
-  float* const sCw = sB2 + 256;
-  float* const sWs = sCw + 256;
   float* const sTap = reinterpret_cast<float*>(wk_smem + L::OFF_TAPS);
   float* const sBias = sTap + PP * 4;
+  float* const sW0 = reinterpret_cast<float*>(wk_smem + L::OFF_W0);
+  auto tab = [&](int s) { return reinterpret_cast<float*>(wk_smem + L::OFF_TAB + s * L::TSET); };
+  auto hbuf = [&](int b) { return reinterpret_cast<u16*>(wk_smem + L::OFF_H + b * L::HBUF); };
+  auto pbuf = [&](int b) { return reinterpret_cast<u16*>(wk_smem + L::OFF_P + b * L::PBUF); };
 
   const int H = a.sh.H, P = a.sh.P, G = a.sh.G, hpg = H / G, nparts = a.nparts;
   // the workgroups of one (sequence, group) run on one XCD, so the group's C, B^T and C B^T blocks
@@ -596,21 +589,22 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   const float Dh = load_uniform(&a.D[h]);
   const bool bc_windows = hh == 0 && part == 0;   // this workgroup also writes the group's B/C windows
 
-  // ---- set-up: taps, the state rows' padding past d_state, the rows before the sequence
+  // ---- set-up: taps, the raw rows before the sequence, the state rows' padding past d_state
   for (int i = tid; i < PP * 4; i += kThreads) {
     const int cl = i / 4, k = i % 4, W = W1 + 1;
     sTap[i] = k >= 4 - W ? a.conv_w[(int64_t)(c0 + cl) * W + k - (4 - W)] : 0.f;
   }
   for (int i = tid; i < PP; i += kThreads) sBias[i] = a.conv_b[c0 + i];
-  if (NP > N) {
-    for (int i = tid; i < NPL * PP * (NP - N); i += kThreads) {
-      const int pl = i / (PP * (NP - N)), p = (i / (NP - N)) % PP, n = N + i % (NP - N);
-      sH[pl * L::HPL + p * LDH + n] = 0;
-    }
-  }
   for (int i = tid; i < 3 * PP; i += kThreads) {
     const int tau = i / PP - 3, cl = i % PP;
-    sRaw[(RING + tau) * LDR + cl] = (sq.has_init && tau >= -W1) ? window_value(a, sq.slot, c0 + cl, W1 + tau) : 0.f;
+    sW0[i] = (sq.has_init && tau >= -W1) ? window_value(a, sq.slot, c0 + cl, W1 + tau) : 0.f;
+  }
+  if (NP > N) {
+    u16* const h0 = hbuf(0);   // both buffers: 2 NPL consecutive planes
+    for (int i = tid; i < 2 * NPL * PP * (NP - N); i += kThreads) {
+      const int pl = i / (PP * (NP - N)), p = (i / (NP - N)) % PP, n = N + i % (NP - N);
+      h0[pl * L::HPL + p * LDH + n] = 0;
+    }
   }
   // the state: wave w holds columns 16w .. 16w+15 for all PT row tiles (lane: rows 4q + r, column l16)
   const bool st_on = wave < NT;
@@ -626,20 +620,114 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       }
     }
   }
-
-  // ---- prefetch of a chunk's raw x rows (8 channels per item) and token values
-  constexpr int OCT = PP / 8;
-  constexpr int RIT = (kMaxRowTiles * 16 * OCT + kThreads - 1) / kThreads;
-  Raw8<IOBF> praw[RIT];
-  float pd = 0.f, pa = 0.f, pr = 0.f;
-  auto prefetch_raw = [&](const PrefillParams& ap, const ChunkEntry& nc) {
+  // the state (bf16 planes) -> LDS state buffer b
+  auto put_state = [&](int b) {
+    if (!st_on) return;
+    u16* const hb = hbuf(b);
 #pragma unroll
-    for (int it = 0; it < RIT; ++it) {
-      const int idx = min(tid + it * kThreads, kMaxRowTiles * 16 * OCT - 1);
-      const int row = idx / OCT, o = idx % OCT;
-      praw[it].load(ap.x, (int64_t)(nc.t0 + (row < nc.len ? row : 0)) * ap.x_stride + c0 + 8 * o);
+    for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u16 hi, lo = 0;
+        if (SPLIT) split2(accS[pt][r], hi, lo);
+        else hi = bits_of(from_f32<bf16>(accS[pt][r]));
+        u16* d = hb + (pt * 16 + 4 * q + r) * LDH + wave * 16 + l16;
+        d[0] = hi;
+        if (SPLIT) d[L::HPL] = lo;
+      }
     }
   };
+
+  // ---- the conv items: thread (channel pair cp, group of TPT tokens); its raw rows j0-3 ..
+  // j0+TPT-1 of the chunk (rows before the sequence come from the slot's window in LDS; rows past
+  // the chunk repeat its last row: finite, and their token weights are zero)
+  constexpr int NCP = PP / 2, TPT = PP == 32 ? 8 : 4, NRW = TPT + 3;
+  static_assert(NCP * (kMaxRowTiles * 16 / TPT) == kThreads, "one conv item per thread");
+  const int cp = tid % NCP, j0 = TPT * (tid / NCP), ccl = 2 * cp;
+  typedef typename std::conditional<IOBF, uint32_t, f32x2>::type RawPair;
+  constexpr int ES = IOBF ? 2 : 4;   // bytes of an x or z element
+  // Rows of a chunk are addressed as a wave-uniform base (the chunk's first row read) plus a
+  // 32-bit byte offset per lane: row pitches are below 16 MiB (checked by the host) and a chunk
+  // spans at most 262 rows.
+  const uint32_t xsb = (uint32_t)(a.x_stride * ES), xcol = (uint32_t)((c0 + ccl) * ES);
+  RawPair rr[NRW];
+  auto prefetch_raw = [&](const PrefillParams& ap, const ChunkEntry& nc) {
+    const int lo = -min(3, nc.tau0), span = nc.len - 1 - lo;
+    const char* const base = static_cast<const char*>(ap.x) + (int64_t)(nc.t0 + lo) * ap.x_stride * ES;
+    const int u0 = j0 - 3 - lo;
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      const uint32_t u = (uint32_t)min(max(u0 + r, 0), span);
+      rr[r] = *reinterpret_cast<const RawPair*>(base + (__umul24(u, xsb) + xcol));
+    }
+  };
+  // the conv of one chunk into plane buffer pl with its tables tb; `mid` runs once the raw rows
+  // are in registers (it issues stores: by then no load that the conv waits for is in flight)
+  auto conv_chunk = [&](u16* pl, const float* tb, int tau0, auto mid) {
+    float rw[NRW][2];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      if constexpr (IOBF) { rw[r][0] = lo_f32(rr[r]); rw[r][1] = hi_f32(rr[r]); }
+      else { rw[r][0] = rr[r][0]; rw[r][1] = rr[r][1]; }
+    }
+    // a chunk that starts fewer than 3 rows into its sequence: the rows before the sequence
+    // (offset tau0 + r - 3 < 0) come from the slot's window
+    if (tau0 < 3 && j0 == 0) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        if (tau0 + r < 3) { rw[r][0] = sW0[(tau0 + r) * PP + ccl]; rw[r][1] = sW0[(tau0 + r) * PP + ccl + 1]; }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    float wsv[TPT], cwv[TPT];
+#pragma unroll
+    for (int m = 0; m < TPT / 4; ++m) {
+      const floatx4 w4 = *reinterpret_cast<const floatx4*>(tb + 768 + j0 + 4 * m);
+      const floatx4 c4 = *reinterpret_cast<const floatx4*>(tb + 512 + j0 + 4 * m);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { wsv[4 * m + e] = w4[e]; cwv[4 * m + e] = c4[e]; }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const floatx4 w4 = *reinterpret_cast<const floatx4*>(sTap + (ccl + e) * 4);
+      const float b = sBias[ccl + e];
+      float xv[TPT], wv[TPT], cv[TPT];
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        float x = b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x += w4[k] * rw[r + k][e];
+        x = silu(x);
+        xv[r] = x;
+        wv[r] = x * wsv[r];
+        cv[r] = x * cwv[r];
+      }
+      auto put = [&](u16* base, const float (&v)[TPT]) {
+        uint32_t hw[TPT / 2], lw[TPT / 2];
+#pragma unroll
+        for (int m = 0; m < TPT / 2; ++m) {
+          hw[m] = pack_bf16x2(v[2 * m], v[2 * m + 1]);
+          if (SPLIT) lw[m] = pack_bf16x2(v[2 * m] - lo_f32(hw[m]), v[2 * m + 1] - hi_f32(hw[m]));
+        }
+        uint32_t* d = reinterpret_cast<uint32_t*>(base + (ccl + e) * LDX + j0);
+#pragma unroll
+        for (int m = 0; m < TPT / 4; ++m) *reinterpret_cast<uint2*>(d + 2 * m) = uint2{hw[2 * m], hw[2 * m + 1]};
+        if (SPLIT) {
+          uint32_t* dl = reinterpret_cast<uint32_t*>(base + XPL + (ccl + e) * LDX + j0);
+#pragma unroll
+          for (int m = 0; m < TPT / 4; ++m) *reinterpret_cast<uint2*>(dl + 2 * m) = uint2{lw[2 * m], lw[2 * m + 1]};
+        }
+      };
+      put(pl, cv);
+      put(pl + NPL * XPL, xv);
+      put(pl + 2 * NPL * XPL, wv);
+    }
+  };
+
+  // ---- a chunk's token values (one token per thread) and its decay tables
+  float pd = 0.f, pa = 0.f, pr = 0.f;
   auto prefetch_tok = [&](const PrefillParams& ap, const ChunkEntry& nc) {
     const int j = min(tid & 255, nc.len - 1);
     const float* dAh = ap.dA + (int64_t)h * T + nc.t0;
@@ -647,26 +735,40 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     pa = dAh[j];
     pr = dAh[min(j | 31, nc.len - 1)];
   };
-  const ChunkEntry first = load_uniform(&a.chunks[sq.chunk0]);
-  prefetch_raw(a, first);
-  prefetch_tok(a, first);
-  __builtin_amdgcn_sched_barrier(0);
+  auto put_tables = [&](float* tb, const ChunkEntry& nc) {
+    const float al = load_uniform(&a.dA[(int64_t)h * T + nc.t0 + nc.len - 1]);
+    if (tid < 256) {
+      const bool ok = tid < nc.len;
+      tb[tid] = ok ? pa * kLog2e : -INFINITY;
+      tb[256 + tid] = ok ? pa * kLog2e - __builtin_amdgcn_logf(pd) : 0.f;
+      tb[512 + tid] = ok ? fast_exp2((pr - pa) * kLog2e) * pd : 0.f;
+      tb[768 + tid] = ok ? fast_exp2((al - pa) * kLog2e) * pd : 0.f;
+    }
+  };
 
   const int rts[2] = {wave, kMaxRowTiles - 1 - wave};
   const int m0 = wave >> 1;           // K-steps below row tile 0 (7 - m0 below row tile 1)
+  // the diagonal block of a row tile, lane (q, l16): row 4q + e against column l16 -> the causal
+  // mask as an exponent offset (0, or -inf above the diagonal) and D on the diagonal
+  float dmask[4], ddiag[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dmask[e] = e <= l16 - 4 * q ? 0.f : -INFINITY;
+    ddiag[e] = e == l16 - 4 * q ? Dh : 0.f;
+  }
 
-  // ---- the output product's operands of a chunk, requested a chunk ahead (after the previous
-  // chunk's outputs, while its state product runs): C columns and C B^T blocks of this wave's row
-  // tiles (below-diagonal blocks of tile 0 in gb[0 .. m0-1], of tile 1 from gb[6] down; the
-  // diagonal blocks in gd), and z (4 channels of one token per lane and column tile)
+  // ---- the output product's operands of a chunk, requested a step ahead (while the previous
+  // chunk's state product runs): C columns and C B^T blocks of this wave's row tiles (below-diagonal
+  // blocks of tile 0 in gb[0 .. m0-1], of tile 1 from gb[6] down; the diagonal blocks in gd), and z
+  // (4 channels of one token per lane and column tile)
   typedef typename std::conditional<IOBF, u16x4, floatx4>::type ZQuad;
+  const uint32_t zsb = (uint32_t)(a.z_stride * ES);
   Frag<SPLIT> cfr[2][NK];
   Frag<SPLIT> gb[7], gd[2];
   ZQuad zr[2][PT];
   // Every load is issued unconditionally (row tiles past the chunk read row tile 0 instead): the
-  // in-order memory counter then lets each later wait cover exactly the loads it needs.  The loads
-  // come in steps, spread over the previous chunk's state product: step 0 / 1 is the diagonal
-  // block and z of tile 0 / 1, step 2 + k is C B^T slot k.
+  // in-order memory counter then lets each later wait cover exactly the loads it needs.  Step 0 /
+  // 1 is the diagonal block and z of tile 0 / 1, step 2 + k is C B^T slot k.
   auto load_op = [&](const PrefillParams& ap, int step, int cidx, const ChunkEntry& nc) {
     const int64_t cgn = (int64_t)cidx * G + g;
     const bool v0 = rts[0] * 16 < nc.len, v1 = rts[1] * 16 < nc.len;
@@ -686,18 +788,19 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       const int t = step;
       const int i = rv[t] * 16 + l16;
       load_g(rv[t], rv[t] >> 1, gd[t]);
-      const int64_t row = nc.t0 + (i < nc.len ? i : 0);
+      const char* const zb = static_cast<const char*>(ap.z) + (int64_t)nc.t0 * ap.z_stride * ES;
+      const uint32_t zrow = __umul24((uint32_t)(i < nc.len ? i : 0), zsb);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const int col = c0 + pt * 16 + 4 * q;
+        const char* const zp = zb + (zrow + (uint32_t)((c0 + pt * 16 + 4 * q) * ES));
         if constexpr (ZYV) {
-          if constexpr (IOBF) zr[t][pt] = *reinterpret_cast<const u16x4*>(static_cast<const u16*>(ap.z) + row * ap.z_stride + col);
-          else zr[t][pt] = *reinterpret_cast<const floatx4*>(static_cast<const float*>(ap.z) + row * ap.z_stride + col);
+          if constexpr (IOBF) zr[t][pt] = *reinterpret_cast<const u16x4*>(zp);
+          else zr[t][pt] = *reinterpret_cast<const floatx4*>(zp);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            if constexpr (IOBF) zr[t][pt][r] = static_cast<const u16*>(ap.z)[row * ap.z_stride + col + r];
-            else zr[t][pt][r] = static_cast<const float*>(ap.z)[row * ap.z_stride + col + r];
+            if constexpr (IOBF) zr[t][pt][r] = reinterpret_cast<const u16*>(zp)[r];
+            else zr[t][pt][r] = reinterpret_cast<const float*>(zp)[r];
           }
         }
       }
@@ -709,181 +812,116 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       load_g(rt, min(kk, rt >> 1), gb[k]);
     }
   };
-#pragma unroll
-  for (int st = 0; st < 9; ++st) load_op(a, st, sq.chunk0, first);
-  // the C columns of this wave's row tiles (requested at the start of each chunk's conv phase)
+  // the C columns of row tile t of this wave
   auto load_c = [&](const PrefillParams& ap, int t, int cidx, const ChunkEntry& nc) {
     const u16* const cfb = ap.Cf + ((int64_t)cidx * G + g) * QC * NP;
-    {
-      const int i = (rts[t] * 16 < nc.len ? rts[t] : 0) * 16 + l16;
+    const int i = (rts[t] * 16 < nc.len ? rts[t] : 0) * 16 + l16;
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        const u16* p = cfb + (int64_t)i * NP + 32 * ks + 8 * q;
-        const u16x8 hi = *reinterpret_cast<const u16x8*>(p);
+    for (int ks = 0; ks < NK; ++ks) {
+      const u16* p = cfb + (int64_t)i * NP + 32 * ks + 8 * q;
+      const u16x8 hi = *reinterpret_cast<const u16x8*>(p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cfr[t][ks].hi[e] = bf_of(hi[e]);
-        if (SPLIT) {
-          const u16x8 lo = *reinterpret_cast<const u16x8*>(p + ap.Cf_plane);
+      for (int e = 0; e < 8; ++e) cfr[t][ks].hi[e] = bf_of(hi[e]);
+      if (SPLIT) {
+        const u16x8 lo = *reinterpret_cast<const u16x8*>(p + ap.Cf_plane);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) cfr[t][ks].lo[e] = bf_of(lo[e]);
-        }
+        for (int e = 0; e < 8; ++e) cfr[t][ks].lo[e] = bf_of(lo[e]);
       }
     }
   };
 
-  // A chunk's gated outputs stay in registers until the next chunk's conv phase issues their
-  // stores (lane: channels c0 + 16 pt + 4q .. +3 of packed row yrow[t], -1 for none).  The waits
-  // then see only loads in flight, except the first wait of the output phase, by which time the
-  // stores issued before the conv have long completed: loads and stores share one counter, and
-  // any wait while both are in flight has to wait for all of them.
+  // A chunk's gated outputs stay in registers until the next step's conv has its raw rows, and
+  // are stored then (lane: channels c0 + 16 pt + 4q .. +3 of row yrow[t] of that chunk).
+  // Loads and stores share one counter, and any wait while both are in flight has to wait for all
+  // of them: the stores go out when the conv's loads have arrived, and the conv's arithmetic
+  // covers them before the output phase's first wait.
   floatx4 ys[2][PT];
-  int yrow[2] = {-1, -1};
+  int yrow[2] = {-1, -1};                 // row inside the stored chunk, -1 for none
+  char* ybase = static_cast<char*>(a.y);  // the stored chunk's first row
+  const int yes = a.y_bf16 ? 2 : 4;
+  const uint32_t ysb = (uint32_t)(a.y_stride * yes);
   auto store_y = [&](const PrefillParams& ap) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (yrow[t] < 0) continue;
-      const int64_t row = yrow[t];
+      const uint32_t yr = __umul24((uint32_t)yrow[t], ysb);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const int col = c0 + pt * 16 + 4 * q;
+        char* const yp = ybase + (yr + (uint32_t)((c0 + pt * 16 + 4 * q) * yes));
         const floatx4 yv = ys[t][pt];
-        if constexpr (ZYV) {
-          if (ap.y_bf16) {
-            u16x4 o;
+        if (ap.y_bf16) {
+          u16x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = bits_of(from_f32<bf16>(yv[r]));
-            *reinterpret_cast<u16x4*>(static_cast<u16*>(ap.y) + row * ap.y_stride + col) = o;
+          for (int r = 0; r < 4; ++r) o[r] = bits_of(from_f32<bf16>(yv[r]));
+          if constexpr (ZYV) {
+            *reinterpret_cast<u16x4*>(yp) = o;
           } else {
-            *reinterpret_cast<floatx4*>(static_cast<float*>(ap.y) + row * ap.y_stride + col) = yv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) reinterpret_cast<u16*>(yp)[r] = o[r];
           }
         } else {
+          if constexpr (ZYV) {
+            *reinterpret_cast<floatx4*>(yp) = yv;
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) store_any(ap.y, row * ap.y_stride + col + r, yv[r], ap.y_bf16);
+            for (int r = 0; r < 4; ++r) reinterpret_cast<float*>(yp)[r] = yv[r];
+          }
         }
       }
+      yrow[t] = -1;
     }
   };
 
+  // ---- before the first step: tables of chunks 0 and 1, the conv of chunk 0, the entering state
+  {
+    const ChunkEntry f0 = load_uniform(&a.chunks[sq.chunk0]);
+    const ChunkEntry f1 = load_uniform(&a.chunks[sq.chunk0 + min(1, sq.nchunk - 1)]);
+    prefetch_raw(a, f0);
+    prefetch_tok(a, f0);
+    put_tables(tab(0), f0);
+    prefetch_tok(a, f1);
+    put_tables(tab(1), f1);
+    lds_sync();   // taps, window rows, tables
+    conv_chunk(pbuf(0), tab(0), f0.tau0, [] {});
+    put_state(0);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_raw(a, f1);
+#pragma unroll
+    for (int st = 0; st < 9; ++st) load_op(a, st, sq.chunk0, f0);
+    load_c(a, 0, sq.chunk0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_sync();
+  }
+
+  int ts0 = 0, ts1 = 1, ts2 = 2;   // table sets of chunks k, k+1, k+2
   for (int kc = 0; kc < sq.nchunk; ++kc) {
+    const int pb = kc & 1;
     const int cidx = sq.chunk0 + kc;
     const ChunkEntry ch = load_uniform(&a.chunks[cidx]);
-    const int cnext = sq.chunk0 + min(kc + 1, sq.nchunk - 1);   // past the last chunk: itself again
+    const int cnext = sq.chunk0 + min(kc + 1, sq.nchunk - 1);   // past the last chunk: the last again
     const ChunkEntry nx = load_uniform(&a.chunks[cnext]);
+    const int cnn = sq.chunk0 + min(kc + 2, sq.nchunk - 1);
+    const ChunkEntry nx2 = load_uniform(&a.chunks[cnn]);
     const int len = ch.len;
     const float alast = load_uniform(&a.dA[(int64_t)h * T + ch.t0 + len - 1]);
     const int64_t cg = (int64_t)cidx * G + g;
+    const float* const sA2 = tab(ts0);
+    const float* const sB2 = sA2 + 256;
+    const u16* const sXC = pbuf(pb);
+    const u16* const sXT = sXC + NPL * XPL;
+    const u16* const sXW = sXT + NPL * XPL;
+    const u16* const sH = hbuf(pb);
 
-    // ---- A. raw rows into the ring (zeros for the rows past the chunk, so that every conv output
-    // there is finite and the zero token weights past the chunk cancel it), token tables
-#pragma unroll
-    for (int it = 0; it < RIT; ++it) {
-      const int idx = tid + it * kThreads;
-      const int row = idx / OCT, o = idx % OCT;
-      if (idx < kMaxRowTiles * 16 * OCT) {
-        const int pos = (ch.tau0 + row) % RING;
-        const bool in = row < len;
-        const floatx4 v0 = in ? floatx4{praw[it].at(0), praw[it].at(1), praw[it].at(2), praw[it].at(3)} : floatx4{0.f, 0.f, 0.f, 0.f};
-        const floatx4 v1 = in ? floatx4{praw[it].at(4), praw[it].at(5), praw[it].at(6), praw[it].at(7)} : floatx4{0.f, 0.f, 0.f, 0.f};
-        float* d = sRaw + pos * LDR + 8 * o;
-        *reinterpret_cast<floatx4*>(d) = v0;
-        *reinterpret_cast<floatx4*>(d + 4) = v1;
-        if (pos < L::MIRROR) {
-          *reinterpret_cast<floatx4*>(d + RING * LDR) = v0;
-          *reinterpret_cast<floatx4*>(d + RING * LDR + 4) = v1;
-        }
-      }
-    }
-    if (tid < 256) {
-      const bool ok = tid < len;
-      sA2[tid] = ok ? pa * kLog2e : -INFINITY;
-      sB2[tid] = ok ? pa * kLog2e - __builtin_amdgcn_logf(pd) : 0.f;
-      sCw[tid] = ok ? fast_exp2((pr - pa) * kLog2e) * pd : 0.f;
-      sWs[tid] = ok ? fast_exp2((alast - pa) * kLog2e) * pd : 0.f;
-    }
-    lds_sync();
+    // ---- B. the conv of the next chunk (the previous chunk's outputs are stored once its raw
+    // rows are in)
+    __builtin_amdgcn_sched_barrier(0);
+    if (kc + 1 < sq.nchunk) conv_chunk(pbuf(pb ^ 1), tab(ts1), nx.tau0, [&] { store_y(a); });
+    else store_y(a);
+    __builtin_amdgcn_sched_barrier(0);
 
     const bool vt[2] = {rts[0] * 16 < len, rts[1] * 16 < len};
-    __builtin_amdgcn_sched_barrier(0);
-    load_c(a, 0, cidx, ch);   // tile 1's C columns follow under tile 0's products
-    __builtin_amdgcn_sched_barrier(0);
-    store_y(a);   // the previous chunk's outputs
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- B. conv of the part's x channels: thread (channel pair cp, token octet to)
-    {
-      constexpr int NCP = PP / 2;
-      const int cp = tid % NCP, to = tid / NCP;
-      if (to < kMaxRowTiles * 2) {
-        const int j0 = 8 * to, cl = 2 * cp;
-        float rw[11][2];   // raw rows j0-3 .. j0+7 of the two channels (zeros past the chunk)
-        {
-          const float* src = sRaw + ((ch.tau0 + j0 - 3 + RING) % RING) * LDR + cl;   // mirrored: no wrap
-#pragma unroll
-          for (int k = 0; k < 11; ++k) {
-            rw[k][0] = src[k * LDR];
-            rw[k][1] = src[k * LDR + 1];
-          }
-        }
-        // per channel: x, (w x) and (c x) of the 8 tokens, each as one plane's 8-token piece (past
-        // the chunk x is finite and both weights are zero)
-        const floatx4 ws0 = *reinterpret_cast<const floatx4*>(sWs + j0), ws1 = *reinterpret_cast<const floatx4*>(sWs + j0 + 4);
-        const floatx4 cw0 = *reinterpret_cast<const floatx4*>(sCw + j0), cw1 = *reinterpret_cast<const floatx4*>(sCw + j0 + 4);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const floatx4 w4 = *reinterpret_cast<const floatx4*>(sTap + (cl + e) * 4);
-          const float b = sBias[cl + e];
-          float xv[8], wv[8], cv[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            float x = b;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) x += w4[k] * rw[r + k][e];
-            x = silu(x);
-            xv[r] = x;
-            wv[r] = x * (r < 4 ? ws0[r] : ws1[r - 4]);
-            cv[r] = x * (r < 4 ? cw0[r] : cw1[r - 4]);
-          }
-          auto put = [&](u16* base, const float (&v)[8]) {
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              hw[m] = pack_bf16x2(v[2 * m], v[2 * m + 1]);
-              if (SPLIT) lw[m] = pack_bf16x2(v[2 * m] - lo_f32(hw[m]), v[2 * m + 1] - hi_f32(hw[m]));
-            }
-            uint32_t* d = reinterpret_cast<uint32_t*>(base + (cl + e) * LDX + j0);
-            *reinterpret_cast<uint2*>(d) = uint2{hw[0], hw[1]};
-            *reinterpret_cast<uint2*>(d + 2) = uint2{hw[2], hw[3]};
-            if (SPLIT) {
-              uint32_t* dl = reinterpret_cast<uint32_t*>(base + L::XPL + (cl + e) * LDX + j0);
-              *reinterpret_cast<uint2*>(dl) = uint2{lw[0], lw[1]};
-              *reinterpret_cast<uint2*>(dl + 2) = uint2{lw[2], lw[3]};
-            }
-          };
-          put(sXT, xv);
-          put(sXW, wv);
-          put(sXC, cv);
-        }
-      }
-    }
-    // the entering state -> LDS rows (bf16 planes)
-    if (st_on) {
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u16 hi, lo = 0;
-          if (SPLIT) split2(accS[pt][r], hi, lo);
-          else hi = bits_of(from_f32<bf16>(accS[pt][r]));
-          u16* d = sH + (pt * 16 + 4 * q + r) * LDH + wave * 16 + l16;
-          d[0] = hi;
-          if (SPLIT) d[L::HPL] = lo;
-        }
-      }
-    }
-    lds_sync();
-
-    // ---- loads of the state product's operand (bf16: now, under the output product), and the
-    // next chunk's raw rows and token values
+    // ---- loads of the state product's operand (bf16: under the output product; fp32-faithful
+    // planes: half there, half at the state product's start)
     const int nkb = (len + 31) / 32;
     Frag<SPLIT> bt[kMaxRowTiles / 2];
     const u16* const btb = a.Btf + (cg * N + (st_on ? wave : 0) * 16 + l16) * QC + 8 * q;
@@ -927,13 +965,22 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       // last tokens R(k): acc <- 2^(a2_R(k) - a2_R(k-1)) acc + (c x)_k^T (C B^T)_k^T (a2_R(-1) = 0,
       // every factor <= 1), with the column factors c_j = exp(a_R(k) - a_j) Delta_j folded into x;
       // at the end the row factor 2^(a2_i - a2_R(last)) gives every term its full decay
+      // (each product's LDS operand is read one product ahead, so its latency hides under the
+      // previous product)
       floatx4 acc[PT];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < PT; ++pt) acc[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      {
+        constexpr int NI = NK * PT;   // product i: K-step i / PT of row block i % PT
+        Frag<SPLIT> hf[2];
+        hf[0] = lds_frag<SPLIT>(sH, L::HPL, LDH, l16, 0, q);
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks)
-          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sH, L::HPL, LDH, pt * 16 + l16, 32 * ks, q), cfr[t][ks], acc[pt]);
+        for (int i = 0; i < NI; ++i) {
+          if (i + 1 < NI) hf[(i + 1) & 1] = lds_frag<SPLIT>(sH, L::HPL, LDH, ((i + 1) % PT) * 16 + l16, 32 * ((i + 1) / PT), q);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[i % PT] = mma<SPLIT>(hf[i & 1], cfr[t][i / PT], acc[i % PT]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // the next operands, requested under this tile's products: tile 1's C columns and the state
       // product's B^T (bf16: all of it; fp32-faithful planes: half here, half at its start)
@@ -946,18 +993,31 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       float aprev = 0.f;
+      {
+        Frag<SPLIT> xf[2][PT];   // the (c x) operands of K-step k + 1 are read during K-step k
+        if (MT[t] > 0) {
 #pragma unroll
-      for (int k = 0; k < MT[t]; ++k) {
-        const int jk = 32 * k;
-        const float aR = sA2[jk + 31];
-        const float sk = fast_exp2(aR - aprev);
-        aprev = aR;
-        const Frag<SPLIT>& gk = t == 0 ? gb[k] : gb[6 - k];
+          for (int pt = 0; pt < PT; ++pt) xf[0][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, pt * 16 + l16, 0, q);
+        }
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
+        for (int k = 0; k < MT[t]; ++k) {
+          const int jk = 32 * k;
+          if (k + 1 < MT[t]) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pt][r] *= sk;
-          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXC, L::XPL, LDX, pt * 16 + l16, jk, q), gk, acc[pt]);
+            for (int pt = 0; pt < PT; ++pt) xf[(k + 1) & 1][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, pt * 16 + l16, jk + 32, q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const float aR = sA2[jk + 31];
+          const float sk = fast_exp2(aR - aprev);
+          aprev = aR;
+          const Frag<SPLIT>& gk = t == 0 ? gb[k] : gb[6 - k];
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pt][r] *= sk;
+            acc[pt] = mma<SPLIT>(xf[k & 1][pt], gk, acc[pt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       {
@@ -972,7 +1032,6 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       // tiles) or entirely above it (even tiles)
       {
         const int jk = 32 * MT[t];
-        const int dsel = l16 - 4 * q;
         const floatx4 bd = *reinterpret_cast<const floatx4*>(&sB2[16 * rt + 4 * q]);
         float gv[8];
 #pragma unroll
@@ -985,25 +1044,23 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
           const floatx4 bb = *reinterpret_cast<const floatx4*>(&sB2[jk + 4 * q]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = fast_exp2(a2i - bd[e]) * gv[e + 4];
-            mv[e + 4] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e + 4] = fmaf(fast_exp2((a2i + dmask[e]) - bd[e]), gv[e + 4], ddiag[e]);
             mv[e] = fast_exp2(a2i - bb[e]) * gv[e];
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = fast_exp2(a2i - bd[e]) * gv[e];
-            mv[e] = (e <= dsel ? v : 0.f) + (e == dsel ? Dh : 0.f);
+            mv[e] = fmaf(fast_exp2((a2i + dmask[e]) - bd[e]), gv[e], ddiag[e]);
             mv[e + 4] = 0.f;
           }
         }
         const Frag<SPLIT> mf = make_frag<SPLIT>(mv);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
-          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXT, L::XPL, LDX, pt * 16 + l16, jk, q), mf, acc[pt]);
+          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXT, XPL, LDX, pt * 16 + l16, jk, q), mf, acc[pt]);
       }
       // the gate: lane holds channels c0 + 16 pt + 4q .. +3 of token i
-      yrow[t] = i < len ? ch.t0 + i : -1;
+      yrow[t] = i < len ? i : -1;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
@@ -1022,11 +1079,16 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       case 2: phase_c(std::integral_constant<int, 2>{}); break;
       default: phase_c(std::integral_constant<int, 3>{}); break;
     }
+    ybase = static_cast<char*>(a.y) + (int64_t)ch.t0 * a.y_stride * yes;
 
     // ---- D. the state: h <- exp(a_last) h + (w x)^T B over the chunk's tokens.  Between its
-    // K-steps the next chunk's loads are issued, in the order that chunk consumes them (raw rows
-    // and token values, then the output operands), so the memory pipeline drains under the MFMAs.
+    // K-steps the next steps' loads are issued, in the order they are consumed: token values
+    // (tables at the end of this step), raw rows (next step's conv), output operands (next step's
+    // output product).
     if (SPLIT) load_bt(a, 4, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_tok(a, nx2);
+    __builtin_amdgcn_sched_barrier(0);
     const float dec = fast_exp2(alast * kLog2e);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -1034,20 +1096,30 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       for (int r = 0; r < 4; ++r) accS[pt][r] *= dec;
     // every K-step, also past a short chunk's end: there the (w x) rows are zeros and the B^T
     // operand repeats the last K-step, so the products add nothing and no branch is needed
+    Frag<SPLIT> wf[2][PT];   // the (w x) operands of K-step kb + 1 are read during K-step kb
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) wf[0][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, pt * 16 + l16, 0, q);
 #pragma unroll
     for (int kb = 0; kb < kMaxRowTiles / 2; ++kb) {
-      if (st_on) {
+      if (kb + 1 < kMaxRowTiles / 2) {
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          accS[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXW, L::XPL, LDX, pt * 16 + l16, 32 * kb, q), bt[kb], accS[pt]);
+        for (int pt = 0; pt < PT; ++pt) wf[(kb + 1) & 1][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, pt * 16 + l16, 32 * kb + 32, q);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (kb == 0) prefetch_raw(a, nx);
-      if (kb == 1) prefetch_tok(a, nx);
+      if (st_on) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) accS[pt] = mma<SPLIT>(wf[kb & 1][pt], bt[kb], accS[pt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb == 0) prefetch_raw(a, nx2);
       if (kb >= 1) load_op(a, kb - 1, cnext, nx);
-      if (kb == 7) load_op(a, 7, cnext, nx), load_op(a, 8, cnext, nx);
+      if (kb == 7) load_op(a, 7, cnext, nx), load_op(a, 8, cnext, nx), load_c(a, 0, cnext, nx);
       __builtin_amdgcn_sched_barrier(0);
     }
+
+    // ---- T, H. tables of chunk k+2; the state leaving this chunk for the next step's outputs
+    if (kc + 2 < sq.nchunk) put_tables(tab(ts2), nx2);
+    put_state(pb ^ 1);
 
     // ---- E. a checkpoint after this chunk: the state (rounded) and the raw-input window
     if (ch.ckpt_slot >= 0) {
@@ -1062,8 +1134,10 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       }
       const int tau = ch.tau0 + len;
       for (int i = tid; i < W1 * PP; i += kThreads) {
-        const int kk = i / PP, cl = i % PP;
-        window_store(ar, ch.ckpt_slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
+        const int kk = i / PP, cl = i % PP, pos = tau - W1 + kk;
+        const float v = pos >= 0 ? load_any(ar.x, (int64_t)(sqr.t0 + pos) * ar.x_stride + c0 + cl, ar.io_bf16)
+                                 : sW0[(3 + pos) * PP + cl];
+        window_store(ar, ch.ckpt_slot, c0 + cl, kk, v);
       }
       if (bc_windows) {
         const int I = ar.sh.I, GN = ar.sh.G * N;
@@ -1081,11 +1155,15 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
           window_store(ar, ch.ckpt_slot, cc, kk, v);
         }
       }
-      // drain the checkpoint stores (this also waits for the next chunk's prefetches, on
-      // checkpoint chunks only): past this branch only loads are in flight on either path
+      // drain the checkpoint stores (this also waits for the next step's loads, on checkpoint
+      // chunks only): past this branch only loads are in flight on either path
       __builtin_amdgcn_s_waitcnt(0);
     }
-    lds_sync();   // every read of this chunk's LDS rows is done
+    lds_sync();   // this step's LDS reads and writes are done
+    const int tr = ts0;
+    ts0 = ts1;
+    ts1 = ts2;
+    ts2 = tr;
   }
 
   store_y(a);   // the last chunk's outputs
@@ -1102,8 +1180,10 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   {
     const int tau = sqr.len;
     for (int i = tid; i < W1 * PP; i += kThreads) {
-      const int kk = i / PP, cl = i % PP;
-      window_store(ar, sqr.slot, c0 + cl, kk, sRaw[((tau - W1 + kk + RING) % RING) * LDR + cl]);
+      const int kk = i / PP, cl = i % PP, pos = tau - W1 + kk;
+      const float v = pos >= 0 ? load_any(ar.x, (int64_t)(sqr.t0 + pos) * ar.x_stride + c0 + cl, ar.io_bf16)
+                               : sW0[(3 + pos) * PP + cl];
+      window_store(ar, sqr.slot, c0 + cl, kk, v);
     }
   }
   if (bc_windows) {

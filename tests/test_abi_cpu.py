@@ -222,6 +222,10 @@ def test_prefill_validation(pool):
     assert prefill(pool, [0, 600], [0], ck=None, max_ck=2, interval=256) == ARG
     assert prefill(pool, [0, 5], [0], x=None) == ARG
     assert prefill(pool, [0, 5], [0], zs=100) == SHAPE
+    # row strides of x, z and y at or above 16 MiB (bf16: 2^23 elements) are refused
+    assert prefill(pool, [0, 5], [0], xs=1 << 23) == SHAPE
+    assert prefill(pool, [0, 5], [0], zs=1 << 23) == SHAPE
+    assert prefill(pool, [0, 5], [0], ys=1 << 23) == SHAPE
     assert prefill(pool, [0, 5], [0], io=5) == DTYPE
     assert prefill(pool, [0, 5], [0], ws=0) == WS
     assert prefill(pool, [0, 5], [0], ws=FAKE + 128) == WS
