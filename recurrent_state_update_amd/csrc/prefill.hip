@@ -912,12 +912,17 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     const u16* const sXW = sXT + NPL * XPL;
     const u16* const sH = hbuf(pb);
 
-    // ---- B. the conv of the next chunk (the previous chunk's outputs are stored once its raw
-    // rows are in)
-    __builtin_amdgcn_sched_barrier(0);
-    if (kc + 1 < sq.nchunk) conv_chunk(pbuf(pb ^ 1), tab(ts1), nx.tau0, [&] { store_y(a); });
-    else store_y(a);
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- B. the conv of the next chunk; the outputs held in registers are stored once its raw
+    // rows are in.  With bf16 operands it runs first (the previous chunk's outputs); with
+    // fp32-faithful operands after the outputs (this chunk's), so that it covers the latency of
+    // the state product's B^T, whose registers would not fit during the output phase
+    auto phase_b = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc + 1 < sq.nchunk) conv_chunk(pbuf(pb ^ 1), tab(ts1), nx.tau0, [&] { store_y(a); });
+      else store_y(a);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (!SPLIT) phase_b();
 
     const bool vt[2] = {rts[0] * 16 < len, rts[1] * 16 < len};
     // ---- loads of the state product's operand (bf16: under the output product; fp32-faithful
@@ -1080,12 +1085,18 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       default: phase_c(std::integral_constant<int, 3>{}); break;
     }
     ybase = static_cast<char*>(a.y) + (int64_t)ch.t0 * a.y_stride * yes;
+    // fp32-faithful planes: the second half of the state product's B^T, now that the output
+    // operands' registers are free; the conv then covers its latency
+    if constexpr (SPLIT) {
+      load_bt(a, 4, 8);
+      phase_b();
+    }
+
 
     // ---- D. the state: h <- exp(a_last) h + (w x)^T B over the chunk's tokens.  Between its
     // K-steps the next steps' loads are issued, in the order they are consumed: token values
     // (tables at the end of this step), raw rows (next step's conv), output operands (next step's
     // output product).
-    if (SPLIT) load_bt(a, 4, 8);
     __builtin_amdgcn_sched_barrier(0);
     prefetch_tok(a, nx2);
     __builtin_amdgcn_sched_barrier(0);
