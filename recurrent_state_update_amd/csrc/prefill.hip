@@ -289,7 +289,8 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
   load_dt(wave);
   // a1. conv + SiLU: thread (octet o, token blocks tb0 + TBS m); octets [0, OCT) are B channels,
   // [OCT, 2 OCT) C channels (past N: zeros); rows outside the sequence or past the chunk read a
-  // valid row and are replaced by zeros (or the slot's window before the sequence)
+  // valid row of the chunk (rows before the sequence are then replaced by the slot's window or
+  // zeros)
   constexpr int OCT = NP / 8, NOCT = 2 * OCT, TBS = kThreads / NOCT;
   constexpr int NIT = (kMaxRowTiles * 2 + TBS - 1) / TBS;
   constexpr int PRE = 1;   // items whose rows are requested ahead (fp32 rows: one)
@@ -306,9 +307,8 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
     const int j0 = 8 * (tb0 + TBS * m);
 #pragma unroll
     for (int k = 0; k < 11; ++k) {
-      const int jj = j0 - 3 + k, tau = ch.tau0 + jj;
-      const bool ok = tau >= 0 && jj < len;
-      r[k].load(src, (int64_t)(sq.t0 + (ok ? tau : ch.tau0)) * stride + col);
+      const int jj = min(max(j0 - 3 + k, -min(3, ch.tau0)), len - 1);   // a row of the sequence
+      r[k].load(src, (int64_t)(sq.t0 + ch.tau0 + jj) * stride + col);
     }
   };
 #pragma unroll
@@ -344,21 +344,22 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
     } else {
       load_rows(m, rr);
     }
-    float xr[11][8];   // the raw rows: zeros outside the sequence or past the chunk
+    // the raw rows; a row past the chunk holds a row of the chunk (finite: the outputs it feeds
+    // are past the chunk, where the walk gives them zero weight or discards them)
+    float xr[11][8];
 #pragma unroll
     for (int k = 0; k < 11; ++k) {
-      const int jj = j0 - 3 + k, tau = ch.tau0 + jj;
-      const bool ok = tau >= 0 && jj < len;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xr[k][e] = ok ? rr[k].at(e) : 0.f;
+      for (int e = 0; e < 8; ++e) xr[k][e] = rr[k].at(e);
     }
-    if (ch.tau0 + j0 < 3 && sq.has_init && chan_ok) {   // rare: rows before the sequence, from the slot's window
+    if (ch.tau0 + j0 < 3) {   // rare: rows before the sequence, from the slot's window or zero
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const int tau = ch.tau0 + j0 - 3 + k;
-        if (tau < 0 && tau >= -W1) {
+        if (tau < 0) {
+          const bool w = sq.has_init && tau >= -W1 && chan_ok;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xr[k][e] = window_value(a, sq.slot, cc0 + e, W1 + tau);
+          for (int e = 0; e < 8; ++e) xr[k][e] = w ? window_value(a, sq.slot, cc0 + e, W1 + tau) : 0.f;
         }
       }
     }
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void bc_kernel(BcArgs args) {
         float x = bias[e];
 #pragma unroll
         for (int k = 0; k < 4; ++k) x += wt[e][k] * xr[r + k][e];
-        v[e] = (chan_ok && j0 + r < len) ? silu(x) : 0.f;
+        v[e] = chan_ok ? silu(x) : 0.f;   // d_state padding: zeros
       }
       uint32_t hw[4], lw[4];
 #pragma unroll
