@@ -48,8 +48,17 @@ __device__ __forceinline__ void load8_any(const void* p, int64_t i, int is_bf16,
 // SiLU(v) = v / (1 + e^-v) with the hardware reciprocal (about 1 ulp) instead of an IEEE divide.
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
-// log(1 + e^v); for v > 20 the correction log1p(e^-v) < 2.1e-9 is below fp32 resolution of v.
-__device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+// log(1 + e^v) from the hardware exp2 and log2.  Above 20 the value is v to fp32 resolution
+// (the correction log1p(e^-v) < 2.1e-9); below, with e = e^v and u = 1 + e rounded,
+// log(u) e / (u - 1) cancels the rounding of u (Goldberg's log1p identity), and is e itself
+// when u rounds to 1.
+__device__ __forceinline__ float softplus(float v) {
+  if (v > 20.f) return v;
+  const float e = __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
+  const float u = 1.f + e;
+  const float um1 = u - 1.f;
+  return um1 == 0.f ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * __builtin_amdgcn_rcpf(um1);
+}
 
 // ------------------------------------------------------------------ MFMA
 // 16x16x32 bf16 tile product on gfx950, fp32 accumulate.  For both operands,

@@ -8,8 +8,7 @@
 // One workgroup of 1024 threads covers a block of channels of one sequence
 // (with states of at most 32 bytes per channel, two channels per lane group).
 // Phase 1: one thread per channel shifts the conv window, convolves, applies
-// SiLU and softplus (from the hardware exp2 and log2, Goldberg's log1p form),
-// and stages x_d and Delta_d in LDS with the row's B and C.
+// SiLU and softplus, and stages x_d and Delta_d in LDS with the row's B and C.
 // Phase 2: a channel's N state values are split over N/VEC lanes, each with one
 // 16-byte non-temporal access (requested before phase 1, so the load overlaps
 // it); the lanes update their values, reduce h' C over the channel's lanes with
@@ -22,16 +21,6 @@ namespace m2 {
 
 constexpr int kM1Threads = 1024;
 
-// log(1 + e^v) from the hardware exp2 and log2.  Above 20 the value is v to fp32 resolution;
-// below, with e = e^v and u = 1 + e rounded, log(u) e / (u - 1) cancels the rounding of u
-// (Goldberg's log1p identity), and is e itself when u rounds to 1.
-__device__ __forceinline__ float m1_softplus(float v) {
-  if (v > 20.f) return v;
-  const float e = __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
-  const float u = 1.f + e;
-  const float um1 = u - 1.f;
-  return um1 == 0.f ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * __builtin_amdgcn_rcpf(um1);
-}
 
 
 template <typename T> struct M1Vec;
@@ -103,7 +92,7 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) v += wt[k] * to_f32(wr[k]);
       s_x[ci] = silu(v);
-      s_dl[ci] = m1_softplus(to_f32(dtr) + dtb) * 1.4426950408889634f;   // Delta log2 e
+      s_dl[ci] = softplus(to_f32(dtr) + dtb) * 1.4426950408889634f;   // Delta log2 e
       // the window keeps raw inputs at the conv dtype: shift the stored words, append the input
 #pragma unroll
       for (int k = 0; k < W - 2; ++k) wp[k] = wr[k + 1];
@@ -348,7 +337,7 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
 #pragma unroll
         for (int k = 0; k < W; ++k) v += w[k] * xs[(r0 + r + k) & (R - 1)][pc];
         const float xv = silu(v);
-        const float dl = m1_softplus((pon ? pdt[m] : 0.f) + bias);
+        const float dl = softplus((pon ? pdt[m] : 0.f) + bias);
         s_dl[r][pc] = dl;
         s_dx[r][pc] = dl * xv;
         if (OUT) {
