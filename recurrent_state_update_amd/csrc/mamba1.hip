@@ -8,7 +8,8 @@
 // One workgroup of 1024 threads covers a block of channels of one sequence
 // (with states of at most 32 bytes per channel, two channels per lane group).
 // Phase 1: one thread per channel shifts the conv window, convolves, applies
-// SiLU and softplus, and stages x_d and Delta_d in LDS with the row's B and C.
+// SiLU and softplus, and stages Delta_d, Delta_d x_d, D_d x_d and SiLU(z_d) in
+// LDS with the row's B and C.
 // Phase 2: a channel's N state values are split over N/VEC lanes, each with one
 // 16-byte non-temporal access (requested before phase 1, so the load overlaps
 // it); the lanes update their values, reduce h' C over the channel's lanes with
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
   constexpr int NPASS = m1_passes<TS, N>(); // passes: with small states a lane holds two channels'
                                             // values, so twice the bytes are in flight
   constexpr int CPW = CPP * NPASS;          // channels per workgroup
-  __shared__ float s_x[CPW], s_dl[CPW], s_B[N], s_C[N];
+  __shared__ float s_dl[CPW], s_dx[CPW], s_yx[CPW], s_g[CPW], s_B[N], s_C[N];
 
   const int b = blockIdx.y;
   const int d0 = blockIdx.x * CPW;
@@ -83,16 +84,20 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
       for (int k = 0; k < W - 1; ++k) wr[k] = wp[k];
       const TI ur = static_cast<const TI*>(a.x)[b * a.x_stride + dc];
       const TI dtr = static_cast<const TI*>(a.dt)[b * a.dt_stride + dc];
+      const TI zr = static_cast<const TI*>(a.z)[b * a.z_stride + dc];
       float wt[W];
 #pragma unroll
       for (int k = 0; k < W; ++k) wt[k] = a.conv_w[(int64_t)dc * W + k];
-      const float cb = a.conv_b[dc], dtb = a.dt_bias[dc];
+      const float cb = a.conv_b[dc], dtb = a.dt_bias[dc], dk = a.Dk[dc];
       const float u = to_f32(ur);
       float v = cb + wt[W - 1] * u;
 #pragma unroll
       for (int k = 0; k < W - 1; ++k) v += wt[k] * to_f32(wr[k]);
-      s_x[ci] = silu(v);
-      s_dl[ci] = softplus(to_f32(dtr) + dtb) * 1.4426950408889634f;   // Delta log2 e
+      const float x = silu(v), dl = softplus(to_f32(dtr) + dtb);
+      s_dl[ci] = dl * 1.4426950408889634f;   // Delta log2 e: the decay exponent per unit of A
+      s_dx[ci] = dl * x;                     // Delta x: the input's weight on B
+      s_yx[ci] = dk * x;                     // the skip term D x
+      s_g[ci] = silu(to_f32(zr));            // the gate
       // the window keeps raw inputs at the conv dtype: shift the stored words, append the input
 #pragma unroll
       for (int k = 0; k < W - 2; ++k) wp[k] = wr[k + 1];
@@ -118,8 +123,7 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
     const int cc = CPP * p + c, d = d0 + cc;
     float part = 0.f;
     if (d < D) {
-      const float x = s_x[cc], dl = s_dl[cc];   // dl: Delta log2 e
-      const float dx = dl * 0.6931471805599453f * x;
+      const float dl = s_dl[cc], dx = s_dx[cc];
       const float* Ar = a.A + (int64_t)d * N + n0;
       vec_t o;
 #pragma unroll
@@ -134,9 +138,7 @@ __global__ __launch_bounds__(kM1Threads) void mamba1_decode_kernel(Mamba1Params 
 #pragma unroll
     for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
     if (d < D && sub == 0) {
-      const float yv = part + a.Dk[d] * s_x[cc];
-      const float zv = load_any(a.z, b * a.z_stride + d, a.io_bf16);
-      store_any(a.y, b * a.y_stride + d, yv * silu(zv), a.y_bf16);
+      store_any(a.y, b * a.y_stride + d, (part + s_yx[cc]) * s_g[cc], a.y_bf16);
     }
   }
 }
