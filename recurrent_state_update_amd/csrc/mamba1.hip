@@ -349,6 +349,14 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
       }
     }
     if (r0 + TB < ch.len) fetch(r0 + TB, ch.len - r0 - TB < TB ? ch.len - r0 - TB : TB);
+    // the block's first checkpoint token: token t ends at absolute position p1 + t
+    const int64_t p1 = (int64_t)sq.start_pos + ch.tau0 + r0 + 1;
+    int tck = nb;   // none
+    if (OUT && a.ckpt_interval > 0) {
+      const int64_t rem = p1 % a.ckpt_interval;
+      const int64_t t0 = rem == 0 ? 0 : a.ckpt_interval - rem;
+      if (t0 < nb) tck = (int)t0;
+    }
     __syncthreads();
     for (int t = 0; t < nb; ++t) {
       const float dl = s_dl[t][rc], dx = s_dx[t][rc];
@@ -367,15 +375,13 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
         for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
         if (ron && sub == 0)
           store_any(a.y, (int64_t)(ch.t0 + r0 + t) * a.y_stride + rd, (part + s_dy[t][rc]) * s_sz[t][rc], a.y_bf16);
-        if (a.ckpt_interval > 0 && ron) {
-          const int64_t p = (int64_t)sq.start_pos + ch.tau0 + r0 + t + 1;
-          if (p % a.ckpt_interval == 0) {
-            const int64_t k = p / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
-            if (k >= 0 && k < sq.nck) {
-              const int slot = a.ck[sq.ck0 + k];
-              if (slot >= 0 && slot < a.num_slots) store_state(slot, r0 + t);
-            }
+        if (t == tck) {   // a checkpoint position (wave-uniform)
+          const int64_t k = (p1 + t) / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
+          if (ron && k >= 0 && k < sq.nck) {
+            const int slot = a.ck[sq.ck0 + k];
+            if (slot >= 0 && slot < a.num_slots) store_state(slot, r0 + t);
           }
+          tck = (int64_t)tck + a.ckpt_interval < nb ? tck + a.ckpt_interval : nb;
         }
       }
     }
