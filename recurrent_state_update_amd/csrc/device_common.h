@@ -99,5 +99,12 @@ __device__ __forceinline__ floatx4 mma(const Frag<SPLIT>& a, const Frag<SPLIT>& 
   }
   return mfma_bf16(a.hi, b.hi, acc);
 }
+// The same three products of hi/lo operands, the high-order one into `hi` and the two low-order
+// ones into `lo` (two independent accumulation chains; the caller adds them).
+__device__ __forceinline__ void mma_split2(const Frag<true>& a, const Frag<true>& b, floatx4& hi, floatx4& lo) {
+  lo = mfma_bf16(a.lo, b.hi, lo);
+  hi = mfma_bf16(a.hi, b.hi, hi);
+  lo = mfma_bf16(a.hi, b.lo, lo);
+}
 
 }  // namespace m2

@@ -980,12 +980,22 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         constexpr int NI = NK * PT;   // product i: K-step i / PT of row block i % PT
         Frag<SPLIT> hf[2];
         hf[0] = lds_frag<SPLIT>(sH, L::HPL, LDH, l16, 0, q);
+        // fp32-faithful planes: the two low-order products go to a second accumulator, so the
+        // dependent chain through each accumulator is half as long
+        floatx4 accl[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) accl[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           if (i + 1 < NI) hf[(i + 1) & 1] = lds_frag<SPLIT>(sH, L::HPL, LDH, ((i + 1) % PT) * 16 + l16, 32 * ((i + 1) / PT), q);
           __builtin_amdgcn_sched_barrier(0);
-          acc[i % PT] = mma<SPLIT>(hf[i & 1], cfr[t][i / PT], acc[i % PT]);
+          if constexpr (SPLIT) mma_split2(hf[i & 1], cfr[t][i / PT], acc[i % PT], accl[i % PT]);
+          else acc[i % PT] = mma<SPLIT>(hf[i & 1], cfr[t][i / PT], acc[i % PT]);
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SPLIT) {
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) acc[pt] += accl[pt];
         }
       }
       // the next operands, requested under this tile's products: tile 1's C columns and the state
@@ -1109,6 +1119,9 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     // every K-step, also past a short chunk's end: there the (w x) rows are zeros and the B^T
     // operand repeats the last K-step, so the products add nothing and no branch is needed
     Frag<SPLIT> wf[2][PT];   // the (w x) operands of K-step kb + 1 are read during K-step kb
+    floatx4 accSl[PT];       // fp32-faithful planes: the low-order products, added at the end
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) accSl[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) wf[0][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, pt * 16 + l16, 0, q);
 #pragma unroll
@@ -1120,13 +1133,21 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       __builtin_amdgcn_sched_barrier(0);
       if (st_on) {
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) accS[pt] = mma<SPLIT>(wf[kb & 1][pt], bt[kb], accS[pt]);
+        for (int pt = 0; pt < PT; ++pt) {
+          if constexpr (SPLIT) mma_split2(wf[kb & 1][pt], bt[kb], accS[pt], accSl[pt]);
+          else accS[pt] = mma<SPLIT>(wf[kb & 1][pt], bt[kb], accS[pt]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kb == 0) prefetch_raw(a, nx2);
       if (kb >= 1) load_op(a, kb - 1, cnext, nx);
       if (kb == 7) load_op(a, 7, cnext, nx), load_op(a, 8, cnext, nx), load_c(a, 0, cnext, nx);
       __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) accS[pt] += accSl[pt];
     }
 
     // ---- T, H. tables of chunk k+2; the state leaving this chunk for the next step's outputs
