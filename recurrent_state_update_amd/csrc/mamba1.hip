@@ -5,7 +5,7 @@
 // and state index exp(Delta_d A[d][n]), B and C shared by all channels, the
 // short conv over the D channels of x.
 //
-// One workgroup of 1024 threads covers a block of channels of one sequence
+// One workgroup of 512 threads covers a block of channels of one sequence
 // (with states of at most 32 bytes per channel, two channels per lane group).
 // Phase 1: one thread per channel shifts the conv window, convolves, applies
 // SiLU and softplus, and stages Delta_d, Delta_d x_d, D_d x_d and SiLU(z_d) in
@@ -20,7 +20,7 @@
 
 namespace m2 {
 
-constexpr int kM1Threads = 1024;
+constexpr int kM1Threads = 512;
 
 
 
