@@ -127,9 +127,9 @@ def test_varlen_prefill_with_seeds_and_checkpoints(ssm_dtype, Q):
     _check_varlen(c, ssm_dtype, Q)
 
 
-# (heads, head_dim, d_state, groups, conv kernel): the supported head_dim / d_state sizes, group
-# counts other than a power of two, and every conv width; the 128 x 128 shape does not fit the
-# per-group output kernel's LDS staging and takes the per-head kernel with single planes
+# (heads, head_dim, d_state, groups, conv kernel): the supported head_dim / d_state sizes (so both
+# walk part widths, 16 and 32 channels, and the d_state padding to 32), group counts other than a
+# power of two, and every conv width
 SHAPES = [(4, 16, 16, 1, 4), (4, 32, 64, 2, 3), (6, 64, 32, 3, 2), (4, 128, 128, 2, 4)]
 
 
