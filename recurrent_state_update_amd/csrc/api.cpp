@@ -596,9 +596,9 @@ m2_status mamba2_prefill_chunked(m2_pool* pool, int32_t layer, const m2_layer_pa
   p.conv_bf16 = pool->d.conv_dtype == M2_BF16;
   p.io_bf16 = io_dtype == M2_BF16;
   p.y_bf16 = y_dtype == M2_BF16;
-  // z and y in 4-element pieces: bases and row pitches aligned to 4 elements
-  p.zy_vec = (reinterpret_cast<uintptr_t>(z) % (4 * ies)) == 0 && (reinterpret_cast<uintptr_t>(y) % (4 * yes)) == 0 &&
-             z_stride % 4 == 0 && y_stride % 4 == 0;
+  // z and y in vector pieces of up to 8 elements: bases and row pitches aligned to 8 elements
+  p.zy_vec = (reinterpret_cast<uintptr_t>(z) % (8 * ies)) == 0 && (reinterpret_cast<uintptr_t>(y) % (8 * yes)) == 0 &&
+             z_stride % 8 == 0 && y_stride % 8 == 0;
   p.sh = sh;
   p.Q = chunk_size;
   p.QC = (int)L.QC;

@@ -27,7 +27,7 @@ struct PrefillParams {
   void* ssm;
   void* conv;
   int ssm_bf16, conv_bf16, io_bf16, y_bf16;
-  int zy_vec;          // z and y allow 4-element vector access (aligned bases and row pitches)
+  int zy_vec;          // z and y allow vector access of up to 8 elements (aligned bases and row pitches)
   LayerShape sh;
   int Q;               // chunk size (multiple of 16, at most 256)
   int QC;              // token capacity of a chunk's operand rows: Q rounded up to 32

@@ -565,6 +565,12 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   constexpr int NP = L::NP, NPL = L::NPL, NK = NP / 32, PT = PP / 16;
   constexpr int NT = N / 16;                     // state column tiles (one per wave)
   constexpr int LDX = L::LDX, LDH = L::LDH, XPL = L::XPL;
+  // The channel of the part (row of the planes and of the state) that MFMA row m of channel
+  // block pt stands for: with two blocks, rows 4q .. 4q+3 of blocks 0 and 1 (the accumulator
+  // values of lane group q) are channels 8q .. 8q+7, so a lane's outputs, gate inputs and state
+  // values are 8 adjacent channels (one 16-byte access for bf16).  Every operand read from the
+  // planes and the state rows uses the same map, so the products are unchanged.
+  auto chan = [](int pt, int m) { return PT == 2 ? 8 * (m >> 2) + 4 * pt + (m & 3) : 16 * pt + m; };
   extern __shared__ __align__(16) unsigned char wk_smem[];
   float* const sTap = reinterpret_cast<float*>(wk_smem + L::OFF_TAPS);
   float* const sBias = sTap + PP * 4;
@@ -617,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       accS[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (sq.has_init && st_on) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accS[pt][r] = to_f32(init[(pt * 16 + 4 * q + r) * N + wave * 16 + l16]);
+        for (int r = 0; r < 4; ++r) accS[pt][r] = to_f32(init[chan(pt, 4 * q + r) * N + wave * 16 + l16]);
       }
     }
   }
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         u16 hi, lo = 0;
         if (SPLIT) split2(accS[pt][r], hi, lo);
         else hi = bits_of(from_f32<bf16>(accS[pt][r]));
-        u16* d = hb + (pt * 16 + 4 * q + r) * LDH + wave * 16 + l16;
+        u16* d = hb + chan(pt, 4 * q + r) * LDH + wave * 16 + l16;
         d[0] = hi;
         if (SPLIT) d[L::HPL] = lo;
       }
@@ -791,9 +797,14 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       load_g(rv[t], rv[t] >> 1, gd[t]);
       const char* const zb = static_cast<const char*>(ap.z) + (int64_t)nc.t0 * ap.z_stride * ES;
       const uint32_t zrow = __umul24((uint32_t)(i < nc.len ? i : 0), zsb);
+      if constexpr (ZYV && IOBF && PT == 2) {   // channels 8q .. 8q+7: one 16-byte load (aligned: ZYV)
+        const u16x8 z8 = *reinterpret_cast<const u16x8*>(zb + (zrow + (uint32_t)((c0 + chan(0, 4 * q)) * ES)));
+        zr[t][0] = u16x4{z8[0], z8[1], z8[2], z8[3]};
+        zr[t][1] = u16x4{z8[4], z8[5], z8[6], z8[7]};
+      } else {
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const char* const zp = zb + (zrow + (uint32_t)((c0 + pt * 16 + 4 * q) * ES));
+        const char* const zp = zb + (zrow + (uint32_t)((c0 + chan(pt, 4 * q)) * ES));
         if constexpr (ZYV) {
           if constexpr (IOBF) zr[t][pt] = *reinterpret_cast<const u16x4*>(zp);
           else zr[t][pt] = *reinterpret_cast<const floatx4*>(zp);
@@ -804,6 +815,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
             else zr[t][pt][r] = reinterpret_cast<const float*>(zp)[r];
           }
         }
+      }
       }
     } else {
       // slot k: a below-diagonal block of tile 0 (k < m0) or of tile 1 (K-step 6 - k)
@@ -846,9 +858,17 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
     for (int t = 0; t < 2; ++t) {
       if (yrow[t] < 0) continue;
       const uint32_t yr = __umul24((uint32_t)yrow[t], ysb);
+      if (ZYV && PT == 2 && ap.y_bf16) {   // channels 8q .. 8q+7: one 16-byte store (aligned: ZYV)
+        u16x8 o;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) o[r] = bits_of(from_f32<bf16>(ys[t][r >> 2][r & 3]));
+        *reinterpret_cast<u16x8*>(ybase + (yr + (uint32_t)((c0 + chan(0, 4 * q)) * yes))) = o;
+        yrow[t] = -1;
+        continue;
+      }
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        char* const yp = ybase + (yr + (uint32_t)((c0 + pt * 16 + 4 * q) * yes));
+        char* const yp = ybase + (yr + (uint32_t)((c0 + chan(pt, 4 * q)) * yes));
         const floatx4 yv = ys[t][pt];
         if (ap.y_bf16) {
           u16x4 o;
@@ -979,7 +999,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       {
         constexpr int NI = NK * PT;   // product i: K-step i / PT of row block i % PT
         Frag<SPLIT> hf[2];
-        hf[0] = lds_frag<SPLIT>(sH, L::HPL, LDH, l16, 0, q);
+        hf[0] = lds_frag<SPLIT>(sH, L::HPL, LDH, chan(0, l16), 0, q);
         // fp32-faithful planes: the two low-order products go to a second accumulator, so the
         // dependent chain through each accumulator is half as long
         floatx4 accl[PT];
@@ -987,7 +1007,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         for (int pt = 0; pt < PT; ++pt) accl[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          if (i + 1 < NI) hf[(i + 1) & 1] = lds_frag<SPLIT>(sH, L::HPL, LDH, ((i + 1) % PT) * 16 + l16, 32 * ((i + 1) / PT), q);
+          if (i + 1 < NI) hf[(i + 1) & 1] = lds_frag<SPLIT>(sH, L::HPL, LDH, chan((i + 1) % PT, l16), 32 * ((i + 1) / PT), q);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (SPLIT) mma_split2(hf[i & 1], cfr[t][i / PT], acc[i % PT], accl[i % PT]);
           else acc[i % PT] = mma<SPLIT>(hf[i & 1], cfr[t][i / PT], acc[i % PT]);
@@ -1013,14 +1033,14 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         Frag<SPLIT> xf[2][PT];   // the (c x) operands of K-step k + 1 are read during K-step k
         if (MT[t] > 0) {
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt) xf[0][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, pt * 16 + l16, 0, q);
+          for (int pt = 0; pt < PT; ++pt) xf[0][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, chan(pt, l16), 0, q);
         }
 #pragma unroll
         for (int k = 0; k < MT[t]; ++k) {
           const int jk = 32 * k;
           if (k + 1 < MT[t]) {
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) xf[(k + 1) & 1][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, pt * 16 + l16, jk + 32, q);
+            for (int pt = 0; pt < PT; ++pt) xf[(k + 1) & 1][pt] = lds_frag<SPLIT>(sXC, XPL, LDX, chan(pt, l16), jk + 32, q);
           }
           __builtin_amdgcn_sched_barrier(0);
           const float aR = sA2[jk + 31];
@@ -1073,7 +1093,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         const Frag<SPLIT> mf = make_frag<SPLIT>(mv);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
-          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXT, XPL, LDX, pt * 16 + l16, jk, q), mf, acc[pt]);
+          acc[pt] = mma<SPLIT>(lds_frag<SPLIT>(sXT, XPL, LDX, chan(pt, l16), jk, q), mf, acc[pt]);
       }
       // the gate: lane holds channels c0 + 16 pt + 4q .. +3 of token i
       yrow[t] = i < len ? i : -1;
@@ -1123,12 +1143,12 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) accSl[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) wf[0][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, pt * 16 + l16, 0, q);
+    for (int pt = 0; pt < PT; ++pt) wf[0][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, chan(pt, l16), 0, q);
 #pragma unroll
     for (int kb = 0; kb < kMaxRowTiles / 2; ++kb) {
       if (kb + 1 < kMaxRowTiles / 2) {
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) wf[(kb + 1) & 1][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, pt * 16 + l16, 32 * kb + 32, q);
+        for (int pt = 0; pt < PT; ++pt) wf[(kb + 1) & 1][pt] = lds_frag<SPLIT>(sXW, XPL, LDX, chan(pt, l16), 32 * kb + 32, q);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (st_on) {
@@ -1163,7 +1183,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(pt * 16 + 4 * q + r) * N + wave * 16 + l16] = from_f32<TS>(accS[pt][r]);
+          for (int r = 0; r < 4; ++r) dst[chan(pt, 4 * q + r) * N + wave * 16 + l16] = from_f32<TS>(accS[pt][r]);
       }
       const int tau = ch.tau0 + len;
       for (int i = tid; i < W1 * PP; i += kThreads) {
@@ -1208,7 +1228,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) head_state[(pt * 16 + 4 * q + r) * N + wave * 16 + l16] = from_f32<TS>(accS[pt][r]);
+      for (int r = 0; r < 4; ++r) head_state[chan(pt, 4 * q + r) * N + wave * 16 + l16] = from_f32<TS>(accS[pt][r]);
   }
   {
     const int tau = sqr.len;
