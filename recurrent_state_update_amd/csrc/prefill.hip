@@ -734,17 +734,21 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
   };
 
   // ---- a chunk's token values (one token per thread) and its decay tables
-  float pd = 0.f, pa = 0.f, pr = 0.f;
+  // (waves 0-3 only: thread j holds token j; the tables are written by those threads)
+  float pd = 0.f, pa = 0.f;
   auto prefetch_tok = [&](const PrefillParams& ap, const ChunkEntry& nc) {
-    const int j = min(tid & 255, nc.len - 1);
-    const float* dAh = ap.dA + (int64_t)h * T + nc.t0;
-    pd = ap.delta[(int64_t)h * T + nc.t0 + j];
-    pa = dAh[j];
-    pr = dAh[min(j | 31, nc.len - 1)];
+    if (wave < 4) {
+      const int j = min(tid, nc.len - 1);
+      pd = ap.delta[(int64_t)h * T + nc.t0 + j];
+      pa = ap.dA[(int64_t)h * T + nc.t0 + j];
+    }
   };
   auto put_tables = [&](float* tb, const ChunkEntry& nc) {
     const float al = load_uniform(&a.dA[(int64_t)h * T + nc.t0 + nc.len - 1]);
     if (tid < 256) {
+      // a at the last token of the token's 32-token K-step (or of the chunk): lane j | 31 holds
+      // token min(j | 31, len - 1)
+      const float pr = __shfl(pa, lane | 31);
       const bool ok = tid < nc.len;
       tb[tid] = ok ? pa * kLog2e : -INFINITY;
       tb[256 + tid] = ok ? pa * kLog2e - __builtin_amdgcn_logf(pd) : 0.f;
