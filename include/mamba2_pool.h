@@ -361,10 +361,12 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
                              int64_t z_stride, const void* dt, int64_t dt_stride, int32_t io_dtype, void* y,
                              int64_t y_stride, int32_t y_dtype, void* stream);
 
-/* Workspace bytes mamba1_prefill needs (same arguments as
- * mamba2_prefill_workspace_size; max_ckpt is the width of the checkpoint table).
+/* Workspace bytes mamba1_prefill needs for num_seqs sequences of total_tokens
+ * rows (chunk_size as in mamba1_prefill; max_ckpt is the width of the
+ * checkpoint table).
  * Errors: M2_ERR_ARG (NULL, negative counts), M2_ERR_UNSUPPORTED (a Mamba2
- * pool, chunk_size outside 16..4096), M2_ERR_SHAPE (size overflow). */
+ * pool, chunk_size neither 0 nor in 16..4096, d_state outside {8, 16, 32, 64,
+ * 128, 256}), M2_ERR_SHAPE (size overflow). */
 m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
                                         int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes);
 
@@ -380,7 +382,12 @@ m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
  * (16-byte aligned with 16-byte multiple row strides), y [T][D].  The work
  * runs in chunks of chunk_size rows (16..4096): each chunk's end state from
  * zero, a pass through each sequence's chunks, then every chunk again from its
- * entering state.  workspace: at least mamba1_prefill_workspace_size(...)
+ * entering state (a sequence's last chunk runs once).  chunk_size 0 lets the
+ * library choose from the shapes alone (D, d_state, num_seqs, total rows):
+ * about total/num_seqs rows per chunk, so sequences stay whole, when the batch
+ * has at least 512 / ceil(D / (1024 / d_state)) sequences; else shorter
+ * chunks, enough for 1024 workgroups (chunk lengths change the fp32 rounding
+ * order only).  workspace: at least mamba1_prefill_workspace_size(...)
  * bytes, 256-byte aligned.  The launch tables travel in the arguments of small
  * upload launches (no allocation, no host-to-device copy, no host wait).
  * Errors: as mamba2_prefill_chunked (slot range, repeats and aliasing

@@ -876,14 +876,37 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
   return ok();
 }
 
+// Rows per chunk when the caller leaves the choice to the library (chunk_size 0).  A chunk costs
+// its rows once more in launch (1) unless it is its sequence's last, so sequences stay whole
+// (about total/num_seqs rows per chunk, which also splits the longest ones of a ragged batch) as
+// long as they give the chunk kernels kM1MinWgs workgroups; fewer sequences are cut into chunks
+// until the chunks give kM1FillWgs.  Workgroups per chunk: ceil(D / channels per workgroup), 256
+// threads over channels of N/4 lanes.  The rule depends on the shapes only, not on the device, so
+// a batch is chunked (and rounded) the same way everywhere.
+constexpr int64_t kM1MinWgs = 512, kM1FillWgs = 1024;
+int64_t m1_auto_chunk(const m2::LayerShape& sh, int64_t num_seqs, int64_t total_tokens) {
+  const int64_t cpw = 256 / (sh.N / 4);
+  const int64_t wgs = (sh.H + cpw - 1) / cpw;
+  int64_t chunks = num_seqs;
+  if (num_seqs * wgs < kM1MinWgs) chunks = (kM1FillWgs + wgs - 1) / wgs;
+  if (chunks < 1) chunks = 1;
+  int64_t q = (total_tokens + chunks - 1) / chunks;
+  q = (q + 15) / 16 * 16;
+  return q < 16 ? 16 : q;
+}
+
 m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, int32_t total_tokens,
                                         int32_t chunk_size, int32_t max_ckpt, uint64_t* bytes) {
   if (!pool || !bytes) return fail(M2_ERR_ARG, "NULL argument");
   if (m2_status st = require_family(pool, M2_FAMILY_MAMBA1, "mamba1_prefill_workspace_size")) return st;
   if (num_seqs < 0 || total_tokens < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative count");
-  if (chunk_size < 16 || chunk_size > 4096) return fail(M2_ERR_UNSUPPORTED, "chunk_size must be in [16, 4096]");
+  if (chunk_size != 0 && (chunk_size < 16 || chunk_size > 4096))
+    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be 0 or in [16, 4096]");
+  if (!m2::mamba1_supported(pool->sh.N, pool->sh.W))
+    return fail(M2_ERR_UNSUPPORTED, "Mamba1 prefill supports d_state in {8,16,32,64,128,256}, got %d", pool->sh.N);
+  const int64_t q = chunk_size ? chunk_size : m1_auto_chunk(pool->sh, num_seqs, total_tokens);
   M1Layout L;
-  if (!m1_layout(pool->sh, num_seqs, (int64_t)total_tokens / chunk_size + num_seqs, (int64_t)num_seqs * max_ckpt, &L))
+  if (!m1_layout(pool->sh, num_seqs, (int64_t)total_tokens / q + num_seqs, (int64_t)num_seqs * max_ckpt, &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();
@@ -903,7 +926,8 @@ m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* pa
   if (num_seqs < 0) return fail(M2_ERR_ARG, "num_seqs is negative");
   if (m2_status st = check_params(pool, params)) return st;
   if (!dtype_ok(io_dtype) || !dtype_ok(y_dtype)) return fail(M2_ERR_DTYPE, "io/y dtype must be F32 or BF16");
-  if (chunk_size < 16 || chunk_size > 4096) return fail(M2_ERR_UNSUPPORTED, "chunk_size must be in [16, 4096]");
+  if (chunk_size != 0 && (chunk_size < 16 || chunk_size > 4096))
+    return fail(M2_ERR_UNSUPPORTED, "chunk_size must be 0 or in [16, 4096]");
   if (ckpt_interval < 0 || max_ckpt < 0) return fail(M2_ERR_ARG, "negative checkpoint interval or count");
   if (num_seqs == 0) return ok();
   if (!cu_seqlens || !slots || !has_init) return fail(M2_ERR_ARG, "cu_seqlens, slots and has_initial_state are required");
@@ -940,15 +964,16 @@ m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* pa
   if (m2_status st = check_io(io, 6)) return st;
   if (!m2::mamba1_supported(sh.N, sh.W))
     return fail(M2_ERR_UNSUPPORTED, "Mamba1 prefill supports d_state in {8,16,32,64,128,256}, got %d", sh.N);
-  // tables: chunks of chunk_size rows from each sequence's first row
+  // tables: chunks of q rows from each sequence's first row
+  const int64_t q = chunk_size ? chunk_size : m1_auto_chunk(sh, num_seqs, T);
   std::vector<m2::M1Seq> seqs(num_seqs);
   std::vector<m2::M1Chunk> chunks;
   for (int s = 0; s < num_seqs; ++s) {
     const int t0 = cu_seqlens[s], len = cu_seqlens[s + 1] - t0;
     seqs[s] = m2::M1Seq{t0, len, slots[s], has_init[s] ? 1 : 0, start_pos ? start_pos[s] : 0,
                         s * (ckpt_on ? max_ckpt : 0), ckpt_on ? max_ckpt : 0, (int32_t)chunks.size()};
-    for (int c0 = 0; c0 < len; c0 += chunk_size)
-      chunks.push_back(m2::M1Chunk{s, t0 + c0, len - c0 < chunk_size ? len - c0 : chunk_size, c0});
+    for (int64_t c0 = 0; c0 < len; c0 += q)
+      chunks.push_back(m2::M1Chunk{s, t0 + (int)c0, (int)(len - c0 < q ? len - c0 : q), (int)c0});
   }
   if (chunks.size() > 65535 || num_seqs > 65535)
     return fail(M2_ERR_UNSUPPORTED, "%zu chunks and %d sequences: at most 65535 of each (raise chunk_size)",

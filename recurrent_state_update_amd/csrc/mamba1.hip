@@ -187,32 +187,64 @@ hipError_t launch_mamba1_decode(const Mamba1Params& p, int N, int W, int batch, 
 // (2) per (sequence, channel, state index) the pass through the sequence's chunks,
 // h <- exp(A sum Delta) h + S_c, writing the state entering each chunk; (3) every chunk again
 // from its entering state, with the outputs, the checkpoint states at their tokens and the final
-// state.  Launches (1) and (3) take a 256-thread workgroup per (chunk, block of channels) and walk
-// the chunk in blocks of TB tokens: the raw rows of the block are loaded cooperatively (the next
-// block's requested while the current one runs), each (token, channel) gets its conv, Delta,
-// Delta x, D x and silu(z) once, into LDS, and then the recurrence runs with a channel's state
-// values spread over N/8 lanes in fp32 registers, h C reduced with xor shuffles.
+// state.  With one chunk per sequence only launch (3) has work.  Launches (1) and (3) take a
+// 256-thread workgroup per (chunk, block of channels) and walk the chunk in blocks of 16 rows:
+// the raw rows of the block are loaded cooperatively (the next block's requested while the
+// current one runs), each (row, channel) gets its conv, Delta, Delta x, D x and silu(z) once,
+// into LDS, and then the recurrence runs with a channel's state values spread over N/4 lanes in
+// fp32 registers.  Rows go in groups of four: each lane keeps one partial h C per row, and the
+// channel's lanes share out the four sums (a reduce-scatter over the lane quad), so every lane
+// finishes one row's output.
 namespace m2 {
 
-constexpr int kM1PV = 8;   // state values per lane
-
-constexpr int kM1Ring = 16;   // rows of the raw-x ring: a token block and the W-1 rows before it
-template <int N, int W> constexpr int m1_tb() { return N / kM1PV == 1 ? 8 : kM1Ring - (W - 1); }
+constexpr int kM1PV = 4;      // state values per lane
+constexpr int kM1G = 4;       // rows per output group
+constexpr int kM1TB = 16;     // rows per staged block (a multiple of kM1G)
+constexpr int kM1Ring = 32;   // rows of the raw-x ring: a block and the W-1 rows before it
 
 template <typename TI> __device__ __forceinline__ float m1_ld(const void* p, int64_t i) {
   return to_f32(static_cast<const TI*>(p)[i]);
 }
 
+// v of the lane whose index differs in bit 0 (bit 1): DPP quad permutes
+__device__ __forceinline__ float m1_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float m1_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Sums of the four row partials p[0..3] over a channel's LPC lanes.  LPC >= 4: on return s0 of
+// lane `sub` is the sum of row (sub & 3), complete in every lane quad.  LPC == 2: s0 is the sum of
+// row (sub & 1) and s1 that of row 2 + (sub & 1).
+template <int LPC> __device__ __forceinline__ void m1_group_sums(const float (&p)[kM1G], int sub, float& s0, float& s1) {
+  const bool b0 = sub & 1;
+  if constexpr (LPC == 2) {
+    s0 = (b0 ? p[1] : p[0]) + m1_xor1(b0 ? p[0] : p[1]);
+    s1 = (b0 ? p[3] : p[2]) + m1_xor1(b0 ? p[2] : p[3]);
+  } else {
+    const bool b1 = sub & 2;
+    const float q0 = (b1 ? p[2] : p[0]) + m1_xor2(b1 ? p[0] : p[2]);   // row 2 b1
+    const float q1 = (b1 ? p[3] : p[1]) + m1_xor2(b1 ? p[1] : p[3]);   // row 2 b1 + 1
+    float r = (b0 ? q1 : q0) + m1_xor1(b0 ? q0 : q1);
+    if constexpr (LPC >= 8) r += __shfl_xor(r, 4);
+    if constexpr (LPC >= 16) r += __shfl_xor(r, 8);
+    if constexpr (LPC >= 32) r += __shfl_xor(r, 16);
+    if constexpr (LPC >= 64) r += __shfl_xor(r, 32);
+    s0 = r;
+    s1 = 0.f;
+  }
+}
+
 // OUT = false: launch (1); OUT = true: launch (3).  TI: the dtype of the x, z, dt, B, C rows.
 template <typename TS, typename TI, bool OUT, int N, int W>
 __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a) {
-  constexpr int LPC = N / kM1PV;             // recurrence lanes per channel
+  constexpr int PV = kM1PV, G = kM1G, TB = kM1TB, R = kM1Ring;
+  constexpr int LPC = N / PV;                // recurrence lanes per channel
   constexpr int CPW = 256 / LPC;             // channels per workgroup
-  constexpr int TB = m1_tb<N, W>();          // tokens per block
-  constexpr int R = kM1Ring;
-  static_assert(TB + W - 1 <= R, "ring too short");
+  static_assert(LPC >= 2 && TB % G == 0 && TB + W - 1 <= R, "block shape");
   constexpr int RS = 256 / CPW;              // staging: row step of one thread
-  constexpr int PP = (TB + RS - 1) / RS;     // staging: (token, channel) pairs per thread
+  constexpr int PP = (TB + RS - 1) / RS;     // staging: (row, channel) pairs per thread
   constexpr int BPT = (TB * N + 255) / 256;  // staging: B (and C) values per thread
   constexpr int NO = OUT ? TB : 1;
   __shared__ float xs[R][CPW];
@@ -228,8 +260,10 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
   if (!OUT && last) return;
   const int tid = threadIdx.x, D = a.D, d0 = blockIdx.x * CPW;
 
-  // staging role: channel pc, rows pr0, pr0 + RS, ...
-  const int pc = tid % CPW, pr0 = tid / CPW;
+  // staging role: channel pc, rows pr0, pr0 + RS, ... (pr0 is the wave's index when a wave
+  // covers whole rows)
+  const int pc = tid % CPW;
+  const int pr0 = CPW % 64 == 0 ? __builtin_amdgcn_readfirstlane(tid / CPW) : tid / CPW;
   const int pd = d0 + pc;
   const bool pon = pd < D;
   const int pdd = pon ? pd : 0;
@@ -257,29 +291,32 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
     }
   }
 
-  // recurrence role: channel rc, state values n0 .. n0+7
+  // recurrence role: channel rc, state values n0 .. n0+PV-1
   const int rc = tid / LPC, sub = tid % LPC;
   const int rd = d0 + rc;
   const bool ron = rd < D;
   const int rdd = ron ? rd : 0;
-  const int n0 = sub * kM1PV;
+  const int n0 = sub * PV;
   const float kLog2e = 1.4426950408889634f;
-  float A2[kM1PV], h[kM1PV];
+  float A2[PV], h[PV];
 #pragma unroll
-  for (int e = 0; e < kM1PV; ++e) A2[e] = a.A[(int64_t)rdd * N + n0 + e] * kLog2e;
+  for (int e = 0; e < PV; ++e) A2[e] = a.A[(int64_t)rdd * N + n0 + e] * kLog2e;
   if (OUT) {
     const float* hin = a.Hin + ((int64_t)ci * D + rdd) * N + n0;
 #pragma unroll
-    for (int e = 0; e < kM1PV; ++e) h[e] = hin[e];
+    for (int e = 0; e < PV; ++e) h[e] = hin[e];
+    // settle these loads here: left in flight they would make the row loop wait for every
+    // memory access before each row
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   } else {
 #pragma unroll
-    for (int e = 0; e < kM1PV; ++e) h[e] = 0.f;
+    for (int e = 0; e < PV; ++e) h[e] = 0.f;
   }
-  // state and window after chunk token q (the window's raw rows are in the ring)
+  // state and window after chunk row q (the window's raw rows are in the ring)
   auto store_state = [&](int slot, int q) {
     TS* st = static_cast<TS*>(a.ssm) + ((int64_t)slot * D + rd) * N + n0;
 #pragma unroll
-    for (int e = 0; e < kM1PV; ++e) st[e] = from_f32<TS>(h[e]);
+    for (int e = 0; e < PV; ++e) st[e] = from_f32<TS>(h[e]);
     if (sub == 0) {
 #pragma unroll
       for (int k = 0; k < W - 1; ++k)
@@ -294,9 +331,9 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
       const int r = pr0 + m * RS;
       if (r < nb && pon) {
         const int64_t row = ch.t0 + r0 + r;
-        px[m] = m1_ld<TI>(a.x, row * a.x_stride + pd);
-        pdt[m] = m1_ld<TI>(a.dt, row * a.dt_stride + pd);
-        if (OUT) pz[m] = m1_ld<TI>(a.z, row * a.z_stride + pd);
+        px[m] = m1_ld<TI>(static_cast<const TI*>(a.x) + row * a.x_stride, (uint32_t)pd);
+        pdt[m] = m1_ld<TI>(static_cast<const TI*>(a.dt) + row * a.dt_stride, (uint32_t)pd);
+        if (OUT) pz[m] = m1_ld<TI>(static_cast<const TI*>(a.z) + row * a.z_stride, (uint32_t)pd);
       }
     }
 #pragma unroll
@@ -314,6 +351,8 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
   fetch(0, ch.len < TB ? ch.len : TB);
   for (int r0 = 0; r0 < ch.len; r0 += TB) {
     const int nb = ch.len - r0 < TB ? ch.len - r0 : TB;
+    const int ng = (nb + G - 1) / G * G;   // rows walked: the last group is padded with rows
+                                           // that leave the state as it is (Delta = 0, B = 0)
     // stage the block's raw rows (rows past nb are left alone: the ring still holds older rows
     // that the final window may need)
 #pragma unroll
@@ -324,13 +363,13 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
 #pragma unroll
     for (int m = 0; m < BPT; ++m) {
       const int i = tid + 256 * m, r = i / N;
-      if (r < nb) {
-        s_B[r][i % N] = pB[m];
-        if (OUT) s_C[r][i % N] = pC[m];
+      if (r < ng) {
+        s_B[r][i % N] = r < nb ? pB[m] : 0.f;
+        if (OUT) s_C[r][i % N] = r < nb ? pC[m] : 0.f;
       }
     }
     __syncthreads();
-    // per (token, channel): conv over the ring, Delta, Delta x, D x, silu(z)
+    // per (row, channel): conv over the ring, Delta, Delta x, D x, silu(z)
 #pragma unroll
     for (int m = 0; m < PP; ++m) {
       const int r = pr0 + m * RS;
@@ -346,42 +385,61 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
           s_dy[r][pc] = Dd * xv;
           s_sz[r][pc] = silu(pon ? pz[m] : 0.f);
         }
+      } else if (r < ng) {
+        s_dl[r][pc] = 0.f;
+        s_dx[r][pc] = 0.f;
       }
     }
     if (r0 + TB < ch.len) fetch(r0 + TB, ch.len - r0 - TB < TB ? ch.len - r0 - TB : TB);
-    // the block's first checkpoint token: token t ends at absolute position p1 + t
+    // the block's first checkpoint row: row t ends at absolute position p1 + t
     const int64_t p1 = (int64_t)sq.start_pos + ch.tau0 + r0 + 1;
-    int tck = nb;   // none
+    int tck = TB;   // none
     if (OUT && a.ckpt_interval > 0) {
       const int64_t rem = p1 % a.ckpt_interval;
       const int64_t t0 = rem == 0 ? 0 : a.ckpt_interval - rem;
       if (t0 < nb) tck = (int)t0;
     }
     __syncthreads();
-    for (int t = 0; t < nb; ++t) {
-      const float dl = s_dl[t][rc], dx = s_dx[t][rc];
-      float Bv[kM1PV];
+    for (int t = 0; t < ng; t += G) {
+      float part[G];
 #pragma unroll
-      for (int e = 0; e < kM1PV; ++e) Bv[e] = s_B[t][n0 + e];
+      for (int g = 0; g < G; ++g) {
+        const float dl = s_dl[t + g][rc], dx = s_dx[t + g][rc];
+        float Bv[PV];
 #pragma unroll
-      for (int e = 0; e < kM1PV; ++e) h[e] = __builtin_amdgcn_exp2f(dl * A2[e]) * h[e] + dx * Bv[e];
-      if (!OUT) {
-        sumd += dl;
-      } else {
-        float part = 0.f;
+        for (int e = 0; e < PV; ++e) Bv[e] = s_B[t + g][n0 + e];
 #pragma unroll
-        for (int e = 0; e < kM1PV; ++e) part += h[e] * s_C[t][n0 + e];
+        for (int e = 0; e < PV; ++e) h[e] = __builtin_amdgcn_exp2f(dl * A2[e]) * h[e] + dx * Bv[e];
+        if (!OUT) {
+          sumd += dl;
+        } else {
+          part[g] = 0.f;
 #pragma unroll
-        for (int m = LPC / 2; m >= 1; m /= 2) part += __shfl_xor(part, m);
-        if (ron && sub == 0)
-          store_any(a.y, (int64_t)(ch.t0 + r0 + t) * a.y_stride + rd, (part + s_dy[t][rc]) * s_sz[t][rc], a.y_bf16);
-        if (t == tck) {   // a checkpoint position (wave-uniform)
-          const int64_t k = (p1 + t) / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
-          if (ron && k >= 0 && k < sq.nck) {
-            const int slot = a.ck[sq.ck0 + k];
-            if (slot >= 0 && slot < a.num_slots) store_state(slot, r0 + t);
+          for (int e = 0; e < PV; ++e) part[g] += h[e] * s_C[t + g][n0 + e];
+          if (t + g == tck) {   // a checkpoint row (wave-uniform)
+            const int64_t k = (p1 + t + g) / a.ckpt_interval - sq.start_pos / a.ckpt_interval - 1;
+            if (ron && k >= 0 && k < sq.nck) {
+              const int slot = a.ck[sq.ck0 + k];
+              if (slot >= 0 && slot < a.num_slots) store_state(slot, r0 + t + g);
+            }
+            tck = (int64_t)tck + a.ckpt_interval < nb ? tck + a.ckpt_interval : TB;
           }
-          tck = (int64_t)tck + a.ckpt_interval < nb ? tck + a.ckpt_interval : nb;
+        }
+      }
+      if (OUT) {
+        float s0, s1;
+        m1_group_sums<LPC>(part, sub, s0, s1);
+        // y of row t + tr: the lane's share of the group's outputs
+        auto put = [&](int tr, float sum) {
+          if (ron && tr < nb)
+            store_any(a.y, (int64_t)(ch.t0 + r0 + tr) * a.y_stride + rd, (sum + s_dy[tr][rc]) * s_sz[tr][rc],
+                      a.y_bf16);
+        };
+        if constexpr (LPC == 2) {
+          put(t + sub, s0);
+          put(t + 2 + sub, s1);
+        } else {
+          if (sub < 4) put(t + sub, s0);
         }
       }
     }
@@ -393,7 +451,7 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
   } else {
     float* s = a.S + ((int64_t)ci * D + rd) * N + n0;
 #pragma unroll
-    for (int e = 0; e < kM1PV; ++e) s[e] = h[e];
+    for (int e = 0; e < PV; ++e) s[e] = h[e];
     if (sub == 0) a.SD[(int64_t)ci * D + rd] = sumd;
   }
 }

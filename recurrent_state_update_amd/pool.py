@@ -136,7 +136,7 @@ class Pool:
                                        _dtype_code(y), _stream()))
         return y
 
-    def mamba1_workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int = 256,
+    def mamba1_workspace_size(self, num_seqs: int, total_tokens: int, chunk_size: int = 0,
                               max_ckpt: int = 0) -> int:
         n = c_uint64()
         check(lib().mamba1_prefill_workspace_size(self._h, num_seqs, total_tokens, chunk_size, max_ckpt,
@@ -144,10 +144,11 @@ class Pool:
         return n.value
 
     def mamba1_prefill(self, layer: int, w: LayerWeights, cu_seqlens, slots, has_init, x, B, C, z, dt, y,
-                       start_pos=None, chunk_size: int = 256, ckpt_interval: int = 0, ckpt_slots=None,
+                       start_pos=None, chunk_size: int = 0, ckpt_interval: int = 0, ckpt_slots=None,
                        workspace: torch.Tensor | None = None):
         """Mamba1 prefill of packed sequences (rows x, z, dt of D; B, C of N); cu_seqlens, slots,
-        has_init, start_pos and ckpt_slots [num_seqs][max_ckpt] are host arrays."""
+        has_init, start_pos and ckpt_slots [num_seqs][max_ckpt] are host arrays; chunk_size 0 lets
+        the library choose the chunking."""
         cu, _ = _host_i32(cu_seqlens)
         sl, sl_p = _host_i32(slots)
         hi = np.ascontiguousarray(np.asarray(has_init, dtype=np.uint8))

@@ -425,6 +425,12 @@ def test_mamba1_prefill_validation():
     assert n1.value - n0.value >= (1000 // 32 - 100 // 32) * 2 * D * N * 4
     assert n2.value >= n1.value and n0.value % 256 == 0
     assert lib().mamba1_prefill_workspace_size(h, 2, 100, 8, 0, byref(n0)) == UNSUP
+    # chunk_size 0: the library chooses; at D 64 two sequences give 2 workgroups per chunk, far
+    # from filling the GPU, so the rows are cut into 16-row chunks
+    n3, n4 = c_uint64(), c_uint64()
+    assert lib().mamba1_prefill_workspace_size(h, 2, 100, 0, 0, byref(n3)) == 0
+    assert lib().mamba1_prefill_workspace_size(h, 2, 100, 16, 0, byref(n4)) == 0
+    assert n3.value == n4.value
     wsize(h, [0, 50, 100], chunk=64, expect=UNSUP)
 
     def call(hh=None, **kw):
@@ -445,6 +451,8 @@ def test_mamba1_prefill_validation():
     assert call(cu=[0, 0, 0]) == 0                        # no rows: nothing to do
     assert call(layer=1) == ARG
     assert call(chunk=8) == UNSUP
+    assert call(chunk=4097) == UNSUP
+    assert call(chunk=0) == WS                            # the library's choice is valid
     assert call(slots=[0, 0]) == SLOT
     assert call(slots=[0, 6]) == SLOT
     assert call(cu=[0, 50, 40]) == SHAPE

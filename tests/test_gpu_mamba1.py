@@ -251,6 +251,33 @@ def test_mamba1_prefill_at_the_7b_width():
         assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
 
 
+@pytest.mark.parametrize("lens", [[1024, 1024, 1024, 1024, 700, 1, 1300, 45], [2000, 1]])
+def test_mamba1_prefill_with_the_library_chunking(lens):
+    """chunk_size 0 at D = 8192, N = 16, bf16: eight sequences (128 workgroups each: chunks of
+    about total/8 = 768 rows, so the longer sequences are cut in two) and two (cut into 256-row
+    chunks to fill the GPU), seeded and zero starts, checkpoints every 300 positions, against the
+    oracle."""
+    D, N, W = synth.MAMBA1_D, synth.MAMBA1_N, synth.MAMBA1_W
+    ns = len(lens)
+    ck = np.full((ns, 7), -1, np.int32)
+    ck[0, :3] = [8, 9, 10]
+    if ns > 2:
+        ck[6, :1] = [11]
+    log(f"case: Mamba1 prefill D={D} N={N}, library chunking, lens {lens}")
+    has = [1, 0] * (ns // 2)
+    sp = np.array([0, 10] * (ns // 2), np.int32)
+    pool, ref, y, y_ref, _, _ = _m1_prefill_case(D, N, W, "bf16", 0, lens, has, sp, 300, ck, 975 + ns, L=1,
+                                                 S=12, layer=0, slots=list(range(ns)))
+    err = rel_err(y, y_ref)
+    log(f"max rel y error: {err:.3e}")
+    assert err <= TOL["bf16"]
+    for s in list(range(ns)) + [8, 9, 10, 11]:
+        if s >= 8 and not (ck == s).any():
+            continue
+        assert rel_err(host(pool.ssm[0, s, :, 0]), ref.ssm[0, s]) <= TOL["bf16"], s
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+
+
 def test_mamba1_prefill_at_the_largest_chunk_size():
     """chunk_size 4096 (the upper bound): a 5000-row sequence (two chunks, the second partial) and a
     4096-row one (one full chunk), seeded, with checkpoints every 1000 positions, against the oracle."""
