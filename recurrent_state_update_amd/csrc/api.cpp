@@ -1025,6 +1025,9 @@ m2_status mamba1_prefill(m2_pool* pool, int32_t layer, const m2_layer_params* pa
   p.num_seqs = num_seqs;
   p.num_chunks = (int)chunks.size();
   p.ckpt_interval = ckpt_on ? ckpt_interval : 0;
+  int nonempty = 0;
+  for (int s = 0; s < num_seqs; ++s) nonempty += seqs[s].len > 0;
+  p.whole_seqs = (int)chunks.size() == nonempty;
   p.seqs = reinterpret_cast<const m2::M1Seq*>(ws);
   p.chunks = reinterpret_cast<const m2::M1Chunk*>(ws + L.off_chunks);
   p.ck = reinterpret_cast<const int32_t*>(ws + L.off_ck);

@@ -59,6 +59,7 @@ struct Mamba1PrefillParams {
   const float* conv_w;
   const float* conv_b;
   int num_seqs, num_chunks, ckpt_interval;
+  int whole_seqs;           // every chunk is a whole sequence: launches (1) and (2) are skipped
   const M1Seq* seqs;        // workspace tables
   const M1Chunk* chunks;
   const int32_t* ck;        // checkpoint slots, sequence s at ck[seqs[s].ck0 ...]

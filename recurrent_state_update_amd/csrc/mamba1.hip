@@ -187,7 +187,8 @@ hipError_t launch_mamba1_decode(const Mamba1Params& p, int N, int W, int batch, 
 // (2) per (sequence, channel, state index) the pass through the sequence's chunks,
 // h <- exp(A sum Delta) h + S_c, writing the state entering each chunk; (3) every chunk again
 // from its entering state, with the outputs, the checkpoint states at their tokens and the final
-// state.  With one chunk per sequence only launch (3) has work.  Launches (1) and (3) take a
+// state.  With one chunk per sequence only launch (3) runs, from the slots' states.  Launches
+// (1) and (3) take a
 // 256-thread workgroup per (chunk, block of channels) and walk the chunk in blocks of 16 rows:
 // the raw rows of the block are loaded cooperatively (the next block's requested while the
 // current one runs), each (row, channel) gets its conv, Delta, Delta x, D x and silu(z) once,
@@ -302,9 +303,15 @@ __global__ __launch_bounds__(256) void mamba1_chunk_kernel(Mamba1PrefillParams a
 #pragma unroll
   for (int e = 0; e < PV; ++e) A2[e] = a.A[(int64_t)rdd * N + n0 + e] * kLog2e;
   if (OUT) {
-    const float* hin = a.Hin + ((int64_t)ci * D + rdd) * N + n0;
+    if (first && last) {   // a whole sequence: its slot is read and written by this lane alone
+      const TS* st = static_cast<const TS*>(a.ssm) + ((int64_t)sq.slot * D + rdd) * N + n0;
 #pragma unroll
-    for (int e = 0; e < PV; ++e) h[e] = hin[e];
+      for (int e = 0; e < PV; ++e) h[e] = sq.has_init ? to_f32(st[e]) : 0.f;
+    } else {
+      const float* hin = a.Hin + ((int64_t)ci * D + rdd) * N + n0;
+#pragma unroll
+      for (int e = 0; e < PV; ++e) h[e] = hin[e];
+    }
     // settle these loads here: left in flight they would make the row loop wait for every
     // memory access before each row
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -479,8 +486,10 @@ static hipError_t launch_m1p_n(const Mamba1PrefillParams& a, int W, hipStream_t 
   constexpr int CPW = 256 / (N / kM1PV);
   const dim3 gc((a.D + CPW - 1) / CPW, a.num_chunks), gp((unsigned)(((int64_t)a.D * N + 255) / 256), a.num_seqs);
 #define M1P_W(WW)                                                                               \
-  hipLaunchKernelGGL((mamba1_chunk_kernel<TS, TI, false, N, WW>), gc, dim3(256), 0, s, a);          \
-  hipLaunchKernelGGL((mamba1_pass_kernel<TS>), gp, dim3(256), 0, s, a, N);                      \
+  if (!a.whole_seqs) {                                                                          \
+    hipLaunchKernelGGL((mamba1_chunk_kernel<TS, TI, false, N, WW>), gc, dim3(256), 0, s, a);        \
+    hipLaunchKernelGGL((mamba1_pass_kernel<TS>), gp, dim3(256), 0, s, a, N);                    \
+  }                                                                                             \
   hipLaunchKernelGGL((mamba1_chunk_kernel<TS, TI, true, N, WW>), gc, dim3(256), 0, s, a);
   switch (W) {
     case 2: M1P_W(2) break;
