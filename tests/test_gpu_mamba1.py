@@ -278,6 +278,26 @@ def test_mamba1_prefill_with_the_library_chunking(lens):
         assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
 
 
+@pytest.mark.parametrize("Q", [0, 16])
+def test_mamba1_prefill_checkpoint_at_every_row(Q):
+    """Checkpoint interval 1: a state after every row, so checkpoints fall on every position of the
+    kernel's 4-row groups and on the last real row before a padded group (lengths 5 and 11, start
+    positions 0 and 2, fp32 state, one sequence seeded): every checkpoint state against the oracle,
+    every window bit for bit."""
+    D, N, W = 64, 16, 4
+    lens = [5, 11]
+    ck = np.full((2, 11), -1, np.int32)
+    ck[0, :5] = np.arange(2, 7)
+    ck[1, :11] = np.arange(7, 18)
+    log(f"case: Mamba1 prefill Q={Q}, checkpoint every row, lens {lens}")
+    pool, ref, y, y_ref, _, _ = _m1_prefill_case(D, N, W, "f32", Q, lens, [1, 0], np.array([0, 2], np.int32), 1,
+                                                 ck, 996, L=1, S=18, layer=0, slots=[0, 1])
+    assert rel_err(y, y_ref) <= TOL["f32"]
+    for s in range(18):
+        assert rel_err(host(pool.ssm[0, s, :, 0]), ref.ssm[0, s]) <= TOL["f32"], s
+        assert np.array_equal(host(pool.conv[0, s]), ref.conv[0, s]), s
+
+
 def test_mamba1_prefill_at_the_largest_chunk_size():
     """chunk_size 4096 (the upper bound): a 5000-row sequence (two chunks, the second partial) and a
     4096-row one (one full chunk), seeded, with checkpoints every 1000 positions, against the oracle."""
