@@ -363,7 +363,8 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
 
 /* Workspace bytes mamba1_prefill needs for num_seqs sequences of total_tokens
  * rows (chunk_size as in mamba1_prefill; max_ckpt is the width of the
- * checkpoint table).
+ * checkpoint table).  The size also serves any call with the same num_seqs,
+ * chunk_size and max_ckpt and at most total_tokens rows.
  * Errors: M2_ERR_ARG (NULL, negative counts), M2_ERR_UNSUPPORTED (a Mamba2
  * pool, chunk_size neither 0 nor in 16..4096, d_state outside {8, 16, 32, 64,
  * 128, 256}), M2_ERR_SHAPE (size overflow). */

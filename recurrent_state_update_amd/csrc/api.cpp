@@ -884,12 +884,14 @@ m2_status mamba1_decode_step(m2_pool* pool, int32_t layer, const m2_layer_params
 // threads over channels of N/4 lanes.  The rule depends on the shapes only, not on the device, so
 // a batch is chunked (and rounded) the same way everywhere.
 constexpr int64_t kM1MinWgs = 512, kM1FillWgs = 1024;
-int64_t m1_auto_chunk(const m2::LayerShape& sh, int64_t num_seqs, int64_t total_tokens) {
+int64_t m1_auto_target(const m2::LayerShape& sh, int64_t num_seqs) {   // chunks aimed at
   const int64_t cpw = 256 / (sh.N / 4);
   const int64_t wgs = (sh.H + cpw - 1) / cpw;
-  int64_t chunks = num_seqs;
-  if (num_seqs * wgs < kM1MinWgs) chunks = (kM1FillWgs + wgs - 1) / wgs;
-  if (chunks < 1) chunks = 1;
+  const int64_t chunks = num_seqs * wgs < kM1MinWgs ? (kM1FillWgs + wgs - 1) / wgs : num_seqs;
+  return chunks < 1 ? 1 : chunks;
+}
+int64_t m1_auto_chunk(const m2::LayerShape& sh, int64_t num_seqs, int64_t total_tokens) {
+  const int64_t chunks = m1_auto_target(sh, num_seqs);
   int64_t q = (total_tokens + chunks - 1) / chunks;
   q = (q + 15) / 16 * 16;
   return q < 16 ? 16 : q;
@@ -904,9 +906,13 @@ m2_status mamba1_prefill_workspace_size(const m2_pool* pool, int32_t num_seqs, i
     return fail(M2_ERR_UNSUPPORTED, "chunk_size must be 0 or in [16, 4096]");
   if (!m2::mamba1_supported(pool->sh.N, pool->sh.W))
     return fail(M2_ERR_UNSUPPORTED, "Mamba1 prefill supports d_state in {8,16,32,64,128,256}, got %d", pool->sh.N);
-  const int64_t q = chunk_size ? chunk_size : m1_auto_chunk(pool->sh, num_seqs, total_tokens);
+  // chunks: sum over sequences of ceil(len / q) <= floor(total / q) + num_seqs.  With the library's
+  // choice floor(T / q) <= min(T / 16, target) for every T <= total_tokens, so a workspace sized
+  // for a bound on the rows also serves any smaller batch of the same sequence count.
+  const int64_t nfull = chunk_size ? (int64_t)total_tokens / chunk_size
+                                   : std::min<int64_t>((int64_t)total_tokens / 16, m1_auto_target(pool->sh, num_seqs));
   M1Layout L;
-  if (!m1_layout(pool->sh, num_seqs, (int64_t)total_tokens / q + num_seqs, (int64_t)num_seqs * max_ckpt, &L))
+  if (!m1_layout(pool->sh, num_seqs, nfull + num_seqs, (int64_t)num_seqs * max_ckpt, &L))
     return fail(M2_ERR_SHAPE, "workspace size overflows 64 bits");
   *bytes = L.total;
   return ok();

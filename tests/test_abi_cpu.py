@@ -431,6 +431,12 @@ def test_mamba1_prefill_validation():
     assert lib().mamba1_prefill_workspace_size(h, 2, 100, 0, 0, byref(n3)) == 0
     assert lib().mamba1_prefill_workspace_size(h, 2, 100, 16, 0, byref(n4)) == 0
     assert n3.value == n4.value
+    # a size taken for more rows serves fewer (the chunk count bound only grows with the rows)
+    for t in (100, 200, 1000, 50000):
+        a_, b_ = c_uint64(), c_uint64()
+        assert lib().mamba1_prefill_workspace_size(h, 2, t, 0, 0, byref(a_)) == 0
+        assert lib().mamba1_prefill_workspace_size(h, 2, t + 37, 0, 0, byref(b_)) == 0
+        assert b_.value >= a_.value
     wsize(h, [0, 50, 100], chunk=64, expect=UNSUP)
 
     def call(hh=None, **kw):
