@@ -187,15 +187,14 @@ hipError_t launch_mamba1_decode(const Mamba1Params& p, int N, int W, int batch, 
 // (2) per (sequence, channel, state index) the pass through the sequence's chunks,
 // h <- exp(A sum Delta) h + S_c, writing the state entering each chunk; (3) every chunk again
 // from its entering state, with the outputs, the checkpoint states at their tokens and the final
-// state.  With one chunk per sequence only launch (3) runs, from the slots' states.  Launches
-// (1) and (3) take a
-// 256-thread workgroup per (chunk, block of channels) and walk the chunk in blocks of 16 rows:
-// the raw rows of the block are loaded cooperatively (the next block's requested while the
-// current one runs), each (row, channel) gets its conv, Delta, Delta x, D x and silu(z) once,
-// into LDS, and then the recurrence runs with a channel's state values spread over N/4 lanes in
-// fp32 registers.  Rows go in groups of four: each lane keeps one partial h C per row, and the
-// channel's lanes share out the four sums (a reduce-scatter over the lane quad), so every lane
-// finishes one row's output.
+// state.  With one chunk per sequence only launch (3) runs, from the slots' states.  Launches (1)
+// and (3) take a 256-thread workgroup per (chunk, block of channels) and walk the chunk in blocks
+// of 16 rows: the raw rows of the block are loaded cooperatively (the next block's requested
+// while the current one runs), each (row, channel) gets its conv, Delta, Delta x, D x and
+// silu(z) once, into LDS, and then the recurrence runs with a channel's state values spread over
+// N/4 lanes in fp32 registers.  Rows go in groups of four: each lane keeps one partial h C per
+// row, and the channel's lanes share out the four sums (a reduce-scatter over the lane quad), so
+// every lane finishes one row's output.
 namespace m2 {
 
 constexpr int kM1PV = 4;      // state values per lane
