@@ -124,6 +124,24 @@ def measured_traffic(root: str, record: str, sources, key: str):
     return rec[key] if sha == rec.get("source_sha256") else None
 
 
+def time_calls(fn, warm: int, reps: int, stream, e0, e1) -> float:
+    """GPU milliseconds per call of fn over reps calls after warm untimed ones (at least one).
+    The last untimed call is queued after the barrier, ahead of the first event, so the GPU is
+    busy while the host enqueues the timed calls: the events then time the calls back to back,
+    not the host's launch latency after the barrier."""
+    import torch
+    for _ in range(max(warm - 1, 0)):
+        fn()
+    torch.cuda.synchronize()
+    fn()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,10 +210,14 @@ def main() -> int:
         legs["mamba1_decode"] = mamba1_decode(dev, stream, e0, e1)
         legs["mamba1_prefill"] = mamba1_prefill_leg(dev, stream, e0, e1)
 
-    for _ in range(args.warmup):
+    # W untimed steps; the last of them is queued after the barrier, ahead of the first event, so
+    # that the GPU is not idle while the host enqueues the first timed step
+    for _ in range(max(args.warmup - 1, 0)):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if args.warmup > 0:
+        step()
     e0.record(stream)
     for _ in range(args.steps):
         step()
@@ -265,16 +287,7 @@ def checkpoint_copy_leg(pool, dev, stream, e0, e1) -> dict:
     n = COPY_PAIRS
     src = torch.arange(0, n, device=dev, dtype=torch.int32)
     dst = torch.arange(n, 2 * n, device=dev, dtype=torch.int32)
-    for _ in range(2):
-        pool.checkpoint(0, src, dst)
-    torch.cuda.synchronize()
-    reps = 10
-    e0.record(stream)
-    for _ in range(reps):
-        pool.checkpoint(0, src, dst)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    cms = e0.elapsed_time(e1) / reps
+    cms = time_calls(lambda: pool.checkpoint(0, src, dst), 2, 10, stream, e0, e1)
     ssm_b, conv_b = pool.info()
     moved = 2 * n * (ssm_b + conv_b)
     gbs = moved / (cms * 1e-3) / 1e9
@@ -299,15 +312,7 @@ def int8_store_leg(pool, sh, dev, stream, e0, e1) -> dict:
     res = {}
     for name, fn, nbytes in (("put", lambda: pool.int8_put(store, 0, sl, ent), put_bytes),
                              ("get", lambda: pool.int8_get(store, 0, ent, dst), get_bytes)):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(10):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 10
+        t = time_calls(fn, 2, 10, stream, e0, e1)
         res[name] = {"ms": t, "states_per_s": n / (t * 1e-3), "bytes_per_launch": nbytes,
                      "gbs": nbytes / (t * 1e-3) / 1e9, "hbm_frac": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
     res["workload"] = (f"{n} bf16 slots quantized into int8 store entries (put) and restored into fresh "
@@ -341,16 +346,7 @@ def prefill_leg(pw, dev, stream, e0, e1) -> dict:
         ppool.prefill(0, PW, pw["cu_seqlens"], [17], [0], px, pB, pC, pz, pdt, py,
                       chunk_size=pw["chunk"], workspace=ws)
 
-    for _ in range(3):
-        pstep()
-    torch.cuda.synchronize()
-    reps = 10
-    e0.record(stream)
-    for _ in range(reps):
-        pstep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    pms = e0.elapsed_time(e1) / reps
+    pms = time_calls(pstep, 3, 10, stream, e0, e1)
     flops = prefill_dense_flops_per_token(psh, pw["chunk"]) * T
     io_bytes = T * (psh.conv_dim + psh.intermediate + psh.nheads + psh.intermediate) * 2 \
         + psh.nheads * psh.head_dim * psh.d_state * 2 + psh.conv_dim * 3 * 2
@@ -397,15 +393,7 @@ def multi_token_decode(dev, stream, e0, e1, w) -> dict:
     W = LayerWeights.from_numpy(w["params"], dev)
     x, B, C = pool.split_xbc(u)
     step = lambda: pool.decode_multi(0, W, ins, outs, x, B, C, z, dt, y)
-    for _ in range(5):
-        step()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(50):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 50
+    t = time_calls(step, 5, 50, stream, e0, e1)
     ssm_b, conv_b = pool.info()
     io = (sh.conv_dim + sh.intermediate + sh.nheads + sh.intermediate) * 2
     nbytes = n * ((1 + K) * (ssm_b + conv_b) + K * io)
@@ -438,15 +426,7 @@ def mamba1_decode(dev, stream, e0, e1) -> dict:
     B, C = (torch.randn((n, N), generator=gen, device=dev).bfloat16() for _ in range(2))
     y = torch.empty((n, D), dtype=torch.bfloat16, device=dev)
     step = lambda: pool.mamba1_decode_step(0, W, sl, x, B, C, z, dt, y)
-    for _ in range(10):
-        step()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(200):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 200
+    t = time_calls(step, 10, 200, stream, e0, e1)
     ssm_b, conv_b = pool.info()
     per_seq = 2 * (ssm_b + conv_b) + (3 * D + 2 * N) * 2 + D * 2
     del pool
@@ -482,15 +462,7 @@ def mamba1_prefill_leg(dev, stream, e0, e1) -> dict:
     zeros = np.zeros(ns, np.uint8)
     ws = torch.empty(pool.mamba1_workspace_size(ns, T, Q), dtype=torch.uint8, device=dev)
     step = lambda: pool.mamba1_prefill(0, W, cu, slots, zeros, x, B, C, z, dt, y, chunk_size=Q, workspace=ws)
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(20):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 20
+    t = time_calls(step, 3, 20, stream, e0, e1)
     ssm_b, conv_b = pool.info()
     nbytes = T * (4 * D + 2 * N) * 2 + ns * (ssm_b + conv_b)
     del pool, ws
@@ -522,15 +494,7 @@ def prefill_workloads(dev, stream, e0, e1) -> dict:
         return u, z, dt, torch.empty(T, sh.intermediate, device=dev, dtype=y_dtype)
 
     def timed(fn, reps, warm=2):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return time_calls(fn, warm, reps, stream, e0, e1)
 
     res = {}
     _, params, lens, p_slots, d_slots, ck = synth.mixed_layout(3)
