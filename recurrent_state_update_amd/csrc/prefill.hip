@@ -951,7 +951,7 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
 
     const bool vt[2] = {rts[0] * 16 < len, rts[1] * 16 < len};
     // ---- loads of the state product's operand (bf16: under the output product; fp32-faithful
-    // planes: half there, half at the state product's start)
+    // planes: after it, so that their registers are free during it)
     const int nkb = (len + 31) / 32;
     Frag<SPLIT> bt[kMaxRowTiles / 2];
     const u16* const btb = a.Btf + (cg * N + (st_on ? wave : 0) * 16 + l16) * QC + 8 * q;
@@ -983,8 +983,6 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
         if (t == 0) {
           load_c(a, 1, cidx, ch);
           if (!SPLIT) load_bt(a, 0, 8);
-        } else if (SPLIT) {
-          load_bt(a, 0, 4);
         }
         continue;
       }
@@ -1022,14 +1020,12 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
           for (int pt = 0; pt < PT; ++pt) acc[pt] += accl[pt];
         }
       }
-      // the next operands, requested under this tile's products: tile 1's C columns and the state
-      // product's B^T (bf16: all of it; fp32-faithful planes: half here, half at its start)
+      // the next operands, requested under this tile's products: tile 1's C columns and (bf16) the
+      // state product's B^T
       __builtin_amdgcn_sched_barrier(0);
       if (t == 0) {
         load_c(a, 1, cidx, ch);
         if (!SPLIT) load_bt(a, 0, 8);
-      } else if (SPLIT) {
-        load_bt(a, 0, 4);
       }
       __builtin_amdgcn_sched_barrier(0);
       float aprev = 0.f;
@@ -1120,10 +1116,10 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(PrefillParams a) {
       default: phase_c(std::integral_constant<int, 3>{}); break;
     }
     ybase = static_cast<char*>(a.y) + (int64_t)ch.t0 * a.y_stride * yes;
-    // fp32-faithful planes: the second half of the state product's B^T, now that the output
-    // operands' registers are free; the conv then covers its latency
+    // fp32-faithful planes: the state product's B^T, now that the output operands' registers are
+    // free (requested during the outputs it made them spill); the conv then covers its latency
     if constexpr (SPLIT) {
-      load_bt(a, 4, 8);
+      load_bt(a, 0, 8);
       phase_b();
     }
 
